@@ -1,0 +1,339 @@
+"""Pins for the oracle: checks against facts that do not come from the oracle.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+the pages, the mathematics, or an independent library routine:
+
+* the printed witness result and the hand-worked witness values
+  (tests/golden/witness.json; tinymesh "Weighted aggregation experiment",
+  "Exact witness");
+* dense brute force: A_w as a dense matrix, Y = A_w X and dX = A_w^T dY as
+  numpy matrix products, dw as the dense product dY X^T sampled at each edge;
+* scipy.sparse on mid-size graphs;
+* numpy's stable argsort / bincount / cumsum for the lowering and the plan;
+* closed-form laws: adjoint identity, COO permutation, duplicate merging,
+  linearity in w, central differences of <dY, A_w X>, the one-node graph,
+  exact zeros on empty rows.
+
+They are plain functions so that tests/test_oracle_mutants.py can run the
+same set against deliberately broken copies of the oracle.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _witness():
+    with open(os.path.join(GOLDEN, "witness.json")) as f:
+        return json.load(f)
+
+
+def _dense(n, src, dst, w):
+    a = np.zeros((n, n), np.float64)
+    np.add.at(a, (dst, src), w.astype(np.float64))
+    return a
+
+
+def _dense_abs(n, src, dst, w):
+    a = np.zeros((n, n), np.float64)
+    np.add.at(a, (dst, src), np.abs(w.astype(np.float64)))
+    return a
+
+
+def _tiny_graphs(count, seed):
+    rng = np.random.default_rng(seed)
+    for _ in range(count):
+        n = int(rng.integers(1, 9))
+        e = int(rng.integers(0, 25))
+        h = int(rng.integers(1, 5))
+        src = rng.integers(0, n, e)
+        dst = rng.integers(0, n, e)
+        w = rng.uniform(-2, 2, e).astype(np.float32)
+        x = rng.standard_normal((n, h)).astype(np.float32)
+        dy = rng.standard_normal((n, h)).astype(np.float32)
+        yield n, src, dst, w, x, dy
+
+
+# --------------------------------------------------------------------------- witness
+
+def pin_witness_printed_edge_order():
+    g = _witness()
+    _, _, order = oracle.lower(g["n"], g["dst"], g["src"])
+    assert order.tolist() == g["printed"]["edge_order"], order
+
+
+def pin_witness_hand_values():
+    g = _witness()
+    hd = g["hand_derived"]
+    n = g["n"]
+    src, dst = np.array(g["src"]), np.array(g["dst"])
+    w = np.array(g["w"], np.float32)
+    x = np.array(g["x"], np.float32)[:, None]
+    dy = np.array(g["dy"], np.float32)[:, None]
+    y, _ = oracle.forward(n, src, dst, w, x)
+    dx, _ = oracle.input_grad(n, src, dst, w, dy)
+    dw, _ = oracle.edge_grad(src, dst, x, dy)
+    assert y[:, 0].tolist() == hd["Y"], y
+    assert dx[:, 0].tolist() == hd["dX"], dx
+    assert dw.tolist() == hd["dw"], dw
+    rowptr, col, order = oracle.lower(n, dst, src)
+    assert rowptr.tolist() == hd["rowptr"] and col.tolist() == hd["col"]
+    rowptr_t, col_t, order_t = oracle.lower(n, src, dst)
+    assert rowptr_t.tolist() == hd["rowptr_t"] and col_t.tolist() == hd["col_t"]
+    assert order_t.tolist() == hd["transpose_order"]
+
+
+def pin_witness_adjoint():
+    g = _witness()
+    n = g["n"]
+    src, dst = np.array(g["src"]), np.array(g["dst"])
+    w = np.array(g["w"], np.float32)
+    x = np.array(g["x"], np.float32)[:, None]
+    dy = np.array(g["dy"], np.float32)[:, None]
+    y, _ = oracle.forward(n, src, dst, w, x)
+    dx, _ = oracle.input_grad(n, src, dst, w, dy)
+    dw, _ = oracle.edge_grad(src, dst, x, dy)
+    a = float((dy.astype(np.float64) * y).sum())
+    b = float((x.astype(np.float64) * dx).sum())
+    c = float((w.astype(np.float64) * dw).sum())
+    assert a == b == c == g["hand_derived"]["adjoint"], (a, b, c)
+
+
+# --------------------------------------------------------------------------- brute force
+
+def pin_dense_bruteforce():
+    """Y = A X, dX = A^T dY, dw_e = (dY X^T)[dst_e, src_e], S from |A| |X|."""
+    for n, src, dst, w, x, dy in _tiny_graphs(400, 11):
+        a = _dense(n, src, dst, w)
+        aa = _dense_abs(n, src, dst, w)
+        x64, dy64 = x.astype(np.float64), dy.astype(np.float64)
+        y, sy = oracle.forward(n, src, dst, w, x)
+        dx, sdx = oracle.input_grad(n, src, dst, w, dy)
+        dw, sdw = oracle.edge_grad(src, dst, x, dy)
+        np.testing.assert_allclose(y, a @ x64, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dx, a.T @ dy64, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(sy, aa @ np.abs(x64), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(sdx, aa.T @ np.abs(dy64), rtol=1e-12, atol=1e-12)
+        g = dy64 @ x64.T
+        ga = np.abs(dy64) @ np.abs(x64).T
+        np.testing.assert_allclose(dw, g[dst, src] if len(src) else np.zeros(0),
+                                   rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(sdw, ga[dst, src] if len(src) else np.zeros(0),
+                                   rtol=1e-12, atol=1e-12)
+
+
+def pin_scipy_midsize():
+    import scipy.sparse as sp
+    for seed, (n, e, h) in enumerate([(300, 5000, 7), (2000, 20000, 16), (50, 3000, 33)]):
+        wl = synth.random_graph(n, e, h, 100 + seed)
+        a = sp.coo_matrix((wl.w.astype(np.float64), (wl.dst, wl.src)), shape=(n, n)).tocsr()
+        y, _ = oracle.forward(n, wl.src, wl.dst, wl.w, wl.x)
+        dx, _ = oracle.input_grad(n, wl.src, wl.dst, wl.w, wl.dy)
+        np.testing.assert_allclose(y, a @ wl.x.astype(np.float64), rtol=1e-10, atol=1e-10)
+        np.testing.assert_allclose(dx, a.T @ wl.dy.astype(np.float64), rtol=1e-10, atol=1e-10)
+        # SDDMM as scipy's elementwise product of the sampled dense product
+        dw, _ = oracle.edge_grad(wl.src, wl.dst, wl.x, wl.dy)
+        ref = np.einsum("eh,eh->e", wl.x[wl.src].astype(np.float64),
+                        wl.dy[wl.dst].astype(np.float64))
+        np.testing.assert_allclose(dw, ref, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- structure
+
+def _check_lowering(n, key, other):
+    rowptr, col, order = oracle.lower(n, key, other)
+    ref_order = np.argsort(key, kind="stable")
+    assert np.array_equal(order, ref_order)
+    ref_rowptr = np.concatenate([[0], np.cumsum(np.bincount(key, minlength=n))])
+    assert np.array_equal(rowptr, ref_rowptr)
+    assert np.array_equal(col, np.asarray(other)[ref_order])
+
+
+def pin_structure_numpy():
+    for n, src, dst, w, x, dy in _tiny_graphs(200, 12):
+        _check_lowering(n, dst, src)
+        _check_lowering(n, src, dst)
+    for wl in (synth.tiny_uniform(), synth.random_graph(5000, 60000, 1, 9)):
+        _check_lowering(wl.n, wl.dst, wl.src)
+        _check_lowering(wl.n, wl.src, wl.dst)
+
+
+def pin_structure_invariants():
+    wl = synth.random_graph(700, 9000, 1, 21)
+    for key, other in ((wl.dst, wl.src), (wl.src, wl.dst)):
+        rowptr, col, order = oracle.lower(wl.n, key, other)
+        assert np.array_equal(np.sort(order), np.arange(wl.e))        # a permutation
+        assert rowptr[0] == 0 and rowptr[-1] == wl.e and np.all(np.diff(rowptr) >= 0)
+        k = key[order]
+        assert np.all(np.diff(k) >= 0)                                 # rows non-decreasing
+        for i in range(wl.n):                                           # stable inside a row
+            seg = order[rowptr[i]:rowptr[i + 1]]
+            assert np.all(np.diff(seg) > 0)
+            assert np.all(key[seg] == i)
+
+
+def pin_out_of_range_rejected():
+    try:
+        oracle.lower(3, np.array([0, 3]), np.array([0, 0]))
+    except IndexError:
+        return
+    raise AssertionError("index 3 with n=3 accepted")
+
+
+# --------------------------------------------------------------------------- laws
+
+def pin_permutation_law():
+    wl = synth.random_graph(200, 3000, 5, 31)
+    rng = np.random.default_rng(3)
+    perm = rng.permutation(wl.e)
+    y0, _ = oracle.forward(wl.n, wl.src, wl.dst, wl.w, wl.x)
+    y1, _ = oracle.forward(wl.n, wl.src[perm], wl.dst[perm], wl.w[perm], wl.x)
+    dx0, _ = oracle.input_grad(wl.n, wl.src, wl.dst, wl.w, wl.dy)
+    dx1, _ = oracle.input_grad(wl.n, wl.src[perm], wl.dst[perm], wl.w[perm], wl.dy)
+    dw0, _ = oracle.edge_grad(wl.src, wl.dst, wl.x, wl.dy)
+    dw1, _ = oracle.edge_grad(wl.src[perm], wl.dst[perm], wl.x, wl.dy)
+    np.testing.assert_allclose(y1, y0, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dx1, dx0, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(dw1, dw0[perm])
+    # the lowering of a permuted COO list: same rows, maps renumbered through perm
+    r0, c0, o0 = oracle.lower(wl.n, wl.dst, wl.src)
+    r1, c1, o1 = oracle.lower(wl.n, wl.dst[perm], wl.src[perm])
+    assert np.array_equal(r0, r1)
+    for i in range(wl.n):
+        a = sorted(zip(perm[o1[r1[i]:r1[i + 1]]].tolist(), c1[r1[i]:r1[i + 1]].tolist()))
+        b = sorted(zip(o0[r0[i]:r0[i + 1]].tolist(), c0[r0[i]:r0[i + 1]].tolist()))
+        assert a == b
+
+
+def pin_duplicate_law():
+    """(s, t, w1) and (s, t, w2) act on Y and dX as one edge of weight w1 + w2,
+    keep separate positions, and each gets the same dw."""
+    src = np.array([0, 1, 1, 2, 1])
+    dst = np.array([1, 2, 2, 0, 2])
+    w = np.array([0.5, 0.25, -1.5, 2.0, 0.75], np.float32)
+    x = np.array([[1.0, -2.0], [3.0, 0.5], [-1.0, 4.0]], np.float32)
+    dy = np.array([[2.0, 1.0], [-0.5, 3.0], [1.5, -1.0]], np.float32)
+    y, _ = oracle.forward(3, src, dst, w, x)
+    msrc, mdst = np.array([0, 1, 2]), np.array([1, 2, 0])
+    mw = np.array([0.5, 0.25 - 1.5 + 0.75, 2.0], np.float32)
+    ym, _ = oracle.forward(3, msrc, mdst, mw, x)
+    np.testing.assert_allclose(y, ym, rtol=1e-12, atol=1e-12)
+    dx, _ = oracle.input_grad(3, src, dst, w, dy)
+    dxm, _ = oracle.input_grad(3, msrc, mdst, mw, dy)
+    np.testing.assert_allclose(dx, dxm, rtol=1e-12, atol=1e-12)
+    dw, _ = oracle.edge_grad(src, dst, x, dy)
+    assert dw[1] == dw[2] == dw[4]
+    rowptr, col, order = oracle.lower(3, dst, src)
+    assert order[rowptr[2]:rowptr[3]].tolist() == [1, 2, 4]          # separate positions
+
+
+def pin_linearity():
+    wl = synth.random_graph(100, 1500, 3, 41)
+    rng = np.random.default_rng(4)
+    w2 = rng.uniform(-1, 1, wl.e).astype(np.float32)
+    a, b = 0.5, -2.0                                  # exact scalings in binary
+    wsum = (a * wl.w + b * w2).astype(np.float32)
+    y1, _ = oracle.forward(wl.n, wl.src, wl.dst, wl.w, wl.x)
+    y2, _ = oracle.forward(wl.n, wl.src, wl.dst, w2, wl.x)
+    ys, _ = oracle.forward(wl.n, wl.src, wl.dst, wsum, wl.x)
+    np.testing.assert_allclose(ys, a * y1 + b * y2, rtol=1e-6, atol=1e-6)
+    dx1, _ = oracle.input_grad(wl.n, wl.src, wl.dst, wl.w, wl.dy)
+    dx2, _ = oracle.input_grad(wl.n, wl.src, wl.dst, w2, wl.dy)
+    dxs, _ = oracle.input_grad(wl.n, wl.src, wl.dst, wsum, wl.dy)
+    np.testing.assert_allclose(dxs, a * dx1 + b * dx2, rtol=1e-6, atol=1e-6)
+
+
+def pin_gradients_central_difference():
+    """f(w, X) = <dY, A_w X> is linear in w and in X, so central differences
+    recover dw = df/dw and dX = df/dX up to rounding."""
+    wl = synth.random_graph(12, 40, 3, 51)
+    dy64 = wl.dy.astype(np.float64)
+
+    def f(w, x):
+        y, _ = oracle.forward(wl.n, wl.src, wl.dst, w, x)
+        return float((dy64 * y).sum())
+
+    dw, _ = oracle.edge_grad(wl.src, wl.dst, wl.x, wl.dy)
+    step = np.float32(0.25)
+    for j in range(wl.e):
+        wp, wm = wl.w.copy(), wl.w.copy()
+        wp[j] += step
+        wm[j] -= step
+        fd = (f(wp, wl.x) - f(wm, wl.x)) / (float(wp[j]) - float(wm[j]))
+        assert abs(fd - dw[j]) <= 1e-9 * (1 + abs(dw[j])), (j, fd, dw[j])
+    dx, _ = oracle.input_grad(wl.n, wl.src, wl.dst, wl.w, wl.dy)
+    for i in range(wl.n):
+        for k in range(wl.h):
+            xp, xm = wl.x.copy(), wl.x.copy()
+            xp[i, k] += step
+            xm[i, k] -= step
+            fd = (f(wl.w, xp) - f(wl.w, xm)) / (float(xp[i, k]) - float(xm[i, k]))
+            assert abs(fd - dx[i, k]) <= 1e-9 * (1 + abs(dx[i, k])), (i, k, fd, dx[i, k])
+
+
+def pin_one_node():
+    e0 = np.zeros(0, np.int64)
+    x = np.array([[1.5, -2.0, 0.25]], np.float32)
+    y, s = oracle.forward(1, e0, e0, np.zeros(0, np.float32), x)
+    dx, _ = oracle.input_grad(1, e0, e0, np.zeros(0, np.float32), x)
+    dw, _ = oracle.edge_grad(e0, e0, x, x)
+    assert np.all(y == 0) and np.all(s == 0) and np.all(dx == 0) and dw.shape == (0,)
+    rowptr, col, order = oracle.lower(1, e0, e0)
+    assert rowptr.tolist() == [0, 0] and col.shape == (0,) and order.shape == (0,)
+    loops = np.zeros(4, np.int64)
+    w = np.array([0.5, -1.0, 2.0, 0.25], np.float32)
+    y, _ = oracle.forward(1, loops, loops, w, x)
+    np.testing.assert_allclose(y, float(w.astype(np.float64).sum()) * x.astype(np.float64),
+                               rtol=1e-12)
+    dw, _ = oracle.edge_grad(loops, loops, x, x)
+    np.testing.assert_allclose(dw, np.full(4, float((x.astype(np.float64) ** 2).sum())))
+
+
+def pin_empty_rows_exact_zero():
+    wl = synth.random_graph(500, 300, 4, 61)          # most rows empty in both directions
+    y, sy = oracle.forward(wl.n, wl.src, wl.dst, wl.w, wl.x)
+    dx, sdx = oracle.input_grad(wl.n, wl.src, wl.dst, wl.w, wl.dy)
+    no_in = np.bincount(wl.dst, minlength=wl.n) == 0
+    no_out = np.bincount(wl.src, minlength=wl.n) == 0
+    assert no_in.sum() > 100 and no_out.sum() > 100
+    assert np.all(y[no_in] == 0) and np.all(sy[no_in] == 0)
+    assert np.all(dx[no_out] == 0) and np.all(sdx[no_out] == 0)
+    assert np.all(sy[~no_in] > 0) and np.all(np.abs(y) <= sy)
+
+
+def pin_sampled_rows_match_full():
+    wl = synth.random_graph(400, 6000, 6, 71)
+    rows = np.array([0, 399, 17, 250, 3], np.int64)
+    y, sy = oracle.forward(wl.n, wl.src, wl.dst, wl.w, wl.x)
+    yr, syr = oracle.forward_rows(wl.n, wl.src, wl.dst, wl.w, wl.x, rows)
+    assert np.array_equal(yr, y[rows]) and np.array_equal(syr, sy[rows])
+    dx, sdx = oracle.input_grad(wl.n, wl.src, wl.dst, wl.w, wl.dy)
+    dxr, sdxr = oracle.input_grad_rows(wl.n, wl.src, wl.dst, wl.w, wl.dy, rows)
+    assert np.array_equal(dxr, dx[rows]) and np.array_equal(sdxr, sdx[rows])
+    dw, sdw = oracle.edge_grad(wl.src, wl.dst, wl.x, wl.dy)
+    edges = np.array([5, 0, 5999, 1234], np.int64)
+    dwe, sdwe = oracle.edge_grad_edges(wl.src, wl.dst, wl.x, wl.dy, edges)
+    assert np.array_equal(dwe, dw[edges]) and np.array_equal(sdwe, sdw[edges])
+
+
+def pin_degree_plan_numpy():
+    """Classes by Python's int.bit_length; plan = numpy stable argsort of -class."""
+    for wl in (synth.witness(), synth.tiny_uniform(), synth.random_graph(3000, 2000, 1, 81),
+               synth.rmat(10, 16, 82, 1)):
+        for key, other in ((wl.dst, wl.src), (wl.src, wl.dst)):
+            rowptr, _, _ = oracle.lower(wl.n, key, other)
+            perm, counts = oracle.degree_plan(wl.n, rowptr)
+            deg = np.diff(rowptr)
+            cls = np.array([int(d).bit_length() for d in deg], np.int64)
+            assert np.array_equal(counts, np.bincount(cls, minlength=33))
+            assert np.array_equal(perm, np.argsort(-cls, kind="stable"))
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

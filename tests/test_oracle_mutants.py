@@ -1,0 +1,68 @@
+"""Plant plausible mistakes in copies of oracle.c (on the CPU) and check that
+every one of them fails at least one pin.  This shows the pins constrain each
+part of the oracle: direction of A_w, operand roles, signs, the weight factor,
+stability and column fill of the lowering, the scale S, and the degree plan."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "forward_scatters_to_source": ("y[dst[j] * h + k] += t;", "y[src[j] * h + k] += t;"),
+    "forward_gathers_destination": ("double t = (double)w[j] * (double)x[src[j] * h + k];",
+                                    "double t = (double)w[j] * (double)x[dst[j] * h + k];"),
+    "forward_drops_weight": ("double t = (double)w[j] * (double)x[src[j] * h + k];",
+                             "double t = (double)x[src[j] * h + k];"),
+    "forward_wrong_sign": ("y[dst[j] * h + k] += t;", "y[dst[j] * h + k] -= t;"),
+    "forward_scale_signed": ("s[dst[j] * h + k] += fabs(t);", "s[dst[j] * h + k] += t;"),
+    "input_grad_scatters_to_destination": ("dx[src[j] * h + k] += t;", "dx[dst[j] * h + k] += t;"),
+    "input_grad_gathers_source": ("double t = (double)w[j] * (double)dy[dst[j] * h + k];\n            dx[src",
+                                  "double t = (double)w[j] * (double)dy[src[j] * h + k];\n            dx[src"),
+    "edge_grad_swapped_rows": ("double t = (double)x[src[j] * h + k] * (double)dy[dst[j] * h + k];\n            acc += t;\n            sa += fabs(t);\n        }\n        dw[j] = acc;",
+                               "double t = (double)x[dst[j] * h + k] * (double)dy[src[j] * h + k];\n            acc += t;\n            sa += fabs(t);\n        }\n        dw[j] = acc;"),
+    "edge_grad_bad_init": ("double acc = 0.0, sa = 0.0;\n        for (k = 0; k < h; k++) {\n            double t = (double)x[src[j] * h + k] * (double)dy[dst[j] * h + k];\n            acc += t;\n            sa += fabs(t);\n        }\n        dw[j] = acc;",
+                           "double acc = 1.0, sa = 0.0;\n        for (k = 0; k < h; k++) {\n            double t = (double)x[src[j] * h + k] * (double)dy[dst[j] * h + k];\n            acc += t;\n            sa += fabs(t);\n        }\n        dw[j] = acc;"),
+    "lower_unstable_descending": ("for (j = 0; j < e; j++) {               /* ascending COO ordinal       */",
+                                  "for (j = e - 1; j >= 0; j--) {"),
+    "lower_col_from_key": ("col[p] = other[j];", "col[p] = key[j];"),
+    "lower_rowptr_unshifted": ("rowptr[key[j] + 1] += 1;", "rowptr[key[j]] += 1;"),
+    "plan_ascending_classes": ("for (c = 32; c >= 0; c--) {", "for (c = 0; c <= 32; c++) {"),
+    "plan_class_off_by_one": ("class_count[k] += 1;", "class_count[k > 0 ? k - 1 : 0] += 1;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(old) >= 1, f"mutation site for {name} not found"
+    mutated = text.replace(old, new, 1)
+    c_path = tmp_path / "mutant.c"
+    so_path = tmp_path / "libmutant.so"
+    c_path.write_text(mutated)
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", str(so_path), str(c_path),
+                    "-lm"], check=True)
+    # Run the pins in a child process: a mutant that corrupts memory must not
+    # take the test runner down with it (a crash also counts as caught).
+    code = (
+        "import sys, oracle\n"
+        "from tests.oracle_pins import ALL_PINS\n"
+        "failed = []\n"
+        f"with oracle.using_library({str(so_path)!r}):\n"
+        "    for pin in ALL_PINS:\n"
+        "        try:\n"
+        "            pin()\n"
+        "        except Exception:\n"
+        "            failed.append(pin.__name__)\n"
+        "print(' '.join(failed))\n"
+        "sys.exit(0 if failed else 3)\n"
+    )
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    proc = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True,
+                          text=True, timeout=600)
+    assert proc.returncode != 3, f"mutant {name} passed every pin"

@@ -1,0 +1,284 @@
+"""gnn_sparse_message_amd -- weighted sparse message passing on AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libmp.so`` (declared in ``include/mp.h``).  Every
+step of the computation runs in the library's HIP kernels; this module only
+marshals arguments: it allocates outputs and graph arrays with torch (torch is
+the device allocator and stream provider), passes raw pointers and sizes, and
+turns status codes into exceptions.
+
+    g  = mp_graph_build(src, dst, num_nodes)      # stable COO -> CSR + transpose, on device
+    Y  = mp_spmm_fwd(g, w, X)                      # Y  = A_w X      (A_w[dst, src] += w)
+    dX = mp_spmm_dx(g, w, dY)                      # dX = A_w^T dY
+    dw = mp_edge_grad_dw(g, X, dY)                 # dw_e = <X[src_e], dY[dst_e]>, COO order
+
+(tinymesh "Weighted aggregation experiment": "Decision", "Edge order is
+explicit".)  The library must be built (``python -m gnn_sparse_message_amd._build``
+or ``__graft_entry__.build()``); importing this package fails loudly otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  -- loaded first so libmp.so binds to torch's HIP runtime
+
+__all__ = [
+    "Graph", "MpError", "mp_graph_build", "mp_graph_build_workspace_size", "mp_spmm_fwd",
+    "mp_spmm_dx", "mp_edge_grad_dw", "mp_status_string", "mp_version", "library_path",
+    "NUM_CLASSES",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmp.so")
+
+MP_OK = 0
+MP_ERR_NULL, MP_ERR_SHAPE, MP_ERR_DTYPE, MP_ERR_DEVICE, MP_ERR_INDEX = -1, -2, -3, -4, -5
+MP_ERR_ALIAS, MP_ERR_ALIGN, MP_ERR_WORKSPACE, MP_ERR_GRAPH, MP_ERR_HIP = -6, -7, -8, -9, -10
+MP_I32, MP_I64, MP_F32, MP_BF16 = 1, 2, 3, 4
+NUM_CLASSES = 33
+
+_DTYPE = {torch.int32: MP_I32, torch.int64: MP_I64, torch.float32: MP_F32,
+          torch.bfloat16: MP_BF16}
+
+
+class MpError(RuntimeError):
+    """A non-OK status from libmp.so; ``.status`` holds the code."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class MpValueError(MpError, ValueError):
+    pass
+
+
+class MpTypeError(MpError, TypeError):
+    pass
+
+
+class MpIndexError(MpError, IndexError):
+    pass
+
+
+_EXC = {MP_ERR_DTYPE: MpTypeError, MP_ERR_INDEX: MpIndexError, MP_ERR_NULL: MpValueError,
+        MP_ERR_SHAPE: MpValueError, MP_ERR_DEVICE: MpValueError, MP_ERR_ALIAS: MpValueError,
+        MP_ERR_ALIGN: MpValueError, MP_ERR_WORKSPACE: MpValueError}
+
+
+class _MpGraph(ctypes.Structure):
+    _fields_ = [
+        ("num_nodes", ctypes.c_int64), ("num_edges", ctypes.c_int64),
+        ("src", ctypes.c_void_p), ("dst", ctypes.c_void_p),
+        ("rowptr", ctypes.c_void_p), ("col", ctypes.c_void_p), ("edge_order", ctypes.c_void_p),
+        ("rowptr_t", ctypes.c_void_p), ("col_t", ctypes.c_void_p),
+        ("transpose_order", ctypes.c_void_p),
+        ("row_plan", ctypes.c_void_p), ("row_plan_t", ctypes.c_void_p),
+        ("class_count", ctypes.c_int64 * NUM_CLASSES),
+        ("class_count_t", ctypes.c_int64 * NUM_CLASSES),
+        ("built", ctypes.c_uint64),
+    ]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: the HIP library has not been built "
+            "(run `python -m gnn_sparse_message_amd._build`). There is no fallback.")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+    gp = ctypes.POINTER(_MpGraph)
+    sigs = {
+        "mp_graph_build_workspace_size": (i32, [i64, i64, ctypes.POINTER(sz)]),
+        "mp_graph_build": (i32, [vp, vp, i32, i64, i64, gp, vp, sz, vp]),
+        "mp_spmm_fwd": (i32, [gp, vp, vp, i32, i64, vp, vp]),
+        "mp_spmm_dx": (i32, [gp, vp, vp, i32, i64, vp, vp]),
+        "mp_edge_grad_dw": (i32, [gp, vp, vp, i32, i64, vp, vp]),
+        "mp_status_string": (ctypes.c_char_p, [i32]),
+        "mp_last_error_detail": (ctypes.c_char_p, []),
+        "mp_version": (i32, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def mp_version() -> int:
+    return int(_lib.mp_version())
+
+
+def mp_status_string(status: int) -> str:
+    return _lib.mp_status_string(status).decode()
+
+
+def _check(status: int, call: str):
+    if status == MP_OK:
+        return
+    detail = _lib.mp_last_error_detail().decode()
+    exc = _EXC.get(status, MpError)
+    raise exc(status, f"{call}: {mp_status_string(status)} -- {detail}")
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _code(t) -> int:
+    return _DTYPE.get(t.dtype, 0)   # 0 -> rejected by the library as MP_ERR_DTYPE
+
+
+def _stream(t) -> int:
+    """The current torch stream of t's GPU (0 for host tensors, which the library rejects)."""
+    return int(torch.cuda.current_stream(t.device).cuda_stream) if t.is_cuda else 0
+
+
+def _need_tensor(name, t):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class Graph:
+    """The lowered topology: torch int32 device tensors plus the C descriptor.
+
+    Arrays (names of ``include/mp.h``): src, dst, rowptr, col, edge_order,
+    rowptr_t, col_t, transpose_order, row_plan, row_plan_t; class_count and
+    class_count_t are host lists.  Read-only after the build.
+    """
+
+    _ARRAYS = ("src", "dst", "rowptr", "col", "edge_order", "rowptr_t", "col_t",
+               "transpose_order", "row_plan", "row_plan_t")
+
+    def __init__(self, num_nodes: int, num_edges: int, device):
+        n, e = int(num_nodes), int(num_edges)
+        self.num_nodes, self.num_edges, self.device = n, e, torch.device(device)
+        sizes = {"src": e, "dst": e, "rowptr": n + 1, "col": e, "edge_order": e,
+                 "rowptr_t": n + 1, "col_t": e, "transpose_order": e, "row_plan": n,
+                 "row_plan_t": n}
+        self.arrays = {k: torch.empty(max(v, 0), dtype=torch.int32, device=self.device)
+                       for k, v in sizes.items()}
+        d = _MpGraph()
+        d.num_nodes, d.num_edges = n, e
+        for k in self._ARRAYS:
+            setattr(d, k, _ptr(self.arrays[k]) if self.arrays[k].numel() else None)
+        self._desc = d
+
+    def __getattr__(self, name):
+        arrays = self.__dict__.get("arrays")
+        if arrays is not None and name in arrays:
+            return arrays[name]
+        raise AttributeError(name)
+
+    @property
+    def class_count(self):
+        return list(self._desc.class_count)
+
+    @property
+    def class_count_t(self):
+        return list(self._desc.class_count_t)
+
+    @property
+    def built(self) -> bool:
+        return self._desc.built != 0
+
+    @classmethod
+    def from_edge_index(cls, edge_index, num_nodes: int) -> "Graph":
+        """Build from a [2, E] edge_index (row 0 = source, row 1 = target)."""
+        _need_tensor("edge_index", edge_index)
+        if edge_index.dim() != 2 or edge_index.shape[0] != 2:
+            raise ValueError("edge_index must have shape [2, E]")
+        return mp_graph_build(edge_index[0], edge_index[1], num_nodes)
+
+
+def mp_graph_build_workspace_size(num_nodes: int, num_edges: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.mp_graph_build_workspace_size(int(num_nodes), int(num_edges), ctypes.byref(out)),
+           "mp_graph_build_workspace_size")
+    return int(out.value)
+
+
+def mp_graph_build(src, dst, num_nodes: int) -> Graph:
+    """Lower COO edges (src[e] -> dst[e], int32 or int64 device tensors) on device."""
+    _need_tensor("src", src)
+    _need_tensor("dst", dst)
+    if src.dim() != 1 or dst.dim() != 1 or src.shape[0] != dst.shape[0]:
+        raise ValueError("src and dst must be 1-D with the same length")
+    e = int(src.shape[0])
+    g = Graph(num_nodes, e, src.device)
+    ws_bytes = mp_graph_build_workspace_size(num_nodes, e)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=src.device)
+    status = _lib.mp_graph_build(_ptr(src) if e else None, _ptr(dst) if e else None, _code(src),
+                                 int(num_nodes), e, ctypes.byref(g._desc), _ptr(ws), ws_bytes,
+                                 _stream(src))
+    _check(status, "mp_graph_build")
+    return g
+
+
+def _features(name, t, g: Graph):
+    _need_tensor(name, t)
+    if t.dim() != 2 or t.shape[0] != g.num_nodes:
+        raise ValueError(f"{name} must have shape [{g.num_nodes}, H], got {tuple(t.shape)}")
+    return int(t.shape[1])
+
+
+def _weights(t, g: Graph):
+    # The C interface takes w as float32 memory; its dtype cannot be checked there.
+    _need_tensor("w", t)
+    if t.dtype != torch.float32:
+        raise TypeError(f"w must be float32, got {t.dtype}")
+    if t.dim() != 1 or t.shape[0] != g.num_edges:
+        raise ValueError(f"w must have shape [{g.num_edges}], got {tuple(t.shape)}")
+
+
+def _out(out, shape, like):
+    if out is None:
+        return torch.empty(shape, dtype=torch.float32, device=like.device)
+    _need_tensor("out", out)
+    if out.dtype != torch.float32:
+        raise TypeError(f"out must be float32, got {out.dtype}")
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out must have shape {tuple(shape)}, got {tuple(out.shape)}")
+    return out
+
+
+def mp_spmm_fwd(g: Graph, w, x, out=None):
+    """Y = A_w X, float32 [N, H]."""
+    _weights(w, g)
+    h = _features("x", x, g)
+    y = _out(out, (g.num_nodes, h), x)
+    _check(_lib.mp_spmm_fwd(ctypes.byref(g._desc), _ptr(w) if g.num_edges else None, _ptr(x),
+                            _code(x), h, _ptr(y), _stream(x)), "mp_spmm_fwd")
+    return y
+
+
+def mp_spmm_dx(g: Graph, w, dy, out=None):
+    """dX = A_w^T dY, float32 [N, H]."""
+    _weights(w, g)
+    h = _features("dy", dy, g)
+    dx = _out(out, (g.num_nodes, h), dy)
+    _check(_lib.mp_spmm_dx(ctypes.byref(g._desc), _ptr(w) if g.num_edges else None, _ptr(dy),
+                           _code(dy), h, _ptr(dx), _stream(dy)), "mp_spmm_dx")
+    return dx
+
+
+def mp_edge_grad_dw(g: Graph, x, dy, out=None):
+    """dw_e = <X[src_e], dY[dst_e]>, float32 [E] in COO order."""
+    h = _features("x", x, g)
+    if _features("dy", dy, g) != h:
+        raise ValueError("x and dy must have the same feature width")
+    code = _code(x) if x.dtype == dy.dtype else 0
+    dw = _out(out, (g.num_edges,), x)
+    _check(_lib.mp_edge_grad_dw(ctypes.byref(g._desc), _ptr(x), _ptr(dy), code, h,
+                                _ptr(dw) if g.num_edges else None, _stream(x)),
+           "mp_edge_grad_dw")
+    return dw

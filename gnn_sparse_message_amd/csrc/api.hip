@@ -1,0 +1,293 @@
+// api.hip -- the extern "C" entry points declared in include/mp.h: argument
+// validation on the host, then the launches in lower.hip, spmm.hip, sddmm.hip.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace mp {
+
+namespace {
+thread_local char g_detail[512] = "";
+constexpr uint64_t kBuiltMagic = 0x6d705f6772617068ull;   // "mp_graph"
+constexpr int64_t kMaxIndex = (int64_t)1 << 31;           // N, E < 2^31
+}  // namespace
+
+mp_status fail(mp_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+mp_status hip_fail(hipError_t e, const char *what) {
+    return fail(MP_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+namespace {
+
+size_t dtype_size(mp_dtype t) {
+    switch (t) {
+        case MP_I32: return 4;
+        case MP_I64: return 8;
+        case MP_F32: return 4;
+        case MP_BF16: return 2;
+        default: return 0;
+    }
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Device memory of the current device?  (Checked only for non-empty arrays.)
+mp_status check_device(const void *p, const char *name) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    hipPointerAttribute_t attr;
+    memset(&attr, 0, sizeof(attr));
+    e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();   // clear the sticky error of the failed query
+        return fail(MP_ERR_DEVICE, "%s is not memory known to the HIP runtime", name);
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+        return fail(MP_ERR_DEVICE, "%s is not device memory (memory type %d)", name,
+                    (int)attr.type);
+    if (attr.device != dev)
+        return fail(MP_ERR_DEVICE, "%s lives on device %d, current device is %d", name,
+                    attr.device, dev);
+    return MP_OK;
+}
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+    const char *name;
+};
+
+Range range(const void *p, int64_t count, size_t elem, const char *name) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + (uintptr_t)count * elem, name};
+}
+
+bool overlap(const Range &a, const Range &b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Ranges of every array a graph descriptor points to.
+int graph_ranges(const mp_graph *g, Range *out) {
+    const int64_t n = g->num_nodes, e = g->num_edges;
+    int k = 0;
+    out[k++] = range(g->src, e, 4, "graph src");
+    out[k++] = range(g->dst, e, 4, "graph dst");
+    out[k++] = range(g->rowptr, n + 1, 4, "graph rowptr");
+    out[k++] = range(g->col, e, 4, "graph col");
+    out[k++] = range(g->edge_order, e, 4, "graph edge_order");
+    out[k++] = range(g->rowptr_t, n + 1, 4, "graph rowptr_t");
+    out[k++] = range(g->col_t, e, 4, "graph col_t");
+    out[k++] = range(g->transpose_order, e, 4, "graph transpose_order");
+    out[k++] = range(g->row_plan, n, 4, "graph row_plan");
+    out[k++] = range(g->row_plan_t, n, 4, "graph row_plan_t");
+    return k;
+}
+
+mp_status check_graph(const mp_graph *g) {
+    if (!g) return fail(MP_ERR_NULL, "graph is NULL");
+    if (g->built != kBuiltMagic)
+        return fail(MP_ERR_GRAPH, "graph was not produced by a successful mp_graph_build");
+    return MP_OK;
+}
+
+mp_status check_sizes(int64_t n, int64_t e) {
+    if (n < 1 || n >= kMaxIndex) return fail(MP_ERR_SHAPE, "num_nodes %lld outside [1, 2^31)", (long long)n);
+    if (e < 0 || e >= kMaxIndex) return fail(MP_ERR_SHAPE, "num_edges %lld outside [0, 2^31)", (long long)e);
+    return MP_OK;
+}
+
+mp_status check_h(int64_t n, int64_t h) {
+    if (h < 1 || h >= kMaxIndex) return fail(MP_ERR_SHAPE, "feature width %lld outside [1, 2^31)", (long long)h);
+    if (n > ((int64_t)1 << 62) / h) return fail(MP_ERR_SHAPE, "N*H overflows");
+    return MP_OK;
+}
+
+// Shared validation of one aggregation call (forward or input gradient).
+mp_status check_spmm(const mp_graph *g, const float *w, const void *x, mp_dtype dt, int64_t h,
+                     float *y, const char *xname, const char *yname) {
+    mp_status st = check_graph(g);
+    if (st != MP_OK) return st;
+    const int64_t n = g->num_nodes, e = g->num_edges;
+    if (!x) return fail(MP_ERR_NULL, "%s is NULL", xname);
+    if (!y) return fail(MP_ERR_NULL, "%s is NULL", yname);
+    if (!w && e > 0) return fail(MP_ERR_NULL, "w is NULL with %lld edges", (long long)e);
+    if ((st = check_h(n, h)) != MP_OK) return st;
+    if (dt != MP_F32 && dt != MP_BF16)
+        return fail(MP_ERR_DTYPE, "%s dtype code %d: expected MP_F32 or MP_BF16", xname, (int)dt);
+    const size_t xs = dtype_size(dt);
+    if (!aligned(x, xs)) return fail(MP_ERR_ALIGN, "%s not aligned to %zu bytes", xname, xs);
+    if (!aligned(y, 4)) return fail(MP_ERR_ALIGN, "%s not aligned to 4 bytes", yname);
+    if (w && !aligned(w, 4)) return fail(MP_ERR_ALIGN, "w not aligned to 4 bytes");
+    if ((st = check_device(x, xname)) != MP_OK) return st;
+    if ((st = check_device(y, yname)) != MP_OK) return st;
+    if (e > 0 && (st = check_device(w, "w")) != MP_OK) return st;
+    const Range ry = range(y, n * h, 4, yname);
+    Range others[12];
+    int k = graph_ranges(g, others);
+    others[k++] = range(x, n * h, xs, xname);
+    others[k++] = range(w, e, 4, "w");
+    for (int i = 0; i < k; ++i)
+        if (overlap(ry, others[i]))
+            return fail(MP_ERR_ALIAS, "%s overlaps %s", yname, others[i].name);
+    return MP_OK;
+}
+
+}  // namespace
+}  // namespace mp
+
+using namespace mp;
+
+extern "C" {
+
+mp_status mp_graph_build_workspace_size(int64_t num_nodes, int64_t num_edges, size_t *bytes) {
+    if (!bytes) return fail(MP_ERR_NULL, "bytes is NULL");
+    mp_status st = check_sizes(num_nodes, num_edges);
+    if (st != MP_OK) return st;
+    *bytes = lower_layout(num_nodes, num_edges).total;
+    return MP_OK;
+}
+
+mp_status mp_graph_build(const void *src, const void *dst, mp_dtype idx_dtype, int64_t num_nodes,
+                         int64_t num_edges, mp_graph *g, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+    if (!g) return fail(MP_ERR_NULL, "graph descriptor is NULL");
+    g->built = 0;
+    mp_status st = check_sizes(num_nodes, num_edges);
+    if (st != MP_OK) return st;
+    const int64_t n = num_nodes, e = num_edges;
+    if (idx_dtype != MP_I32 && idx_dtype != MP_I64)
+        return fail(MP_ERR_DTYPE, "index dtype code %d: expected MP_I32 or MP_I64", (int)idx_dtype);
+    if (e > 0 && (!src || !dst)) return fail(MP_ERR_NULL, "src or dst is NULL with %lld edges", (long long)e);
+    struct {
+        const void *p;
+        const char *name;
+        int64_t count;
+    } arrays[] = {
+        {g->src, "graph src", e},       {g->dst, "graph dst", e},
+        {g->rowptr, "graph rowptr", n + 1}, {g->col, "graph col", e},
+        {g->edge_order, "graph edge_order", e}, {g->rowptr_t, "graph rowptr_t", n + 1},
+        {g->col_t, "graph col_t", e},   {g->transpose_order, "graph transpose_order", e},
+        {g->row_plan, "graph row_plan", n}, {g->row_plan_t, "graph row_plan_t", n},
+    };
+    for (const auto &a : arrays) {
+        if (a.count > 0 && !a.p) return fail(MP_ERR_NULL, "%s is NULL", a.name);
+        if (a.p && !aligned(a.p, 4)) return fail(MP_ERR_ALIGN, "%s not aligned to 4 bytes", a.name);
+    }
+    const size_t need = lower_layout(n, e).total;
+    if (!workspace) return fail(MP_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes < need)
+        return fail(MP_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    if (!aligned(workspace, 256)) return fail(MP_ERR_ALIGN, "workspace not aligned to 256 bytes");
+    const size_t is = dtype_size(idx_dtype);
+    if (e > 0) {
+        if (!aligned(src, is) || !aligned(dst, is))
+            return fail(MP_ERR_ALIGN, "src/dst not aligned to %zu bytes", is);
+        if ((st = check_device(src, "src")) != MP_OK) return st;
+        if ((st = check_device(dst, "dst")) != MP_OK) return st;
+    }
+    for (const auto &a : arrays)
+        if (a.count > 0 && (st = check_device(a.p, a.name)) != MP_OK) return st;
+    if ((st = check_device(workspace, "workspace")) != MP_OK) return st;
+
+    // Outputs (graph arrays, workspace) must not overlap each other or the inputs.
+    Range r[13];
+    g->num_nodes = n;
+    g->num_edges = e;
+    int k = graph_ranges(g, r);
+    r[k++] = Range{reinterpret_cast<uintptr_t>(workspace),
+                   reinterpret_cast<uintptr_t>(workspace) + need, "workspace"};
+    const Range in_s = range(src, e, is, "src"), in_d = range(dst, e, is, "dst");
+    for (int i = 0; i < k; ++i) {
+        if (overlap(r[i], in_s) || overlap(r[i], in_d))
+            return fail(MP_ERR_ALIAS, "%s overlaps the input edge list", r[i].name);
+        for (int j = i + 1; j < k; ++j)
+            if (overlap(r[i], r[j]))
+                return fail(MP_ERR_ALIAS, "%s overlaps %s", r[i].name, r[j].name);
+    }
+
+    int bad = 0;
+    st = lower_run(src, dst, idx_dtype, n, e, g, workspace, static_cast<hipStream_t>(stream), &bad);
+    if (st != MP_OK) return st;
+    if (bad) return fail(MP_ERR_INDEX, "an edge endpoint lies outside [0, %lld)", (long long)n);
+    g->built = kBuiltMagic;
+    return MP_OK;
+}
+
+mp_status mp_spmm_fwd(const mp_graph *g, const float *w, const void *x, mp_dtype x_dtype,
+                      int64_t h, float *y, void *stream) {
+    mp_status st = check_spmm(g, w, x, x_dtype, h, y, "x", "y");
+    if (st != MP_OK) return st;
+    CsrView v{g->rowptr, g->col, g->edge_order, g->row_plan, g->class_count, g->num_nodes,
+              g->num_edges};
+    return spmm_run(v, w, x, x_dtype, h, y, static_cast<hipStream_t>(stream));
+}
+
+mp_status mp_spmm_dx(const mp_graph *g, const float *w, const void *dy, mp_dtype dy_dtype,
+                     int64_t h, float *dx, void *stream) {
+    mp_status st = check_spmm(g, w, dy, dy_dtype, h, dx, "dy", "dx");
+    if (st != MP_OK) return st;
+    CsrView v{g->rowptr_t, g->col_t, g->transpose_order, g->row_plan_t, g->class_count_t,
+              g->num_nodes, g->num_edges};
+    return spmm_run(v, w, dy, dy_dtype, h, dx, static_cast<hipStream_t>(stream));
+}
+
+mp_status mp_edge_grad_dw(const mp_graph *g, const void *x, const void *dy, mp_dtype dtype,
+                          int64_t h, float *dw, void *stream) {
+    mp_status st = check_graph(g);
+    if (st != MP_OK) return st;
+    const int64_t n = g->num_nodes, e = g->num_edges;
+    if (!x || !dy) return fail(MP_ERR_NULL, "x or dy is NULL");
+    if (!dw && e > 0) return fail(MP_ERR_NULL, "dw is NULL with %lld edges", (long long)e);
+    if ((st = check_h(n, h)) != MP_OK) return st;
+    if (dtype != MP_F32 && dtype != MP_BF16)
+        return fail(MP_ERR_DTYPE, "feature dtype code %d: expected MP_F32 or MP_BF16", (int)dtype);
+    const size_t xs = dtype_size(dtype);
+    if (!aligned(x, xs) || !aligned(dy, xs))
+        return fail(MP_ERR_ALIGN, "x/dy not aligned to %zu bytes", xs);
+    if (dw && !aligned(dw, 4)) return fail(MP_ERR_ALIGN, "dw not aligned to 4 bytes");
+    if ((st = check_device(x, "x")) != MP_OK) return st;
+    if ((st = check_device(dy, "dy")) != MP_OK) return st;
+    if (e == 0) return MP_OK;
+    if ((st = check_device(dw, "dw")) != MP_OK) return st;
+    const Range rdw = range(dw, e, 4, "dw");
+    Range others[12];
+    int k = graph_ranges(g, others);
+    others[k++] = range(x, n * h, xs, "x");
+    others[k++] = range(dy, n * h, xs, "dy");
+    for (int i = 0; i < k; ++i)
+        if (overlap(rdw, others[i])) return fail(MP_ERR_ALIAS, "dw overlaps %s", others[i].name);
+    return sddmm_run(g->src, g->dst, e, x, dy, dtype, h, dw, static_cast<hipStream_t>(stream));
+}
+
+const char *mp_status_string(mp_status s) {
+    switch (s) {
+        case MP_OK: return "MP_OK";
+        case MP_ERR_NULL: return "MP_ERR_NULL: a required pointer is NULL";
+        case MP_ERR_SHAPE: return "MP_ERR_SHAPE: a size is out of range";
+        case MP_ERR_DTYPE: return "MP_ERR_DTYPE: unsupported dtype";
+        case MP_ERR_DEVICE: return "MP_ERR_DEVICE: pointer is not device memory of the current GPU";
+        case MP_ERR_INDEX: return "MP_ERR_INDEX: edge endpoint outside [0, N)";
+        case MP_ERR_ALIAS: return "MP_ERR_ALIAS: output overlaps an input or the graph";
+        case MP_ERR_ALIGN: return "MP_ERR_ALIGN: pointer misaligned for its element type";
+        case MP_ERR_WORKSPACE: return "MP_ERR_WORKSPACE: workspace missing or too small";
+        case MP_ERR_GRAPH: return "MP_ERR_GRAPH: graph not built";
+        case MP_ERR_HIP: return "MP_ERR_HIP: HIP runtime error";
+        default: return "unknown mp_status";
+    }
+}
+
+const char *mp_last_error_detail(void) { return g_detail; }
+
+int32_t mp_version(void) { return 100; }   // 0.1.0
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// common.h -- internal declarations shared by the library's translation units.
+// Not part of the public interface (that is include/mp.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "mp.h"
+
+namespace mp {
+
+constexpr int kWave = 64;             // CDNA wavefront width
+constexpr int kBlock = 256;           // threads per workgroup for every kernel here
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// Record a failure detail for mp_last_error_detail() and return `s`.
+mp_status fail(mp_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// Map a HIP error to MP_ERR_HIP with `what` in the detail text.
+mp_status hip_fail(hipError_t e, const char *what);
+
+#define MP_HIP_CHECK(expr, what)                       \
+    do {                                               \
+        hipError_t e__ = (expr);                       \
+        if (e__ != hipSuccess) return mp::hip_fail(e__, what); \
+    } while (0)
+
+// ---------------------------------------------------------------- lowering
+// Workspace layout for the lowering (byte offsets from the workspace base).
+struct LowerLayout {
+    size_t k0, k1, v0;        // [E] u32 ping-pong keys, one value buffer
+    size_t hist;              // [256 * max_blocks] u32 per-block digit counts
+    size_t dtot;              // [256] u32 digit totals of the current pass
+    size_t small;             // [64 + 256 + 256] u32: flag, plan totals fwd, plan totals t
+    size_t total;
+};
+LowerLayout lower_layout(int64_t n, int64_t e);
+
+// Enqueue the whole lowering; on success copies the class counts and the
+// index flag back to the host (synchronising `stream`).
+mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_t n, int64_t e,
+                    mp_graph *g, void *ws, hipStream_t stream, int *bad_index);
+
+// ---------------------------------------------------------------- SpMM
+// One aggregation over a CSR form (rows = owners).  `x` holds [n, h] features
+// of dtype `dt`; `out` receives [n, h] float32.
+struct CsrView {
+    const int32_t *rowptr;
+    const int32_t *col;
+    const int32_t *order;
+    const int32_t *plan;
+    const int64_t *class_count;   // host, MP_NUM_CLASSES entries
+    int64_t n;
+    int64_t e;
+};
+mp_status spmm_run(const CsrView &csr, const float *w, const void *x, mp_dtype dt, int64_t h,
+                   float *out, hipStream_t stream);
+
+// ---------------------------------------------------------------- SDDMM
+mp_status sddmm_run(const int32_t *src, const int32_t *dst, int64_t e, const void *x,
+                    const void *dy, mp_dtype dt, int64_t h, float *dw, hipStream_t stream);
+
+}  // namespace mp

@@ -1,0 +1,333 @@
+// spmm.hip -- weighted CSR aggregation out[i, :] = sum_p w[order[p]] * in[col[p], :]
+// over p in [rowptr[i], rowptr[i+1]), with w in COO order.
+//
+// The forward pass Y = A_w X runs it on the destination-owned CSR with
+// edge_order, the input gradient dX = A_w^T dY on the source-owned CSR with
+// transpose_order (tinymesh "Weighted aggregation experiment", "Decision" and
+// the two columns of the diagram under "Edge order is explicit").  Each output
+// row has exactly one owner, there are no atomics and no [E, H] message rows.
+//
+// Mapping on gfx950.  A feature row is split over a "group" of L lanes, each
+// lane holding VEC contiguous features (16-byte loads: 4 fp32 or 8 bf16).  Rows
+// are visited through the degree plan (rows sorted by length class, longest
+// first) and handed to owners of three sizes within ONE launch, so long rows
+// start first and their tail overlaps the short ones:
+//   hub  rows -> a whole 256-thread workgroup (4 waves split the edges, then a
+//                fixed-order LDS reduction);
+//   long rows -> one 64-lane wave (64/L groups split the edges, butterfly
+//                reduction across groups);
+//   short rows (and empty rows, written as zeros) -> one group of L lanes.
+// For each run of edges the team loads col[p] and w[order[p]] once, coalesced,
+// one edge per lane, then broadcasts them with lane permutes while every group
+// gathers U feature rows at a time (several 16-byte loads in flight per lane).
+// Accumulation is fp32; bf16 inputs are widened exactly.  Feature widths above
+// 64*VEC are covered by column blocks in gridDim.y.
+#include "common.h"
+
+#include <stdlib.h>
+
+namespace mp {
+namespace {
+
+constexpr int kUnroll = 4;   // feature rows in flight per group per step
+
+// ------------------------------------------------------------------ feature loads
+template <typename T, int VEC>
+struct Feat;
+
+template <>
+struct Feat<float, 4> {
+    static __device__ __forceinline__ void load(const float *p, float (&v)[4]) {
+        const float4 q = *reinterpret_cast<const float4 *>(p);
+        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    }
+};
+template <>
+struct Feat<float, 1> {
+    static __device__ __forceinline__ void load(const float *p, float (&v)[1]) { v[0] = *p; }
+};
+template <>
+struct Feat<uint16_t, 8> {   // bf16: widen exactly by placing the bits in the high half
+    static __device__ __forceinline__ void load(const uint16_t *p, float (&v)[8]) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(p);
+        const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(u[i] << 16);
+            v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
+    }
+};
+template <>
+struct Feat<uint16_t, 1> {
+    static __device__ __forceinline__ void load(const uint16_t *p, float (&v)[1]) {
+        v[0] = __uint_as_float((uint32_t)(*p) << 16);
+    }
+};
+
+template <int VEC>
+__device__ __forceinline__ void store_row(float *p, const float (&v)[VEC]) {
+    if constexpr (VEC % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < VEC; i += 4)
+            *reinterpret_cast<float4 *>(p + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) p[i] = v[i];
+    }
+}
+
+struct SpmmArgs {
+    const int32_t *rowptr;
+    const int32_t *col;
+    const int32_t *order;
+    const int32_t *plan;
+    const float *w;
+    const void *x;
+    float *y;
+    int64_t h;
+    int64_t n, e;                     // rows, edges (bounds for the data-dependent indices)
+    int32_t n_hub, n_wave, n_group;   // rows of each owner kind, consecutive in the plan
+    int32_t blk_hub, blk_wave, blk_group;   // blocks given to each kind (wave and group
+                                            // owners stride over their rows)
+};
+
+// Accumulate edges [beg, end) of one row into acc.  The team is TL lanes of one
+// wave (TL = 64 for wave and hub owners, TL = L for group owners) and walks the
+// row in runs of TL edges: run starts are `first`, `first + stride`, ...  All
+// lanes of the team execute every permute with the same trip count, so each
+// permute reads from an active lane.
+template <typename T, int VEC, int L, int TL>
+__device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int64_t end,
+                                           int64_t stride, int lane, int64_t hoff, bool active,
+                                           float (&acc)[VEC]) {
+    constexpr int G = TL / L;                 // groups per team
+    const int tl = lane % TL;
+    const int tb = lane - tl;                 // first lane of the team
+    const int g = tl / L;
+    const T *__restrict__ X = static_cast<const T *>(a.x);
+    for (int64_t base = first; base < end; base += stride) {
+        const int64_t p = base + tl;
+        int c = 0;
+        float wt = 0.f;
+        if (p < end) {
+            c = a.col[p];
+            const uint32_t o = (uint32_t)a.order[p];
+            wt = a.w[(int64_t)o < a.e ? o : 0u];   // order is a permutation of [0, e)
+        }
+        const int n = end - base < TL ? (int)(end - base) : TL;
+        const int trips = (n + G - 1) / G;
+        for (int j = 0; j < trips; j += kUnroll) {
+            int cu[kUnroll];
+            float wu[kUnroll];
+            bool ok[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int k = g + (j + u) * G;
+                ok[u] = (j + u < trips) && k < n;
+                const int sl = tb + (k < n ? k : n - 1);
+                cu[u] = __shfl(c, sl);
+                wu[u] = __shfl(wt, sl);
+            }
+            float xv[kUnroll][VEC];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                if (ok[u] && active) {
+                    Feat<T, VEC>::load(X + (int64_t)cu[u] * a.h + hoff, xv[u]);
+                } else {
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) xv[u][v] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const float wv = ok[u] ? wu[u] : 0.f;
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) acc[v] = fmaf(wv, xv[u][v], acc[v]);
+            }
+        }
+    }
+}
+
+template <typename T, int VEC, int L>
+__global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int sub = lane % L;
+    const int64_t hoff = (int64_t)blockIdx.y * (L * VEC) + (int64_t)sub * VEC;
+    const bool active = hoff < a.h;
+    float acc[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+
+    int64_t b = blockIdx.x;
+    if (b < a.blk_hub) {
+        // ---- hub row: the whole workgroup
+        __shared__ float s_red[kWavesPerBlock][L * VEC];
+        const int row = a.plan[b];
+        if ((uint32_t)row >= (uint64_t)a.n) return;   // the plan is a permutation of [0, n)
+        const int64_t beg = a.rowptr[row], end = a.rowptr[row + 1];
+        accumulate<T, VEC, L, kWave>(a, beg + (int64_t)wv * kWave, end,
+                                     (int64_t)kBlock, lane, hoff, active, acc);
+#pragma unroll
+        for (int off = L; off < kWave; off <<= 1)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) acc[v] += __shfl_xor(acc[v], off);
+        if (lane < L) {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) s_red[wv][sub * VEC + v] = acc[v];
+        }
+        __syncthreads();
+        if (wv == 0 && lane < L && active) {
+            float r[VEC];
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                float s = s_red[0][sub * VEC + v];
+#pragma unroll
+                for (int w2 = 1; w2 < kWavesPerBlock; ++w2) s += s_red[w2][sub * VEC + v];
+                r[v] = s;
+            }
+            store_row<VEC>(a.y + (int64_t)row * a.h + hoff, r);
+        }
+        return;
+    }
+    b -= a.blk_hub;
+    if (b < a.blk_wave) {
+        // ---- long rows: one wave each
+        for (int64_t idx = b * kWavesPerBlock + wv; idx < a.n_wave;
+             idx += (int64_t)a.blk_wave * kWavesPerBlock) {
+            const int row = a.plan[a.n_hub + idx];
+            if ((uint32_t)row >= (uint64_t)a.n) continue;
+            const int64_t beg = a.rowptr[row], end = a.rowptr[row + 1];
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+            accumulate<T, VEC, L, kWave>(a, beg, end, (int64_t)kWave, lane, hoff, active, acc);
+#pragma unroll
+            for (int off = L; off < kWave; off <<= 1)
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) acc[v] += __shfl_xor(acc[v], off);
+            if (lane < L && active) store_row<VEC>(a.y + (int64_t)row * a.h + hoff, acc);
+        }
+        return;
+    }
+    b -= a.blk_wave;
+    // ---- short or empty rows: one group of L lanes each
+    constexpr int64_t kRowsPerBlock = kBlock / L;
+    for (int64_t idx = b * kRowsPerBlock + threadIdx.x / L; idx < a.n_group;
+         idx += (int64_t)a.blk_group * kRowsPerBlock) {
+        const int row = a.plan[a.n_hub + a.n_wave + idx];
+        if ((uint32_t)row >= (uint64_t)a.n) continue;
+        const int64_t beg = a.rowptr[row], end = a.rowptr[row + 1];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+        accumulate<T, VEC, L, L>(a, beg, end, (int64_t)L, lane, hoff, active, acc);
+        if (active) store_row<VEC>(a.y + (int64_t)row * a.h + hoff, acc);
+    }
+}
+
+// ------------------------------------------------------------------ dispatch
+struct Thresholds {
+    int hub_min_len;     // rows this long or longer get a workgroup
+    int wave_min_len;    // rows this long or longer (below hub) get a wave
+};
+
+// Owner-size thresholds.  MP_HUB_MIN_LEN / MP_WAVE_MIN_LEN override them (tuning).
+Thresholds thresholds_for(int L) {
+    Thresholds t;
+    const int G = kWave / L;
+    t.hub_min_len = 4096;
+    t.wave_min_len = G > 1 ? 4 * G : (1 << 30);
+    if (const char *s = getenv("MP_HUB_MIN_LEN")) t.hub_min_len = atoi(s);
+    if (const char *s = getenv("MP_WAVE_MIN_LEN")) t.wave_min_len = atoi(s);
+    if (t.hub_min_len < 1) t.hub_min_len = 1;
+    if (t.wave_min_len < 1) t.wave_min_len = 1;
+    return t;
+}
+
+// Number of plan rows (from the front) whose length is >= len: the classes are
+// sorted high to low, and a class is counted only if all its rows qualify,
+// i.e. 2^(c-1) >= len.
+int64_t rows_at_least(const int64_t *cc, int64_t len) {
+    int64_t r = 0;
+    for (int c = MP_NUM_CLASSES - 1; c >= 1; --c)
+        if (((int64_t)1 << (c - 1)) >= len) r += cc[c];
+    return r;
+}
+
+template <typename T, int VEC, int L>
+mp_status launch(const CsrView &csr, const float *w, const void *x, int64_t h, float *out,
+                 hipStream_t s) {
+    const Thresholds th = thresholds_for(L);
+    SpmmArgs a;
+    a.rowptr = csr.rowptr;
+    a.col = csr.col;
+    a.order = csr.order;
+    a.plan = csr.plan;
+    a.w = w;
+    a.x = x;
+    a.y = out;
+    a.h = h;
+    a.n = csr.n;
+    a.e = csr.e;
+    const int64_t at_hub = rows_at_least(csr.class_count, th.hub_min_len);
+    int64_t at_wave = rows_at_least(csr.class_count, th.wave_min_len);
+    if (at_wave < at_hub) at_wave = at_hub;
+    a.n_hub = (int32_t)at_hub;
+    a.n_wave = (int32_t)(at_wave - at_hub);
+    a.n_group = (int32_t)(csr.n - at_wave);
+    // A launch holds at most 2^32 - 1 work-items; wave and group owners stride.
+    constexpr int64_t kMaxKindBlocks = 1 << 22;
+    const int64_t rows_per_blk = kBlock / L;
+    const int64_t blk_wave = (a.n_wave + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t blk_group = (a.n_group + rows_per_blk - 1) / rows_per_blk;
+    a.blk_hub = a.n_hub;
+    a.blk_wave = (int32_t)(blk_wave < kMaxKindBlocks ? blk_wave : kMaxKindBlocks);
+    a.blk_group = (int32_t)(blk_group < kMaxKindBlocks ? blk_group : kMaxKindBlocks);
+    const int64_t gx = (int64_t)a.blk_hub + a.blk_wave + a.blk_group;
+    const int64_t gy = (h + (int64_t)L * VEC - 1) / ((int64_t)L * VEC);
+    if (gx <= 0) return MP_OK;
+    if (gx > (int64_t)3 << 22 || gy > 65535)
+        return fail(MP_ERR_SHAPE, "launch grid too large (%lld x %lld)", (long long)gx,
+                    (long long)gy);
+    spmm_kernel<T, VEC, L><<<dim3((unsigned)gx, (unsigned)gy), kBlock, 0, s>>>(a);
+    MP_HIP_CHECK(hipGetLastError(), "spmm launch");
+    return MP_OK;
+}
+
+int lanes_for(int64_t h, int vec) {
+    const int64_t need = (h + vec - 1) / vec;
+    int L = 1;
+    while (L < kWave && L < need) L <<= 1;
+    return L;
+}
+
+template <typename T, int VEC>
+mp_status launch_lanes(const CsrView &csr, const float *w, const void *x, int64_t h, float *out,
+                       hipStream_t s) {
+    switch (lanes_for(h, VEC)) {
+        case 1: return launch<T, VEC, 1>(csr, w, x, h, out, s);
+        case 2: return launch<T, VEC, 2>(csr, w, x, h, out, s);
+        case 4: return launch<T, VEC, 4>(csr, w, x, h, out, s);
+        case 8: return launch<T, VEC, 8>(csr, w, x, h, out, s);
+        case 16: return launch<T, VEC, 16>(csr, w, x, h, out, s);
+        case 32: return launch<T, VEC, 32>(csr, w, x, h, out, s);
+        default: return launch<T, VEC, 64>(csr, w, x, h, out, s);
+    }
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+mp_status spmm_run(const CsrView &csr, const float *w, const void *x, mp_dtype dt, int64_t h,
+                   float *out, hipStream_t s) {
+    const bool vec_ok = aligned16(x) && aligned16(out);
+    if (dt == MP_F32) {
+        if (vec_ok && h % 4 == 0) return launch_lanes<float, 4>(csr, w, x, h, out, s);
+        return launch_lanes<float, 1>(csr, w, x, h, out, s);
+    }
+    if (vec_ok && h % 8 == 0) return launch_lanes<uint16_t, 8>(csr, w, x, h, out, s);
+    return launch_lanes<uint16_t, 1>(csr, w, x, h, out, s);
+}
+
+}  // namespace mp

@@ -1,0 +1,189 @@
+/*
+ * mp.h -- C ABI of the weighted sparse message-passing library (libmp.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (tinymesh, "Weighted aggregation experiment"):
+ *   given COO edges e = 0..E-1 with (src_e, dst_e) in [0, N)^2, one scalar
+ *   weight w_e per edge in COO order, node features X[N, H] and an upstream
+ *   gradient dY[N, H], with A_w[dst_e, src_e] += w_e (duplicates add):
+ *     forward          Y  = A_w   X     destination-owned CSR    ("Decision")
+ *     input gradient   dX = A_w^T dY    source-owned (transpose) CSR
+ *     edge gradient    dw_e = <X[src_e, :], dY[dst_e, :]>, one owner per edge
+ *   No call materialises per-edge [E, H] message rows; the forward and input
+ *   gradient use no atomics; w and dw stay in the caller's COO order
+ *   ("Edge order is explicit").
+ *
+ * Conventions shared by every entry point
+ *   - Memory: every array argument is device memory on the current HIP device,
+ *     allocated and owned by the caller.  The library never allocates device
+ *     memory, never frees caller memory, never keeps a pointer past a call
+ *     except those stored in an mp_graph, and never writes an input.
+ *   - Layout: X, dY, Y, dX are contiguous row-major [N, H]; w and dw are
+ *     contiguous [E] in COO order; graph arrays are contiguous int32.
+ *   - Sizes: 1 <= N < 2^31, 0 <= E < 2^31, 1 <= H < 2^31, N*H < 2^62.
+ *   - Outputs are overwritten completely (never accumulated into); a row with
+ *     no edges is written as exact zeros.
+ *   - Streams: `stream` is a hipStream_t (0 = the null stream).  All device
+ *     work is enqueued on it.  Only mp_graph_build synchronises that stream
+ *     (once, at its end); the three compute calls return without waiting.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued; a rejected call launches nothing and writes nothing.  No C++
+ *     exception crosses this interface.  mp_last_error_detail() returns a
+ *     thread-local text describing the last non-OK status on this thread.
+ *   - Determinism: for a fixed graph, H, feature dtype and device, results
+ *     are bitwise reproducible (fixed reduction order, no atomics).
+ */
+#ifndef MP_H
+#define MP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+typedef int32_t mp_status;
+#define MP_OK             0
+#define MP_ERR_NULL      (-1)   /* a required pointer is NULL                         */
+#define MP_ERR_SHAPE     (-2)   /* a size is out of range                             */
+#define MP_ERR_DTYPE     (-3)   /* unsupported dtype code for this argument           */
+#define MP_ERR_DEVICE    (-4)   /* a pointer is not device memory of the current GPU  */
+#define MP_ERR_INDEX     (-5)   /* an edge endpoint lies outside [0, N)               */
+#define MP_ERR_ALIAS     (-6)   /* an output overlaps an input or the graph           */
+#define MP_ERR_ALIGN     (-7)   /* a pointer is not aligned to its element size       */
+#define MP_ERR_WORKSPACE (-8)   /* workspace missing or smaller than required         */
+#define MP_ERR_GRAPH     (-9)   /* mp_graph not produced by a successful build        */
+#define MP_ERR_HIP      (-10)   /* the HIP runtime reported an error (see detail)     */
+
+/* Element type codes. */
+typedef int32_t mp_dtype;
+#define MP_I32  1
+#define MP_I64  2
+#define MP_F32  3
+#define MP_BF16 4
+
+/* Number of degree classes: class 0 holds rows with no edges, class c >= 1
+ * holds rows whose length has c binary digits (lengths 2^(c-1) .. 2^c - 1). */
+#define MP_NUM_CLASSES 33
+
+/*
+ * mp_graph -- the lowered topology, a plain descriptor in host memory.
+ *
+ * The caller allocates the descriptor and every device array it points to
+ * (sizes below), fills in the pointers, and passes it to mp_graph_build,
+ * which writes every array and the host-side fields.  Afterwards the arrays
+ * are read-only; the graph stays valid as long as the caller keeps them.
+ *
+ *   src, dst           [E]    edge identity in COO order (int32 copies of the
+ *                             caller's endpoints)
+ *   rowptr             [N+1]  forward CSR (rows = destinations)
+ *   col                [E]    col[p] = src[edge_order[p]]
+ *   edge_order         [E]    CSR position -> COO ordinal, ascending ordinal
+ *                             inside a row ("Edge order is explicit")
+ *   rowptr_t           [N+1]  transpose CSR (rows = sources)
+ *   col_t              [E]    col_t[q] = dst[transpose_order[q]]
+ *   transpose_order    [E]    transpose position -> COO ordinal
+ *   row_plan, row_plan_t [N]  rows of each CSR listed by degree class, highest
+ *                             class first, ascending row id within a class
+ *   class_count, class_count_t  host copies of the number of rows per class
+ *
+ * Together the two CSR forms hold 2E + 2(N+1) integers and the edge identity
+ * 4E integers, as tallied in "Edge order is explicit"; the two plans add 2N.
+ */
+typedef struct mp_graph {
+    int64_t num_nodes;
+    int64_t num_edges;
+    int32_t *src;
+    int32_t *dst;
+    int32_t *rowptr;
+    int32_t *col;
+    int32_t *edge_order;
+    int32_t *rowptr_t;
+    int32_t *col_t;
+    int32_t *transpose_order;
+    int32_t *row_plan;
+    int32_t *row_plan_t;
+    int64_t class_count[MP_NUM_CLASSES];
+    int64_t class_count_t[MP_NUM_CLASSES];
+    uint64_t built;     /* set by a successful mp_graph_build; 0 otherwise */
+} mp_graph;
+
+/*
+ * Device workspace (bytes) that mp_graph_build needs for N nodes and E edges.
+ * Returns MP_ERR_SHAPE for sizes out of range, MP_ERR_NULL if `bytes` is NULL.
+ */
+mp_status mp_graph_build_workspace_size(int64_t num_nodes, int64_t num_edges, size_t *bytes);
+
+/*
+ * Lower a COO edge list into the two CSR forms, their order maps and the
+ * degree plans (tinymesh "Weighted aggregation experiment", "Edge order is
+ * explicit": a stable sort by destination gives edge_order, by source gives
+ * transpose_order; the witness of "Exact witness" lowers to edge_order =
+ * (2, 0, 1)).
+ *
+ *   src, dst    device arrays [E] of `idx_dtype` (MP_I32 or MP_I64), COO order;
+ *               e.g. the two rows of a PyTorch edge_index.
+ *   num_nodes   N (explicit; trailing isolated nodes are allowed).
+ *   num_edges   E (0 allowed).
+ *   g           descriptor with every device array pointer set (see mp_graph).
+ *   workspace   device scratch of at least mp_graph_build_workspace_size bytes,
+ *               256-byte aligned; contents on entry are ignored.
+ *   stream      hipStream_t.
+ *
+ * Enqueues the lowering on `stream`, then synchronises it once to read the
+ * class counts and the index check back.  An endpoint outside [0, N) returns
+ * MP_ERR_INDEX and leaves g->built = 0 (the arrays then hold unspecified
+ * values).  On success g->built is set.
+ */
+mp_status mp_graph_build(const void *src, const void *dst, mp_dtype idx_dtype,
+                         int64_t num_nodes, int64_t num_edges, mp_graph *g,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Forward aggregation Y = A_w X ("Decision"; the left column of the diagram
+ * under "Edge order is explicit").
+ *   w      [E] float32, COO order (may be NULL when E = 0).
+ *   x      [N, H] of `x_dtype` (MP_F32 or MP_BF16); products and sums in fp32.
+ *   y      [N, H] float32 output; must not overlap w, x or the graph arrays.
+ * Enqueued on `stream`; does not synchronise.
+ */
+mp_status mp_spmm_fwd(const mp_graph *g, const float *w, const void *x, mp_dtype x_dtype,
+                      int64_t h, float *y, void *stream);
+
+/*
+ * Input gradient dX = A_w^T dY over the transpose CSR ("Decision"; the right
+ * column of the diagram under "Edge order is explicit").
+ *   w      [E] float32, COO order (may be NULL when E = 0).
+ *   dy     [N, H] of `dy_dtype` (MP_F32 or MP_BF16).
+ *   dx     [N, H] float32 output; must not overlap w, dy or the graph arrays.
+ */
+mp_status mp_spmm_dx(const mp_graph *g, const float *w, const void *dy, mp_dtype dy_dtype,
+                     int64_t h, float *dx, void *stream);
+
+/*
+ * Edge-weight gradient dw_e = <X[src_e, :], dY[dst_e, :]> for every edge, in
+ * COO order, one owner per edge ("Decision"; the bottom of the diagram under
+ * "Edge order is explicit").
+ *   x, dy  [N, H] of `dtype` (MP_F32 or MP_BF16), same dtype for both.
+ *   dw     [E] float32 output (may be NULL when E = 0); must not overlap x, dy
+ *          or the graph arrays.
+ */
+mp_status mp_edge_grad_dw(const mp_graph *g, const void *x, const void *dy, mp_dtype dtype,
+                          int64_t h, float *dw, void *stream);
+
+/* Static text for a status code. */
+const char *mp_status_string(mp_status status);
+
+/* Thread-local detail for the last non-OK status returned on this thread. */
+const char *mp_last_error_detail(void);
+
+/* Library version, as major * 10000 + minor * 100 + patch. */
+int32_t mp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MP_H */

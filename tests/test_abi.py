@@ -1,0 +1,156 @@
+"""CPU-only checks of the C ABI (no kernel is launched; nothing here needs a GPU):
+
+* libmp.so loads and exports every function include/mp.h declares;
+* the ctypes mirror of mp_graph matches the C layout (sizeof / offsetof by gcc);
+* host-side validation rejects bad arguments before any HIP call;
+* the forward / input-gradient kernels contain no atomic instruction (scan of
+  the gfx950 assembly built here from spmm.hip);
+* the product package never imports the oracle.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mp.h")
+PKG = os.path.join(ROOT, "gnn_sparse_message_amd")
+
+
+@pytest.fixture(scope="module")
+def mp():
+    import gnn_sparse_message_amd
+    return gnn_sparse_message_amd
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mp_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("mp_graph_build", "mp_graph_build_workspace_size", "mp_spmm_fwd",
+                     "mp_spmm_dx", "mp_edge_grad_dw", "mp_status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(mp):
+    lib = ctypes.CDLL(mp.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", mp.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(mp_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_graph_struct_layout_matches_ctypes(mp, tmp_path):
+    fields = [f for f, _ in mp._MpGraph._fields_]
+    prog = ["#include <stdio.h>", "#include <stddef.h>", '#include "mp.h"', "int main(void) {",
+            'printf("%zu\\n", sizeof(mp_graph));']
+    prog += [f'printf("%zu\\n", offsetof(mp_graph, {f}));' for f in fields]
+    prog += ["return 0; }"]
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(prog))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.dirname(HEADER), str(c), "-o", str(exe)], check=True)
+    vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(mp._MpGraph)
+    for f, off in zip(fields, vals[1:]):
+        assert getattr(mp._MpGraph, f).offset == off, f
+
+
+def test_status_strings(mp):
+    for code in range(0, -11, -1):
+        s = mp.mp_status_string(code)
+        assert s.startswith("MP_OK" if code == 0 else "MP_ERR_"), (code, s)
+    assert "unknown" in mp.mp_status_string(-99)
+
+
+def test_workspace_size_validation(mp):
+    lib = mp._lib
+    out = ctypes.c_size_t(0)
+    assert lib.mp_graph_build_workspace_size(0, 10, ctypes.byref(out)) == mp.MP_ERR_SHAPE
+    assert lib.mp_graph_build_workspace_size(10, -1, ctypes.byref(out)) == mp.MP_ERR_SHAPE
+    assert lib.mp_graph_build_workspace_size(1 << 31, 1, ctypes.byref(out)) == mp.MP_ERR_SHAPE
+    assert lib.mp_graph_build_workspace_size(10, 10, None) == mp.MP_ERR_NULL
+    assert lib.mp_graph_build_workspace_size(2_000_000, 100_000_000, ctypes.byref(out)) == 0
+    assert out.value >= 12 * 100_000_000          # three [E] u32 sort buffers
+    assert out.value < 13 * 100_000_000           # O(N + E): no [E, H] buffer
+
+
+def _fake_graph(mp, n, e, base=0x10000):
+    g = mp._MpGraph()
+    g.num_nodes, g.num_edges = n, e
+    for i, f in enumerate(mp.Graph._ARRAYS):
+        setattr(g, f, base + i * 0x100000)
+    return g
+
+
+def test_build_rejects_before_any_device_call(mp):
+    lib = mp._lib
+    g = _fake_graph(mp, 10, 20)
+    fake_src, fake_dst = 0x9000000, 0xA000000
+    ws_need = mp.mp_graph_build_workspace_size(10, 20)
+    assert lib.mp_graph_build(fake_src, fake_dst, mp.MP_I64, 10, 20, None, 0x100, ws_need, None) \
+        == mp.MP_ERR_NULL
+    assert lib.mp_graph_build(fake_src, fake_dst, 7, 10, 20, ctypes.byref(g), 0x100, ws_need,
+                              None) == mp.MP_ERR_DTYPE
+    assert lib.mp_graph_build(fake_src, fake_dst, mp.MP_I64, 0, 20, ctypes.byref(g), 0x100,
+                              ws_need, None) == mp.MP_ERR_SHAPE
+    assert lib.mp_graph_build(None, fake_dst, mp.MP_I64, 10, 20, ctypes.byref(g), 0x100, ws_need,
+                              None) == mp.MP_ERR_NULL
+    assert lib.mp_graph_build(fake_src, fake_dst, mp.MP_I64, 10, 20, ctypes.byref(g), None,
+                              ws_need, None) == mp.MP_ERR_WORKSPACE
+    assert lib.mp_graph_build(fake_src, fake_dst, mp.MP_I64, 10, 20, ctypes.byref(g), 0x100,
+                              ws_need - 1, None) == mp.MP_ERR_WORKSPACE
+    assert lib.mp_graph_build(fake_src, fake_dst, mp.MP_I64, 10, 20, ctypes.byref(g), 0x104,
+                              ws_need, None) == mp.MP_ERR_ALIGN
+    g.col = None
+    assert lib.mp_graph_build(fake_src, fake_dst, mp.MP_I64, 10, 20, ctypes.byref(g), 0x100,
+                              ws_need, None) == mp.MP_ERR_NULL
+    g.col = 0x20002
+    assert lib.mp_graph_build(fake_src, fake_dst, mp.MP_I64, 10, 20, ctypes.byref(g), 0x100,
+                              ws_need, None) == mp.MP_ERR_ALIGN
+    assert g.built == 0
+    assert "aligned" in lib.mp_last_error_detail().decode()
+
+
+def test_compute_calls_reject_unbuilt_graphs(mp):
+    lib = mp._lib
+    g = _fake_graph(mp, 10, 20)
+    for fn in (lib.mp_spmm_fwd, lib.mp_spmm_dx):
+        assert fn(None, 0x100, 0x200, mp.MP_F32, 4, 0x300, None) == mp.MP_ERR_NULL
+        assert fn(ctypes.byref(g), 0x100, 0x200, mp.MP_F32, 4, 0x300, None) == mp.MP_ERR_GRAPH
+    assert lib.mp_edge_grad_dw(None, 0x100, 0x200, mp.MP_F32, 4, 0x300, None) == mp.MP_ERR_NULL
+    assert lib.mp_edge_grad_dw(ctypes.byref(g), 0x100, 0x200, mp.MP_F32, 4, 0x300, None) \
+        == mp.MP_ERR_GRAPH
+
+
+def test_forward_and_input_grad_kernels_have_no_atomics(tmp_path):
+    """Scan the gfx950 assembly of spmm.hip (built here) for atomic instructions."""
+    asm = tmp_path / "spmm.s"
+    from gnn_sparse_message_amd import _build
+    cmd = [_build.HIPCC, f"--offload-arch={_build.ARCH}", "--cuda-device-only", "-S", "-O3",
+           "-std=c++17", "-I", _build.INCLUDE, "-I", _build.CSRC, "-Xclang", "-target-feature",
+           "-Xclang", "-packed-fp32-ops", os.path.join(_build.CSRC, "spmm.hip"), "-o", str(asm)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    text = asm.read_text()
+    kernels = re.findall(r"^(_Z\w*spmm_kernel\w*):", text, re.M)
+    assert len(kernels) >= 28                       # 2 dtypes x 2 vector widths x 7 lane counts
+    insts = [ln for ln in text.splitlines() if re.match(r"\s+[a-z_0-9]+atomic", ln)]
+    assert not insts, insts[:5]
+    assert "global_load_dwordx4" in text            # 16-byte feature-row loads are emitted
+
+
+def test_product_never_imports_the_oracle():
+    for dirpath, _, files in os.walk(PKG):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "oracle.c" not in text and "liboracle" not in text, f

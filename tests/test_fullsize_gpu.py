@@ -1,0 +1,95 @@
+"""The full-size power-law workload (N = 2,000,000, E = 100,000,000, H = 128,
+bf16 features, fp32 accumulation) through the same entry points and launch
+configuration the benchmark times.  The whole lowering is compared with the
+oracle bit for bit; float outputs are compared on sampled rows and edges that
+the oracle evaluates one by one (hub rows, empty rows, random rows, the last
+row; random edges and every edge of the largest rows)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.harness import TAU, check_close, upload
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def run():
+    import gnn_sparse_message_amd as mp
+    wl = synth.chung_lu()
+    t = upload(wl, DEV, torch.int64)
+    g = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    y = mp.mp_spmm_fwd(g, t["w"], t["x"])
+    dx = mp.mp_spmm_dx(g, t["w"], t["dy"])
+    dw = mp.mp_edge_grad_dw(g, t["x"], t["dy"])
+    torch.cuda.synchronize()
+    out = {"g": {k: v.cpu().numpy() for k, v in g.arrays.items()},
+           "cc": g.class_count, "cc_t": g.class_count_t,
+           "y": y.cpu().numpy(), "dx": dx.cpu().numpy(), "dw": dw.cpu().numpy()}
+    del t, g, y, dx, dw
+    torch.cuda.empty_cache()
+    return wl, out
+
+
+def _sample_rows(deg, rng):
+    order = np.argsort(-deg, kind="stable")
+    rows = [order[:8], rng.choice(deg.shape[0], 48, replace=False),
+            np.nonzero(deg == 0)[0][:4], np.array([deg.shape[0] - 1]),
+            rng.choice(np.nonzero((deg >= 16) & (deg < 4096))[0], 16, replace=False)]
+    return np.unique(np.concatenate(rows)).astype(np.int64)
+
+
+def test_fullsize_lowering_bit_exact(run):
+    wl, out = run
+    for key, other, names in ((wl.dst, wl.src, ("rowptr", "col", "edge_order")),
+                              (wl.src, wl.dst, ("rowptr_t", "col_t", "transpose_order"))):
+        ref = oracle.lower(wl.n, key, other)
+        for name, r in zip(names, ref):
+            assert np.array_equal(out["g"][name], r), name
+    rowptr, _, _ = oracle.lower(wl.n, wl.dst, wl.src)
+    plan, cc = oracle.degree_plan(wl.n, rowptr)
+    assert np.array_equal(out["g"]["row_plan"], plan)
+    assert out["cc"] == cc.tolist()
+
+
+def test_fullsize_forward_sampled(run):
+    wl, out = run
+    rng = np.random.default_rng(1)
+    rows = _sample_rows(np.bincount(wl.dst, minlength=wl.n), rng)
+    ref, s = oracle.forward_rows(wl.n, wl.src, wl.dst, wl.w, wl.x, rows)
+    worst = check_close("Y rows", out["y"][rows], ref, s, TAU["bf16"])
+    # fp32 accumulation: the fp32 bound holds as well on every sampled row
+    check_close("Y rows (fp32 bound)", out["y"][rows], ref, s, TAU["f32"])
+    print("forward max |err|/S", worst)
+
+
+def test_fullsize_input_grad_sampled(run):
+    wl, out = run
+    rng = np.random.default_rng(2)
+    rows = _sample_rows(np.bincount(wl.src, minlength=wl.n), rng)
+    ref, s = oracle.input_grad_rows(wl.n, wl.src, wl.dst, wl.w, wl.dy, rows)
+    check_close("dX rows", out["dx"][rows], ref, s, TAU["bf16"])
+    check_close("dX rows (fp32 bound)", out["dx"][rows], ref, s, TAU["f32"])
+
+
+def test_fullsize_edge_grad_sampled(run):
+    wl, out = run
+    rng = np.random.default_rng(3)
+    hub = int(np.argmax(np.bincount(wl.dst, minlength=wl.n)))
+    edges = np.unique(np.concatenate([rng.choice(wl.e, 20000, replace=False),
+                                      np.nonzero(wl.dst == hub)[0][:5000],
+                                      np.array([0, wl.e - 1])])).astype(np.int64)
+    ref, s = oracle.edge_grad_edges(wl.src, wl.dst, wl.x, wl.dy, edges)
+    check_close("dw edges", out["dw"][edges], ref, s, TAU["bf16"])
+    check_close("dw edges (fp32 bound)", out["dw"][edges], ref, s, TAU["f32"])
+
+
+def test_fullsize_outputs_finite_everywhere(run):
+    wl, out = run
+    assert np.isfinite(out["y"]).all() and np.isfinite(out["dx"]).all()
+    assert np.isfinite(out["dw"]).all()
+    empty = np.bincount(wl.dst, minlength=wl.n) == 0
+    assert np.all(out["y"][empty] == 0)

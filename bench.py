@@ -1,0 +1,218 @@
+"""Benchmark: weighted sparse message passing on one MI355X.
+
+One step = one pass of the whole path over one synthetic input: the device
+lowering (mp_graph_build), the forward aggregation (mp_spmm_fwd), the input
+gradient (mp_spmm_dx) and the edge gradient (mp_edge_grad_dw).  Workload: the
+power-law Chung-Lu graph, N = 2,000,000, E = 100,000,000, degree exponent 2.1,
+per-direction expected degree capped at 100,000, H = 128 bf16 features with
+fp32 accumulation and fp32 outputs; inputs are resident in HBM before timing.
+
+Throughput is effective HBM bandwidth over algorithmic bytes (each edge
+touches its operand rows once):
+    B_fwd   = E (H s + 12) + 4 (N + 1) + 4 N H        s = bytes per feature
+    B_dX    = B_fwd
+    B_dw    = E (2 H s + 12)
+    B_build = E (2 s_idx + 16) + 8 (N + 1)            s_idx = 8 (int64 input)
+value = (B_build + B_fwd + B_dX + B_dw) / step time.  Per-op times come from
+HIP events recorded on the stream the kernels run on.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E peak, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["gnn_sparse_message_amd/csrc/spmm.hip", "gnn_sparse_message_amd/csrc/sddmm.hip",
+                  "gnn_sparse_message_amd/csrc/lower.hip", "gnn_sparse_message_amd/csrc/common.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(n, e, h, s_feat, s_idx):
+    fwd = e * (h * s_feat + 12) + 4 * (n + 1) + 4 * n * h
+    return {"build": e * (2 * s_idx + 16) + 8 * (n + 1), "fwd": fwd, "dx": fwd,
+            "dw": e * (2 * h * s_feat + 12)}
+
+
+def kernel_source_hash():
+    hsh = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            hsh.update(f.read())
+    return hsh.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel_key)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, sample_edges):
+    """The oracle as it stands (single-threaded C, fp64) on the first
+    `sample_edges` COO edges of the same workload, all N nodes, same H."""
+    import oracle
+    n, h = wl.n, wl.h
+    src, dst, w = wl.src[:sample_edges], wl.dst[:sample_edges], wl.w[:sample_edges]
+    oracle._load()
+    t0 = time.perf_counter()
+    oracle.lower(n, dst, src)
+    oracle.lower(n, src, dst)
+    oracle.forward(n, src, dst, w, wl.x)
+    oracle.input_grad(n, src, dst, w, wl.dy)
+    oracle.edge_grad(src, dst, wl.x, wl.dy)
+    dt = time.perf_counter() - t0
+    b = algorithmic_bytes(n, sample_edges, h, 2, 8)
+    return {"value": round(sum(b.values()) / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "edges_per_s": round(sample_edges / dt, 1),
+            "sample": f"first {sample_edges} of the {wl.e} COO edges, all {n} nodes, H={h}; "
+                      "lowering (both directions) + forward + input gradient + edge gradient, "
+                      "single-threaded fp64 C oracle"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-sample-edges", type=int, default=10_000_000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the steps, run one plain 1 GiB -> 1 GiB elementwise copy "
+                         "(reference for the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py: this build runs on exactly one GPU (got --gpus {args.gpus}); "
+              "multi-GPU sharding is described in the design notes, not implemented.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gnn_sparse_message_amd as mp
+    import synth
+
+    t0 = time.perf_counter()
+    wl = synth.chung_lu()
+    log(f"generated N={wl.n} E={wl.e} H={wl.h} ({wl.feat_dtype}) in {time.perf_counter() - t0:.1f}s")
+    dev = torch.device("cuda:0")
+    src = torch.from_numpy(wl.src).to(dev)
+    dst = torch.from_numpy(wl.dst).to(dev)
+    w = torch.from_numpy(wl.w).to(dev)
+    x = torch.from_numpy(wl.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    dy = torch.from_numpy(wl.dy_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    n, e, h = wl.n, wl.e, wl.h
+    y = torch.empty((n, h), dtype=torch.float32, device=dev)
+    dx = torch.empty_like(y)
+    dw = torch.empty(e, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    ops = ("build", "fwd", "dx", "dw")
+    times = {k: [] for k in ops}
+
+    def step(record):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
+        if record:
+            ev[0].record(stream)
+        g = mp.mp_graph_build(src, dst, n)
+        if record:
+            ev[1].record(stream)
+        mp.mp_spmm_fwd(g, w, x, out=y)
+        if record:
+            ev[2].record(stream)
+        mp.mp_spmm_dx(g, w, dy, out=dx)
+        if record:
+            ev[3].record(stream)
+        mp.mp_edge_grad_dw(g, x, dy, out=dw)
+        if record:
+            ev[4].record(stream)
+        return ev
+
+    for i in range(args.warmup):
+        step(False)
+        log(f"warmup step {i + 1}/{args.warmup}")
+    torch.cuda.synchronize()
+    events = []
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        events.append(step(True))
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    for ev in events:
+        for k, name in enumerate(ops):
+            times[name].append(ev[k].elapsed_time(ev[k + 1]))
+    log(f"timed {args.steps} steps in {t_total:.3f}s")
+
+    if args.copy_calibration:
+        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB read, 1 GiB written")
+
+    bytes_ = algorithmic_bytes(n, e, h, 2, 8)
+    ms_step = t_total / args.steps * 1e3
+    per_op = {}
+    for k in ops:
+        med = statistics.median(times[k])
+        gbps = bytes_[k] / (med * 1e-3) / 1e9
+        per_op[k] = {"ms": round(med, 4), "GBps": round(gbps, 1),
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "edges_per_s": round(e / (med * 1e-3), 1),
+                     "algorithmic_bytes": bytes_[k]}
+    dominant = max(("fwd", "dx", "dw"), key=lambda k: per_op[k]["ms"])
+    kernel_key = {"fwd": "spmm_kernel", "dx": "spmm_kernel", "dw": "sddmm_kernel"}[dominant]
+    achieved = per_op[dominant]["GBps"]
+    total_bytes = sum(bytes_.values())
+    value = total_bytes / (ms_step * 1e-3) / 1e9
+    traffic = measured_traffic(f"{kernel_key}:{dominant}")
+    out = {
+        "metric": "SpMM fwd/dX + SDDMM dw effective HBM GB/s and edges/s; % of HBM roofline",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "chung_lu_powerlaw", "num_nodes": n, "num_edges": e,
+                   "feature_width": h, "degree_exponent": 2.1, "degree_cap": 100000,
+                   "feature_storage": "bf16", "index_input": "int64",
+                   "step": "mp_graph_build + mp_spmm_fwd + mp_spmm_dx + mp_edge_grad_dw"},
+        "edges_per_s": round(e / (ms_step * 1e-3), 1),
+        "frac_of_hbm_peak": round(value / PEAK_HBM_GBPS, 4),
+        "per_op": per_op,
+        "roofline": {"bound": "hbm", "kernel": f"{kernel_key} ({dominant})",
+                     "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_sample_edges} edges ...")
+        out["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_sample_edges, e))
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -29,8 +29,8 @@ mp_status hip_fail(hipError_t e, const char *what);
 // ---------------------------------------------------------------- lowering
 // Workspace layout for the lowering (byte offsets from the workspace base).
 struct LowerLayout {
-    size_t k0, k1, v0;        // [E] u32 ping-pong keys, one value buffer
-    size_t hist;              // [256 * max_blocks] u32 per-block digit counts
+    size_t k0, k1, v0, o0;    // [E] u32: ping-pong keys, one ordinal and one endpoint buffer
+    size_t hist;              // [256 * tiles] u32 per-tile digit counts (digit-major)
     size_t dtot;              // [256] u32 digit totals of the current pass
     size_t small;             // [64 + 256 + 256] u32: flag, plan totals fwd, plan totals t
     size_t total;

@@ -16,8 +16,9 @@
 //                digits with 64-lane ballots (stable: rank order = input order),
 //                regroups the tile by digit in LDS and writes it out in runs.
 // Block-local ranks, never atomics, decide where equal keys land, so the
-// result is the unique stable order.  Rows are then delimited by a binary
-// search per row over the sorted keys, and col[p] = other[order[p]].
+// result is the unique stable order.  The opposite endpoint travels with each
+// key, so the last pass writes col[p] = other[order[p]] directly.  Rows are
+// then delimited by a binary search per row over the sorted keys.
 #include "common.h"
 
 namespace mp {
@@ -28,7 +29,6 @@ constexpr int kTile = kBlock * kItems;            // 4096 keys per tile
 constexpr int kWaveChunk = kWave * kItems;        // 1024 keys per wave per tile
 constexpr int kBins = 256;                        // 8-bit digits
 constexpr int kDigitBits = 8;
-constexpr int kMaxBlocks = 1024;                  // sort blocks per pass (bounds the count table)
 constexpr int kSmallFlag = 0;                     // small[0]: index-range flag
 constexpr int kSmallPlanF = 64;                   // small[64..320): digit totals of the forward plan
 constexpr int kSmallPlanT = 64 + kBins;           // small[320..576): digit totals of the transpose plan
@@ -38,15 +38,18 @@ constexpr int kPlanBits = 6;                      // plan keys 32 - class lie in
 static_assert(kBlock == kBins, "scan and downsweep map one thread to one digit");
 
 // ------------------------------------------------------------------ key sources
+// A key source is read at 32-bit offsets from the start of a tile (`at`).
 struct KeysFromArray {
     const uint32_t *k;
-    __device__ __forceinline__ uint32_t operator()(int64_t i) const { return k[i]; }
+    __device__ __forceinline__ KeysFromArray at(int64_t base) const { return {k + base}; }
+    __device__ __forceinline__ uint32_t operator()(int i) const { return k[i]; }
 };
 
 // Plan key of row i: 32 - class(length), so the highest class sorts first.
 struct KeysFromDegree {
     const int32_t *rowptr;
-    __device__ __forceinline__ uint32_t operator()(int64_t i) const {
+    __device__ __forceinline__ KeysFromDegree at(int64_t base) const { return {rowptr + base}; }
+    __device__ __forceinline__ uint32_t operator()(int i) const {
         uint32_t d = (uint32_t)(rowptr[i + 1] - rowptr[i]);
         uint32_t c = d == 0 ? 0u : 32u - (uint32_t)__clz(d);
         return 32u - c;
@@ -117,10 +120,20 @@ __global__ void zero_words_kernel(uint32_t *p, int n) {
 }
 
 // ------------------------------------------------------------------ radix pass kernels
+// Every block sorts exactly one 4096-key tile.  Blocks are handed out round-robin
+// over the 8 XCDs, so the logical tile of a block is chosen to make consecutive
+// tiles run on the same XCD: their output runs for a digit are adjacent in
+// memory and merge in that XCD's L2 instead of being written as partial lines
+// from several L2s.
+__device__ __forceinline__ int64_t xcd_local_tile() {
+    const int64_t g = gridDim.x, b = blockIdx.x;
+    const int64_t q = g >> 3, r = g & 7, x = b & 7;
+    return x * q + (x < r ? x : r) + (b >> 3);
+}
+
 template <class KeySrc>
 __global__ __launch_bounds__(kBlock) void rs_upsweep(KeySrc keys, int64_t count, int shift,
-                                                     int bits, int64_t tiles_per_block,
-                                                     int64_t ntiles, int nblocks,
+                                                     int bits, int64_t ntiles,
                                                      uint32_t *__restrict__ hist) {
     __shared__ uint32_t s_cnt[kWavesPerBlock][kBins];
     const int lane = threadIdx.x & (kWave - 1);
@@ -128,65 +141,79 @@ __global__ __launch_bounds__(kBlock) void rs_upsweep(KeySrc keys, int64_t count,
     for (int i = threadIdx.x; i < kWavesPerBlock * kBins; i += kBlock) (&s_cnt[0][0])[i] = 0u;
     __syncthreads();
     const uint32_t mask = (1u << bits) - 1u;
-    const int64_t t0 = (int64_t)blockIdx.x * tiles_per_block;
-    const int64_t t1 = t0 + tiles_per_block < ntiles ? t0 + tiles_per_block : ntiles;
-    for (int64_t t = t0; t < t1; ++t) {
-        const int64_t base = t * kTile + (int64_t)wv * kWaveChunk + lane;
-        uint32_t k[kItems];
+    const int64_t t = xcd_local_tile();
+    const int64_t left = count - t * kTile;
+    const int lim = left < kTile ? (int)left : kTile;        // keys in this tile
+    const KeySrc tk = keys.at(t * kTile);
+    const int li0 = wv * kWaveChunk + lane;                   // tile-local index, round 0
+    uint32_t k[kItems];
 #pragma unroll
-        for (int r = 0; r < kItems; ++r) {
-            const int64_t i = base + (int64_t)r * kWave;
-            k[r] = i < count ? keys(i) : 0u;
-        }
+    for (int r = 0; r < kItems; ++r) {
+        const int li = li0 + r * kWave;
+        k[r] = li < lim ? tk(li) : 0u;
+    }
 #pragma unroll
-        for (int r = 0; r < kItems; ++r) {
-            const bool valid = base + (int64_t)r * kWave < count;
-            const uint32_t d = (k[r] >> shift) & mask;
-            const uint64_t m = match_digit(d, valid, bits);
-            // One leader per distinct digit updates this wave's private counter.
-            if (valid && __builtin_ctzll(m) == lane) s_cnt[wv][d] += (uint32_t)__popcll(m);
-        }
+    for (int r = 0; r < kItems; ++r) {
+        const bool valid = li0 + r * kWave < lim;
+        const uint32_t d = (k[r] >> shift) & mask;
+        const uint64_t m = match_digit(d, valid, bits);
+        // One leader per distinct digit updates this wave's private counter.
+        if (valid && __builtin_ctzll(m) == lane) s_cnt[wv][d] += (uint32_t)__popcll(m);
     }
     __syncthreads();
     const int d = threadIdx.x;
     uint32_t c = 0;
 #pragma unroll
     for (int w = 0; w < kWavesPerBlock; ++w) c += s_cnt[w][d];
-    hist[(int64_t)d * nblocks + blockIdx.x] = c;
+    hist[(int64_t)d * ntiles + t] = c;
 }
 
-// One block per digit: exclusive scan of that digit's per-block counts (in place),
-// and the digit's total.
-__global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist, int nblocks,
+// One block per digit: exclusive scan, in tile order, of that digit's per-tile
+// counts (in place), and the digit's total.
+__global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist, int64_t ntiles,
                                                   uint32_t *__restrict__ dtot) {
-    constexpr int kPer = kMaxBlocks / kBlock;
-    uint32_t *row = hist + (int64_t)blockIdx.x * nblocks;
-    const int beg = threadIdx.x * kPer;
-    uint32_t v[kPer];
-    uint32_t sum = 0;
+    constexpr int kPer = 16;
+    uint32_t *row = hist + (int64_t)blockIdx.x * ntiles;
+    uint32_t carry = 0;
+    for (int64_t chunk = 0; chunk < ntiles; chunk += (int64_t)kBlock * kPer) {
+        const int64_t beg = chunk + (int64_t)threadIdx.x * kPer;
+        uint32_t v[kPer];
+        uint32_t sum = 0;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        v[j] = beg + j < nblocks ? row[beg + j] : 0u;
-        sum += v[j];
-    }
-    uint32_t total;
-    uint32_t run = block_exclusive_scan(sum, &total);
+        for (int j = 0; j < kPer; ++j) {
+            v[j] = beg + j < ntiles ? row[beg + j] : 0u;
+            sum += v[j];
+        }
+        uint32_t total;
+        uint32_t run = carry + block_exclusive_scan(sum, &total);
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        if (beg + j < nblocks) row[beg + j] = run;
-        run += v[j];
+        for (int j = 0; j < kPer; ++j) {
+            if (beg + j < ntiles) row[beg + j] = run;
+            run += v[j];
+        }
+        carry += total;
     }
-    if (threadIdx.x == 0) dtot[blockIdx.x] = total;
+    if (threadIdx.x == 0) dtot[blockIdx.x] = carry;
 }
 
-template <class KeySrc, bool kIotaVals, bool kWriteKeys>
-__global__ __launch_bounds__(kBlock) void rs_downsweep(
-    KeySrc keys, const uint32_t *__restrict__ vals_in, int64_t count, int shift, int bits,
-    int64_t tiles_per_block, int64_t ntiles, int nblocks, const uint32_t *__restrict__ hist,
-    const uint32_t *__restrict__ dtot, uint32_t *__restrict__ keys_out,
-    uint32_t *__restrict__ vals_out) {
-    __shared__ uint32_t s_key[kTile];
-    __shared__ uint32_t s_val[kTile];
+// Payload arrays carried by a pass.  vals are COO ordinals (generated on the
+// first pass), other is the opposite endpoint (so the final pass writes the
+// column array directly, with no gather).
+struct Payload {
+    const uint32_t *vals_in;
+    const uint32_t *other_in;
+    uint32_t *keys_out;
+    uint32_t *vals_out;
+    uint32_t *other_out;
+};
+
+template <class KeySrc, bool kIotaVals, bool kOther, bool kWriteKeys>
+__global__ __launch_bounds__(kBlock) void rs_downsweep(KeySrc keys, Payload pl, int64_t count,
+                                                       int shift, int bits, int64_t ntiles,
+                                                       const uint32_t *__restrict__ hist,
+                                                       const uint32_t *__restrict__ dtot) {
+    __shared__ uint32_t s_buf[kTile];          // one payload at a time, in tile-sorted order
+    __shared__ uint8_t s_dig[kTile];           // digit of each tile-sorted position
     __shared__ uint32_t s_cnt[kWavesPerBlock][kBins];
     __shared__ uint32_t s_tstart[kBins];
     __shared__ uint32_t s_gbase[kBins];
@@ -195,73 +222,97 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(
     const int wv = tid / kWave;
     const uint32_t mask = (1u << bits) - 1u;
     const uint64_t lanes_below = (1ull << lane) - 1ull;
+    const int64_t t = xcd_local_tile();
+    const int64_t tbase = t * kTile;
+    const int64_t left = count - tbase;
+    const int lim = left < kTile ? (int)left : kTile;        // keys in this tile
+    const KeySrc tk = keys.at(tbase);
+    const int li0 = wv * kWaveChunk + lane;                   // tile-local index, round 0
 
-    {   // where this block's run of each digit starts in the output
-        uint32_t tot;
-        const uint32_t dbase = block_exclusive_scan(dtot[tid], &tot);
-        s_gbase[tid] = dbase + hist[(int64_t)tid * nblocks + blockIdx.x];
+    for (int i = tid; i < kWavesPerBlock * kBins; i += kBlock) (&s_cnt[0][0])[i] = 0u;
+    uint32_t k[kItems];
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {
+        const int li = li0 + r * kWave;
+        k[r] = li < lim ? tk(li) : 0u;
     }
-    const int64_t t0 = (int64_t)blockIdx.x * tiles_per_block;
-    const int64_t t1 = t0 + tiles_per_block < ntiles ? t0 + tiles_per_block : ntiles;
-    for (int64_t t = t0; t < t1; ++t) {
-        for (int i = tid; i < kWavesPerBlock * kBins; i += kBlock) (&s_cnt[0][0])[i] = 0u;
+    __syncthreads();
+    // Rank inside the wave: earlier rounds (running count) + lower lanes now.
+    uint32_t pos[kItems];
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {
+        const bool valid = li0 + r * kWave < lim;
+        const uint32_t d = (k[r] >> shift) & mask;
+        const uint64_t m = match_digit(d, valid, bits);
+        const uint32_t before = s_cnt[wv][d];
+        pos[r] = before + (uint32_t)__popcll(m & lanes_below);
+        if (valid && __builtin_ctzll(m) == lane) s_cnt[wv][d] = before + (uint32_t)__popcll(m);
+    }
+    __syncthreads();
+    // Thread `tid` owns digit `tid`: per-wave starts, the tile's digit starts and
+    // the global start of this tile's run of the digit.
+    const uint32_t c0 = s_cnt[0][tid], c1 = s_cnt[1][tid], c2 = s_cnt[2][tid], c3 = s_cnt[3][tid];
+    uint32_t all;
+    const uint32_t tstart = block_exclusive_scan(c0 + c1 + c2 + c3, &all);   // barriers inside
+    const uint32_t dbase = block_exclusive_scan(dtot[tid], &all);
+    s_cnt[0][tid] = tstart;
+    s_cnt[1][tid] = tstart + c0;
+    s_cnt[2][tid] = tstart + c0 + c1;
+    s_cnt[3][tid] = tstart + c0 + c1 + c2;
+    s_tstart[tid] = tstart;
+    s_gbase[tid] = dbase + hist[(int64_t)tid * ntiles + t];
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {
+        const uint32_t d = (k[r] >> shift) & mask;
+        pos[r] += s_cnt[wv][d];          // tile-local sorted position
+        if (li0 + r * kWave < lim) s_dig[pos[r]] = (uint8_t)d;
+    }
+    __syncthreads();
+    uint32_t gp[kItems];                  // output position of tile-sorted slot tid + j * kBlock
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+        const int i = tid + j * kBlock;
+        gp[j] = 0xffffffffu;
+        if (i < lim) {
+            const uint32_t d = s_dig[i];
+            gp[j] = s_gbase[d] + ((uint32_t)i - s_tstart[d]);
+        }
+    }
+    // Regroup each payload through LDS, then write it out in digit runs.  The
+    // ordinal and endpoint payloads are read only now, which keeps few
+    // registers live across the ranking (more resident blocks per CU).
+    auto emit = [&](const uint32_t(&src)[kItems], uint32_t *__restrict__ out) {
+#pragma unroll
+        for (int r = 0; r < kItems; ++r)
+            if (li0 + r * kWave < lim) s_buf[pos[r]] = src[r];
         __syncthreads();
-        const int64_t base = t * kTile + (int64_t)wv * kWaveChunk + lane;
-        uint32_t k[kItems], v[kItems], rk[kItems];
+#pragma unroll
+        for (int j = 0; j < kItems; ++j)
+            if ((int64_t)gp[j] < count) out[gp[j]] = s_buf[tid + j * kBlock];
+        __syncthreads();
+    };
+    if (kWriteKeys) emit(k, pl.keys_out);
+    {
+        uint32_t v[kItems];
+        const uint32_t *vin = kIotaVals ? nullptr : pl.vals_in + tbase;
 #pragma unroll
         for (int r = 0; r < kItems; ++r) {
-            const int64_t i = base + (int64_t)r * kWave;
-            const bool valid = i < count;
-            k[r] = valid ? keys(i) : 0u;
-            if (kIotaVals) v[r] = (uint32_t)i;
-            else v[r] = valid ? vals_in[i] : 0u;
+            const int li = li0 + r * kWave;
+            if (kIotaVals) v[r] = (uint32_t)tbase + (uint32_t)li;
+            else v[r] = li < lim ? vin[li] : 0u;
         }
-        // Rank inside the wave: earlier rounds (running count) + lower lanes now.
+        emit(v, pl.vals_out);
+    }
+    if (kOther) {
+        uint32_t o[kItems];
+        const uint32_t *oin = pl.other_in + tbase;
 #pragma unroll
         for (int r = 0; r < kItems; ++r) {
-            const bool valid = base + (int64_t)r * kWave < count;
-            const uint32_t d = (k[r] >> shift) & mask;
-            const uint64_t m = match_digit(d, valid, bits);
-            const uint32_t before = s_cnt[wv][d];
-            rk[r] = before + (uint32_t)__popcll(m & lanes_below);
-            if (valid && __builtin_ctzll(m) == lane) s_cnt[wv][d] = before + (uint32_t)__popcll(m);
+            const int li = li0 + r * kWave;
+            o[r] = li < lim ? oin[li] : 0u;
         }
-        __syncthreads();
-        // Thread `tid` owns digit `tid`: per-wave offsets and the tile's digit starts.
-        const uint32_t c0 = s_cnt[0][tid], c1 = s_cnt[1][tid], c2 = s_cnt[2][tid],
-                       c3 = s_cnt[3][tid];
-        const uint32_t ttot = c0 + c1 + c2 + c3;
-        uint32_t all;
-        const uint32_t tstart = block_exclusive_scan(ttot, &all);   // barriers inside
-        s_cnt[0][tid] = tstart;
-        s_cnt[1][tid] = tstart + c0;
-        s_cnt[2][tid] = tstart + c0 + c1;
-        s_cnt[3][tid] = tstart + c0 + c1 + c2;
-        s_tstart[tid] = tstart;
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < kItems; ++r) {
-            if (base + (int64_t)r * kWave < count) {
-                const uint32_t d = (k[r] >> shift) & mask;
-                const uint32_t pos = s_cnt[wv][d] + rk[r];
-                s_key[pos] = k[r];
-                s_val[pos] = v[r];
-            }
-        }
-        __syncthreads();
-        const int64_t left = count - t * kTile;
-        const int tile_n = left < kTile ? (int)left : kTile;
-        for (int i = tid; i < tile_n; i += kBlock) {
-            const uint32_t kk = s_key[i];
-            const uint32_t d = (kk >> shift) & mask;
-            const uint32_t g = s_gbase[d] + ((uint32_t)i - s_tstart[d]);
-            if ((int64_t)g < count) {   // always true for a consistent count table
-                if (kWriteKeys) keys_out[g] = kk;
-                vals_out[g] = s_val[i];
-            }
-        }
-        __syncthreads();
-        s_gbase[tid] += ttot;
+        emit(o, pl.other_out);
     }
 }
 
@@ -282,31 +333,8 @@ __global__ __launch_bounds__(kBlock) void rowptr_kernel(const uint32_t *__restri
     }
 }
 
-__global__ __launch_bounds__(kBlock) void gather_kernel(const int32_t *__restrict__ order,
-                                                        const int32_t *__restrict__ other,
-                                                        int64_t e, int32_t *__restrict__ out) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < e; i += stride) {
-        const uint32_t o = (uint32_t)order[i];
-        out[i] = (int64_t)o < e ? other[o] : 0;   // order is a permutation of [0, e)
-    }
-}
-
 // ------------------------------------------------------------------ host side
-struct Part {
-    int64_t ntiles;
-    int64_t tpb;
-    int nblocks;
-};
-
-Part partition(int64_t count) {
-    Part p;
-    p.ntiles = count > 0 ? (count + kTile - 1) / kTile : 1;
-    int64_t nb = p.ntiles < kMaxBlocks ? p.ntiles : kMaxBlocks;
-    p.tpb = (p.ntiles + nb - 1) / nb;
-    p.nblocks = (int)((p.ntiles + p.tpb - 1) / p.tpb);
-    return p;
-}
+int64_t tiles_for(int64_t count) { return count > 0 ? (count + kTile - 1) / kTile : 1; }
 
 unsigned grid_for(int64_t items, int64_t cap = 65536) {
     int64_t b = (items + kBlock - 1) / kBlock;
@@ -320,79 +348,79 @@ int key_bits(int64_t n) {
     return bits > 0 ? bits : 1;   // one pass even for n = 1 (a stable copy)
 }
 
-template <class KeySrc>
-mp_status radix_pass(KeySrc keys, const uint32_t *vals_in, bool iota_vals, bool write_keys,
-                     int64_t count, int shift, int bits, uint32_t *hist, uint32_t *dtot,
-                     uint32_t *keys_out, uint32_t *vals_out, hipStream_t s) {
-    const Part p = partition(count);
-    rs_upsweep<KeySrc><<<p.nblocks, kBlock, 0, s>>>(keys, count, shift, bits, p.tpb, p.ntiles,
-                                                    p.nblocks, hist);
-    rs_scan<<<kBins, kBlock, 0, s>>>(hist, p.nblocks, dtot);
-    if (iota_vals && write_keys)
-        rs_downsweep<KeySrc, true, true><<<p.nblocks, kBlock, 0, s>>>(
-            keys, vals_in, count, shift, bits, p.tpb, p.ntiles, p.nblocks, hist, dtot, keys_out,
-            vals_out);
-    else if (iota_vals)
-        rs_downsweep<KeySrc, true, false><<<p.nblocks, kBlock, 0, s>>>(
-            keys, vals_in, count, shift, bits, p.tpb, p.ntiles, p.nblocks, hist, dtot, keys_out,
-            vals_out);
-    else if (write_keys)
-        rs_downsweep<KeySrc, false, true><<<p.nblocks, kBlock, 0, s>>>(
-            keys, vals_in, count, shift, bits, p.tpb, p.ntiles, p.nblocks, hist, dtot, keys_out,
-            vals_out);
-    else
-        rs_downsweep<KeySrc, false, false><<<p.nblocks, kBlock, 0, s>>>(
-            keys, vals_in, count, shift, bits, p.tpb, p.ntiles, p.nblocks, hist, dtot, keys_out,
-            vals_out);
+template <class KeySrc, bool kIota, bool kOther, bool kWriteKeys>
+mp_status radix_pass(KeySrc keys, const Payload &pl, int64_t count, int shift, int bits,
+                     uint32_t *hist, uint32_t *dtot, hipStream_t s) {
+    const int64_t ntiles = tiles_for(count);
+    rs_upsweep<KeySrc><<<(unsigned)ntiles, kBlock, 0, s>>>(keys, count, shift, bits, ntiles, hist);
+    rs_scan<<<kBins, kBlock, 0, s>>>(hist, ntiles, dtot);
+    rs_downsweep<KeySrc, kIota, kOther, kWriteKeys><<<(unsigned)ntiles, kBlock, 0, s>>>(
+        keys, pl, count, shift, bits, ntiles, hist, dtot);
     MP_HIP_CHECK(hipGetLastError(), "radix pass launch");
     return MP_OK;
 }
 
-// Stable sort of the ordinals 0..e-1 by key[0..e); final ordinals land in
-// `order`, final keys in *sorted (one of k0 / k1).
-mp_status sort_edges(const int32_t *key, int64_t e, int64_t n, uint32_t *k0, uint32_t *k1,
-                     uint32_t *v0, uint32_t *hist, uint32_t *dtot, int32_t *order,
-                     const uint32_t **sorted, hipStream_t s) {
+// Stable sort of the edges by key[0..e): the final pass writes the sorted keys
+// to one of k0 / k1 (*sorted), the ordinals to `order` and other[order[p]] to `col`.
+mp_status sort_edges(const int32_t *key, const int32_t *other, int64_t e, int64_t n,
+                     uint32_t *k0, uint32_t *k1, uint32_t *v0, uint32_t *o0, uint32_t *hist,
+                     uint32_t *dtot, int32_t *order, int32_t *col, const uint32_t **sorted,
+                     hipStream_t s) {
     const int bits = key_bits(n);
     const int passes = (bits + kDigitBits - 1) / kDigitBits;
     const uint32_t *kin = reinterpret_cast<const uint32_t *>(key);
-    const uint32_t *vin = nullptr;
+    Payload pl;
+    pl.vals_in = nullptr;
+    pl.other_in = reinterpret_cast<const uint32_t *>(other);
     uint32_t *kbuf[2] = {k0, k1};
     for (int pass = 0; pass < passes; ++pass) {
         const int shift = pass * kDigitBits;
         const int pb = bits - shift < kDigitBits ? bits - shift : kDigitBits;
-        // Values alternate between `order` and v0 so that the last pass lands in `order`.
-        uint32_t *vout = ((passes - 1 - pass) % 2 == 0) ? reinterpret_cast<uint32_t *>(order) : v0;
-        uint32_t *kout = kbuf[pass % 2];
-        mp_status st = radix_pass(KeysFromArray{kin}, vin, pass == 0, true, e, shift, pb, hist,
-                                  dtot, kout, vout, s);
+        // Payloads alternate between the outputs and v0 / o0 so that the last
+        // pass lands in `order` and `col`.
+        const bool to_out = (passes - 1 - pass) % 2 == 0;
+        pl.keys_out = kbuf[pass % 2];
+        pl.vals_out = to_out ? reinterpret_cast<uint32_t *>(order) : v0;
+        pl.other_out = to_out ? reinterpret_cast<uint32_t *>(col) : o0;
+        mp_status st = pass == 0
+            ? radix_pass<KeysFromArray, true, true, true>(KeysFromArray{kin}, pl, e, shift, pb,
+                                                           hist, dtot, s)
+            : radix_pass<KeysFromArray, false, true, true>(KeysFromArray{kin}, pl, e, shift, pb,
+                                                            hist, dtot, s);
         if (st != MP_OK) return st;
-        kin = kout;
-        vin = vout;
+        kin = pl.keys_out;
+        pl.vals_in = pl.vals_out;
+        pl.other_in = pl.other_out;
     }
     *sorted = kin;
     return MP_OK;
 }
 
 mp_status lower_direction(const int32_t *key, const int32_t *other, int64_t e, int64_t n,
-                          uint32_t *k0, uint32_t *k1, uint32_t *v0, uint32_t *hist,
+                          uint32_t *k0, uint32_t *k1, uint32_t *v0, uint32_t *o0, uint32_t *hist,
                           uint32_t *dtot, int32_t *rowptr, int32_t *col, int32_t *order,
                           hipStream_t s) {
     const uint32_t *sorted = k0;
     if (e > 0) {
-        mp_status st = sort_edges(key, e, n, k0, k1, v0, hist, dtot, order, &sorted, s);
+        mp_status st = sort_edges(key, other, e, n, k0, k1, v0, o0, hist, dtot, order, col,
+                                  &sorted, s);
         if (st != MP_OK) return st;
     }
     rowptr_kernel<<<grid_for(n + 1), kBlock, 0, s>>>(sorted, e, n, rowptr);
-    if (e > 0) gather_kernel<<<grid_for(e), kBlock, 0, s>>>(order, other, e, col);
-    MP_HIP_CHECK(hipGetLastError(), "row/column launch");
+    MP_HIP_CHECK(hipGetLastError(), "row pointer launch");
     return MP_OK;
 }
 
 mp_status plan_direction(const int32_t *rowptr, int64_t n, uint32_t *hist, uint32_t *totals,
                          int32_t *plan, hipStream_t s) {
-    return radix_pass(KeysFromDegree{rowptr}, nullptr, true, false, n, 0, kPlanBits, hist,
-                      totals, nullptr, reinterpret_cast<uint32_t *>(plan), s);
+    Payload pl;
+    pl.vals_in = nullptr;
+    pl.other_in = nullptr;
+    pl.keys_out = nullptr;
+    pl.vals_out = reinterpret_cast<uint32_t *>(plan);
+    pl.other_out = nullptr;
+    return radix_pass<KeysFromDegree, true, false, false>(KeysFromDegree{rowptr}, pl, n, 0,
+                                                          kPlanBits, hist, totals, s);
 }
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -400,14 +428,15 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
 LowerLayout lower_layout(int64_t n, int64_t e) {
-    (void)n;
     LowerLayout L;
     size_t off = 0;
     const size_t ebytes = align_up((size_t)(e > 0 ? e : 1) * sizeof(uint32_t));
+    const int64_t most = e > n ? e : n;
     L.k0 = off; off += ebytes;
     L.k1 = off; off += ebytes;
     L.v0 = off; off += ebytes;
-    L.hist = off; off += align_up((size_t)kBins * kMaxBlocks * sizeof(uint32_t));
+    L.o0 = off; off += ebytes;
+    L.hist = off; off += align_up((size_t)kBins * tiles_for(most) * sizeof(uint32_t));
     L.dtot = off; off += align_up(kBins * sizeof(uint32_t));
     L.small = off; off += align_up(kSmallWords * sizeof(uint32_t));
     L.total = off;
@@ -421,6 +450,7 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
     uint32_t *k0 = reinterpret_cast<uint32_t *>(base + L.k0);
     uint32_t *k1 = reinterpret_cast<uint32_t *>(base + L.k1);
     uint32_t *v0 = reinterpret_cast<uint32_t *>(base + L.v0);
+    uint32_t *o0 = reinterpret_cast<uint32_t *>(base + L.o0);
     uint32_t *hist = reinterpret_cast<uint32_t *>(base + L.hist);
     uint32_t *dtot = reinterpret_cast<uint32_t *>(base + L.dtot);
     uint32_t *small = reinterpret_cast<uint32_t *>(base + L.small);
@@ -438,10 +468,10 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
     }
     MP_HIP_CHECK(hipGetLastError(), "intake launch");
 
-    mp_status st = lower_direction(g->dst, g->src, e, n, k0, k1, v0, hist, dtot, g->rowptr,
+    mp_status st = lower_direction(g->dst, g->src, e, n, k0, k1, v0, o0, hist, dtot, g->rowptr,
                                    g->col, g->edge_order, s);
     if (st != MP_OK) return st;
-    st = lower_direction(g->src, g->dst, e, n, k0, k1, v0, hist, dtot, g->rowptr_t, g->col_t,
+    st = lower_direction(g->src, g->dst, e, n, k0, k1, v0, o0, hist, dtot, g->rowptr_t, g->col_t,
                          g->transpose_order, s);
     if (st != MP_OK) return st;
     st = plan_direction(g->rowptr, n, hist, small + kSmallPlanF, g->row_plan, s);

@@ -79,8 +79,8 @@ def test_workspace_size_validation(mp):
     assert lib.mp_graph_build_workspace_size(1 << 31, 1, ctypes.byref(out)) == mp.MP_ERR_SHAPE
     assert lib.mp_graph_build_workspace_size(10, 10, None) == mp.MP_ERR_NULL
     assert lib.mp_graph_build_workspace_size(2_000_000, 100_000_000, ctypes.byref(out)) == 0
-    assert out.value >= 12 * 100_000_000          # three [E] u32 sort buffers
-    assert out.value < 13 * 100_000_000           # O(N + E): no [E, H] buffer
+    assert out.value >= 16 * 100_000_000          # four [E] u32 sort buffers
+    assert out.value < 17 * 100_000_000           # O(N + E): no [E, H] buffer
 
 
 def _fake_graph(mp, n, e, base=0x10000):

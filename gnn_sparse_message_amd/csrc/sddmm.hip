@@ -75,9 +75,9 @@ __global__ __launch_bounds__(kBlock) void sddmm_kernel(const int32_t *__restrict
          base < e; base += nwaves * kWave) {
         const int64_t me = base + lane;
         int s = 0, d = 0;
-        if (me < e) {
-            s = src[me];
-            d = dst[me];
+        if (me < e) {   // streamed once: non-temporal, so L2 keeps the feature rows
+            s = __builtin_nontemporal_load(&src[me]);
+            d = __builtin_nontemporal_load(&dst[me]);
         }
         const int n = e - base < kWave ? (int)(e - base) : kWave;
         const int trips = (n + G - 1) / G;
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kBlock) void sddmm_kernel(const int32_t *__restrict
                 if (lane / G == j + u) mine = got;
             }
         }
-        if (me < e) dw[me] = mine;
+        if (me < e) __builtin_nontemporal_store(mine, &dw[me]);
     }
 }
 

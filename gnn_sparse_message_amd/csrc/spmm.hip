@@ -65,15 +65,21 @@ struct Feat<uint16_t, 1> {
     }
 };
 
+// Output rows are written once and not read again here: non-temporal stores
+// keep them from displacing hot feature rows in L2.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 template <int VEC>
 __device__ __forceinline__ void store_row(float *p, const float (&v)[VEC]) {
     if constexpr (VEC % 4 == 0) {
 #pragma unroll
-        for (int i = 0; i < VEC; i += 4)
-            *reinterpret_cast<float4 *>(p + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+        for (int i = 0; i < VEC; i += 4) {
+            const f32x4 q = {v[i], v[i + 1], v[i + 2], v[i + 3]};
+            __builtin_nontemporal_store(q, reinterpret_cast<f32x4 *>(p + i));
+        }
     } else {
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) p[i] = v[i];
+        for (int i = 0; i < VEC; ++i) __builtin_nontemporal_store(v[i], p + i);
     }
 }
 
@@ -110,24 +116,24 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
         const int64_t p = base + tl;
         int c = 0;
         float wt = 0.f;
-        if (p < end) {
-            c = a.col[p];
-            const uint32_t o = (uint32_t)a.order[p];
-            wt = a.w[(int64_t)o < a.e ? o : 0u];   // order is a permutation of [0, e)
+        if (p < end) {   // streamed once: non-temporal, so L2 keeps the feature rows
+            c = __builtin_nontemporal_load(&a.col[p]);
+            const uint32_t o = (uint32_t)__builtin_nontemporal_load(&a.order[p]);
+            wt = __builtin_nontemporal_load(&a.w[(int64_t)o < a.e ? o : 0u]);   // o < e always
         }
         const int n = end - base < TL ? (int)(end - base) : TL;
         const int trips = (n + G - 1) / G;
         for (int j = 0; j < trips; j += kUnroll) {
-            int cu[kUnroll];
-            float wu[kUnroll];
+            // Column indices first, so the feature-row loads are in flight
+            // before the weights (a dependent gather) are waited for.
+            int cu[kUnroll], slu[kUnroll];
             bool ok[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int k = g + (j + u) * G;
                 ok[u] = (j + u < trips) && k < n;
-                const int sl = tb + (k < n ? k : n - 1);
-                cu[u] = __shfl(c, sl);
-                wu[u] = __shfl(wt, sl);
+                slu[u] = tb + (k < n ? k : n - 1);
+                cu[u] = __shfl(c, slu[u]);
             }
             float xv[kUnroll][VEC];
 #pragma unroll
@@ -141,7 +147,8 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                const float wv = ok[u] ? wu[u] : 0.f;
+                const float wu = __shfl(wt, slu[u]);
+                const float wv = ok[u] ? wu : 0.f;
 #pragma unroll
                 for (int v = 0; v < VEC; ++v) acc[v] = fmaf(wv, xv[u][v], acc[v]);
             }

@@ -28,7 +28,7 @@ constexpr int kItems = 16;                        // keys per thread per tile
 constexpr int kTile = kBlock * kItems;            // 4096 keys per tile
 constexpr int kWaveChunk = kWave * kItems;        // 1024 keys per wave per tile
 constexpr int kBins = 256;                        // 8-bit digits
-constexpr int kDigitBits = 8;
+constexpr int kDigitBits = 8;                     // at most 8 bits per pass
 constexpr int kSmallFlag = 0;                     // small[0]: index-range flag
 constexpr int kSmallPlanF = 64;                   // small[64..320): digit totals of the forward plan
 constexpr int kSmallPlanT = 64 + kBins;           // small[320..576): digit totals of the transpose plan
@@ -374,8 +374,11 @@ mp_status sort_edges(const int32_t *key, const int32_t *other, int64_t e, int64_
     pl.other_in = reinterpret_cast<const uint32_t *>(other);
     uint32_t *kbuf[2] = {k0, k1};
     for (int pass = 0; pass < passes; ++pass) {
-        const int shift = pass * kDigitBits;
-        const int pb = bits - shift < kDigitBits ? bits - shift : kDigitBits;
+        // Split the key bits evenly over the passes (21 bits -> 7 + 7 + 7): fewer
+        // bins per pass than 8 + 8 + 5 gives longer output runs per tile.
+        const int per = (bits + passes - 1) / passes;
+        const int shift = pass * per;
+        const int pb = bits - shift < per ? bits - shift : per;
         // Payloads alternate between the outputs and v0 / o0 so that the last
         // pass lands in `order` and `col`.
         const bool to_out = (passes - 1 - pass) % 2 == 0;

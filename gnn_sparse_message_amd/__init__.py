@@ -10,6 +10,7 @@ turns status codes into exceptions.
     Y  = mp_spmm_fwd(g, w, X)                      # Y  = A_w X      (A_w[dst, src] += w)
     dX = mp_spmm_dx(g, w, dY)                      # dX = A_w^T dY
     dw = mp_edge_grad_dw(g, X, dY)                 # dw_e = <X[src_e], dY[dst_e]>, COO order
+    dX, dw = mp_spmm_dx_edge_grad(g, w, X, dY)     # both gradients in one pass
 
 (tinymesh "Weighted aggregation experiment": "Decision", "Edge order is
 explicit".)  The library must be built (``python -m gnn_sparse_message_amd._build``
@@ -24,7 +25,7 @@ import torch  # noqa: F401  -- loaded first so libmp.so binds to torch's HIP run
 
 __all__ = [
     "Graph", "MpError", "mp_graph_build", "mp_graph_build_workspace_size", "mp_spmm_fwd",
-    "mp_spmm_dx", "mp_edge_grad_dw", "mp_status_string", "mp_version", "library_path",
+    "mp_spmm_dx", "mp_edge_grad_dw", "mp_spmm_dx_edge_grad", "mp_status_string", "mp_version", "library_path",
     "NUM_CLASSES",
 ]
 
@@ -94,6 +95,7 @@ def _load():
         "mp_spmm_fwd": (i32, [gp, vp, vp, i32, i64, vp, vp]),
         "mp_spmm_dx": (i32, [gp, vp, vp, i32, i64, vp, vp]),
         "mp_edge_grad_dw": (i32, [gp, vp, vp, i32, i64, vp, vp]),
+        "mp_spmm_dx_edge_grad": (i32, [gp, vp, vp, vp, i32, i64, vp, vp, vp]),
         "mp_status_string": (ctypes.c_char_p, [i32]),
         "mp_last_error_detail": (ctypes.c_char_p, []),
         "mp_version": (i32, []),
@@ -282,3 +284,20 @@ def mp_edge_grad_dw(g: Graph, x, dy, out=None):
                                 _ptr(dw) if g.num_edges else None, _stream(x)),
            "mp_edge_grad_dw")
     return dw
+
+
+def mp_spmm_dx_edge_grad(g: Graph, w, x, dy, out_dx=None, out_dw=None):
+    """(dX, dw) in one pass over the transpose CSR; equal to mp_spmm_dx and
+    mp_edge_grad_dw."""
+    _weights(w, g)
+    h = _features("x", x, g)
+    if _features("dy", dy, g) != h:
+        raise ValueError("x and dy must have the same feature width")
+    code = _code(dy) if x.dtype == dy.dtype else 0
+    dx = _out(out_dx, (g.num_nodes, h), dy)
+    dw = _out(out_dw, (g.num_edges,), dy)
+    _check(_lib.mp_spmm_dx_edge_grad(ctypes.byref(g._desc), _ptr(w) if g.num_edges else None,
+                                     _ptr(x), _ptr(dy), code, h, _ptr(dx),
+                                     _ptr(dw) if g.num_edges else None, _stream(dy)),
+           "mp_spmm_dx_edge_grad")
+    return dx, dw

@@ -269,6 +269,41 @@ mp_status mp_edge_grad_dw(const mp_graph *g, const void *x, const void *dy, mp_d
     return sddmm_run(g->src, g->dst, e, x, dy, dtype, h, dw, static_cast<hipStream_t>(stream));
 }
 
+mp_status mp_spmm_dx_edge_grad(const mp_graph *g, const float *w, const void *x,
+                               const void *dy, mp_dtype dtype, int64_t h, float *dx, float *dw,
+                               void *stream) {
+    mp_status st = check_spmm(g, w, dy, dtype, h, dx, "dy", "dx");
+    if (st != MP_OK) return st;
+    const int64_t n = g->num_nodes, e = g->num_edges;
+    if (!x) return fail(MP_ERR_NULL, "x is NULL");
+    if (!dw && e > 0) return fail(MP_ERR_NULL, "dw is NULL with %lld edges", (long long)e);
+    const size_t xs = dtype_size(dtype);
+    if (!aligned(x, xs)) return fail(MP_ERR_ALIGN, "x not aligned to %zu bytes", xs);
+    if (dw && !aligned(dw, 4)) return fail(MP_ERR_ALIGN, "dw not aligned to 4 bytes");
+    if ((st = check_device(x, "x")) != MP_OK) return st;
+    if (e > 0 && (st = check_device(dw, "dw")) != MP_OK) return st;
+    const Range rdx = range(dx, n * h, 4, "dx"), rdw = range(dw, e, 4, "dw");
+    const Range rx = range(x, n * h, xs, "x");
+    if (overlap(rdx, rx)) return fail(MP_ERR_ALIAS, "dx overlaps x");
+    Range others[13];
+    int k = graph_ranges(g, others);
+    others[k++] = rx;
+    others[k++] = range(dy, n * h, xs, "dy");
+    others[k++] = range(w, e, 4, "w");
+    others[k++] = rdx;
+    for (int i = 0; i < k; ++i)
+        if (overlap(rdw, others[i])) return fail(MP_ERR_ALIAS, "dw overlaps %s", others[i].name);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    CsrView v{g->rowptr_t, g->col_t, g->transpose_order, g->row_plan_t, g->class_count_t,
+              g->num_nodes, g->num_edges};
+    if (spmm_fused_supported(dtype, h, dy, x, dx))
+        return spmm_fused_run(v, w, dy, dtype, h, dx, x, e > 0 ? dw : nullptr, s);
+    // Feature rows wider than one column block: the two kernels back to back.
+    if ((st = spmm_run(v, w, dy, dtype, h, dx, s)) != MP_OK) return st;
+    if (e == 0) return MP_OK;
+    return sddmm_run(g->src, g->dst, e, x, dy, dtype, h, dw, s);
+}
+
 const char *mp_status_string(mp_status s) {
     switch (s) {
         case MP_OK: return "MP_OK";

@@ -56,6 +56,13 @@ struct CsrView {
 };
 mp_status spmm_run(const CsrView &csr, const float *w, const void *x, mp_dtype dt, int64_t h,
                    float *out, hipStream_t stream);
+// The same aggregation over the transpose CSR that also writes, for every edge
+// q of owner row j, dw[order[q]] = <x_own[j, :], x[col[q], :]> (fused backward).
+// Only for feature rows that fit one column block (spmm_fused_supported).
+bool spmm_fused_supported(mp_dtype dt, int64_t h, const void *x, const void *x_own,
+                          const void *out);
+mp_status spmm_fused_run(const CsrView &csr, const float *w, const void *x, mp_dtype dt,
+                         int64_t h, float *out, const void *x_own, float *dw, hipStream_t stream);
 
 // ---------------------------------------------------------------- SDDMM
 mp_status sddmm_run(const int32_t *src, const int32_t *dst, int64_t e, const void *x,

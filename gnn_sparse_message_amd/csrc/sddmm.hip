@@ -25,7 +25,7 @@ struct Feat2<float, 4> {
     static __device__ __forceinline__ float dot(const float *a, const float *b) {
         const float4 p = *reinterpret_cast<const float4 *>(a);
         const float4 q = *reinterpret_cast<const float4 *>(b);
-        float s = p.x * q.x;
+        float s = fmaf(p.x, q.x, 0.f);
         s = fmaf(p.y, q.y, s);
         s = fmaf(p.z, q.z, s);
         return fmaf(p.w, q.w, s);
@@ -33,7 +33,9 @@ struct Feat2<float, 4> {
 };
 template <>
 struct Feat2<float, 1> {
-    static __device__ __forceinline__ float dot(const float *a, const float *b) { return *a * *b; }
+    static __device__ __forceinline__ float dot(const float *a, const float *b) {
+        return fmaf(*a, *b, 0.f);
+    }
 };
 template <>
 struct Feat2<uint16_t, 8> {
@@ -54,7 +56,7 @@ struct Feat2<uint16_t, 8> {
 template <>
 struct Feat2<uint16_t, 1> {
     static __device__ __forceinline__ float dot(const uint16_t *a, const uint16_t *b) {
-        return __uint_as_float((uint32_t)(*a) << 16) * __uint_as_float((uint32_t)(*b) << 16);
+        return fmaf(__uint_as_float((uint32_t)(*a) << 16), __uint_as_float((uint32_t)(*b) << 16), 0.f);
     }
 };
 
@@ -91,13 +93,17 @@ __global__ __launch_bounds__(kBlock) void sddmm_kernel(const int32_t *__restrict
                 const int sl = k < n ? k : n - 1;
                 const int su = __shfl(s, sl);
                 const int du = __shfl(d, sl);
+                // Lane-local dot: an fma chain from zero per chunk (no bare product
+                // that could be contracted into the lane reduction below).
                 float acc = 0.f;
                 if (ok) {
                     for (int64_t f = 0; f < nf; ++f) {
                         const int64_t hoff = (f * L + sub) * VEC;
-                        if (hoff < h)
-                            acc += Feat2<T, VEC>::dot(X + (int64_t)su * h + hoff,
-                                                      dY + (int64_t)du * h + hoff);
+                        if (hoff < h) {
+                            const float d = Feat2<T, VEC>::dot(X + (int64_t)su * h + hoff,
+                                                               dY + (int64_t)du * h + hoff);
+                            acc = f == 0 ? d : acc + d;
+                        }
                     }
                 }
                 part[u] = acc;

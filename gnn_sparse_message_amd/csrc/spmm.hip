@@ -83,14 +83,28 @@ __device__ __forceinline__ void store_row(float *p, const float (&v)[VEC]) {
     }
 }
 
+// Lane-local part of <xr, xv>: an fma chain from zero in element order, the
+// same operations as the COO-order edge-gradient kernel (so both give equal dw).
+// No bare product is left, so nothing can be contracted into the lane
+// reduction that follows.
+template <typename T, int VEC>
+__device__ __forceinline__ float edge_dot(const float (&xr)[VEC], const float (&xv)[VEC]) {
+    float s = 0.f;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) s = fmaf(xr[v], xv[v], s);
+    return s;
+}
+
 struct SpmmArgs {
     const int32_t *rowptr;
     const int32_t *col;
     const int32_t *order;
     const int32_t *plan;
     const float *w;
-    const void *x;
+    const void *x;                    // gathered rows (X forward, dY input gradient)
     float *y;
+    const void *x_own;                // fused backward only: X, read at the owner row
+    float *dw;                        // fused backward only: edge gradients, COO order
     int64_t h;
     int64_t n, e;                     // rows, edges (bounds for the data-dependent indices)
     int32_t n_hub, n_wave, n_group;   // rows of each owner kind, consecutive in the plan
@@ -103,10 +117,14 @@ struct SpmmArgs {
 // row in runs of TL edges: run starts are `first`, `first + stride`, ...  All
 // lanes of the team execute every permute with the same trip count, so each
 // permute reads from an active lane.
-template <typename T, int VEC, int L, int TL>
+// With kEdgeGrad (the fused backward over the transpose CSR, rows = sources)
+// every gathered dY slice also meets the owner row's X slice `xr`: the group
+// reduces their dot product over its L lanes (same lane order and butterfly as
+// the COO-order edge-gradient kernel) and one lane writes dw[order[p]].
+template <typename T, int VEC, int L, int TL, bool kEdgeGrad>
 __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int64_t end,
                                            int64_t stride, int lane, int64_t hoff, bool active,
-                                           float (&acc)[VEC]) {
+                                           const float (&xr)[VEC], float (&acc)[VEC]) {
     constexpr int G = TL / L;                 // groups per team
     const int tl = lane % TL;
     const int tb = lane - tl;                 // first lane of the team
@@ -115,11 +133,13 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
     for (int64_t base = first; base < end; base += stride) {
         const int64_t p = base + tl;
         int c = 0;
+        uint32_t o = 0;
         float wt = 0.f;
         if (p < end) {   // streamed once: non-temporal, so L2 keeps the feature rows
             c = __builtin_nontemporal_load(&a.col[p]);
-            const uint32_t o = (uint32_t)__builtin_nontemporal_load(&a.order[p]);
-            wt = __builtin_nontemporal_load(&a.w[(int64_t)o < a.e ? o : 0u]);   // o < e always
+            o = (uint32_t)__builtin_nontemporal_load(&a.order[p]);
+            if ((int64_t)o >= a.e) o = 0u;   // never taken: order is a permutation of [0, e)
+            wt = __builtin_nontemporal_load(&a.w[o]);
         }
         const int n = end - base < TL ? (int)(end - base) : TL;
         const int trips = (n + G - 1) / G;
@@ -152,18 +172,39 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
 #pragma unroll
                 for (int v = 0; v < VEC; ++v) acc[v] = fmaf(wv, xv[u][v], acc[v]);
             }
+            if constexpr (kEdgeGrad) {
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    float part = edge_dot<T, VEC>(xr, xv[u]);
+#pragma unroll
+                    for (int off = L / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+                    const uint32_t ou = (uint32_t)__shfl((int)o, slu[u]);
+                    if (ok[u] && (lane % L) == 0) a.dw[ou] = part;
+                }
+            }
         }
     }
 }
 
-template <typename T, int VEC, int L>
+// The owner row's slice of X (fused backward only).
+template <typename T, int VEC, bool kEdgeGrad>
+__device__ __forceinline__ void own_row(const SpmmArgs &a, int row, int64_t hoff, bool active,
+                                        float (&xr)[VEC]) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) xr[v] = 0.f;
+    if constexpr (kEdgeGrad) {
+        if (active) Feat<T, VEC>::load(static_cast<const T *>(a.x_own) + (int64_t)row * a.h + hoff, xr);
+    }
+}
+
+template <typename T, int VEC, int L, bool kEdgeGrad>
 __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
     const int sub = lane % L;
     const int64_t hoff = (int64_t)blockIdx.y * (L * VEC) + (int64_t)sub * VEC;
     const bool active = hoff < a.h;
-    float acc[VEC];
+    float acc[VEC], xr[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
 
@@ -174,8 +215,9 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
         const int row = a.plan[b];
         if ((uint32_t)row >= (uint64_t)a.n) return;   // the plan is a permutation of [0, n)
         const int64_t beg = a.rowptr[row], end = a.rowptr[row + 1];
-        accumulate<T, VEC, L, kWave>(a, beg + (int64_t)wv * kWave, end,
-                                     (int64_t)kBlock, lane, hoff, active, acc);
+        own_row<T, VEC, kEdgeGrad>(a, row, hoff, active, xr);
+        accumulate<T, VEC, L, kWave, kEdgeGrad>(a, beg + (int64_t)wv * kWave, end,
+                                                (int64_t)kBlock, lane, hoff, active, xr, acc);
 #pragma unroll
         for (int off = L; off < kWave; off <<= 1)
 #pragma unroll
@@ -208,7 +250,9 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
             const int64_t beg = a.rowptr[row], end = a.rowptr[row + 1];
 #pragma unroll
             for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
-            accumulate<T, VEC, L, kWave>(a, beg, end, (int64_t)kWave, lane, hoff, active, acc);
+            own_row<T, VEC, kEdgeGrad>(a, row, hoff, active, xr);
+            accumulate<T, VEC, L, kWave, kEdgeGrad>(a, beg, end, (int64_t)kWave, lane, hoff,
+                                                    active, xr, acc);
 #pragma unroll
             for (int off = L; off < kWave; off <<= 1)
 #pragma unroll
@@ -227,7 +271,8 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
         const int64_t beg = a.rowptr[row], end = a.rowptr[row + 1];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
-        accumulate<T, VEC, L, L>(a, beg, end, (int64_t)L, lane, hoff, active, acc);
+        own_row<T, VEC, kEdgeGrad>(a, row, hoff, active && end > beg, xr);
+        accumulate<T, VEC, L, L, kEdgeGrad>(a, beg, end, (int64_t)L, lane, hoff, active, xr, acc);
         if (active) store_row<VEC>(a.y + (int64_t)row * a.h + hoff, acc);
     }
 }
@@ -263,7 +308,7 @@ int64_t rows_at_least(const int64_t *cc, int64_t len) {
 
 template <typename T, int VEC, int L>
 mp_status launch(const CsrView &csr, const float *w, const void *x, int64_t h, float *out,
-                 hipStream_t s) {
+                 const void *x_own, float *dw, hipStream_t s) {
     const Thresholds th = thresholds_for(L);
     SpmmArgs a;
     a.rowptr = csr.rowptr;
@@ -273,6 +318,8 @@ mp_status launch(const CsrView &csr, const float *w, const void *x, int64_t h, f
     a.w = w;
     a.x = x;
     a.y = out;
+    a.x_own = x_own;
+    a.dw = dw;
     a.h = h;
     a.n = csr.n;
     a.e = csr.e;
@@ -296,7 +343,12 @@ mp_status launch(const CsrView &csr, const float *w, const void *x, int64_t h, f
     if (gx > (int64_t)3 << 22 || gy > 65535)
         return fail(MP_ERR_SHAPE, "launch grid too large (%lld x %lld)", (long long)gx,
                     (long long)gy);
-    spmm_kernel<T, VEC, L><<<dim3((unsigned)gx, (unsigned)gy), kBlock, 0, s>>>(a);
+    if (dw) {   // fused backward: one column block holds the whole feature row
+        if (gy != 1) return fail(MP_ERR_SHAPE, "fused backward needs H <= %d", L * VEC);
+        spmm_kernel<T, VEC, L, true><<<dim3((unsigned)gx, 1), kBlock, 0, s>>>(a);
+    } else {
+        spmm_kernel<T, VEC, L, false><<<dim3((unsigned)gx, (unsigned)gy), kBlock, 0, s>>>(a);
+    }
     MP_HIP_CHECK(hipGetLastError(), "spmm launch");
     return MP_OK;
 }
@@ -310,15 +362,15 @@ int lanes_for(int64_t h, int vec) {
 
 template <typename T, int VEC>
 mp_status launch_lanes(const CsrView &csr, const float *w, const void *x, int64_t h, float *out,
-                       hipStream_t s) {
+                       const void *x_own, float *dw, hipStream_t s) {
     switch (lanes_for(h, VEC)) {
-        case 1: return launch<T, VEC, 1>(csr, w, x, h, out, s);
-        case 2: return launch<T, VEC, 2>(csr, w, x, h, out, s);
-        case 4: return launch<T, VEC, 4>(csr, w, x, h, out, s);
-        case 8: return launch<T, VEC, 8>(csr, w, x, h, out, s);
-        case 16: return launch<T, VEC, 16>(csr, w, x, h, out, s);
-        case 32: return launch<T, VEC, 32>(csr, w, x, h, out, s);
-        default: return launch<T, VEC, 64>(csr, w, x, h, out, s);
+        case 1: return launch<T, VEC, 1>(csr, w, x, h, out, x_own, dw, s);
+        case 2: return launch<T, VEC, 2>(csr, w, x, h, out, x_own, dw, s);
+        case 4: return launch<T, VEC, 4>(csr, w, x, h, out, x_own, dw, s);
+        case 8: return launch<T, VEC, 8>(csr, w, x, h, out, x_own, dw, s);
+        case 16: return launch<T, VEC, 16>(csr, w, x, h, out, x_own, dw, s);
+        case 32: return launch<T, VEC, 32>(csr, w, x, h, out, x_own, dw, s);
+        default: return launch<T, VEC, 64>(csr, w, x, h, out, x_own, dw, s);
     }
 }
 
@@ -328,13 +380,25 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 mp_status spmm_run(const CsrView &csr, const float *w, const void *x, mp_dtype dt, int64_t h,
                    float *out, hipStream_t s) {
-    const bool vec_ok = aligned16(x) && aligned16(out);
+    return spmm_fused_run(csr, w, x, dt, h, out, nullptr, nullptr, s);
+}
+
+bool spmm_fused_supported(mp_dtype dt, int64_t h, const void *x, const void *x_own,
+                          const void *out) {
+    const int vec = dt == MP_F32 ? 4 : 8;
+    const bool vec_ok = aligned16(x) && aligned16(out) && aligned16(x_own) && h % vec == 0;
+    return h <= (int64_t)kWave * (vec_ok ? vec : 1);
+}
+
+mp_status spmm_fused_run(const CsrView &csr, const float *w, const void *x, mp_dtype dt,
+                         int64_t h, float *out, const void *x_own, float *dw, hipStream_t s) {
+    const bool vec_ok = aligned16(x) && aligned16(out) && (!x_own || aligned16(x_own));
     if (dt == MP_F32) {
-        if (vec_ok && h % 4 == 0) return launch_lanes<float, 4>(csr, w, x, h, out, s);
-        return launch_lanes<float, 1>(csr, w, x, h, out, s);
+        if (vec_ok && h % 4 == 0) return launch_lanes<float, 4>(csr, w, x, h, out, x_own, dw, s);
+        return launch_lanes<float, 1>(csr, w, x, h, out, x_own, dw, s);
     }
-    if (vec_ok && h % 8 == 0) return launch_lanes<uint16_t, 8>(csr, w, x, h, out, s);
-    return launch_lanes<uint16_t, 1>(csr, w, x, h, out, s);
+    if (vec_ok && h % 8 == 0) return launch_lanes<uint16_t, 8>(csr, w, x, h, out, x_own, dw, s);
+    return launch_lanes<uint16_t, 1>(csr, w, x, h, out, x_own, dw, s);
 }
 
 }  // namespace mp

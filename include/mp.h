@@ -173,6 +173,23 @@ mp_status mp_spmm_dx(const mp_graph *g, const float *w, const void *dy, mp_dtype
 mp_status mp_edge_grad_dw(const mp_graph *g, const void *x, const void *dy, mp_dtype dtype,
                           int64_t h, float *dw, void *stream);
 
+/*
+ * Both first-order gradients in one pass ("Decision": dX = A_w^T dY and
+ * dw_e = <X[src_e, :], dY[dst_e, :]>).  The transpose CSR groups edges by
+ * source, so the owner of row j holds X[j, :] while it gathers dY[dst, :] for
+ * each of its edges; that one gathered row feeds both the dX accumulation and
+ * the edge's dot product.  Results are exactly those of mp_spmm_dx followed by
+ * mp_edge_grad_dw (bitwise, for H <= 64 x the 16-byte vector width, i.e. 256
+ * fp32 or 512 bf16 features with 16-byte aligned arrays; wider or unaligned
+ * rows run the two separate kernels).
+ *   w      [E] float32, COO order (may be NULL when E = 0).
+ *   x, dy  [N, H] of `dtype` (MP_F32 or MP_BF16).
+ *   dx     [N, H] float32 output;  dw  [E] float32 output, COO order.
+ *   Outputs must not overlap each other, the inputs or the graph arrays.
+ */
+mp_status mp_spmm_dx_edge_grad(const mp_graph *g, const float *w, const void *x, const void *dy,
+                               mp_dtype dtype, int64_t h, float *dx, float *dw, void *stream);
+
 /* Static text for a status code. */
 const char *mp_status_string(mp_status status);
 

@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for required in ("mp_graph_build", "mp_graph_build_workspace_size", "mp_spmm_fwd",
-                     "mp_spmm_dx", "mp_edge_grad_dw", "mp_status_string"):
+                     "mp_spmm_dx", "mp_edge_grad_dw", "mp_spmm_dx_edge_grad", "mp_status_string"):
         assert required in names
 
 
@@ -129,6 +129,10 @@ def test_compute_calls_reject_unbuilt_graphs(mp):
     assert lib.mp_edge_grad_dw(None, 0x100, 0x200, mp.MP_F32, 4, 0x300, None) == mp.MP_ERR_NULL
     assert lib.mp_edge_grad_dw(ctypes.byref(g), 0x100, 0x200, mp.MP_F32, 4, 0x300, None) \
         == mp.MP_ERR_GRAPH
+    fused = lib.mp_spmm_dx_edge_grad
+    assert fused(None, 0x100, 0x200, 0x300, mp.MP_F32, 4, 0x400, 0x500, None) == mp.MP_ERR_NULL
+    assert fused(ctypes.byref(g), 0x100, 0x200, 0x300, mp.MP_F32, 4, 0x400, 0x500, None) \
+        == mp.MP_ERR_GRAPH
 
 
 def test_forward_and_input_grad_kernels_have_no_atomics(tmp_path):
@@ -141,7 +145,7 @@ def test_forward_and_input_grad_kernels_have_no_atomics(tmp_path):
     subprocess.run(cmd, check=True, capture_output=True)
     text = asm.read_text()
     kernels = re.findall(r"^(_Z\w*spmm_kernel\w*):", text, re.M)
-    assert len(kernels) >= 28                       # 2 dtypes x 2 vector widths x 7 lane counts
+    assert len(kernels) >= 56                       # 2 dtypes x 2 widths x 7 lane counts x fused
     insts = [ln for ln in text.splitlines() if re.match(r"\s+[a-z_0-9]+atomic", ln)]
     assert not insts, insts[:5]
     assert "global_load_dwordx4" in text            # 16-byte feature-row loads are emitted

@@ -196,3 +196,53 @@ def test_rejections(mp):
     torch.cuda.synchronize()
     ry, sy = oracle.forward(wl.n, wl.src, wl.dst, wl.w, wl.x)
     check_close("Y", y, ry, sy, TAU["f32"])
+
+
+@pytest.mark.parametrize("feat,h", [("f32", 1), ("f32", 3), ("f32", 16), ("f32", 64), ("f32", 256),
+                                    ("f32", 260), ("bf16", 8), ("bf16", 128), ("bf16", 512),
+                                    ("bf16", 520)])
+def test_fused_backward_matches_separate_calls(mp, feat, h):
+    """mp_spmm_dx_edge_grad: dX and dw equal the separate entry points bit for bit
+    and the oracle to tolerance, on a graph with all owner kinds."""
+    wl = _power_law_small(90 + h, n=4000, e=80000, h=h, feat=feat)
+    t = upload(wl, DEV)
+    g = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    dx_sep = mp.mp_spmm_dx(g, t["w"], t["dy"])
+    dw_sep = mp.mp_edge_grad_dw(g, t["x"], t["dy"])
+    dx, dw = mp.mp_spmm_dx_edge_grad(g, t["w"], t["x"], t["dy"])
+    torch.cuda.synchronize()
+    assert torch.equal(dx, dx_sep)
+    assert torch.equal(dw, dw_sep)
+    rdx, sdx = oracle.input_grad(wl.n, wl.src, wl.dst, wl.w, wl.dy)
+    rdw, sdw = oracle.edge_grad(wl.src, wl.dst, wl.x, wl.dy)
+    check_close("dX", dx, rdx, sdx, TAU[feat])
+    check_close("dw", dw, rdw, sdw, TAU[feat])
+
+
+def test_fused_backward_witness_and_empty(mp):
+    wl = synth.witness()
+    t = upload(wl, DEV)
+    g = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    dx, dw = mp.mp_spmm_dx_edge_grad(g, t["w"], t["x"], t["dy"])
+    assert dx[:, 0].cpu().tolist() == [29.0, -7.0, 0.0]
+    assert dw.cpu().tolist() == [14.0, 28.0, 10.0]
+    wl = synth.random_graph(7, 0, 16, 3)
+    t = upload(wl, DEV)
+    g = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    dx, dw = mp.mp_spmm_dx_edge_grad(g, t["w"], t["x"], t["dy"])
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dx) == 0 and dw.numel() == 0
+
+
+def test_fused_backward_rejections(mp):
+    wl = synth.random_graph(100, 500, 8, 82)
+    t = upload(wl, DEV)
+    g = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    dx = torch.empty((wl.n, 8), device=DEV)
+    with pytest.raises(ValueError):                      # dw aliases dx
+        mp.mp_spmm_dx_edge_grad(g, t["w"], t["x"], t["dy"], out_dx=dx,
+                                out_dw=dx.view(-1)[:wl.e])
+    with pytest.raises(ValueError):                      # dx aliases x
+        mp.mp_spmm_dx_edge_grad(g, t["w"], t["x"], t["dy"], out_dx=t["x"])
+    with pytest.raises(TypeError):                       # x and dy dtypes differ
+        mp.mp_spmm_dx_edge_grad(g, t["w"], t["x"].bfloat16(), t["dy"])

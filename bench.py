@@ -1,8 +1,10 @@
 """Benchmark: weighted sparse message passing on one MI355X.
 
 One step = one pass of the whole path over one synthetic input: the device
-lowering (mp_graph_build), the forward aggregation (mp_spmm_fwd), the input
-gradient (mp_spmm_dx) and the edge gradient (mp_edge_grad_dw).  Workload: the
+lowering (mp_graph_build), the forward aggregation (mp_spmm_fwd), and both
+gradients (mp_spmm_dx_edge_grad: the input gradient and the edge-weight
+gradient in one pass over the transpose CSR, bitwise equal to mp_spmm_dx and
+mp_edge_grad_dw, which are timed on their own after the steps).  Workload: the
 power-law Chung-Lu graph, N = 2,000,000, E = 100,000,000, degree exponent 2.1,
 per-direction expected degree capped at 100,000, H = 128 bf16 features with
 fp32 accumulation and fp32 outputs; inputs are resident in HBM before timing.
@@ -131,11 +133,11 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
 
-    ops = ("build", "fwd", "dx", "dw")
+    ops = ("build", "fwd", "bwd")
     times = {k: [] for k in ops}
 
     def step(record):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
         if record:
             ev[0].record(stream)
         g = mp.mp_graph_build(src, dst, n)
@@ -144,13 +146,10 @@ def main():
         mp.mp_spmm_fwd(g, w, x, out=y)
         if record:
             ev[2].record(stream)
-        mp.mp_spmm_dx(g, w, dy, out=dx)
+        mp.mp_spmm_dx_edge_grad(g, w, x, dy, out_dx=dx, out_dw=dw)
         if record:
             ev[3].record(stream)
-        mp.mp_edge_grad_dw(g, x, dy, out=dw)
-        if record:
-            ev[4].record(stream)
-        return ev
+        return ev, g
 
     for i in range(args.warmup):
         step(False)
@@ -159,13 +158,35 @@ def main():
     events = []
     t_start = time.perf_counter()
     for i in range(args.steps):
-        events.append(step(True))
+        events.append(step(True)[0])
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
     for ev in events:
         for k, name in enumerate(ops):
             times[name].append(ev[k].elapsed_time(ev[k + 1]))
     log(f"timed {args.steps} steps in {t_total:.3f}s")
+
+    # The separate gradient entry points, outside the timed steps.
+    g = mp.mp_graph_build(src, dst, n)
+    dx_alone = torch.empty_like(dx)
+    dw_alone = torch.empty_like(dw)
+    standalone = {}
+    for name, fn in (("dx", lambda: mp.mp_spmm_dx(g, w, dy, out=dx_alone)),
+                     ("dw", lambda: mp.mp_edge_grad_dw(g, x, dy, out=dw_alone))):
+        fn()
+        ts = []
+        for _ in range(5):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        standalone[name] = statistics.median(ts)
+    same = bool(torch.equal(dx_alone, dx) and torch.equal(dw_alone, dw))
+    log(f"standalone dx {standalone['dx']:.3f} ms, dw {standalone['dw']:.3f} ms, "
+        f"equal to the fused results: {same}")
 
     if args.copy_calibration:
         a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -175,34 +196,37 @@ def main():
         log("copy calibration: 1 GiB read, 1 GiB written")
 
     bytes_ = algorithmic_bytes(n, e, h, 2, 8)
+    bytes_["bwd"] = bytes_["dx"] + bytes_["dw"]
     ms_step = t_total / args.steps * 1e3
-    per_op = {}
-    for k in ops:
-        med = statistics.median(times[k])
-        gbps = bytes_[k] / (med * 1e-3) / 1e9
-        per_op[k] = {"ms": round(med, 4), "GBps": round(gbps, 1),
-                     "frac": round(gbps / PEAK_HBM_GBPS, 4),
-                     "edges_per_s": round(e / (med * 1e-3), 1),
-                     "algorithmic_bytes": bytes_[k]}
-    # Kernels of the compute ops: spmm_kernel runs twice per step (forward and
-    # input gradient), sddmm_kernel once.  The dominant kernel is the one with
-    # the most GPU time per step; its achieved bandwidth is algorithmic bytes
-    # per launch over its average launch duration.
-    kernels = {"spmm_kernel": ("fwd", "dx"), "sddmm_kernel": ("dw",)}
+
+    def rate(nbytes, ms):
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        return {"ms": round(ms, 4), "GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                "edges_per_s": round(e / (ms * 1e-3), 1), "algorithmic_bytes": nbytes}
+
+    per_op = {k: rate(bytes_[k], statistics.median(times[k])) for k in ops}
+    per_op_standalone = {k: rate(bytes_[k], v) for k, v in standalone.items()}
+    per_op_standalone["equal_to_fused"] = same
+    # Kernels of the compute ops.  The dominant kernel is the one with the most
+    # GPU time per step; its achieved bandwidth is the algorithmic bytes of the
+    # units one launch processes over its average launch duration (the fused
+    # backward processes both the dX and the dw units).  `traffic` is the
+    # calibrated HBM counter bytes of one launch.
+    kernels = {"spmm_kernel_fused_backward": ("bwd", "spmm_kernel:bwd"),
+               "spmm_kernel": ("fwd", "spmm_kernel:fwd")}
     roof = {}
-    for kname, kops in kernels.items():
-        launch_ms = statistics.mean(per_op[k]["ms"] for k in kops)
-        launch_bytes = statistics.mean(bytes_[k] for k in kops)
-        achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
-        traffic = [measured_traffic(f"{kname}:{k}") for k in kops]
-        roof[kname] = {"bound": "hbm", "kernel": f"{kname} ({', '.join(kops)})",
+    for kname, (op, tkey) in kernels.items():
+        launch_ms = per_op[op]["ms"]
+        achieved = bytes_[op] / (launch_ms * 1e-3) / 1e9
+        traffic = measured_traffic(tkey)
+        roof[kname] = {"bound": "hbm", "kernel": f"{kname} ({op})",
                        "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                       "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                       "traffic": None if None in traffic else round(statistics.mean(traffic)),
-                       "algorithmic_bytes_per_launch": launch_bytes,
-                       "avg_launch_ms": round(launch_ms, 4), "ms_per_step": round(launch_ms * len(kops), 4)}
-    dominant = max(roof, key=lambda k: roof[k]["ms_per_step"])
-    total_bytes = sum(bytes_.values())
+                       "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                       "traffic_GBps": None if traffic is None
+                       else round(traffic / (launch_ms * 1e-3) / 1e9, 1),
+                       "algorithmic_bytes_per_launch": bytes_[op], "avg_launch_ms": launch_ms}
+    dominant = max(roof, key=lambda k: roof[k]["avg_launch_ms"])
+    total_bytes = bytes_["build"] + bytes_["fwd"] + bytes_["dx"] + bytes_["dw"]
     value = total_bytes / (ms_step * 1e-3) / 1e9
     out = {
         "metric": "SpMM fwd/dX + SDDMM dw effective HBM GB/s and edges/s; % of HBM roofline",
@@ -212,10 +236,11 @@ def main():
         "config": {"workload": "chung_lu_powerlaw", "num_nodes": n, "num_edges": e,
                    "feature_width": h, "degree_exponent": 2.1, "degree_cap": 100000,
                    "feature_storage": "bf16", "index_input": "int64",
-                   "step": "mp_graph_build + mp_spmm_fwd + mp_spmm_dx + mp_edge_grad_dw"},
+                   "step": "mp_graph_build + mp_spmm_fwd + mp_spmm_dx_edge_grad"},
         "edges_per_s": round(e / (ms_step * 1e-3), 1),
         "frac_of_hbm_peak": round(value / PEAK_HBM_GBPS, 4),
         "per_op": per_op,
+        "per_op_standalone": per_op_standalone,
         "roofline": roof[dominant],
         "roofline_other_kernels": {k: v for k, v in roof.items() if k != dominant},
     }

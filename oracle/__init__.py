@@ -48,6 +48,8 @@ def _bind(lib):
         "oracle_input_grad_rows": (ctypes.c_int, [i64, i64, i64, vp, vp, vp, vp, i64, vp, vp, vp]),
         "oracle_edge_grad_edges": (None, [i64, i64, vp, vp, vp, vp, vp, vp, vp]),
         "oracle_degree_plan": (None, [i64, vp, vp, vp]),
+        "oracle_edge_softmax": (None, [i64, i64, vp, vp, vp, vp, vp]),
+        "oracle_edge_softmax_backward": (None, [i64, i64, vp, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -186,3 +188,28 @@ def degree_plan(n: int, rowptr):
     counts = np.empty(33, np.int64)
     _load().oracle_degree_plan(n, _p(rowptr), _p(perm), _p(counts))
     return perm, counts
+
+
+def edge_softmax(n: int, dst, s):
+    """alpha_e = softmax of the scores over the incoming edges of dst_e (float64),
+    plus the row maxima and row sums (-inf / 0 for rows without edges)."""
+    dst, s = _i64(dst), _f32(s)
+    e = dst.shape[0]
+    alpha = np.empty(e, np.float64)
+    rmax = np.empty(n, np.float64)
+    rsum = np.empty(n, np.float64)
+    _load().oracle_edge_softmax(n, e, _p(dst), _p(s), _p(alpha), _p(rmax), _p(rsum))
+    return alpha, rmax, rsum
+
+
+def edge_softmax_backward(n: int, dst, alpha, dalpha):
+    """ds_e = alpha_e (dalpha_e - sum over the row of alpha * dalpha), with the row
+    dots and the per-edge scale S (all float64).  alpha, dalpha: float32 inputs."""
+    dst, alpha, dalpha = _i64(dst), _f32(alpha), _f32(dalpha)
+    e = dst.shape[0]
+    ds = np.empty(e, np.float64)
+    rdot = np.empty(n, np.float64)
+    scale = np.empty(e, np.float64)
+    _load().oracle_edge_softmax_backward(n, e, _p(dst), _p(alpha), _p(dalpha), _p(ds),
+                                         _p(rdot), _p(scale))
+    return ds, rdot, scale

@@ -285,3 +285,58 @@ void oracle_degree_plan(int64_t n, const int64_t *rowptr, int64_t *perm,
         }
     }
 }
+
+/* ------------------------------------------------------------------------- */
+/* Target normalisation of scalar edge scores ([W] "Limits": a sparse          */
+/* attention step puts learned scalar scores through a normalisation over the  */
+/* edges of each target before this aggregation).  Plain definition, a softmax */
+/* over the incoming edges of each destination:                                 */
+/*   alpha_e = exp(s_e - m_i) / z_i,  m_i = max over e' into i of s_e',        */
+/*   z_i = sum over e' into i of exp(s_e' - m_i),   i = dst_e.                 */
+/* Duplicates are separate terms.  Row statistics m_i, z_i are returned too    */
+/* (m_i = -inf and z_i = 0 for a row with no edges).                           */
+/* ------------------------------------------------------------------------- */
+void oracle_edge_softmax(int64_t n, int64_t e, const int64_t *dst, const float *s,
+                         double *alpha, double *row_max, double *row_sum)
+{
+    int64_t i, j;
+    for (i = 0; i < n; i++) {
+        row_max[i] = -INFINITY;
+        row_sum[i] = 0.0;
+    }
+    for (j = 0; j < e; j++)
+        if ((double)s[j] > row_max[dst[j]])
+            row_max[dst[j]] = (double)s[j];
+    for (j = 0; j < e; j++)
+        row_sum[dst[j]] += exp((double)s[j] - row_max[dst[j]]);
+    for (j = 0; j < e; j++)
+        alpha[j] = exp((double)s[j] - row_max[dst[j]]) / row_sum[dst[j]];
+}
+
+/* ------------------------------------------------------------------------- */
+/* Backward of the target softmax: with upstream gradient dalpha_e,            */
+/*   ds_e = alpha_e * (dalpha_e - t_i),  t_i = sum over e' into i of           */
+/*                                             alpha_e' * dalpha_e'.           */
+/* (the Jacobian of a softmax applied row by row).  S_e = alpha_e * (|dalpha_e| */
+/* + sum over e' into i of alpha_e' |dalpha_e'|) is the scale of each term.    */
+/* ------------------------------------------------------------------------- */
+void oracle_edge_softmax_backward(int64_t n, int64_t e, const int64_t *dst,
+                                  const float *alpha, const float *dalpha,
+                                  double *ds, double *row_dot, double *s_scale)
+{
+    int64_t i, j;
+    double *row_abs = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    for (i = 0; i < n; i++) {
+        row_dot[i] = 0.0;
+        row_abs[i] = 0.0;
+    }
+    for (j = 0; j < e; j++) {
+        row_dot[dst[j]] += (double)alpha[j] * (double)dalpha[j];
+        row_abs[dst[j]] += fabs((double)alpha[j] * (double)dalpha[j]);
+    }
+    for (j = 0; j < e; j++) {
+        ds[j] = (double)alpha[j] * ((double)dalpha[j] - row_dot[dst[j]]);
+        s_scale[j] = fabs((double)alpha[j]) * (fabs((double)dalpha[j]) + row_abs[dst[j]]);
+    }
+    free(row_abs);
+}

@@ -336,4 +336,125 @@ def pin_degree_plan_numpy():
             assert np.array_equal(perm, np.argsort(-cls, kind="stable"))
 
 
+# --------------------------------------------------------------------------- target softmax
+
+def _segments(dst):
+    """Edge ids of each destination, in COO order."""
+    order = np.argsort(dst, kind="stable")
+    bounds = np.concatenate([[0], np.cumsum(np.bincount(dst))])
+    return order, bounds
+
+
+def pin_softmax_scipy_segments():
+    from scipy.special import softmax
+    for seed, (n, e) in enumerate([(50, 400), (300, 3000), (7, 60)]):
+        rng = np.random.default_rng(200 + seed)
+        dst = rng.integers(0, n, e)
+        s = (rng.standard_normal(e) * 3).astype(np.float32)
+        alpha, rmax, rsum = oracle.edge_softmax(n, dst, s)
+        order, bounds = _segments(dst)
+        for i in range(n):
+            ids = order[bounds[i]:bounds[i + 1]]
+            if ids.size == 0:
+                assert rmax[i] == -np.inf and rsum[i] == 0
+                continue
+            np.testing.assert_allclose(alpha[ids], softmax(s[ids].astype(np.float64)),
+                                       rtol=1e-12, atol=1e-15)
+            assert rmax[i] == s[ids].max()
+            np.testing.assert_allclose(np.log(rsum[i]) + rmax[i],
+                                       np.log(np.exp(s[ids].astype(np.float64)).sum()),
+                                       rtol=1e-12)
+
+
+def pin_softmax_laws():
+    rng = np.random.default_rng(211)
+    n, e = 120, 2000
+    dst = rng.integers(0, n, e)
+    s = rng.standard_normal(e).astype(np.float32)
+    alpha, _, _ = oracle.edge_softmax(n, dst, s)
+    assert np.all(alpha > 0)
+    sums = np.bincount(dst, weights=alpha, minlength=n)
+    has = np.bincount(dst, minlength=n) > 0
+    np.testing.assert_allclose(sums[has], 1.0, rtol=1e-12)
+    # equal scores -> 1/deg
+    a_eq, _, _ = oracle.edge_softmax(n, dst, np.full(e, 0.75, np.float32))
+    np.testing.assert_allclose(a_eq, 1.0 / np.bincount(dst, minlength=n)[dst], rtol=1e-12)
+    # a constant per destination row changes nothing (scores on a 2^-10 grid and
+    # shifts on a 2^-4 grid, so every shifted score is exact in fp32)
+    sg = (rng.integers(-4096, 4096, e) / 1024.0).astype(np.float32)
+    shift = (rng.integers(-64, 64, n) / 16.0).astype(np.float32)
+    a_g, _, _ = oracle.edge_softmax(n, dst, sg)
+    a_sh, _, _ = oracle.edge_softmax(n, dst, (sg + shift[dst]).astype(np.float32))
+    np.testing.assert_allclose(a_sh, a_g, rtol=1e-12)
+    # large scores stay finite (the row maximum is subtracted)
+    a_big, _, _ = oracle.edge_softmax(n, dst, (s + 1000.0).astype(np.float32))
+    assert np.all(np.isfinite(a_big))
+    np.testing.assert_allclose(np.bincount(dst, weights=a_big, minlength=n)[has], 1.0, rtol=1e-12)
+
+
+def pin_softmax_backward_jacobian():
+    """ds = J dalpha with the explicit per-row Jacobian J = diag(a) - a a^T."""
+    rng = np.random.default_rng(221)
+    n, e = 40, 500
+    dst = rng.integers(0, n, e)
+    alpha = rng.uniform(0.01, 1, e).astype(np.float32)      # any positive values
+    dalpha = rng.standard_normal(e).astype(np.float32)
+    ds, rdot, scale = oracle.edge_softmax_backward(n, dst, alpha, dalpha)
+    order, bounds = _segments(dst)
+    a64, d64 = alpha.astype(np.float64), dalpha.astype(np.float64)
+    for i in range(n):
+        ids = order[bounds[i]:bounds[i + 1]]
+        if ids.size == 0:
+            assert rdot[i] == 0
+            continue
+        jac = np.diag(a64[ids]) - np.outer(a64[ids], a64[ids])
+        np.testing.assert_allclose(ds[ids], jac @ d64[ids], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(rdot[i], a64[ids] @ d64[ids], rtol=1e-12, atol=1e-14)
+    assert np.all(scale >= np.abs(ds) * (1 - 1e-12))
+
+
+def pin_softmax_backward_central_difference():
+    """f(s) = sum_e c_e alpha_e(s): central differences equal the backward with dalpha = c."""
+    rng = np.random.default_rng(231)
+    n, e = 9, 40
+    dst = rng.integers(0, n, e)
+    s = rng.standard_normal(e).astype(np.float32)
+    c = rng.standard_normal(e)
+    alpha, _, _ = oracle.edge_softmax(n, dst, s)
+    ds, _, _ = oracle.edge_softmax_backward(n, dst, alpha.astype(np.float32),
+                                            c.astype(np.float32))
+    for j in range(e):
+        sp, sm = s.copy(), s.copy()
+        sp[j] += np.float32(1e-2)
+        sm[j] -= np.float32(1e-2)
+        fp = float(c @ oracle.edge_softmax(n, dst, sp)[0])
+        fm = float(c @ oracle.edge_softmax(n, dst, sm)[0])
+        fd = (fp - fm) / (float(sp[j]) - float(sm[j]))
+        assert abs(fd - ds[j]) <= 2e-4 * (1 + abs(ds[j])), (j, fd, ds[j])
+
+
+def pin_attention_layer_gradient():
+    """Y = A_alpha(s) X with alpha the target softmax of s: d<dY, Y>/ds by central
+    differences equals softmax_backward(alpha, edge_grad(X, dY))."""
+    wl = synth.random_graph(10, 45, 3, 241)
+    s = wl.w
+    dy64 = wl.dy.astype(np.float64)
+
+    def f(scores):
+        a, _, _ = oracle.edge_softmax(wl.n, wl.dst, scores)
+        y, _ = oracle.forward(wl.n, wl.src, wl.dst, a.astype(np.float32), wl.x)
+        return float((dy64 * y).sum())
+
+    alpha, _, _ = oracle.edge_softmax(wl.n, wl.dst, s)
+    dalpha, _ = oracle.edge_grad(wl.src, wl.dst, wl.x, wl.dy)
+    ds, _, _ = oracle.edge_softmax_backward(wl.n, wl.dst, alpha.astype(np.float32),
+                                            dalpha.astype(np.float32))
+    for j in range(wl.e):
+        sp, sm = s.copy(), s.copy()
+        sp[j] += np.float32(1e-2)
+        sm[j] -= np.float32(1e-2)
+        fd = (f(sp) - f(sm)) / (float(sp[j]) - float(sm[j]))
+        assert abs(fd - ds[j]) <= 1e-3 * (1 + abs(ds[j])), (j, fd, ds[j])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -33,6 +33,14 @@ MUTANTS = {
     "lower_rowptr_unshifted": ("rowptr[key[j] + 1] += 1;", "rowptr[key[j]] += 1;"),
     "plan_ascending_classes": ("for (c = 32; c >= 0; c--) {", "for (c = 0; c <= 32; c++) {"),
     "plan_class_off_by_one": ("class_count[k] += 1;", "class_count[k > 0 ? k - 1 : 0] += 1;"),
+    "softmax_no_max_shift": ("        row_sum[dst[j]] += exp((double)s[j] - row_max[dst[j]]);",
+                             "        row_sum[dst[j]] += exp((double)s[j]);"),
+    "softmax_over_source_rows": ("        alpha[j] = exp((double)s[j] - row_max[dst[j]]) / row_sum[dst[j]];",
+                                 "        alpha[j] = exp((double)s[j] - row_max[dst[j]]) / row_sum[dst[j] > 0 ? dst[j] - 1 : 0];"),
+    "softmax_backward_sign": ("        ds[j] = (double)alpha[j] * ((double)dalpha[j] - row_dot[dst[j]]);",
+                              "        ds[j] = (double)alpha[j] * ((double)dalpha[j] + row_dot[dst[j]]);"),
+    "softmax_backward_row_dot_unweighted": ("        row_dot[dst[j]] += (double)alpha[j] * (double)dalpha[j];",
+                                            "        row_dot[dst[j]] += (double)dalpha[j];"),
 }
 
 

@@ -11,6 +11,8 @@ turns status codes into exceptions.
     dX = mp_spmm_dx(g, w, dY)                      # dX = A_w^T dY
     dw = mp_edge_grad_dw(g, X, dY)                 # dw_e = <X[src_e], dY[dst_e]>, COO order
     dX, dw = mp_spmm_dx_edge_grad(g, w, X, dY)     # both gradients in one pass
+    a, m, z = mp_edge_softmax(g, s)                # softmax of edge scores per destination
+    ds, t = mp_edge_softmax_backward(g, a, da)     # its backward
 
 (tinymesh "Weighted aggregation experiment": "Decision", "Edge order is
 explicit".)  The library must be built (``python -m gnn_sparse_message_amd._build``
@@ -25,7 +27,8 @@ import torch  # noqa: F401  -- loaded first so libmp.so binds to torch's HIP run
 
 __all__ = [
     "Graph", "MpError", "mp_graph_build", "mp_graph_build_workspace_size", "mp_spmm_fwd",
-    "mp_spmm_dx", "mp_edge_grad_dw", "mp_spmm_dx_edge_grad", "mp_status_string", "mp_version", "library_path",
+    "mp_spmm_dx", "mp_edge_grad_dw", "mp_spmm_dx_edge_grad", "mp_edge_softmax",
+    "mp_edge_softmax_backward", "mp_status_string", "mp_version", "library_path",
     "NUM_CLASSES",
 ]
 
@@ -96,6 +99,8 @@ def _load():
         "mp_spmm_dx": (i32, [gp, vp, vp, i32, i64, vp, vp]),
         "mp_edge_grad_dw": (i32, [gp, vp, vp, i32, i64, vp, vp]),
         "mp_spmm_dx_edge_grad": (i32, [gp, vp, vp, vp, i32, i64, vp, vp, vp]),
+        "mp_edge_softmax": (i32, [gp, vp, vp, vp, vp, vp]),
+        "mp_edge_softmax_backward": (i32, [gp, vp, vp, vp, vp, vp]),
         "mp_status_string": (ctypes.c_char_p, [i32]),
         "mp_last_error_detail": (ctypes.c_char_p, []),
         "mp_version": (i32, []),
@@ -301,3 +306,38 @@ def mp_spmm_dx_edge_grad(g: Graph, w, x, dy, out_dx=None, out_dw=None):
                                      _ptr(dw) if g.num_edges else None, _stream(dy)),
            "mp_spmm_dx_edge_grad")
     return dx, dw
+
+
+def _edge_f32(name, t, g: Graph):
+    _need_tensor(name, t)
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if t.dim() != 1 or t.shape[0] != g.num_edges:
+        raise ValueError(f"{name} must have shape [{g.num_edges}], got {tuple(t.shape)}")
+
+
+def mp_edge_softmax(g: Graph, scores, out_alpha=None, out_row_max=None, out_row_sum=None):
+    """Softmax of the edge scores over the incoming edges of each destination:
+    returns (alpha [E] COO order, row_max [N], row_sum [N]), all float32."""
+    _edge_f32("scores", scores, g)
+    alpha = _out(out_alpha, (g.num_edges,), scores)
+    rmax = _out(out_row_max, (g.num_nodes,), scores)
+    rsum = _out(out_row_sum, (g.num_nodes,), scores)
+    _check(_lib.mp_edge_softmax(ctypes.byref(g._desc), _ptr(scores) if g.num_edges else None,
+                                _ptr(alpha) if g.num_edges else None, _ptr(rmax), _ptr(rsum),
+                                _stream(scores)), "mp_edge_softmax")
+    return alpha, rmax, rsum
+
+
+def mp_edge_softmax_backward(g: Graph, alpha, dalpha, out_dscores=None, out_row_dot=None):
+    """Backward of mp_edge_softmax: returns (dscores [E] COO order, row_dot [N])."""
+    _edge_f32("alpha", alpha, g)
+    _edge_f32("dalpha", dalpha, g)
+    ds = _out(out_dscores, (g.num_edges,), alpha)
+    rdot = _out(out_row_dot, (g.num_nodes,), alpha)
+    _check(_lib.mp_edge_softmax_backward(ctypes.byref(g._desc),
+                                         _ptr(alpha) if g.num_edges else None,
+                                         _ptr(dalpha) if g.num_edges else None,
+                                         _ptr(ds) if g.num_edges else None, _ptr(rdot),
+                                         _stream(alpha)), "mp_edge_softmax_backward")
+    return ds, rdot

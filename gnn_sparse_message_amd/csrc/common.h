@@ -68,4 +68,10 @@ mp_status spmm_fused_run(const CsrView &csr, const float *w, const void *x, mp_d
 mp_status sddmm_run(const int32_t *src, const int32_t *dst, int64_t e, const void *x,
                     const void *dy, mp_dtype dt, int64_t h, float *dw, hipStream_t stream);
 
+// ---------------------------------------------------------------- target softmax
+mp_status edge_softmax_run(const mp_graph *g, const float *s, float *alpha, float *row_max,
+                           float *row_sum, hipStream_t stream);
+mp_status edge_softmax_backward_run(const mp_graph *g, const float *alpha, const float *dalpha,
+                                    float *ds, float *row_dot, hipStream_t stream);
+
 }  // namespace mp

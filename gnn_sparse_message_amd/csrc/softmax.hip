@@ -1,0 +1,258 @@
+// softmax.hip -- target normalisation of scalar edge scores for sparse
+// attention over the fixed topology (tinymesh "Weighted aggregation
+// experiment", "Limits": learned scalar scores normalised over the edges of
+// each target, then aggregated by this operation):
+//   alpha_e = exp(s_e - m_i) / z_i  for i = dst_e, with the row maximum m_i and
+//   z_i = sum over the row of exp(s - m_i);
+// and its backward  ds_e = alpha_e (dalpha_e - t_i),  t_i = sum over the row of
+// alpha * dalpha.
+//
+// Both run in two steps: per-destination row statistics over the forward CSR
+// (rows in degree-plan order; a workgroup owns a hub row, a wave a long row, a
+// single lane a short row; each owner combines its lanes in a fixed order, no
+// atomics), then one elementwise pass over the edges in COO order, which reads
+// s / alpha / dalpha coalesced and the per-row statistics by dst (node-sized
+// arrays that stay in cache).  The row statistics are outputs of the calls.
+#include "common.h"
+
+#include <math.h>
+
+namespace mp {
+namespace {
+
+constexpr int kHubLen = 4096;   // rows this long get a workgroup
+constexpr int kWaveLen = 64;    // rows this long (below kHubLen) get a wave
+
+// Online (max, sum of exp(x - max)) pair.
+struct MaxSum {
+    float m, z;
+};
+
+__device__ __forceinline__ MaxSum ms_add(MaxSum a, float x) {
+    if (x > a.m) {   // also the first element: a.m = -inf, a.z = 0
+        a.z = (a.m == -INFINITY ? 0.f : a.z * expf(a.m - x)) + 1.f;
+        a.m = x;
+    } else {
+        a.z += expf(x - a.m);
+    }
+    return a;
+}
+
+__device__ __forceinline__ MaxSum ms_merge(MaxSum a, MaxSum b) {
+    const float m = fmaxf(a.m, b.m);
+    if (m == -INFINITY) return a;   // both empty
+    const float za = a.m == -INFINITY ? 0.f : a.z * expf(a.m - m);
+    const float zb = b.m == -INFINITY ? 0.f : b.z * expf(b.m - m);
+    return MaxSum{m, za + zb};
+}
+
+// Wave-wide combine in a fixed butterfly order; every lane ends with the total.
+__device__ __forceinline__ MaxSum ms_wave(MaxSum v) {
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) {
+        MaxSum o{__shfl_xor(v.m, off), __shfl_xor(v.z, off)};
+        v = ms_merge(v, o);
+    }
+    return v;
+}
+
+__device__ __forceinline__ float sum_wave(float v) {
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+struct RowArgs {
+    const int32_t *rowptr;
+    const int32_t *order;
+    const int32_t *plan;
+    const float *a;         // scores (forward) or alpha (backward), COO order
+    const float *b;         // dalpha (backward only), COO order
+    float *out0;            // row_max (forward) or row_dot (backward), [N]
+    float *out1;            // row_sum (forward only), [N]
+    int64_t n, e;
+    int32_t n_hub, n_wave, n_lane;
+    int32_t blk_hub, blk_wave, blk_lane;
+};
+
+__device__ __forceinline__ uint32_t coo(const RowArgs &r, int64_t p) {
+    const uint32_t o = (uint32_t)r.order[p];
+    return (int64_t)o < r.e ? o : 0u;   // order is a permutation of [0, e)
+}
+
+// kBackward = false: online max / sum of exp of the scores.
+// kBackward = true : sum of alpha * dalpha.
+template <bool kBackward>
+__global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    int64_t b = blockIdx.x;
+    auto finish = [&](int row, MaxSum ms, float dot) {
+        if (kBackward) {
+            r.out0[row] = dot;
+        } else {
+            r.out0[row] = ms.m;
+            r.out1[row] = ms.m == -INFINITY ? 0.f : ms.z;
+        }
+    };
+    if (b < r.blk_hub) {   // hub row: the whole workgroup, lanes strided over the edges
+        __shared__ float s_m[kWavesPerBlock], s_z[kWavesPerBlock];
+        const int row = r.plan[b];
+        if ((uint32_t)row >= (uint64_t)r.n) return;
+        const int64_t beg = r.rowptr[row], end = r.rowptr[row + 1];
+        MaxSum ms{-INFINITY, 0.f};
+        float dot = 0.f;
+        for (int64_t p = beg + threadIdx.x; p < end; p += kBlock) {
+            const uint32_t o = coo(r, p);
+            if (kBackward) dot = fmaf(r.a[o], r.b[o], dot);
+            else ms = ms_add(ms, r.a[o]);
+        }
+        if (kBackward) dot = sum_wave(dot);
+        else ms = ms_wave(ms);
+        if (lane == 0) {
+            s_m[wv] = kBackward ? dot : ms.m;
+            s_z[wv] = ms.z;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            MaxSum t{s_m[0], s_z[0]};
+            float d = s_m[0];
+            for (int w = 1; w < kWavesPerBlock; ++w) {
+                if (kBackward) d += s_m[w];
+                else t = ms_merge(t, MaxSum{s_m[w], s_z[w]});
+            }
+            finish(row, t, d);
+        }
+        return;
+    }
+    b -= r.blk_hub;
+    if (b < r.blk_wave) {   // long rows: one wave each
+        for (int64_t idx = b * kWavesPerBlock + wv; idx < r.n_wave;
+             idx += (int64_t)r.blk_wave * kWavesPerBlock) {
+            const int row = r.plan[r.n_hub + idx];
+            if ((uint32_t)row >= (uint64_t)r.n) continue;
+            const int64_t beg = r.rowptr[row], end = r.rowptr[row + 1];
+            MaxSum ms{-INFINITY, 0.f};
+            float dot = 0.f;
+            for (int64_t p = beg + lane; p < end; p += kWave) {
+                const uint32_t o = coo(r, p);
+                if (kBackward) dot = fmaf(r.a[o], r.b[o], dot);
+                else ms = ms_add(ms, r.a[o]);
+            }
+            if (kBackward) dot = sum_wave(dot);
+            else ms = ms_wave(ms);
+            if (lane == 0) finish(row, ms, dot);
+        }
+        return;
+    }
+    b -= r.blk_wave;
+    // short and empty rows: one lane each
+    for (int64_t idx = b * kBlock + threadIdx.x; idx < r.n_lane;
+         idx += (int64_t)r.blk_lane * kBlock) {
+        const int row = r.plan[r.n_hub + r.n_wave + idx];
+        if ((uint32_t)row >= (uint64_t)r.n) continue;
+        const int64_t beg = r.rowptr[row], end = r.rowptr[row + 1];
+        MaxSum ms{-INFINITY, 0.f};
+        float dot = 0.f;
+        for (int64_t p = beg; p < end; ++p) {
+            const uint32_t o = coo(r, p);
+            if (kBackward) dot = fmaf(r.a[o], r.b[o], dot);
+            else ms = ms_add(ms, r.a[o]);
+        }
+        finish(row, ms, dot);
+    }
+}
+
+// alpha_e = exp(s_e - m[dst_e]) / z[dst_e]
+__global__ __launch_bounds__(kBlock) void softmax_apply_kernel(const int32_t *__restrict__ dst,
+                                                               const float *__restrict__ s,
+                                                               const float *__restrict__ rmax,
+                                                               const float *__restrict__ rsum,
+                                                               float *__restrict__ alpha,
+                                                               int64_t e) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < e; i += stride) {
+        const int d = dst[i];
+        alpha[i] = expf(s[i] - rmax[d]) / rsum[d];
+    }
+}
+
+// ds_e = alpha_e (dalpha_e - t[dst_e])
+__global__ __launch_bounds__(kBlock) void softmax_backward_apply_kernel(
+    const int32_t *__restrict__ dst, const float *__restrict__ alpha,
+    const float *__restrict__ dalpha, const float *__restrict__ rdot, float *__restrict__ ds,
+    int64_t e) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < e; i += stride)
+        ds[i] = alpha[i] * (dalpha[i] - rdot[dst[i]]);
+}
+
+int64_t rows_at_least(const int64_t *cc, int64_t len) {
+    int64_t r = 0;
+    for (int c = MP_NUM_CLASSES - 1; c >= 1; --c)
+        if (((int64_t)1 << (c - 1)) >= len) r += cc[c];
+    return r;
+}
+
+RowArgs row_args(const mp_graph *g) {
+    RowArgs r;
+    r.rowptr = g->rowptr;
+    r.order = g->edge_order;
+    r.plan = g->row_plan;
+    r.n = g->num_nodes;
+    r.e = g->num_edges;
+    const int64_t at_hub = rows_at_least(g->class_count, kHubLen);
+    const int64_t at_wave = rows_at_least(g->class_count, kWaveLen);
+    r.n_hub = (int32_t)at_hub;
+    r.n_wave = (int32_t)(at_wave - at_hub);
+    r.n_lane = (int32_t)(g->num_nodes - at_wave);
+    constexpr int64_t kCap = 1 << 22;
+    const int64_t bw = (r.n_wave + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t bl = (r.n_lane + kBlock - 1) / kBlock;
+    r.blk_hub = r.n_hub;
+    r.blk_wave = (int32_t)(bw < kCap ? bw : kCap);
+    r.blk_lane = (int32_t)(bl < kCap ? bl : kCap);
+    return r;
+}
+
+unsigned grid_for(int64_t items) {
+    int64_t b = (items + kBlock - 1) / kBlock;
+    if (b < 1) b = 1;
+    return (unsigned)(b < 65536 ? b : 65536);
+}
+
+}  // namespace
+
+mp_status edge_softmax_run(const mp_graph *g, const float *s, float *alpha, float *rmax,
+                           float *rsum, hipStream_t st) {
+    RowArgs r = row_args(g);
+    r.a = s;
+    r.b = nullptr;
+    r.out0 = rmax;
+    r.out1 = rsum;
+    const int64_t gx = (int64_t)r.blk_hub + r.blk_wave + r.blk_lane;
+    row_stats_kernel<false><<<(unsigned)gx, kBlock, 0, st>>>(r);
+    if (g->num_edges > 0)
+        softmax_apply_kernel<<<grid_for(g->num_edges), kBlock, 0, st>>>(g->dst, s, rmax, rsum,
+                                                                         alpha, g->num_edges);
+    MP_HIP_CHECK(hipGetLastError(), "edge softmax launch");
+    return MP_OK;
+}
+
+mp_status edge_softmax_backward_run(const mp_graph *g, const float *alpha, const float *dalpha,
+                                    float *ds, float *rdot, hipStream_t st) {
+    RowArgs r = row_args(g);
+    r.a = alpha;
+    r.b = dalpha;
+    r.out0 = rdot;
+    r.out1 = nullptr;
+    const int64_t gx = (int64_t)r.blk_hub + r.blk_wave + r.blk_lane;
+    row_stats_kernel<true><<<(unsigned)gx, kBlock, 0, st>>>(r);
+    if (g->num_edges > 0)
+        softmax_backward_apply_kernel<<<grid_for(g->num_edges), kBlock, 0, st>>>(
+            g->dst, alpha, dalpha, rdot, ds, g->num_edges);
+    MP_HIP_CHECK(hipGetLastError(), "edge softmax backward launch");
+    return MP_OK;
+}
+
+}  // namespace mp

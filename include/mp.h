@@ -190,6 +190,36 @@ mp_status mp_edge_grad_dw(const mp_graph *g, const void *x, const void *dy, mp_d
 mp_status mp_spmm_dx_edge_grad(const mp_graph *g, const float *w, const void *x, const void *dy,
                                mp_dtype dtype, int64_t h, float *dx, float *dw, void *stream);
 
+/*
+ * Target normalisation of scalar edge scores, the step a sparse attention layer
+ * puts between learned scores and this aggregation ("Limits": scores
+ * normalised over the edges of each target).  For every edge e with i = dst_e:
+ *   alpha_e = exp(s_e - row_max[i]) / row_sum[i],
+ *   row_max[i] = max over the edges into i of s,
+ *   row_sum[i] = sum over the edges into i of exp(s - row_max[i]);
+ * duplicate edges are separate terms; a row with no edges gets row_max = -inf
+ * and row_sum = 0.  Scores must be finite.  Row statistics are computed per
+ * destination over the forward CSR (one owner per row, no atomics), alpha in
+ * COO order; fp32 throughout.
+ *   scores  [E] float32, COO order.    alpha  [E] float32 output, COO order.
+ *   row_max, row_sum  [N] float32 outputs.
+ * Then Y = A_alpha X is mp_spmm_fwd(g, alpha, X, ...).
+ */
+mp_status mp_edge_softmax(const mp_graph *g, const float *scores, float *alpha, float *row_max,
+                          float *row_sum, void *stream);
+
+/*
+ * Backward of mp_edge_softmax: given alpha and the upstream gradient dalpha
+ * (for the attention layer, dalpha = mp_edge_grad_dw(g, X, dY) or the dw of
+ * mp_spmm_dx_edge_grad), writes
+ *   dscores_e = alpha_e * (dalpha_e - row_dot[dst_e]),
+ *   row_dot[i] = sum over the edges into i of alpha * dalpha.
+ *   alpha, dalpha  [E] float32, COO order.   dscores  [E] float32 output.
+ *   row_dot  [N] float32 output.
+ */
+mp_status mp_edge_softmax_backward(const mp_graph *g, const float *alpha, const float *dalpha,
+                                   float *dscores, float *row_dot, void *stream);
+
 /* Static text for a status code. */
 const char *mp_status_string(mp_status status);
 

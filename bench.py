@@ -185,6 +185,26 @@ def main():
             ts.append(a.elapsed_time(b))
         standalone[name] = statistics.median(ts)
     same = bool(torch.equal(dx_alone, dx) and torch.equal(dw_alone, dw))
+    # Sparse attention pieces on the same topology (scores = the edge weights).
+    alpha = torch.empty_like(w)
+    rmax = torch.empty(n, dtype=torch.float32, device=dev)
+    rsum = torch.empty_like(rmax)
+    dscores = torch.empty_like(w)
+    rdot = torch.empty_like(rmax)
+    for name, fn in (("edge_softmax", lambda: mp.mp_edge_softmax(g, w, alpha, rmax, rsum)),
+                     ("edge_softmax_backward",
+                      lambda: mp.mp_edge_softmax_backward(g, alpha, dw, dscores, rdot))):
+        fn()
+        ts = []
+        for _ in range(5):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        standalone[name] = statistics.median(ts)
     log(f"standalone dx {standalone['dx']:.3f} ms, dw {standalone['dw']:.3f} ms, "
         f"equal to the fused results: {same}")
 
@@ -197,6 +217,11 @@ def main():
 
     bytes_ = algorithmic_bytes(n, e, h, 2, 8)
     bytes_["bwd"] = bytes_["dx"] + bytes_["dw"]
+    # target softmax: row pass reads order + score per edge and writes 2 stats per
+    # row; the edge pass reads dst + score, writes alpha.  Backward: row pass reads
+    # order + alpha + dalpha, the edge pass dst + alpha + dalpha and writes ds.
+    bytes_["edge_softmax"] = 20 * e + 24 * n
+    bytes_["edge_softmax_backward"] = 28 * e + 16 * n
     ms_step = t_total / args.steps * 1e3
 
     def rate(nbytes, ms):

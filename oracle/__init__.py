@@ -50,6 +50,7 @@ def _bind(lib):
         "oracle_degree_plan": (None, [i64, vp, vp, vp]),
         "oracle_edge_softmax": (None, [i64, i64, vp, vp, vp, vp, vp]),
         "oracle_edge_softmax_backward": (None, [i64, i64, vp, vp, vp, vp, vp, vp]),
+        "oracle_edge_normalize": (ctypes.c_int, [i64, i64, vp, vp, ctypes.c_int, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -213,3 +214,18 @@ def edge_softmax_backward(n: int, dst, alpha, dalpha):
     _load().oracle_edge_softmax_backward(n, e, _p(dst), _p(alpha), _p(dalpha), _p(ds),
                                          _p(rdot), _p(scale))
     return ds, rdot, scale
+
+
+NORM_MEAN, NORM_SYM = 1, 2
+
+
+def edge_normalize(n: int, src, dst, mode: int, values):
+    """out_e = values_e / deg_in(dst_e) (mode 1) or / sqrt(deg_out(src_e) deg_in(dst_e))
+    (mode 2), degrees being edge counts; float64."""
+    src, dst, values = _i64(src), _i64(dst), _f32(values)
+    out = np.empty(src.shape[0], np.float64)
+    rc = _load().oracle_edge_normalize(n, src.shape[0], _p(src), _p(dst), int(mode), _p(values),
+                                       _p(out))
+    if rc != 0:
+        raise ValueError(f"unknown normalisation mode {mode}")
+    return out

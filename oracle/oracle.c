@@ -340,3 +340,45 @@ void oracle_edge_softmax_backward(int64_t n, int64_t e, const int64_t *dst,
     }
     free(row_abs);
 }
+
+/* ------------------------------------------------------------------------- */
+/* Degree normalisation of edge values, for mean and symmetric-normalised     */
+/* aggregation ([P] Step 3: GCN builds a normalised adjacency before its       */
+/* single SpMM, SAGE aggregates a mean; [P] "Done when": sum and mean are the  */
+/* reductions that keep gradients).  Degrees are edge counts (duplicates and   */
+/* self-loops counted): deg_in(i) = edges ending at i, deg_out(j) = edges      */
+/* leaving j.                                                                   */
+/*   mode 1 (mean):      out_e = in_e / deg_in(dst_e)                           */
+/*   mode 2 (symmetric): out_e = in_e / sqrt(deg_out(src_e) * deg_in(dst_e))    */
+/* The same scaling maps a weight gradient dL/dw' back to dL/dw (w' = c w).   */
+/* Returns -1 for an unknown mode.                                              */
+/* ------------------------------------------------------------------------- */
+int oracle_edge_normalize(int64_t n, int64_t e, const int64_t *src, const int64_t *dst,
+                          int mode, const float *in, double *out)
+{
+    int64_t i, j;
+    double *din = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    double *dout = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    if (mode != 1 && mode != 2) {
+        free(din);
+        free(dout);
+        return -1;
+    }
+    for (i = 0; i < n; i++) {
+        din[i] = 0.0;
+        dout[i] = 0.0;
+    }
+    for (j = 0; j < e; j++) {
+        din[dst[j]] += 1.0;
+        dout[src[j]] += 1.0;
+    }
+    for (j = 0; j < e; j++) {
+        if (mode == 1)
+            out[j] = (double)in[j] / din[dst[j]];
+        else
+            out[j] = (double)in[j] / sqrt(dout[src[j]] * din[dst[j]]);
+    }
+    free(din);
+    free(dout);
+    return 0;
+}

@@ -457,4 +457,71 @@ def pin_attention_layer_gradient():
         assert abs(fd - ds[j]) <= 1e-3 * (1 + abs(ds[j])), (j, fd, ds[j])
 
 
+# --------------------------------------------------------------------------- degree normalisation
+
+def pin_normalize_dense():
+    """Dense forms: mean = D_in^-1 A, symmetric = D_in^-1/2 A D_out^-1/2, with
+    D from the edge counts (row and column sums of the unweighted A)."""
+    for n, src, dst, w, x, dy in _tiny_graphs(300, 251):
+        if len(src) == 0:
+            continue
+        ones = np.zeros((n, n))
+        np.add.at(ones, (dst, src), 1.0)
+        din, dout = ones.sum(axis=1), ones.sum(axis=0)
+        a = _dense(n, src, dst, w)
+        wm = oracle.edge_normalize(n, src, dst, oracle.NORM_MEAN, w)
+        ws = oracle.edge_normalize(n, src, dst, oracle.NORM_SYM, w)
+        am = _dense(n, src, dst, wm)
+        asym = _dense(n, src, dst, ws)
+        with np.errstate(divide="ignore"):
+            rin = np.where(din > 0, 1.0 / din, 0.0)
+            rsin = np.where(din > 0, din ** -0.5, 0.0)
+            rsout = np.where(dout > 0, dout ** -0.5, 0.0)
+        np.testing.assert_allclose(am, rin[:, None] * a, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(asym, rsin[:, None] * a * rsout[None, :], rtol=1e-12,
+                                   atol=1e-14)
+
+
+def pin_normalize_laws():
+    wl = synth.random_graph(400, 6000, 1, 261)
+    ones = np.ones(wl.e, np.float32)
+    mean = oracle.edge_normalize(wl.n, wl.src, wl.dst, oracle.NORM_MEAN, ones)
+    sums = np.bincount(wl.dst, weights=mean, minlength=wl.n)
+    has = np.bincount(wl.dst, minlength=wl.n) > 0
+    np.testing.assert_allclose(sums[has], 1.0, rtol=1e-12)             # mean rows sum to 1
+    # symmetric normalisation of an undirected graph (each edge in both directions)
+    # is a symmetric matrix whose spectral radius is 1 for a connected graph
+    src = np.concatenate([wl.src, wl.dst])
+    dst = np.concatenate([wl.dst, wl.src])
+    sym = oracle.edge_normalize(wl.n, src, dst, oracle.NORM_SYM, np.ones(src.shape[0], np.float32))
+    a = _dense(wl.n, src, dst, sym)
+    assert np.allclose(a, a.T, atol=1e-14)
+    ev = np.linalg.eigvalsh(a)
+    assert abs(max(abs(ev.max()), abs(ev.min())) - 1.0) < 1e-9
+    try:
+        oracle.edge_normalize(wl.n, wl.src, wl.dst, 7, ones)
+    except ValueError:
+        return
+    raise AssertionError("mode 7 accepted")
+
+
+def pin_normalized_layer_gradient():
+    """f(w) = <dY, A_norm(w) X>: central differences in w equal normalize(edge_grad)."""
+    wl = synth.random_graph(11, 50, 3, 271)
+    dy64 = wl.dy.astype(np.float64)
+    for mode in (oracle.NORM_MEAN, oracle.NORM_SYM):
+        def f(w):
+            wn = oracle.edge_normalize(wl.n, wl.src, wl.dst, mode, w).astype(np.float32)
+            y, _ = oracle.forward(wl.n, wl.src, wl.dst, wn, wl.x)
+            return float((dy64 * y).sum())
+        dwp, _ = oracle.edge_grad(wl.src, wl.dst, wl.x, wl.dy)
+        dw = oracle.edge_normalize(wl.n, wl.src, wl.dst, mode, dwp.astype(np.float32))
+        for j in range(wl.e):
+            wp, wm = wl.w.copy(), wl.w.copy()
+            wp[j] += np.float32(0.25)
+            wm[j] -= np.float32(0.25)
+            fd = (f(wp) - f(wm)) / (float(wp[j]) - float(wm[j]))
+            assert abs(fd - dw[j]) <= 1e-5 * (1 + abs(dw[j])), (mode, j, fd, dw[j])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -39,6 +39,12 @@ MUTANTS = {
                                  "        alpha[j] = exp((double)s[j] - row_max[dst[j]]) / row_sum[dst[j] > 0 ? dst[j] - 1 : 0];"),
     "softmax_backward_sign": ("        ds[j] = (double)alpha[j] * ((double)dalpha[j] - row_dot[dst[j]]);",
                               "        ds[j] = (double)alpha[j] * ((double)dalpha[j] + row_dot[dst[j]]);"),
+    "normalize_mean_by_out_degree": ("            out[j] = (double)in[j] / din[dst[j]];",
+                                     "            out[j] = (double)in[j] / dout[dst[j]];"),
+    "normalize_sym_squared": ("            out[j] = (double)in[j] / sqrt(dout[src[j]] * din[dst[j]]);",
+                              "            out[j] = (double)in[j] / (dout[src[j]] * din[dst[j]]);"),
+    "normalize_sym_swapped_ends": ("            out[j] = (double)in[j] / sqrt(dout[src[j]] * din[dst[j]]);",
+                                   "            out[j] = (double)in[j] / sqrt(dout[dst[j]] * din[src[j]]);"),
     "softmax_backward_row_dot_unweighted": ("        row_dot[dst[j]] += (double)alpha[j] * (double)dalpha[j];",
                                             "        row_dot[dst[j]] += (double)dalpha[j];"),
 }

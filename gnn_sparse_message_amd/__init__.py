@@ -13,6 +13,7 @@ turns status codes into exceptions.
     dX, dw = mp_spmm_dx_edge_grad(g, w, X, dY)     # both gradients in one pass
     a, m, z = mp_edge_softmax(g, s)                # softmax of edge scores per destination
     ds, t = mp_edge_softmax_backward(g, a, da)     # its backward
+    wn = mp_edge_normalize(g, MP_NORM_SYM, w)      # w / sqrt(deg_out(src) deg_in(dst))
 
 (tinymesh "Weighted aggregation experiment": "Decision", "Edge order is
 explicit".)  The library must be built (``python -m gnn_sparse_message_amd._build``
@@ -28,7 +29,8 @@ import torch  # noqa: F401  -- loaded first so libmp.so binds to torch's HIP run
 __all__ = [
     "Graph", "MpError", "mp_graph_build", "mp_graph_build_workspace_size", "mp_spmm_fwd",
     "mp_spmm_dx", "mp_edge_grad_dw", "mp_spmm_dx_edge_grad", "mp_edge_softmax",
-    "mp_edge_softmax_backward", "mp_status_string", "mp_version", "library_path",
+    "mp_edge_softmax_backward", "mp_edge_normalize", "MP_NORM_MEAN", "MP_NORM_SYM",
+    "mp_status_string", "mp_version", "library_path",
     "NUM_CLASSES",
 ]
 
@@ -39,6 +41,7 @@ MP_OK = 0
 MP_ERR_NULL, MP_ERR_SHAPE, MP_ERR_DTYPE, MP_ERR_DEVICE, MP_ERR_INDEX = -1, -2, -3, -4, -5
 MP_ERR_ALIAS, MP_ERR_ALIGN, MP_ERR_WORKSPACE, MP_ERR_GRAPH, MP_ERR_HIP = -6, -7, -8, -9, -10
 MP_I32, MP_I64, MP_F32, MP_BF16 = 1, 2, 3, 4
+MP_NORM_MEAN, MP_NORM_SYM = 1, 2
 NUM_CLASSES = 33
 
 _DTYPE = {torch.int32: MP_I32, torch.int64: MP_I64, torch.float32: MP_F32,
@@ -101,6 +104,7 @@ def _load():
         "mp_spmm_dx_edge_grad": (i32, [gp, vp, vp, vp, i32, i64, vp, vp, vp]),
         "mp_edge_softmax": (i32, [gp, vp, vp, vp, vp, vp]),
         "mp_edge_softmax_backward": (i32, [gp, vp, vp, vp, vp, vp]),
+        "mp_edge_normalize": (i32, [gp, i32, vp, vp, vp]),
         "mp_status_string": (ctypes.c_char_p, [i32]),
         "mp_last_error_detail": (ctypes.c_char_p, []),
         "mp_version": (i32, []),
@@ -341,3 +345,15 @@ def mp_edge_softmax_backward(g: Graph, alpha, dalpha, out_dscores=None, out_row_
                                          _ptr(ds) if g.num_edges else None, _ptr(rdot),
                                          _stream(alpha)), "mp_edge_softmax_backward")
     return ds, rdot
+
+
+def mp_edge_normalize(g: Graph, mode: int, values, out=None):
+    """values / deg_in(dst) (MP_NORM_MEAN) or / sqrt(deg_out(src) deg_in(dst))
+    (MP_NORM_SYM), float32 [E] in COO order; `out` may be `values` itself."""
+    _edge_f32("values", values, g)
+    res = _out(out, (g.num_edges,), values)
+    _check(_lib.mp_edge_normalize(ctypes.byref(g._desc), int(mode),
+                                  _ptr(values) if g.num_edges else None,
+                                  _ptr(res) if g.num_edges else None, _stream(values)),
+           "mp_edge_normalize")
+    return res

@@ -361,6 +361,30 @@ mp_status mp_edge_softmax_backward(const mp_graph *g, const float *alpha, const 
                                      static_cast<hipStream_t>(stream));
 }
 
+mp_status mp_edge_normalize(const mp_graph *g, int32_t mode, const float *in, float *out,
+                            void *stream) {
+    mp_status st = check_graph(g);
+    if (st != MP_OK) return st;
+    if (mode != MP_NORM_MEAN && mode != MP_NORM_SYM)
+        return fail(MP_ERR_DTYPE, "mp_edge_normalize: unknown mode %d", (int)mode);
+    const int64_t e = g->num_edges;
+    if (e == 0) return MP_OK;
+    if (!in || !out) return fail(MP_ERR_NULL, "mp_edge_normalize: in or out is NULL");
+    if (!aligned(in, 4) || !aligned(out, 4))
+        return fail(MP_ERR_ALIGN, "mp_edge_normalize: in/out not aligned to 4 bytes");
+    if ((st = check_device(in, "in")) != MP_OK) return st;
+    if ((st = check_device(out, "out")) != MP_OK) return st;
+    const Range ro = range(out, e, 4, "out"), ri = range(in, e, 4, "in");
+    if (ro.lo != ri.lo && overlap(ro, ri))
+        return fail(MP_ERR_ALIAS, "mp_edge_normalize: out partially overlaps in");
+    Range others[12];
+    const int k = graph_ranges(g, others);
+    for (int i = 0; i < k; ++i)
+        if (overlap(ro, others[i]))
+            return fail(MP_ERR_ALIAS, "mp_edge_normalize: out overlaps %s", others[i].name);
+    return edge_normalize_run(g, mode, in, out, static_cast<hipStream_t>(stream));
+}
+
 const char *mp_status_string(mp_status s) {
     switch (s) {
         case MP_OK: return "MP_OK";

@@ -74,4 +74,8 @@ mp_status edge_softmax_run(const mp_graph *g, const float *s, float *alpha, floa
 mp_status edge_softmax_backward_run(const mp_graph *g, const float *alpha, const float *dalpha,
                                     float *ds, float *row_dot, hipStream_t stream);
 
+// ---------------------------------------------------------------- degree normalisation
+mp_status edge_normalize_run(const mp_graph *g, int mode, const float *in, float *out,
+                             hipStream_t stream);
+
 }  // namespace mp

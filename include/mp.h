@@ -220,6 +220,28 @@ mp_status mp_edge_softmax(const mp_graph *g, const float *scores, float *alpha, 
 mp_status mp_edge_softmax_backward(const mp_graph *g, const float *alpha, const float *dalpha,
                                    float *dscores, float *row_dot, void *stream);
 
+/* Normalisation modes for mp_edge_normalize. */
+#define MP_NORM_MEAN 1
+#define MP_NORM_SYM  2
+
+/*
+ * Degree normalisation of per-edge values, in COO order, for mean and
+ * symmetric-normalised aggregation ("PyTorch Geometric: one abstraction, the
+ * whole GNN literature", Step 3: GCN's normalised adjacency and SAGE's mean,
+ * each followed by one SpMM).  Degrees are edge counts taken from the two CSR
+ * row pointers (duplicates and self-loops counted):
+ *   MP_NORM_MEAN:  out_e = in_e / deg_in(dst_e)
+ *   MP_NORM_SYM:   out_e = in_e / sqrt(deg_out(src_e) * deg_in(dst_e))
+ * Forward: mp_spmm_fwd(g, normalize(w), X).  Backward: dX through the same
+ * normalised weights, and the weight gradient is normalize(dw') where dw' is
+ * the edge gradient (the factor is constant in w).  fp32 in and out; the
+ * factor is formed in double and rounded once.  `out` may equal `in` (the map
+ * is elementwise) but must not overlap it otherwise, nor the graph arrays.
+ *   in, out  [E] float32, COO order.   mode  MP_NORM_MEAN or MP_NORM_SYM.
+ */
+mp_status mp_edge_normalize(const mp_graph *g, int32_t mode, const float *in, float *out,
+                            void *stream);
+
 /* Static text for a status code. */
 const char *mp_status_string(mp_status status);
 

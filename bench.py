@@ -191,9 +191,12 @@ def main():
     rsum = torch.empty_like(rmax)
     dscores = torch.empty_like(w)
     rdot = torch.empty_like(rmax)
+    wn = torch.empty_like(w)
     for name, fn in (("edge_softmax", lambda: mp.mp_edge_softmax(g, w, alpha, rmax, rsum)),
                      ("edge_softmax_backward",
-                      lambda: mp.mp_edge_softmax_backward(g, alpha, dw, dscores, rdot))):
+                      lambda: mp.mp_edge_softmax_backward(g, alpha, dw, dscores, rdot)),
+                     ("edge_normalize_sym",
+                      lambda: mp.mp_edge_normalize(g, mp.MP_NORM_SYM, w, out=wn))):
         fn()
         ts = []
         for _ in range(5):
@@ -222,6 +225,8 @@ def main():
     # order + alpha + dalpha, the edge pass dst + alpha + dalpha and writes ds.
     bytes_["edge_softmax"] = 20 * e + 24 * n
     bytes_["edge_softmax_backward"] = 28 * e + 16 * n
+    # symmetric normalisation: in, out, src, dst per edge; both row pointers once.
+    bytes_["edge_normalize_sym"] = 16 * e + 8 * (n + 1)
     ms_step = t_total / args.steps * 1e3
 
     def rate(nbytes, ms):

@@ -57,15 +57,22 @@ struct KeysFromDegree {
 };
 
 // ------------------------------------------------------------------ wave / block helpers
-// Mask of the valid lanes of this wave whose digit equals ours.
-__device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid, int bits) {
-    uint64_t m = __builtin_amdgcn_ballot_w64(valid);
-    for (int b = 0; b < bits; ++b) {
-        const bool bit = (d >> b) & 1u;
-        const uint64_t bb = __builtin_amdgcn_ballot_w64(bit);
-        m &= bit ? bb : ~bb;
+// Mask of the valid lanes of this wave whose digit equals ours.  One ballot per
+// digit bit (digits are masked, so bits above the pass width are zero in every
+// lane and leave the mask unchanged); each half of the mask keeps the lanes
+// whose bit agrees with ours, m &= ~(ballot ^ f) with f = 0 or ~0 from our bit,
+// as one three-input bit operation (truth table 0x90: a & (b == c)).
+__device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
+    const uint64_t v = __builtin_amdgcn_ballot_w64(valid);
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+#pragma unroll
+    for (int b = 0; b < kDigitBits; ++b) {
+        const uint32_t f = (uint32_t)__builtin_amdgcn_sbfe((int)d, b, 1);
+        const uint64_t bb = __builtin_amdgcn_ballot_w64(f != 0u);
+        lo = __builtin_amdgcn_bitop3_b32(lo, (uint32_t)bb, f, 0x90);
+        hi = __builtin_amdgcn_bitop3_b32(hi, (uint32_t)(bb >> 32), f, 0x90);
     }
-    return m;
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // Exclusive prefix sum over the 256 threads of a block; *total receives the sum.
@@ -156,7 +163,7 @@ __global__ __launch_bounds__(kBlock) void rs_upsweep(KeySrc keys, int64_t count,
     for (int r = 0; r < kItems; ++r) {
         const bool valid = li0 + r * kWave < lim;
         const uint32_t d = (k[r] >> shift) & mask;
-        const uint64_t m = match_digit(d, valid, bits);
+        const uint64_t m = match_digit(d, valid);
         // One leader per distinct digit updates this wave's private counter.
         if (valid && __builtin_ctzll(m) == lane) s_cnt[wv][d] += (uint32_t)__popcll(m);
     }
@@ -243,7 +250,7 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(KeySrc keys, Payload pl, 
     for (int r = 0; r < kItems; ++r) {
         const bool valid = li0 + r * kWave < lim;
         const uint32_t d = (k[r] >> shift) & mask;
-        const uint64_t m = match_digit(d, valid, bits);
+        const uint64_t m = match_digit(d, valid);
         const uint32_t before = s_cnt[wv][d];
         pos[r] = before + (uint32_t)__popcll(m & lanes_below);
         if (valid && __builtin_ctzll(m) == lane) s_cnt[wv][d] = before + (uint32_t)__popcll(m);

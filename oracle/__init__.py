@@ -51,6 +51,12 @@ def _bind(lib):
         "oracle_edge_softmax": (None, [i64, i64, vp, vp, vp, vp, vp]),
         "oracle_edge_softmax_backward": (None, [i64, i64, vp, vp, vp, vp, vp, vp]),
         "oracle_edge_normalize": (ctypes.c_int, [i64, i64, vp, vp, ctypes.c_int, vp, vp]),
+        "oracle_forward_heads": (ctypes.c_int, [i64, i64, i64, i64, vp, vp, vp, vp, i64, vp,
+                                                vp, vp]),
+        "oracle_input_grad_heads": (ctypes.c_int, [i64, i64, i64, i64, vp, vp, vp, vp, i64, vp,
+                                                   vp, vp]),
+        "oracle_edge_grad_heads": (ctypes.c_int, [i64, i64, i64, vp, vp, vp, vp, i64, vp, vp,
+                                                  vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -229,3 +235,69 @@ def edge_normalize(n: int, src, dst, mode: int, values):
     if rc != 0:
         raise ValueError(f"unknown normalisation mode {mode}")
     return out
+
+
+def _heads_w(w, e):
+    w = _f32(w)
+    if w.ndim != 2 or w.shape[0] != e:
+        raise ValueError("multi-head weights must be [e, k]")
+    return np.ascontiguousarray(w), w.shape[1]
+
+
+def _rows_arg(rows):
+    if rows is None:
+        return None, 0, None
+    rows = _i64(rows)
+    return rows, rows.shape[0], _p(rows)
+
+
+def forward_heads(n: int, src, dst, w, x, rows=None):
+    """Multi-head Y: w is [e, k] (one weight per edge and head), x is [n, h] with
+    h = k * (h/k); head q of Y[i] sums w[e, q] * X[src_e] over head q's columns.
+    ``rows`` restricts the output to those rows.  Returns (Y, S) in float64."""
+    src, dst, x = _i64(src), _i64(dst), _f32(x)
+    w, k = _heads_w(w, src.shape[0])
+    h = x.shape[1]
+    rows, nr, prow = _rows_arg(rows)
+    y = np.empty((nr if rows is not None else n, h), np.float64)
+    s = np.empty_like(y)
+    rc = _load().oracle_forward_heads(n, src.shape[0], h, k, _p(src), _p(dst), _p(w), _p(x),
+                                      nr, prow, _p(y), _p(s))
+    if rc == -1:
+        raise ValueError("feature width is not a multiple of the head count")
+    if rc != 0:
+        raise MemoryError("oracle_forward_heads")
+    return y, s
+
+
+def input_grad_heads(n: int, src, dst, w, dy, rows=None):
+    """Multi-head dX (the transpose of forward_heads); (dX, S) in float64."""
+    src, dst, dy = _i64(src), _i64(dst), _f32(dy)
+    w, k = _heads_w(w, src.shape[0])
+    h = dy.shape[1]
+    rows, nr, prow = _rows_arg(rows)
+    dx = np.empty((nr if rows is not None else n, h), np.float64)
+    s = np.empty_like(dx)
+    rc = _load().oracle_input_grad_heads(n, src.shape[0], h, k, _p(src), _p(dst), _p(w),
+                                         _p(dy), nr, prow, _p(dx), _p(s))
+    if rc == -1:
+        raise ValueError("feature width is not a multiple of the head count")
+    if rc != 0:
+        raise MemoryError("oracle_input_grad_heads")
+    return dx, s
+
+
+def edge_grad_heads(src, dst, x, dy, k: int, edges=None):
+    """Multi-head dw[e, q] = <X[src_e], dY[dst_e]> over head q's columns; [e, k]
+    (or [len(edges), k]) float64, with S."""
+    src, dst, x, dy = _i64(src), _i64(dst), _f32(x), _f32(dy)
+    h = x.shape[1]
+    edges, ne, pe = _rows_arg(edges)
+    count = ne if edges is not None else src.shape[0]
+    dw = np.empty((count, k), np.float64)
+    s = np.empty_like(dw)
+    rc = _load().oracle_edge_grad_heads(src.shape[0], h, k, _p(src), _p(dst), _p(x), _p(dy),
+                                        ne, pe, _p(dw), _p(s))
+    if rc == -1:
+        raise ValueError("feature width is not a multiple of the head count")
+    return dw, s

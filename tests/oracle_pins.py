@@ -524,4 +524,126 @@ def pin_normalized_layer_gradient():
             assert abs(fd - dw[j]) <= 1e-5 * (1 + abs(dw[j])), (mode, j, fd, dw[j])
 
 
+# --------------------------------------------------------------------------- multi-head weights
+
+def _tiny_head_graphs(count, seed):
+    rng = np.random.default_rng(seed)
+    for _ in range(count):
+        n = int(rng.integers(1, 8))
+        e = int(rng.integers(0, 20))
+        k = int(rng.integers(1, 5))
+        hh = int(rng.integers(1, 4))
+        src = rng.integers(0, n, e)
+        dst = rng.integers(0, n, e)
+        w = rng.uniform(-2, 2, (e, k)).astype(np.float32)
+        x = rng.standard_normal((n, k * hh)).astype(np.float32)
+        dy = rng.standard_normal((n, k * hh)).astype(np.float32)
+        yield n, src, dst, w, x, dy, k, hh
+
+
+def pin_heads_dense_bruteforce():
+    """Head q: Y_q = A_q X_q, dX_q = A_q^T dY_q, dw[e, q] = (dY_q X_q^T)[dst_e, src_e],
+    with A_q the dense matrix of the weights w[:, q] and X_q the head's columns."""
+    for n, src, dst, w, x, dy, k, hh in _tiny_head_graphs(400, 301):
+        y, sy = oracle.forward_heads(n, src, dst, w, x)
+        dx, sdx = oracle.input_grad_heads(n, src, dst, w, dy)
+        dw, sdw = oracle.edge_grad_heads(src, dst, x, dy, k)
+        assert dw.shape == (len(src), k)
+        for q in range(k):
+            cols = slice(q * hh, (q + 1) * hh)
+            a = _dense(n, src, dst, w[:, q])
+            aa = _dense_abs(n, src, dst, w[:, q])
+            xq, dyq = x[:, cols].astype(np.float64), dy[:, cols].astype(np.float64)
+            np.testing.assert_allclose(y[:, cols], a @ xq, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(dx[:, cols], a.T @ dyq, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(sy[:, cols], aa @ np.abs(xq), rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(sdx[:, cols], aa.T @ np.abs(dyq), rtol=1e-12, atol=1e-12)
+            g = dyq @ xq.T
+            ga = np.abs(dyq) @ np.abs(xq).T
+            if len(src):
+                np.testing.assert_allclose(dw[:, q], g[dst, src], rtol=1e-12, atol=1e-12)
+                np.testing.assert_allclose(sdw[:, q], ga[dst, src], rtol=1e-12, atol=1e-12)
+
+
+def pin_heads_scipy_midsize():
+    import scipy.sparse as sp
+    for seed, (n, e, k, hh) in enumerate([(300, 4000, 4, 8), (1000, 9000, 3, 5)]):
+        wl = synth.random_graph(n, e, k * hh, 310 + seed)
+        w = np.random.default_rng(seed).standard_normal((e, k)).astype(np.float32)
+        y, _ = oracle.forward_heads(n, wl.src, wl.dst, w, wl.x)
+        dx, _ = oracle.input_grad_heads(n, wl.src, wl.dst, w, wl.dy)
+        dw, _ = oracle.edge_grad_heads(wl.src, wl.dst, wl.x, wl.dy, k)
+        for q in range(k):
+            cols = slice(q * hh, (q + 1) * hh)
+            a = sp.coo_matrix((w[:, q].astype(np.float64), (wl.dst, wl.src)), shape=(n, n)).tocsr()
+            np.testing.assert_allclose(y[:, cols], a @ wl.x[:, cols].astype(np.float64),
+                                       rtol=1e-10, atol=1e-10)
+            np.testing.assert_allclose(dx[:, cols], a.T @ wl.dy[:, cols].astype(np.float64),
+                                       rtol=1e-10, atol=1e-10)
+            ref = np.einsum("eh,eh->e", wl.x[wl.src][:, cols].astype(np.float64),
+                            wl.dy[wl.dst][:, cols].astype(np.float64))
+            np.testing.assert_allclose(dw[:, q], ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_heads_laws():
+    """Adjoint identity <dY, Y> = <X, dX> = sum w * dw; the per-head edge gradients
+    add up to the single-head one; equal weights in every head give the scalar
+    aggregation; central differences in w[e, q] (the function is linear in w)."""
+    wl = synth.random_graph(40, 300, 12, 321)
+    k = 4
+    w = np.random.default_rng(5).standard_normal((wl.e, k)).astype(np.float32)
+    y, _ = oracle.forward_heads(wl.n, wl.src, wl.dst, w, wl.x)
+    dx, _ = oracle.input_grad_heads(wl.n, wl.src, wl.dst, w, wl.dy)
+    dw, _ = oracle.edge_grad_heads(wl.src, wl.dst, wl.x, wl.dy, k)
+    x64, dy64 = wl.x.astype(np.float64), wl.dy.astype(np.float64)
+    a, b, c = (dy64 * y).sum(), (x64 * dx).sum(), (w.astype(np.float64) * dw).sum()
+    np.testing.assert_allclose([b, c], [a, a], rtol=1e-11)
+    dw1, _ = oracle.edge_grad(wl.src, wl.dst, wl.x, wl.dy)
+    np.testing.assert_allclose(dw.sum(axis=1), dw1, rtol=1e-11, atol=1e-11)
+    same = np.repeat(wl.w[:, None], k, axis=1)
+    ys, _ = oracle.forward_heads(wl.n, wl.src, wl.dst, same, wl.x)
+    y1, _ = oracle.forward(wl.n, wl.src, wl.dst, wl.w, wl.x)
+    np.testing.assert_allclose(ys, y1, rtol=1e-12, atol=1e-12)
+    small = synth.random_graph(6, 20, 6, 322)
+    ws = np.random.default_rng(6).standard_normal((small.e, 3)).astype(np.float32)
+    dws, _ = oracle.edge_grad_heads(small.src, small.dst, small.x, small.dy, 3)
+
+    def f(wt):
+        yy, _ = oracle.forward_heads(small.n, small.src, small.dst, wt, small.x)
+        return float((small.dy.astype(np.float64) * yy).sum())
+    for j in range(small.e):
+        for q in range(3):
+            wp, wm = ws.copy(), ws.copy()
+            wp[j, q] += np.float32(0.5)
+            wm[j, q] -= np.float32(0.5)
+            fd = (f(wp) - f(wm)) / (float(wp[j, q]) - float(wm[j, q]))
+            assert abs(fd - dws[j, q]) <= 1e-9 * (1 + abs(dws[j, q])), (j, q, fd, dws[j, q])
+
+
+def pin_heads_samples_and_rejection():
+    """Sampled rows / edges equal the full outputs; a width that is not a multiple
+    of the head count is rejected."""
+    wl = synth.random_graph(500, 6000, 16, 331)
+    w = np.random.default_rng(7).standard_normal((wl.e, 2)).astype(np.float32)
+    rows = np.array([0, 7, 499, 123, 250])
+    y, sy = oracle.forward_heads(wl.n, wl.src, wl.dst, w, wl.x)
+    yr, syr = oracle.forward_heads(wl.n, wl.src, wl.dst, w, wl.x, rows=rows)
+    assert np.array_equal(yr, y[rows]) and np.array_equal(syr, sy[rows])
+    dx, _ = oracle.input_grad_heads(wl.n, wl.src, wl.dst, w, wl.dy)
+    dxr, _ = oracle.input_grad_heads(wl.n, wl.src, wl.dst, w, wl.dy, rows=rows)
+    assert np.array_equal(dxr, dx[rows])
+    dw, _ = oracle.edge_grad_heads(wl.src, wl.dst, wl.x, wl.dy, 2)
+    edges = np.array([5, 0, 5999, 42])
+    dwe, _ = oracle.edge_grad_heads(wl.src, wl.dst, wl.x, wl.dy, 2, edges=edges)
+    assert np.array_equal(dwe, dw[edges])
+    for call in (lambda: oracle.forward_heads(wl.n, wl.src, wl.dst,
+                                              np.ones((wl.e, 3), np.float32), wl.x),
+                 lambda: oracle.edge_grad_heads(wl.src, wl.dst, wl.x, wl.dy, 3)):
+        try:
+            call()
+        except ValueError:
+            continue
+        raise AssertionError("width 16 accepted with 3 heads")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -45,6 +45,16 @@ MUTANTS = {
                               "            out[j] = (double)in[j] / (dout[src[j]] * din[dst[j]]);"),
     "normalize_sym_swapped_ends": ("            out[j] = (double)in[j] / sqrt(dout[src[j]] * din[dst[j]]);",
                                    "            out[j] = (double)in[j] / sqrt(dout[dst[j]] * din[src[j]]);"),
+    "heads_weight_head_major": ("double t = (double)w[j * k + c / hh] * (double)in[other[j] * h + c];",
+                                "double t = (double)w[(c / hh) * e + j] * (double)in[other[j] * h + c];"),
+    "heads_interleaved_columns": ("double t = (double)w[j * k + c / hh] * (double)in[other[j] * h + c];",
+                                  "double t = (double)w[j * k + c % k] * (double)in[other[j] * h + c];"),
+    "heads_forward_roles_swapped": ("return heads_aggregate(n, e, h, k, dst, src, w, x, nr, rows, y, s);",
+                                    "return heads_aggregate(n, e, h, k, src, dst, w, x, nr, rows, y, s);"),
+    "heads_edge_grad_strided": ("for (c = q * hh; c < (q + 1) * hh; c++) {",
+                                "for (c = q; c < h; c += k) {"),
+    "heads_edge_grad_transposed_out": ("            dw[i * k + q] = acc;",
+                                       "            dw[q * count + i] = acc;"),
     "softmax_backward_row_dot_unweighted": ("        row_dot[dst[j]] += (double)alpha[j] * (double)dalpha[j];",
                                             "        row_dot[dst[j]] += (double)dalpha[j];"),
 }

@@ -28,7 +28,8 @@ import torch  # noqa: F401  -- loaded first so libmp.so binds to torch's HIP run
 
 __all__ = [
     "Graph", "MpError", "mp_graph_build", "mp_graph_build_workspace_size", "mp_spmm_fwd",
-    "mp_spmm_dx", "mp_edge_grad_dw", "mp_spmm_dx_edge_grad", "mp_edge_softmax",
+    "mp_spmm_dx", "mp_edge_grad_dw", "mp_spmm_dx_edge_grad", "mp_spmm_fwd_heads",
+    "mp_spmm_dx_heads", "mp_edge_grad_dw_heads", "mp_spmm_dx_edge_grad_heads", "mp_edge_softmax",
     "mp_edge_softmax_backward", "mp_edge_normalize", "MP_NORM_MEAN", "MP_NORM_SYM",
     "mp_status_string", "mp_version", "library_path",
     "NUM_CLASSES",
@@ -102,6 +103,10 @@ def _load():
         "mp_spmm_dx": (i32, [gp, vp, vp, i32, i64, vp, vp]),
         "mp_edge_grad_dw": (i32, [gp, vp, vp, i32, i64, vp, vp]),
         "mp_spmm_dx_edge_grad": (i32, [gp, vp, vp, vp, i32, i64, vp, vp, vp]),
+        "mp_spmm_fwd_heads": (i32, [gp, vp, i64, vp, i32, i64, vp, vp]),
+        "mp_spmm_dx_heads": (i32, [gp, vp, i64, vp, i32, i64, vp, vp]),
+        "mp_edge_grad_dw_heads": (i32, [gp, vp, vp, i32, i64, i64, vp, vp]),
+        "mp_spmm_dx_edge_grad_heads": (i32, [gp, vp, i64, vp, vp, i32, i64, vp, vp, vp]),
         "mp_edge_softmax": (i32, [gp, vp, vp, vp, vp, vp]),
         "mp_edge_softmax_backward": (i32, [gp, vp, vp, vp, vp, vp]),
         "mp_edge_normalize": (i32, [gp, i32, vp, vp, vp]),
@@ -309,6 +314,73 @@ def mp_spmm_dx_edge_grad(g: Graph, w, x, dy, out_dx=None, out_dw=None):
                                      _ptr(x), _ptr(dy), code, h, _ptr(dx),
                                      _ptr(dw) if g.num_edges else None, _stream(dy)),
            "mp_spmm_dx_edge_grad")
+    return dx, dw
+
+
+def _head_weights(t, g: Graph, h: int) -> int:
+    """Check w as [E, K] float32 (K heads dividing the feature width h); returns K."""
+    _need_tensor("w", t)
+    if t.dtype != torch.float32:
+        raise TypeError(f"w must be float32, got {t.dtype}")
+    if t.dim() != 2 or t.shape[0] != g.num_edges:
+        raise ValueError(f"w must have shape [{g.num_edges}, K], got {tuple(t.shape)}")
+    k = int(t.shape[1])
+    if k < 1 or h % k != 0:
+        raise ValueError(f"{k} heads do not divide the feature width {h}")
+    return k
+
+
+def mp_spmm_fwd_heads(g: Graph, w, x, out=None):
+    """Multi-head Y: w is [E, K]; head q of Y (columns q*H/K .. (q+1)*H/K - 1)
+    aggregates head q of X with weights w[:, q].  float32 [N, H]."""
+    h = _features("x", x, g)
+    k = _head_weights(w, g, h)
+    y = _out(out, (g.num_nodes, h), x)
+    _check(_lib.mp_spmm_fwd_heads(ctypes.byref(g._desc), _ptr(w) if g.num_edges else None, k,
+                                  _ptr(x), _code(x), h, _ptr(y), _stream(x)),
+           "mp_spmm_fwd_heads")
+    return y
+
+
+def mp_spmm_dx_heads(g: Graph, w, dy, out=None):
+    """Multi-head dX = per-head A_w^T dY, float32 [N, H]."""
+    h = _features("dy", dy, g)
+    k = _head_weights(w, g, h)
+    dx = _out(out, (g.num_nodes, h), dy)
+    _check(_lib.mp_spmm_dx_heads(ctypes.byref(g._desc), _ptr(w) if g.num_edges else None, k,
+                                 _ptr(dy), _code(dy), h, _ptr(dx), _stream(dy)),
+           "mp_spmm_dx_heads")
+    return dx
+
+
+def mp_edge_grad_dw_heads(g: Graph, x, dy, heads: int, out=None):
+    """dw[e, q] = <X[src_e], dY[dst_e]> over head q's columns, float32 [E, K]."""
+    h = _features("x", x, g)
+    if _features("dy", dy, g) != h:
+        raise ValueError("x and dy must have the same feature width")
+    code = _code(x) if x.dtype == dy.dtype else 0
+    dw = _out(out, (g.num_edges, int(heads)), x)
+    _check(_lib.mp_edge_grad_dw_heads(ctypes.byref(g._desc), _ptr(x), _ptr(dy), code, h,
+                                      int(heads), _ptr(dw) if g.num_edges else None,
+                                      _stream(x)), "mp_edge_grad_dw_heads")
+    return dw
+
+
+def mp_spmm_dx_edge_grad_heads(g: Graph, w, x, dy, out_dx=None, out_dw=None):
+    """Multi-head (dX, dw[E, K]) in one pass; equal to mp_spmm_dx_heads and
+    mp_edge_grad_dw_heads."""
+    h = _features("x", x, g)
+    if _features("dy", dy, g) != h:
+        raise ValueError("x and dy must have the same feature width")
+    k = _head_weights(w, g, h)
+    code = _code(dy) if x.dtype == dy.dtype else 0
+    dx = _out(out_dx, (g.num_nodes, h), dy)
+    dw = _out(out_dw, (g.num_edges, k), dy)
+    _check(_lib.mp_spmm_dx_edge_grad_heads(ctypes.byref(g._desc),
+                                           _ptr(w) if g.num_edges else None, k, _ptr(x),
+                                           _ptr(dy), code, h, _ptr(dx),
+                                           _ptr(dw) if g.num_edges else None, _stream(dy)),
+           "mp_spmm_dx_edge_grad_heads")
     return dx, dw
 
 

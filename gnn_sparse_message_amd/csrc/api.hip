@@ -112,9 +112,18 @@ mp_status check_h(int64_t n, int64_t h) {
     return MP_OK;
 }
 
-// Shared validation of one aggregation call (forward or input gradient).
-mp_status check_spmm(const mp_graph *g, const float *w, const void *x, mp_dtype dt, int64_t h,
-                     float *y, const char *xname, const char *yname) {
+// Head count: 1 <= heads <= h, heads divides h.
+mp_status check_heads(int64_t h, int64_t heads) {
+    if (heads < 1 || heads > h || h % heads != 0)
+        return fail(MP_ERR_SHAPE, "head count %lld does not divide the feature width %lld",
+                    (long long)heads, (long long)h);
+    return MP_OK;
+}
+
+// Shared validation of one aggregation call (forward or input gradient); w
+// holds `heads` weights per edge.
+mp_status check_spmm(const mp_graph *g, const float *w, int64_t heads, const void *x,
+                     mp_dtype dt, int64_t h, float *y, const char *xname, const char *yname) {
     mp_status st = check_graph(g);
     if (st != MP_OK) return st;
     const int64_t n = g->num_nodes, e = g->num_edges;
@@ -122,6 +131,7 @@ mp_status check_spmm(const mp_graph *g, const float *w, const void *x, mp_dtype 
     if (!y) return fail(MP_ERR_NULL, "%s is NULL", yname);
     if (!w && e > 0) return fail(MP_ERR_NULL, "w is NULL with %lld edges", (long long)e);
     if ((st = check_h(n, h)) != MP_OK) return st;
+    if ((st = check_heads(h, heads)) != MP_OK) return st;
     if (dt != MP_F32 && dt != MP_BF16)
         return fail(MP_ERR_DTYPE, "%s dtype code %d: expected MP_F32 or MP_BF16", xname, (int)dt);
     const size_t xs = dtype_size(dt);
@@ -135,11 +145,94 @@ mp_status check_spmm(const mp_graph *g, const float *w, const void *x, mp_dtype 
     Range others[12];
     int k = graph_ranges(g, others);
     others[k++] = range(x, n * h, xs, xname);
-    others[k++] = range(w, e, 4, "w");
+    others[k++] = range(w, e * heads, 4, "w");
     for (int i = 0; i < k; ++i)
         if (overlap(ry, others[i]))
             return fail(MP_ERR_ALIAS, "%s overlaps %s", yname, others[i].name);
     return MP_OK;
+}
+
+mp_status spmm_fwd_impl(const mp_graph *g, const float *w, int64_t heads, const void *x,
+                        mp_dtype x_dtype, int64_t h, float *y, void *stream) {
+    mp_status st = check_spmm(g, w, heads, x, x_dtype, h, y, "x", "y");
+    if (st != MP_OK) return st;
+    CsrView v{g->rowptr, g->col, g->edge_order, g->row_plan, g->class_count, g->num_nodes,
+              g->num_edges};
+    return spmm_run(v, w, heads, x, x_dtype, h, y, static_cast<hipStream_t>(stream));
+}
+
+mp_status spmm_dx_impl(const mp_graph *g, const float *w, int64_t heads, const void *dy,
+                       mp_dtype dy_dtype, int64_t h, float *dx, void *stream) {
+    mp_status st = check_spmm(g, w, heads, dy, dy_dtype, h, dx, "dy", "dx");
+    if (st != MP_OK) return st;
+    CsrView v{g->rowptr_t, g->col_t, g->transpose_order, g->row_plan_t, g->class_count_t,
+              g->num_nodes, g->num_edges};
+    return spmm_run(v, w, heads, dy, dy_dtype, h, dx, static_cast<hipStream_t>(stream));
+}
+
+mp_status edge_grad_impl(const mp_graph *g, const void *x, const void *dy, mp_dtype dtype,
+                         int64_t h, int64_t heads, float *dw, void *stream) {
+    mp_status st = check_graph(g);
+    if (st != MP_OK) return st;
+    const int64_t n = g->num_nodes, e = g->num_edges;
+    if (!x || !dy) return fail(MP_ERR_NULL, "x or dy is NULL");
+    if (!dw && e > 0) return fail(MP_ERR_NULL, "dw is NULL with %lld edges", (long long)e);
+    if ((st = check_h(n, h)) != MP_OK) return st;
+    if ((st = check_heads(h, heads)) != MP_OK) return st;
+    if (dtype != MP_F32 && dtype != MP_BF16)
+        return fail(MP_ERR_DTYPE, "feature dtype code %d: expected MP_F32 or MP_BF16", (int)dtype);
+    const size_t xs = dtype_size(dtype);
+    if (!aligned(x, xs) || !aligned(dy, xs))
+        return fail(MP_ERR_ALIGN, "x/dy not aligned to %zu bytes", xs);
+    if (dw && !aligned(dw, 4)) return fail(MP_ERR_ALIGN, "dw not aligned to 4 bytes");
+    if ((st = check_device(x, "x")) != MP_OK) return st;
+    if ((st = check_device(dy, "dy")) != MP_OK) return st;
+    if (e == 0) return MP_OK;
+    if ((st = check_device(dw, "dw")) != MP_OK) return st;
+    const Range rdw = range(dw, e * heads, 4, "dw");
+    Range others[12];
+    int k = graph_ranges(g, others);
+    others[k++] = range(x, n * h, xs, "x");
+    others[k++] = range(dy, n * h, xs, "dy");
+    for (int i = 0; i < k; ++i)
+        if (overlap(rdw, others[i])) return fail(MP_ERR_ALIAS, "dw overlaps %s", others[i].name);
+    return sddmm_run(g->src, g->dst, e, x, dy, dtype, h, heads, dw,
+                     static_cast<hipStream_t>(stream));
+}
+
+mp_status dx_edge_grad_impl(const mp_graph *g, const float *w, int64_t heads, const void *x,
+                            const void *dy, mp_dtype dtype, int64_t h, float *dx, float *dw,
+                            void *stream) {
+    mp_status st = check_spmm(g, w, heads, dy, dtype, h, dx, "dy", "dx");
+    if (st != MP_OK) return st;
+    const int64_t n = g->num_nodes, e = g->num_edges;
+    if (!x) return fail(MP_ERR_NULL, "x is NULL");
+    if (!dw && e > 0) return fail(MP_ERR_NULL, "dw is NULL with %lld edges", (long long)e);
+    const size_t xs = dtype_size(dtype);
+    if (!aligned(x, xs)) return fail(MP_ERR_ALIGN, "x not aligned to %zu bytes", xs);
+    if (dw && !aligned(dw, 4)) return fail(MP_ERR_ALIGN, "dw not aligned to 4 bytes");
+    if ((st = check_device(x, "x")) != MP_OK) return st;
+    if (e > 0 && (st = check_device(dw, "dw")) != MP_OK) return st;
+    const Range rdx = range(dx, n * h, 4, "dx"), rdw = range(dw, e * heads, 4, "dw");
+    const Range rx = range(x, n * h, xs, "x");
+    if (overlap(rdx, rx)) return fail(MP_ERR_ALIAS, "dx overlaps x");
+    Range others[13];
+    int k = graph_ranges(g, others);
+    others[k++] = rx;
+    others[k++] = range(dy, n * h, xs, "dy");
+    others[k++] = range(w, e * heads, 4, "w");
+    others[k++] = rdx;
+    for (int i = 0; i < k; ++i)
+        if (overlap(rdw, others[i])) return fail(MP_ERR_ALIAS, "dw overlaps %s", others[i].name);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    CsrView v{g->rowptr_t, g->col_t, g->transpose_order, g->row_plan_t, g->class_count_t,
+              g->num_nodes, g->num_edges};
+    if (spmm_fused_supported(dtype, h, heads, dy, x, dx))
+        return spmm_fused_run(v, w, heads, dy, dtype, h, dx, x, e > 0 ? dw : nullptr, s);
+    // Feature rows wider than one column block: the two kernels back to back.
+    if ((st = spmm_run(v, w, heads, dy, dtype, h, dx, s)) != MP_OK) return st;
+    if (e == 0) return MP_OK;
+    return sddmm_run(g->src, g->dst, e, x, dy, dtype, h, heads, dw, s);
 }
 
 }  // namespace
@@ -225,83 +318,45 @@ mp_status mp_graph_build(const void *src, const void *dst, mp_dtype idx_dtype, i
 
 mp_status mp_spmm_fwd(const mp_graph *g, const float *w, const void *x, mp_dtype x_dtype,
                       int64_t h, float *y, void *stream) {
-    mp_status st = check_spmm(g, w, x, x_dtype, h, y, "x", "y");
-    if (st != MP_OK) return st;
-    CsrView v{g->rowptr, g->col, g->edge_order, g->row_plan, g->class_count, g->num_nodes,
-              g->num_edges};
-    return spmm_run(v, w, x, x_dtype, h, y, static_cast<hipStream_t>(stream));
+    return spmm_fwd_impl(g, w, 1, x, x_dtype, h, y, stream);
 }
 
 mp_status mp_spmm_dx(const mp_graph *g, const float *w, const void *dy, mp_dtype dy_dtype,
                      int64_t h, float *dx, void *stream) {
-    mp_status st = check_spmm(g, w, dy, dy_dtype, h, dx, "dy", "dx");
-    if (st != MP_OK) return st;
-    CsrView v{g->rowptr_t, g->col_t, g->transpose_order, g->row_plan_t, g->class_count_t,
-              g->num_nodes, g->num_edges};
-    return spmm_run(v, w, dy, dy_dtype, h, dx, static_cast<hipStream_t>(stream));
+    return spmm_dx_impl(g, w, 1, dy, dy_dtype, h, dx, stream);
 }
 
 mp_status mp_edge_grad_dw(const mp_graph *g, const void *x, const void *dy, mp_dtype dtype,
                           int64_t h, float *dw, void *stream) {
-    mp_status st = check_graph(g);
-    if (st != MP_OK) return st;
-    const int64_t n = g->num_nodes, e = g->num_edges;
-    if (!x || !dy) return fail(MP_ERR_NULL, "x or dy is NULL");
-    if (!dw && e > 0) return fail(MP_ERR_NULL, "dw is NULL with %lld edges", (long long)e);
-    if ((st = check_h(n, h)) != MP_OK) return st;
-    if (dtype != MP_F32 && dtype != MP_BF16)
-        return fail(MP_ERR_DTYPE, "feature dtype code %d: expected MP_F32 or MP_BF16", (int)dtype);
-    const size_t xs = dtype_size(dtype);
-    if (!aligned(x, xs) || !aligned(dy, xs))
-        return fail(MP_ERR_ALIGN, "x/dy not aligned to %zu bytes", xs);
-    if (dw && !aligned(dw, 4)) return fail(MP_ERR_ALIGN, "dw not aligned to 4 bytes");
-    if ((st = check_device(x, "x")) != MP_OK) return st;
-    if ((st = check_device(dy, "dy")) != MP_OK) return st;
-    if (e == 0) return MP_OK;
-    if ((st = check_device(dw, "dw")) != MP_OK) return st;
-    const Range rdw = range(dw, e, 4, "dw");
-    Range others[12];
-    int k = graph_ranges(g, others);
-    others[k++] = range(x, n * h, xs, "x");
-    others[k++] = range(dy, n * h, xs, "dy");
-    for (int i = 0; i < k; ++i)
-        if (overlap(rdw, others[i])) return fail(MP_ERR_ALIAS, "dw overlaps %s", others[i].name);
-    return sddmm_run(g->src, g->dst, e, x, dy, dtype, h, dw, static_cast<hipStream_t>(stream));
+    return edge_grad_impl(g, x, dy, dtype, h, 1, dw, stream);
 }
 
 mp_status mp_spmm_dx_edge_grad(const mp_graph *g, const float *w, const void *x,
                                const void *dy, mp_dtype dtype, int64_t h, float *dx, float *dw,
                                void *stream) {
-    mp_status st = check_spmm(g, w, dy, dtype, h, dx, "dy", "dx");
-    if (st != MP_OK) return st;
-    const int64_t n = g->num_nodes, e = g->num_edges;
-    if (!x) return fail(MP_ERR_NULL, "x is NULL");
-    if (!dw && e > 0) return fail(MP_ERR_NULL, "dw is NULL with %lld edges", (long long)e);
-    const size_t xs = dtype_size(dtype);
-    if (!aligned(x, xs)) return fail(MP_ERR_ALIGN, "x not aligned to %zu bytes", xs);
-    if (dw && !aligned(dw, 4)) return fail(MP_ERR_ALIGN, "dw not aligned to 4 bytes");
-    if ((st = check_device(x, "x")) != MP_OK) return st;
-    if (e > 0 && (st = check_device(dw, "dw")) != MP_OK) return st;
-    const Range rdx = range(dx, n * h, 4, "dx"), rdw = range(dw, e, 4, "dw");
-    const Range rx = range(x, n * h, xs, "x");
-    if (overlap(rdx, rx)) return fail(MP_ERR_ALIAS, "dx overlaps x");
-    Range others[13];
-    int k = graph_ranges(g, others);
-    others[k++] = rx;
-    others[k++] = range(dy, n * h, xs, "dy");
-    others[k++] = range(w, e, 4, "w");
-    others[k++] = rdx;
-    for (int i = 0; i < k; ++i)
-        if (overlap(rdw, others[i])) return fail(MP_ERR_ALIAS, "dw overlaps %s", others[i].name);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    CsrView v{g->rowptr_t, g->col_t, g->transpose_order, g->row_plan_t, g->class_count_t,
-              g->num_nodes, g->num_edges};
-    if (spmm_fused_supported(dtype, h, dy, x, dx))
-        return spmm_fused_run(v, w, dy, dtype, h, dx, x, e > 0 ? dw : nullptr, s);
-    // Feature rows wider than one column block: the two kernels back to back.
-    if ((st = spmm_run(v, w, dy, dtype, h, dx, s)) != MP_OK) return st;
-    if (e == 0) return MP_OK;
-    return sddmm_run(g->src, g->dst, e, x, dy, dtype, h, dw, s);
+    return dx_edge_grad_impl(g, w, 1, x, dy, dtype, h, dx, dw, stream);
+}
+
+mp_status mp_spmm_fwd_heads(const mp_graph *g, const float *w, int64_t heads, const void *x,
+                            mp_dtype x_dtype, int64_t h, float *y, void *stream) {
+    return spmm_fwd_impl(g, w, heads, x, x_dtype, h, y, stream);
+}
+
+mp_status mp_spmm_dx_heads(const mp_graph *g, const float *w, int64_t heads, const void *dy,
+                           mp_dtype dy_dtype, int64_t h, float *dx, void *stream) {
+    return spmm_dx_impl(g, w, heads, dy, dy_dtype, h, dx, stream);
+}
+
+mp_status mp_edge_grad_dw_heads(const mp_graph *g, const void *x, const void *dy,
+                                mp_dtype dtype, int64_t h, int64_t heads, float *dw,
+                                void *stream) {
+    return edge_grad_impl(g, x, dy, dtype, h, heads, dw, stream);
+}
+
+mp_status mp_spmm_dx_edge_grad_heads(const mp_graph *g, const float *w, int64_t heads,
+                                     const void *x, const void *dy, mp_dtype dtype, int64_t h,
+                                     float *dx, float *dw, void *stream) {
+    return dx_edge_grad_impl(g, w, heads, x, dy, dtype, h, dx, dw, stream);
 }
 
 namespace {

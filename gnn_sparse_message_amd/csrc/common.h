@@ -54,19 +54,26 @@ struct CsrView {
     int64_t n;
     int64_t e;
 };
-mp_status spmm_run(const CsrView &csr, const float *w, const void *x, mp_dtype dt, int64_t h,
-                   float *out, hipStream_t stream);
+// `heads` = K: w holds K weights per edge ([E, K], edge-major) and head q owns
+// columns [q*h/K, (q+1)*h/K) of every row (h is a multiple of K; K = 1 is the
+// scalar case).
+mp_status spmm_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
+                   mp_dtype dt, int64_t h, float *out, hipStream_t stream);
 // The same aggregation over the transpose CSR that also writes, for every edge
-// q of owner row j, dw[order[q]] = <x_own[j, :], x[col[q], :]> (fused backward).
-// Only for feature rows that fit one column block (spmm_fused_supported).
-bool spmm_fused_supported(mp_dtype dt, int64_t h, const void *x, const void *x_own,
-                          const void *out);
-mp_status spmm_fused_run(const CsrView &csr, const float *w, const void *x, mp_dtype dt,
-                         int64_t h, float *out, const void *x_own, float *dw, hipStream_t stream);
+// q of owner row j, dw[order[q]] = <x_own[j, :], x[col[q], :]> (fused backward;
+// per head, dw[order[q] * K + head], when K > 1).  Only for feature rows that
+// fit one column block (spmm_fused_supported).
+bool spmm_fused_supported(mp_dtype dt, int64_t h, int64_t heads, const void *x,
+                          const void *x_own, const void *out);
+mp_status spmm_fused_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
+                         mp_dtype dt, int64_t h, float *out, const void *x_own, float *dw,
+                         hipStream_t stream);
 
 // ---------------------------------------------------------------- SDDMM
+// dw[e * K + q] = <x[src_e], dy[dst_e]> over head q's columns, COO order.
 mp_status sddmm_run(const int32_t *src, const int32_t *dst, int64_t e, const void *x,
-                    const void *dy, mp_dtype dt, int64_t h, float *dw, hipStream_t stream);
+                    const void *dy, mp_dtype dt, int64_t h, int64_t heads, float *dw,
+                    hipStream_t stream);
 
 // ---------------------------------------------------------------- target softmax
 mp_status edge_softmax_run(const mp_graph *g, const float *s, float *alpha, float *row_max,

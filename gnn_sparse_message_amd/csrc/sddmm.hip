@@ -10,6 +10,13 @@
 // group reduces its dot product across its L lanes with xor-permutes, the
 // results are collected so that lane k holds edge k, and the wave writes its
 // 64 values with one coalesced store.  fp32 accumulation; bf16 widened exactly.
+//
+// Multi-head weights (K per edge, head q owning columns [q*H/K, (q+1)*H/K)):
+// the work items are the E*K (edge, head) pairs in dw's own [E, K] order, each
+// a dot product over one head's columns, so the store stays coalesced.  A
+// head's lanes are reduced with an xor butterfly when their count is a power of
+// two (or the whole wave), else in lane order -- the same order as the fused
+// backward, so both give equal dw.
 #include "common.h"
 
 namespace mp {
@@ -60,26 +67,37 @@ struct Feat2<uint16_t, 1> {
     }
 };
 
-template <typename T, int VEC, int L>
+// Items are edges (kHeads = false; hw = h) or (edge, head) pairs, item i being
+// edge i / heads and head i % heads, over hw = h / heads columns.
+template <typename T, int VEC, int L, bool kHeads>
 __global__ __launch_bounds__(kBlock) void sddmm_kernel(const int32_t *__restrict__ src,
                                                        const int32_t *__restrict__ dst,
                                                        const T *__restrict__ X,
                                                        const T *__restrict__ dY,
                                                        float *__restrict__ dw, int64_t e,
-                                                       int64_t h) {
-    constexpr int G = kWave / L;                       // edges per wave step
+                                                       int64_t h, int32_t heads, int32_t hw) {
+    constexpr int G = kWave / L;                       // items per wave step
     const int lane = threadIdx.x & (kWave - 1);
     const int g = lane / L;
     const int sub = lane % L;
-    const int64_t nf = (h + (int64_t)L * VEC - 1) / ((int64_t)L * VEC);   // feature chunks
+    const int64_t nf = (hw + (int64_t)L * VEC - 1) / ((int64_t)L * VEC);  // feature chunks
+    const int seg = hw / VEC;                          // lanes holding one head (multi-head)
+    const bool tree = (seg & (seg - 1)) == 0 || seg >= kWave;
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
     for (int64_t base = ((int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave) * kWave;
          base < e; base += nwaves * kWave) {
         const int64_t me = base + lane;
-        int s = 0, d = 0;
+        int s = 0, d = 0, q = 0;
         if (me < e) {   // streamed once: non-temporal, so L2 keeps the feature rows
-            s = __builtin_nontemporal_load(&src[me]);
-            d = __builtin_nontemporal_load(&dst[me]);
+            if constexpr (kHeads) {
+                const int64_t ed = me / heads;
+                q = (int)(me - ed * heads);
+                s = src[ed];
+                d = dst[ed];
+            } else {
+                s = __builtin_nontemporal_load(&src[me]);
+                d = __builtin_nontemporal_load(&dst[me]);
+            }
         }
         const int n = e - base < kWave ? (int)(e - base) : kWave;
         const int trips = (n + G - 1) / G;
@@ -93,15 +111,16 @@ __global__ __launch_bounds__(kBlock) void sddmm_kernel(const int32_t *__restrict
                 const int sl = k < n ? k : n - 1;
                 const int su = __shfl(s, sl);
                 const int du = __shfl(d, sl);
+                const int64_t col0 = kHeads ? (int64_t)__shfl(q, sl) * hw : 0;
                 // Lane-local dot: an fma chain from zero per chunk (no bare product
                 // that could be contracted into the lane reduction below).
                 float acc = 0.f;
                 if (ok) {
                     for (int64_t f = 0; f < nf; ++f) {
                         const int64_t hoff = (f * L + sub) * VEC;
-                        if (hoff < h) {
-                            const float d = Feat2<T, VEC>::dot(X + (int64_t)su * h + hoff,
-                                                               dY + (int64_t)du * h + hoff);
+                        if (hoff < hw) {
+                            const float d = Feat2<T, VEC>::dot(X + (int64_t)su * h + col0 + hoff,
+                                                               dY + (int64_t)du * h + col0 + hoff);
                             acc = f == 0 ? d : acc + d;
                         }
                     }
@@ -110,8 +129,14 @@ __global__ __launch_bounds__(kBlock) void sddmm_kernel(const int32_t *__restrict
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
+                if (!kHeads || tree) {
 #pragma unroll
-                for (int off = L / 2; off >= 1; off >>= 1) part[u] += __shfl_xor(part[u], off);
+                    for (int off = L / 2; off >= 1; off >>= 1) part[u] += __shfl_xor(part[u], off);
+                } else {   // a head of seg < 64 lanes, seg not a power of two: lane order
+                    float t = __shfl(part[u], g * L);
+                    for (int i = 1; i < seg; ++i) t += __shfl(part[u], g * L + i);
+                    part[u] = t;
+                }
                 // Edge k = g' + (j+u)*G sits in every lane of group g'; lane k collects it.
                 const float got = __shfl(part[u], (lane % G) * L);
                 if (lane / G == j + u) mine = got;
@@ -123,14 +148,21 @@ __global__ __launch_bounds__(kBlock) void sddmm_kernel(const int32_t *__restrict
 
 template <typename T, int VEC, int L>
 mp_status launch(const int32_t *src, const int32_t *dst, int64_t e, const void *x,
-                 const void *dy, int64_t h, float *dw, hipStream_t s) {
+                 const void *dy, int64_t h, int64_t heads, float *dw, hipStream_t s) {
+    const int64_t items = e * heads;
     const int64_t per_block = (int64_t)kWavesPerBlock * kWave;
-    int64_t blocks = (e + per_block - 1) / per_block;
+    int64_t blocks = (items + per_block - 1) / per_block;
     const int64_t cap = 1 << 22;
     if (blocks > cap) blocks = cap;
     if (blocks <= 0) return MP_OK;
-    sddmm_kernel<T, VEC, L><<<(unsigned)blocks, kBlock, 0, s>>>(
-        src, dst, static_cast<const T *>(x), static_cast<const T *>(dy), dw, e, h);
+    const T *xt = static_cast<const T *>(x), *dyt = static_cast<const T *>(dy);
+    const int32_t hw = (int32_t)(h / heads);
+    if (heads > 1)
+        sddmm_kernel<T, VEC, L, true><<<(unsigned)blocks, kBlock, 0, s>>>(
+            src, dst, xt, dyt, dw, items, h, (int32_t)heads, hw);
+    else
+        sddmm_kernel<T, VEC, L, false><<<(unsigned)blocks, kBlock, 0, s>>>(
+            src, dst, xt, dyt, dw, items, h, 1, hw);
     MP_HIP_CHECK(hipGetLastError(), "sddmm launch");
     return MP_OK;
 }
@@ -142,17 +174,18 @@ int lanes_for(int64_t h, int vec) {
     return L;
 }
 
+// Lanes per item come from the columns one item covers (a head's, or the row's).
 template <typename T, int VEC>
 mp_status launch_lanes(const int32_t *src, const int32_t *dst, int64_t e, const void *x,
-                       const void *dy, int64_t h, float *dw, hipStream_t s) {
-    switch (lanes_for(h, VEC)) {
-        case 1: return launch<T, VEC, 1>(src, dst, e, x, dy, h, dw, s);
-        case 2: return launch<T, VEC, 2>(src, dst, e, x, dy, h, dw, s);
-        case 4: return launch<T, VEC, 4>(src, dst, e, x, dy, h, dw, s);
-        case 8: return launch<T, VEC, 8>(src, dst, e, x, dy, h, dw, s);
-        case 16: return launch<T, VEC, 16>(src, dst, e, x, dy, h, dw, s);
-        case 32: return launch<T, VEC, 32>(src, dst, e, x, dy, h, dw, s);
-        default: return launch<T, VEC, 64>(src, dst, e, x, dy, h, dw, s);
+                       const void *dy, int64_t h, int64_t heads, float *dw, hipStream_t s) {
+    switch (lanes_for(h / heads, VEC)) {
+        case 1: return launch<T, VEC, 1>(src, dst, e, x, dy, h, heads, dw, s);
+        case 2: return launch<T, VEC, 2>(src, dst, e, x, dy, h, heads, dw, s);
+        case 4: return launch<T, VEC, 4>(src, dst, e, x, dy, h, heads, dw, s);
+        case 8: return launch<T, VEC, 8>(src, dst, e, x, dy, h, heads, dw, s);
+        case 16: return launch<T, VEC, 16>(src, dst, e, x, dy, h, heads, dw, s);
+        case 32: return launch<T, VEC, 32>(src, dst, e, x, dy, h, heads, dw, s);
+        default: return launch<T, VEC, 64>(src, dst, e, x, dy, h, heads, dw, s);
     }
 }
 
@@ -161,14 +194,18 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 }  // namespace
 
 mp_status sddmm_run(const int32_t *src, const int32_t *dst, int64_t e, const void *x,
-                    const void *dy, mp_dtype dt, int64_t h, float *dw, hipStream_t s) {
+                    const void *dy, mp_dtype dt, int64_t h, int64_t heads, float *dw,
+                    hipStream_t s) {
     const bool vec_ok = aligned16(x) && aligned16(dy);
+    const int64_t hw = h / heads;
     if (dt == MP_F32) {
-        if (vec_ok && h % 4 == 0) return launch_lanes<float, 4>(src, dst, e, x, dy, h, dw, s);
-        return launch_lanes<float, 1>(src, dst, e, x, dy, h, dw, s);
+        if (vec_ok && hw % 4 == 0)
+            return launch_lanes<float, 4>(src, dst, e, x, dy, h, heads, dw, s);
+        return launch_lanes<float, 1>(src, dst, e, x, dy, h, heads, dw, s);
     }
-    if (vec_ok && h % 8 == 0) return launch_lanes<uint16_t, 8>(src, dst, e, x, dy, h, dw, s);
-    return launch_lanes<uint16_t, 1>(src, dst, e, x, dy, h, dw, s);
+    if (vec_ok && hw % 8 == 0)
+        return launch_lanes<uint16_t, 8>(src, dst, e, x, dy, h, heads, dw, s);
+    return launch_lanes<uint16_t, 1>(src, dst, e, x, dy, h, heads, dw, s);
 }
 
 }  // namespace mp

@@ -22,6 +22,13 @@
 // gathers U feature rows at a time (several 16-byte loads in flight per lane).
 // Accumulation is fp32; bf16 inputs are widened exactly.  Feature widths above
 // 64*VEC are covered by column blocks in gridDim.y.
+//
+// Multi-head weights (w is [E, K], head q owning columns [q*H/K, (q+1)*H/K) of
+// every row; the per-head reading of vector edge weights, which tinymesh
+// "Weighted aggregation experiment", "Limits" names as not yet covered): every
+// lane's VEC columns lie in one head, so a lane reads the weight of its own
+// head, w[order[p] * K + q], beside the feature row; the fused backward reduces
+// the edge dot product over the lanes of each head separately.
 #include "common.h"
 
 #include <stdlib.h>
@@ -95,6 +102,22 @@ __device__ __forceinline__ float edge_dot(const float (&xr)[VEC], const float (&
     return s;
 }
 
+// Sum of `part` over the `seg` lanes of one head (aligned runs of seg lanes
+// inside a group; every lane of the run gets the total).  A power-of-two run is
+// reduced with an xor butterfly, any other in lane order; the COO-order
+// multi-head edge-gradient kernel reduces its lanes the same way, so both give
+// equal dw.  `seg` is uniform across the wave.
+__device__ __forceinline__ float head_sum(float part, int lane, int sub, int seg) {
+    if ((seg & (seg - 1)) == 0) {
+        for (int off = seg >> 1; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+        return part;
+    }
+    const int first = lane - sub % seg;
+    float t = __shfl(part, first);
+    for (int i = 1; i < seg; ++i) t += __shfl(part, first + i);
+    return t;
+}
+
 struct SpmmArgs {
     const int32_t *rowptr;
     const int32_t *col;
@@ -106,6 +129,8 @@ struct SpmmArgs {
     const void *x_own;                // fused backward only: X, read at the owner row
     float *dw;                        // fused backward only: edge gradients, COO order
     int64_t h;
+    int32_t heads;                    // K weights per edge (multi-head kernels only)
+    int32_t head_w;                   // H / K columns per head
     int64_t n, e;                     // rows, edges (bounds for the data-dependent indices)
     int32_t n_hub, n_wave, n_group;   // rows of each owner kind, consecutive in the plan
     int32_t blk_hub, blk_wave, blk_group;   // blocks given to each kind (wave and group
@@ -121,10 +146,12 @@ struct SpmmArgs {
 // every gathered dY slice also meets the owner row's X slice `xr`: the group
 // reduces their dot product over its L lanes (same lane order and butterfly as
 // the COO-order edge-gradient kernel) and one lane writes dw[order[p]].
-template <typename T, int VEC, int L, int TL, bool kEdgeGrad>
+// With kHeads every lane reads the weight of its own head, `head`, per edge.
+template <typename T, int VEC, int L, int TL, bool kEdgeGrad, bool kHeads>
 __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int64_t end,
-                                           int64_t stride, int lane, int64_t hoff, bool active,
-                                           const float (&xr)[VEC], float (&acc)[VEC]) {
+                                           int64_t stride, int lane, int64_t hoff, int head,
+                                           bool active, const float (&xr)[VEC],
+                                           float (&acc)[VEC]) {
     constexpr int G = TL / L;                 // groups per team
     const int tl = lane % TL;
     const int tb = lane - tl;                 // first lane of the team
@@ -139,7 +166,7 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
             c = __builtin_nontemporal_load(&a.col[p]);
             o = (uint32_t)__builtin_nontemporal_load(&a.order[p]);
             if ((int64_t)o >= a.e) o = 0u;   // never taken: order is a permutation of [0, e)
-            wt = __builtin_nontemporal_load(&a.w[o]);
+            if constexpr (!kHeads) wt = __builtin_nontemporal_load(&a.w[o]);
         }
         const int n = end - base < TL ? (int)(end - base) : TL;
         const int trips = (n + G - 1) / G;
@@ -155,6 +182,15 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
                 slu[u] = tb + (k < n ? k : n - 1);
                 cu[u] = __shfl(c, slu[u]);
             }
+            uint32_t oh[kUnroll];   // multi-head: the edge's COO ordinal, then its weight
+            float wh[kUnroll];
+            if constexpr (kHeads) {
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    oh[u] = (uint32_t)__shfl((int)o, slu[u]);
+                    wh[u] = ok[u] && active ? a.w[(int64_t)oh[u] * a.heads + head] : 0.f;
+                }
+            }
             float xv[kUnroll][VEC];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
@@ -167,12 +203,17 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                const float wu = __shfl(wt, slu[u]);
-                const float wv = ok[u] ? wu : 0.f;
+                float wv;
+                if constexpr (kHeads) {
+                    wv = wh[u];
+                } else {
+                    const float wu = __shfl(wt, slu[u]);
+                    wv = ok[u] ? wu : 0.f;
+                }
 #pragma unroll
                 for (int v = 0; v < VEC; ++v) acc[v] = fmaf(wv, xv[u][v], acc[v]);
             }
-            if constexpr (kEdgeGrad) {
+            if constexpr (kEdgeGrad && !kHeads) {
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
                     float part = edge_dot<T, VEC>(xr, xv[u]);
@@ -180,6 +221,16 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
                     for (int off = L / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
                     const uint32_t ou = (uint32_t)__shfl((int)o, slu[u]);
                     if (ok[u] && (lane % L) == 0) a.dw[ou] = part;
+                }
+            }
+            if constexpr (kEdgeGrad && kHeads) {
+                const int seg = a.head_w / VEC;    // lanes per head
+                const int sub = lane % L;
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const float part = head_sum(edge_dot<T, VEC>(xr, xv[u]), lane, sub, seg);
+                    if (ok[u] && active && sub % seg == 0)
+                        a.dw[(int64_t)oh[u] * a.heads + head] = part;
                 }
             }
         }
@@ -197,13 +248,14 @@ __device__ __forceinline__ void own_row(const SpmmArgs &a, int row, int64_t hoff
     }
 }
 
-template <typename T, int VEC, int L, bool kEdgeGrad>
+template <typename T, int VEC, int L, bool kEdgeGrad, bool kHeads>
 __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
     const int sub = lane % L;
     const int64_t hoff = (int64_t)blockIdx.y * (L * VEC) + (int64_t)sub * VEC;
     const bool active = hoff < a.h;
+    const int head = kHeads && active ? (int)(hoff / a.head_w) : 0;
     float acc[VEC], xr[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
@@ -216,8 +268,9 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
         if ((uint32_t)row >= (uint64_t)a.n) return;   // the plan is a permutation of [0, n)
         const int64_t beg = a.rowptr[row], end = a.rowptr[row + 1];
         own_row<T, VEC, kEdgeGrad>(a, row, hoff, active, xr);
-        accumulate<T, VEC, L, kWave, kEdgeGrad>(a, beg + (int64_t)wv * kWave, end,
-                                                (int64_t)kBlock, lane, hoff, active, xr, acc);
+        accumulate<T, VEC, L, kWave, kEdgeGrad, kHeads>(a, beg + (int64_t)wv * kWave, end,
+                                                        (int64_t)kBlock, lane, hoff, head, active,
+                                                        xr, acc);
 #pragma unroll
         for (int off = L; off < kWave; off <<= 1)
 #pragma unroll
@@ -251,8 +304,8 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
 #pragma unroll
             for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
             own_row<T, VEC, kEdgeGrad>(a, row, hoff, active, xr);
-            accumulate<T, VEC, L, kWave, kEdgeGrad>(a, beg, end, (int64_t)kWave, lane, hoff,
-                                                    active, xr, acc);
+            accumulate<T, VEC, L, kWave, kEdgeGrad, kHeads>(a, beg, end, (int64_t)kWave, lane,
+                                                            hoff, head, active, xr, acc);
 #pragma unroll
             for (int off = L; off < kWave; off <<= 1)
 #pragma unroll
@@ -272,7 +325,8 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
 #pragma unroll
         for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
         own_row<T, VEC, kEdgeGrad>(a, row, hoff, active && end > beg, xr);
-        accumulate<T, VEC, L, L, kEdgeGrad>(a, beg, end, (int64_t)L, lane, hoff, active, xr, acc);
+        accumulate<T, VEC, L, L, kEdgeGrad, kHeads>(a, beg, end, (int64_t)L, lane, hoff, head,
+                                                    active, xr, acc);
         if (active) store_row<VEC>(a.y + (int64_t)row * a.h + hoff, acc);
     }
 }
@@ -307,8 +361,8 @@ int64_t rows_at_least(const int64_t *cc, int64_t len) {
 }
 
 template <typename T, int VEC, int L>
-mp_status launch(const CsrView &csr, const float *w, const void *x, int64_t h, float *out,
-                 const void *x_own, float *dw, hipStream_t s) {
+mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *x, int64_t h,
+                 float *out, const void *x_own, float *dw, hipStream_t s) {
     const Thresholds th = thresholds_for(L);
     SpmmArgs a;
     a.rowptr = csr.rowptr;
@@ -321,6 +375,8 @@ mp_status launch(const CsrView &csr, const float *w, const void *x, int64_t h, f
     a.x_own = x_own;
     a.dw = dw;
     a.h = h;
+    a.heads = (int32_t)heads;
+    a.head_w = (int32_t)(h / heads);
     a.n = csr.n;
     a.e = csr.e;
     const int64_t at_hub = rows_at_least(csr.class_count, th.hub_min_len);
@@ -343,11 +399,14 @@ mp_status launch(const CsrView &csr, const float *w, const void *x, int64_t h, f
     if (gx > (int64_t)3 << 22 || gy > 65535)
         return fail(MP_ERR_SHAPE, "launch grid too large (%lld x %lld)", (long long)gx,
                     (long long)gy);
+    const dim3 grid((unsigned)gx, (unsigned)gy);
     if (dw) {   // fused backward: one column block holds the whole feature row
         if (gy != 1) return fail(MP_ERR_SHAPE, "fused backward needs H <= %d", L * VEC);
-        spmm_kernel<T, VEC, L, true><<<dim3((unsigned)gx, 1), kBlock, 0, s>>>(a);
+        if (heads > 1) spmm_kernel<T, VEC, L, true, true><<<grid, kBlock, 0, s>>>(a);
+        else spmm_kernel<T, VEC, L, true, false><<<grid, kBlock, 0, s>>>(a);
     } else {
-        spmm_kernel<T, VEC, L, false><<<dim3((unsigned)gx, (unsigned)gy), kBlock, 0, s>>>(a);
+        if (heads > 1) spmm_kernel<T, VEC, L, false, true><<<grid, kBlock, 0, s>>>(a);
+        else spmm_kernel<T, VEC, L, false, false><<<grid, kBlock, 0, s>>>(a);
     }
     MP_HIP_CHECK(hipGetLastError(), "spmm launch");
     return MP_OK;
@@ -361,16 +420,16 @@ int lanes_for(int64_t h, int vec) {
 }
 
 template <typename T, int VEC>
-mp_status launch_lanes(const CsrView &csr, const float *w, const void *x, int64_t h, float *out,
-                       const void *x_own, float *dw, hipStream_t s) {
+mp_status launch_lanes(const CsrView &csr, const float *w, int64_t heads, const void *x,
+                       int64_t h, float *out, const void *x_own, float *dw, hipStream_t s) {
     switch (lanes_for(h, VEC)) {
-        case 1: return launch<T, VEC, 1>(csr, w, x, h, out, x_own, dw, s);
-        case 2: return launch<T, VEC, 2>(csr, w, x, h, out, x_own, dw, s);
-        case 4: return launch<T, VEC, 4>(csr, w, x, h, out, x_own, dw, s);
-        case 8: return launch<T, VEC, 8>(csr, w, x, h, out, x_own, dw, s);
-        case 16: return launch<T, VEC, 16>(csr, w, x, h, out, x_own, dw, s);
-        case 32: return launch<T, VEC, 32>(csr, w, x, h, out, x_own, dw, s);
-        default: return launch<T, VEC, 64>(csr, w, x, h, out, x_own, dw, s);
+        case 1: return launch<T, VEC, 1>(csr, w, heads, x, h, out, x_own, dw, s);
+        case 2: return launch<T, VEC, 2>(csr, w, heads, x, h, out, x_own, dw, s);
+        case 4: return launch<T, VEC, 4>(csr, w, heads, x, h, out, x_own, dw, s);
+        case 8: return launch<T, VEC, 8>(csr, w, heads, x, h, out, x_own, dw, s);
+        case 16: return launch<T, VEC, 16>(csr, w, heads, x, h, out, x_own, dw, s);
+        case 32: return launch<T, VEC, 32>(csr, w, heads, x, h, out, x_own, dw, s);
+        default: return launch<T, VEC, 64>(csr, w, heads, x, h, out, x_own, dw, s);
     }
 }
 
@@ -378,27 +437,35 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 }  // namespace
 
-mp_status spmm_run(const CsrView &csr, const float *w, const void *x, mp_dtype dt, int64_t h,
-                   float *out, hipStream_t s) {
-    return spmm_fused_run(csr, w, x, dt, h, out, nullptr, nullptr, s);
+mp_status spmm_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
+                   mp_dtype dt, int64_t h, float *out, hipStream_t s) {
+    return spmm_fused_run(csr, w, heads, x, dt, h, out, nullptr, nullptr, s);
 }
 
-bool spmm_fused_supported(mp_dtype dt, int64_t h, const void *x, const void *x_own,
-                          const void *out) {
+// 16-byte lanes need aligned rows and heads that are whole lanes wide.
+bool vector_lanes_ok(int vec, int64_t h, int64_t heads, const void *x, const void *x_own,
+                     const void *out) {
+    return aligned16(x) && aligned16(out) && (!x_own || aligned16(x_own)) &&
+           (h / heads) % vec == 0;
+}
+
+bool spmm_fused_supported(mp_dtype dt, int64_t h, int64_t heads, const void *x,
+                          const void *x_own, const void *out) {
     const int vec = dt == MP_F32 ? 4 : 8;
-    const bool vec_ok = aligned16(x) && aligned16(out) && aligned16(x_own) && h % vec == 0;
-    return h <= (int64_t)kWave * (vec_ok ? vec : 1);
+    return h <= (int64_t)kWave * (vector_lanes_ok(vec, h, heads, x, x_own, out) ? vec : 1);
 }
 
-mp_status spmm_fused_run(const CsrView &csr, const float *w, const void *x, mp_dtype dt,
-                         int64_t h, float *out, const void *x_own, float *dw, hipStream_t s) {
-    const bool vec_ok = aligned16(x) && aligned16(out) && (!x_own || aligned16(x_own));
+mp_status spmm_fused_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
+                         mp_dtype dt, int64_t h, float *out, const void *x_own, float *dw,
+                         hipStream_t s) {
     if (dt == MP_F32) {
-        if (vec_ok && h % 4 == 0) return launch_lanes<float, 4>(csr, w, x, h, out, x_own, dw, s);
-        return launch_lanes<float, 1>(csr, w, x, h, out, x_own, dw, s);
+        if (vector_lanes_ok(4, h, heads, x, x_own, out))
+            return launch_lanes<float, 4>(csr, w, heads, x, h, out, x_own, dw, s);
+        return launch_lanes<float, 1>(csr, w, heads, x, h, out, x_own, dw, s);
     }
-    if (vec_ok && h % 8 == 0) return launch_lanes<uint16_t, 8>(csr, w, x, h, out, x_own, dw, s);
-    return launch_lanes<uint16_t, 1>(csr, w, x, h, out, x_own, dw, s);
+    if (vector_lanes_ok(8, h, heads, x, x_own, out))
+        return launch_lanes<uint16_t, 8>(csr, w, heads, x, h, out, x_own, dw, s);
+    return launch_lanes<uint16_t, 1>(csr, w, heads, x, h, out, x_own, dw, s);
 }
 
 }  // namespace mp

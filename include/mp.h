@@ -191,6 +191,36 @@ mp_status mp_spmm_dx_edge_grad(const mp_graph *g, const float *w, const void *x,
                                mp_dtype dtype, int64_t h, float *dx, float *dw, void *stream);
 
 /*
+ * Multi-head edge weights.  tinymesh "Weighted aggregation experiment",
+ * "Limits" lists vector edge weights among what the scalar experiment leaves
+ * open; these calls take the per-head reading of it.  Each edge carries
+ * `heads` = K weights, w[e * K + q] ([E, K] row-major, COO order), the feature
+ * width H is a multiple of K, and head q owns columns [q*H/K, (q+1)*H/K) of
+ * every feature row.  Head q of the output aggregates head q of the inputs
+ * with weight w[e, q]:
+ *   Y[i, c]  = sum over edges e into i   of w[e, q(c)] * X[src_e, c],
+ *   dX[j, c] = sum over edges e out of j of w[e, q(c)] * dY[dst_e, c],
+ *   dw[e, q] = sum over c in head q of X[src_e, c] * dY[dst_e, c],
+ * q(c) = c / (H/K).  K = 1 is exactly the scalar call of the same name.  No
+ * [E, H] intermediate is formed; the owners, layouts, tolerances and error
+ * codes are those of the scalar calls, plus MP_ERR_SHAPE when K < 1 or K does
+ * not divide H.  dw is [E, K] float32 in COO order.  The fused call gives dX
+ * and dw bitwise equal to mp_spmm_dx_heads and mp_edge_grad_dw_heads under the
+ * same condition as mp_spmm_dx_edge_grad (H within one column block, 16-byte
+ * aligned rows whose heads are whole 16-byte lanes wide).
+ */
+mp_status mp_spmm_fwd_heads(const mp_graph *g, const float *w, int64_t heads, const void *x,
+                            mp_dtype x_dtype, int64_t h, float *y, void *stream);
+mp_status mp_spmm_dx_heads(const mp_graph *g, const float *w, int64_t heads, const void *dy,
+                           mp_dtype dy_dtype, int64_t h, float *dx, void *stream);
+mp_status mp_edge_grad_dw_heads(const mp_graph *g, const void *x, const void *dy,
+                                mp_dtype dtype, int64_t h, int64_t heads, float *dw,
+                                void *stream);
+mp_status mp_spmm_dx_edge_grad_heads(const mp_graph *g, const float *w, int64_t heads,
+                                     const void *x, const void *dy, mp_dtype dtype, int64_t h,
+                                     float *dx, float *dw, void *stream);
+
+/*
  * Target normalisation of scalar edge scores, the step a sparse attention layer
  * puts between learned scores and this aggregation ("Limits": scores
  * normalised over the edges of each target).  For every edge e with i = dst_e:

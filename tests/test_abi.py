@@ -133,6 +133,16 @@ def test_compute_calls_reject_unbuilt_graphs(mp):
     assert fused(None, 0x100, 0x200, 0x300, mp.MP_F32, 4, 0x400, 0x500, None) == mp.MP_ERR_NULL
     assert fused(ctypes.byref(g), 0x100, 0x200, 0x300, mp.MP_F32, 4, 0x400, 0x500, None) \
         == mp.MP_ERR_GRAPH
+    for fn in (lib.mp_spmm_fwd_heads, lib.mp_spmm_dx_heads):
+        assert fn(None, 0x100, 2, 0x200, mp.MP_F32, 4, 0x300, None) == mp.MP_ERR_NULL
+        assert fn(ctypes.byref(g), 0x100, 2, 0x200, mp.MP_F32, 4, 0x300, None) == mp.MP_ERR_GRAPH
+    dwh = lib.mp_edge_grad_dw_heads
+    assert dwh(None, 0x100, 0x200, mp.MP_F32, 4, 2, 0x300, None) == mp.MP_ERR_NULL
+    assert dwh(ctypes.byref(g), 0x100, 0x200, mp.MP_F32, 4, 2, 0x300, None) == mp.MP_ERR_GRAPH
+    fh = lib.mp_spmm_dx_edge_grad_heads
+    assert fh(None, 0x100, 2, 0x200, 0x300, mp.MP_F32, 4, 0x400, 0x500, None) == mp.MP_ERR_NULL
+    assert fh(ctypes.byref(g), 0x100, 2, 0x200, 0x300, mp.MP_F32, 4, 0x400, 0x500, None) \
+        == mp.MP_ERR_GRAPH
 
 
 def test_forward_and_input_grad_kernels_have_no_atomics(tmp_path):

@@ -166,16 +166,10 @@ def main():
             times[name].append(ev[k].elapsed_time(ev[k + 1]))
     log(f"timed {args.steps} steps in {t_total:.3f}s")
 
-    # The separate gradient entry points, outside the timed steps.
-    g = mp.mp_graph_build(src, dst, n)
-    dx_alone = torch.empty_like(dx)
-    dw_alone = torch.empty_like(dw)
-    standalone = {}
-    for name, fn in (("dx", lambda: mp.mp_spmm_dx(g, w, dy, out=dx_alone)),
-                     ("dw", lambda: mp.mp_edge_grad_dw(g, x, dy, out=dw_alone))):
+    def time_op(fn, reps=5):
         fn()
         ts = []
-        for _ in range(5):
+        for _ in range(reps):
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
@@ -183,7 +177,15 @@ def main():
             b.record(stream)
             torch.cuda.synchronize()
             ts.append(a.elapsed_time(b))
-        standalone[name] = statistics.median(ts)
+        return statistics.median(ts)
+
+    # The separate gradient entry points, outside the timed steps.
+    g = mp.mp_graph_build(src, dst, n)
+    dx_alone = torch.empty_like(dx)
+    dw_alone = torch.empty_like(dw)
+    standalone = {}
+    standalone["dx"] = time_op(lambda: mp.mp_spmm_dx(g, w, dy, out=dx_alone))
+    standalone["dw"] = time_op(lambda: mp.mp_edge_grad_dw(g, x, dy, out=dw_alone))
     same = bool(torch.equal(dx_alone, dx) and torch.equal(dw_alone, dw))
     # Sparse attention pieces on the same topology (scores = the edge weights).
     alpha = torch.empty_like(w)
@@ -192,24 +194,28 @@ def main():
     dscores = torch.empty_like(w)
     rdot = torch.empty_like(rmax)
     wn = torch.empty_like(w)
-    for name, fn in (("edge_softmax", lambda: mp.mp_edge_softmax(g, w, alpha, rmax, rsum)),
-                     ("edge_softmax_backward",
-                      lambda: mp.mp_edge_softmax_backward(g, alpha, dw, dscores, rdot)),
-                     ("edge_normalize_sym",
-                      lambda: mp.mp_edge_normalize(g, mp.MP_NORM_SYM, w, out=wn))):
-        fn()
-        ts = []
-        for _ in range(5):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fn()
-            b.record(stream)
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b))
-        standalone[name] = statistics.median(ts)
+    standalone["edge_softmax"] = time_op(lambda: mp.mp_edge_softmax(g, w, alpha, rmax, rsum))
+    standalone["edge_softmax_backward"] = time_op(
+        lambda: mp.mp_edge_softmax_backward(g, alpha, dw, dscores, rdot))
+    standalone["edge_normalize_sym"] = time_op(
+        lambda: mp.mp_edge_normalize(g, mp.MP_NORM_SYM, w, out=wn))
     log(f"standalone dx {standalone['dx']:.3f} ms, dw {standalone['dw']:.3f} ms, "
         f"equal to the fused results: {same}")
+    del alpha, rmax, rsum, dscores, rdot, wn
+    # Multi-head weights on the same graph: K heads of H/K columns, w [E, K].
+    heads = 4
+    wk = torch.rand((e, heads), generator=torch.Generator(device=dev).manual_seed(7),
+                    device=dev) * 2 - 1
+    dwk = torch.empty((e, heads), dtype=torch.float32, device=dev)
+    dxk = torch.empty_like(dx)
+    standalone["fwd_heads"] = time_op(lambda: mp.mp_spmm_fwd_heads(g, wk, x, out=y))
+    standalone["bwd_heads"] = time_op(
+        lambda: mp.mp_spmm_dx_edge_grad_heads(g, wk, x, dy, out_dx=dxk, out_dw=dwk))
+    same_heads = bool(torch.equal(mp.mp_spmm_dx_heads(g, wk, dy), dxk)
+                      and torch.equal(mp.mp_edge_grad_dw_heads(g, x, dy, heads), dwk))
+    log(f"heads={heads}: fwd {standalone['fwd_heads']:.3f} ms, fused bwd "
+        f"{standalone['bwd_heads']:.3f} ms, equal to the separate calls: {same_heads}")
+    del wk, dwk, dxk
 
     if args.copy_calibration:
         a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -227,6 +233,9 @@ def main():
     bytes_["edge_softmax_backward"] = 28 * e + 16 * n
     # symmetric normalisation: in, out, src, dst per edge; both row pointers once.
     bytes_["edge_normalize_sym"] = 16 * e + 8 * (n + 1)
+    # multi-head: the edge's weight (or dw) term grows from 4 to 4K bytes.
+    bytes_["fwd_heads"] = bytes_["fwd"] + 4 * (heads - 1) * e
+    bytes_["bwd_heads"] = bytes_["dx"] + bytes_["dw"] + 8 * (heads - 1) * e
     ms_step = t_total / args.steps * 1e3
 
     def rate(nbytes, ms):
@@ -237,6 +246,8 @@ def main():
     per_op = {k: rate(bytes_[k], statistics.median(times[k])) for k in ops}
     per_op_standalone = {k: rate(bytes_[k], v) for k, v in standalone.items()}
     per_op_standalone["equal_to_fused"] = same
+    per_op_standalone["heads"] = heads
+    per_op_standalone["heads_fused_equal_to_separate"] = same_heads
     # Kernels of the compute ops.  The dominant kernel is the one with the most
     # GPU time per step; its achieved bandwidth is the algorithmic bytes of the
     # units one launch processes over its average launch duration (the fused

@@ -27,7 +27,8 @@ import os
 import torch  # noqa: F401  -- loaded first so libmp.so binds to torch's HIP runtime
 
 __all__ = [
-    "Graph", "MpError", "mp_graph_build", "mp_graph_build_workspace_size", "mp_spmm_fwd",
+    "Graph", "MpError", "mp_graph_build", "mp_graph_build_async", "mp_graph_finish",
+    "mp_graph_build_workspace_size", "mp_spmm_fwd",
     "mp_spmm_dx", "mp_edge_grad_dw", "mp_spmm_dx_edge_grad", "mp_spmm_fwd_heads",
     "mp_spmm_dx_heads", "mp_edge_grad_dw_heads", "mp_spmm_dx_edge_grad_heads", "mp_edge_softmax",
     "mp_edge_softmax_backward", "mp_edge_normalize", "MP_NORM_MEAN", "MP_NORM_SYM",
@@ -43,6 +44,8 @@ MP_ERR_NULL, MP_ERR_SHAPE, MP_ERR_DTYPE, MP_ERR_DEVICE, MP_ERR_INDEX = -1, -2, -
 MP_ERR_ALIAS, MP_ERR_ALIGN, MP_ERR_WORKSPACE, MP_ERR_GRAPH, MP_ERR_HIP = -6, -7, -8, -9, -10
 MP_I32, MP_I64, MP_F32, MP_BF16 = 1, 2, 3, 4
 MP_NORM_MEAN, MP_NORM_SYM = 1, 2
+GRAPH_INFO_WORDS = 576
+GRAPH_BUILT, GRAPH_ON_DEVICE = 0x6d705f6772617068, 0x6d705f6465766963
 NUM_CLASSES = 33
 
 _DTYPE = {torch.int32: MP_I32, torch.int64: MP_I64, torch.float32: MP_F32,
@@ -71,7 +74,7 @@ class MpIndexError(MpError, IndexError):
 
 _EXC = {MP_ERR_DTYPE: MpTypeError, MP_ERR_INDEX: MpIndexError, MP_ERR_NULL: MpValueError,
         MP_ERR_SHAPE: MpValueError, MP_ERR_DEVICE: MpValueError, MP_ERR_ALIAS: MpValueError,
-        MP_ERR_ALIGN: MpValueError, MP_ERR_WORKSPACE: MpValueError}
+        MP_ERR_ALIGN: MpValueError, MP_ERR_WORKSPACE: MpValueError, MP_ERR_GRAPH: MpValueError}
 
 
 class _MpGraph(ctypes.Structure):
@@ -82,6 +85,7 @@ class _MpGraph(ctypes.Structure):
         ("rowptr_t", ctypes.c_void_p), ("col_t", ctypes.c_void_p),
         ("transpose_order", ctypes.c_void_p),
         ("row_plan", ctypes.c_void_p), ("row_plan_t", ctypes.c_void_p),
+        ("info", ctypes.c_void_p),
         ("class_count", ctypes.c_int64 * NUM_CLASSES),
         ("class_count_t", ctypes.c_int64 * NUM_CLASSES),
         ("built", ctypes.c_uint64),
@@ -99,6 +103,8 @@ def _load():
     sigs = {
         "mp_graph_build_workspace_size": (i32, [i64, i64, ctypes.POINTER(sz)]),
         "mp_graph_build": (i32, [vp, vp, i32, i64, i64, gp, vp, sz, vp]),
+        "mp_graph_build_async": (i32, [vp, vp, i32, i64, i64, gp, vp, sz, vp]),
+        "mp_graph_finish": (i32, [gp, vp]),
         "mp_spmm_fwd": (i32, [gp, vp, vp, i32, i64, vp, vp]),
         "mp_spmm_dx": (i32, [gp, vp, vp, i32, i64, vp, vp]),
         "mp_edge_grad_dw": (i32, [gp, vp, vp, i32, i64, vp, vp]),
@@ -183,10 +189,13 @@ class Graph:
                  "row_plan_t": n}
         self.arrays = {k: torch.empty(max(v, 0), dtype=torch.int32, device=self.device)
                        for k, v in sizes.items()}
+        # the build's device record (index check, rows per class of both plans)
+        self.info = torch.empty(GRAPH_INFO_WORDS, dtype=torch.int32, device=self.device)
         d = _MpGraph()
         d.num_nodes, d.num_edges = n, e
         for k in self._ARRAYS:
             setattr(d, k, _ptr(self.arrays[k]) if self.arrays[k].numel() else None)
+        d.info = _ptr(self.info)
         self._desc = d
 
     def __getattr__(self, name):
@@ -207,6 +216,19 @@ class Graph:
     def built(self) -> bool:
         return self._desc.built != 0
 
+    @property
+    def on_device(self) -> bool:
+        """True after mp_graph_build_async until mp_graph_finish: the class counts
+        exist on the device only (the compute calls read them there)."""
+        return self._desc.built == GRAPH_ON_DEVICE
+
+    def record_stream(self, stream) -> None:
+        """Tell torch's allocator that `stream` uses the graph's arrays (needed
+        before the Graph is dropped while work on another stream may still read it)."""
+        for t in list(self.arrays.values()) + [self.info]:
+            if t.numel():
+                t.record_stream(stream)
+
     @classmethod
     def from_edge_index(cls, edge_index, num_nodes: int) -> "Graph":
         """Build from a [2, E] edge_index (row 0 = source, row 1 = target)."""
@@ -223,8 +245,7 @@ def mp_graph_build_workspace_size(num_nodes: int, num_edges: int) -> int:
     return int(out.value)
 
 
-def mp_graph_build(src, dst, num_nodes: int) -> Graph:
-    """Lower COO edges (src[e] -> dst[e], int32 or int64 device tensors) on device."""
+def _build_graph(fn, name, src, dst, num_nodes, workspace):
     _need_tensor("src", src)
     _need_tensor("dst", dst)
     if src.dim() != 1 or dst.dim() != 1 or src.shape[0] != dst.shape[0]:
@@ -232,11 +253,40 @@ def mp_graph_build(src, dst, num_nodes: int) -> Graph:
     e = int(src.shape[0])
     g = Graph(num_nodes, e, src.device)
     ws_bytes = mp_graph_build_workspace_size(num_nodes, e)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=src.device)
-    status = _lib.mp_graph_build(_ptr(src) if e else None, _ptr(dst) if e else None, _code(src),
-                                 int(num_nodes), e, ctypes.byref(g._desc), _ptr(ws), ws_bytes,
-                                 _stream(src))
-    _check(status, "mp_graph_build")
+    if workspace is None:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=src.device)
+    else:
+        _need_tensor("workspace", workspace)
+        if workspace.dtype != torch.uint8 or workspace.numel() < ws_bytes:
+            raise ValueError(f"workspace must be a uint8 tensor of at least {ws_bytes} bytes")
+        ws = workspace
+    status = fn(_ptr(src) if e else None, _ptr(dst) if e else None, _code(src), int(num_nodes),
+                e, ctypes.byref(g._desc), _ptr(ws), ws.numel(), _stream(src))
+    _check(status, name)
+    return g
+
+
+def mp_graph_build(src, dst, num_nodes: int, workspace=None) -> Graph:
+    """Lower COO edges (src[e] -> dst[e], int32 or int64 device tensors) on device,
+    on the current stream; returns once the build has run (one synchronisation)."""
+    return _build_graph(_lib.mp_graph_build, "mp_graph_build", src, dst, num_nodes, workspace)
+
+
+def mp_graph_build_async(src, dst, num_nodes: int, workspace=None) -> Graph:
+    """The same lowering, only enqueued on the current stream (no synchronisation):
+    the graph's class counts stay on the device and the compute calls read them
+    there.  The index check is reported by mp_graph_finish.  Concurrent builds on
+    several streams need their own workspaces (mp_graph_build_workspace_size)."""
+    return _build_graph(_lib.mp_graph_build_async, "mp_graph_build_async", src, dst, num_nodes,
+                  workspace)
+
+
+def mp_graph_finish(g: Graph, stream=None) -> Graph:
+    """Wait for an asynchronous build (on `stream`, default the current one), copy
+    its class counts to the host and raise IndexError if an endpoint was outside
+    [0, N).  No-op for a finished graph."""
+    st = torch.cuda.current_stream(g.device) if stream is None else stream
+    _check(_lib.mp_graph_finish(ctypes.byref(g._desc), st.cuda_stream), "mp_graph_finish")
     return g
 
 

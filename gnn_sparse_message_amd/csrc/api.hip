@@ -1,6 +1,7 @@
 // api.hip -- the extern "C" entry points declared in include/mp.h: argument
 // validation on the host, then the launches in lower.hip, spmm.hip, sddmm.hip.
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -10,7 +11,6 @@ namespace mp {
 
 namespace {
 thread_local char g_detail[512] = "";
-constexpr uint64_t kBuiltMagic = 0x6d705f6772617068ull;   // "mp_graph"
 constexpr int64_t kMaxIndex = (int64_t)1 << 31;           // N, E < 2^31
 }  // namespace
 
@@ -76,28 +76,61 @@ bool overlap(const Range &a, const Range &b) {
     return a.lo < b.hi && b.lo < a.hi;
 }
 
-// Ranges of every array a graph descriptor points to.
-int graph_ranges(const mp_graph *g, Range *out) {
-    const int64_t n = g->num_nodes, e = g->num_edges;
+// A short list of address ranges with a fixed capacity; adding beyond it
+// aborts rather than writing past the end.
+struct RangeList {
+    static constexpr int kCap = 24;
+    Range r[kCap];
     int k = 0;
-    out[k++] = range(g->src, e, 4, "graph src");
-    out[k++] = range(g->dst, e, 4, "graph dst");
-    out[k++] = range(g->rowptr, n + 1, 4, "graph rowptr");
-    out[k++] = range(g->col, e, 4, "graph col");
-    out[k++] = range(g->edge_order, e, 4, "graph edge_order");
-    out[k++] = range(g->rowptr_t, n + 1, 4, "graph rowptr_t");
-    out[k++] = range(g->col_t, e, 4, "graph col_t");
-    out[k++] = range(g->transpose_order, e, 4, "graph transpose_order");
-    out[k++] = range(g->row_plan, n, 4, "graph row_plan");
-    out[k++] = range(g->row_plan_t, n, 4, "graph row_plan_t");
-    return k;
+    void add(const Range &x) {
+        if (k >= kCap) abort();
+        r[k++] = x;
+    }
+    // Name of the first range that overlaps `x`, or nullptr.
+    const char *overlapping(const Range &x) const {
+        for (int i = 0; i < k; ++i)
+            if (overlap(x, r[i])) return r[i].name;
+        return nullptr;
+    }
+};
+
+// Ranges of every array a graph descriptor points to.
+RangeList graph_ranges(const mp_graph *g) {
+    const int64_t n = g->num_nodes, e = g->num_edges;
+    RangeList out;
+    out.add(range(g->src, e, 4, "graph src"));
+    out.add(range(g->dst, e, 4, "graph dst"));
+    out.add(range(g->rowptr, n + 1, 4, "graph rowptr"));
+    out.add(range(g->col, e, 4, "graph col"));
+    out.add(range(g->edge_order, e, 4, "graph edge_order"));
+    out.add(range(g->rowptr_t, n + 1, 4, "graph rowptr_t"));
+    out.add(range(g->col_t, e, 4, "graph col_t"));
+    out.add(range(g->transpose_order, e, 4, "graph transpose_order"));
+    out.add(range(g->row_plan, n, 4, "graph row_plan"));
+    out.add(range(g->row_plan_t, n, 4, "graph row_plan_t"));
+    out.add(range(g->info, MP_GRAPH_INFO_WORDS, 4, "graph info"));
+    return out;
 }
 
 mp_status check_graph(const mp_graph *g) {
     if (!g) return fail(MP_ERR_NULL, "graph is NULL");
-    if (g->built != kBuiltMagic)
+    if (g->built != MP_GRAPH_BUILT && g->built != MP_GRAPH_ON_DEVICE)
         return fail(MP_ERR_GRAPH, "graph was not produced by a successful mp_graph_build");
     return MP_OK;
+}
+
+// The two CSR forms of a built graph; an asynchronously built graph hands the
+// kernels its device plan record instead of host counts.
+CsrView forward_view(const mp_graph *g) {
+    const bool dev = g->built == MP_GRAPH_ON_DEVICE;
+    return CsrView{g->rowptr, g->col, g->edge_order, g->row_plan, g->class_count,
+                   dev ? g->info + kInfoPlanF : nullptr, g->num_nodes, g->num_edges};
+}
+
+CsrView transpose_view(const mp_graph *g) {
+    const bool dev = g->built == MP_GRAPH_ON_DEVICE;
+    return CsrView{g->rowptr_t, g->col_t, g->transpose_order, g->row_plan_t, g->class_count_t,
+                   dev ? g->info + kInfoPlanT : nullptr, g->num_nodes, g->num_edges};
 }
 
 mp_status check_sizes(int64_t n, int64_t e) {
@@ -142,13 +175,11 @@ mp_status check_spmm(const mp_graph *g, const float *w, int64_t heads, const voi
     if ((st = check_device(y, yname)) != MP_OK) return st;
     if (e > 0 && (st = check_device(w, "w")) != MP_OK) return st;
     const Range ry = range(y, n * h, 4, yname);
-    Range others[12];
-    int k = graph_ranges(g, others);
-    others[k++] = range(x, n * h, xs, xname);
-    others[k++] = range(w, e * heads, 4, "w");
-    for (int i = 0; i < k; ++i)
-        if (overlap(ry, others[i]))
-            return fail(MP_ERR_ALIAS, "%s overlaps %s", yname, others[i].name);
+    RangeList others = graph_ranges(g);
+    others.add(range(x, n * h, xs, xname));
+    others.add(range(w, e * heads, 4, "w"));
+    if (const char *hit = others.overlapping(ry))
+        return fail(MP_ERR_ALIAS, "%s overlaps %s", yname, hit);
     return MP_OK;
 }
 
@@ -156,18 +187,16 @@ mp_status spmm_fwd_impl(const mp_graph *g, const float *w, int64_t heads, const 
                         mp_dtype x_dtype, int64_t h, float *y, void *stream) {
     mp_status st = check_spmm(g, w, heads, x, x_dtype, h, y, "x", "y");
     if (st != MP_OK) return st;
-    CsrView v{g->rowptr, g->col, g->edge_order, g->row_plan, g->class_count, g->num_nodes,
-              g->num_edges};
-    return spmm_run(v, w, heads, x, x_dtype, h, y, static_cast<hipStream_t>(stream));
+    return spmm_run(forward_view(g), w, heads, x, x_dtype, h, y,
+                    static_cast<hipStream_t>(stream));
 }
 
 mp_status spmm_dx_impl(const mp_graph *g, const float *w, int64_t heads, const void *dy,
                        mp_dtype dy_dtype, int64_t h, float *dx, void *stream) {
     mp_status st = check_spmm(g, w, heads, dy, dy_dtype, h, dx, "dy", "dx");
     if (st != MP_OK) return st;
-    CsrView v{g->rowptr_t, g->col_t, g->transpose_order, g->row_plan_t, g->class_count_t,
-              g->num_nodes, g->num_edges};
-    return spmm_run(v, w, heads, dy, dy_dtype, h, dx, static_cast<hipStream_t>(stream));
+    return spmm_run(transpose_view(g), w, heads, dy, dy_dtype, h, dx,
+                    static_cast<hipStream_t>(stream));
 }
 
 mp_status edge_grad_impl(const mp_graph *g, const void *x, const void *dy, mp_dtype dtype,
@@ -190,12 +219,11 @@ mp_status edge_grad_impl(const mp_graph *g, const void *x, const void *dy, mp_dt
     if (e == 0) return MP_OK;
     if ((st = check_device(dw, "dw")) != MP_OK) return st;
     const Range rdw = range(dw, e * heads, 4, "dw");
-    Range others[12];
-    int k = graph_ranges(g, others);
-    others[k++] = range(x, n * h, xs, "x");
-    others[k++] = range(dy, n * h, xs, "dy");
-    for (int i = 0; i < k; ++i)
-        if (overlap(rdw, others[i])) return fail(MP_ERR_ALIAS, "dw overlaps %s", others[i].name);
+    RangeList others = graph_ranges(g);
+    others.add(range(x, n * h, xs, "x"));
+    others.add(range(dy, n * h, xs, "dy"));
+    if (const char *hit = others.overlapping(rdw))
+        return fail(MP_ERR_ALIAS, "dw overlaps %s", hit);
     return sddmm_run(g->src, g->dst, e, x, dy, dtype, h, heads, dw,
                      static_cast<hipStream_t>(stream));
 }
@@ -216,17 +244,15 @@ mp_status dx_edge_grad_impl(const mp_graph *g, const float *w, int64_t heads, co
     const Range rdx = range(dx, n * h, 4, "dx"), rdw = range(dw, e * heads, 4, "dw");
     const Range rx = range(x, n * h, xs, "x");
     if (overlap(rdx, rx)) return fail(MP_ERR_ALIAS, "dx overlaps x");
-    Range others[13];
-    int k = graph_ranges(g, others);
-    others[k++] = rx;
-    others[k++] = range(dy, n * h, xs, "dy");
-    others[k++] = range(w, e * heads, 4, "w");
-    others[k++] = rdx;
-    for (int i = 0; i < k; ++i)
-        if (overlap(rdw, others[i])) return fail(MP_ERR_ALIAS, "dw overlaps %s", others[i].name);
+    RangeList others = graph_ranges(g);
+    others.add(rx);
+    others.add(range(dy, n * h, xs, "dy"));
+    others.add(range(w, e * heads, 4, "w"));
+    others.add(rdx);
+    if (const char *hit = others.overlapping(rdw))
+        return fail(MP_ERR_ALIAS, "dw overlaps %s", hit);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    CsrView v{g->rowptr_t, g->col_t, g->transpose_order, g->row_plan_t, g->class_count_t,
-              g->num_nodes, g->num_edges};
+    const CsrView v = transpose_view(g);
     if (spmm_fused_supported(dtype, h, heads, dy, x, dx))
         return spmm_fused_run(v, w, heads, dy, dtype, h, dx, x, e > 0 ? dw : nullptr, s);
     // Feature rows wider than one column block: the two kernels back to back.
@@ -250,9 +276,13 @@ mp_status mp_graph_build_workspace_size(int64_t num_nodes, int64_t num_edges, si
     return MP_OK;
 }
 
-mp_status mp_graph_build(const void *src, const void *dst, mp_dtype idx_dtype, int64_t num_nodes,
-                         int64_t num_edges, mp_graph *g, void *workspace, size_t workspace_bytes,
-                         void *stream) {
+}  // extern "C"
+
+namespace mp {
+namespace {
+mp_status build_impl(const void *src, const void *dst, mp_dtype idx_dtype, int64_t num_nodes,
+                     int64_t num_edges, mp_graph *g, void *workspace, size_t workspace_bytes,
+                     void *stream, bool async) {
     if (!g) return fail(MP_ERR_NULL, "graph descriptor is NULL");
     g->built = 0;
     mp_status st = check_sizes(num_nodes, num_edges);
@@ -271,6 +301,7 @@ mp_status mp_graph_build(const void *src, const void *dst, mp_dtype idx_dtype, i
         {g->edge_order, "graph edge_order", e}, {g->rowptr_t, "graph rowptr_t", n + 1},
         {g->col_t, "graph col_t", e},   {g->transpose_order, "graph transpose_order", e},
         {g->row_plan, "graph row_plan", n}, {g->row_plan_t, "graph row_plan_t", n},
+        {g->info, "graph info", MP_GRAPH_INFO_WORDS},
     };
     for (const auto &a : arrays) {
         if (a.count > 0 && !a.p) return fail(MP_ERR_NULL, "%s is NULL", a.name);
@@ -293,28 +324,64 @@ mp_status mp_graph_build(const void *src, const void *dst, mp_dtype idx_dtype, i
     if ((st = check_device(workspace, "workspace")) != MP_OK) return st;
 
     // Outputs (graph arrays, workspace) must not overlap each other or the inputs.
-    Range r[13];
     g->num_nodes = n;
     g->num_edges = e;
-    int k = graph_ranges(g, r);
-    r[k++] = Range{reinterpret_cast<uintptr_t>(workspace),
-                   reinterpret_cast<uintptr_t>(workspace) + need, "workspace"};
+    RangeList r = graph_ranges(g);
+    r.add(Range{reinterpret_cast<uintptr_t>(workspace),
+                reinterpret_cast<uintptr_t>(workspace) + need, "workspace"});
     const Range in_s = range(src, e, is, "src"), in_d = range(dst, e, is, "dst");
-    for (int i = 0; i < k; ++i) {
-        if (overlap(r[i], in_s) || overlap(r[i], in_d))
-            return fail(MP_ERR_ALIAS, "%s overlaps the input edge list", r[i].name);
-        for (int j = i + 1; j < k; ++j)
-            if (overlap(r[i], r[j]))
-                return fail(MP_ERR_ALIAS, "%s overlaps %s", r[i].name, r[j].name);
+    for (int i = 0; i < r.k; ++i) {
+        if (overlap(r.r[i], in_s) || overlap(r.r[i], in_d))
+            return fail(MP_ERR_ALIAS, "%s overlaps the input edge list", r.r[i].name);
+        for (int j = i + 1; j < r.k; ++j)
+            if (overlap(r.r[i], r.r[j]))
+                return fail(MP_ERR_ALIAS, "%s overlaps %s", r.r[i].name, r.r[j].name);
     }
 
     int bad = 0;
-    st = lower_run(src, dst, idx_dtype, n, e, g, workspace, static_cast<hipStream_t>(stream), &bad);
+    st = lower_run(src, dst, idx_dtype, n, e, g, workspace, static_cast<hipStream_t>(stream),
+                   async, &bad);
     if (st != MP_OK) return st;
     if (bad) return fail(MP_ERR_INDEX, "an edge endpoint lies outside [0, %lld)", (long long)n);
-    g->built = kBuiltMagic;
+    g->built = async ? MP_GRAPH_ON_DEVICE : MP_GRAPH_BUILT;
     return MP_OK;
 }
+}  // namespace
+}  // namespace mp
+
+extern "C" {
+
+mp_status mp_graph_build(const void *src, const void *dst, mp_dtype idx_dtype, int64_t num_nodes,
+                         int64_t num_edges, mp_graph *g, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+    return build_impl(src, dst, idx_dtype, num_nodes, num_edges, g, workspace, workspace_bytes,
+                      stream, false);
+}
+
+mp_status mp_graph_build_async(const void *src, const void *dst, mp_dtype idx_dtype,
+                               int64_t num_nodes, int64_t num_edges, mp_graph *g,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+    return build_impl(src, dst, idx_dtype, num_nodes, num_edges, g, workspace, workspace_bytes,
+                      stream, true);
+}
+
+mp_status mp_graph_finish(mp_graph *g, void *stream) {
+    if (!g) return fail(MP_ERR_NULL, "graph descriptor is NULL");
+    if (g->built == MP_GRAPH_BUILT) return MP_OK;
+    if (g->built != MP_GRAPH_ON_DEVICE)
+        return fail(MP_ERR_GRAPH, "graph was not produced by a successful build");
+    int bad = 0;
+    mp_status st = lower_read_info(g, static_cast<hipStream_t>(stream), &bad);
+    if (st != MP_OK) return st;
+    if (bad) {
+        g->built = 0;
+        return fail(MP_ERR_INDEX, "an edge endpoint lies outside [0, %lld)",
+                    (long long)g->num_nodes);
+    }
+    g->built = MP_GRAPH_BUILT;
+    return MP_OK;
+}
+
 
 mp_status mp_spmm_fwd(const mp_graph *g, const float *w, const void *x, mp_dtype x_dtype,
                       int64_t h, float *y, void *stream) {
@@ -381,14 +448,12 @@ mp_status check_softmax(const mp_graph *g, const float *edge_in, const float *ed
     }
     Range outs[3] = {range(edge_out, e, 4, "edge output"), range(row_out, n, 4, "row output"),
                      range(row_out2, row_out2 ? n : 0, 4, "second row output")};
-    Range others[14];
-    int k = graph_ranges(g, others);
-    others[k++] = range(edge_in, e, 4, "edge input");
-    others[k++] = range(edge_in2, edge_in2 ? e : 0, 4, "second edge input");
+    RangeList others = graph_ranges(g);
+    others.add(range(edge_in, e, 4, "edge input"));
+    others.add(range(edge_in2, edge_in2 ? e : 0, 4, "second edge input"));
     for (int i = 0; i < 3; ++i) {
-        for (int j = 0; j < k; ++j)
-            if (overlap(outs[i], others[j]))
-                return fail(MP_ERR_ALIAS, "%s: %s overlaps %s", what, outs[i].name, others[j].name);
+        if (const char *hit = others.overlapping(outs[i]))
+            return fail(MP_ERR_ALIAS, "%s: %s overlaps %s", what, outs[i].name, hit);
         for (int j = i + 1; j < 3; ++j)
             if (overlap(outs[i], outs[j]))
                 return fail(MP_ERR_ALIAS, "%s: %s overlaps %s", what, outs[i].name, outs[j].name);
@@ -432,11 +497,8 @@ mp_status mp_edge_normalize(const mp_graph *g, int32_t mode, const float *in, fl
     const Range ro = range(out, e, 4, "out"), ri = range(in, e, 4, "in");
     if (ro.lo != ri.lo && overlap(ro, ri))
         return fail(MP_ERR_ALIAS, "mp_edge_normalize: out partially overlaps in");
-    Range others[12];
-    const int k = graph_ranges(g, others);
-    for (int i = 0; i < k; ++i)
-        if (overlap(ro, others[i]))
-            return fail(MP_ERR_ALIAS, "mp_edge_normalize: out overlaps %s", others[i].name);
+    if (const char *hit = graph_ranges(g).overlapping(ro))
+        return fail(MP_ERR_ALIAS, "mp_edge_normalize: out overlaps %s", hit);
     return edge_normalize_run(g, mode, in, out, static_cast<hipStream_t>(stream));
 }
 

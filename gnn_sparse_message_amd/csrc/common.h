@@ -27,20 +27,46 @@ mp_status hip_fail(hipError_t e, const char *what);
     } while (0)
 
 // ---------------------------------------------------------------- lowering
+// Layout of mp_graph.info (u32 words): the index-range flag, then the digit
+// totals of the two plan passes.  A plan key is 32 - class, so the number of
+// rows of class c is info[kInfoPlanF + 32 - c] (forward) / [kInfoPlanT + 32 - c].
+constexpr int kInfoFlag = 0;
+constexpr int kInfoPlanF = 64;
+constexpr int kInfoPlanT = 64 + 256;
+static_assert(kInfoPlanT + 256 == MP_GRAPH_INFO_WORDS, "info layout");
+
 // Workspace layout for the lowering (byte offsets from the workspace base).
 struct LowerLayout {
     size_t k0, k1, v0, o0;    // [E] u32: ping-pong keys, one ordinal and one endpoint buffer
     size_t hist;              // [256 * tiles] u32 per-tile digit counts (digit-major)
     size_t dtot;              // [256] u32 digit totals of the current pass
-    size_t small;             // [64 + 256 + 256] u32: flag, plan totals fwd, plan totals t
     size_t total;
 };
 LowerLayout lower_layout(int64_t n, int64_t e);
 
-// Enqueue the whole lowering; on success copies the class counts and the
-// index flag back to the host (synchronising `stream`).
+// Enqueue the whole lowering.  Unless `async`, then synchronise `stream` and
+// copy the class counts and the index flag back to the host.
 mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_t n, int64_t e,
-                    mp_graph *g, void *ws, hipStream_t stream, int *bad_index);
+                    mp_graph *g, void *ws, hipStream_t stream, bool async, int *bad_index);
+// Copy the class counts and the index flag of g->info to the host (synchronous).
+mp_status lower_read_info(mp_graph *g, hipStream_t stream, int *bad_index);
+
+// Rows whose length is >= len, from class counts: classes are sorted high to
+// low in the plan, and a class counts only if all its rows qualify (2^(c-1) >= len).
+inline int64_t rows_at_least_host(const int64_t *cc, int64_t len) {
+    int64_t r = 0;
+    for (int c = MP_NUM_CLASSES - 1; c >= 1; --c)
+        if (((int64_t)1 << (c - 1)) >= len) r += cc[c];
+    return r;
+}
+// The same from the device record of a plan (digit totals indexed by 32 - class),
+// never more than the n rows there are.
+__device__ inline int64_t rows_at_least_device(const uint32_t *totals, int64_t len, int64_t n) {
+    int64_t r = 0;
+    for (int c = MP_NUM_CLASSES - 1; c >= 1; --c)
+        if (((int64_t)1 << (c - 1)) >= len) r += totals[32 - c];
+    return r < n ? r : n;
+}
 
 // ---------------------------------------------------------------- SpMM
 // One aggregation over a CSR form (rows = owners).  `x` holds [n, h] features
@@ -51,6 +77,8 @@ struct CsrView {
     const int32_t *order;
     const int32_t *plan;
     const int64_t *class_count;   // host, MP_NUM_CLASSES entries
+    const uint32_t *dev_totals;   // device plan record instead (asynchronously built
+                                  // graph), else nullptr
     int64_t n;
     int64_t e;
 };

@@ -29,13 +29,10 @@ constexpr int kTile = kBlock * kItems;            // 4096 keys per tile
 constexpr int kWaveChunk = kWave * kItems;        // 1024 keys per wave per tile
 constexpr int kBins = 256;                        // 8-bit digits
 constexpr int kDigitBits = 8;                     // at most 8 bits per pass
-constexpr int kSmallFlag = 0;                     // small[0]: index-range flag
-constexpr int kSmallPlanF = 64;                   // small[64..320): digit totals of the forward plan
-constexpr int kSmallPlanT = 64 + kBins;           // small[320..576): digit totals of the transpose plan
-constexpr int kSmallWords = 64 + 2 * kBins;
 constexpr int kPlanBits = 6;                      // plan keys 32 - class lie in [0, 32]
 
 static_assert(kBlock == kBins, "scan and downsweep map one thread to one digit");
+static_assert(kInfoPlanT - kInfoPlanF == kBins, "one plan record holds every digit total");
 
 // ------------------------------------------------------------------ key sources
 // A key source is read at 32-bit offsets from the start of a tile (`at`).
@@ -448,13 +445,25 @@ LowerLayout lower_layout(int64_t n, int64_t e) {
     L.o0 = off; off += ebytes;
     L.hist = off; off += align_up((size_t)kBins * tiles_for(most) * sizeof(uint32_t));
     L.dtot = off; off += align_up(kBins * sizeof(uint32_t));
-    L.small = off; off += align_up(kSmallWords * sizeof(uint32_t));
     L.total = off;
     return L;
 }
 
+mp_status lower_read_info(mp_graph *g, hipStream_t s, int *bad_index) {
+    uint32_t host[MP_GRAPH_INFO_WORDS];
+    MP_HIP_CHECK(hipMemcpyAsync(host, g->info, sizeof(host), hipMemcpyDeviceToHost, s),
+                 "copy of build results to host");
+    MP_HIP_CHECK(hipStreamSynchronize(s), "build synchronisation");
+    *bad_index = host[kInfoFlag] != 0u;
+    for (int c = 0; c < MP_NUM_CLASSES; ++c) {
+        g->class_count[c] = host[kInfoPlanF + (32 - c)];
+        g->class_count_t[c] = host[kInfoPlanT + (32 - c)];
+    }
+    return MP_OK;
+}
+
 mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_t n, int64_t e,
-                    mp_graph *g, void *ws, hipStream_t s, int *bad_index) {
+                    mp_graph *g, void *ws, hipStream_t s, bool async, int *bad_index) {
     const LowerLayout L = lower_layout(n, e);
     char *base = static_cast<char *>(ws);
     uint32_t *k0 = reinterpret_cast<uint32_t *>(base + L.k0);
@@ -463,18 +472,19 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
     uint32_t *o0 = reinterpret_cast<uint32_t *>(base + L.o0);
     uint32_t *hist = reinterpret_cast<uint32_t *>(base + L.hist);
     uint32_t *dtot = reinterpret_cast<uint32_t *>(base + L.dtot);
-    uint32_t *small = reinterpret_cast<uint32_t *>(base + L.small);
+    uint32_t *info = g->info;
 
-    zero_words_kernel<<<1, kBlock, 0, s>>>(small, kSmallWords);
+    // A fill kernel, not a memset: the sequence stays valid under graph capture.
+    zero_words_kernel<<<1, kBlock, 0, s>>>(info, MP_GRAPH_INFO_WORDS);
     if (e > 0) {
         if (idx_dtype == MP_I64)
             intake_kernel<int64_t><<<grid_for(e), kBlock, 0, s>>>(
                 static_cast<const int64_t *>(src), static_cast<const int64_t *>(dst), e, n, g->src,
-                g->dst, small + kSmallFlag);
+                g->dst, info + kInfoFlag);
         else
             intake_kernel<int32_t><<<grid_for(e), kBlock, 0, s>>>(
                 static_cast<const int32_t *>(src), static_cast<const int32_t *>(dst), e, n, g->src,
-                g->dst, small + kSmallFlag);
+                g->dst, info + kInfoFlag);
     }
     MP_HIP_CHECK(hipGetLastError(), "intake launch");
 
@@ -484,21 +494,17 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
     st = lower_direction(g->src, g->dst, e, n, k0, k1, v0, o0, hist, dtot, g->rowptr_t, g->col_t,
                          g->transpose_order, s);
     if (st != MP_OK) return st;
-    st = plan_direction(g->rowptr, n, hist, small + kSmallPlanF, g->row_plan, s);
+    st = plan_direction(g->rowptr, n, hist, info + kInfoPlanF, g->row_plan, s);
     if (st != MP_OK) return st;
-    st = plan_direction(g->rowptr_t, n, hist, small + kSmallPlanT, g->row_plan_t, s);
+    st = plan_direction(g->rowptr_t, n, hist, info + kInfoPlanT, g->row_plan_t, s);
     if (st != MP_OK) return st;
 
-    uint32_t host[kSmallWords];
-    MP_HIP_CHECK(hipMemcpyAsync(host, small, sizeof(host), hipMemcpyDeviceToHost, s),
-                 "copy of build results to host");
-    MP_HIP_CHECK(hipStreamSynchronize(s), "build synchronisation");
-    *bad_index = host[kSmallFlag] != 0u;
-    for (int c = 0; c < MP_NUM_CLASSES; ++c) {
-        g->class_count[c] = host[kSmallPlanF + (32 - c)];
-        g->class_count_t[c] = host[kSmallPlanT + (32 - c)];
+    *bad_index = 0;
+    if (async) {
+        for (int c = 0; c < MP_NUM_CLASSES; ++c) g->class_count[c] = g->class_count_t[c] = 0;
+        return MP_OK;
     }
-    return MP_OK;
+    return lower_read_info(g, s, bad_index);
 }
 
 }  // namespace mp

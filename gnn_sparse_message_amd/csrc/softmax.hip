@@ -73,7 +73,29 @@ struct RowArgs {
     int64_t n, e;
     int32_t n_hub, n_wave, n_lane;
     int32_t blk_hub, blk_wave, blk_lane;
+    const uint32_t *dev_totals;   // asynchronously built graph: rows per class on the
+                                  // device, from which the six fields above are derived
 };
+
+constexpr int64_t kCap = 1 << 22;   // wave and lane owners stride beyond this many blocks
+
+struct RowSplit {
+    int32_t n_hub, n_wave, n_lane, blk_hub, blk_wave, blk_lane;
+};
+
+__host__ __device__ inline RowSplit row_split(int64_t at_hub, int64_t at_wave, int64_t n) {
+    if (at_wave < at_hub) at_wave = at_hub;
+    RowSplit r;
+    r.n_hub = (int32_t)at_hub;
+    r.n_wave = (int32_t)(at_wave - at_hub);
+    r.n_lane = (int32_t)(n - at_wave);
+    const int64_t bw = (r.n_wave + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t bl = (r.n_lane + kBlock - 1) / kBlock;
+    r.blk_hub = r.n_hub;
+    r.blk_wave = (int32_t)(bw < kCap ? bw : kCap);
+    r.blk_lane = (int32_t)(bl < kCap ? bl : kCap);
+    return r;
+}
 
 __device__ __forceinline__ uint32_t coo(const RowArgs &r, int64_t p) {
     const uint32_t o = (uint32_t)r.order[p];
@@ -86,6 +108,10 @@ template <bool kBackward>
 __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
+    RowSplit sp{r.n_hub, r.n_wave, r.n_lane, r.blk_hub, r.blk_wave, r.blk_lane};
+    if (r.dev_totals)   // counts on the device only: the grid is an upper bound
+        sp = row_split(rows_at_least_device(r.dev_totals, kHubLen, r.n),
+                       rows_at_least_device(r.dev_totals, kWaveLen, r.n), r.n);
     int64_t b = blockIdx.x;
     auto finish = [&](int row, MaxSum ms, float dot) {
         if (kBackward) {
@@ -95,7 +121,7 @@ __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
             r.out1[row] = ms.m == -INFINITY ? 0.f : ms.z;
         }
     };
-    if (b < r.blk_hub) {   // hub row: the whole workgroup, lanes strided over the edges
+    if (b < sp.blk_hub) {   // hub row: the whole workgroup, lanes strided over the edges
         __shared__ float s_m[kWavesPerBlock], s_z[kWavesPerBlock];
         const int row = r.plan[b];
         if ((uint32_t)row >= (uint64_t)r.n) return;
@@ -125,11 +151,11 @@ __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
         }
         return;
     }
-    b -= r.blk_hub;
-    if (b < r.blk_wave) {   // long rows: one wave each
-        for (int64_t idx = b * kWavesPerBlock + wv; idx < r.n_wave;
-             idx += (int64_t)r.blk_wave * kWavesPerBlock) {
-            const int row = r.plan[r.n_hub + idx];
+    b -= sp.blk_hub;
+    if (b < sp.blk_wave) {   // long rows: one wave each
+        for (int64_t idx = b * kWavesPerBlock + wv; idx < sp.n_wave;
+             idx += (int64_t)sp.blk_wave * kWavesPerBlock) {
+            const int row = r.plan[sp.n_hub + idx];
             if ((uint32_t)row >= (uint64_t)r.n) continue;
             const int64_t beg = r.rowptr[row], end = r.rowptr[row + 1];
             MaxSum ms{-INFINITY, 0.f};
@@ -145,11 +171,12 @@ __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
         }
         return;
     }
-    b -= r.blk_wave;
+    b -= sp.blk_wave;
+    if (b >= sp.blk_lane) return;   // beyond the work of a device-side split
     // short and empty rows: one lane each
-    for (int64_t idx = b * kBlock + threadIdx.x; idx < r.n_lane;
-         idx += (int64_t)r.blk_lane * kBlock) {
-        const int row = r.plan[r.n_hub + r.n_wave + idx];
+    for (int64_t idx = b * kBlock + threadIdx.x; idx < sp.n_lane;
+         idx += (int64_t)sp.blk_lane * kBlock) {
+        const int row = r.plan[sp.n_hub + sp.n_wave + idx];
         if ((uint32_t)row >= (uint64_t)r.n) continue;
         const int64_t beg = r.rowptr[row], end = r.rowptr[row + 1];
         MaxSum ms{-INFINITY, 0.f};
@@ -187,13 +214,6 @@ __global__ __launch_bounds__(kBlock) void softmax_backward_apply_kernel(
         ds[i] = alpha[i] * (dalpha[i] - rdot[dst[i]]);
 }
 
-int64_t rows_at_least(const int64_t *cc, int64_t len) {
-    int64_t r = 0;
-    for (int c = MP_NUM_CLASSES - 1; c >= 1; --c)
-        if (((int64_t)1 << (c - 1)) >= len) r += cc[c];
-    return r;
-}
-
 RowArgs row_args(const mp_graph *g) {
     RowArgs r;
     r.rowptr = g->rowptr;
@@ -201,17 +221,26 @@ RowArgs row_args(const mp_graph *g) {
     r.plan = g->row_plan;
     r.n = g->num_nodes;
     r.e = g->num_edges;
-    const int64_t at_hub = rows_at_least(g->class_count, kHubLen);
-    const int64_t at_wave = rows_at_least(g->class_count, kWaveLen);
-    r.n_hub = (int32_t)at_hub;
-    r.n_wave = (int32_t)(at_wave - at_hub);
-    r.n_lane = (int32_t)(g->num_nodes - at_wave);
-    constexpr int64_t kCap = 1 << 22;
-    const int64_t bw = (r.n_wave + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t bl = (r.n_lane + kBlock - 1) / kBlock;
-    r.blk_hub = r.n_hub;
-    r.blk_wave = (int32_t)(bw < kCap ? bw : kCap);
-    r.blk_lane = (int32_t)(bl < kCap ? bl : kCap);
+    RowSplit sp;
+    if (g->built == MP_GRAPH_ON_DEVICE) {
+        // Launch for the largest split N and E allow; the kernel derives the real one.
+        r.dev_totals = g->info + kInfoPlanF;
+        auto most = [&](int64_t len) { return r.e / len < r.n ? r.e / len : r.n; };
+        sp.blk_hub = row_split(most(kHubLen), most(kHubLen), most(kHubLen)).blk_hub;
+        sp.blk_wave = row_split(0, most(kWaveLen), most(kWaveLen)).blk_wave;
+        sp.blk_lane = row_split(0, 0, r.n).blk_lane;
+        sp.n_hub = sp.n_wave = sp.n_lane = 0;
+    } else {
+        r.dev_totals = nullptr;
+        sp = row_split(rows_at_least_host(g->class_count, kHubLen),
+                       rows_at_least_host(g->class_count, kWaveLen), r.n);
+    }
+    r.n_hub = sp.n_hub;
+    r.n_wave = sp.n_wave;
+    r.n_lane = sp.n_lane;
+    r.blk_hub = sp.blk_hub;
+    r.blk_wave = sp.blk_wave;
+    r.blk_lane = sp.blk_lane;
     return r;
 }
 

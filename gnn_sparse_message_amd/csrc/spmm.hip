@@ -135,7 +135,33 @@ struct SpmmArgs {
     int32_t n_hub, n_wave, n_group;   // rows of each owner kind, consecutive in the plan
     int32_t blk_hub, blk_wave, blk_group;   // blocks given to each kind (wave and group
                                             // owners stride over their rows)
+    const uint32_t *dev_totals;       // asynchronously built graph: the plan's rows per class
+                                      // on the device; the six fields above are then derived
+    int32_t hub_min, wave_min;        // in the kernel from these owner-size thresholds
 };
+
+constexpr int64_t kMaxKindBlocks = 1 << 22;   // wave and group owners stride beyond this
+
+// Owner partition of a plan: rows of each kind and blocks given to each.
+struct Partition {
+    int32_t n_hub, n_wave, n_group, blk_hub, blk_wave, blk_group;
+};
+
+template <int L>
+__host__ __device__ inline Partition partition(int64_t at_hub, int64_t at_wave, int64_t n) {
+    if (at_wave < at_hub) at_wave = at_hub;
+    Partition p;
+    p.n_hub = (int32_t)at_hub;
+    p.n_wave = (int32_t)(at_wave - at_hub);
+    p.n_group = (int32_t)(n - at_wave);
+    const int64_t rows_per_blk = kBlock / L;
+    const int64_t bw = (p.n_wave + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t bg = (p.n_group + rows_per_blk - 1) / rows_per_blk;
+    p.blk_hub = p.n_hub;
+    p.blk_wave = (int32_t)(bw < kMaxKindBlocks ? bw : kMaxKindBlocks);
+    p.blk_group = (int32_t)(bg < kMaxKindBlocks ? bg : kMaxKindBlocks);
+    return p;
+}
 
 // Accumulate edges [beg, end) of one row into acc.  The team is TL lanes of one
 // wave (TL = 64 for wave and hub owners, TL = L for group owners) and walks the
@@ -260,8 +286,12 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
 
+    Partition pt{a.n_hub, a.n_wave, a.n_group, a.blk_hub, a.blk_wave, a.blk_group};
+    if (a.dev_totals)   // counts on the device only: the grid is an upper bound
+        pt = partition<L>(rows_at_least_device(a.dev_totals, a.hub_min, a.n),
+                          rows_at_least_device(a.dev_totals, a.wave_min, a.n), a.n);
     int64_t b = blockIdx.x;
-    if (b < a.blk_hub) {
+    if (b < pt.blk_hub) {
         // ---- hub row: the whole workgroup
         __shared__ float s_red[kWavesPerBlock][L * VEC];
         const int row = a.plan[b];
@@ -293,12 +323,12 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
         }
         return;
     }
-    b -= a.blk_hub;
-    if (b < a.blk_wave) {
+    b -= pt.blk_hub;
+    if (b < pt.blk_wave) {
         // ---- long rows: one wave each
-        for (int64_t idx = b * kWavesPerBlock + wv; idx < a.n_wave;
-             idx += (int64_t)a.blk_wave * kWavesPerBlock) {
-            const int row = a.plan[a.n_hub + idx];
+        for (int64_t idx = b * kWavesPerBlock + wv; idx < pt.n_wave;
+             idx += (int64_t)pt.blk_wave * kWavesPerBlock) {
+            const int row = a.plan[pt.n_hub + idx];
             if ((uint32_t)row >= (uint64_t)a.n) continue;
             const int64_t beg = a.rowptr[row], end = a.rowptr[row + 1];
 #pragma unroll
@@ -314,12 +344,13 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
         }
         return;
     }
-    b -= a.blk_wave;
+    b -= pt.blk_wave;
+    if (b >= pt.blk_group) return;   // beyond the work of a device-side partition
     // ---- short or empty rows: one group of L lanes each
     constexpr int64_t kRowsPerBlock = kBlock / L;
-    for (int64_t idx = b * kRowsPerBlock + threadIdx.x / L; idx < a.n_group;
-         idx += (int64_t)a.blk_group * kRowsPerBlock) {
-        const int row = a.plan[a.n_hub + a.n_wave + idx];
+    for (int64_t idx = b * kRowsPerBlock + threadIdx.x / L; idx < pt.n_group;
+         idx += (int64_t)pt.blk_group * kRowsPerBlock) {
+        const int row = a.plan[pt.n_hub + pt.n_wave + idx];
         if ((uint32_t)row >= (uint64_t)a.n) continue;
         const int64_t beg = a.rowptr[row], end = a.rowptr[row + 1];
 #pragma unroll
@@ -350,16 +381,6 @@ Thresholds thresholds_for(int L) {
     return t;
 }
 
-// Number of plan rows (from the front) whose length is >= len: the classes are
-// sorted high to low, and a class is counted only if all its rows qualify,
-// i.e. 2^(c-1) >= len.
-int64_t rows_at_least(const int64_t *cc, int64_t len) {
-    int64_t r = 0;
-    for (int c = MP_NUM_CLASSES - 1; c >= 1; --c)
-        if (((int64_t)1 << (c - 1)) >= len) r += cc[c];
-    return r;
-}
-
 template <typename T, int VEC, int L>
 mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *x, int64_t h,
                  float *out, const void *x_own, float *dw, hipStream_t s) {
@@ -379,20 +400,35 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
     a.head_w = (int32_t)(h / heads);
     a.n = csr.n;
     a.e = csr.e;
-    const int64_t at_hub = rows_at_least(csr.class_count, th.hub_min_len);
-    int64_t at_wave = rows_at_least(csr.class_count, th.wave_min_len);
-    if (at_wave < at_hub) at_wave = at_hub;
-    a.n_hub = (int32_t)at_hub;
-    a.n_wave = (int32_t)(at_wave - at_hub);
-    a.n_group = (int32_t)(csr.n - at_wave);
+    a.dev_totals = csr.dev_totals;
+    a.hub_min = th.hub_min_len;
+    a.wave_min = th.wave_min_len;
     // A launch holds at most 2^32 - 1 work-items; wave and group owners stride.
-    constexpr int64_t kMaxKindBlocks = 1 << 22;
-    const int64_t rows_per_blk = kBlock / L;
-    const int64_t blk_wave = (a.n_wave + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t blk_group = (a.n_group + rows_per_blk - 1) / rows_per_blk;
-    a.blk_hub = a.n_hub;
-    a.blk_wave = (int32_t)(blk_wave < kMaxKindBlocks ? blk_wave : kMaxKindBlocks);
-    a.blk_group = (int32_t)(blk_group < kMaxKindBlocks ? blk_group : kMaxKindBlocks);
+    Partition pt;
+    if (csr.dev_totals) {
+        // Counts live on the device: launch for the largest partition N and E
+        // allow (a row of length >= len needs len edges of its own).
+        auto most = [&](int64_t len) {
+            const int64_t r = csr.e / (len > 0 ? len : 1);
+            return r < csr.n ? r : csr.n;
+        };
+        pt = partition<L>(0, 0, 0);
+        const Partition ph = partition<L>(most(th.hub_min_len), most(th.hub_min_len), 0);
+        const Partition pw = partition<L>(0, most(th.wave_min_len), 0);
+        const Partition pg = partition<L>(0, 0, csr.n);
+        pt.blk_hub = ph.blk_hub;
+        pt.blk_wave = pw.blk_wave;
+        pt.blk_group = pg.blk_group;
+    } else {
+        pt = partition<L>(rows_at_least_host(csr.class_count, th.hub_min_len),
+                          rows_at_least_host(csr.class_count, th.wave_min_len), csr.n);
+    }
+    a.n_hub = pt.n_hub;
+    a.n_wave = pt.n_wave;
+    a.n_group = pt.n_group;
+    a.blk_hub = pt.blk_hub;
+    a.blk_wave = pt.blk_wave;
+    a.blk_group = pt.blk_group;
     const int64_t gx = (int64_t)a.blk_hub + a.blk_wave + a.blk_group;
     const int64_t gy = (h + (int64_t)L * VEC - 1) / ((int64_t)L * VEC);
     if (gx <= 0) return MP_OK;

@@ -68,6 +68,9 @@ typedef int32_t mp_dtype;
  * holds rows whose length has c binary digits (lengths 2^(c-1) .. 2^c - 1). */
 #define MP_NUM_CLASSES 33
 
+/* Words of the device-side build record a graph carries (mp_graph.info). */
+#define MP_GRAPH_INFO_WORDS 576
+
 /*
  * mp_graph -- the lowered topology, a plain descriptor in host memory.
  *
@@ -87,6 +90,10 @@ typedef int32_t mp_dtype;
  *   transpose_order    [E]    transpose position -> COO ordinal
  *   row_plan, row_plan_t [N]  rows of each CSR listed by degree class, highest
  *                             class first, ascending row id within a class
+ *   info   [MP_GRAPH_INFO_WORDS] uint32, device: the build's own record (the
+ *                             index check and the rows per class of both
+ *                             plans), read by the compute calls when the host
+ *                             copies below are not filled in yet
  *   class_count, class_count_t  host copies of the number of rows per class
  *
  * Together the two CSR forms hold 2E + 2(N+1) integers and the edge identity
@@ -105,10 +112,16 @@ typedef struct mp_graph {
     int32_t *transpose_order;
     int32_t *row_plan;
     int32_t *row_plan_t;
+    uint32_t *info;
     int64_t class_count[MP_NUM_CLASSES];
     int64_t class_count_t[MP_NUM_CLASSES];
-    uint64_t built;     /* set by a successful mp_graph_build; 0 otherwise */
+    uint64_t built;     /* MP_GRAPH_BUILT, MP_GRAPH_ON_DEVICE or 0 */
 } mp_graph;
+
+/* States of mp_graph.built. */
+#define MP_GRAPH_BUILT     0x6d705f6772617068ull  /* lowered; host counts valid      */
+#define MP_GRAPH_ON_DEVICE 0x6d705f6465766963ull  /* lowered on the stream; counts
+                                                    on the device only (async build) */
 
 /*
  * Device workspace (bytes) that mp_graph_build needs for N nodes and E edges.
@@ -140,6 +153,39 @@ mp_status mp_graph_build_workspace_size(int64_t num_nodes, int64_t num_edges, si
 mp_status mp_graph_build(const void *src, const void *dst, mp_dtype idx_dtype,
                          int64_t num_nodes, int64_t num_edges, mp_graph *g,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The same lowering without the final synchronisation, for back-to-back
+ * batches with a changing topology (tinymesh "Weighted aggregation
+ * experiment", "Limits", names batching and topology changes as open): the
+ * host can enqueue the build of the next batch on one stream while the
+ * current batch computes on another, and the whole sequence can be captured
+ * in a HIP graph (nothing here waits on the host or sets memory with memset).
+ *
+ * Arguments and host-side validation are those of mp_graph_build.  On return
+ * the work is only enqueued: g->built = MP_GRAPH_ON_DEVICE, the host class
+ * counts are zero, and every compute call on `g` reads the counts from g->info
+ * on the device instead (its launch then covers the largest plan N and E
+ * allow; blocks without work exit).  Work on other streams must wait for
+ * `stream` (an event) before using the graph.  The workspace is in use until
+ * the build has run: concurrent builds need separate workspaces.
+ *
+ * The index check is not reported here.  An endpoint outside [0, N) is stored
+ * as 0, so later kernels stay in bounds, but the graph then describes a
+ * different edge list; mp_graph_finish reports it.
+ */
+mp_status mp_graph_build_async(const void *src, const void *dst, mp_dtype idx_dtype,
+                               int64_t num_nodes, int64_t num_edges, mp_graph *g,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Complete an asynchronous build: synchronise `stream`, copy the class counts
+ * from g->info into the descriptor and check the endpoints.  Returns MP_OK and
+ * sets g->built = MP_GRAPH_BUILT, or MP_ERR_INDEX (and g->built = 0) when an
+ * endpoint lay outside [0, N).  A graph that is already MP_GRAPH_BUILT is left
+ * as it is (MP_OK); an unbuilt one gives MP_ERR_GRAPH.
+ */
+mp_status mp_graph_finish(mp_graph *g, void *stream);
 
 /*
  * Forward aggregation Y = A_w X ("Decision"; the left column of the diagram

@@ -64,6 +64,32 @@ def test_graph_struct_layout_matches_ctypes(mp, tmp_path):
         assert getattr(mp._MpGraph, f).offset == off, f
 
 
+def _header_defines():
+    text = open(HEADER).read()
+    return {k: int(v.rstrip("ull"), 0) for k, v in
+            re.findall(r"^#define\s+(MP_\w+)\s+\(?(-?(?:0x[0-9a-fA-F]+|\d+)(?:ull)?)\)?", text, re.M)}
+
+
+def test_binding_constants_match_header(mp):
+    d = _header_defines()
+    assert d["MP_GRAPH_INFO_WORDS"] == mp.GRAPH_INFO_WORDS
+    assert d["MP_GRAPH_BUILT"] == mp.GRAPH_BUILT
+    assert d["MP_GRAPH_ON_DEVICE"] == mp.GRAPH_ON_DEVICE
+    assert d["MP_NUM_CLASSES"] == mp.NUM_CLASSES
+    for name in ("MP_ERR_NULL", "MP_ERR_SHAPE", "MP_ERR_INDEX", "MP_ERR_GRAPH", "MP_F32",
+                 "MP_BF16", "MP_I32", "MP_I64", "MP_NORM_MEAN", "MP_NORM_SYM"):
+        assert d[name] == getattr(mp, name), name
+
+
+def test_finish_rejects_unbuilt_graph(mp):
+    lib = mp._lib
+    g = _fake_graph(mp, 10, 20)
+    assert lib.mp_graph_finish(None, None) == mp.MP_ERR_NULL
+    assert lib.mp_graph_finish(ctypes.byref(g), None) == mp.MP_ERR_GRAPH
+    g.built = mp.GRAPH_BUILT               # an already finished graph is left as it is
+    assert lib.mp_graph_finish(ctypes.byref(g), None) == mp.MP_OK
+
+
 def test_status_strings(mp):
     for code in range(0, -11, -1):
         s = mp.mp_status_string(code)
@@ -88,6 +114,7 @@ def _fake_graph(mp, n, e, base=0x10000):
     g.num_nodes, g.num_edges = n, e
     for i, f in enumerate(mp.Graph._ARRAYS):
         setattr(g, f, base + i * 0x100000)
+    g.info = base + len(mp.Graph._ARRAYS) * 0x100000
     return g
 
 

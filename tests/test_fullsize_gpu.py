@@ -93,3 +93,42 @@ def test_fullsize_outputs_finite_everywhere(run):
     assert np.isfinite(out["dw"]).all()
     empty = np.bincount(wl.dst, minlength=wl.n) == 0
     assert np.all(out["y"][empty] == 0)
+
+
+@pytest.fixture(scope="module")
+def run_heads(run):
+    """Multi-head weights (K = 4 heads of 32 columns) on the same full-size graph,
+    through the forward and the fused backward the benchmark times."""
+    import gnn_sparse_message_amd as mp
+    wl, _ = run
+    k = 4
+    w_np = np.random.default_rng(41).uniform(-1, 1, (wl.e, k)).astype(np.float32)
+    t = upload(wl, DEV, torch.int64)
+    g = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    w = torch.from_numpy(w_np).to(DEV)
+    y = mp.mp_spmm_fwd_heads(g, w, t["x"])
+    dx, dw = mp.mp_spmm_dx_edge_grad_heads(g, w, t["x"], t["dy"])
+    torch.cuda.synchronize()
+    out = {"y": y.cpu().numpy(), "dx": dx.cpu().numpy(), "dw": dw.cpu().numpy()}
+    del t, g, w, y, dx, dw
+    torch.cuda.empty_cache()
+    return wl, k, w_np, out
+
+
+def test_fullsize_heads_sampled(run_heads):
+    wl, k, w_np, out = run_heads
+    rng = np.random.default_rng(5)
+    rows = _sample_rows(np.bincount(wl.dst, minlength=wl.n), rng)
+    ref, s = oracle.forward_heads(wl.n, wl.src, wl.dst, w_np, wl.x, rows=rows)
+    check_close("Y heads rows", out["y"][rows], ref, s, TAU["f32"])
+    rows_t = _sample_rows(np.bincount(wl.src, minlength=wl.n), rng)
+    ref, s = oracle.input_grad_heads(wl.n, wl.src, wl.dst, w_np, wl.dy, rows=rows_t)
+    check_close("dX heads rows", out["dx"][rows_t], ref, s, TAU["f32"])
+    hub = int(np.argmax(np.bincount(wl.src, minlength=wl.n)))
+    edges = np.unique(np.concatenate([rng.choice(wl.e, 20000, replace=False),
+                                      np.nonzero(wl.src == hub)[0][:5000],
+                                      np.array([0, wl.e - 1])])).astype(np.int64)
+    ref, s = oracle.edge_grad_heads(wl.src, wl.dst, wl.x, wl.dy, k, edges=edges)
+    check_close("dw heads edges", out["dw"][edges], ref, s, TAU["f32"])
+    assert np.isfinite(out["y"]).all() and np.isfinite(out["dx"]).all()
+    assert np.isfinite(out["dw"]).all()

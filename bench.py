@@ -94,6 +94,103 @@ def cpu_baseline(wl, sample_edges):
                       "single-threaded fp64 C oracle"}
 
 
+def minibatch_bench(mp, torch, dev, n_batches=64, h=256):
+    """Back-to-back sampled minibatches (2-hop, fanout 15 then 10, 1,024 seeds,
+    topology changing every batch), each one step: build + forward + fused
+    backward, H = 256 fp32.  Topology and weights come from the seeded sampler;
+    X and dY are drawn on the device (torch normal, seed 500 + b).  Three
+    schedules over the same staged batches:
+      sync      -- mp_graph_build (one host synchronisation per batch), then the
+                   compute, all on one stream;
+      async     -- mp_graph_build_async, no host synchronisation, one stream;
+      pipelined -- mp_graph_build_async of batch b + 1 on a second stream while
+                   batch b computes (two workspaces, events between the streams).
+    Returns the timings and the aggregate algorithmic rates."""
+    import synth
+    batches = synth.minibatches(n_batches, h=h, features=False)
+    staged = []
+    for b, wl in enumerate(batches):
+        gen = torch.Generator(device=dev).manual_seed(500 + b)
+        staged.append({"n": wl.n, "e": wl.e, "src": torch.from_numpy(wl.src).to(dev),
+                       "dst": torch.from_numpy(wl.dst).to(dev),
+                       "w": torch.from_numpy(wl.w).to(dev),
+                       "x": torch.randn((wl.n, h), generator=gen, device=dev),
+                       "dy": torch.randn((wl.n, h), generator=gen, device=dev)})
+    n_max = max(t["n"] for t in staged)
+    e_max = max(t["e"] for t in staged)
+    y = torch.empty((n_max, h), device=dev)
+    dx = torch.empty_like(y)
+    dw = torch.empty(e_max, device=dev)
+    ws_bytes = max(mp.mp_graph_build_workspace_size(t["n"], t["e"]) for t in staged)
+    wss = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(2)]
+
+    def compute(t, g):
+        n, e = t["n"], t["e"]
+        mp.mp_spmm_fwd(g, t["w"], t["x"], out=y[:n])
+        mp.mp_spmm_dx_edge_grad(g, t["w"], t["x"], t["dy"], out_dx=dx[:n], out_dw=dw[:e])
+
+    def run_sync():
+        for t in staged:
+            compute(t, mp.mp_graph_build(t["src"], t["dst"], t["n"], workspace=wss[0]))
+
+    def run_async():
+        for t in staged:
+            compute(t, mp.mp_graph_build_async(t["src"], t["dst"], t["n"], workspace=wss[0]))
+
+    sa, sb = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+
+    def run_pipelined():
+        sa.wait_stream(torch.cuda.current_stream(dev))
+        sb.wait_stream(torch.cuda.current_stream(dev))
+        graphs, ready = [None] * len(staged), [None] * len(staged)
+
+        def build(b):
+            with torch.cuda.stream(sb):
+                t = staged[b]
+                graphs[b] = mp.mp_graph_build_async(t["src"], t["dst"], t["n"],
+                                                    workspace=wss[b % 2])
+                ready[b] = torch.cuda.Event()
+                ready[b].record(sb)
+        build(0)
+        for b in range(len(staged)):
+            if b + 1 < len(staged):
+                build(b + 1)
+            with torch.cuda.stream(sa):
+                sa.wait_event(ready[b])
+                compute(staged[b], graphs[b])
+                graphs[b].record_stream(sa)
+                graphs[b] = None
+        torch.cuda.current_stream(dev).wait_stream(sa)
+
+    out = {}
+    for name, fn in (("sync", run_sync), ("async", run_async), ("pipelined", run_pipelined)):
+        fn()                                  # warm-up: allocator, code objects
+        torch.cuda.synchronize()
+        reps = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            reps.append(time.perf_counter() - t0)
+        out[name] = statistics.median(reps) * 1e3
+    b_total = 0
+    for t in staged:
+        bb = algorithmic_bytes(t["n"], t["e"], h, 4, 8)
+        b_total += bb["build"] + bb["fwd"] + bb["dx"] + bb["dw"]
+    e_total = sum(t["e"] for t in staged)
+    res = {"batches": len(staged), "feature_width": h, "feature_dtype": "f32",
+           "edges_total": e_total, "nodes_max": n_max, "edges_max": e_max,
+           "algorithmic_bytes_total": b_total,
+           "step": "per batch: build + mp_spmm_fwd + mp_spmm_dx_edge_grad"}
+    for name, ms in out.items():
+        res[name] = {"ms_total": round(ms, 3), "ms_per_batch": round(ms / len(staged), 4),
+                     "GBps": round(b_total / (ms * 1e-3) / 1e9, 1),
+                     "edges_per_s": round(e_total / (ms * 1e-3), 1)}
+    del staged, y, dx, dw, wss
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +198,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-sample-edges", type=int, default=10_000_000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-minibatch", action="store_true",
+                    help="skip the back-to-back minibatch schedules")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the steps, run one plain 1 GiB -> 1 GiB elementwise copy "
                          "(reference for the HBM byte counters)")
@@ -285,6 +384,13 @@ def main():
         "roofline": roof[dominant],
         "roofline_other_kernels": {k: v for k, v in roof.items() if k != dominant},
     }
+    if not args.no_minibatch:
+        del g, dx_alone, dw_alone
+        torch.cuda.empty_cache()
+        log("minibatch schedules (64 sampled batches) ...")
+        out["minibatch"] = minibatch_bench(mp, torch, dev)
+        log("minibatch ms per batch: " + ", ".join(
+            f"{k} {out['minibatch'][k]['ms_per_batch']}" for k in ("sync", "async", "pipelined")))
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_sample_edges} edges ...")
         out["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_sample_edges, e))

@@ -35,11 +35,14 @@ constexpr int kInfoPlanF = 64;
 constexpr int kInfoPlanT = 64 + 256;
 static_assert(kInfoPlanT + 256 == MP_GRAPH_INFO_WORDS, "info layout");
 
-// Workspace layout for the lowering (byte offsets from the workspace base).
+// Workspace layout for the lowering (byte offsets from the workspace base), per
+// direction (forward, transpose).  When the two directions are sorted one after
+// the other their sort buffers coincide.
 struct LowerLayout {
-    size_t k0, k1, v0, o0;    // [E] u32: ping-pong keys, one ordinal and one endpoint buffer
-    size_t hist;              // [256 * tiles] u32 per-tile digit counts (digit-major)
-    size_t dtot;              // [256] u32 digit totals of the current pass
+    size_t k0[2], k1[2];      // [E] u32: ping-pong keys
+    size_t v0[2], o0[2];      // [E] u32: one ordinal and one endpoint buffer
+    size_t hist[2];           // [256 * tiles] u32 per-tile digit counts (digit-major)
+    size_t dtot[2];           // [256] u32 digit totals of the current pass
     size_t total;
 };
 LowerLayout lower_layout(int64_t n, int64_t e);

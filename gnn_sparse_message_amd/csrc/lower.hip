@@ -9,12 +9,16 @@
 // witness" lowers to edge_order = (2, 0, 1)).
 //
 // How it is computed (gfx950): a least-significant-digit radix sort of
-// (key, ordinal) pairs with 8-bit digits.  Each pass is three kernels:
-//   upsweep   -- every block counts the digits of its contiguous run of tiles;
-//   scan      -- one block per digit turns the per-block counts into offsets;
-//   downsweep -- every block re-reads its tiles, ranks each key among equal
+// (key, ordinal) pairs with digits of at most 8 bits.  Each pass is three kernels:
+//   upsweep   -- every block counts the digits of its 4096-key tile;
+//   scan      -- one block per digit turns the per-tile counts into offsets;
+//   downsweep -- every block re-reads its tile, ranks each key among equal
 //                digits with 64-lane ballots (stable: rank order = input order),
 //                regroups the tile by digit in LDS and writes it out in runs.
+// Small edge lists (a sampled minibatch) are launch-bound rather than
+// bandwidth-bound, so there both directions share every launch and, when a
+// pass has few tiles, each downsweep block sums the per-tile counts it needs
+// itself (no scan kernel).
 // Block-local ranks, never atomics, decide where equal keys land, so the
 // result is the unique stable order.  The opposite endpoint travels with each
 // key, so the last pass writes col[p] = other[order[p]] directly.  Rows are
@@ -42,14 +46,19 @@ struct KeysFromArray {
     __device__ __forceinline__ uint32_t operator()(int i) const { return k[i]; }
 };
 
-// Plan key of row i: 32 - class(length), so the highest class sorts first.
+// Plan key of a row of length d: 32 - class(d), so the highest class sorts
+// first (class 0 for d = 0, else the number of binary digits of d).
+__device__ __forceinline__ uint32_t plan_key(uint32_t d) {
+    const uint32_t c = d == 0 ? 0u : 32u - (uint32_t)__clz(d);
+    return 32u - c;
+}
+
+// Plan key of row i from the row pointers.
 struct KeysFromDegree {
     const int32_t *rowptr;
     __device__ __forceinline__ KeysFromDegree at(int64_t base) const { return {rowptr + base}; }
     __device__ __forceinline__ uint32_t operator()(int i) const {
-        uint32_t d = (uint32_t)(rowptr[i + 1] - rowptr[i]);
-        uint32_t c = d == 0 ? 0u : 32u - (uint32_t)__clz(d);
-        return 32u - c;
+        return plan_key((uint32_t)(rowptr[i + 1] - rowptr[i]));
     }
 };
 
@@ -135,27 +144,54 @@ __device__ __forceinline__ int64_t xcd_local_tile() {
     return x * q + (x < r ? x : r) + (b >> 3);
 }
 
+// Block -> (direction, tile).  A launch for one direction renumbers its tiles
+// per XCD; a launch for both gives blocks [0, ntiles) to direction 0 and the
+// rest to direction 1.
+template <bool kDual>
+__device__ __forceinline__ int64_t block_tile(int64_t ntiles, int &dir) {
+    if constexpr (kDual) {
+        const int64_t b = blockIdx.x;
+        dir = b >= ntiles ? 1 : 0;
+        return dir ? b - ntiles : b;
+    } else {
+        dir = 0;
+        return xcd_local_tile();
+    }
+}
+
+// Payload arrays carried by a pass.  vals are COO ordinals (generated on the
+// first pass), other is the opposite endpoint (so the final pass writes the
+// column array directly, with no gather).
+struct Payload {
+    const uint32_t *vals_in;
+    const uint32_t *other_in;
+    uint32_t *keys_out;
+    uint32_t *vals_out;
+    uint32_t *other_out;
+};
+
+// One direction's share of a pass.
 template <class KeySrc>
-__global__ __launch_bounds__(kBlock) void rs_upsweep(KeySrc keys, int64_t count, int shift,
-                                                     int bits, int64_t ntiles,
-                                                     uint32_t *__restrict__ hist) {
+struct PassDir {
+    KeySrc keys;
+    Payload pl;
+    uint32_t *hist;   // [kBins * ntiles] per-tile digit counts, digit-major
+    uint32_t *dtot;   // [kBins] digit totals (from the scan, or from tile 0 of an
+                      // inline-scan downsweep when not nullptr)
+};
+
+// Digit counts of one tile: k[r] is the key at tile-local index li0 + r * 64,
+// valid below lim.  Writes hist[d * ntiles + t] for every digit d.  Contains
+// barriers: every thread of the block calls it.
+__device__ __forceinline__ void tile_digit_counts(const uint32_t (&k)[kItems], int li0, int lim,
+                                                  int shift, uint32_t mask,
+                                                  uint32_t *__restrict__ hist, int64_t ntiles,
+                                                  int64_t t) {
     __shared__ uint32_t s_cnt[kWavesPerBlock][kBins];
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
     for (int i = threadIdx.x; i < kWavesPerBlock * kBins; i += kBlock) (&s_cnt[0][0])[i] = 0u;
     __syncthreads();
-    const uint32_t mask = (1u << bits) - 1u;
-    const int64_t t = xcd_local_tile();
-    const int64_t left = count - t * kTile;
-    const int lim = left < kTile ? (int)left : kTile;        // keys in this tile
-    const KeySrc tk = keys.at(t * kTile);
-    const int li0 = wv * kWaveChunk + lane;                   // tile-local index, round 0
-    uint32_t k[kItems];
-#pragma unroll
-    for (int r = 0; r < kItems; ++r) {
-        const int li = li0 + r * kWave;
-        k[r] = li < lim ? tk(li) : 0u;
-    }
 #pragma unroll
     for (int r = 0; r < kItems; ++r) {
         const bool valid = li0 + r * kWave < lim;
@@ -172,12 +208,40 @@ __global__ __launch_bounds__(kBlock) void rs_upsweep(KeySrc keys, int64_t count,
     hist[(int64_t)d * ntiles + t] = c;
 }
 
-// One block per digit: exclusive scan, in tile order, of that digit's per-tile
-// counts (in place), and the digit's total.
-__global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist, int64_t ntiles,
-                                                  uint32_t *__restrict__ dtot) {
+template <class KeySrc, bool kDual>
+__global__ __launch_bounds__(kBlock) void rs_upsweep(PassDir<KeySrc> a0, PassDir<KeySrc> a1,
+                                                     int64_t count, int shift, int bits,
+                                                     int64_t ntiles) {
+    int dir;
+    const int64_t t = block_tile<kDual>(ntiles, dir);
+    const PassDir<KeySrc> &a = dir ? a1 : a0;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const uint32_t mask = (1u << bits) - 1u;
+    const int64_t left = count - t * kTile;
+    const int lim = left < kTile ? (int)left : kTile;        // keys in this tile
+    const KeySrc tk = a.keys.at(t * kTile);
+    const int li0 = wv * kWaveChunk + lane;                   // tile-local index, round 0
+    uint32_t k[kItems];
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {
+        const int li = li0 + r * kWave;
+        k[r] = li < lim ? tk(li) : 0u;
+    }
+    tile_digit_counts(k, li0, lim, shift, mask, a.hist, ntiles, t);
+}
+
+// One block per digit (and direction): exclusive scan, in tile order, of that
+// digit's per-tile counts (in place), and the digit's total.
+template <bool kDual>
+__global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist0,
+                                                  uint32_t *__restrict__ dtot0,
+                                                  uint32_t *__restrict__ hist1,
+                                                  uint32_t *__restrict__ dtot1, int64_t ntiles) {
     constexpr int kPer = 16;
-    uint32_t *row = hist + (int64_t)blockIdx.x * ntiles;
+    const int dir = kDual && blockIdx.x >= kBins ? 1 : 0;
+    const int digit = blockIdx.x - dir * kBins;
+    uint32_t *row = (dir ? hist1 : hist0) + (int64_t)digit * ntiles;
     uint32_t carry = 0;
     for (int64_t chunk = 0; chunk < ntiles; chunk += (int64_t)kBlock * kPer) {
         const int64_t beg = chunk + (int64_t)threadIdx.x * kPer;
@@ -197,40 +261,34 @@ __global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist, i
         }
         carry += total;
     }
-    if (threadIdx.x == 0) dtot[blockIdx.x] = carry;
+    if (threadIdx.x == 0) (dir ? dtot1 : dtot0)[digit] = carry;
 }
 
-// Payload arrays carried by a pass.  vals are COO ordinals (generated on the
-// first pass), other is the opposite endpoint (so the final pass writes the
-// column array directly, with no gather).
-struct Payload {
-    const uint32_t *vals_in;
-    const uint32_t *other_in;
-    uint32_t *keys_out;
-    uint32_t *vals_out;
-    uint32_t *other_out;
-};
-
-template <class KeySrc, bool kIotaVals, bool kOther, bool kWriteKeys>
-__global__ __launch_bounds__(kBlock) void rs_downsweep(KeySrc keys, Payload pl, int64_t count,
-                                                       int shift, int bits, int64_t ntiles,
-                                                       const uint32_t *__restrict__ hist,
-                                                       const uint32_t *__restrict__ dtot) {
+// kInlineScan: hist holds raw per-tile counts (no scan kernel ran); each thread
+// sums its digit's counts over all tiles and over the tiles before this one.
+template <class KeySrc, bool kIotaVals, bool kOther, bool kWriteKeys, bool kDual,
+          bool kInlineScan>
+__global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassDir<KeySrc> a1,
+                                                       int64_t count, int shift, int bits,
+                                                       int64_t ntiles) {
     __shared__ uint32_t s_buf[kTile];          // one payload at a time, in tile-sorted order
     __shared__ uint8_t s_dig[kTile];           // digit of each tile-sorted position
     __shared__ uint32_t s_cnt[kWavesPerBlock][kBins];
     __shared__ uint32_t s_tstart[kBins];
     __shared__ uint32_t s_gbase[kBins];
+    int dir;
+    const int64_t t = block_tile<kDual>(ntiles, dir);
+    const PassDir<KeySrc> &a = dir ? a1 : a0;
+    const Payload &pl = a.pl;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wv = tid / kWave;
     const uint32_t mask = (1u << bits) - 1u;
     const uint64_t lanes_below = (1ull << lane) - 1ull;
-    const int64_t t = xcd_local_tile();
     const int64_t tbase = t * kTile;
     const int64_t left = count - tbase;
     const int lim = left < kTile ? (int)left : kTile;        // keys in this tile
-    const KeySrc tk = keys.at(tbase);
+    const KeySrc tk = a.keys.at(tbase);
     const int li0 = wv * kWaveChunk + lane;                   // tile-local index, round 0
 
     for (int i = tid; i < kWavesPerBlock * kBins; i += kBlock) (&s_cnt[0][0])[i] = 0u;
@@ -258,13 +316,34 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(KeySrc keys, Payload pl, 
     const uint32_t c0 = s_cnt[0][tid], c1 = s_cnt[1][tid], c2 = s_cnt[2][tid], c3 = s_cnt[3][tid];
     uint32_t all;
     const uint32_t tstart = block_exclusive_scan(c0 + c1 + c2 + c3, &all);   // barriers inside
-    const uint32_t dbase = block_exclusive_scan(dtot[tid], &all);
+    uint32_t dsum, before_tile;
+    if constexpr (kInlineScan) {
+        // 16 independent loads in flight per step (ntiles is small here).
+        const uint32_t *row = a.hist + (int64_t)tid * ntiles;
+        dsum = 0u;
+        before_tile = 0u;
+        for (int64_t u0 = 0; u0 < ntiles; u0 += 16) {
+            uint32_t c[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) c[j] = u0 + j < ntiles ? row[u0 + j] : 0u;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                dsum += c[j];
+                before_tile += u0 + j < t ? c[j] : 0u;
+            }
+        }
+        if (t == 0 && a.dtot) a.dtot[tid] = dsum;
+    } else {
+        dsum = a.dtot[tid];
+        before_tile = a.hist[(int64_t)tid * ntiles + t];
+    }
+    const uint32_t dbase = block_exclusive_scan(dsum, &all);
     s_cnt[0][tid] = tstart;
     s_cnt[1][tid] = tstart + c0;
     s_cnt[2][tid] = tstart + c0 + c1;
     s_cnt[3][tid] = tstart + c0 + c1 + c2;
     s_tstart[tid] = tstart;
-    s_gbase[tid] = dbase + hist[(int64_t)tid * ntiles + t];
+    s_gbase[tid] = dbase + before_tile;
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < kItems; ++r) {
@@ -320,20 +399,31 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(KeySrc keys, Payload pl, 
     }
 }
 
-// ------------------------------------------------------------------ rows and columns
-// rowptr[i] = number of sorted keys below i (binary search), for i in [0, n].
-__global__ __launch_bounds__(kBlock) void rowptr_kernel(const uint32_t *__restrict__ sorted,
-                                                        int64_t e, int64_t n,
-                                                        int32_t *__restrict__ rowptr) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i <= n; i += stride) {
+// ------------------------------------------------------------------ rows
+// One direction's row pointers: rowptr[i] = number of sorted keys below i.
+struct RowsDir {
+    const uint32_t *sorted;   // the direction's keys in sorted order [e]
+    int32_t *rowptr;          // [n + 1]
+};
+
+// One thread per row pointer (binary search over the sorted keys); with kDual
+// the first half of the grid serves r0, the second half r1.
+template <bool kDual>
+__global__ __launch_bounds__(kBlock) void rowptr_kernel(RowsDir r0, RowsDir r1, int64_t e,
+                                                        int64_t n, int64_t blocks_per_dir) {
+    int64_t b = blockIdx.x;
+    const int dir = kDual && b >= blocks_per_dir ? 1 : 0;
+    b -= dir * blocks_per_dir;
+    const RowsDir &r = dir ? r1 : r0;
+    const int64_t stride = blocks_per_dir * kBlock;
+    for (int64_t i = b * kBlock + threadIdx.x; i <= n; i += stride) {
         int64_t lo = 0, hi = e;
         while (lo < hi) {
             const int64_t mid = (lo + hi) >> 1;
-            if ((int64_t)sorted[mid] < i) lo = mid + 1;
+            if ((int64_t)r.sorted[mid] < i) lo = mid + 1;
             else hi = mid;
         }
-        rowptr[i] = (int32_t)lo;
+        r.rowptr[i] = (int32_t)lo;
     }
 }
 
@@ -352,31 +442,70 @@ int key_bits(int64_t n) {
     return bits > 0 ? bits : 1;   // one pass even for n = 1 (a stable copy)
 }
 
-template <class KeySrc, bool kIota, bool kOther, bool kWriteKeys>
-mp_status radix_pass(KeySrc keys, const Payload &pl, int64_t count, int shift, int bits,
-                     uint32_t *hist, uint32_t *dtot, hipStream_t s) {
+// Edge lists up to this size run both directions in every launch (their
+// workspace then holds a second set of sort buffers).
+constexpr int64_t kDualMaxEdges = (int64_t)1 << 22;
+// Passes over at most this many tiles sum the per-tile counts inside the
+// downsweep instead of launching the scan.
+constexpr int64_t kInlineScanMaxTiles = 64;
+
+bool dual_mode(int64_t e) { return e <= kDualMaxEdges; }
+
+// One radix pass for one direction (d1 unused) or both (kDual).
+template <class KeySrc, bool kIota, bool kOther, bool kWriteKeys, bool kDual>
+mp_status radix_pass(const PassDir<KeySrc> &d0, const PassDir<KeySrc> &d1, int64_t count,
+                     int shift, int bits, hipStream_t s) {
     const int64_t ntiles = tiles_for(count);
-    rs_upsweep<KeySrc><<<(unsigned)ntiles, kBlock, 0, s>>>(keys, count, shift, bits, ntiles, hist);
-    rs_scan<<<kBins, kBlock, 0, s>>>(hist, ntiles, dtot);
-    rs_downsweep<KeySrc, kIota, kOther, kWriteKeys><<<(unsigned)ntiles, kBlock, 0, s>>>(
-        keys, pl, count, shift, bits, ntiles, hist, dtot);
+    const unsigned grid = (unsigned)((kDual ? 2 : 1) * ntiles);
+    rs_upsweep<KeySrc, kDual><<<grid, kBlock, 0, s>>>(d0, d1, count, shift, bits, ntiles);
+    if (ntiles <= kInlineScanMaxTiles) {
+        rs_downsweep<KeySrc, kIota, kOther, kWriteKeys, kDual, true><<<grid, kBlock, 0, s>>>(
+            d0, d1, count, shift, bits, ntiles);
+    } else {
+        rs_scan<kDual><<<(kDual ? 2 : 1) * kBins, kBlock, 0, s>>>(d0.hist, d0.dtot, d1.hist,
+                                                                   d1.dtot, ntiles);
+        rs_downsweep<KeySrc, kIota, kOther, kWriteKeys, kDual, false><<<grid, kBlock, 0, s>>>(
+            d0, d1, count, shift, bits, ntiles);
+    }
     MP_HIP_CHECK(hipGetLastError(), "radix pass launch");
     return MP_OK;
 }
 
-// Stable sort of the edges by key[0..e): the final pass writes the sorted keys
-// to one of k0 / k1 (*sorted), the ordinals to `order` and other[order[p]] to `col`.
-mp_status sort_edges(const int32_t *key, const int32_t *other, int64_t e, int64_t n,
-                     uint32_t *k0, uint32_t *k1, uint32_t *v0, uint32_t *o0, uint32_t *hist,
-                     uint32_t *dtot, int32_t *order, int32_t *col, const uint32_t **sorted,
+// Sort buffers of one direction.
+struct SortBufs {
+    uint32_t *k0, *k1, *v0, *o0, *hist, *dtot;
+};
+
+// One direction of the edge sort: keys, the opposite endpoint, and where the
+// final pass puts the ordinals (order) and endpoints (col).
+struct EdgeDir {
+    const int32_t *key;
+    const int32_t *other;
+    int32_t *order;
+    int32_t *col;
+    SortBufs b;
+};
+
+// Stable sort of the edges by key for each direction given: the final pass
+// writes the ordinals to `order` and other[order[p]] to `col`; sorted[i]
+// receives the buffer holding direction i's sorted keys.  kDual: both
+// directions in every launch; else dirs[0] only.
+template <bool kDual>
+mp_status sort_edges(const EdgeDir *dirs, int64_t e, int64_t n, const uint32_t **sorted,
                      hipStream_t s) {
+    constexpr int kDirs = kDual ? 2 : 1;
     const int bits = key_bits(n);
     const int passes = (bits + kDigitBits - 1) / kDigitBits;
-    const uint32_t *kin = reinterpret_cast<const uint32_t *>(key);
-    Payload pl;
-    pl.vals_in = nullptr;
-    pl.other_in = reinterpret_cast<const uint32_t *>(other);
-    uint32_t *kbuf[2] = {k0, k1};
+    PassDir<KeysFromArray> pd[2];
+    const uint32_t *kin[2];
+    for (int i = 0; i < kDirs; ++i) {
+        kin[i] = reinterpret_cast<const uint32_t *>(dirs[i].key);
+        pd[i].pl.vals_in = nullptr;
+        pd[i].pl.other_in = reinterpret_cast<const uint32_t *>(dirs[i].other);
+        pd[i].hist = dirs[i].b.hist;
+        pd[i].dtot = dirs[i].b.dtot;
+    }
+    if (!kDual) pd[1] = pd[0];
     for (int pass = 0; pass < passes; ++pass) {
         // Split the key bits evenly over the passes (21 bits -> 7 + 7 + 7): fewer
         // bins per pass than 8 + 8 + 5 gives longer output runs per tile.
@@ -386,48 +515,56 @@ mp_status sort_edges(const int32_t *key, const int32_t *other, int64_t e, int64_
         // Payloads alternate between the outputs and v0 / o0 so that the last
         // pass lands in `order` and `col`.
         const bool to_out = (passes - 1 - pass) % 2 == 0;
-        pl.keys_out = kbuf[pass % 2];
-        pl.vals_out = to_out ? reinterpret_cast<uint32_t *>(order) : v0;
-        pl.other_out = to_out ? reinterpret_cast<uint32_t *>(col) : o0;
+        for (int i = 0; i < kDirs; ++i) {
+            const SortBufs &b = dirs[i].b;
+            pd[i].keys = KeysFromArray{kin[i]};
+            pd[i].pl.keys_out = pass % 2 == 0 ? b.k0 : b.k1;
+            pd[i].pl.vals_out = to_out ? reinterpret_cast<uint32_t *>(dirs[i].order) : b.v0;
+            pd[i].pl.other_out = to_out ? reinterpret_cast<uint32_t *>(dirs[i].col) : b.o0;
+        }
+        if (!kDual) pd[1] = pd[0];
         mp_status st = pass == 0
-            ? radix_pass<KeysFromArray, true, true, true>(KeysFromArray{kin}, pl, e, shift, pb,
-                                                           hist, dtot, s)
-            : radix_pass<KeysFromArray, false, true, true>(KeysFromArray{kin}, pl, e, shift, pb,
-                                                            hist, dtot, s);
+            ? radix_pass<KeysFromArray, true, true, true, kDual>(pd[0], pd[1], e, shift, pb, s)
+            : radix_pass<KeysFromArray, false, true, true, kDual>(pd[0], pd[1], e, shift, pb, s);
         if (st != MP_OK) return st;
-        kin = pl.keys_out;
-        pl.vals_in = pl.vals_out;
-        pl.other_in = pl.other_out;
+        for (int i = 0; i < kDirs; ++i) {
+            kin[i] = pd[i].pl.keys_out;
+            pd[i].pl.vals_in = pd[i].pl.vals_out;
+            pd[i].pl.other_in = pd[i].pl.other_out;
+        }
     }
-    *sorted = kin;
+    for (int i = 0; i < kDirs; ++i) sorted[i] = kin[i];
     return MP_OK;
 }
 
-mp_status lower_direction(const int32_t *key, const int32_t *other, int64_t e, int64_t n,
-                          uint32_t *k0, uint32_t *k1, uint32_t *v0, uint32_t *o0, uint32_t *hist,
-                          uint32_t *dtot, int32_t *rowptr, int32_t *col, int32_t *order,
-                          hipStream_t s) {
-    const uint32_t *sorted = k0;
-    if (e > 0) {
-        mp_status st = sort_edges(key, other, e, n, k0, k1, v0, o0, hist, dtot, order, col,
-                                  &sorted, s);
-        if (st != MP_OK) return st;
-    }
-    rowptr_kernel<<<grid_for(n + 1), kBlock, 0, s>>>(sorted, e, n, rowptr);
+// Row pointers of one direction (r1 unused) or both (kDual).
+template <bool kDual>
+mp_status row_pointers(const RowsDir &r0, const RowsDir &r1, int64_t e, int64_t n,
+                       hipStream_t s) {
+    const int64_t per_dir = grid_for(n + 1);
+    rowptr_kernel<kDual><<<(unsigned)((kDual ? 2 : 1) * per_dir), kBlock, 0, s>>>(
+        r0, r1, e, n, per_dir);
     MP_HIP_CHECK(hipGetLastError(), "row pointer launch");
     return MP_OK;
 }
 
-mp_status plan_direction(const int32_t *rowptr, int64_t n, uint32_t *hist, uint32_t *totals,
-                         int32_t *plan, hipStream_t s) {
-    Payload pl;
-    pl.vals_in = nullptr;
-    pl.other_in = nullptr;
-    pl.keys_out = nullptr;
-    pl.vals_out = reinterpret_cast<uint32_t *>(plan);
-    pl.other_out = nullptr;
-    return radix_pass<KeysFromDegree, true, false, false>(KeysFromDegree{rowptr}, pl, n, 0,
-                                                          kPlanBits, hist, totals, s);
+// Degree plans of both directions from their row pointers: one radix pass on
+// the plan key, both directions in each launch (its scan only when there are
+// many row tiles).  The digit totals, i.e. the rows per class, land in
+// totals0 / totals1.
+mp_status plans(int64_t n, mp_graph *g, uint32_t *hist0, uint32_t *hist1, uint32_t *totals0,
+                uint32_t *totals1, hipStream_t s) {
+    PassDir<KeysFromDegree> p0, p1;
+    p0.keys = KeysFromDegree{g->rowptr};
+    p1.keys = KeysFromDegree{g->rowptr_t};
+    p0.pl = Payload{nullptr, nullptr, nullptr, reinterpret_cast<uint32_t *>(g->row_plan), nullptr};
+    p1.pl = Payload{nullptr, nullptr, nullptr, reinterpret_cast<uint32_t *>(g->row_plan_t),
+                    nullptr};
+    p0.hist = hist0;
+    p1.hist = hist1;
+    p0.dtot = totals0;
+    p1.dtot = totals1;
+    return radix_pass<KeysFromDegree, true, false, false, true>(p0, p1, n, 0, kPlanBits, s);
 }
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -439,12 +576,22 @@ LowerLayout lower_layout(int64_t n, int64_t e) {
     size_t off = 0;
     const size_t ebytes = align_up((size_t)(e > 0 ? e : 1) * sizeof(uint32_t));
     const int64_t most = e > n ? e : n;
-    L.k0 = off; off += ebytes;
-    L.k1 = off; off += ebytes;
-    L.v0 = off; off += ebytes;
-    L.o0 = off; off += ebytes;
-    L.hist = off; off += align_up((size_t)kBins * tiles_for(most) * sizeof(uint32_t));
-    L.dtot = off; off += align_up(kBins * sizeof(uint32_t));
+    const size_t hbytes = align_up((size_t)kBins * tiles_for(most) * sizeof(uint32_t));
+    for (int i = 0; i < 2; ++i) {
+        if (i == 1 && !dual_mode(e)) {   // one direction at a time: one set of sort buffers
+            L.k0[1] = L.k0[0];
+            L.k1[1] = L.k1[0];
+            L.v0[1] = L.v0[0];
+            L.o0[1] = L.o0[0];
+        } else {
+            L.k0[i] = off; off += ebytes;
+            L.k1[i] = off; off += ebytes;
+            L.v0[i] = off; off += ebytes;
+            L.o0[i] = off; off += ebytes;
+        }
+        L.hist[i] = off; off += hbytes;
+        L.dtot[i] = off; off += align_up(kBins * sizeof(uint32_t));
+    }
     L.total = off;
     return L;
 }
@@ -466,12 +613,11 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
                     mp_graph *g, void *ws, hipStream_t s, bool async, int *bad_index) {
     const LowerLayout L = lower_layout(n, e);
     char *base = static_cast<char *>(ws);
-    uint32_t *k0 = reinterpret_cast<uint32_t *>(base + L.k0);
-    uint32_t *k1 = reinterpret_cast<uint32_t *>(base + L.k1);
-    uint32_t *v0 = reinterpret_cast<uint32_t *>(base + L.v0);
-    uint32_t *o0 = reinterpret_cast<uint32_t *>(base + L.o0);
-    uint32_t *hist = reinterpret_cast<uint32_t *>(base + L.hist);
-    uint32_t *dtot = reinterpret_cast<uint32_t *>(base + L.dtot);
+    auto at = [&](size_t off) { return reinterpret_cast<uint32_t *>(base + off); };
+    SortBufs b[2];
+    for (int i = 0; i < 2; ++i)
+        b[i] = SortBufs{at(L.k0[i]), at(L.k1[i]), at(L.v0[i]), at(L.o0[i]), at(L.hist[i]),
+                        at(L.dtot[i])};
     uint32_t *info = g->info;
 
     // A fill kernel, not a memset: the sequence stays valid under graph capture.
@@ -488,15 +634,28 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
     }
     MP_HIP_CHECK(hipGetLastError(), "intake launch");
 
-    mp_status st = lower_direction(g->dst, g->src, e, n, k0, k1, v0, o0, hist, dtot, g->rowptr,
-                                   g->col, g->edge_order, s);
-    if (st != MP_OK) return st;
-    st = lower_direction(g->src, g->dst, e, n, k0, k1, v0, o0, hist, dtot, g->rowptr_t, g->col_t,
-                         g->transpose_order, s);
-    if (st != MP_OK) return st;
-    st = plan_direction(g->rowptr, n, hist, info + kInfoPlanF, g->row_plan, s);
-    if (st != MP_OK) return st;
-    st = plan_direction(g->rowptr_t, n, hist, info + kInfoPlanT, g->row_plan_t, s);
+    // Forward CSR: keyed by destination; transpose CSR: keyed by source.
+    const EdgeDir dirs[2] = {{g->dst, g->src, g->edge_order, g->col, b[0]},
+                             {g->src, g->dst, g->transpose_order, g->col_t, b[1]}};
+    // Sorted keys of each direction (not read when e = 0).  One direction at a
+    // time shares the sort buffers, so its row pointers are taken before the
+    // other direction's sort overwrites them.
+    const uint32_t *sorted[2] = {b[0].k0, b[1].k0};
+    mp_status st = MP_OK;
+    if (dual_mode(e)) {
+        if (e > 0) st = sort_edges<true>(dirs, e, n, sorted, s);
+        if (st == MP_OK)
+            st = row_pointers<true>(RowsDir{sorted[0], g->rowptr},
+                                    RowsDir{sorted[1], g->rowptr_t}, e, n, s);
+    } else {
+        for (int i = 0; i < 2 && st == MP_OK; ++i) {
+            st = sort_edges<false>(&dirs[i], e, n, &sorted[i], s);
+            const RowsDir r{sorted[i], i == 0 ? g->rowptr : g->rowptr_t};
+            if (st == MP_OK) st = row_pointers<false>(r, r, e, n, s);
+        }
+    }
+    if (st == MP_OK)
+        st = plans(n, g, b[0].hist, b[1].hist, info + kInfoPlanF, info + kInfoPlanT, s);
     if (st != MP_OK) return st;
 
     *bad_index = 0;

@@ -269,14 +269,15 @@ def _sample_without_replacement(rng, nbr_rows: np.ndarray, k: int) -> np.ndarray
 
 def minibatches(n_batches: int = 64, seed: int = 5, batch_size: int = 1024,
                 fanout=(15, 10), h: int = 256, nbr: Optional[np.ndarray] = None,
-                first: int = 0) -> List[Workload]:
+                first: int = 0, features: bool = True) -> List[Workload]:
     """2-hop sampled subgraphs.  Seeds: disjoint slices of one seeded permutation
     of the base nodes.  Hop 1: each seed samples fanout[0] neighbours; hop 2:
     each newly discovered node samples fanout[1].  Relabel: seeds 0..B-1, then
     new nodes in discovery order; nodes already seen keep their id and are not
     expanded again.  Edges: src = sampled neighbour, dst = the node that sampled
     it, in sampler order.  Batch b draws from seed 500 + b.  Returns batches
-    first .. first + n_batches - 1."""
+    first .. first + n_batches - 1.  The features are drawn after the weights,
+    so features=False gives the same topology and weights."""
     if nbr is None:
         nbr = base_graph(seed)
     n_base = nbr.shape[0]
@@ -309,7 +310,8 @@ def minibatches(n_batches: int = 64, seed: int = 5, batch_size: int = 1024,
         dst = np.concatenate(dsts).astype(np.int64)
         local[n_id] = -1
         w = rng.uniform(0.0, 1.0, src.shape[0]).astype(np.float32)
-        x, dy, _, _ = _features(rng, n_loc, h, "f32")
+        # features=False leaves X and dY out (None): topology and weights only
+        x, dy, _, _ = _features(rng, n_loc, h, "f32") if features else (None, None, None, None)
         out.append(Workload(f"minibatch{b}", n_loc, src, dst, w, x, dy,
                             meta={"n_id": n_id, "batch_size": batch_size}))
     return out

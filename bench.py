@@ -35,8 +35,13 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E peak, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["gnn_sparse_message_amd/csrc/spmm.hip", "gnn_sparse_message_amd/csrc/sddmm.hip",
-                  "gnn_sparse_message_amd/csrc/lower.hip", "gnn_sparse_message_amd/csrc/common.h"]
+# Sources that define each counted kernel: its recorded counter bytes stand only
+# while these files are unchanged.
+KERNEL_SOURCES = {
+    "spmm_kernel": ["gnn_sparse_message_amd/csrc/spmm.hip", "gnn_sparse_message_amd/csrc/common.h"],
+    "sddmm_kernel": ["gnn_sparse_message_amd/csrc/sddmm.hip",
+                     "gnn_sparse_message_amd/csrc/common.h"],
+}
 
 
 def log(*a):
@@ -49,26 +54,28 @@ def algorithmic_bytes(n, e, h, s_feat, s_idx):
             "dw": e * (2 * h * s_feat + 12)}
 
 
-def kernel_source_hash():
+def kernel_source_hash(kernel):
+    """Hash of the source files that define `kernel` (a key of KERNEL_SOURCES)."""
     hsh = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             hsh.update(f.read())
     return hsh.hexdigest()[:16]
 
 
 def measured_traffic(kernel_key):
-    """HBM bytes per launch from the committed counter summary, or None when the
-    kernel sources changed since the counters were taken."""
+    """HBM bytes per launch ("kernel:use" key) from the committed counter
+    summary, or None when that kernel's sources changed since the counters were
+    taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_hash") != kernel_source_hash():
-        return None
     k = rec.get("kernels", {}).get(kernel_key)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    if k is None or k.get("source_hash") != kernel_source_hash(kernel_key.split(":")[0]):
+        return None
+    return k.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(wl, sample_edges):
@@ -303,8 +310,8 @@ def main():
     del alpha, rmax, rsum, dscores, rdot, wn
     # Multi-head weights on the same graph: K heads of H/K columns, w [E, K].
     heads = 4
-    wk = torch.rand((e, heads), generator=torch.Generator(device=dev).manual_seed(7),
-                    device=dev) * 2 - 1
+    wk = torch.empty((e, heads), device=dev).uniform_(
+        -1.0, 1.0, generator=torch.Generator(device=dev).manual_seed(7))
     dwk = torch.empty((e, heads), dtype=torch.float32, device=dev)
     dxk = torch.empty_like(dx)
     standalone["fwd_heads"] = time_op(lambda: mp.mp_spmm_fwd_heads(g, wk, x, out=y))

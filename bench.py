@@ -295,19 +295,18 @@ def main():
     same = bool(torch.equal(dx_alone, dx) and torch.equal(dw_alone, dw))
     # Sparse attention pieces on the same topology (scores = the edge weights).
     alpha = torch.empty_like(w)
-    rmax = torch.empty(n, dtype=torch.float32, device=dev)
-    rsum = torch.empty_like(rmax)
+    rstats = torch.empty((n, 2), dtype=torch.float32, device=dev)
     dscores = torch.empty_like(w)
-    rdot = torch.empty_like(rmax)
+    rdot = torch.empty(n, dtype=torch.float32, device=dev)
     wn = torch.empty_like(w)
-    standalone["edge_softmax"] = time_op(lambda: mp.mp_edge_softmax(g, w, alpha, rmax, rsum))
+    standalone["edge_softmax"] = time_op(lambda: mp.mp_edge_softmax(g, w, alpha, rstats))
     standalone["edge_softmax_backward"] = time_op(
         lambda: mp.mp_edge_softmax_backward(g, alpha, dw, dscores, rdot))
     standalone["edge_normalize_sym"] = time_op(
         lambda: mp.mp_edge_normalize(g, mp.MP_NORM_SYM, w, out=wn))
     log(f"standalone dx {standalone['dx']:.3f} ms, dw {standalone['dw']:.3f} ms, "
         f"equal to the fused results: {same}")
-    del alpha, rmax, rsum, dscores, rdot, wn
+    del alpha, rstats, dscores, rdot, wn
     # Multi-head weights on the same graph: K heads of H/K columns, w [E, K].
     heads = 4
     wk = torch.empty((e, heads), device=dev).uniform_(
@@ -335,6 +334,7 @@ def main():
     # target softmax: row pass reads order + score per edge and writes 2 stats per
     # row; the edge pass reads dst + score, writes alpha.  Backward: row pass reads
     # order + alpha + dalpha, the edge pass dst + alpha + dalpha and writes ds.
+    # (Definition bytes of the operation, not of this implementation's passes.)
     bytes_["edge_softmax"] = 20 * e + 24 * n
     bytes_["edge_softmax_backward"] = 28 * e + 16 * n
     # symmetric normalisation: in, out, src, dst per edge; both row pointers once.

@@ -113,7 +113,7 @@ def _load():
         "mp_spmm_dx_heads": (i32, [gp, vp, i64, vp, i32, i64, vp, vp]),
         "mp_edge_grad_dw_heads": (i32, [gp, vp, vp, i32, i64, i64, vp, vp]),
         "mp_spmm_dx_edge_grad_heads": (i32, [gp, vp, i64, vp, vp, i32, i64, vp, vp, vp]),
-        "mp_edge_softmax": (i32, [gp, vp, vp, vp, vp, vp]),
+        "mp_edge_softmax": (i32, [gp, vp, vp, vp, vp]),
         "mp_edge_softmax_backward": (i32, [gp, vp, vp, vp, vp, vp]),
         "mp_edge_normalize": (i32, [gp, i32, vp, vp, vp]),
         "mp_status_string": (ctypes.c_char_p, [i32]),
@@ -442,17 +442,17 @@ def _edge_f32(name, t, g: Graph):
         raise ValueError(f"{name} must have shape [{g.num_edges}], got {tuple(t.shape)}")
 
 
-def mp_edge_softmax(g: Graph, scores, out_alpha=None, out_row_max=None, out_row_sum=None):
+def mp_edge_softmax(g: Graph, scores, out_alpha=None, out_row_stats=None):
     """Softmax of the edge scores over the incoming edges of each destination:
-    returns (alpha [E] COO order, row_max [N], row_sum [N]), all float32."""
+    returns (alpha [E] in COO order, row_stats [N, 2] holding each row's maximum
+    and sum of exp(score - maximum)), all float32."""
     _edge_f32("scores", scores, g)
     alpha = _out(out_alpha, (g.num_edges,), scores)
-    rmax = _out(out_row_max, (g.num_nodes,), scores)
-    rsum = _out(out_row_sum, (g.num_nodes,), scores)
+    stats = _out(out_row_stats, (g.num_nodes, 2), scores)
     _check(_lib.mp_edge_softmax(ctypes.byref(g._desc), _ptr(scores) if g.num_edges else None,
-                                _ptr(alpha) if g.num_edges else None, _ptr(rmax), _ptr(rsum),
+                                _ptr(alpha) if g.num_edges else None, _ptr(stats),
                                 _stream(scores)), "mp_edge_softmax")
-    return alpha, rmax, rsum
+    return alpha, stats
 
 
 def mp_edge_softmax_backward(g: Graph, alpha, dalpha, out_dscores=None, out_row_dot=None):

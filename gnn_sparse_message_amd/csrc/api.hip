@@ -428,9 +428,9 @@ mp_status mp_spmm_dx_edge_grad_heads(const mp_graph *g, const float *w, int64_t 
 
 namespace {
 // Shared validation of the softmax calls: `edge_in` / `edge_in2` are [E] float
-// inputs, `edge_out` an [E] float output, `row_out` / `row_out2` [N] outputs.
+// inputs, `edge_out` an [E] float output, `row_out` an [N * row_width] output.
 mp_status check_softmax(const mp_graph *g, const float *edge_in, const float *edge_in2,
-                        float *edge_out, float *row_out, float *row_out2, const char *what) {
+                        float *edge_out, float *row_out, int row_width, const char *what) {
     mp_status st = check_graph(g);
     if (st != MP_OK) return st;
     const int64_t n = g->num_nodes, e = g->num_edges;
@@ -439,42 +439,39 @@ mp_status check_softmax(const mp_graph *g, const float *edge_in, const float *ed
         int64_t count;
         const char *name;
     } arr[] = {{edge_in, e, "edge input"}, {edge_in2, edge_in2 ? e : 0, "second edge input"},
-               {edge_out, e, "edge output"}, {row_out, n, "row output"},
-               {row_out2, row_out2 ? n : 0, "second row output"}};
+               {edge_out, e, "edge output"}, {row_out, n * row_width, "row output"}};
     for (const auto &a : arr) {
         if (a.count > 0 && !a.p) return fail(MP_ERR_NULL, "%s: %s is NULL", what, a.name);
-        if (a.p && !aligned(a.p, 4)) return fail(MP_ERR_ALIGN, "%s: %s misaligned", what, a.name);
+        if (a.p && !aligned(a.p, row_width == 2 && a.p == row_out ? 8 : 4))
+            return fail(MP_ERR_ALIGN, "%s: %s misaligned", what, a.name);
         if (a.count > 0 && (st = check_device(a.p, a.name)) != MP_OK) return st;
     }
-    Range outs[3] = {range(edge_out, e, 4, "edge output"), range(row_out, n, 4, "row output"),
-                     range(row_out2, row_out2 ? n : 0, 4, "second row output")};
+    Range outs[2] = {range(edge_out, e, 4, "edge output"),
+                     range(row_out, n * row_width, 4, "row output")};
     RangeList others = graph_ranges(g);
     others.add(range(edge_in, e, 4, "edge input"));
     others.add(range(edge_in2, edge_in2 ? e : 0, 4, "second edge input"));
-    for (int i = 0; i < 3; ++i) {
+    for (int i = 0; i < 2; ++i)
         if (const char *hit = others.overlapping(outs[i]))
             return fail(MP_ERR_ALIAS, "%s: %s overlaps %s", what, outs[i].name, hit);
-        for (int j = i + 1; j < 3; ++j)
-            if (overlap(outs[i], outs[j]))
-                return fail(MP_ERR_ALIAS, "%s: %s overlaps %s", what, outs[i].name, outs[j].name);
-    }
+    if (overlap(outs[0], outs[1]))
+        return fail(MP_ERR_ALIAS, "%s: edge output overlaps row output", what);
     return MP_OK;
 }
 }  // namespace
 
-mp_status mp_edge_softmax(const mp_graph *g, const float *scores, float *alpha, float *row_max,
-                          float *row_sum, void *stream) {
-    mp_status st = check_softmax(g, scores, nullptr, alpha, row_max, row_sum, "mp_edge_softmax");
+mp_status mp_edge_softmax(const mp_graph *g, const float *scores, float *alpha, float *row_stats,
+                          void *stream) {
+    mp_status st = check_softmax(g, scores, nullptr, alpha, row_stats, 2, "mp_edge_softmax");
     if (st != MP_OK) return st;
-    if (!row_sum) return fail(MP_ERR_NULL, "mp_edge_softmax: row_sum is NULL");
-    return edge_softmax_run(g, scores, alpha, row_max, row_sum, static_cast<hipStream_t>(stream));
+    return edge_softmax_run(g, scores, alpha, row_stats, static_cast<hipStream_t>(stream));
 }
 
 mp_status mp_edge_softmax_backward(const mp_graph *g, const float *alpha, const float *dalpha,
                                    float *dscores, float *row_dot, void *stream) {
     if (!dalpha && g && g->num_edges > 0)
         return fail(MP_ERR_NULL, "mp_edge_softmax_backward: dalpha is NULL");
-    mp_status st = check_softmax(g, alpha, dalpha, dscores, row_dot, nullptr,
+    mp_status st = check_softmax(g, alpha, dalpha, dscores, row_dot, 1,
                                  "mp_edge_softmax_backward");
     if (st != MP_OK) return st;
     return edge_softmax_backward_run(g, alpha, dalpha, dscores, row_dot,

@@ -107,8 +107,8 @@ mp_status sddmm_run(const int32_t *src, const int32_t *dst, int64_t e, const voi
                     hipStream_t stream);
 
 // ---------------------------------------------------------------- target softmax
-mp_status edge_softmax_run(const mp_graph *g, const float *s, float *alpha, float *row_max,
-                           float *row_sum, hipStream_t stream);
+mp_status edge_softmax_run(const mp_graph *g, const float *s, float *alpha, float *row_stats,
+                           hipStream_t stream);
 mp_status edge_softmax_backward_run(const mp_graph *g, const float *alpha, const float *dalpha,
                                     float *ds, float *row_dot, hipStream_t stream);
 

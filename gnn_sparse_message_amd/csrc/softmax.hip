@@ -11,8 +11,13 @@
 // (rows in degree-plan order; a workgroup owns a hub row, a wave a long row, a
 // single lane a short row; each owner combines its lanes in a fixed order, no
 // atomics), then one elementwise pass over the edges in COO order, which reads
-// s / alpha / dalpha coalesced and the per-row statistics by dst (node-sized
-// arrays that stay in cache).  The row statistics are outputs of the calls.
+// s / alpha / dalpha coalesced and the per-row statistics by dst.  Both steps
+// are priced by their random reads: the row step gathers one value per edge
+// through edge_order, the edge step one per edge by dst.  So the forward keeps
+// a row's (max, sum) side by side (one 8-byte read per edge), and the backward
+// first writes the products alpha * dalpha into its output (one coalesced
+// pass) and gathers those, instead of gathering alpha and dalpha separately.
+// The row statistics are outputs of the calls.
 #include "common.h"
 
 #include <math.h>
@@ -66,10 +71,9 @@ struct RowArgs {
     const int32_t *rowptr;
     const int32_t *order;
     const int32_t *plan;
-    const float *a;         // scores (forward) or alpha (backward), COO order
-    const float *b;         // dalpha (backward only), COO order
-    float *out0;            // row_max (forward) or row_dot (backward), [N]
-    float *out1;            // row_sum (forward only), [N]
+    const float *a;         // scores (forward) or alpha * dalpha (backward), COO order
+    float2 *stats;          // forward: (row max, row sum) per row, [N]
+    float *dot;             // backward: row sums of alpha * dalpha, [N]
     int64_t n, e;
     int32_t n_hub, n_wave, n_lane;
     int32_t blk_hub, blk_wave, blk_lane;
@@ -103,7 +107,7 @@ __device__ __forceinline__ uint32_t coo(const RowArgs &r, int64_t p) {
 }
 
 // kBackward = false: online max / sum of exp of the scores.
-// kBackward = true : sum of alpha * dalpha.
+// kBackward = true : sum of the products alpha * dalpha.
 template <bool kBackward>
 __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -114,12 +118,8 @@ __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
                        rows_at_least_device(r.dev_totals, kWaveLen, r.n), r.n);
     int64_t b = blockIdx.x;
     auto finish = [&](int row, MaxSum ms, float dot) {
-        if (kBackward) {
-            r.out0[row] = dot;
-        } else {
-            r.out0[row] = ms.m;
-            r.out1[row] = ms.m == -INFINITY ? 0.f : ms.z;
-        }
+        if (kBackward) r.dot[row] = dot;
+        else r.stats[row] = make_float2(ms.m, ms.m == -INFINITY ? 0.f : ms.z);
     };
     if (b < sp.blk_hub) {   // hub row: the whole workgroup, lanes strided over the edges
         __shared__ float s_m[kWavesPerBlock], s_z[kWavesPerBlock];
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
         float dot = 0.f;
         for (int64_t p = beg + threadIdx.x; p < end; p += kBlock) {
             const uint32_t o = coo(r, p);
-            if (kBackward) dot = fmaf(r.a[o], r.b[o], dot);
+            if (kBackward) dot += r.a[o];
             else ms = ms_add(ms, r.a[o]);
         }
         if (kBackward) dot = sum_wave(dot);
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
             float dot = 0.f;
             for (int64_t p = beg + lane; p < end; p += kWave) {
                 const uint32_t o = coo(r, p);
-                if (kBackward) dot = fmaf(r.a[o], r.b[o], dot);
+                if (kBackward) dot += r.a[o];
                 else ms = ms_add(ms, r.a[o]);
             }
             if (kBackward) dot = sum_wave(dot);
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
         float dot = 0.f;
         for (int64_t p = beg; p < end; ++p) {
             const uint32_t o = coo(r, p);
-            if (kBackward) dot = fmaf(r.a[o], r.b[o], dot);
+            if (kBackward) dot += r.a[o];
             else ms = ms_add(ms, r.a[o]);
         }
         finish(row, ms, dot);
@@ -193,15 +193,23 @@ __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
 // alpha_e = exp(s_e - m[dst_e]) / z[dst_e]
 __global__ __launch_bounds__(kBlock) void softmax_apply_kernel(const int32_t *__restrict__ dst,
                                                                const float *__restrict__ s,
-                                                               const float *__restrict__ rmax,
-                                                               const float *__restrict__ rsum,
+                                                               const float2 *__restrict__ stats,
                                                                float *__restrict__ alpha,
                                                                int64_t e) {
     const int64_t stride = (int64_t)gridDim.x * kBlock;
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < e; i += stride) {
-        const int d = dst[i];
-        alpha[i] = expf(s[i] - rmax[d]) / rsum[d];
+        const float2 st = stats[dst[i]];
+        alpha[i] = expf(s[i] - st.x) / st.y;
     }
+}
+
+// p_e = alpha_e * dalpha_e (into the output array, read back by the row step)
+__global__ __launch_bounds__(kBlock) void edge_product_kernel(const float *__restrict__ alpha,
+                                                              const float *__restrict__ dalpha,
+                                                              float *__restrict__ p, int64_t e) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < e; i += stride)
+        p[i] = alpha[i] * dalpha[i];
 }
 
 // ds_e = alpha_e (dalpha_e - t[dst_e])
@@ -252,18 +260,17 @@ unsigned grid_for(int64_t items) {
 
 }  // namespace
 
-mp_status edge_softmax_run(const mp_graph *g, const float *s, float *alpha, float *rmax,
-                           float *rsum, hipStream_t st) {
+mp_status edge_softmax_run(const mp_graph *g, const float *s, float *alpha, float *row_stats,
+                           hipStream_t st) {
     RowArgs r = row_args(g);
     r.a = s;
-    r.b = nullptr;
-    r.out0 = rmax;
-    r.out1 = rsum;
+    r.stats = reinterpret_cast<float2 *>(row_stats);
+    r.dot = nullptr;
     const int64_t gx = (int64_t)r.blk_hub + r.blk_wave + r.blk_lane;
     row_stats_kernel<false><<<(unsigned)gx, kBlock, 0, st>>>(r);
     if (g->num_edges > 0)
-        softmax_apply_kernel<<<grid_for(g->num_edges), kBlock, 0, st>>>(g->dst, s, rmax, rsum,
-                                                                         alpha, g->num_edges);
+        softmax_apply_kernel<<<grid_for(g->num_edges), kBlock, 0, st>>>(
+            g->dst, s, reinterpret_cast<const float2 *>(row_stats), alpha, g->num_edges);
     MP_HIP_CHECK(hipGetLastError(), "edge softmax launch");
     return MP_OK;
 }
@@ -271,11 +278,13 @@ mp_status edge_softmax_run(const mp_graph *g, const float *s, float *alpha, floa
 mp_status edge_softmax_backward_run(const mp_graph *g, const float *alpha, const float *dalpha,
                                     float *ds, float *rdot, hipStream_t st) {
     RowArgs r = row_args(g);
-    r.a = alpha;
-    r.b = dalpha;
-    r.out0 = rdot;
-    r.out1 = nullptr;
+    r.a = ds;                // holds alpha * dalpha until the last step overwrites it
+    r.stats = nullptr;
+    r.dot = rdot;
     const int64_t gx = (int64_t)r.blk_hub + r.blk_wave + r.blk_lane;
+    if (g->num_edges > 0)
+        edge_product_kernel<<<grid_for(g->num_edges), kBlock, 0, st>>>(alpha, dalpha, ds,
+                                                                        g->num_edges);
     row_stats_kernel<true><<<(unsigned)gx, kBlock, 0, st>>>(r);
     if (g->num_edges > 0)
         softmax_backward_apply_kernel<<<grid_for(g->num_edges), kBlock, 0, st>>>(

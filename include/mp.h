@@ -270,19 +270,20 @@ mp_status mp_spmm_dx_edge_grad_heads(const mp_graph *g, const float *w, int64_t 
  * Target normalisation of scalar edge scores, the step a sparse attention layer
  * puts between learned scores and this aggregation ("Limits": scores
  * normalised over the edges of each target).  For every edge e with i = dst_e:
- *   alpha_e = exp(s_e - row_max[i]) / row_sum[i],
- *   row_max[i] = max over the edges into i of s,
- *   row_sum[i] = sum over the edges into i of exp(s - row_max[i]);
- * duplicate edges are separate terms; a row with no edges gets row_max = -inf
- * and row_sum = 0.  Scores must be finite.  Row statistics are computed per
- * destination over the forward CSR (one owner per row, no atomics), alpha in
- * COO order; fp32 throughout.
- *   scores  [E] float32, COO order.    alpha  [E] float32 output, COO order.
- *   row_max, row_sum  [N] float32 outputs.
+ *   alpha_e = exp(s_e - m_i) / z_i,
+ *   m_i = max over the edges into i of s,
+ *   z_i = sum over the edges into i of exp(s - m_i);
+ * duplicate edges are separate terms; a row with no edges gets m = -inf and
+ * z = 0.  Scores must be finite.  Row statistics are computed per destination
+ * over the forward CSR (one owner per row, no atomics), alpha in COO order;
+ * fp32 throughout.
+ *   scores     [E] float32, COO order.    alpha  [E] float32 output, COO order.
+ *   row_stats  [N][2] float32 output: (m_i, z_i) side by side, so the edge pass
+ *              fetches both statistics of a row in one access.
  * Then Y = A_alpha X is mp_spmm_fwd(g, alpha, X, ...).
  */
-mp_status mp_edge_softmax(const mp_graph *g, const float *scores, float *alpha, float *row_max,
-                          float *row_sum, void *stream);
+mp_status mp_edge_softmax(const mp_graph *g, const float *scores, float *alpha, float *row_stats,
+                          void *stream);
 
 /*
  * Backward of mp_edge_softmax: given alpha and the upstream gradient dalpha
@@ -290,6 +291,8 @@ mp_status mp_edge_softmax(const mp_graph *g, const float *scores, float *alpha, 
  * mp_spmm_dx_edge_grad), writes
  *   dscores_e = alpha_e * (dalpha_e - row_dot[dst_e]),
  *   row_dot[i] = sum over the edges into i of alpha * dalpha.
+ * dscores first holds the products alpha * dalpha (one coalesced pass), so the
+ * per-row sums gather one value per edge instead of two.
  *   alpha, dalpha  [E] float32, COO order.   dscores  [E] float32 output.
  *   row_dot  [N] float32 output.
  */

@@ -37,8 +37,8 @@ def _all_outputs(mp, g, t, heads_w):
     out += list(mp.mp_spmm_dx_edge_grad(g, t["w"], t["x"], t["dy"]))
     out += [mp.mp_spmm_fwd_heads(g, heads_w, t["x"]), mp.mp_spmm_dx_heads(g, heads_w, t["dy"])]
     out += list(mp.mp_spmm_dx_edge_grad_heads(g, heads_w, t["x"], t["dy"]))
-    alpha, rmax, rsum = mp.mp_edge_softmax(g, t["w"])
-    out += [alpha, rmax, rsum]
+    alpha, stats = mp.mp_edge_softmax(g, t["w"])
+    out += [alpha, stats]
     out += list(mp.mp_edge_softmax_backward(g, alpha, out[2]))
     out += [mp.mp_edge_normalize(g, mp.MP_NORM_SYM, t["w"])]
     return out

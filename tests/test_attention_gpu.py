@@ -50,9 +50,9 @@ def _softmax(mp, wl, scores):
     t = upload(wl, DEV)
     g = mp.mp_graph_build(t["src"], t["dst"], wl.n)
     s = torch.from_numpy(scores).to(DEV)
-    alpha, rmax, rsum = mp.mp_edge_softmax(g, s)
+    alpha, stats = mp.mp_edge_softmax(g, s)
     torch.cuda.synchronize()
-    return g, t, s, alpha, rmax, rsum
+    return g, t, s, alpha, stats[:, 0], stats[:, 1]
 
 
 def _check_softmax(wl, scores, alpha, rmax, rsum):
@@ -179,6 +179,8 @@ def test_rejections(mp):
         mp.mp_edge_softmax(g, t["w"], out_alpha=t["w"])
     with pytest.raises(ValueError):                      # host memory
         mp.mp_edge_softmax(g, t["w"].cpu())
-    a, _, _ = mp.mp_edge_softmax(g, t["w"])
+    with pytest.raises(ValueError):                      # row statistics are [N, 2]
+        mp.mp_edge_softmax(g, t["w"], out_row_stats=torch.empty(wl.n, device=DEV))
+    a, _ = mp.mp_edge_softmax(g, t["w"])
     with pytest.raises(ValueError):                      # ds aliases dalpha
         mp.mp_edge_softmax_backward(g, a, t["w"], out_dscores=t["w"])

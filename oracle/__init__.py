@@ -57,6 +57,8 @@ def _bind(lib):
                                                    vp, vp]),
         "oracle_edge_grad_heads": (ctypes.c_int, [i64, i64, i64, vp, vp, vp, vp, i64, vp, vp,
                                                   vp]),
+        "oracle_edge_softmax_heads": (None, [i64, i64, i64, vp, vp, vp, vp, vp]),
+        "oracle_edge_softmax_backward_heads": (None, [i64, i64, i64, vp, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -301,3 +303,33 @@ def edge_grad_heads(src, dst, x, dy, k: int, edges=None):
     if rc == -1:
         raise ValueError("feature width is not a multiple of the head count")
     return dw, s
+
+
+def edge_softmax_heads(n: int, dst, s):
+    """Per-head target softmax of scores s [e, k]: alpha [e, k], row_max and
+    row_sum [n, k] (float64)."""
+    dst, s = _i64(dst), _f32(s)
+    if s.ndim != 2 or s.shape[0] != dst.shape[0]:
+        raise ValueError("multi-head scores must be [e, k]")
+    s = np.ascontiguousarray(s)
+    e, k = s.shape
+    alpha = np.empty((e, k), np.float64)
+    rmax = np.empty((n, k), np.float64)
+    rsum = np.empty((n, k), np.float64)
+    _load().oracle_edge_softmax_heads(n, e, k, _p(dst), _p(s), _p(alpha), _p(rmax), _p(rsum))
+    return alpha, rmax, rsum
+
+
+def edge_softmax_backward_heads(n: int, dst, alpha, dalpha):
+    """Per-head backward: ds [e, k], row_dot [n, k] and the scale S [e, k] (float64)."""
+    dst, alpha, dalpha = _i64(dst), _f32(alpha), _f32(dalpha)
+    if alpha.ndim != 2 or alpha.shape != dalpha.shape or alpha.shape[0] != dst.shape[0]:
+        raise ValueError("alpha and dalpha must be [e, k]")
+    alpha, dalpha = np.ascontiguousarray(alpha), np.ascontiguousarray(dalpha)
+    e, k = alpha.shape
+    ds = np.empty((e, k), np.float64)
+    rdot = np.empty((n, k), np.float64)
+    scale = np.empty((e, k), np.float64)
+    _load().oracle_edge_softmax_backward_heads(n, e, k, _p(dst), _p(alpha), _p(dalpha), _p(ds),
+                                               _p(rdot), _p(scale))
+    return ds, rdot, scale

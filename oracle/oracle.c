@@ -475,3 +475,60 @@ int oracle_edge_grad_heads(int64_t e, int64_t h, int64_t k,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Multi-head scores: edge e carries one score per head, s[e*k + q] ([e, k],   */
+/* COO order), and each head is normalised on its own over the edges of each   */
+/* target -- the target softmax above applied to every head's column, the     */
+/* scores of a multi-head attention layer feeding the multi-head aggregation. */
+/* Row statistics are [n, k] (row_max[i*k + q], row_sum[i*k + q]).             */
+/* ------------------------------------------------------------------------- */
+void oracle_edge_softmax_heads(int64_t n, int64_t e, int64_t k, const int64_t *dst,
+                               const float *s, double *alpha, double *row_max,
+                               double *row_sum)
+{
+    int64_t i, j, q;
+    for (i = 0; i < n * k; i++) {
+        row_max[i] = -INFINITY;
+        row_sum[i] = 0.0;
+    }
+    for (j = 0; j < e; j++)
+        for (q = 0; q < k; q++)
+            if ((double)s[j * k + q] > row_max[dst[j] * k + q])
+                row_max[dst[j] * k + q] = (double)s[j * k + q];
+    for (j = 0; j < e; j++)
+        for (q = 0; q < k; q++)
+            row_sum[dst[j] * k + q] += exp((double)s[j * k + q] - row_max[dst[j] * k + q]);
+    for (j = 0; j < e; j++)
+        for (q = 0; q < k; q++)
+            alpha[j * k + q] = exp((double)s[j * k + q] - row_max[dst[j] * k + q])
+                               / row_sum[dst[j] * k + q];
+}
+
+/* Backward per head: ds[e,q] = alpha[e,q] (dalpha[e,q] - t[dst_e,q]),         */
+/* t[i,q] = sum over e into i of alpha[e,q] dalpha[e,q]; S as for one head.    */
+void oracle_edge_softmax_backward_heads(int64_t n, int64_t e, int64_t k, const int64_t *dst,
+                                        const float *alpha, const float *dalpha,
+                                        double *ds, double *row_dot, double *s_scale)
+{
+    int64_t i, j, q;
+    double *row_abs = (double *)malloc((size_t)(n * k > 0 ? n * k : 1) * sizeof(double));
+    for (i = 0; i < n * k; i++) {
+        row_dot[i] = 0.0;
+        row_abs[i] = 0.0;
+    }
+    for (j = 0; j < e; j++)
+        for (q = 0; q < k; q++) {
+            double t = (double)alpha[j * k + q] * (double)dalpha[j * k + q];
+            row_dot[dst[j] * k + q] += t;
+            row_abs[dst[j] * k + q] += fabs(t);
+        }
+    for (j = 0; j < e; j++)
+        for (q = 0; q < k; q++) {
+            int64_t r = dst[j] * k + q;
+            ds[j * k + q] = (double)alpha[j * k + q] * ((double)dalpha[j * k + q] - row_dot[r]);
+            s_scale[j * k + q] = fabs((double)alpha[j * k + q])
+                                 * (fabs((double)dalpha[j * k + q]) + row_abs[r]);
+        }
+    free(row_abs);
+}

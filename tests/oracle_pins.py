@@ -646,4 +646,79 @@ def pin_heads_samples_and_rejection():
         raise AssertionError("width 16 accepted with 3 heads")
 
 
+# --------------------------------------------------------------------------- multi-head softmax
+
+def pin_softmax_heads_scipy_columns():
+    """Every head's column is scipy's softmax over each destination segment, with
+    its own row maximum and log-sum-exp."""
+    from scipy.special import softmax
+    for seed, (n, e, k) in enumerate([(40, 500, 3), (9, 70, 4), (200, 2500, 2)]):
+        rng = np.random.default_rng(400 + seed)
+        dst = rng.integers(0, n, e)
+        sc = (rng.standard_normal((e, k)) * 3).astype(np.float32)
+        alpha, rmax, rsum = oracle.edge_softmax_heads(n, dst, sc)
+        order, bounds = _segments(dst)
+        for i in range(n):
+            ids = order[bounds[i]:bounds[i + 1]]
+            for q in range(k):
+                if ids.size == 0:
+                    assert rmax[i, q] == -np.inf and rsum[i, q] == 0
+                    continue
+                col = sc[ids, q].astype(np.float64)
+                np.testing.assert_allclose(alpha[ids, q], softmax(col), rtol=1e-12, atol=1e-15)
+                assert rmax[i, q] == col.max()
+                np.testing.assert_allclose(np.log(rsum[i, q]) + rmax[i, q],
+                                           np.log(np.exp(col).sum()), rtol=1e-12)
+
+
+def pin_softmax_heads_backward_jacobian():
+    """Per head and row, ds = (diag(a) - a a^T) dalpha."""
+    rng = np.random.default_rng(411)
+    n, e, k = 30, 400, 3
+    dst = rng.integers(0, n, e)
+    alpha = rng.uniform(0.01, 1, (e, k)).astype(np.float32)
+    dalpha = rng.standard_normal((e, k)).astype(np.float32)
+    ds, rdot, scale = oracle.edge_softmax_backward_heads(n, dst, alpha, dalpha)
+    order, bounds = _segments(dst)
+    for i in range(n):
+        ids = order[bounds[i]:bounds[i + 1]]
+        for q in range(k):
+            a = alpha[ids, q].astype(np.float64)
+            d = dalpha[ids, q].astype(np.float64)
+            if ids.size == 0:
+                assert rdot[i, q] == 0
+                continue
+            jac = np.diag(a) - np.outer(a, a)
+            np.testing.assert_allclose(ds[ids, q], jac @ d, rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(rdot[i, q], a @ d, rtol=1e-12, atol=1e-14)
+    assert np.all(scale >= np.abs(ds) * (1 - 1e-12))
+
+
+def pin_multihead_attention_gradient():
+    """Y = per-head A_alpha(S) X with alpha the per-head target softmax of S:
+    d<dY, Y>/dS[e, q] by central differences equals
+    softmax_backward_heads(alpha, edge_grad_heads(X, dY))."""
+    wl = synth.random_graph(8, 36, 6, 421)
+    k = 3
+    sc = np.random.default_rng(8).standard_normal((wl.e, k)).astype(np.float32)
+    dy64 = wl.dy.astype(np.float64)
+
+    def f(scores):
+        a, _, _ = oracle.edge_softmax_heads(wl.n, wl.dst, scores)
+        y, _ = oracle.forward_heads(wl.n, wl.src, wl.dst, a.astype(np.float32), wl.x)
+        return float((dy64 * y).sum())
+
+    alpha, _, _ = oracle.edge_softmax_heads(wl.n, wl.dst, sc)
+    dalpha, _ = oracle.edge_grad_heads(wl.src, wl.dst, wl.x, wl.dy, k)
+    ds, _, _ = oracle.edge_softmax_backward_heads(wl.n, wl.dst, alpha.astype(np.float32),
+                                                  dalpha.astype(np.float32))
+    for j in range(wl.e):
+        for q in range(k):
+            sp, sm = sc.copy(), sc.copy()
+            sp[j, q] += np.float32(1e-2)
+            sm[j, q] -= np.float32(1e-2)
+            fd = (f(sp) - f(sm)) / (float(sp[j, q]) - float(sm[j, q]))
+            assert abs(fd - ds[j, q]) <= 1e-3 * (1 + abs(ds[j, q])), (j, q, fd, ds[j, q])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

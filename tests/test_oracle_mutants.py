@@ -55,6 +55,12 @@ MUTANTS = {
                                 "for (c = q; c < h; c += k) {"),
     "heads_edge_grad_transposed_out": ("            dw[i * k + q] = acc;",
                                        "            dw[q * count + i] = acc;"),
+    "softmax_heads_head_major": ("            alpha[j * k + q] = exp((double)s[j * k + q] - row_max[dst[j] * k + q])",
+                                 "            alpha[j * k + q] = exp((double)s[q * e + j] - row_max[dst[j] * k + q])"),
+    "softmax_heads_shared_row_max": ("            if ((double)s[j * k + q] > row_max[dst[j] * k + q])\n                row_max[dst[j] * k + q] = (double)s[j * k + q];",
+                                     "            if ((double)s[j * k + q] > row_max[dst[j] * k])\n                row_max[dst[j] * k] = (double)s[j * k + q];"),
+    "softmax_backward_heads_row_dot_without_head": ("            row_dot[dst[j] * k + q] += t;",
+                                                    "            row_dot[dst[j] * k] += t;"),
     "softmax_backward_row_dot_unweighted": ("        row_dot[dst[j]] += (double)alpha[j] * (double)dalpha[j];",
                                             "        row_dot[dst[j]] += (double)dalpha[j];"),
 }

@@ -16,7 +16,7 @@ turns status codes into exceptions.
     wn = mp_edge_normalize(g, MP_NORM_SYM, w)      # w / sqrt(deg_out(src) deg_in(dst))
 
 (tinymesh "Weighted aggregation experiment": "Decision", "Edge order is
-explicit".)  The library must be built (``python -m gnn_sparse_message_amd._build``
+explicit".)  The library must be built (``python gnn_sparse_message_amd/_build.py``
 or ``__graft_entry__.build()``); importing this package fails loudly otherwise.
 """
 from __future__ import annotations
@@ -31,7 +31,8 @@ __all__ = [
     "mp_graph_build_workspace_size", "mp_spmm_fwd",
     "mp_spmm_dx", "mp_edge_grad_dw", "mp_spmm_dx_edge_grad", "mp_spmm_fwd_heads",
     "mp_spmm_dx_heads", "mp_edge_grad_dw_heads", "mp_spmm_dx_edge_grad_heads", "mp_edge_softmax",
-    "mp_edge_softmax_backward", "mp_edge_normalize", "MP_NORM_MEAN", "MP_NORM_SYM",
+    "mp_edge_softmax_backward", "mp_edge_softmax_heads", "mp_edge_softmax_backward_heads",
+    "mp_edge_normalize", "MP_NORM_MEAN", "MP_NORM_SYM",
     "mp_status_string", "mp_version", "library_path",
     "NUM_CLASSES",
 ]
@@ -96,7 +97,8 @@ def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
             f"{_LIB_PATH} is missing: the HIP library has not been built "
-            "(run `python -m gnn_sparse_message_amd._build`). There is no fallback.")
+            "(run `python __graft_entry__.py` or `python gnn_sparse_message_amd/_build.py`). "
+            "There is no fallback.")
     lib = ctypes.CDLL(_LIB_PATH)
     i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
     gp = ctypes.POINTER(_MpGraph)
@@ -115,6 +117,8 @@ def _load():
         "mp_spmm_dx_edge_grad_heads": (i32, [gp, vp, i64, vp, vp, i32, i64, vp, vp, vp]),
         "mp_edge_softmax": (i32, [gp, vp, vp, vp, vp]),
         "mp_edge_softmax_backward": (i32, [gp, vp, vp, vp, vp, vp]),
+        "mp_edge_softmax_heads": (i32, [gp, vp, i64, vp, vp, vp]),
+        "mp_edge_softmax_backward_heads": (i32, [gp, vp, vp, i64, vp, vp, vp]),
         "mp_edge_normalize": (i32, [gp, i32, vp, vp, vp]),
         "mp_status_string": (ctypes.c_char_p, [i32]),
         "mp_last_error_detail": (ctypes.c_char_p, []),
@@ -466,6 +470,44 @@ def mp_edge_softmax_backward(g: Graph, alpha, dalpha, out_dscores=None, out_row_
                                          _ptr(dalpha) if g.num_edges else None,
                                          _ptr(ds) if g.num_edges else None, _ptr(rdot),
                                          _stream(alpha)), "mp_edge_softmax_backward")
+    return ds, rdot
+
+
+def _edge_heads_f32(name, t, g: Graph) -> int:
+    """Check t as [E, K] float32 (multi-head edge values); returns K."""
+    _need_tensor(name, t)
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if t.dim() != 2 or t.shape[0] != g.num_edges or t.shape[1] < 1:
+        raise ValueError(f"{name} must have shape [{g.num_edges}, K], got {tuple(t.shape)}")
+    return int(t.shape[1])
+
+
+def mp_edge_softmax_heads(g: Graph, scores, out_alpha=None, out_row_stats=None):
+    """Per-head softmax of scores [E, K] over each destination's edges: returns
+    (alpha [E, K], row_stats [N, K, 2] = (maximum, sum)), float32."""
+    k = _edge_heads_f32("scores", scores, g)
+    alpha = _out(out_alpha, (g.num_edges, k), scores)
+    stats = _out(out_row_stats, (g.num_nodes, k, 2), scores)
+    _check(_lib.mp_edge_softmax_heads(ctypes.byref(g._desc),
+                                      _ptr(scores) if g.num_edges else None, k,
+                                      _ptr(alpha) if g.num_edges else None, _ptr(stats),
+                                      _stream(scores)), "mp_edge_softmax_heads")
+    return alpha, stats
+
+
+def mp_edge_softmax_backward_heads(g: Graph, alpha, dalpha, out_dscores=None, out_row_dot=None):
+    """Per-head backward: returns (dscores [E, K], row_dot [N, K])."""
+    k = _edge_heads_f32("alpha", alpha, g)
+    if _edge_heads_f32("dalpha", dalpha, g) != k:
+        raise ValueError("alpha and dalpha must have the same number of heads")
+    ds = _out(out_dscores, (g.num_edges, k), alpha)
+    rdot = _out(out_row_dot, (g.num_nodes, k), alpha)
+    _check(_lib.mp_edge_softmax_backward_heads(ctypes.byref(g._desc),
+                                               _ptr(alpha) if g.num_edges else None,
+                                               _ptr(dalpha) if g.num_edges else None, k,
+                                               _ptr(ds) if g.num_edges else None, _ptr(rdot),
+                                               _stream(alpha)), "mp_edge_softmax_backward_heads")
     return ds, rdot
 
 

@@ -11,6 +11,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -195,3 +196,13 @@ def test_product_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
                 assert "oracle.c" not in text and "liboracle" not in text, f
+
+
+def test_build_script_loads_without_the_library():
+    """build() must work on a fresh tree, where the package cannot be imported yet
+    (it loads libmp.so at import): the build script is loaded by path."""
+    code = ("import sys, __graft_entry__ as ge\n"
+            "m = ge._build_module()\n"
+            "assert callable(m.build) and m.ARCH == 'gfx950'\n"
+            "assert 'gnn_sparse_message_amd' not in sys.modules\n")
+    subprocess.run([sys.executable, "-c", code], cwd=ROOT, check=True)

@@ -318,6 +318,15 @@ def main():
         lambda: mp.mp_spmm_dx_edge_grad_heads(g, wk, x, dy, out_dx=dxk, out_dw=dwk))
     same_heads = bool(torch.equal(mp.mp_spmm_dx_heads(g, wk, dy), dxk)
                       and torch.equal(mp.mp_edge_grad_dw_heads(g, x, dy, heads), dwk))
+    # per-head softmax of [E, K] scores (the multi-head weights as scores)
+    ak = torch.empty_like(wk)
+    sk = torch.empty((n, heads, 2), dtype=torch.float32, device=dev)
+    standalone["edge_softmax_heads"] = time_op(lambda: mp.mp_edge_softmax_heads(g, wk, ak, sk))
+    dsk = torch.empty_like(wk)
+    rdk = torch.empty((n, heads), dtype=torch.float32, device=dev)
+    standalone["edge_softmax_backward_heads"] = time_op(
+        lambda: mp.mp_edge_softmax_backward_heads(g, ak, dwk, dsk, rdk))
+    del ak, sk, dsk, rdk
     log(f"heads={heads}: fwd {standalone['fwd_heads']:.3f} ms, fused bwd "
         f"{standalone['bwd_heads']:.3f} ms, equal to the separate calls: {same_heads}")
     del wk, dwk, dxk
@@ -342,6 +351,9 @@ def main():
     # multi-head: the edge's weight (or dw) term grows from 4 to 4K bytes.
     bytes_["fwd_heads"] = bytes_["fwd"] + 4 * (heads - 1) * e
     bytes_["bwd_heads"] = bytes_["dx"] + bytes_["dw"] + 8 * (heads - 1) * e
+    # per-head softmax: the single-head bytes with K values per edge and per row
+    bytes_["edge_softmax_heads"] = 4 * e + 16 * e * heads + 24 * n * heads
+    bytes_["edge_softmax_backward_heads"] = 8 * e + 20 * e * heads + 16 * n * heads
     ms_step = t_total / args.steps * 1e3
 
     def rate(nbytes, ms):

@@ -427,30 +427,34 @@ mp_status mp_spmm_dx_edge_grad_heads(const mp_graph *g, const float *w, int64_t 
 }
 
 namespace {
-// Shared validation of the softmax calls: `edge_in` / `edge_in2` are [E] float
-// inputs, `edge_out` an [E] float output, `row_out` an [N * row_width] output.
-mp_status check_softmax(const mp_graph *g, const float *edge_in, const float *edge_in2,
-                        float *edge_out, float *row_out, int row_width, const char *what) {
+// Shared validation of the softmax calls: `edge_in` / `edge_in2` are [E, K]
+// float inputs, `edge_out` an [E, K] float output, `row_out` an
+// [N, K, row_width] output.
+mp_status check_softmax(const mp_graph *g, int64_t heads, const float *edge_in,
+                        const float *edge_in2, float *edge_out, float *row_out, int row_width,
+                        const char *what) {
     mp_status st = check_graph(g);
     if (st != MP_OK) return st;
+    if (heads < 1 || heads > (1 << 20))
+        return fail(MP_ERR_SHAPE, "%s: head count %lld outside [1, 2^20]", what, (long long)heads);
     const int64_t n = g->num_nodes, e = g->num_edges;
+    const int64_t ek = e * heads, nk = n * heads * row_width;
     const struct {
         const void *p;
         int64_t count;
         const char *name;
-    } arr[] = {{edge_in, e, "edge input"}, {edge_in2, edge_in2 ? e : 0, "second edge input"},
-               {edge_out, e, "edge output"}, {row_out, n * row_width, "row output"}};
+    } arr[] = {{edge_in, ek, "edge input"}, {edge_in2, edge_in2 ? ek : 0, "second edge input"},
+               {edge_out, ek, "edge output"}, {row_out, nk, "row output"}};
     for (const auto &a : arr) {
         if (a.count > 0 && !a.p) return fail(MP_ERR_NULL, "%s: %s is NULL", what, a.name);
         if (a.p && !aligned(a.p, row_width == 2 && a.p == row_out ? 8 : 4))
             return fail(MP_ERR_ALIGN, "%s: %s misaligned", what, a.name);
         if (a.count > 0 && (st = check_device(a.p, a.name)) != MP_OK) return st;
     }
-    Range outs[2] = {range(edge_out, e, 4, "edge output"),
-                     range(row_out, n * row_width, 4, "row output")};
+    Range outs[2] = {range(edge_out, ek, 4, "edge output"), range(row_out, nk, 4, "row output")};
     RangeList others = graph_ranges(g);
-    others.add(range(edge_in, e, 4, "edge input"));
-    others.add(range(edge_in2, edge_in2 ? e : 0, 4, "second edge input"));
+    others.add(range(edge_in, ek, 4, "edge input"));
+    others.add(range(edge_in2, edge_in2 ? ek : 0, 4, "second edge input"));
     for (int i = 0; i < 2; ++i)
         if (const char *hit = others.overlapping(outs[i]))
             return fail(MP_ERR_ALIAS, "%s: %s overlaps %s", what, outs[i].name, hit);
@@ -458,24 +462,46 @@ mp_status check_softmax(const mp_graph *g, const float *edge_in, const float *ed
         return fail(MP_ERR_ALIAS, "%s: edge output overlaps row output", what);
     return MP_OK;
 }
+
+mp_status softmax_impl(const mp_graph *g, const float *scores, int64_t heads, float *alpha,
+                       float *row_stats, void *stream, const char *what) {
+    mp_status st = check_softmax(g, heads, scores, nullptr, alpha, row_stats, 2, what);
+    if (st != MP_OK) return st;
+    return edge_softmax_run(g, scores, heads, alpha, row_stats, static_cast<hipStream_t>(stream));
+}
+
+mp_status softmax_backward_impl(const mp_graph *g, const float *alpha, const float *dalpha,
+                                int64_t heads, float *dscores, float *row_dot, void *stream,
+                                const char *what) {
+    if (!dalpha && g && g->num_edges > 0) return fail(MP_ERR_NULL, "%s: dalpha is NULL", what);
+    mp_status st = check_softmax(g, heads, alpha, dalpha, dscores, row_dot, 1, what);
+    if (st != MP_OK) return st;
+    return edge_softmax_backward_run(g, alpha, dalpha, heads, dscores, row_dot,
+                                     static_cast<hipStream_t>(stream));
+}
 }  // namespace
 
 mp_status mp_edge_softmax(const mp_graph *g, const float *scores, float *alpha, float *row_stats,
                           void *stream) {
-    mp_status st = check_softmax(g, scores, nullptr, alpha, row_stats, 2, "mp_edge_softmax");
-    if (st != MP_OK) return st;
-    return edge_softmax_run(g, scores, alpha, row_stats, static_cast<hipStream_t>(stream));
+    return softmax_impl(g, scores, 1, alpha, row_stats, stream, "mp_edge_softmax");
 }
 
 mp_status mp_edge_softmax_backward(const mp_graph *g, const float *alpha, const float *dalpha,
                                    float *dscores, float *row_dot, void *stream) {
-    if (!dalpha && g && g->num_edges > 0)
-        return fail(MP_ERR_NULL, "mp_edge_softmax_backward: dalpha is NULL");
-    mp_status st = check_softmax(g, alpha, dalpha, dscores, row_dot, 1,
+    return softmax_backward_impl(g, alpha, dalpha, 1, dscores, row_dot, stream,
                                  "mp_edge_softmax_backward");
-    if (st != MP_OK) return st;
-    return edge_softmax_backward_run(g, alpha, dalpha, dscores, row_dot,
-                                     static_cast<hipStream_t>(stream));
+}
+
+mp_status mp_edge_softmax_heads(const mp_graph *g, const float *scores, int64_t heads,
+                                float *alpha, float *row_stats, void *stream) {
+    return softmax_impl(g, scores, heads, alpha, row_stats, stream, "mp_edge_softmax_heads");
+}
+
+mp_status mp_edge_softmax_backward_heads(const mp_graph *g, const float *alpha,
+                                         const float *dalpha, int64_t heads, float *dscores,
+                                         float *row_dot, void *stream) {
+    return softmax_backward_impl(g, alpha, dalpha, heads, dscores, row_dot, stream,
+                                 "mp_edge_softmax_backward_heads");
 }
 
 mp_status mp_edge_normalize(const mp_graph *g, int32_t mode, const float *in, float *out,

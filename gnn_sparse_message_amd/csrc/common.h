@@ -107,10 +107,11 @@ mp_status sddmm_run(const int32_t *src, const int32_t *dst, int64_t e, const voi
                     hipStream_t stream);
 
 // ---------------------------------------------------------------- target softmax
-mp_status edge_softmax_run(const mp_graph *g, const float *s, float *alpha, float *row_stats,
-                           hipStream_t stream);
+// `heads` = K score columns per edge ([E, K]); statistics are [N, K].
+mp_status edge_softmax_run(const mp_graph *g, const float *s, int64_t heads, float *alpha,
+                           float *row_stats, hipStream_t stream);
 mp_status edge_softmax_backward_run(const mp_graph *g, const float *alpha, const float *dalpha,
-                                    float *ds, float *row_dot, hipStream_t stream);
+                                    int64_t heads, float *ds, float *row_dot, hipStream_t stream);
 
 // ---------------------------------------------------------------- degree normalisation
 mp_status edge_normalize_run(const mp_graph *g, int mode, const float *in, float *out,

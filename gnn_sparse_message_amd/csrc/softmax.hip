@@ -7,6 +7,9 @@
 // and its backward  ds_e = alpha_e (dalpha_e - t_i),  t_i = sum over the row of
 // alpha * dalpha.
 //
+// With K heads the scores are [E, K] (edge-major, COO order) and every head is
+// normalised on its own; statistics are then [N, K].
+//
 // Both run in two steps: per-destination row statistics over the forward CSR
 // (rows in degree-plan order; a workgroup owns a hub row, a wave a long row, a
 // single lane a short row; each owner combines its lanes in a fixed order, no
@@ -79,6 +82,7 @@ struct RowArgs {
     int32_t blk_hub, blk_wave, blk_lane;
     const uint32_t *dev_totals;   // asynchronously built graph: rows per class on the
                                   // device, from which the six fields above are derived
+    int32_t heads;                // K values per edge ([E, K]) with the multi-head kernels
 };
 
 constexpr int64_t kCap = 1 << 22;   // wave and lane owners stride beyond this many blocks
@@ -108,46 +112,54 @@ __device__ __forceinline__ uint32_t coo(const RowArgs &r, int64_t p) {
 
 // kBackward = false: online max / sum of exp of the scores.
 // kBackward = true : sum of the products alpha * dalpha.
-template <bool kBackward>
+// kHeads: the edge values are [E, K] and each head is reduced on its own (the
+// owner walks its row once per head; the row's values of all heads share cache
+// lines, so the later walks hit in L2); statistics are [N, K].
+template <bool kBackward, bool kHeads>
 __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
+    const int K = kHeads ? r.heads : 1;
     RowSplit sp{r.n_hub, r.n_wave, r.n_lane, r.blk_hub, r.blk_wave, r.blk_lane};
     if (r.dev_totals)   // counts on the device only: the grid is an upper bound
         sp = row_split(rows_at_least_device(r.dev_totals, kHubLen, r.n),
                        rows_at_least_device(r.dev_totals, kWaveLen, r.n), r.n);
     int64_t b = blockIdx.x;
-    auto finish = [&](int row, MaxSum ms, float dot) {
-        if (kBackward) r.dot[row] = dot;
-        else r.stats[row] = make_float2(ms.m, ms.m == -INFINITY ? 0.f : ms.z);
+    auto finish = [&](int64_t slot, MaxSum ms, float dot) {   // slot = row * K + head
+        if (kBackward) r.dot[slot] = dot;
+        else r.stats[slot] = make_float2(ms.m, ms.m == -INFINITY ? 0.f : ms.z);
     };
+    auto value = [&](uint32_t o, int q) { return kHeads ? r.a[(int64_t)o * K + q] : r.a[o]; };
     if (b < sp.blk_hub) {   // hub row: the whole workgroup, lanes strided over the edges
         __shared__ float s_m[kWavesPerBlock], s_z[kWavesPerBlock];
         const int row = r.plan[b];
         if ((uint32_t)row >= (uint64_t)r.n) return;
         const int64_t beg = r.rowptr[row], end = r.rowptr[row + 1];
-        MaxSum ms{-INFINITY, 0.f};
-        float dot = 0.f;
-        for (int64_t p = beg + threadIdx.x; p < end; p += kBlock) {
-            const uint32_t o = coo(r, p);
-            if (kBackward) dot += r.a[o];
-            else ms = ms_add(ms, r.a[o]);
-        }
-        if (kBackward) dot = sum_wave(dot);
-        else ms = ms_wave(ms);
-        if (lane == 0) {
-            s_m[wv] = kBackward ? dot : ms.m;
-            s_z[wv] = ms.z;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            MaxSum t{s_m[0], s_z[0]};
-            float d = s_m[0];
-            for (int w = 1; w < kWavesPerBlock; ++w) {
-                if (kBackward) d += s_m[w];
-                else t = ms_merge(t, MaxSum{s_m[w], s_z[w]});
+        for (int q = 0; q < K; ++q) {
+            MaxSum ms{-INFINITY, 0.f};
+            float dot = 0.f;
+            for (int64_t p = beg + threadIdx.x; p < end; p += kBlock) {
+                const uint32_t o = coo(r, p);
+                if (kBackward) dot += value(o, q);
+                else ms = ms_add(ms, value(o, q));
             }
-            finish(row, t, d);
+            if (kBackward) dot = sum_wave(dot);
+            else ms = ms_wave(ms);
+            if (lane == 0) {
+                s_m[wv] = kBackward ? dot : ms.m;
+                s_z[wv] = ms.z;
+            }
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                MaxSum t{s_m[0], s_z[0]};
+                float d = s_m[0];
+                for (int w = 1; w < kWavesPerBlock; ++w) {
+                    if (kBackward) d += s_m[w];
+                    else t = ms_merge(t, MaxSum{s_m[w], s_z[w]});
+                }
+                finish((int64_t)row * K + q, t, d);
+            }
+            if (kHeads) __syncthreads();   // s_m / s_z are reused by the next head
         }
         return;
     }
@@ -158,16 +170,18 @@ __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
             const int row = r.plan[sp.n_hub + idx];
             if ((uint32_t)row >= (uint64_t)r.n) continue;
             const int64_t beg = r.rowptr[row], end = r.rowptr[row + 1];
-            MaxSum ms{-INFINITY, 0.f};
-            float dot = 0.f;
-            for (int64_t p = beg + lane; p < end; p += kWave) {
-                const uint32_t o = coo(r, p);
-                if (kBackward) dot += r.a[o];
-                else ms = ms_add(ms, r.a[o]);
+            for (int q = 0; q < K; ++q) {
+                MaxSum ms{-INFINITY, 0.f};
+                float dot = 0.f;
+                for (int64_t p = beg + lane; p < end; p += kWave) {
+                    const uint32_t o = coo(r, p);
+                    if (kBackward) dot += value(o, q);
+                    else ms = ms_add(ms, value(o, q));
+                }
+                if (kBackward) dot = sum_wave(dot);
+                else ms = ms_wave(ms);
+                if (lane == 0) finish((int64_t)row * K + q, ms, dot);
             }
-            if (kBackward) dot = sum_wave(dot);
-            else ms = ms_wave(ms);
-            if (lane == 0) finish(row, ms, dot);
         }
         return;
     }
@@ -179,26 +193,37 @@ __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
         const int row = r.plan[sp.n_hub + sp.n_wave + idx];
         if ((uint32_t)row >= (uint64_t)r.n) continue;
         const int64_t beg = r.rowptr[row], end = r.rowptr[row + 1];
-        MaxSum ms{-INFINITY, 0.f};
-        float dot = 0.f;
-        for (int64_t p = beg; p < end; ++p) {
-            const uint32_t o = coo(r, p);
-            if (kBackward) dot += r.a[o];
-            else ms = ms_add(ms, r.a[o]);
+        for (int q = 0; q < K; ++q) {
+            MaxSum ms{-INFINITY, 0.f};
+            float dot = 0.f;
+            for (int64_t p = beg; p < end; ++p) {
+                const uint32_t o = coo(r, p);
+                if (kBackward) dot += value(o, q);
+                else ms = ms_add(ms, value(o, q));
+            }
+            finish((int64_t)row * K + q, ms, dot);
         }
-        finish(row, ms, dot);
     }
 }
 
-// alpha_e = exp(s_e - m[dst_e]) / z[dst_e]
+// Item i of the [E, K] edge values: edge i / K, head i % K.
+template <bool kHeads>
+__device__ __forceinline__ int64_t stat_slot(const int32_t *dst, int64_t i, int k) {
+    if (!kHeads) return dst[i];
+    const int64_t e = i / k;
+    return (int64_t)dst[e] * k + (i - e * k);
+}
+
+// alpha_e = exp(s_e - m[dst_e]) / z[dst_e]   (per head with kHeads)
+template <bool kHeads>
 __global__ __launch_bounds__(kBlock) void softmax_apply_kernel(const int32_t *__restrict__ dst,
                                                                const float *__restrict__ s,
                                                                const float2 *__restrict__ stats,
                                                                float *__restrict__ alpha,
-                                                               int64_t e) {
+                                                               int64_t items, int k) {
     const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < e; i += stride) {
-        const float2 st = stats[dst[i]];
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < items; i += stride) {
+        const float2 st = stats[stat_slot<kHeads>(dst, i, k)];
         alpha[i] = expf(s[i] - st.x) / st.y;
     }
 }
@@ -212,14 +237,15 @@ __global__ __launch_bounds__(kBlock) void edge_product_kernel(const float *__res
         p[i] = alpha[i] * dalpha[i];
 }
 
-// ds_e = alpha_e (dalpha_e - t[dst_e])
+// ds_e = alpha_e (dalpha_e - t[dst_e])   (per head with kHeads)
+template <bool kHeads>
 __global__ __launch_bounds__(kBlock) void softmax_backward_apply_kernel(
     const int32_t *__restrict__ dst, const float *__restrict__ alpha,
     const float *__restrict__ dalpha, const float *__restrict__ rdot, float *__restrict__ ds,
-    int64_t e) {
+    int64_t items, int k) {
     const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < e; i += stride)
-        ds[i] = alpha[i] * (dalpha[i] - rdot[dst[i]]);
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < items; i += stride)
+        ds[i] = alpha[i] * (dalpha[i] - rdot[stat_slot<kHeads>(dst, i, k)]);
 }
 
 RowArgs row_args(const mp_graph *g) {
@@ -260,35 +286,53 @@ unsigned grid_for(int64_t items) {
 
 }  // namespace
 
-mp_status edge_softmax_run(const mp_graph *g, const float *s, float *alpha, float *row_stats,
-                           hipStream_t st) {
+mp_status edge_softmax_run(const mp_graph *g, const float *s, int64_t heads, float *alpha,
+                           float *row_stats, hipStream_t st) {
     RowArgs r = row_args(g);
     r.a = s;
     r.stats = reinterpret_cast<float2 *>(row_stats);
     r.dot = nullptr;
+    r.heads = (int32_t)heads;
     const int64_t gx = (int64_t)r.blk_hub + r.blk_wave + r.blk_lane;
-    row_stats_kernel<false><<<(unsigned)gx, kBlock, 0, st>>>(r);
-    if (g->num_edges > 0)
-        softmax_apply_kernel<<<grid_for(g->num_edges), kBlock, 0, st>>>(
-            g->dst, s, reinterpret_cast<const float2 *>(row_stats), alpha, g->num_edges);
+    const int64_t items = g->num_edges * heads;
+    const float2 *stats = reinterpret_cast<const float2 *>(row_stats);
+    if (heads > 1) {
+        row_stats_kernel<false, true><<<(unsigned)gx, kBlock, 0, st>>>(r);
+        if (items > 0)
+            softmax_apply_kernel<true><<<grid_for(items), kBlock, 0, st>>>(
+                g->dst, s, stats, alpha, items, (int)heads);
+    } else {
+        row_stats_kernel<false, false><<<(unsigned)gx, kBlock, 0, st>>>(r);
+        if (items > 0)
+            softmax_apply_kernel<false><<<grid_for(items), kBlock, 0, st>>>(g->dst, s, stats,
+                                                                            alpha, items, 1);
+    }
     MP_HIP_CHECK(hipGetLastError(), "edge softmax launch");
     return MP_OK;
 }
 
 mp_status edge_softmax_backward_run(const mp_graph *g, const float *alpha, const float *dalpha,
-                                    float *ds, float *rdot, hipStream_t st) {
+                                    int64_t heads, float *ds, float *rdot, hipStream_t st) {
     RowArgs r = row_args(g);
     r.a = ds;                // holds alpha * dalpha until the last step overwrites it
     r.stats = nullptr;
     r.dot = rdot;
+    r.heads = (int32_t)heads;
     const int64_t gx = (int64_t)r.blk_hub + r.blk_wave + r.blk_lane;
-    if (g->num_edges > 0)
-        edge_product_kernel<<<grid_for(g->num_edges), kBlock, 0, st>>>(alpha, dalpha, ds,
-                                                                        g->num_edges);
-    row_stats_kernel<true><<<(unsigned)gx, kBlock, 0, st>>>(r);
-    if (g->num_edges > 0)
-        softmax_backward_apply_kernel<<<grid_for(g->num_edges), kBlock, 0, st>>>(
-            g->dst, alpha, dalpha, rdot, ds, g->num_edges);
+    const int64_t items = g->num_edges * heads;
+    if (items > 0)
+        edge_product_kernel<<<grid_for(items), kBlock, 0, st>>>(alpha, dalpha, ds, items);
+    if (heads > 1) {
+        row_stats_kernel<true, true><<<(unsigned)gx, kBlock, 0, st>>>(r);
+        if (items > 0)
+            softmax_backward_apply_kernel<true><<<grid_for(items), kBlock, 0, st>>>(
+                g->dst, alpha, dalpha, rdot, ds, items, (int)heads);
+    } else {
+        row_stats_kernel<true, false><<<(unsigned)gx, kBlock, 0, st>>>(r);
+        if (items > 0)
+            softmax_backward_apply_kernel<false><<<grid_for(items), kBlock, 0, st>>>(
+                g->dst, alpha, dalpha, rdot, ds, items, 1);
+    }
     MP_HIP_CHECK(hipGetLastError(), "edge softmax backward launch");
     return MP_OK;
 }

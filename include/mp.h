@@ -299,6 +299,21 @@ mp_status mp_edge_softmax(const mp_graph *g, const float *scores, float *alpha, 
 mp_status mp_edge_softmax_backward(const mp_graph *g, const float *alpha, const float *dalpha,
                                    float *dscores, float *row_dot, void *stream);
 
+/*
+ * Multi-head scores, for a multi-head attention layer over the multi-head
+ * aggregation above: each edge carries `heads` = K scores, scores[e * K + q]
+ * ([E, K] row-major, COO order), and every head is normalised on its own, as
+ * mp_edge_softmax does for one ("Limits": scores normalised over each target;
+ * the per-head reading of vector edge values).  alpha and dscores are [E, K];
+ * row_stats is [N][K][2] (maximum, sum) and row_dot [N, K].  K = 1 is exactly
+ * the single-head call.  MP_ERR_SHAPE for K outside [1, 2^20].
+ */
+mp_status mp_edge_softmax_heads(const mp_graph *g, const float *scores, int64_t heads,
+                                float *alpha, float *row_stats, void *stream);
+mp_status mp_edge_softmax_backward_heads(const mp_graph *g, const float *alpha,
+                                         const float *dalpha, int64_t heads, float *dscores,
+                                         float *row_dot, void *stream);
+
 /* Normalisation modes for mp_edge_normalize. */
 #define MP_NORM_MEAN 1
 #define MP_NORM_SYM  2

@@ -184,3 +184,94 @@ def test_rejections(mp):
     a, _ = mp.mp_edge_softmax(g, t["w"])
     with pytest.raises(ValueError):                      # ds aliases dalpha
         mp.mp_edge_softmax_backward(g, a, t["w"], out_dscores=t["w"])
+
+
+# ---------------------------------------------------------------- multi-head scores
+
+def _check_softmax_heads(wl, scores, alpha, stats):
+    k = scores.shape[1]
+    ra, rm, rz = oracle.edge_softmax_heads(wl.n, wl.dst, scores)
+    got = alpha.cpu().numpy().astype(np.float64)
+    bound = _alpha_bound(wl.dst, wl.n)[:, None]
+    rel = np.abs(got - ra) / ra
+    assert not (rel > bound).any(), f"alpha: worst rel {rel.max():.3e}"
+    st = stats.cpu().numpy()
+    has = np.bincount(wl.dst, minlength=wl.n) > 0
+    assert np.array_equal(st[has, :, 0].astype(np.float64), rm[has])       # max is exact
+    assert np.all(np.isneginf(st[~has, :, 0])) and np.all(st[~has, :, 1] == 0)
+    deg = np.bincount(wl.dst, minlength=wl.n)
+    zb = (2.0 * (np.ceil(deg / _lanes(deg)) + 30) * U)[:, None]
+    assert np.all(np.abs(st[has, :, 1] - rz[has]) <= zb[has] * rz[has])
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("kind", ["random", "power_law"])
+def test_softmax_heads_against_oracle(mp, k, kind):
+    if kind == "random":
+        wl = synth.random_graph(3000, 60000, 1, 600 + k)
+    else:
+        wl = synth.chung_lu(seed=37, n=20000, e=400000, cap=20000.0, h=1, feat_dtype="f32")
+    rng = np.random.default_rng(k)
+    scores = (rng.standard_normal((wl.e, k)) * 3).astype(np.float32)
+    t = upload(wl, DEV)
+    g = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    s = torch.from_numpy(scores).to(DEV)
+    alpha, stats = mp.mp_edge_softmax_heads(g, s)
+    dalpha_np = rng.standard_normal((wl.e, k)).astype(np.float32)
+    ds, rdot = mp.mp_edge_softmax_backward_heads(g, alpha, torch.from_numpy(dalpha_np).to(DEV))
+    torch.cuda.synchronize()
+    _check_softmax_heads(wl, scores, alpha, stats)
+    a32 = alpha.cpu().numpy()
+    rds, rrdot, scale = oracle.edge_softmax_backward_heads(wl.n, wl.dst, a32, dalpha_np)
+    err = np.abs(ds.cpu().numpy().astype(np.float64) - rds)
+    assert np.all(err <= _back_bound(wl.dst, wl.n)[:, None] * scale)
+    if k == 1:                                       # one head is exactly the scalar call
+        a1, st1 = mp.mp_edge_softmax(g, s[:, 0].contiguous())
+        d1, r1 = mp.mp_edge_softmax_backward(g, alpha[:, 0].contiguous(),
+                                             torch.from_numpy(dalpha_np[:, 0].copy()).to(DEV))
+        torch.cuda.synchronize()
+        assert torch.equal(a1, alpha[:, 0]) and torch.equal(st1, stats[:, 0, :])
+        assert torch.equal(d1, ds[:, 0]) and torch.equal(r1, rdot[:, 0])
+
+
+def test_multihead_attention_layer_end_to_end(mp):
+    """alpha = per-head softmax(S); Y = multi-head A_alpha X; (dX, dalpha) from the
+    multi-head fused backward; dS from the per-head softmax backward -- each stage
+    against the oracle fed the device's previous stage."""
+    k = 4
+    wl = synth.chung_lu(seed=41, n=8000, e=160000, cap=8000.0, h=64, feat_dtype="bf16")
+    rng = np.random.default_rng(9)
+    scores = rng.standard_normal((wl.e, k)).astype(np.float32)
+    t = upload(wl, DEV)
+    g = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    alpha, stats = mp.mp_edge_softmax_heads(g, torch.from_numpy(scores).to(DEV))
+    y = mp.mp_spmm_fwd_heads(g, alpha, t["x"])
+    dx, dalpha = mp.mp_spmm_dx_edge_grad_heads(g, alpha, t["x"], t["dy"])
+    ds, _ = mp.mp_edge_softmax_backward_heads(g, alpha, dalpha)
+    torch.cuda.synchronize()
+    _check_softmax_heads(wl, scores, alpha, stats)
+    a32 = alpha.cpu().numpy()
+    ry, sy = oracle.forward_heads(wl.n, wl.src, wl.dst, a32, wl.x)
+    check_close("Y", y, ry, sy, TAU["f32"])
+    rdx, sdx = oracle.input_grad_heads(wl.n, wl.src, wl.dst, a32, wl.dy)
+    check_close("dX", dx, rdx, sdx, TAU["f32"])
+    rda, sda = oracle.edge_grad_heads(wl.src, wl.dst, wl.x, wl.dy, k)
+    check_close("dalpha", dalpha, rda, sda, TAU["f32"])
+    rds, _, scale = oracle.edge_softmax_backward_heads(wl.n, wl.dst, a32, dalpha.cpu().numpy())
+    err = np.abs(ds.cpu().numpy().astype(np.float64) - rds)
+    assert np.all(err <= _back_bound(wl.dst, wl.n)[:, None] * scale)
+
+
+def test_softmax_heads_rejections(mp):
+    wl = synth.random_graph(100, 500, 1, 12)
+    t = upload(wl, DEV)
+    g = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    s3 = torch.zeros((wl.e, 3), device=DEV)
+    with pytest.raises(ValueError):                  # scores must be [E, K]
+        mp.mp_edge_softmax_heads(g, torch.zeros(wl.e * 3, device=DEV))
+    with pytest.raises(ValueError):                  # statistics are [N, K, 2]
+        mp.mp_edge_softmax_heads(g, s3, out_row_stats=torch.empty((wl.n, 3), device=DEV))
+    with pytest.raises(ValueError):                  # head counts differ
+        mp.mp_edge_softmax_backward_heads(g, s3, torch.zeros((wl.e, 2), device=DEV))
+    with pytest.raises(ValueError):                  # dscores aliases dalpha
+        mp.mp_edge_softmax_backward_heads(g, s3, s3, out_dscores=s3)

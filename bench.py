@@ -101,6 +101,44 @@ def cpu_baseline(wl, sample_edges):
                       "single-threaded fp64 C oracle"}
 
 
+def cpu_baseline_adjacent(wl, sample_edges, heads=4):
+    """The oracle on the adjacent operations: target softmax and its backward and
+    symmetric normalisation on the same sample as cpu_baseline, and the 4-head
+    forward / input gradient / edge gradient on its first fifth (those loops cost
+    about 10x more per edge).  Per op: seconds and the same algorithmic bytes per
+    second as the GPU figures."""
+    import numpy as np
+    import oracle
+    n, h = wl.n, wl.h
+    e = sample_edges
+    src, dst, w = wl.src[:e], wl.dst[:e], wl.w[:e]
+    out = {}
+
+    def timed(name, nbytes, fn):
+        t0 = time.perf_counter()
+        res = fn()
+        dt = time.perf_counter() - t0
+        out[name] = {"seconds": round(dt, 3), "GBps": round(nbytes / dt / 1e9, 3)}
+        return res
+
+    alpha, _, _ = timed("edge_softmax", 20 * e + 24 * n, lambda: oracle.edge_softmax(n, dst, w))
+    timed("edge_softmax_backward", 28 * e + 16 * n,
+          lambda: oracle.edge_softmax_backward(n, dst, alpha.astype(np.float32), w))
+    timed("edge_normalize_sym", 16 * e + 8 * (n + 1),
+          lambda: oracle.edge_normalize(n, src, dst, oracle.NORM_SYM, w))
+    eh = max(e // 5, 1)
+    wk = np.random.default_rng(7).uniform(-1, 1, (eh, heads)).astype(np.float32)
+    b = algorithmic_bytes(n, eh, h, 2, 8)
+    timed("fwd_heads", b["fwd"] + 4 * (heads - 1) * eh,
+          lambda: oracle.forward_heads(n, src[:eh], dst[:eh], wk, wl.x))
+    timed("bwd_heads", b["dx"] + b["dw"] + 8 * (heads - 1) * eh,
+          lambda: (oracle.input_grad_heads(n, src[:eh], dst[:eh], wk, wl.dy),
+                   oracle.edge_grad_heads(src[:eh], dst[:eh], wl.x, wl.dy, heads)))
+    return {"kind": "oracle", "cores": 1, "unit": "GB/s", "ops": out,
+            "sample": f"first {e} of the {wl.e} COO edges ({eh} for the {heads}-head ops), "
+                      f"all {n} nodes, H={h}; single-threaded fp64 C oracle"}
+
+
 def minibatch_bench(mp, torch, dev, n_batches=64, h=256):
     """Back-to-back sampled minibatches (2-hop, fanout 15 then 10, 1,024 seeds,
     topology changing every batch), each one step: build + forward + fused
@@ -413,6 +451,8 @@ def main():
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_sample_edges} edges ...")
         out["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_sample_edges, e))
+        log("cpu baseline of the adjacent operations ...")
+        out["cpu_baseline_adjacent"] = cpu_baseline_adjacent(wl, min(args.cpu_sample_edges, e))
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

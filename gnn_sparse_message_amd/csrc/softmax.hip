@@ -83,6 +83,7 @@ struct RowArgs {
     const uint32_t *dev_totals;   // asynchronously built graph: rows per class on the
                                   // device, from which the six fields above are derived
     int32_t heads;                // K values per edge ([E, K]) with the multi-head kernels
+    bool vec_ok;                  // `a` allows 8- / 16-byte loads of an edge's heads
 };
 
 constexpr int64_t kCap = 1 << 22;   // wave and lane owners stride beyond this many blocks
@@ -110,16 +111,43 @@ __device__ __forceinline__ uint32_t coo(const RowArgs &r, int64_t p) {
     return (int64_t)o < r.e ? o : 0u;   // order is a permutation of [0, e)
 }
 
+// An edge's KW adjacent values: one 8- or 16-byte load each when `vec` (the
+// row base is aligned to it), else one 4-byte load per value.
+template <int KW>
+__device__ __forceinline__ void load_heads(const float *p, bool vec, float (&v)[KW]) {
+    if constexpr (KW % 4 == 0) {
+        if (vec) {
+#pragma unroll
+            for (int j = 0; j < KW; j += 4) {
+                const float4 q = *reinterpret_cast<const float4 *>(p + j);
+                v[j] = q.x; v[j + 1] = q.y; v[j + 2] = q.z; v[j + 3] = q.w;
+            }
+            return;
+        }
+    } else if constexpr (KW == 2) {
+        if (vec) {
+            const float2 q = *reinterpret_cast<const float2 *>(p);
+            v[0] = q.x;
+            v[1] = q.y;
+            return;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < KW; ++j) v[j] = p[j];
+}
+
 // kBackward = false: online max / sum of exp of the scores.
 // kBackward = true : sum of the products alpha * dalpha.
-// kHeads: the edge values are [E, K] and each head is reduced on its own (the
-// owner walks its row once per head; the row's values of all heads share cache
-// lines, so the later walks hit in L2); statistics are [N, K].
-template <bool kBackward, bool kHeads>
+// KT heads per edge are reduced in one walk over the row (KT accumulators per
+// lane; an edge's KT values are adjacent, so one gathered line serves them
+// all).  KT = 0 takes any head count K from the arguments and walks the row
+// once per head.  Statistics are [N, K]; KT = 1 is the single-head case.
+template <bool kBackward, int KT>
 __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
+    constexpr int KW = KT > 0 ? KT : 1;           // heads reduced per walk
+    const int K = KT > 0 ? KT : r.heads;
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
-    const int K = kHeads ? r.heads : 1;
     RowSplit sp{r.n_hub, r.n_wave, r.n_lane, r.blk_hub, r.blk_wave, r.blk_lane};
     if (r.dev_totals)   // counts on the device only: the grid is an upper bound
         sp = row_split(rows_at_least_device(r.dev_totals, kHubLen, r.n),
@@ -129,37 +157,56 @@ __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
         if (kBackward) r.dot[slot] = dot;
         else r.stats[slot] = make_float2(ms.m, ms.m == -INFINITY ? 0.f : ms.z);
     };
-    auto value = [&](uint32_t o, int q) { return kHeads ? r.a[(int64_t)o * K + q] : r.a[o]; };
+    // Lane-local pass over positions beg, beg + step, ... < end for heads q0 .. q0 + KW - 1.
+    auto walk = [&](int64_t beg, int64_t end, int64_t step, int q0, MaxSum (&ms)[KW],
+                    float (&dot)[KW]) {
+#pragma unroll
+        for (int j = 0; j < KW; ++j) {
+            ms[j] = MaxSum{-INFINITY, 0.f};
+            dot[j] = 0.f;
+        }
+        for (int64_t p = beg; p < end; p += step) {
+            float v[KW];
+            load_heads<KW>(r.a + (int64_t)coo(r, p) * K + q0, r.vec_ok, v);
+#pragma unroll
+            for (int j = 0; j < KW; ++j) {
+                if (kBackward) dot[j] += v[j];
+                else ms[j] = ms_add(ms[j], v[j]);
+            }
+        }
+    };
+    MaxSum ms[KW];
+    float dot[KW];
     if (b < sp.blk_hub) {   // hub row: the whole workgroup, lanes strided over the edges
-        __shared__ float s_m[kWavesPerBlock], s_z[kWavesPerBlock];
+        __shared__ float s_m[kWavesPerBlock][KW], s_z[kWavesPerBlock][KW];
         const int row = r.plan[b];
         if ((uint32_t)row >= (uint64_t)r.n) return;
         const int64_t beg = r.rowptr[row], end = r.rowptr[row + 1];
-        for (int q = 0; q < K; ++q) {
-            MaxSum ms{-INFINITY, 0.f};
-            float dot = 0.f;
-            for (int64_t p = beg + threadIdx.x; p < end; p += kBlock) {
-                const uint32_t o = coo(r, p);
-                if (kBackward) dot += value(o, q);
-                else ms = ms_add(ms, value(o, q));
-            }
-            if (kBackward) dot = sum_wave(dot);
-            else ms = ms_wave(ms);
-            if (lane == 0) {
-                s_m[wv] = kBackward ? dot : ms.m;
-                s_z[wv] = ms.z;
+        for (int q0 = 0; q0 < K; q0 += KW) {
+            walk(beg + threadIdx.x, end, kBlock, q0, ms, dot);
+#pragma unroll
+            for (int j = 0; j < KW; ++j) {
+                if (kBackward) dot[j] = sum_wave(dot[j]);
+                else ms[j] = ms_wave(ms[j]);
+                if (lane == 0) {
+                    s_m[wv][j] = kBackward ? dot[j] : ms[j].m;
+                    s_z[wv][j] = ms[j].z;
+                }
             }
             __syncthreads();
             if (threadIdx.x == 0) {
-                MaxSum t{s_m[0], s_z[0]};
-                float d = s_m[0];
-                for (int w = 1; w < kWavesPerBlock; ++w) {
-                    if (kBackward) d += s_m[w];
-                    else t = ms_merge(t, MaxSum{s_m[w], s_z[w]});
+#pragma unroll
+                for (int j = 0; j < KW; ++j) {
+                    MaxSum t{s_m[0][j], s_z[0][j]};
+                    float d = s_m[0][j];
+                    for (int w = 1; w < kWavesPerBlock; ++w) {
+                        if (kBackward) d += s_m[w][j];
+                        else t = ms_merge(t, MaxSum{s_m[w][j], s_z[w][j]});
+                    }
+                    finish((int64_t)row * K + q0 + j, t, d);
                 }
-                finish((int64_t)row * K + q, t, d);
             }
-            if (kHeads) __syncthreads();   // s_m / s_z are reused by the next head
+            if (KT == 0) __syncthreads();   // s_m / s_z are reused by the next head
         }
         return;
     }
@@ -170,17 +217,14 @@ __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
             const int row = r.plan[sp.n_hub + idx];
             if ((uint32_t)row >= (uint64_t)r.n) continue;
             const int64_t beg = r.rowptr[row], end = r.rowptr[row + 1];
-            for (int q = 0; q < K; ++q) {
-                MaxSum ms{-INFINITY, 0.f};
-                float dot = 0.f;
-                for (int64_t p = beg + lane; p < end; p += kWave) {
-                    const uint32_t o = coo(r, p);
-                    if (kBackward) dot += value(o, q);
-                    else ms = ms_add(ms, value(o, q));
+            for (int q0 = 0; q0 < K; q0 += KW) {
+                walk(beg + lane, end, kWave, q0, ms, dot);
+#pragma unroll
+                for (int j = 0; j < KW; ++j) {
+                    if (kBackward) dot[j] = sum_wave(dot[j]);
+                    else ms[j] = ms_wave(ms[j]);
+                    if (lane == 0) finish((int64_t)row * K + q0 + j, ms[j], dot[j]);
                 }
-                if (kBackward) dot = sum_wave(dot);
-                else ms = ms_wave(ms);
-                if (lane == 0) finish((int64_t)row * K + q, ms, dot);
             }
         }
         return;
@@ -193,16 +237,26 @@ __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
         const int row = r.plan[sp.n_hub + sp.n_wave + idx];
         if ((uint32_t)row >= (uint64_t)r.n) continue;
         const int64_t beg = r.rowptr[row], end = r.rowptr[row + 1];
-        for (int q = 0; q < K; ++q) {
-            MaxSum ms{-INFINITY, 0.f};
-            float dot = 0.f;
-            for (int64_t p = beg; p < end; ++p) {
-                const uint32_t o = coo(r, p);
-                if (kBackward) dot += value(o, q);
-                else ms = ms_add(ms, value(o, q));
-            }
-            finish((int64_t)row * K + q, ms, dot);
+        for (int q0 = 0; q0 < K; q0 += KW) {
+            walk(beg, end, 1, q0, ms, dot);
+#pragma unroll
+            for (int j = 0; j < KW; ++j) finish((int64_t)row * K + q0 + j, ms[j], dot[j]);
         }
+    }
+}
+
+// Row statistics launch for `heads` values per edge.
+template <bool kBackward>
+void launch_row_stats(RowArgs r, int64_t heads, unsigned grid, hipStream_t st) {
+    // vector loads need the array base aligned to an edge's KW values
+    const uintptr_t base = reinterpret_cast<uintptr_t>(r.a);
+    r.vec_ok = (heads == 2 && base % 8 == 0) || ((heads == 4 || heads == 8) && base % 16 == 0);
+    switch (heads) {
+        case 1: row_stats_kernel<kBackward, 1><<<grid, kBlock, 0, st>>>(r); break;
+        case 2: row_stats_kernel<kBackward, 2><<<grid, kBlock, 0, st>>>(r); break;
+        case 4: row_stats_kernel<kBackward, 4><<<grid, kBlock, 0, st>>>(r); break;
+        case 8: row_stats_kernel<kBackward, 8><<<grid, kBlock, 0, st>>>(r); break;
+        default: row_stats_kernel<kBackward, 0><<<grid, kBlock, 0, st>>>(r); break;
     }
 }
 
@@ -210,7 +264,8 @@ __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
 template <bool kHeads>
 __device__ __forceinline__ int64_t stat_slot(const int32_t *dst, int64_t i, int k) {
     if (!kHeads) return dst[i];
-    const int64_t e = i / k;
+    // 32-bit division while the item index fits (E * K < 2^32, the usual case)
+    const int64_t e = i < ((int64_t)1 << 32) ? (int64_t)((uint32_t)i / (uint32_t)k) : i / k;
     return (int64_t)dst[e] * k + (i - e * k);
 }
 
@@ -296,13 +351,12 @@ mp_status edge_softmax_run(const mp_graph *g, const float *s, int64_t heads, flo
     const int64_t gx = (int64_t)r.blk_hub + r.blk_wave + r.blk_lane;
     const int64_t items = g->num_edges * heads;
     const float2 *stats = reinterpret_cast<const float2 *>(row_stats);
+    launch_row_stats<false>(r, heads, (unsigned)gx, st);
     if (heads > 1) {
-        row_stats_kernel<false, true><<<(unsigned)gx, kBlock, 0, st>>>(r);
         if (items > 0)
             softmax_apply_kernel<true><<<grid_for(items), kBlock, 0, st>>>(
                 g->dst, s, stats, alpha, items, (int)heads);
     } else {
-        row_stats_kernel<false, false><<<(unsigned)gx, kBlock, 0, st>>>(r);
         if (items > 0)
             softmax_apply_kernel<false><<<grid_for(items), kBlock, 0, st>>>(g->dst, s, stats,
                                                                             alpha, items, 1);
@@ -322,13 +376,12 @@ mp_status edge_softmax_backward_run(const mp_graph *g, const float *alpha, const
     const int64_t items = g->num_edges * heads;
     if (items > 0)
         edge_product_kernel<<<grid_for(items), kBlock, 0, st>>>(alpha, dalpha, ds, items);
+    launch_row_stats<true>(r, heads, (unsigned)gx, st);
     if (heads > 1) {
-        row_stats_kernel<true, true><<<(unsigned)gx, kBlock, 0, st>>>(r);
         if (items > 0)
             softmax_backward_apply_kernel<true><<<grid_for(items), kBlock, 0, st>>>(
                 g->dst, alpha, dalpha, rdot, ds, items, (int)heads);
     } else {
-        row_stats_kernel<true, false><<<(unsigned)gx, kBlock, 0, st>>>(r);
         if (items > 0)
             softmax_backward_apply_kernel<false><<<grid_for(items), kBlock, 0, st>>>(
                 g->dst, alpha, dalpha, rdot, ds, items, 1);

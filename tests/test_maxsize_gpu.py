@@ -80,3 +80,55 @@ def test_maximum_edge_count(mp):
     del msg
     ref = torch.index_select(x[:, 0], 0, src) * torch.index_select(dy[:, 0], 0, dst)
     assert torch.equal(dw, ref)
+
+
+def _classes(deg):
+    """Degree class: 0 for no edges, else the number of binary digits."""
+    c = torch.zeros_like(deg)
+    nz = deg > 0
+    c[nz] = torch.floor(torch.log2(deg[nz].to(torch.float64))).to(deg.dtype) + 1
+    return c
+
+
+def test_maximum_node_count(mp):
+    """N = 2^31 - 1 nodes (E = 2^20): 31-bit keys, row pointers and degree plans
+    over 2^31 rows, and the forward over as many rows (almost all empty)."""
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info(DEV)
+    if free < 200 * 2**30:
+        pytest.skip(f"needs about 200 GB of free device memory, {free / 2**30:.0f} GB free")
+    n, e = 2**31 - 1, 2**20
+    gen = torch.Generator(device=DEV).manual_seed(2025)
+    src = torch.randint(0, n, (e,), generator=gen, device=DEV, dtype=torch.int64)
+    dst = torch.randint(0, n, (e,), generator=gen, device=DEV, dtype=torch.int64)
+    dst[:4096] = n - 1                                  # a hub row at the last node
+    g = mp.mp_graph_build(src, dst, n)
+    torch.cuda.synchronize()
+    deg = torch.bincount(dst, minlength=n)
+    rowptr = g.rowptr.to(torch.int64)
+    assert rowptr[0].item() == 0 and rowptr[-1].item() == e
+    assert torch.equal(rowptr[1:] - rowptr[:-1], deg)
+    del rowptr
+    order = g.edge_order.to(torch.int64)
+    keys = dst[order]
+    assert bool((keys[1:] >= keys[:-1]).all())
+    assert bool(((order[1:] > order[:-1]) | (keys[1:] != keys[:-1])).all())
+    assert torch.equal(g.col.to(torch.int64), src[order])
+    del order, keys
+    # degree plan: a permutation of the rows, classes non-increasing along it,
+    # ascending row id inside a class, and the host class counts agree
+    plan = g.row_plan.to(torch.int64)
+    assert bool((torch.bincount(plan, minlength=n) == 1).all())
+    cls = _classes(deg)[plan]
+    assert bool((cls[1:] <= cls[:-1]).all())
+    assert bool(((plan[1:] > plan[:-1]) | (cls[1:] != cls[:-1])).all())
+    counts = torch.bincount(cls, minlength=33).cpu().tolist()
+    assert counts == g.class_count
+    del plan, cls, deg
+    torch.cuda.empty_cache()
+    # forward with small integers (exact): Y = weighted bincount by destination
+    w = _small_ints((e,), gen)
+    x = _small_ints((n, 1), gen)
+    y = mp.mp_spmm_fwd(g, w, x)
+    ref = torch.bincount(dst, weights=w * x[src, 0], minlength=n)
+    assert torch.equal(y[:, 0], ref)

@@ -28,9 +28,9 @@
 namespace mp {
 namespace {
 
-constexpr int kItems = 16;                        // keys per thread per tile
-constexpr int kTile = kBlock * kItems;            // 4096 keys per tile
-constexpr int kWaveChunk = kWave * kItems;        // 1024 keys per wave per tile
+constexpr int kItems = 16;                        // keys per thread per tile (large lists)
+constexpr int kItemsSmall = 4;                    // the same for small lists: 1024-key tiles,
+                                                  // four times the blocks per pass
 constexpr int kBins = 256;                        // 8-bit digits
 constexpr int kDigitBits = 8;                     // at most 8 bits per pass
 constexpr int kPlanBits = 6;                      // plan keys 32 - class lie in [0, 32]
@@ -183,7 +183,8 @@ struct PassDir {
 // Digit counts of one tile: k[r] is the key at tile-local index li0 + r * 64,
 // valid below lim.  Writes hist[d * ntiles + t] for every digit d.  Contains
 // barriers: every thread of the block calls it.
-__device__ __forceinline__ void tile_digit_counts(const uint32_t (&k)[kItems], int li0, int lim,
+template <int IT>
+__device__ __forceinline__ void tile_digit_counts(const uint32_t (&k)[IT], int li0, int lim,
                                                   int shift, uint32_t mask,
                                                   uint32_t *__restrict__ hist, int64_t ntiles,
                                                   int64_t t) {
@@ -193,7 +194,7 @@ __device__ __forceinline__ void tile_digit_counts(const uint32_t (&k)[kItems], i
     for (int i = threadIdx.x; i < kWavesPerBlock * kBins; i += kBlock) (&s_cnt[0][0])[i] = 0u;
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < kItems; ++r) {
+    for (int r = 0; r < IT; ++r) {
         const bool valid = li0 + r * kWave < lim;
         const uint32_t d = (k[r] >> shift) & mask;
         const uint64_t m = match_digit(d, valid);
@@ -208,7 +209,7 @@ __device__ __forceinline__ void tile_digit_counts(const uint32_t (&k)[kItems], i
     hist[(int64_t)d * ntiles + t] = c;
 }
 
-template <class KeySrc, bool kDual>
+template <class KeySrc, bool kDual, int IT>
 __global__ __launch_bounds__(kBlock) void rs_upsweep(PassDir<KeySrc> a0, PassDir<KeySrc> a1,
                                                      int64_t count, int shift, int bits,
                                                      int64_t ntiles) {
@@ -218,13 +219,13 @@ __global__ __launch_bounds__(kBlock) void rs_upsweep(PassDir<KeySrc> a0, PassDir
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
     const uint32_t mask = (1u << bits) - 1u;
-    const int64_t left = count - t * kTile;
-    const int lim = left < kTile ? (int)left : kTile;        // keys in this tile
-    const KeySrc tk = a.keys.at(t * kTile);
-    const int li0 = wv * kWaveChunk + lane;                   // tile-local index, round 0
-    uint32_t k[kItems];
+    const int64_t left = count - t * (kBlock * IT);
+    const int lim = left < (kBlock * IT) ? (int)left : (kBlock * IT);        // keys in this tile
+    const KeySrc tk = a.keys.at(t * (kBlock * IT));
+    const int li0 = wv * (kWave * IT) + lane;                   // tile-local index, round 0
+    uint32_t k[IT];
 #pragma unroll
-    for (int r = 0; r < kItems; ++r) {
+    for (int r = 0; r < IT; ++r) {
         const int li = li0 + r * kWave;
         k[r] = li < lim ? tk(li) : 0u;
     }
@@ -267,12 +268,12 @@ __global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist0,
 // kInlineScan: hist holds raw per-tile counts (no scan kernel ran); each thread
 // sums its digit's counts over all tiles and over the tiles before this one.
 template <class KeySrc, bool kIotaVals, bool kOther, bool kWriteKeys, bool kDual,
-          bool kInlineScan>
+          bool kInlineScan, int IT>
 __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassDir<KeySrc> a1,
                                                        int64_t count, int shift, int bits,
                                                        int64_t ntiles) {
-    __shared__ uint32_t s_buf[kTile];          // one payload at a time, in tile-sorted order
-    __shared__ uint8_t s_dig[kTile];           // digit of each tile-sorted position
+    __shared__ uint32_t s_buf[(kBlock * IT)];          // one payload at a time, in tile-sorted order
+    __shared__ uint8_t s_dig[(kBlock * IT)];           // digit of each tile-sorted position
     __shared__ uint32_t s_cnt[kWavesPerBlock][kBins];
     __shared__ uint32_t s_tstart[kBins];
     __shared__ uint32_t s_gbase[kBins];
@@ -285,24 +286,24 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
     const int wv = tid / kWave;
     const uint32_t mask = (1u << bits) - 1u;
     const uint64_t lanes_below = (1ull << lane) - 1ull;
-    const int64_t tbase = t * kTile;
+    const int64_t tbase = t * (kBlock * IT);
     const int64_t left = count - tbase;
-    const int lim = left < kTile ? (int)left : kTile;        // keys in this tile
+    const int lim = left < (kBlock * IT) ? (int)left : (kBlock * IT);        // keys in this tile
     const KeySrc tk = a.keys.at(tbase);
-    const int li0 = wv * kWaveChunk + lane;                   // tile-local index, round 0
+    const int li0 = wv * (kWave * IT) + lane;                   // tile-local index, round 0
 
     for (int i = tid; i < kWavesPerBlock * kBins; i += kBlock) (&s_cnt[0][0])[i] = 0u;
-    uint32_t k[kItems];
+    uint32_t k[IT];
 #pragma unroll
-    for (int r = 0; r < kItems; ++r) {
+    for (int r = 0; r < IT; ++r) {
         const int li = li0 + r * kWave;
         k[r] = li < lim ? tk(li) : 0u;
     }
     __syncthreads();
     // Rank inside the wave: earlier rounds (running count) + lower lanes now.
-    uint32_t pos[kItems];
+    uint32_t pos[IT];
 #pragma unroll
-    for (int r = 0; r < kItems; ++r) {
+    for (int r = 0; r < IT; ++r) {
         const bool valid = li0 + r * kWave < lim;
         const uint32_t d = (k[r] >> shift) & mask;
         const uint64_t m = match_digit(d, valid);
@@ -346,15 +347,15 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
     s_gbase[tid] = dbase + before_tile;
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < kItems; ++r) {
+    for (int r = 0; r < IT; ++r) {
         const uint32_t d = (k[r] >> shift) & mask;
         pos[r] += s_cnt[wv][d];          // tile-local sorted position
         if (li0 + r * kWave < lim) s_dig[pos[r]] = (uint8_t)d;
     }
     __syncthreads();
-    uint32_t gp[kItems];                  // output position of tile-sorted slot tid + j * kBlock
+    uint32_t gp[IT];                  // output position of tile-sorted slot tid + j * kBlock
 #pragma unroll
-    for (int j = 0; j < kItems; ++j) {
+    for (int j = 0; j < IT; ++j) {
         const int i = tid + j * kBlock;
         gp[j] = 0xffffffffu;
         if (i < lim) {
@@ -365,22 +366,22 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
     // Regroup each payload through LDS, then write it out in digit runs.  The
     // ordinal and endpoint payloads are read only now, which keeps few
     // registers live across the ranking (more resident blocks per CU).
-    auto emit = [&](const uint32_t(&src)[kItems], uint32_t *__restrict__ out) {
+    auto emit = [&](const uint32_t(&src)[IT], uint32_t *__restrict__ out) {
 #pragma unroll
-        for (int r = 0; r < kItems; ++r)
+        for (int r = 0; r < IT; ++r)
             if (li0 + r * kWave < lim) s_buf[pos[r]] = src[r];
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < kItems; ++j)
+        for (int j = 0; j < IT; ++j)
             if ((int64_t)gp[j] < count) out[gp[j]] = s_buf[tid + j * kBlock];
         __syncthreads();
     };
     if (kWriteKeys) emit(k, pl.keys_out);
     {
-        uint32_t v[kItems];
+        uint32_t v[IT];
         const uint32_t *vin = kIotaVals ? nullptr : pl.vals_in + tbase;
 #pragma unroll
-        for (int r = 0; r < kItems; ++r) {
+        for (int r = 0; r < IT; ++r) {
             const int li = li0 + r * kWave;
             if (kIotaVals) v[r] = (uint32_t)tbase + (uint32_t)li;
             else v[r] = li < lim ? vin[li] : 0u;
@@ -388,10 +389,10 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
         emit(v, pl.vals_out);
     }
     if (kOther) {
-        uint32_t o[kItems];
+        uint32_t o[IT];
         const uint32_t *oin = pl.other_in + tbase;
 #pragma unroll
-        for (int r = 0; r < kItems; ++r) {
+        for (int r = 0; r < IT; ++r) {
             const int li = li0 + r * kWave;
             o[r] = li < lim ? oin[li] : 0u;
         }
@@ -428,7 +429,10 @@ __global__ __launch_bounds__(kBlock) void rowptr_kernel(RowsDir r0, RowsDir r1, 
 }
 
 // ------------------------------------------------------------------ host side
-int64_t tiles_for(int64_t count) { return count > 0 ? (count + kTile - 1) / kTile : 1; }
+int64_t tiles_for(int64_t count, int it) {
+    const int64_t tile = (int64_t)kBlock * it;
+    return count > 0 ? (count + tile - 1) / tile : 1;
+}
 
 unsigned grid_for(int64_t items, int64_t cap = 65536) {
     int64_t b = (items + kBlock - 1) / kBlock;
@@ -451,21 +455,22 @@ constexpr int64_t kInlineScanMaxTiles = 64;
 
 bool dual_mode(int64_t e) { return e <= kDualMaxEdges; }
 
-// One radix pass for one direction (d1 unused) or both (kDual).
-template <class KeySrc, bool kIota, bool kOther, bool kWriteKeys, bool kDual>
+// One radix pass for one direction (d1 unused) or both (kDual), with tiles of
+// 256 * IT keys.
+template <class KeySrc, bool kIota, bool kOther, bool kWriteKeys, bool kDual, int IT>
 mp_status radix_pass(const PassDir<KeySrc> &d0, const PassDir<KeySrc> &d1, int64_t count,
                      int shift, int bits, hipStream_t s) {
-    const int64_t ntiles = tiles_for(count);
+    const int64_t ntiles = tiles_for(count, IT);
     const unsigned grid = (unsigned)((kDual ? 2 : 1) * ntiles);
-    rs_upsweep<KeySrc, kDual><<<grid, kBlock, 0, s>>>(d0, d1, count, shift, bits, ntiles);
+    rs_upsweep<KeySrc, kDual, IT><<<grid, kBlock, 0, s>>>(d0, d1, count, shift, bits, ntiles);
     if (ntiles <= kInlineScanMaxTiles) {
-        rs_downsweep<KeySrc, kIota, kOther, kWriteKeys, kDual, true><<<grid, kBlock, 0, s>>>(
-            d0, d1, count, shift, bits, ntiles);
+        rs_downsweep<KeySrc, kIota, kOther, kWriteKeys, kDual, true, IT>
+            <<<grid, kBlock, 0, s>>>(d0, d1, count, shift, bits, ntiles);
     } else {
         rs_scan<kDual><<<(kDual ? 2 : 1) * kBins, kBlock, 0, s>>>(d0.hist, d0.dtot, d1.hist,
                                                                    d1.dtot, ntiles);
-        rs_downsweep<KeySrc, kIota, kOther, kWriteKeys, kDual, false><<<grid, kBlock, 0, s>>>(
-            d0, d1, count, shift, bits, ntiles);
+        rs_downsweep<KeySrc, kIota, kOther, kWriteKeys, kDual, false, IT>
+            <<<grid, kBlock, 0, s>>>(d0, d1, count, shift, bits, ntiles);
     }
     MP_HIP_CHECK(hipGetLastError(), "radix pass launch");
     return MP_OK;
@@ -523,9 +528,12 @@ mp_status sort_edges(const EdgeDir *dirs, int64_t e, int64_t n, const uint32_t *
             pd[i].pl.other_out = to_out ? reinterpret_cast<uint32_t *>(dirs[i].col) : b.o0;
         }
         if (!kDual) pd[1] = pd[0];
+        // Small lists (both directions per launch) use small tiles.
+        constexpr int IT = kDual ? kItemsSmall : kItems;
         mp_status st = pass == 0
-            ? radix_pass<KeysFromArray, true, true, true, kDual>(pd[0], pd[1], e, shift, pb, s)
-            : radix_pass<KeysFromArray, false, true, true, kDual>(pd[0], pd[1], e, shift, pb, s);
+            ? radix_pass<KeysFromArray, true, true, true, kDual, IT>(pd[0], pd[1], e, shift, pb, s)
+            : radix_pass<KeysFromArray, false, true, true, kDual, IT>(pd[0], pd[1], e, shift, pb,
+                                                                     s);
         if (st != MP_OK) return st;
         for (int i = 0; i < kDirs; ++i) {
             kin[i] = pd[i].pl.keys_out;
@@ -552,6 +560,7 @@ mp_status row_pointers(const RowsDir &r0, const RowsDir &r1, int64_t e, int64_t 
 // the plan key, both directions in each launch (its scan only when there are
 // many row tiles).  The digit totals, i.e. the rows per class, land in
 // totals0 / totals1.
+template <int IT>
 mp_status plans(int64_t n, mp_graph *g, uint32_t *hist0, uint32_t *hist1, uint32_t *totals0,
                 uint32_t *totals1, hipStream_t s) {
     PassDir<KeysFromDegree> p0, p1;
@@ -564,7 +573,7 @@ mp_status plans(int64_t n, mp_graph *g, uint32_t *hist0, uint32_t *hist1, uint32
     p1.hist = hist1;
     p0.dtot = totals0;
     p1.dtot = totals1;
-    return radix_pass<KeysFromDegree, true, false, false, true>(p0, p1, n, 0, kPlanBits, s);
+    return radix_pass<KeysFromDegree, true, false, false, true, IT>(p0, p1, n, 0, kPlanBits, s);
 }
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -576,7 +585,8 @@ LowerLayout lower_layout(int64_t n, int64_t e) {
     size_t off = 0;
     const size_t ebytes = align_up((size_t)(e > 0 ? e : 1) * sizeof(uint32_t));
     const int64_t most = e > n ? e : n;
-    const size_t hbytes = align_up((size_t)kBins * tiles_for(most) * sizeof(uint32_t));
+    const int it = dual_mode(e) ? kItemsSmall : kItems;
+    const size_t hbytes = align_up((size_t)kBins * tiles_for(most, it) * sizeof(uint32_t));
     for (int i = 0; i < 2; ++i) {
         if (i == 1 && !dual_mode(e)) {   // one direction at a time: one set of sort buffers
             L.k0[1] = L.k0[0];
@@ -655,7 +665,10 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
         }
     }
     if (st == MP_OK)
-        st = plans(n, g, b[0].hist, b[1].hist, info + kInfoPlanF, info + kInfoPlanT, s);
+        st = dual_mode(e)
+            ? plans<kItemsSmall>(n, g, b[0].hist, b[1].hist, info + kInfoPlanF,
+                                 info + kInfoPlanT, s)
+            : plans<kItems>(n, g, b[0].hist, b[1].hist, info + kInfoPlanF, info + kInfoPlanT, s);
     if (st != MP_OK) return st;
 
     *bad_index = 0;

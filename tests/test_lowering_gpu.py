@@ -44,6 +44,12 @@ def test_tiny_uniform(mp, idx_dtype):
     (1, 0, 1), (1, 5, 2), (2, 1, 3), (5, 0, 4), (3, 4095, 5), (3, 4096, 6), (3, 4097, 7),
     (257, 1000, 8), (256, 65537, 9), (70000, 9000, 10), (1 << 17, 300000, 11),
     (3_000_000, 200_000, 12),       # 22-bit keys: three digit passes, mostly empty rows
+    # small lists sort with 1024-key tiles and both directions per launch:
+    # tile edges, the last pass without a scan kernel (<= 64 tiles) and the first
+    # with one, and both sides of the switch to one direction per launch
+    (50, 1023, 20), (50, 1024, 21), (50, 1025, 22), (5000, 65536, 23), (5000, 65537, 24),
+    (1 << 16, (1 << 22), 25), (1 << 16, (1 << 22) + 1, 26),
+    (70000, 1024, 27),              # row tiles: 69 plan tiles, past the in-kernel tile sums
 ])
 def test_random_sizes(mp, n, e, seed):
     wl = synth.random_graph(n, e, 1, seed)

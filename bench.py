@@ -342,6 +342,13 @@ def main():
         lambda: mp.mp_edge_softmax_backward(g, alpha, dw, dscores, rdot))
     standalone["edge_normalize_sym"] = time_op(
         lambda: mp.mp_edge_normalize(g, mp.MP_NORM_SYM, w, out=wn))
+    # The whole attention backward in one call (alpha = the edge weights, Y = the
+    # forward output of the steps): replaces the fused backward + softmax backward.
+    dx_att = torch.empty_like(dx)
+    standalone["attention_backward"] = time_op(
+        lambda: mp.mp_attention_backward(g, w, x, dy, y, out_dx=dx_att, out_dscores=dscores,
+                                         out_row_dot=rdot))
+    del dx_att
     log(f"standalone dx {standalone['dx']:.3f} ms, dw {standalone['dw']:.3f} ms, "
         f"equal to the fused results: {same}")
     del alpha, rstats, dscores, rdot, wn
@@ -364,6 +371,10 @@ def main():
     rdk = torch.empty((n, heads), dtype=torch.float32, device=dev)
     standalone["edge_softmax_backward_heads"] = time_op(
         lambda: mp.mp_edge_softmax_backward_heads(g, ak, dwk, dsk, rdk))
+    mp.mp_spmm_fwd_heads(g, wk, x, out=y)
+    standalone["attention_backward_heads"] = time_op(
+        lambda: mp.mp_attention_backward(g, wk, x, dy, y, out_dx=dxk, out_dscores=dsk,
+                                         out_row_dot=rdk))
     del ak, sk, dsk, rdk
     log(f"heads={heads}: fwd {standalone['fwd_heads']:.3f} ms, fused bwd "
         f"{standalone['bwd_heads']:.3f} ms, equal to the separate calls: {same_heads}")
@@ -392,6 +403,12 @@ def main():
     # per-head softmax: the single-head bytes with K values per edge and per row
     bytes_["edge_softmax_heads"] = 4 * e + 16 * e * heads + 24 * n * heads
     bytes_["edge_softmax_backward_heads"] = 8 * e + 20 * e * heads + 16 * n * heads
+    # attention backward: the fused backward's bytes (alpha for w, ds for dw) plus
+    # the kept forward output Y and dY read once more for the row dots, and the
+    # row dots written; with K heads, K values per edge and per row.
+    bytes_["attention_backward"] = bytes_["bwd"] + (4 + 2) * n * h + 4 * n
+    bytes_["attention_backward_heads"] = (bytes_["attention_backward"] + 8 * (heads - 1) * e
+                                          + 4 * (heads - 1) * n)
     ms_step = t_total / args.steps * 1e3
 
     def rate(nbytes, ms):
@@ -404,6 +421,11 @@ def main():
     per_op_standalone["equal_to_fused"] = same
     per_op_standalone["heads"] = heads
     per_op_standalone["heads_fused_equal_to_separate"] = same_heads
+    # what the one-call attention backward replaces: fused backward + softmax backward
+    per_op_standalone["attention_backward_unfused_ms"] = round(
+        statistics.median(times["bwd"]) + standalone["edge_softmax_backward"], 4)
+    per_op_standalone["attention_backward_heads_unfused_ms"] = round(
+        standalone["bwd_heads"] + standalone["edge_softmax_backward_heads"], 4)
     # Kernels of the compute ops.  The dominant kernel is the one with the most
     # GPU time per step; its achieved bandwidth is the algorithmic bytes of the
     # units one launch processes over its average launch duration (the fused

@@ -32,6 +32,7 @@ __all__ = [
     "mp_spmm_dx", "mp_edge_grad_dw", "mp_spmm_dx_edge_grad", "mp_spmm_fwd_heads",
     "mp_spmm_dx_heads", "mp_edge_grad_dw_heads", "mp_spmm_dx_edge_grad_heads", "mp_edge_softmax",
     "mp_edge_softmax_backward", "mp_edge_softmax_heads", "mp_edge_softmax_backward_heads",
+    "mp_attention_backward",
     "mp_edge_normalize", "MP_NORM_MEAN", "MP_NORM_SYM",
     "mp_status_string", "mp_version", "library_path",
     "NUM_CLASSES",
@@ -119,6 +120,7 @@ def _load():
         "mp_edge_softmax_backward": (i32, [gp, vp, vp, vp, vp, vp]),
         "mp_edge_softmax_heads": (i32, [gp, vp, i64, vp, vp, vp]),
         "mp_edge_softmax_backward_heads": (i32, [gp, vp, vp, i64, vp, vp, vp]),
+        "mp_attention_backward": (i32, [gp, vp, i64, vp, vp, vp, i32, i64, vp, vp, vp, vp]),
         "mp_edge_normalize": (i32, [gp, i32, vp, vp, vp]),
         "mp_status_string": (ctypes.c_char_p, [i32]),
         "mp_last_error_detail": (ctypes.c_char_p, []),
@@ -509,6 +511,35 @@ def mp_edge_softmax_backward_heads(g: Graph, alpha, dalpha, out_dscores=None, ou
                                                _ptr(ds) if g.num_edges else None, _ptr(rdot),
                                                _stream(alpha)), "mp_edge_softmax_backward_heads")
     return ds, rdot
+
+
+def mp_attention_backward(g: Graph, alpha, x, dy, y, out_dx=None, out_dscores=None,
+                          out_row_dot=None):
+    """Backward of the attention layer Y = A_alpha X, alpha = softmax(scores):
+    returns (dX [N, H], dscores shaped like alpha, row_dot [N] or [N, K]) with
+    row_dot = <Y, dY> per row (and head).  alpha is [E] (one head) or [E, K];
+    y is the float32 forward output for these alpha and x."""
+    h = _features("x", x, g)
+    if _features("dy", dy, g) != h or _features("y", y, g) != h:
+        raise ValueError("x, dy and y must have the same feature width")
+    if y.dtype != torch.float32:
+        raise TypeError(f"y must be float32, got {y.dtype}")
+    _need_tensor("alpha", alpha)
+    if alpha.dim() == 1:
+        _weights(alpha, g)
+        k = 1
+    else:
+        k = _head_weights(alpha, g, h)
+    code = _code(dy) if x.dtype == dy.dtype else 0
+    dx = _out(out_dx, (g.num_nodes, h), dy)
+    ds = _out(out_dscores, tuple(alpha.shape), dy)
+    rdot = _out(out_row_dot, (g.num_nodes,) if alpha.dim() == 1 else (g.num_nodes, k), dy)
+    _check(_lib.mp_attention_backward(ctypes.byref(g._desc),
+                                      _ptr(alpha) if g.num_edges else None, k, _ptr(x),
+                                      _ptr(dy), _ptr(y), code, h, _ptr(dx),
+                                      _ptr(ds) if g.num_edges else None, _ptr(rdot),
+                                      _stream(dy)), "mp_attention_backward")
+    return dx, ds, rdot
 
 
 def mp_edge_normalize(g: Graph, mode: int, values, out=None):

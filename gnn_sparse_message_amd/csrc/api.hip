@@ -254,7 +254,8 @@ mp_status dx_edge_grad_impl(const mp_graph *g, const float *w, int64_t heads, co
     hipStream_t s = static_cast<hipStream_t>(stream);
     const CsrView v = transpose_view(g);
     if (spmm_fused_supported(dtype, h, heads, dy, x, dx))
-        return spmm_fused_run(v, w, heads, dy, dtype, h, dx, x, e > 0 ? dw : nullptr, s);
+        return spmm_fused_run(v, w, heads, dy, dtype, h, dx, x, e > 0 ? dw : nullptr,
+                              nullptr, s);
     // Feature rows wider than one column block: the two kernels back to back.
     if ((st = spmm_run(v, w, heads, dy, dtype, h, dx, s)) != MP_OK) return st;
     if (e == 0) return MP_OK;
@@ -502,6 +503,64 @@ mp_status mp_edge_softmax_backward_heads(const mp_graph *g, const float *alpha,
                                          float *row_dot, void *stream) {
     return softmax_backward_impl(g, alpha, dalpha, heads, dscores, row_dot, stream,
                                  "mp_edge_softmax_backward_heads");
+}
+
+namespace {
+mp_status attention_backward_impl(const mp_graph *g, const float *alpha, int64_t heads,
+                                  const void *x, const void *dy, const float *y, mp_dtype dtype,
+                                  int64_t h, float *dx, float *dscores, float *row_dot,
+                                  void *stream) {
+    mp_status st = check_spmm(g, alpha, heads, dy, dtype, h, dx, "dy", "dx");
+    if (st != MP_OK) return st;
+    const int64_t n = g->num_nodes, e = g->num_edges;
+    if (!x) return fail(MP_ERR_NULL, "x is NULL");
+    if (!y) return fail(MP_ERR_NULL, "y is NULL");
+    if (!row_dot) return fail(MP_ERR_NULL, "row_dot is NULL");
+    if (!dscores && e > 0) return fail(MP_ERR_NULL, "dscores is NULL with %lld edges", (long long)e);
+    const size_t xs = dtype_size(dtype);
+    if (!aligned(x, xs)) return fail(MP_ERR_ALIGN, "x not aligned to %zu bytes", xs);
+    if (!aligned(y, 4) || !aligned(row_dot, 4) || (dscores && !aligned(dscores, 4)))
+        return fail(MP_ERR_ALIGN, "y, dscores or row_dot not aligned to 4 bytes");
+    if ((st = check_device(x, "x")) != MP_OK) return st;
+    if ((st = check_device(y, "y")) != MP_OK) return st;
+    if ((st = check_device(row_dot, "row_dot")) != MP_OK) return st;
+    if (e > 0 && (st = check_device(dscores, "dscores")) != MP_OK) return st;
+    const Range rdx = range(dx, n * h, 4, "dx"), rds = range(dscores, e * heads, 4, "dscores");
+    const Range rt = range(row_dot, n * heads, 4, "row_dot");
+    RangeList others = graph_ranges(g);
+    others.add(range(x, n * h, xs, "x"));
+    others.add(range(dy, n * h, xs, "dy"));
+    others.add(range(y, n * h, 4, "y"));
+    others.add(range(alpha, e * heads, 4, "alpha"));
+    if (const char *hit = others.overlapping(rdx)) return fail(MP_ERR_ALIAS, "dx overlaps %s", hit);
+    others.add(rdx);
+    if (const char *hit = others.overlapping(rds))
+        return fail(MP_ERR_ALIAS, "dscores overlaps %s", hit);
+    others.add(rds);
+    if (const char *hit = others.overlapping(rt))
+        return fail(MP_ERR_ALIAS, "row_dot overlaps %s", hit);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = attention_row_dot_run(y, dy, dtype, n, h, heads, row_dot, s)) != MP_OK) return st;
+    const CsrView v = transpose_view(g);
+    if (spmm_fused_supported(dtype, h, heads, dy, x, dx))
+        return spmm_fused_run(v, alpha, heads, dy, dtype, h, dx, x, e > 0 ? dscores : nullptr,
+                              row_dot, s);
+    // Feature rows wider than one column block: dX, then dalpha into dscores,
+    // then the score gradient in place.
+    if ((st = spmm_run(v, alpha, heads, dy, dtype, h, dx, s)) != MP_OK) return st;
+    if (e == 0) return MP_OK;
+    if ((st = sddmm_run(g->src, g->dst, e, x, dy, dtype, h, heads, dscores, s)) != MP_OK)
+        return st;
+    return score_grad_apply_run(g->dst, alpha, row_dot, e, heads, dscores, s);
+}
+}  // namespace
+
+mp_status mp_attention_backward(const mp_graph *g, const float *alpha, int64_t heads,
+                                const void *x, const void *dy, const float *y, mp_dtype dtype,
+                                int64_t h, float *dx, float *dscores, float *row_dot,
+                                void *stream) {
+    return attention_backward_impl(g, alpha, heads, x, dy, y, dtype, h, dx, dscores, row_dot,
+                                   stream);
 }
 
 mp_status mp_edge_normalize(const mp_graph *g, int32_t mode, const float *in, float *out,

@@ -92,13 +92,15 @@ mp_status spmm_run(const CsrView &csr, const float *w, int64_t heads, const void
                    mp_dtype dt, int64_t h, float *out, hipStream_t stream);
 // The same aggregation over the transpose CSR that also writes, for every edge
 // q of owner row j, dw[order[q]] = <x_own[j, :], x[col[q], :]> (fused backward;
-// per head, dw[order[q] * K + head], when K > 1).  Only for feature rows that
-// fit one column block (spmm_fused_supported).
+// per head, dw[order[q] * K + head], when K > 1).  With row_dot (attention
+// backward: w = alpha, row_dot [N, K]) it writes the score gradient
+// w * (<x_own[j], x[col[q]]> - row_dot[col[q]]) in that slot instead.  Only for
+// feature rows that fit one column block (spmm_fused_supported).
 bool spmm_fused_supported(mp_dtype dt, int64_t h, int64_t heads, const void *x,
                           const void *x_own, const void *out);
 mp_status spmm_fused_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
                          mp_dtype dt, int64_t h, float *out, const void *x_own, float *dw,
-                         hipStream_t stream);
+                         const float *row_dot, hipStream_t stream);
 
 // ---------------------------------------------------------------- SDDMM
 // dw[e * K + q] = <x[src_e], dy[dst_e]> over head q's columns, COO order.
@@ -112,6 +114,14 @@ mp_status edge_softmax_run(const mp_graph *g, const float *s, int64_t heads, flo
                            float *row_stats, hipStream_t stream);
 mp_status edge_softmax_backward_run(const mp_graph *g, const float *alpha, const float *dalpha,
                                     int64_t heads, float *ds, float *row_dot, hipStream_t stream);
+
+// ---------------------------------------------------------------- attention backward
+// t[i * K + q] = <y[i], dy[i]> over head q's columns (y fp32 [N, H], dy of dt).
+mp_status attention_row_dot_run(const float *y, const void *dy, mp_dtype dt, int64_t n,
+                                int64_t h, int64_t heads, float *t, hipStream_t stream);
+// ds[e * K + q] = alpha[e * K + q] (ds[e * K + q] - t[dst_e * K + q]) in place.
+mp_status score_grad_apply_run(const int32_t *dst, const float *alpha, const float *t,
+                               int64_t e, int64_t heads, float *ds, hipStream_t stream);
 
 // ---------------------------------------------------------------- degree normalisation
 mp_status edge_normalize_run(const mp_graph *g, int mode, const float *in, float *out,

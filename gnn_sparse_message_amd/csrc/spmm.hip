@@ -118,6 +118,11 @@ __device__ __forceinline__ float head_sum(float part, int lane, int sub, int seg
     return t;
 }
 
+// What the kernel writes besides the aggregation.
+constexpr int kPlain = 0;        // nothing: forward or input gradient
+constexpr int kDw = 1;           // edge-weight gradients (fused backward)
+constexpr int kScoreGrad = 2;    // gradients of the scores behind softmax weights
+
 struct SpmmArgs {
     const int32_t *rowptr;
     const int32_t *col;
@@ -127,7 +132,10 @@ struct SpmmArgs {
     const void *x;                    // gathered rows (X forward, dY input gradient)
     float *y;
     const void *x_own;                // fused backward only: X, read at the owner row
-    float *dw;                        // fused backward only: edge gradients, COO order
+    float *dw;                        // fused backward only: edge gradients (or score
+                                      // gradients, see row_dot), COO order
+    const float *row_dot;             // score-gradient mode: t[dst, head] = <Y, dY> of the
+                                      // row; dw then receives w * (<x_own, x> - t)
     int64_t h;
     int32_t heads;                    // K weights per edge (multi-head kernels only)
     int32_t head_w;                   // H / K columns per head
@@ -168,12 +176,14 @@ __host__ __device__ inline Partition partition(int64_t at_hub, int64_t at_wave, 
 // row in runs of TL edges: run starts are `first`, `first + stride`, ...  All
 // lanes of the team execute every permute with the same trip count, so each
 // permute reads from an active lane.
-// With kEdgeGrad (the fused backward over the transpose CSR, rows = sources)
+// With kMode >= kDw (the fused backward over the transpose CSR, rows = sources)
 // every gathered dY slice also meets the owner row's X slice `xr`: the group
 // reduces their dot product over its L lanes (same lane order and butterfly as
-// the COO-order edge-gradient kernel) and one lane writes dw[order[p]].
+// the COO-order edge-gradient kernel) and one lane writes dw[order[p]].  With
+// kMode == kScoreGrad the weights are softmax outputs alpha and that lane
+// writes the score gradient alpha * (dot - t[dst]) instead (t from row_dot).
 // With kHeads every lane reads the weight of its own head, `head`, per edge.
-template <typename T, int VEC, int L, int TL, bool kEdgeGrad, bool kHeads>
+template <typename T, int VEC, int L, int TL, int kMode, bool kHeads>
 __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int64_t end,
                                            int64_t stride, int lane, int64_t hoff, int head,
                                            bool active, const float (&xr)[VEC],
@@ -227,6 +237,16 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
                     for (int v = 0; v < VEC; ++v) xv[u][v] = 0.f;
                 }
             }
+            // Score-gradient mode: the row terms of the gathered rows, loaded with
+            // the feature rows so their latency overlaps (a random 4-byte read each).
+            float tv[kUnroll];
+            if constexpr (kMode == kScoreGrad) {
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const int64_t slot = kHeads ? (int64_t)cu[u] * a.heads + head : cu[u];
+                    tv[u] = ok[u] && active ? a.row_dot[slot] : 0.f;
+                }
+            }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 float wv;
@@ -239,24 +259,34 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
 #pragma unroll
                 for (int v = 0; v < VEC; ++v) acc[v] = fmaf(wv, xv[u][v], acc[v]);
             }
-            if constexpr (kEdgeGrad && !kHeads) {
+            if constexpr (kMode != kPlain && !kHeads) {
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
                     float part = edge_dot<T, VEC>(xr, xv[u]);
 #pragma unroll
                     for (int off = L / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
                     const uint32_t ou = (uint32_t)__shfl((int)o, slu[u]);
-                    if (ok[u] && (lane % L) == 0) a.dw[ou] = part;
+                    if constexpr (kMode == kScoreGrad) {
+                        const float wu = __shfl(wt, slu[u]);
+                        if (ok[u] && (lane % L) == 0) a.dw[ou] = wu * (part - tv[u]);
+                    } else {
+                        if (ok[u] && (lane % L) == 0) a.dw[ou] = part;
+                    }
                 }
             }
-            if constexpr (kEdgeGrad && kHeads) {
+            if constexpr (kMode != kPlain && kHeads) {
                 const int seg = a.head_w / VEC;    // lanes per head
                 const int sub = lane % L;
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
                     const float part = head_sum(edge_dot<T, VEC>(xr, xv[u]), lane, sub, seg);
-                    if (ok[u] && active && sub % seg == 0)
-                        a.dw[(int64_t)oh[u] * a.heads + head] = part;
+                    if (ok[u] && active && sub % seg == 0) {
+                        const int64_t slot = (int64_t)oh[u] * a.heads + head;
+                        if constexpr (kMode == kScoreGrad)
+                            a.dw[slot] = wh[u] * (part - tv[u]);
+                        else
+                            a.dw[slot] = part;
+                    }
                 }
             }
         }
@@ -264,17 +294,17 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
 }
 
 // The owner row's slice of X (fused backward only).
-template <typename T, int VEC, bool kEdgeGrad>
+template <typename T, int VEC, int kMode>
 __device__ __forceinline__ void own_row(const SpmmArgs &a, int row, int64_t hoff, bool active,
                                         float (&xr)[VEC]) {
 #pragma unroll
     for (int v = 0; v < VEC; ++v) xr[v] = 0.f;
-    if constexpr (kEdgeGrad) {
+    if constexpr (kMode != kPlain) {
         if (active) Feat<T, VEC>::load(static_cast<const T *>(a.x_own) + (int64_t)row * a.h + hoff, xr);
     }
 }
 
-template <typename T, int VEC, int L, bool kEdgeGrad, bool kHeads>
+template <typename T, int VEC, int L, int kMode, bool kHeads>
 __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
@@ -297,8 +327,8 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
         const int row = a.plan[b];
         if ((uint32_t)row >= (uint64_t)a.n) return;   // the plan is a permutation of [0, n)
         const int64_t beg = a.rowptr[row], end = a.rowptr[row + 1];
-        own_row<T, VEC, kEdgeGrad>(a, row, hoff, active, xr);
-        accumulate<T, VEC, L, kWave, kEdgeGrad, kHeads>(a, beg + (int64_t)wv * kWave, end,
+        own_row<T, VEC, kMode>(a, row, hoff, active, xr);
+        accumulate<T, VEC, L, kWave, kMode, kHeads>(a, beg + (int64_t)wv * kWave, end,
                                                         (int64_t)kBlock, lane, hoff, head, active,
                                                         xr, acc);
 #pragma unroll
@@ -333,8 +363,8 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
             const int64_t beg = a.rowptr[row], end = a.rowptr[row + 1];
 #pragma unroll
             for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
-            own_row<T, VEC, kEdgeGrad>(a, row, hoff, active, xr);
-            accumulate<T, VEC, L, kWave, kEdgeGrad, kHeads>(a, beg, end, (int64_t)kWave, lane,
+            own_row<T, VEC, kMode>(a, row, hoff, active, xr);
+            accumulate<T, VEC, L, kWave, kMode, kHeads>(a, beg, end, (int64_t)kWave, lane,
                                                             hoff, head, active, xr, acc);
 #pragma unroll
             for (int off = L; off < kWave; off <<= 1)
@@ -355,8 +385,8 @@ __global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
         const int64_t beg = a.rowptr[row], end = a.rowptr[row + 1];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
-        own_row<T, VEC, kEdgeGrad>(a, row, hoff, active && end > beg, xr);
-        accumulate<T, VEC, L, L, kEdgeGrad, kHeads>(a, beg, end, (int64_t)L, lane, hoff, head,
+        own_row<T, VEC, kMode>(a, row, hoff, active && end > beg, xr);
+        accumulate<T, VEC, L, L, kMode, kHeads>(a, beg, end, (int64_t)L, lane, hoff, head,
                                                     active, xr, acc);
         if (active) store_row<VEC>(a.y + (int64_t)row * a.h + hoff, acc);
     }
@@ -383,7 +413,8 @@ Thresholds thresholds_for(int L) {
 
 template <typename T, int VEC, int L>
 mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *x, int64_t h,
-                 float *out, const void *x_own, float *dw, hipStream_t s) {
+                 float *out, const void *x_own, float *dw, const float *row_dot,
+                 hipStream_t s) {
     const Thresholds th = thresholds_for(L);
     SpmmArgs a;
     a.rowptr = csr.rowptr;
@@ -395,6 +426,7 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
     a.y = out;
     a.x_own = x_own;
     a.dw = dw;
+    a.row_dot = row_dot;
     a.h = h;
     a.heads = (int32_t)heads;
     a.head_w = (int32_t)(h / heads);
@@ -438,11 +470,16 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
     const dim3 grid((unsigned)gx, (unsigned)gy);
     if (dw) {   // fused backward: one column block holds the whole feature row
         if (gy != 1) return fail(MP_ERR_SHAPE, "fused backward needs H <= %d", L * VEC);
-        if (heads > 1) spmm_kernel<T, VEC, L, true, true><<<grid, kBlock, 0, s>>>(a);
-        else spmm_kernel<T, VEC, L, true, false><<<grid, kBlock, 0, s>>>(a);
+        if (row_dot) {
+            if (heads > 1) spmm_kernel<T, VEC, L, kScoreGrad, true><<<grid, kBlock, 0, s>>>(a);
+            else spmm_kernel<T, VEC, L, kScoreGrad, false><<<grid, kBlock, 0, s>>>(a);
+        } else {
+            if (heads > 1) spmm_kernel<T, VEC, L, kDw, true><<<grid, kBlock, 0, s>>>(a);
+            else spmm_kernel<T, VEC, L, kDw, false><<<grid, kBlock, 0, s>>>(a);
+        }
     } else {
-        if (heads > 1) spmm_kernel<T, VEC, L, false, true><<<grid, kBlock, 0, s>>>(a);
-        else spmm_kernel<T, VEC, L, false, false><<<grid, kBlock, 0, s>>>(a);
+        if (heads > 1) spmm_kernel<T, VEC, L, kPlain, true><<<grid, kBlock, 0, s>>>(a);
+        else spmm_kernel<T, VEC, L, kPlain, false><<<grid, kBlock, 0, s>>>(a);
     }
     MP_HIP_CHECK(hipGetLastError(), "spmm launch");
     return MP_OK;
@@ -457,15 +494,16 @@ int lanes_for(int64_t h, int vec) {
 
 template <typename T, int VEC>
 mp_status launch_lanes(const CsrView &csr, const float *w, int64_t heads, const void *x,
-                       int64_t h, float *out, const void *x_own, float *dw, hipStream_t s) {
+                       int64_t h, float *out, const void *x_own, float *dw,
+                       const float *row_dot, hipStream_t s) {
     switch (lanes_for(h, VEC)) {
-        case 1: return launch<T, VEC, 1>(csr, w, heads, x, h, out, x_own, dw, s);
-        case 2: return launch<T, VEC, 2>(csr, w, heads, x, h, out, x_own, dw, s);
-        case 4: return launch<T, VEC, 4>(csr, w, heads, x, h, out, x_own, dw, s);
-        case 8: return launch<T, VEC, 8>(csr, w, heads, x, h, out, x_own, dw, s);
-        case 16: return launch<T, VEC, 16>(csr, w, heads, x, h, out, x_own, dw, s);
-        case 32: return launch<T, VEC, 32>(csr, w, heads, x, h, out, x_own, dw, s);
-        default: return launch<T, VEC, 64>(csr, w, heads, x, h, out, x_own, dw, s);
+        case 1: return launch<T, VEC, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
+        case 2: return launch<T, VEC, 2>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
+        case 4: return launch<T, VEC, 4>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
+        case 8: return launch<T, VEC, 8>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
+        case 16: return launch<T, VEC, 16>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
+        case 32: return launch<T, VEC, 32>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
+        default: return launch<T, VEC, 64>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
     }
 }
 
@@ -475,7 +513,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 mp_status spmm_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
                    mp_dtype dt, int64_t h, float *out, hipStream_t s) {
-    return spmm_fused_run(csr, w, heads, x, dt, h, out, nullptr, nullptr, s);
+    return spmm_fused_run(csr, w, heads, x, dt, h, out, nullptr, nullptr, nullptr, s);
 }
 
 // 16-byte lanes need aligned rows and heads that are whole lanes wide.
@@ -493,15 +531,15 @@ bool spmm_fused_supported(mp_dtype dt, int64_t h, int64_t heads, const void *x,
 
 mp_status spmm_fused_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
                          mp_dtype dt, int64_t h, float *out, const void *x_own, float *dw,
-                         hipStream_t s) {
+                         const float *row_dot, hipStream_t s) {
     if (dt == MP_F32) {
         if (vector_lanes_ok(4, h, heads, x, x_own, out))
-            return launch_lanes<float, 4>(csr, w, heads, x, h, out, x_own, dw, s);
-        return launch_lanes<float, 1>(csr, w, heads, x, h, out, x_own, dw, s);
+            return launch_lanes<float, 4>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
+        return launch_lanes<float, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
     }
     if (vector_lanes_ok(8, h, heads, x, x_own, out))
-        return launch_lanes<uint16_t, 8>(csr, w, heads, x, h, out, x_own, dw, s);
-    return launch_lanes<uint16_t, 1>(csr, w, heads, x, h, out, x_own, dw, s);
+        return launch_lanes<uint16_t, 8>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
+    return launch_lanes<uint16_t, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
 }
 
 }  // namespace mp

@@ -314,6 +314,36 @@ mp_status mp_edge_softmax_backward_heads(const mp_graph *g, const float *alpha,
                                          const float *dalpha, int64_t heads, float *dscores,
                                          float *row_dot, void *stream);
 
+/*
+ * Whole backward of the attention layer Y = A_alpha X with alpha =
+ * softmax(scores) over each target ("Limits"; per head when heads > 1), in one
+ * walk of the transpose CSR instead of an input gradient, an edge gradient and
+ * a softmax backward one after another.  It rests on the identity
+ *   sum over the edges e into i of alpha_e <X[src_e], dY[i]> = <Y[i], dY[i]>
+ * (over head q's columns with K heads), so the row term of the softmax
+ * backward is a row-wise dot product of the kept forward output with dY, and
+ * each edge's score gradient is written where its dalpha is formed:
+ *   row_dot[i * K + q]   = <Y[i], dY[i]> over head q's columns,
+ *   dX                   = A_alpha^T dY            (as mp_spmm_dx_heads),
+ *   dscores[e * K + q]   = alpha[e * K + q] (<X[src_e], dY[dst_e]>_q - row_dot[dst_e * K + q]).
+ * Equal, up to rounding order, to mp_spmm_dx_edge_grad_heads followed by
+ * mp_edge_softmax_backward_heads; row_dot is the same quantity computed the
+ * other way.
+ *   alpha    [E, K] float32, COO order: the softmax weights the forward used.
+ *   x, dy    [N, H] of `dtype` (MP_F32 or MP_BF16).   h = H, a multiple of K.
+ *   y        [N, H] float32: the forward output A_alpha X for these alpha and x.
+ *   dx       [N, H] float32 output.   dscores  [E, K] float32 output, COO order.
+ *   row_dot  [N, K] float32 output.
+ * No output may overlap an input, another output or the graph arrays
+ * (MP_ERR_ALIAS).  Feature rows wider than one column block take the unfused
+ * path (dX, the edge gradients into dscores, then the score gradient in place),
+ * with the same results up to rounding order.
+ */
+mp_status mp_attention_backward(const mp_graph *g, const float *alpha, int64_t heads,
+                                const void *x, const void *dy, const float *y, mp_dtype dtype,
+                                int64_t h, float *dx, float *dscores, float *row_dot,
+                                void *stream);
+
 /* Normalisation modes for mp_edge_normalize. */
 #define MP_NORM_MEAN 1
 #define MP_NORM_SYM  2

@@ -171,6 +171,10 @@ def test_compute_calls_reject_unbuilt_graphs(mp):
     assert fh(None, 0x100, 2, 0x200, 0x300, mp.MP_F32, 4, 0x400, 0x500, None) == mp.MP_ERR_NULL
     assert fh(ctypes.byref(g), 0x100, 2, 0x200, 0x300, mp.MP_F32, 4, 0x400, 0x500, None) \
         == mp.MP_ERR_GRAPH
+    ab = lib.mp_attention_backward
+    args = (0x100, 2, 0x200, 0x300, 0x380, mp.MP_F32, 4, 0x400, 0x500, 0x600, None)
+    assert ab(None, *args) == mp.MP_ERR_NULL
+    assert ab(ctypes.byref(g), *args) == mp.MP_ERR_GRAPH
 
 
 def test_forward_and_input_grad_kernels_have_no_atomics(tmp_path):
@@ -183,7 +187,7 @@ def test_forward_and_input_grad_kernels_have_no_atomics(tmp_path):
     subprocess.run(cmd, check=True, capture_output=True)
     text = asm.read_text()
     kernels = re.findall(r"^(_Z\w*spmm_kernel\w*):", text, re.M)
-    assert len(kernels) >= 56                       # 2 dtypes x 2 widths x 7 lane counts x fused
+    assert len(kernels) >= 84                       # 2 dtypes x 2 widths x 7 lane counts x 3 modes
     insts = [ln for ln in text.splitlines() if re.match(r"\s+[a-z_0-9]+atomic", ln)]
     assert not insts, insts[:5]
     assert "global_load_dwordx4" in text            # 16-byte feature-row loads are emitted

@@ -275,3 +275,168 @@ def test_softmax_heads_rejections(mp):
         mp.mp_edge_softmax_backward_heads(g, s3, torch.zeros((wl.e, 2), device=DEV))
     with pytest.raises(ValueError):                  # dscores aliases dalpha
         mp.mp_edge_softmax_backward_heads(g, s3, s3, out_dscores=s3)
+
+
+# ---------------------------------------------------------------- fused attention backward
+#
+# mp_attention_backward against the oracle composition: dX = input_grad(alpha,
+# dY), dalpha = edge_grad(X, dY), (ds, t) = softmax_backward(alpha, dalpha).
+# The device takes the row term t_i from the kept forward output, <Y_i, dY_i>
+# per head; that equals the row sum of alpha * dalpha exactly, and its error
+# is bounded by T_i = sum_c |dY_ic| S_Y[i, c] (S_Y the forward's |term| sums)
+# times the forward's tau, plus the dot product's own rounding, which the same
+# T_i bounds.  So, per edge e into i and head q:
+#   |ds - ds_ref| <= tau (alpha_e (S_dalpha_e + T_i) + scale_e),
+# scale_e = alpha_e (|dalpha_e| + sum over the row of alpha |dalpha|) covering
+# the fp32 rounding of dalpha the oracle is fed, and |t - t_ref| <= tau T_i.
+
+def _attention_case(wl, k, seed):
+    rng = np.random.default_rng(seed)
+    scores = (rng.standard_normal((wl.e, k)) * 2).astype(np.float32)
+    ra, _, _ = oracle.edge_softmax_heads(wl.n, wl.dst, scores)
+    a32 = ra.astype(np.float32)
+    ry, sy = oracle.forward_heads(wl.n, wl.src, wl.dst, a32, wl.x)
+    return a32, ry, sy
+
+
+def _attention_reference(wl, a32, sy):
+    k = a32.shape[1]
+    rdx, sdx = oracle.input_grad_heads(wl.n, wl.src, wl.dst, a32, wl.dy)
+    rda, sda = oracle.edge_grad_heads(wl.src, wl.dst, wl.x, wl.dy, k)
+    rds, rt, scale = oracle.edge_softmax_backward_heads(wl.n, wl.dst, a32, rda.astype(np.float32))
+    hw = wl.h // k
+    tt = (np.abs(wl.dy.astype(np.float64)) * sy).reshape(wl.n, k, hw).sum(axis=2)
+    return rdx, sdx, rda, sda, rds, rt, scale, tt
+
+
+def _check_attention(wl, a32, sy, dx, ds, rdot, tau=TAU["f32"]):
+    rdx, sdx, rda, sda, rds, rt, scale, tt = _attention_reference(wl, a32, sy)
+    check_close("dX", dx, rdx, sdx, tau)
+    k = a32.shape[1]
+    got_ds = ds.cpu().numpy().reshape(wl.e, k).astype(np.float64)
+    bound = tau * (a32 * (sda + tt[wl.dst]) + scale)
+    err = np.abs(got_ds - rds)
+    bad = err > bound
+    assert not bad.any(), (f"dscores: {int(bad.sum())} outside the bound, worst "
+                           f"{(err / np.maximum(bound, 1e-300)).max():.3g} x bound")
+    got_t = rdot.cpu().numpy().reshape(wl.n, k).astype(np.float64)
+    terr = np.abs(got_t - rt)
+    assert np.all(terr <= tau * tt), f"row_dot: worst {(terr / np.maximum(tt, 1e-300)).max():.3g}"
+
+
+@pytest.mark.parametrize("case", [
+    ("power_law_f32_h64_k1", lambda: synth.chung_lu(seed=51, n=20000, e=400000, cap=20000.0,
+                                                    h=64, feat_dtype="f32"), 1),
+    ("power_law_bf16_h128_k1", lambda: synth.chung_lu(seed=52, n=8000, e=200000, cap=8000.0,
+                                                      h=128, feat_dtype="bf16"), 1),
+    ("power_law_bf16_h128_k4", lambda: synth.chung_lu(seed=53, n=8000, e=200000, cap=8000.0,
+                                                      h=128, feat_dtype="bf16"), 4),
+    ("random_f32_h32_k2", lambda: synth.random_graph(3000, 50000, 32, 54), 2),
+    ("ragged_f32_h6_k2", lambda: synth.random_graph(1500, 20000, 6, 55), 2),
+    ("ragged_bf16_h15_k3", lambda: synth.random_graph(1500, 20000, 15, 56, feat_dtype="bf16"), 3),
+    ("wide_f32_h600_k3", lambda: synth.random_graph(700, 9000, 600, 57), 3),
+    ("wide_bf16_h1024_k2", lambda: synth.random_graph(500, 6000, 1024, 58, feat_dtype="bf16"), 2),
+    ("one_node_no_edges", lambda: synth.random_graph(1, 0, 8, 59), 2),
+    ("no_edges", lambda: synth.random_graph(50, 0, 16, 60), 1),
+], ids=lambda c: c[0])
+def test_attention_backward_against_oracle(mp, case):
+    _, make, k = case
+    wl = make()
+    a32, ry, sy = _attention_case(wl, k, 7)
+    t = upload(wl, DEV)
+    g = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    alpha = torch.from_numpy(a32 if k > 1 else a32[:, 0].copy()).to(DEV)
+    y = torch.from_numpy(ry.astype(np.float32)).to(DEV)
+    dx, ds, rdot = mp.mp_attention_backward(g, alpha, t["x"], t["dy"], y)
+    torch.cuda.synchronize()
+    assert ds.shape == alpha.shape and rdot.shape == ((wl.n,) if k == 1 else (wl.n, k))
+    _check_attention(wl, a32, sy, dx, ds, rdot)
+
+
+@pytest.mark.parametrize("k", [1, 4])
+def test_attention_backward_equals_unfused_chain(mp, k):
+    """Same graph and inputs: dX is bit-identical to the fused input/edge
+    gradient call, and each score gradient is exactly alpha * (dalpha - t[dst])
+    formed from that call's dalpha and this call's row_dot."""
+    wl = synth.chung_lu(seed=61, n=20000, e=400000, cap=20000.0, h=128, feat_dtype="bf16")
+    a32, ry, sy = _attention_case(wl, k, 8)
+    t = upload(wl, DEV)
+    g = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    alpha = torch.from_numpy(a32).to(DEV)
+    y = mp.mp_spmm_fwd_heads(g, alpha, t["x"])                   # the device forward
+    dx, ds, rdot = mp.mp_attention_backward(g, alpha, t["x"], t["dy"], y)
+    dx2, dalpha = mp.mp_spmm_dx_edge_grad_heads(g, alpha, t["x"], t["dy"])
+    dst = t["dst"].long()
+    expect = alpha * (dalpha - rdot[dst])
+    torch.cuda.synchronize()
+    assert torch.equal(dx, dx2)
+    assert torch.equal(ds, expect)
+    # and the chain through the device forward still meets the oracle bound
+    _check_attention(wl, a32, sy, dx, ds, rdot)
+
+
+def test_attention_layer_fused_end_to_end(mp):
+    """scores -> softmax -> forward -> fused backward, all on the device, against
+    the all-oracle chain (alpha from the oracle softmax of the same scores)."""
+    k = 2
+    wl = synth.chung_lu(seed=62, n=8000, e=160000, cap=8000.0, h=64, feat_dtype="bf16")
+    rng = np.random.default_rng(10)
+    scores = rng.standard_normal((wl.e, k)).astype(np.float32)
+    t = upload(wl, DEV)
+    g = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    alpha, _ = mp.mp_edge_softmax_heads(g, torch.from_numpy(scores).to(DEV))
+    y = mp.mp_spmm_fwd_heads(g, alpha, t["x"])
+    dx, ds, rdot = mp.mp_attention_backward(g, alpha, t["x"], t["dy"], y)
+    torch.cuda.synchronize()
+    a32 = alpha.cpu().numpy()             # the device's alpha feeds the oracle chain
+    _, sy = oracle.forward_heads(wl.n, wl.src, wl.dst, a32, wl.x)
+    _check_attention(wl, a32, sy, dx, ds, rdot)
+    # against the all-fp64 softmax as well, relative to the score-gradient scale
+    ra, _, _ = oracle.edge_softmax_heads(wl.n, wl.dst, scores)
+    rda, _ = oracle.edge_grad_heads(wl.src, wl.dst, wl.x, wl.dy, k)
+    full, _, fscale = oracle.edge_softmax_backward_heads(wl.n, wl.dst, ra.astype(np.float32),
+                                                         rda.astype(np.float32))
+    rel = np.abs(ds.cpu().numpy() - full) / np.maximum(fscale, 1e-30)
+    assert rel.max() < 1e-4, rel.max()
+
+
+def test_attention_backward_async_graph(mp):
+    """On a graph whose class counts are still on the device the call returns
+    the same bits as on the finished graph."""
+    wl = synth.chung_lu(seed=63, n=6000, e=90000, cap=6000.0, h=64, feat_dtype="f32")
+    a32, ry, sy = _attention_case(wl, 2, 9)
+    t = upload(wl, DEV)
+    alpha = torch.from_numpy(a32).to(DEV)
+    y = torch.from_numpy(ry.astype(np.float32)).to(DEV)
+    g1 = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    g2 = mp.mp_graph_build_async(t["src"], t["dst"], wl.n)
+    r1 = mp.mp_attention_backward(g1, alpha, t["x"], t["dy"], y)
+    r2 = mp.mp_attention_backward(g2, alpha, t["x"], t["dy"], y)
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+    mp.mp_graph_finish(g2)
+
+
+def test_attention_backward_rejections(mp):
+    wl = synth.random_graph(100, 500, 8, 13)
+    t = upload(wl, DEV)
+    g = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    alpha = torch.rand((wl.e, 2), device=DEV)
+    y = torch.zeros((wl.n, 8), device=DEV)
+    with pytest.raises(TypeError):                   # y must be float32
+        mp.mp_attention_backward(g, alpha, t["x"], t["dy"], y.bfloat16())
+    with pytest.raises(ValueError):                  # widths differ
+        mp.mp_attention_backward(g, alpha, t["x"], t["dy"], y[:, :4].contiguous())
+    with pytest.raises(ValueError):                  # 3 heads do not divide 8
+        mp.mp_attention_backward(g, torch.rand((wl.e, 3), device=DEV), t["x"], t["dy"], y)
+    with pytest.raises(ValueError):                  # dx aliases y
+        mp.mp_attention_backward(g, alpha, t["x"], t["dy"], y, out_dx=y)
+    with pytest.raises(ValueError):                  # dscores aliases alpha
+        mp.mp_attention_backward(g, alpha, t["x"], t["dy"], y, out_dscores=alpha)
+    ds = torch.empty((wl.e, 2), device=DEV)
+    with pytest.raises(ValueError):                  # row_dot inside dscores
+        mp.mp_attention_backward(g, alpha, t["x"], t["dy"], y, out_dscores=ds,
+                                 out_row_dot=ds.view(-1)[:wl.n * 2].view(wl.n, 2))
+    with pytest.raises(TypeError):                   # x and dy dtypes differ
+        mp.mp_attention_backward(g, alpha, t["x"].bfloat16(), t["dy"], y)

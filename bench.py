@@ -139,6 +139,58 @@ def cpu_baseline_adjacent(wl, sample_edges, heads=4):
                       f"all {n} nodes, H={h}; single-threaded fp64 C oracle"}
 
 
+def other_configs_bench(mp, torch, dev, reps=20):
+    """The smaller configurations (tiny uniform, SBM, RMAT-16; fp32 features):
+    every entry point timed on its own, median / p10 / p90 of `reps` calls after
+    3 warm-ups, with the same algorithmic bytes as the main workload.  These
+    graphs fit the caches, so the fractions are reported, not targeted."""
+    import numpy as np
+    import synth
+    out = {}
+    for wl in (synth.tiny_uniform(), synth.sbm(), synth.rmat16()):
+        src = torch.from_numpy(wl.src).to(dev)
+        dst = torch.from_numpy(wl.dst).to(dev)
+        w = torch.from_numpy(wl.w).to(dev)
+        x = torch.from_numpy(wl.x).to(dev)
+        dy = torch.from_numpy(wl.dy).to(dev)
+        n, e, h = wl.n, wl.e, wl.h
+        y = torch.empty((n, h), device=dev)
+        dx = torch.empty_like(y)
+        dw = torch.empty(e, device=dev)
+        g = mp.mp_graph_build(src, dst, n)
+        stream = torch.cuda.current_stream(dev)
+        calls = {"build": lambda: mp.mp_graph_build(src, dst, n),
+                 "fwd": lambda: mp.mp_spmm_fwd(g, w, x, out=y),
+                 "dx": lambda: mp.mp_spmm_dx(g, w, dy, out=dx),
+                 "dw": lambda: mp.mp_edge_grad_dw(g, x, dy, out=dw),
+                 "bwd": lambda: mp.mp_spmm_dx_edge_grad(g, w, x, dy, out_dx=dx, out_dw=dw)}
+        b = algorithmic_bytes(n, e, h, 4, 8)
+        b["bwd"] = b["dx"] + b["dw"]
+        res = {"num_nodes": n, "num_edges": e, "feature_width": h, "feature_storage": "f32"}
+        for name, fn in calls.items():
+            for _ in range(3):
+                fn()
+            ts = []
+            for _ in range(reps):
+                a0 = torch.cuda.Event(enable_timing=True)
+                a1 = torch.cuda.Event(enable_timing=True)
+                a0.record(stream)
+                fn()
+                a1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(a0.elapsed_time(a1))
+            med = float(np.median(ts))
+            res[name] = {"ms": round(med, 4), "p10_ms": round(float(np.percentile(ts, 10)), 4),
+                         "p90_ms": round(float(np.percentile(ts, 90)), 4),
+                         "GBps": round(b[name] / (med * 1e-3) / 1e9, 1),
+                         "frac": round(b[name] / (med * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                         "edges_per_s": round(e / (med * 1e-3), 1),
+                         "algorithmic_bytes": b[name]}
+        out[wl.name] = res
+        del g, src, dst, w, x, dy, y, dx, dw
+    return out
+
+
 def minibatch_bench(mp, torch, dev, n_batches=64, h=256):
     """Back-to-back sampled minibatches (2-hop, fanout 15 then 10, 1,024 seeds,
     topology changing every batch), each one step: build + forward + fused
@@ -245,6 +297,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-minibatch", action="store_true",
                     help="skip the back-to-back minibatch schedules")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the timings of the small configurations")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the steps, run one plain 1 GiB -> 1 GiB elementwise copy "
                          "(reference for the HBM byte counters)")
@@ -416,7 +470,14 @@ def main():
         return {"ms": round(ms, 4), "GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4),
                 "edges_per_s": round(e / (ms * 1e-3), 1), "algorithmic_bytes": nbytes}
 
+    def pct(v, q):
+        v = sorted(v)
+        return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+
     per_op = {k: rate(bytes_[k], statistics.median(times[k])) for k in ops}
+    for k in ops:
+        per_op[k]["p10_ms"] = round(pct(times[k], 0.1), 4)
+        per_op[k]["p90_ms"] = round(pct(times[k], 0.9), 4)
     per_op_standalone = {k: rate(bytes_[k], v) for k, v in standalone.items()}
     per_op_standalone["equal_to_fused"] = same
     per_op_standalone["heads"] = heads
@@ -463,6 +524,11 @@ def main():
         "roofline": roof[dominant],
         "roofline_other_kernels": {k: v for k, v in roof.items() if k != dominant},
     }
+    if not args.no_other_configs:
+        log("smaller configurations (tiny, SBM, RMAT-16) ...")
+        out["other_configs"] = other_configs_bench(mp, torch, dev)
+        log("smaller configurations: " + ", ".join(
+            f"{k} fwd {v['fwd']['ms']} ms" for k, v in out["other_configs"].items()))
     if not args.no_minibatch:
         del g, dx_alone, dw_alone
         torch.cuda.empty_cache()

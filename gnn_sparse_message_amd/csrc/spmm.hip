@@ -304,8 +304,13 @@ __device__ __forceinline__ void own_row(const SpmmArgs &a, int row, int64_t hoff
     }
 }
 
+// The single-head fused backward needs a few registers more than fit five waves
+// per SIMD; holding it to five (two spilled registers) measured 8.20 ms against
+// 8.80 ms at four.  The multi-head variants spill more and are left alone.
 template <typename T, int VEC, int L, int kMode, bool kHeads>
-__global__ __launch_bounds__(kBlock) void spmm_kernel(SpmmArgs a) {
+__global__ __launch_bounds__(kBlock)
+__attribute__((amdgpu_waves_per_eu(kMode != kPlain && !kHeads ? 5 : 1)))
+void spmm_kernel(SpmmArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
     const int sub = lane % L;

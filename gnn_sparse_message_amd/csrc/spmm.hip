@@ -36,8 +36,6 @@
 namespace mp {
 namespace {
 
-constexpr int kUnroll = 4;   // feature rows in flight per group per step
-
 // ------------------------------------------------------------------ feature loads
 template <typename T, int VEC>
 struct Feat;
@@ -123,6 +121,13 @@ constexpr int kPlain = 0;        // nothing: forward or input gradient
 constexpr int kDw = 1;           // edge-weight gradients (fused backward)
 constexpr int kScoreGrad = 2;    // gradients of the scores behind softmax weights
 
+// Feature rows in flight per group per step.  The aggregation alone keeps six
+// (held to four waves per SIMD: 4.89 ms against 5.04 ms with four rows at six
+// waves on the power-law graph); the fused backward, which also holds the owner
+// row and the dot products, keeps four.
+template <int kMode, bool kHeads>
+constexpr int unroll_for() { return kMode == kPlain && !kHeads ? 6 : 4; }
+
 struct SpmmArgs {
     const int32_t *rowptr;
     const int32_t *col;
@@ -189,6 +194,7 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
                                            bool active, const float (&xr)[VEC],
                                            float (&acc)[VEC]) {
     constexpr int G = TL / L;                 // groups per team
+    constexpr int kUnroll = unroll_for<kMode, kHeads>();
     const int tl = lane % TL;
     const int tb = lane - tl;                 // first lane of the team
     const int g = tl / L;
@@ -304,12 +310,16 @@ __device__ __forceinline__ void own_row(const SpmmArgs &a, int row, int64_t hoff
     }
 }
 
-// The single-head fused backward needs a few registers more than fit five waves
-// per SIMD; holding it to five (two spilled registers) measured 8.20 ms against
-// 8.80 ms at four.  The multi-head variants spill more and are left alone.
+// Occupancy: the single-head fused backward needs a few registers more than fit
+// five waves per SIMD; holding it to five (two spilled registers) measured
+// 8.20 ms against 8.80 ms at four.  The single-head aggregation is held to four
+// (its six rows in flight).  The multi-head variants are left to the compiler.
+template <int kMode, bool kHeads>
+constexpr int min_waves_for() { return kHeads ? 1 : (kMode == kPlain ? 4 : 5); }
+
 template <typename T, int VEC, int L, int kMode, bool kHeads>
 __global__ __launch_bounds__(kBlock)
-__attribute__((amdgpu_waves_per_eu(kMode != kPlain && !kHeads ? 5 : 1)))
+__attribute__((amdgpu_waves_per_eu(min_waves_for<kMode, kHeads>())))
 void spmm_kernel(SpmmArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;

@@ -396,6 +396,18 @@ def main():
         lambda: mp.mp_edge_softmax_backward(g, alpha, dw, dscores, rdot))
     standalone["edge_normalize_sym"] = time_op(
         lambda: mp.mp_edge_normalize(g, mp.MP_NORM_SYM, w, out=wn))
+    # Degree normalisation applied at the weight fetch (GCN's symmetric and
+    # SAGE's mean), against normalising the weights first (edge_normalize_sym).
+    standalone["fwd_norm_sym"] = time_op(
+        lambda: mp.mp_spmm_fwd_norm(g, mp.MP_NORM_SYM, w, x, out=y))
+    standalone["fwd_norm_mean"] = time_op(
+        lambda: mp.mp_spmm_fwd_norm(g, mp.MP_NORM_MEAN, w, x, out=y))
+    dx_n = torch.empty_like(dx)
+    dw_n = torch.empty_like(dw)
+    standalone["bwd_norm_sym"] = time_op(
+        lambda: mp.mp_spmm_dx_edge_grad_norm(g, mp.MP_NORM_SYM, w, x, dy, out_dx=dx_n,
+                                             out_dw=dw_n))
+    del dx_n, dw_n
     # The whole attention backward in one call (alpha = the edge weights, Y = the
     # forward output of the steps): replaces the fused backward + softmax backward.
     dx_att = torch.empty_like(dx)
@@ -461,6 +473,11 @@ def main():
     # the kept forward output Y and dY read once more for the row dots, and the
     # row dots written; with K heads, K values per edge and per row.
     bytes_["attention_backward"] = bytes_["bwd"] + (4 + 2) * n * h + 4 * n
+    # normalised at the fetch: the plain call's bytes plus the other CSR's row
+    # pointers, where the degrees come from
+    bytes_["fwd_norm_sym"] = bytes_["fwd"] + 4 * (n + 1)
+    bytes_["fwd_norm_mean"] = bytes_["fwd"]
+    bytes_["bwd_norm_sym"] = bytes_["bwd"] + 4 * (n + 1)
     bytes_["attention_backward_heads"] = (bytes_["attention_backward"] + 8 * (heads - 1) * e
                                           + 4 * (heads - 1) * n)
     ms_step = t_total / args.steps * 1e3
@@ -482,6 +499,11 @@ def main():
     per_op_standalone["equal_to_fused"] = same
     per_op_standalone["heads"] = heads
     per_op_standalone["heads_fused_equal_to_separate"] = same_heads
+    # what the fetch-time normalisation replaces: a normalisation pass, then the call
+    per_op_standalone["fwd_norm_two_calls_ms"] = round(
+        standalone["edge_normalize_sym"] + statistics.median(times["fwd"]), 4)
+    per_op_standalone["bwd_norm_two_calls_ms"] = round(
+        standalone["edge_normalize_sym"] * 2 + statistics.median(times["bwd"]), 4)
     # what the one-call attention backward replaces: fused backward + softmax backward
     per_op_standalone["attention_backward_unfused_ms"] = round(
         statistics.median(times["bwd"]) + standalone["edge_softmax_backward"], 4)

@@ -32,7 +32,7 @@ __all__ = [
     "mp_spmm_dx", "mp_edge_grad_dw", "mp_spmm_dx_edge_grad", "mp_spmm_fwd_heads",
     "mp_spmm_dx_heads", "mp_edge_grad_dw_heads", "mp_spmm_dx_edge_grad_heads", "mp_edge_softmax",
     "mp_edge_softmax_backward", "mp_edge_softmax_heads", "mp_edge_softmax_backward_heads",
-    "mp_attention_backward",
+    "mp_attention_backward", "mp_spmm_fwd_norm", "mp_spmm_dx_norm", "mp_spmm_dx_edge_grad_norm",
     "mp_edge_normalize", "MP_NORM_MEAN", "MP_NORM_SYM",
     "mp_status_string", "mp_version", "library_path",
     "NUM_CLASSES",
@@ -121,6 +121,9 @@ def _load():
         "mp_edge_softmax_heads": (i32, [gp, vp, i64, vp, vp, vp]),
         "mp_edge_softmax_backward_heads": (i32, [gp, vp, vp, i64, vp, vp, vp]),
         "mp_attention_backward": (i32, [gp, vp, i64, vp, vp, vp, i32, i64, vp, vp, vp, vp]),
+        "mp_spmm_fwd_norm": (i32, [gp, i32, vp, vp, i32, i64, vp, vp]),
+        "mp_spmm_dx_norm": (i32, [gp, i32, vp, vp, i32, i64, vp, vp]),
+        "mp_spmm_dx_edge_grad_norm": (i32, [gp, i32, vp, vp, vp, i32, i64, vp, vp, vp]),
         "mp_edge_normalize": (i32, [gp, i32, vp, vp, vp]),
         "mp_status_string": (ctypes.c_char_p, [i32]),
         "mp_last_error_detail": (ctypes.c_char_p, []),
@@ -341,6 +344,47 @@ def mp_spmm_dx(g: Graph, w, dy, out=None):
     _check(_lib.mp_spmm_dx(ctypes.byref(g._desc), _ptr(w) if g.num_edges else None, _ptr(dy),
                            _code(dy), h, _ptr(dx), _stream(dy)), "mp_spmm_dx")
     return dx
+
+
+def mp_spmm_fwd_norm(g: Graph, mode: int, w, x, out=None):
+    """Y = A_{norm(w)} X with the degree normalisation (MP_NORM_MEAN or
+    MP_NORM_SYM) applied as each weight is fetched; bitwise
+    mp_spmm_fwd(g, mp_edge_normalize(g, mode, w), x)."""
+    _weights(w, g)
+    h = _features("x", x, g)
+    y = _out(out, (g.num_nodes, h), x)
+    _check(_lib.mp_spmm_fwd_norm(ctypes.byref(g._desc), int(mode),
+                                 _ptr(w) if g.num_edges else None, _ptr(x), _code(x), h,
+                                 _ptr(y), _stream(x)), "mp_spmm_fwd_norm")
+    return y
+
+
+def mp_spmm_dx_norm(g: Graph, mode: int, w, dy, out=None):
+    """dX = A_{norm(w)}^T dY, normalised at the fetch."""
+    _weights(w, g)
+    h = _features("dy", dy, g)
+    dx = _out(out, (g.num_nodes, h), dy)
+    _check(_lib.mp_spmm_dx_norm(ctypes.byref(g._desc), int(mode),
+                                _ptr(w) if g.num_edges else None, _ptr(dy), _code(dy), h,
+                                _ptr(dx), _stream(dy)), "mp_spmm_dx_norm")
+    return dx
+
+
+def mp_spmm_dx_edge_grad_norm(g: Graph, mode: int, w, x, dy, out_dx=None, out_dw=None):
+    """(dX, dw) for Y = A_{norm(w)} X: dX through the normalised weights and dw
+    the gradient with respect to the raw weights, c_e <X[src_e], dY[dst_e]>."""
+    _weights(w, g)
+    h = _features("x", x, g)
+    if _features("dy", dy, g) != h:
+        raise ValueError("x and dy must have the same feature width")
+    code = _code(dy) if x.dtype == dy.dtype else 0
+    dx = _out(out_dx, (g.num_nodes, h), dy)
+    dw = _out(out_dw, (g.num_edges,), dy)
+    _check(_lib.mp_spmm_dx_edge_grad_norm(ctypes.byref(g._desc), int(mode),
+                                          _ptr(w) if g.num_edges else None, _ptr(x), _ptr(dy),
+                                          code, h, _ptr(dx), _ptr(dw) if g.num_edges else None,
+                                          _stream(dy)), "mp_spmm_dx_edge_grad_norm")
+    return dx, dw
 
 
 def mp_edge_grad_dw(g: Graph, x, dy, out=None):

@@ -228,9 +228,21 @@ mp_status edge_grad_impl(const mp_graph *g, const void *x, const void *dy, mp_dt
                      static_cast<hipStream_t>(stream));
 }
 
+// Fetch-time normalisation of a walk over the forward (rows = destinations) or
+// the transpose CSR.
+NormSpec norm_spec(const mp_graph *g, int32_t mode, bool forward) {
+    return NormSpec{mode, forward, forward ? g->rowptr_t : g->rowptr};
+}
+
+mp_status check_norm_mode(int32_t mode, const char *what) {
+    if (mode != MP_NORM_MEAN && mode != MP_NORM_SYM)
+        return fail(MP_ERR_DTYPE, "%s: unknown normalisation mode %d", what, (int)mode);
+    return MP_OK;
+}
+
 mp_status dx_edge_grad_impl(const mp_graph *g, const float *w, int64_t heads, const void *x,
                             const void *dy, mp_dtype dtype, int64_t h, float *dx, float *dw,
-                            void *stream) {
+                            void *stream, int32_t norm_mode = 0) {
     mp_status st = check_spmm(g, w, heads, dy, dtype, h, dx, "dy", "dx");
     if (st != MP_OK) return st;
     const int64_t n = g->num_nodes, e = g->num_edges;
@@ -253,13 +265,17 @@ mp_status dx_edge_grad_impl(const mp_graph *g, const float *w, int64_t heads, co
         return fail(MP_ERR_ALIAS, "dw overlaps %s", hit);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const CsrView v = transpose_view(g);
+    const NormSpec nm = norm_spec(g, norm_mode, false);
+    const NormSpec *pn = norm_mode ? &nm : nullptr;
     if (spmm_fused_supported(dtype, h, heads, dy, x, dx))
         return spmm_fused_run(v, w, heads, dy, dtype, h, dx, x, e > 0 ? dw : nullptr,
-                              nullptr, s);
-    // Feature rows wider than one column block: the two kernels back to back.
-    if ((st = spmm_run(v, w, heads, dy, dtype, h, dx, s)) != MP_OK) return st;
+                              nullptr, s, pn);
+    // Feature rows wider than one column block: the two kernels back to back
+    // (and the edge gradients scaled by their factors in place).
+    if ((st = spmm_run(v, w, heads, dy, dtype, h, dx, s, pn)) != MP_OK) return st;
     if (e == 0) return MP_OK;
-    return sddmm_run(g->src, g->dst, e, x, dy, dtype, h, heads, dw, s);
+    if ((st = sddmm_run(g->src, g->dst, e, x, dy, dtype, h, heads, dw, s)) != MP_OK) return st;
+    return norm_mode ? edge_normalize_run(g, norm_mode, dw, dw, s) : MP_OK;
 }
 
 }  // namespace
@@ -503,6 +519,34 @@ mp_status mp_edge_softmax_backward_heads(const mp_graph *g, const float *alpha,
                                          float *row_dot, void *stream) {
     return softmax_backward_impl(g, alpha, dalpha, heads, dscores, row_dot, stream,
                                  "mp_edge_softmax_backward_heads");
+}
+
+mp_status mp_spmm_fwd_norm(const mp_graph *g, int32_t mode, const float *w, const void *x,
+                           mp_dtype x_dtype, int64_t h, float *y, void *stream) {
+    mp_status st = check_norm_mode(mode, "mp_spmm_fwd_norm");
+    if (st != MP_OK) return st;
+    if ((st = check_spmm(g, w, 1, x, x_dtype, h, y, "x", "y")) != MP_OK) return st;
+    const NormSpec nm = norm_spec(g, mode, true);
+    return spmm_run(forward_view(g), w, 1, x, x_dtype, h, y, static_cast<hipStream_t>(stream),
+                    &nm);
+}
+
+mp_status mp_spmm_dx_norm(const mp_graph *g, int32_t mode, const float *w, const void *dy,
+                          mp_dtype dy_dtype, int64_t h, float *dx, void *stream) {
+    mp_status st = check_norm_mode(mode, "mp_spmm_dx_norm");
+    if (st != MP_OK) return st;
+    if ((st = check_spmm(g, w, 1, dy, dy_dtype, h, dx, "dy", "dx")) != MP_OK) return st;
+    const NormSpec nm = norm_spec(g, mode, false);
+    return spmm_run(transpose_view(g), w, 1, dy, dy_dtype, h, dx,
+                    static_cast<hipStream_t>(stream), &nm);
+}
+
+mp_status mp_spmm_dx_edge_grad_norm(const mp_graph *g, int32_t mode, const float *w,
+                                    const void *x, const void *dy, mp_dtype dtype, int64_t h,
+                                    float *dx, float *dw, void *stream) {
+    mp_status st = check_norm_mode(mode, "mp_spmm_dx_edge_grad_norm");
+    if (st != MP_OK) return st;
+    return dx_edge_grad_impl(g, w, 1, x, dy, dtype, h, dx, dw, stream, mode);
 }
 
 namespace {

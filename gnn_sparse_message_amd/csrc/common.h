@@ -85,22 +85,39 @@ struct CsrView {
     int64_t n;
     int64_t e;
 };
+// Degree normalisation applied to every weight as it is fetched (mode 0: none).
+// The edge's weight becomes w * (float)c, c formed in double as
+// 1 / deg_in(dst) (MP_NORM_MEAN) or 1 / sqrt(deg_out(src) * deg_in(dst))
+// (MP_NORM_SYM), exactly as the normalisation pass forms it; degrees are row
+// lengths of the two CSR forms.  own_is_dst: the walked CSR's rows are
+// destinations (forward); rowptr_other: row pointers of the other form, which
+// give the gathered endpoint's degree.
+struct NormSpec {
+    int32_t mode;
+    bool own_is_dst;
+    const int32_t *rowptr_other;
+};
+
 // `heads` = K: w holds K weights per edge ([E, K], edge-major) and head q owns
 // columns [q*h/K, (q+1)*h/K) of every row (h is a multiple of K; K = 1 is the
 // scalar case).
 mp_status spmm_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
-                   mp_dtype dt, int64_t h, float *out, hipStream_t stream);
+                   mp_dtype dt, int64_t h, float *out, hipStream_t stream,
+                   const NormSpec *norm = nullptr);
 // The same aggregation over the transpose CSR that also writes, for every edge
 // q of owner row j, dw[order[q]] = <x_own[j, :], x[col[q], :]> (fused backward;
 // per head, dw[order[q] * K + head], when K > 1).  With row_dot (attention
 // backward: w = alpha, row_dot [N, K]) it writes the score gradient
-// w * (<x_own[j], x[col[q]]> - row_dot[col[q]]) in that slot instead.  Only for
-// feature rows that fit one column block (spmm_fused_supported).
+// w * (<x_own[j], x[col[q]]> - row_dot[col[q]]) in that slot instead.  With a
+// normalisation (one head only) the dot is scaled by the edge's factor c, the
+// gradient of the raw weight.  Only for feature rows that fit one column block
+// (spmm_fused_supported).
 bool spmm_fused_supported(mp_dtype dt, int64_t h, int64_t heads, const void *x,
                           const void *x_own, const void *out);
 mp_status spmm_fused_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
                          mp_dtype dt, int64_t h, float *out, const void *x_own, float *dw,
-                         const float *row_dot, hipStream_t stream);
+                         const float *row_dot, hipStream_t stream,
+                         const NormSpec *norm = nullptr);
 
 // ---------------------------------------------------------------- SDDMM
 // dw[e * K + q] = <x[src_e], dy[dst_e]> over head q's columns, COO order.

@@ -31,6 +31,7 @@
 // the edge dot product over the lanes of each head separately.
 #include "common.h"
 
+#include <math.h>
 #include <stdlib.h>
 
 namespace mp {
@@ -151,6 +152,7 @@ struct SpmmArgs {
     const uint32_t *dev_totals;       // asynchronously built graph: the plan's rows per class
                                       // on the device; the six fields above are then derived
     int32_t hub_min, wave_min;        // in the kernel from these owner-size thresholds
+    NormSpec norm;                    // normalising kernels only: fetch-time weight scaling
 };
 
 constexpr int64_t kMaxKindBlocks = 1 << 22;   // wave and group owners stride beyond this
@@ -188,11 +190,14 @@ __host__ __device__ inline Partition partition(int64_t at_hub, int64_t at_wave, 
 // kMode == kScoreGrad the weights are softmax outputs alpha and that lane
 // writes the score gradient alpha * (dot - t[dst]) instead (t from row_dot).
 // With kHeads every lane reads the weight of its own head, `head`, per edge.
-template <typename T, int VEC, int L, int TL, int kMode, bool kHeads>
+// With kNorm every weight is scaled as it is fetched by its edge's degree
+// factor (own_deg: the owner row's length), and the fused backward's dot by the
+// same factor.
+template <typename T, int VEC, int L, int TL, int kMode, bool kHeads, bool kNorm>
 __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int64_t end,
                                            int64_t stride, int lane, int64_t hoff, int head,
                                            bool active, const float (&xr)[VEC],
-                                           float (&acc)[VEC]) {
+                                           float (&acc)[VEC], double own_deg) {
     constexpr int G = TL / L;                 // groups per team
     constexpr int kUnroll = unroll_for<kMode, kHeads>();
     const int tl = lane % TL;
@@ -204,11 +209,26 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
         int c = 0;
         uint32_t o = 0;
         float wt = 0.f;
+        float sc = 1.f;   // kNorm: the edge's degree factor
         if (p < end) {   // streamed once: non-temporal, so L2 keeps the feature rows
             c = __builtin_nontemporal_load(&a.col[p]);
             o = (uint32_t)__builtin_nontemporal_load(&a.order[p]);
             if ((int64_t)o >= a.e) o = 0u;   // never taken: order is a permutation of [0, e)
             if constexpr (!kHeads) wt = __builtin_nontemporal_load(&a.w[o]);
+            if constexpr (kNorm) {
+                // mean needs only the destination's degree, the owner's in the
+                // forward; otherwise the gathered endpoint's row length is read
+                const bool mean_own = a.norm.mode == MP_NORM_MEAN && a.norm.own_is_dst;
+                const uint32_t cc = (uint64_t)(uint32_t)c < (uint64_t)a.n ? (uint32_t)c : 0u;
+                const double other = mean_own ? 0.0
+                                              : (double)(a.norm.rowptr_other[cc + 1] -
+                                                         a.norm.rowptr_other[cc]);
+                double f;
+                if (a.norm.mode == MP_NORM_MEAN) f = 1.0 / (a.norm.own_is_dst ? own_deg : other);
+                else f = 1.0 / sqrt(own_deg * other);
+                sc = (float)f;
+                wt = wt * sc;
+            }
         }
         const int n = end - base < TL ? (int)(end - base) : TL;
         const int trips = (n + G - 1) / G;
@@ -275,6 +295,9 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
                     if constexpr (kMode == kScoreGrad) {
                         const float wu = __shfl(wt, slu[u]);
                         if (ok[u] && (lane % L) == 0) a.dw[ou] = wu * (part - tv[u]);
+                    } else if constexpr (kNorm) {
+                        const float su = __shfl(sc, slu[u]);
+                        if (ok[u] && (lane % L) == 0) a.dw[ou] = part * su;
                     } else {
                         if (ok[u] && (lane % L) == 0) a.dw[ou] = part;
                     }
@@ -317,7 +340,7 @@ __device__ __forceinline__ void own_row(const SpmmArgs &a, int row, int64_t hoff
 template <int kMode, bool kHeads>
 constexpr int min_waves_for() { return kHeads ? 1 : (kMode == kPlain ? 4 : 5); }
 
-template <typename T, int VEC, int L, int kMode, bool kHeads>
+template <typename T, int VEC, int L, int kMode, bool kHeads, bool kNorm>
 __global__ __launch_bounds__(kBlock)
 __attribute__((amdgpu_waves_per_eu(min_waves_for<kMode, kHeads>())))
 void spmm_kernel(SpmmArgs a) {
@@ -343,9 +366,10 @@ void spmm_kernel(SpmmArgs a) {
         if ((uint32_t)row >= (uint64_t)a.n) return;   // the plan is a permutation of [0, n)
         const int64_t beg = a.rowptr[row], end = a.rowptr[row + 1];
         own_row<T, VEC, kMode>(a, row, hoff, active, xr);
-        accumulate<T, VEC, L, kWave, kMode, kHeads>(a, beg + (int64_t)wv * kWave, end,
-                                                        (int64_t)kBlock, lane, hoff, head, active,
-                                                        xr, acc);
+        accumulate<T, VEC, L, kWave, kMode, kHeads, kNorm>(a, beg + (int64_t)wv * kWave, end,
+                                                               (int64_t)kBlock, lane, hoff, head,
+                                                               active, xr, acc,
+                                                               (double)(end - beg));
 #pragma unroll
         for (int off = L; off < kWave; off <<= 1)
 #pragma unroll
@@ -379,8 +403,9 @@ void spmm_kernel(SpmmArgs a) {
 #pragma unroll
             for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
             own_row<T, VEC, kMode>(a, row, hoff, active, xr);
-            accumulate<T, VEC, L, kWave, kMode, kHeads>(a, beg, end, (int64_t)kWave, lane,
-                                                            hoff, head, active, xr, acc);
+            accumulate<T, VEC, L, kWave, kMode, kHeads, kNorm>(a, beg, end, (int64_t)kWave,
+                                                                   lane, hoff, head, active, xr,
+                                                                   acc, (double)(end - beg));
 #pragma unroll
             for (int off = L; off < kWave; off <<= 1)
 #pragma unroll
@@ -401,8 +426,9 @@ void spmm_kernel(SpmmArgs a) {
 #pragma unroll
         for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
         own_row<T, VEC, kMode>(a, row, hoff, active && end > beg, xr);
-        accumulate<T, VEC, L, L, kMode, kHeads>(a, beg, end, (int64_t)L, lane, hoff, head,
-                                                    active, xr, acc);
+        accumulate<T, VEC, L, L, kMode, kHeads, kNorm>(a, beg, end, (int64_t)L, lane, hoff,
+                                                           head, active, xr, acc,
+                                                           (double)(end - beg));
         if (active) store_row<VEC>(a.y + (int64_t)row * a.h + hoff, acc);
     }
 }
@@ -429,7 +455,10 @@ Thresholds thresholds_for(int L) {
 template <typename T, int VEC, int L>
 mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *x, int64_t h,
                  float *out, const void *x_own, float *dw, const float *row_dot,
-                 hipStream_t s) {
+                 const NormSpec *norm, hipStream_t s) {
+    const bool normed = norm && norm->mode != 0;
+    if (normed && (heads != 1 || row_dot))
+        return fail(MP_ERR_SHAPE, "fetch-time normalisation takes one head and no row dots");
     const Thresholds th = thresholds_for(L);
     SpmmArgs a;
     a.rowptr = csr.rowptr;
@@ -450,6 +479,7 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
     a.dev_totals = csr.dev_totals;
     a.hub_min = th.hub_min_len;
     a.wave_min = th.wave_min_len;
+    a.norm = normed ? *norm : NormSpec{0, false, nullptr};
     // A launch holds at most 2^32 - 1 work-items; wave and group owners stride.
     Partition pt;
     if (csr.dev_totals) {
@@ -486,15 +516,21 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
     if (dw) {   // fused backward: one column block holds the whole feature row
         if (gy != 1) return fail(MP_ERR_SHAPE, "fused backward needs H <= %d", L * VEC);
         if (row_dot) {
-            if (heads > 1) spmm_kernel<T, VEC, L, kScoreGrad, true><<<grid, kBlock, 0, s>>>(a);
-            else spmm_kernel<T, VEC, L, kScoreGrad, false><<<grid, kBlock, 0, s>>>(a);
+            if (heads > 1)
+                spmm_kernel<T, VEC, L, kScoreGrad, true, false><<<grid, kBlock, 0, s>>>(a);
+            else
+                spmm_kernel<T, VEC, L, kScoreGrad, false, false><<<grid, kBlock, 0, s>>>(a);
+        } else if (normed) {
+            spmm_kernel<T, VEC, L, kDw, false, true><<<grid, kBlock, 0, s>>>(a);
         } else {
-            if (heads > 1) spmm_kernel<T, VEC, L, kDw, true><<<grid, kBlock, 0, s>>>(a);
-            else spmm_kernel<T, VEC, L, kDw, false><<<grid, kBlock, 0, s>>>(a);
+            if (heads > 1) spmm_kernel<T, VEC, L, kDw, true, false><<<grid, kBlock, 0, s>>>(a);
+            else spmm_kernel<T, VEC, L, kDw, false, false><<<grid, kBlock, 0, s>>>(a);
         }
+    } else if (normed) {
+        spmm_kernel<T, VEC, L, kPlain, false, true><<<grid, kBlock, 0, s>>>(a);
     } else {
-        if (heads > 1) spmm_kernel<T, VEC, L, kPlain, true><<<grid, kBlock, 0, s>>>(a);
-        else spmm_kernel<T, VEC, L, kPlain, false><<<grid, kBlock, 0, s>>>(a);
+        if (heads > 1) spmm_kernel<T, VEC, L, kPlain, true, false><<<grid, kBlock, 0, s>>>(a);
+        else spmm_kernel<T, VEC, L, kPlain, false, false><<<grid, kBlock, 0, s>>>(a);
     }
     MP_HIP_CHECK(hipGetLastError(), "spmm launch");
     return MP_OK;
@@ -510,15 +546,15 @@ int lanes_for(int64_t h, int vec) {
 template <typename T, int VEC>
 mp_status launch_lanes(const CsrView &csr, const float *w, int64_t heads, const void *x,
                        int64_t h, float *out, const void *x_own, float *dw,
-                       const float *row_dot, hipStream_t s) {
+                       const float *row_dot, const NormSpec *nm, hipStream_t s) {
     switch (lanes_for(h, VEC)) {
-        case 1: return launch<T, VEC, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
-        case 2: return launch<T, VEC, 2>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
-        case 4: return launch<T, VEC, 4>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
-        case 8: return launch<T, VEC, 8>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
-        case 16: return launch<T, VEC, 16>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
-        case 32: return launch<T, VEC, 32>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
-        default: return launch<T, VEC, 64>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
+        case 1: return launch<T, VEC, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
+        case 2: return launch<T, VEC, 2>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
+        case 4: return launch<T, VEC, 4>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
+        case 8: return launch<T, VEC, 8>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
+        case 16: return launch<T, VEC, 16>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
+        case 32: return launch<T, VEC, 32>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
+        default: return launch<T, VEC, 64>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
     }
 }
 
@@ -527,8 +563,8 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 }  // namespace
 
 mp_status spmm_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
-                   mp_dtype dt, int64_t h, float *out, hipStream_t s) {
-    return spmm_fused_run(csr, w, heads, x, dt, h, out, nullptr, nullptr, nullptr, s);
+                   mp_dtype dt, int64_t h, float *out, hipStream_t s, const NormSpec *norm) {
+    return spmm_fused_run(csr, w, heads, x, dt, h, out, nullptr, nullptr, nullptr, s, norm);
 }
 
 // 16-byte lanes need aligned rows and heads that are whole lanes wide.
@@ -546,15 +582,15 @@ bool spmm_fused_supported(mp_dtype dt, int64_t h, int64_t heads, const void *x,
 
 mp_status spmm_fused_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
                          mp_dtype dt, int64_t h, float *out, const void *x_own, float *dw,
-                         const float *row_dot, hipStream_t s) {
+                         const float *row_dot, hipStream_t s, const NormSpec *nm) {
     if (dt == MP_F32) {
         if (vector_lanes_ok(4, h, heads, x, x_own, out))
-            return launch_lanes<float, 4>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
-        return launch_lanes<float, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
+            return launch_lanes<float, 4>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
+        return launch_lanes<float, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
     }
     if (vector_lanes_ok(8, h, heads, x, x_own, out))
-        return launch_lanes<uint16_t, 8>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
-    return launch_lanes<uint16_t, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, s);
+        return launch_lanes<uint16_t, 8>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
+    return launch_lanes<uint16_t, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
 }
 
 }  // namespace mp

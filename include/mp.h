@@ -366,6 +366,32 @@ mp_status mp_attention_backward(const mp_graph *g, const float *alpha, int64_t h
 mp_status mp_edge_normalize(const mp_graph *g, int32_t mode, const float *in, float *out,
                             void *stream);
 
+/*
+ * The same normalisation applied to each weight as the aggregation fetches it
+ * (Step 3's normalised adjacency without a separate pass over the weights):
+ * every edge's weight is used as w_e * (float)c_e, with c_e formed in double
+ * exactly as mp_edge_normalize forms it, so each call returns bit for bit what
+ * mp_edge_normalize followed by the plain call returns.
+ *   mp_spmm_fwd_norm           Y  = A_{norm(w)} X        (as mp_spmm_fwd)
+ *   mp_spmm_dx_norm            dX = A_{norm(w)}^T dY     (as mp_spmm_dx)
+ *   mp_spmm_dx_edge_grad_norm  dX as above and dw_e = c_e <X[src_e], dY[dst_e]>,
+ *                              the gradient with respect to the raw weights
+ *                              (as mp_spmm_dx_edge_grad, then mp_edge_normalize
+ *                              of its dw).
+ * In the forward walk deg_in(dst) is the owner row's length, so MP_NORM_MEAN
+ * reads nothing extra there; the other cases read the gathered endpoint's row
+ * length, one 8-byte random read per edge.  One weight per edge (no heads).
+ * Arguments and errors as the plain calls, plus MP_ERR_DTYPE for an unknown
+ * mode.
+ */
+mp_status mp_spmm_fwd_norm(const mp_graph *g, int32_t mode, const float *w, const void *x,
+                           mp_dtype x_dtype, int64_t h, float *y, void *stream);
+mp_status mp_spmm_dx_norm(const mp_graph *g, int32_t mode, const float *w, const void *dy,
+                          mp_dtype dy_dtype, int64_t h, float *dx, void *stream);
+mp_status mp_spmm_dx_edge_grad_norm(const mp_graph *g, int32_t mode, const float *w,
+                                    const void *x, const void *dy, mp_dtype dtype, int64_t h,
+                                    float *dx, float *dw, void *stream);
+
 /* Static text for a status code. */
 const char *mp_status_string(mp_status status);
 

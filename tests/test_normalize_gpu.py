@@ -93,3 +93,98 @@ def test_rejections(mp):
         mp.mp_edge_normalize(g, 1, t["w"], out=g.col.view(torch.float32))
     with pytest.raises(TypeError):
         mp.mp_edge_normalize(g, 1, t["w"].double())
+
+
+# ---------------------------------------------------------------- normalised at the fetch
+#
+# mp_spmm_fwd_norm / mp_spmm_dx_norm / mp_spmm_dx_edge_grad_norm form each
+# edge's factor exactly as mp_edge_normalize does and use w * factor in the same
+# accumulation order, so they equal the two-call chains bit for bit; the chains
+# themselves are held to the oracle above and below.
+
+def _fetch_cases():
+    yield "witness", synth.witness()
+    yield "one_node_no_edges", synth.random_graph(1, 0, 8, 41)
+    yield "self_loops_one_node", synth.random_graph(1, 9, 4, 42)
+    yield "random_f32_h16", synth.random_graph(700, 9000, 16, 43)
+    yield "ragged_f32_h6", synth.random_graph(900, 12000, 6, 44)
+    yield "power_law_f32_h32", synth.chung_lu(seed=45, n=20000, e=400000, cap=20000.0, h=32,
+                                              feat_dtype="f32")
+    yield "power_law_bf16_h128", synth.chung_lu(seed=46, n=8000, e=200000, cap=8000.0, h=128,
+                                                feat_dtype="bf16")
+    yield "wide_f32_h600", synth.random_graph(400, 5000, 600, 47)
+
+
+FETCH_CASES = list(_fetch_cases())
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("idx", range(len(FETCH_CASES)), ids=[c[0] for c in FETCH_CASES])
+def test_fetch_normalisation_equals_two_calls(mp, mode, idx):
+    wl = FETCH_CASES[idx][1]
+    g, t = _graph(mp, wl)
+    wn = mp.mp_edge_normalize(g, mode, t["w"])
+    y_ref = mp.mp_spmm_fwd(g, wn, t["x"])
+    dx_ref = mp.mp_spmm_dx(g, wn, t["dy"])
+    dw_ref = mp.mp_edge_normalize(g, mode, mp.mp_edge_grad_dw(g, t["x"], t["dy"]))
+    y = mp.mp_spmm_fwd_norm(g, mode, t["w"], t["x"])
+    dx = mp.mp_spmm_dx_norm(g, mode, t["w"], t["dy"])
+    dx2, dw = mp.mp_spmm_dx_edge_grad_norm(g, mode, t["w"], t["x"], t["dy"])
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref), "forward"
+    assert torch.equal(dx, dx_ref), "input gradient"
+    assert torch.equal(dx2, dx_ref), "fused input gradient"
+    assert torch.equal(dw, dw_ref), "fused weight gradient"
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_fetch_normalisation_against_oracle(mp, mode):
+    """The whole normalised layer from raw weights against the oracle: weights
+    normalised by the oracle (rounded to fp32, within 2^-22 of the device's),
+    then the oracle's aggregation, input gradient and edge gradient, the last
+    scaled by the oracle's factors."""
+    wl = synth.chung_lu(seed=48, n=20000, e=400000, cap=20000.0, h=64, feat_dtype="bf16")
+    g, t = _graph(mp, wl)
+    y = mp.mp_spmm_fwd_norm(g, mode, t["w"], t["x"])
+    dx, dw = mp.mp_spmm_dx_edge_grad_norm(g, mode, t["w"], t["x"], t["dy"])
+    torch.cuda.synchronize()
+    wn = oracle.edge_normalize(wl.n, wl.src, wl.dst, mode, wl.w).astype(np.float32)
+    ry, sy = oracle.forward(wl.n, wl.src, wl.dst, wn, wl.x)
+    check_close("Y", y, ry, sy, TAU["f32"])
+    rdx, sdx = oracle.input_grad(wl.n, wl.src, wl.dst, wn, wl.dy)
+    check_close("dX", dx, rdx, sdx, TAU["f32"])
+    factor = oracle.edge_normalize(wl.n, wl.src, wl.dst, mode, np.ones(wl.e, np.float32))
+    rdot, sdot = oracle.edge_grad(wl.src, wl.dst, wl.x, wl.dy)
+    check_close("dw", dw, rdot * factor, sdot * factor, TAU["f32"] + 4 * REL)
+
+
+def test_fetch_normalisation_async_graph(mp):
+    """A graph whose class counts are still on the device gives the same bits."""
+    wl = synth.chung_lu(seed=49, n=6000, e=90000, cap=6000.0, h=64, feat_dtype="f32")
+    t = upload(wl, DEV)
+    g1 = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    g2 = mp.mp_graph_build_async(t["src"], t["dst"], wl.n)
+    for mode in (1, 2):
+        a = [mp.mp_spmm_fwd_norm(g1, mode, t["w"], t["x"]),
+             *mp.mp_spmm_dx_edge_grad_norm(g1, mode, t["w"], t["x"], t["dy"])]
+        b = [mp.mp_spmm_fwd_norm(g2, mode, t["w"], t["x"]),
+             *mp.mp_spmm_dx_edge_grad_norm(g2, mode, t["w"], t["x"], t["dy"])]
+        torch.cuda.synchronize()
+        for u, v in zip(a, b):
+            assert torch.equal(u, v)
+    mp.mp_graph_finish(g2)
+
+
+def test_fetch_normalisation_rejections(mp):
+    wl = synth.random_graph(100, 500, 8, 50)
+    g, t = _graph(mp, wl)
+    with pytest.raises(TypeError):                       # unknown mode
+        mp.mp_spmm_fwd_norm(g, 0, t["w"], t["x"])
+    with pytest.raises(TypeError):
+        mp.mp_spmm_dx_norm(g, 3, t["w"], t["dy"])
+    with pytest.raises(TypeError):
+        mp.mp_spmm_dx_edge_grad_norm(g, 7, t["w"], t["x"], t["dy"])
+    with pytest.raises(ValueError):                      # output aliases the features
+        mp.mp_spmm_fwd_norm(g, 1, t["w"], t["x"], out=t["x"])
+    with pytest.raises(ValueError):                      # dw aliases w
+        mp.mp_spmm_dx_edge_grad_norm(g, 2, t["w"], t["x"], t["dy"], out_dw=t["w"])

@@ -125,9 +125,10 @@ constexpr int kScoreGrad = 2;    // gradients of the scores behind softmax weigh
 // Feature rows in flight per group per step.  The aggregation alone keeps six
 // (held to four waves per SIMD: 4.89 ms against 5.04 ms with four rows at six
 // waves on the power-law graph); the fused backward, which also holds the owner
-// row and the dot products, keeps four.
-template <int kMode, bool kHeads>
-constexpr int unroll_for() { return kMode == kPlain && !kHeads ? 6 : 4; }
+// row and the dot products, keeps four, and so does the aggregation that
+// normalises its weights at the fetch (4.98 ms against 5.62 ms with six).
+template <int kMode, bool kHeads, bool kNorm>
+constexpr int unroll_for() { return kMode == kPlain && !kHeads && !kNorm ? 6 : 4; }
 
 struct SpmmArgs {
     const int32_t *rowptr;
@@ -199,7 +200,7 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
                                            bool active, const float (&xr)[VEC],
                                            float (&acc)[VEC], double own_deg) {
     constexpr int G = TL / L;                 // groups per team
-    constexpr int kUnroll = unroll_for<kMode, kHeads>();
+    constexpr int kUnroll = unroll_for<kMode, kHeads, kNorm>();
     const int tl = lane % TL;
     const int tb = lane - tl;                 // first lane of the team
     const int g = tl / L;

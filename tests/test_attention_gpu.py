@@ -440,3 +440,43 @@ def test_attention_backward_rejections(mp):
                                  out_row_dot=ds.view(-1)[:wl.n * 2].view(wl.n, 2))
     with pytest.raises(TypeError):                   # x and dy dtypes differ
         mp.mp_attention_backward(g, alpha, t["x"].bfloat16(), t["dy"], y)
+
+
+def test_dot_product_attention_layer_chain(mp):
+    """Scores from the SDDMM, softmax over each target's edges, aggregation, and
+    the whole backward including the query and key gradients, all through the
+    library; every stage against the oracle fed the device's previous stage:
+      s = <K[src], Q[dst]>          mp_edge_grad_dw(g, K, Q)
+      alpha = softmax_dst(s)        mp_edge_softmax
+      Y = A_alpha V                 mp_spmm_fwd
+      dV, ds                        mp_attention_backward(g, alpha, V, dY, Y)
+      dK[src] += ds_e Q[dst_e]      mp_spmm_dx(g, ds, Q)
+      dQ[dst] += ds_e K[src_e]      mp_spmm_fwd(g, ds, K)"""
+    wl = synth.chung_lu(seed=64, n=6000, e=120000, cap=6000.0, h=64, feat_dtype="f32")
+    other = synth.random_graph(wl.n, 1, wl.h, 65)          # two more feature arrays
+    kk, qq = wl.x, (wl.dy / 8.0).astype(np.float32)         # /8 = 1/sqrt(H), exact
+    vv, dout = other.x, other.dy
+    t = upload(wl, DEV)
+    g = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    K, Q, V, dY = (torch.from_numpy(a).to(DEV) for a in (kk, qq, vv, dout))
+    s = mp.mp_edge_grad_dw(g, K, Q)
+    alpha, stats = mp.mp_edge_softmax(g, s)
+    y = mp.mp_spmm_fwd(g, alpha, V)
+    dv, ds, rdot = mp.mp_attention_backward(g, alpha, V, dY, y)
+    dk = mp.mp_spmm_dx(g, ds, Q)
+    dq = mp.mp_spmm_fwd(g, ds, K)
+    torch.cuda.synchronize()
+    rs, ss = oracle.edge_grad(wl.src, wl.dst, kk, qq)
+    check_close("scores", s, rs, ss, TAU["f32"])
+    s32 = s.cpu().numpy()
+    _check_softmax(wl, s32, alpha, stats[:, 0], stats[:, 1])
+    a32 = alpha.cpu().numpy()
+    ry, sy = oracle.forward(wl.n, wl.src, wl.dst, a32, vv)
+    check_close("Y", y, ry, sy, TAU["f32"])
+    chain = synth.Workload("chain", wl.n, wl.src, wl.dst, a32, vv, dout, "f32", None, None)
+    _check_attention(chain, a32[:, None], sy, dv, ds.view(-1, 1), rdot.view(-1, 1))
+    ds32 = ds.cpu().numpy()
+    rdk, sdk = oracle.input_grad(wl.n, wl.src, wl.dst, ds32, qq)
+    check_close("dK", dk, rdk, sdk, TAU["f32"])
+    rdq, sdq = oracle.forward(wl.n, wl.src, wl.dst, ds32, kk)
+    check_close("dQ", dq, rdq, sdq, TAU["f32"])

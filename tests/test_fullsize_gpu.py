@@ -25,11 +25,14 @@ def run():
     y = mp.mp_spmm_fwd(g, t["w"], t["x"])
     dx = mp.mp_spmm_dx(g, t["w"], t["dy"])
     dw = mp.mp_edge_grad_dw(g, t["x"], t["dy"])
+    # the fused backward the benchmark's step runs, against the two calls
+    fdx, fdw = mp.mp_spmm_dx_edge_grad(g, t["w"], t["x"], t["dy"])
     torch.cuda.synchronize()
+    fused_equal = bool(torch.equal(fdx, dx) and torch.equal(fdw, dw))
     out = {"g": {k: v.cpu().numpy() for k, v in g.arrays.items()},
-           "cc": g.class_count, "cc_t": g.class_count_t,
+           "cc": g.class_count, "cc_t": g.class_count_t, "fused_equal": fused_equal,
            "y": y.cpu().numpy(), "dx": dx.cpu().numpy(), "dw": dw.cpu().numpy()}
-    del t, g, y, dx, dw
+    del t, g, y, dx, dw, fdx, fdw
     torch.cuda.empty_cache()
     return wl, out
 
@@ -85,6 +88,13 @@ def test_fullsize_edge_grad_sampled(run):
     ref, s = oracle.edge_grad_edges(wl.src, wl.dst, wl.x, wl.dy, edges)
     check_close("dw edges", out["dw"][edges], ref, s, TAU["bf16"])
     check_close("dw edges (fp32 bound)", out["dw"][edges], ref, s, TAU["f32"])
+
+
+def test_fullsize_fused_backward_equals_separate_calls(run):
+    """The step's fused backward returns the bits of mp_spmm_dx and
+    mp_edge_grad_dw, which the tests above hold to the oracle."""
+    _, out = run
+    assert out["fused_equal"]
 
 
 def test_fullsize_outputs_finite_everywhere(run):

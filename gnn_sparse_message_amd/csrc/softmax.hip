@@ -165,13 +165,36 @@ __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowArgs r) {
             ms[j] = MaxSum{-INFINITY, 0.f};
             dot[j] = 0.f;
         }
-        for (int64_t p = beg; p < end; p += step) {
-            float v[KW];
-            load_heads<KW>(r.a + (int64_t)coo(r, p) * K + q0, r.vec_ok, v);
+        // kU edges at a time: their order entries, then their values, are in
+        // flight together before the first is combined (the same sequence of
+        // updates as one edge at a time, so the same bits).
+        constexpr int kU = KW <= 2 ? 8 : 4;
+        for (int64_t p0 = beg; p0 < end; p0 += step * kU) {
+            uint32_t o[kU];
 #pragma unroll
-            for (int j = 0; j < KW; ++j) {
-                if (kBackward) dot[j] += v[j];
-                else ms[j] = ms_add(ms[j], v[j]);
+            for (int u = 0; u < kU; ++u) {
+                const int64_t p = p0 + u * step;
+                o[u] = p < end ? coo(r, p) : 0u;
+            }
+            float v[kU][KW];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                if (p0 + u * step < end) {
+                    load_heads<KW>(r.a + (int64_t)o[u] * K + q0, r.vec_ok, v[u]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < KW; ++j) v[u][j] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                if (p0 + u * step < end) {
+#pragma unroll
+                    for (int j = 0; j < KW; ++j) {
+                        if (kBackward) dot[j] += v[u][j];
+                        else ms[j] = ms_add(ms[j], v[u][j]);
+                    }
+                }
             }
         }
     };
@@ -269,6 +292,10 @@ __device__ __forceinline__ int64_t stat_slot(const int32_t *dst, int64_t i, int 
     return (int64_t)dst[e] * k + (i - e * k);
 }
 
+// Items per thread in flight in the edge passes: each item's statistics are a
+// gather that depends on its dst, so several chains run side by side.
+constexpr int kApplyU = 4;
+
 // alpha_e = exp(s_e - m[dst_e]) / z[dst_e]   (per head with kHeads)
 template <bool kHeads>
 __global__ __launch_bounds__(kBlock) void softmax_apply_kernel(const int32_t *__restrict__ dst,
@@ -277,9 +304,21 @@ __global__ __launch_bounds__(kBlock) void softmax_apply_kernel(const int32_t *__
                                                                float *__restrict__ alpha,
                                                                int64_t items, int k) {
     const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < items; i += stride) {
-        const float2 st = stats[stat_slot<kHeads>(dst, i, k)];
-        alpha[i] = expf(s[i] - st.x) / st.y;
+    for (int64_t i0 = (int64_t)blockIdx.x * kBlock + threadIdx.x; i0 < items;
+         i0 += stride * kApplyU) {
+        float2 st[kApplyU];
+        float sv[kApplyU];
+#pragma unroll
+        for (int u = 0; u < kApplyU; ++u) {
+            const int64_t i = i0 + u * stride;
+            st[u] = i < items ? stats[stat_slot<kHeads>(dst, i, k)] : make_float2(0.f, 1.f);
+            sv[u] = i < items ? s[i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kApplyU; ++u) {
+            const int64_t i = i0 + u * stride;
+            if (i < items) alpha[i] = expf(sv[u] - st[u].x) / st[u].y;
+        }
     }
 }
 
@@ -299,8 +338,22 @@ __global__ __launch_bounds__(kBlock) void softmax_backward_apply_kernel(
     const float *__restrict__ dalpha, const float *__restrict__ rdot, float *__restrict__ ds,
     int64_t items, int k) {
     const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < items; i += stride)
-        ds[i] = alpha[i] * (dalpha[i] - rdot[stat_slot<kHeads>(dst, i, k)]);
+    for (int64_t i0 = (int64_t)blockIdx.x * kBlock + threadIdx.x; i0 < items;
+         i0 += stride * kApplyU) {
+        float t[kApplyU], av[kApplyU], dv[kApplyU];
+#pragma unroll
+        for (int u = 0; u < kApplyU; ++u) {
+            const int64_t i = i0 + u * stride;
+            t[u] = i < items ? rdot[stat_slot<kHeads>(dst, i, k)] : 0.f;
+            av[u] = i < items ? alpha[i] : 0.f;
+            dv[u] = i < items ? dalpha[i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kApplyU; ++u) {
+            const int64_t i = i0 + u * stride;
+            if (i < items) ds[i] = av[u] * (dv[u] - t[u]);
+        }
+    }
 }
 
 RowArgs row_args(const mp_graph *g) {

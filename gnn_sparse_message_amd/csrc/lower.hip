@@ -232,6 +232,48 @@ __global__ __launch_bounds__(kBlock) void rs_upsweep(PassDir<KeySrc> a0, PassDir
     tile_digit_counts(k, li0, lim, shift, mask, a.hist, ntiles, t);
 }
 
+// Intake that also counts: block t copies tile t of the endpoints to int32
+// (the checks of intake_kernel) and writes the first pass's digit counts of
+// both keys, dst for the forward sort and src for the transpose sort, so the
+// first pass of each direction needs no upsweep of its own.  Tiles as in the
+// radix passes (IT keys per thread, digit-major counts).
+template <typename IdxT, int IT>
+__global__ __launch_bounds__(kBlock) void intake_count_kernel(
+    const IdxT *__restrict__ src, const IdxT *__restrict__ dst, int64_t e, int64_t n,
+    int32_t *__restrict__ src32, int32_t *__restrict__ dst32, uint32_t *__restrict__ flag,
+    int bits, uint32_t *__restrict__ hist_f, uint32_t *__restrict__ hist_t, int64_t ntiles) {
+    const int64_t t = xcd_local_tile();
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int64_t tbase = t * (kBlock * IT);
+    const int64_t left = e - tbase;
+    const int lim = left < (kBlock * IT) ? (int)left : (kBlock * IT);
+    const int li0 = wv * (kWave * IT) + lane;
+    uint32_t kd[IT], ks[IT];
+    bool bad = false;
+#pragma unroll
+    for (int r = 0; r < IT; ++r) {
+        const int li = li0 + r * kWave;
+        kd[r] = ks[r] = 0u;
+        if (li < lim) {
+            const int64_t sv = (int64_t)src[tbase + li];
+            const int64_t dv = (int64_t)dst[tbase + li];
+            const bool ok_s = sv >= 0 && sv < n;
+            const bool ok_d = dv >= 0 && dv < n;
+            ks[r] = ok_s ? (uint32_t)sv : 0u;
+            kd[r] = ok_d ? (uint32_t)dv : 0u;
+            src32[tbase + li] = (int32_t)ks[r];
+            dst32[tbase + li] = (int32_t)kd[r];
+            bad |= !(ok_s && ok_d);
+        }
+    }
+    if (bad) *flag = 1u;   // plain store: every writer stores the same value
+    const uint32_t mask = (1u << bits) - 1u;
+    tile_digit_counts(kd, li0, lim, 0, mask, hist_f, ntiles, t);
+    __syncthreads();       // the counts' LDS is reused by the second key
+    tile_digit_counts(ks, li0, lim, 0, mask, hist_t, ntiles, t);
+}
+
 // One block per digit (and direction): exclusive scan, in tile order, of that
 // digit's per-tile counts (in place), and the digit's total.
 template <bool kDual>
@@ -446,6 +488,14 @@ int key_bits(int64_t n) {
     return bits > 0 ? bits : 1;   // one pass even for n = 1 (a stable copy)
 }
 
+// Width of the first pass's digit, as sort_edges splits the key bits.
+int first_pass_bits(int64_t n) {
+    const int bits = key_bits(n);
+    const int passes = (bits + kDigitBits - 1) / kDigitBits;
+    const int per = (bits + passes - 1) / passes;
+    return per < bits ? per : bits;
+}
+
 // Edge lists up to this size run both directions in every launch (their
 // workspace then holds a second set of sort buffers).
 constexpr int64_t kDualMaxEdges = (int64_t)1 << 22;
@@ -457,12 +507,15 @@ bool dual_mode(int64_t e) { return e <= kDualMaxEdges; }
 
 // One radix pass for one direction (d1 unused) or both (kDual), with tiles of
 // 256 * IT keys.
+// counted: the per-tile digit counts are already in hist (the counting intake).
 template <class KeySrc, bool kIota, bool kOther, bool kWriteKeys, bool kDual, int IT>
 mp_status radix_pass(const PassDir<KeySrc> &d0, const PassDir<KeySrc> &d1, int64_t count,
-                     int shift, int bits, hipStream_t s) {
+                     int shift, int bits, hipStream_t s, bool counted = false) {
     const int64_t ntiles = tiles_for(count, IT);
     const unsigned grid = (unsigned)((kDual ? 2 : 1) * ntiles);
-    rs_upsweep<KeySrc, kDual, IT><<<grid, kBlock, 0, s>>>(d0, d1, count, shift, bits, ntiles);
+    if (!counted)
+        rs_upsweep<KeySrc, kDual, IT><<<grid, kBlock, 0, s>>>(d0, d1, count, shift, bits,
+                                                              ntiles);
     if (ntiles <= kInlineScanMaxTiles) {
         rs_downsweep<KeySrc, kIota, kOther, kWriteKeys, kDual, true, IT>
             <<<grid, kBlock, 0, s>>>(d0, d1, count, shift, bits, ntiles);
@@ -495,9 +548,11 @@ struct EdgeDir {
 // writes the ordinals to `order` and other[order[p]] to `col`; sorted[i]
 // receives the buffer holding direction i's sorted keys.  kDual: both
 // directions in every launch; else dirs[0] only.
+// first_counted: the first pass's per-tile counts are already in the hist
+// buffers (the counting intake).
 template <bool kDual>
 mp_status sort_edges(const EdgeDir *dirs, int64_t e, int64_t n, const uint32_t **sorted,
-                     hipStream_t s) {
+                     hipStream_t s, bool first_counted = false) {
     constexpr int kDirs = kDual ? 2 : 1;
     const int bits = key_bits(n);
     const int passes = (bits + kDigitBits - 1) / kDigitBits;
@@ -531,7 +586,8 @@ mp_status sort_edges(const EdgeDir *dirs, int64_t e, int64_t n, const uint32_t *
         // Small lists (both directions per launch) use small tiles.
         constexpr int IT = kDual ? kItemsSmall : kItems;
         mp_status st = pass == 0
-            ? radix_pass<KeysFromArray, true, true, true, kDual, IT>(pd[0], pd[1], e, shift, pb, s)
+            ? radix_pass<KeysFromArray, true, true, true, kDual, IT>(pd[0], pd[1], e, shift, pb, s,
+                                                                    first_counted)
             : radix_pass<KeysFromArray, false, true, true, kDual, IT>(pd[0], pd[1], e, shift, pb,
                                                                      s);
         if (st != MP_OK) return st;
@@ -632,7 +688,20 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
 
     // A fill kernel, not a memset: the sequence stays valid under graph capture.
     zero_words_kernel<<<1, kBlock, 0, s>>>(info, MP_GRAPH_INFO_WORDS);
-    if (e > 0) {
+    // Large lists: the intake also counts the first pass's digits of both keys.
+    const bool counted = e > 0 && !dual_mode(e);
+    if (counted) {
+        const int64_t nt = tiles_for(e, kItems);
+        const int fb = first_pass_bits(n);
+        if (idx_dtype == MP_I64)
+            intake_count_kernel<int64_t, kItems><<<(unsigned)nt, kBlock, 0, s>>>(
+                static_cast<const int64_t *>(src), static_cast<const int64_t *>(dst), e, n, g->src,
+                g->dst, info + kInfoFlag, fb, b[0].hist, b[1].hist, nt);
+        else
+            intake_count_kernel<int32_t, kItems><<<(unsigned)nt, kBlock, 0, s>>>(
+                static_cast<const int32_t *>(src), static_cast<const int32_t *>(dst), e, n, g->src,
+                g->dst, info + kInfoFlag, fb, b[0].hist, b[1].hist, nt);
+    } else if (e > 0) {
         if (idx_dtype == MP_I64)
             intake_kernel<int64_t><<<grid_for(e), kBlock, 0, s>>>(
                 static_cast<const int64_t *>(src), static_cast<const int64_t *>(dst), e, n, g->src,
@@ -659,7 +728,7 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
                                     RowsDir{sorted[1], g->rowptr_t}, e, n, s);
     } else {
         for (int i = 0; i < 2 && st == MP_OK; ++i) {
-            st = sort_edges<false>(&dirs[i], e, n, &sorted[i], s);
+            st = sort_edges<false>(&dirs[i], e, n, &sorted[i], s, counted);
             const RowsDir r{sorted[i], i == 0 ? g->rowptr : g->rowptr_t};
             if (st == MP_OK) st = row_pointers<false>(r, r, e, n, s);
         }

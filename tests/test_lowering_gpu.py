@@ -50,10 +50,36 @@ def test_tiny_uniform(mp, idx_dtype):
     (50, 1023, 20), (50, 1024, 21), (50, 1025, 22), (5000, 65536, 23), (5000, 65537, 24),
     (1 << 16, (1 << 22), 25), (1 << 16, (1 << 22) + 1, 26),
     (70000, 1024, 27),              # row tiles: 69 plan tiles, past the in-kernel tile sums
+    # large lists: the intake counts the first pass's digits of both keys
+    (100, 5_000_001, 28),           # 7-bit keys: the counted pass is the only one
+    (1 << 16, 6_000_000, 29),       # 16-bit keys: two passes
+    (3_000_000, 5_000_000, 30),     # 22-bit keys: three passes, mostly empty rows
+    (2, (1 << 22) + 4096 * 3 + 1, 31),   # 1-bit keys, one key past a tile edge
 ])
 def test_random_sizes(mp, n, e, seed):
     wl = synth.random_graph(n, e, 1, seed)
     check_structure(_build(mp, wl), wl)
+
+
+@pytest.mark.parametrize("idx_dtype", [torch.int32, torch.int64])
+def test_large_list_index_dtypes(mp, idx_dtype):
+    wl = synth.random_graph(40000, 4_500_000, 1, 32)
+    check_structure(_build(mp, wl, idx_dtype), wl)
+
+
+def test_large_list_bad_index(mp):
+    """An endpoint out of range in a list long enough for the counting intake
+    is reported, and the build still leaves every array in bounds."""
+    wl = synth.random_graph(1000, 5_000_000, 1, 33)
+    src = torch.from_numpy(wl.src).to(DEV)
+    dst = torch.from_numpy(wl.dst).to(DEV)
+    dst[4_999_999] = 1000
+    with pytest.raises(IndexError):
+        mp.mp_graph_build(src, dst, 1000)
+    src[123] = -5
+    dst[4_999_999] = 7
+    with pytest.raises(IndexError):
+        mp.mp_graph_build(src.to(torch.int32), dst.to(torch.int32), 1000)
 
 
 def test_all_edges_one_row(mp):

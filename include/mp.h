@@ -24,8 +24,9 @@
  *   - Outputs are overwritten completely (never accumulated into); a row with
  *     no edges is written as exact zeros.
  *   - Streams: `stream` is a hipStream_t (0 = the null stream).  All device
- *     work is enqueued on it.  Only mp_graph_build synchronises that stream
- *     (once, at its end); the three compute calls return without waiting.
+ *     work is enqueued on it.  Only mp_graph_build and mp_graph_finish
+ *     synchronise that stream (once, at their end); every compute call returns
+ *     without waiting.
  *   - Errors: arguments are validated on the host before anything is
  *     enqueued; a rejected call launches nothing and writes nothing.  No C++
  *     exception crosses this interface.  mp_last_error_detail() returns a

@@ -15,10 +15,12 @@
 //   downsweep -- every block re-reads its tile, ranks each key among equal
 //                digits with 64-lane ballots (stable: rank order = input order),
 //                regroups the tile by digit in LDS and writes it out in runs.
-// Small edge lists (a sampled minibatch) are launch-bound rather than
-// bandwidth-bound, so there both directions share every launch and, when a
-// pass has few tiles, each downsweep block sums the per-tile counts it needs
-// itself (no scan kernel).
+// For long lists the intake already counts the first pass's digits of both
+// keys, so the first pass of each direction starts at its scan.  Small edge
+// lists (a sampled minibatch) are launch-bound rather than bandwidth-bound, so
+// there both directions share every launch and, when a pass has few tiles,
+// each downsweep block sums the per-tile counts it needs itself (no scan
+// kernel).
 // Block-local ranks, never atomics, decide where equal keys land, so the
 // result is the unique stable order.  The opposite endpoint travels with each
 // key, so the last pass writes col[p] = other[order[p]] directly.  Rows are

@@ -17,11 +17,17 @@
 //   long rows -> one 64-lane wave (64/L groups split the edges, butterfly
 //                reduction across groups);
 //   short rows (and empty rows, written as zeros) -> one group of L lanes.
-// For each run of edges the team loads col[p] and w[order[p]] once, coalesced,
-// one edge per lane, then broadcasts them with lane permutes while every group
-// gathers U feature rows at a time (several 16-byte loads in flight per lane).
-// Accumulation is fp32; bf16 inputs are widened exactly.  Feature widths above
-// 64*VEC are covered by column blocks in gridDim.y.
+// For each run of edges the team loads col[p] and order[p] once, coalesced, one
+// edge per lane, and gathers w[order[p]]; it broadcasts them with lane permutes
+// while every group gathers U feature rows at a time (several 16-byte loads in
+// flight per lane).  Accumulation is fp32; bf16 inputs are widened exactly.
+// Feature widths above 64*VEC are covered by column blocks in gridDim.y.
+//
+// The same walk serves the fused backward over the transpose CSR (kDw: the
+// edge gradients formed from the gathered dY rows and the owner's X row), the
+// attention backward (kScoreGrad: score gradients instead, from the row dots
+// <Y, dY>) and the degree normalisation at the fetch (kNorm: each weight
+// scaled by its edge's degree factor as it is read).
 //
 // Multi-head weights (w is [E, K], head q owning columns [q*H/K, (q+1)*H/K) of
 // every row; the per-head reading of vector edge weights, which tinymesh

@@ -15,8 +15,8 @@
 //   downsweep -- every block re-reads its tile, ranks each key among equal
 //                digits with 64-lane ballots (stable: rank order = input order),
 //                regroups the tile by digit in LDS and writes it out in runs.
-// For long lists the intake already counts the first pass's digits of both
-// keys, so the first pass of each direction starts at its scan.  Small edge
+// The intake already counts the first pass's digits of both keys, so the
+// first pass of each direction starts at its scan.  Small edge
 // lists (a sampled minibatch) are launch-bound rather than bandwidth-bound, so
 // there both directions share every launch and, when a pass has few tiles,
 // each downsweep block sums the per-tile counts it needs itself (no scan
@@ -110,26 +110,6 @@ __device__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *total) {
 }
 
 // ------------------------------------------------------------------ intake
-// Copy the caller's endpoints to int32, checking 0 <= v < n.  Out-of-range
-// values are stored as 0 (so later kernels stay in bounds) and raise the flag.
-template <typename IdxT>
-__global__ __launch_bounds__(kBlock) void intake_kernel(const IdxT *__restrict__ src,
-                                                        const IdxT *__restrict__ dst, int64_t e,
-                                                        int64_t n, int32_t *__restrict__ src32,
-                                                        int32_t *__restrict__ dst32,
-                                                        uint32_t *__restrict__ flag) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < e; i += stride) {
-        const int64_t s = (int64_t)src[i];
-        const int64_t d = (int64_t)dst[i];
-        const bool ok_s = s >= 0 && s < n;
-        const bool ok_d = d >= 0 && d < n;
-        src32[i] = ok_s ? (int32_t)s : 0;
-        dst32[i] = ok_d ? (int32_t)d : 0;
-        if (!(ok_s && ok_d)) *flag = 1u;   // plain store: every writer stores the same value
-    }
-}
-
 __global__ void zero_words_kernel(uint32_t *p, int n) {
     for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
 }
@@ -234,8 +214,9 @@ __global__ __launch_bounds__(kBlock) void rs_upsweep(PassDir<KeySrc> a0, PassDir
     tile_digit_counts(k, li0, lim, shift, mask, a.hist, ntiles, t);
 }
 
-// Intake that also counts: block t copies tile t of the endpoints to int32
-// (the checks of intake_kernel) and writes the first pass's digit counts of
+// Intake: block t copies tile t of the caller's endpoints to int32, checking
+// 0 <= v < n (an out-of-range value is stored as 0, so later kernels stay in
+// bounds, and raises the flag), and writes the first pass's digit counts of
 // both keys, dst for the forward sort and src for the transpose sort, so the
 // first pass of each direction needs no upsweep of its own.  Tiles as in the
 // radix passes (IT keys per thread, digit-major counts).
@@ -498,6 +479,23 @@ int first_pass_bits(int64_t n) {
     return per < bits ? per : bits;
 }
 
+// Counting intake over tiles of 256 * IT edges.
+template <int IT>
+void intake_count(const void *src, const void *dst, mp_dtype idx_dtype, int64_t e, int64_t n,
+                  mp_graph *g, int first_bits, uint32_t *hist_f, uint32_t *hist_t,
+                  hipStream_t s) {
+    const int64_t nt = tiles_for(e, IT);
+    if (idx_dtype == MP_I64)
+        intake_count_kernel<int64_t, IT><<<(unsigned)nt, kBlock, 0, s>>>(
+            static_cast<const int64_t *>(src), static_cast<const int64_t *>(dst), e, n, g->src,
+            g->dst, g->info + kInfoFlag, first_bits, hist_f, hist_t, nt);
+    else
+        intake_count_kernel<int32_t, IT><<<(unsigned)nt, kBlock, 0, s>>>(
+            static_cast<const int32_t *>(src), static_cast<const int32_t *>(dst), e, n, g->src,
+            g->dst, g->info + kInfoFlag, first_bits, hist_f, hist_t, nt);
+}
+
+
 // Edge lists up to this size run both directions in every launch (their
 // workspace then holds a second set of sort buffers).
 constexpr int64_t kDualMaxEdges = (int64_t)1 << 22;
@@ -690,28 +688,15 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
 
     // A fill kernel, not a memset: the sequence stays valid under graph capture.
     zero_words_kernel<<<1, kBlock, 0, s>>>(info, MP_GRAPH_INFO_WORDS);
-    // Large lists: the intake also counts the first pass's digits of both keys.
-    const bool counted = e > 0 && !dual_mode(e);
+    // The intake also counts the first pass's digits of both keys, in the tiles
+    // of that pass (1024 keys when both directions share the launches).
+    const bool counted = e > 0;
     if (counted) {
-        const int64_t nt = tiles_for(e, kItems);
         const int fb = first_pass_bits(n);
-        if (idx_dtype == MP_I64)
-            intake_count_kernel<int64_t, kItems><<<(unsigned)nt, kBlock, 0, s>>>(
-                static_cast<const int64_t *>(src), static_cast<const int64_t *>(dst), e, n, g->src,
-                g->dst, info + kInfoFlag, fb, b[0].hist, b[1].hist, nt);
+        if (dual_mode(e))
+            intake_count<kItemsSmall>(src, dst, idx_dtype, e, n, g, fb, b[0].hist, b[1].hist, s);
         else
-            intake_count_kernel<int32_t, kItems><<<(unsigned)nt, kBlock, 0, s>>>(
-                static_cast<const int32_t *>(src), static_cast<const int32_t *>(dst), e, n, g->src,
-                g->dst, info + kInfoFlag, fb, b[0].hist, b[1].hist, nt);
-    } else if (e > 0) {
-        if (idx_dtype == MP_I64)
-            intake_kernel<int64_t><<<grid_for(e), kBlock, 0, s>>>(
-                static_cast<const int64_t *>(src), static_cast<const int64_t *>(dst), e, n, g->src,
-                g->dst, info + kInfoFlag);
-        else
-            intake_kernel<int32_t><<<grid_for(e), kBlock, 0, s>>>(
-                static_cast<const int32_t *>(src), static_cast<const int32_t *>(dst), e, n, g->src,
-                g->dst, info + kInfoFlag);
+            intake_count<kItems>(src, dst, idx_dtype, e, n, g, fb, b[0].hist, b[1].hist, s);
     }
     MP_HIP_CHECK(hipGetLastError(), "intake launch");
 
@@ -724,7 +709,7 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
     const uint32_t *sorted[2] = {b[0].k0, b[1].k0};
     mp_status st = MP_OK;
     if (dual_mode(e)) {
-        if (e > 0) st = sort_edges<true>(dirs, e, n, sorted, s);
+        if (e > 0) st = sort_edges<true>(dirs, e, n, sorted, s, counted);
         if (st == MP_OK)
             st = row_pointers<true>(RowsDir{sorted[0], g->rowptr},
                                     RowsDir{sorted[1], g->rowptr_t}, e, n, s);

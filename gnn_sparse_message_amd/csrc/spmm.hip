@@ -77,6 +77,42 @@ struct Feat<uint16_t, 1> {
     }
 };
 
+// A gathered feature slice as loaded: bf16 stays packed two to a register until
+// each value is used (widening is exact, so the values are those of Feat), which
+// halves the registers a row in flight holds.
+template <typename T, int VEC>
+struct Raw;
+
+template <int VEC>
+struct Raw<float, VEC> {
+    float f[VEC];
+    __device__ __forceinline__ void load(const float *p) { Feat<float, VEC>::load(p, f); }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) f[v] = 0.f;
+    }
+    __device__ __forceinline__ float at(int v) const { return f[v]; }
+};
+template <>
+struct Raw<uint16_t, 8> {
+    uint32_t q[4];
+    __device__ __forceinline__ void load(const uint16_t *p) {
+        const uint4 r = *reinterpret_cast<const uint4 *>(p);
+        q[0] = r.x; q[1] = r.y; q[2] = r.z; q[3] = r.w;
+    }
+    __device__ __forceinline__ void zero() { q[0] = q[1] = q[2] = q[3] = 0u; }
+    __device__ __forceinline__ float at(int v) const {
+        return (v & 1) ? __uint_as_float(q[v >> 1] & 0xffff0000u) : __uint_as_float(q[v >> 1] << 16);
+    }
+};
+template <>
+struct Raw<uint16_t, 1> {
+    uint32_t q;
+    __device__ __forceinline__ void load(const uint16_t *p) { q = (uint32_t)(*p); }
+    __device__ __forceinline__ void zero() { q = 0u; }
+    __device__ __forceinline__ float at(int) const { return __uint_as_float(q << 16); }
+};
+
 // Output rows are written once and not read again here: non-temporal stores
 // keep them from displacing hot feature rows in L2.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -100,10 +136,10 @@ __device__ __forceinline__ void store_row(float *p, const float (&v)[VEC]) {
 // No bare product is left, so nothing can be contracted into the lane
 // reduction that follows.
 template <typename T, int VEC>
-__device__ __forceinline__ float edge_dot(const float (&xr)[VEC], const float (&xv)[VEC]) {
+__device__ __forceinline__ float edge_dot(const float (&xr)[VEC], const Raw<T, VEC> &xv) {
     float s = 0.f;
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) s = fmaf(xr[v], xv[v], s);
+    for (int v = 0; v < VEC; ++v) s = fmaf(xr[v], xv.at(v), s);
     return s;
 }
 
@@ -128,13 +164,12 @@ constexpr int kPlain = 0;        // nothing: forward or input gradient
 constexpr int kDw = 1;           // edge-weight gradients (fused backward)
 constexpr int kScoreGrad = 2;    // gradients of the scores behind softmax weights
 
-// Feature rows in flight per group per step.  The aggregation alone keeps six
-// (held to four waves per SIMD: 4.89 ms against 5.04 ms with four rows at six
-// waves on the power-law graph); the fused backward, which also holds the owner
-// row and the dot products, keeps four, and so does the aggregation that
-// normalises its weights at the fetch (4.98 ms against 5.62 ms with six).
+// Feature rows in flight per group per step.  The single-head aggregation
+// keeps six, the fused backward (which also holds the owner row and the dot
+// products) and the multi-head kernels four; with the rows held packed (Raw)
+// the single-head aggregation then fits seven waves per SIMD.
 template <int kMode, bool kHeads, bool kNorm>
-constexpr int unroll_for() { return kMode == kPlain && !kHeads && !kNorm ? 6 : 4; }
+constexpr int unroll_for() { return kMode == kPlain && !kHeads ? 6 : 4; }
 
 struct SpmmArgs {
     const int32_t *rowptr;
@@ -260,15 +295,11 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
                     wh[u] = ok[u] && active ? a.w[(int64_t)oh[u] * a.heads + head] : 0.f;
                 }
             }
-            float xv[kUnroll][VEC];
+            Raw<T, VEC> xv[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                if (ok[u] && active) {
-                    Feat<T, VEC>::load(X + (int64_t)cu[u] * a.h + hoff, xv[u]);
-                } else {
-#pragma unroll
-                    for (int v = 0; v < VEC; ++v) xv[u][v] = 0.f;
-                }
+                if (ok[u] && active) xv[u].load(X + (int64_t)cu[u] * a.h + hoff);
+                else xv[u].zero();
             }
             // Score-gradient mode: the row terms of the gathered rows, loaded with
             // the feature rows so their latency overlaps (a random 4-byte read each).
@@ -290,7 +321,7 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
                     wv = ok[u] ? wu : 0.f;
                 }
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) acc[v] = fmaf(wv, xv[u][v], acc[v]);
+                for (int v = 0; v < VEC; ++v) acc[v] = fmaf(wv, xv[u].at(v), acc[v]);
             }
             if constexpr (kMode != kPlain && !kHeads) {
 #pragma unroll
@@ -340,10 +371,10 @@ __device__ __forceinline__ void own_row(const SpmmArgs &a, int row, int64_t hoff
     }
 }
 
-// Occupancy: the single-head fused backward needs a few registers more than fit
-// five waves per SIMD; holding it to five (two spilled registers) measured
-// 8.20 ms against 8.80 ms at four.  The single-head aggregation is held to four
-// (its six rows in flight).  The multi-head variants are left to the compiler.
+// Occupancy floors: the single-head fused backward is held to five waves per
+// SIMD (8.20 ms against 8.80 ms at four before the rows were held packed; it
+// now fits five without spilling), the single-head aggregation to four.  The
+// multi-head variants are left to the compiler.
 template <int kMode, bool kHeads>
 constexpr int min_waves_for() { return kHeads ? 1 : (kMode == kPlain ? 4 : 5); }
 

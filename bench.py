@@ -408,6 +408,14 @@ def main():
         lambda: mp.mp_spmm_dx_edge_grad_norm(g, mp.MP_NORM_SYM, w, x, dy, out_dx=dx_n,
                                              out_dw=dw_n))
     del dx_n, dw_n
+    # The fused backward with weights and gradients interleaved ([E, 2]).
+    wg = torch.empty((e, 2), dtype=torch.float32, device=dev)
+    wg[:, 0] = w
+    dx_p = torch.empty_like(dx)
+    standalone["bwd_pair"] = time_op(
+        lambda: mp.mp_spmm_dx_edge_grad_pair(g, wg, x, dy, out_dx=dx_p))
+    same_pair = bool(torch.equal(dx_p, dx) and torch.equal(wg[:, 1], dw))
+    del wg, dx_p
     # The whole attention backward in one call (alpha = the edge weights, Y = the
     # forward output of the steps): replaces the fused backward + softmax backward.
     dx_att = torch.empty_like(dx)
@@ -475,6 +483,7 @@ def main():
     bytes_["attention_backward"] = bytes_["bwd"] + (4 + 2) * n * h + 4 * n
     # normalised at the fetch: the plain call's bytes plus the other CSR's row
     # pointers, where the degrees come from
+    bytes_["bwd_pair"] = bytes_["bwd"]
     bytes_["fwd_norm_sym"] = bytes_["fwd"] + 4 * (n + 1)
     bytes_["fwd_norm_mean"] = bytes_["fwd"]
     bytes_["bwd_norm_sym"] = bytes_["bwd"] + 4 * (n + 1)
@@ -499,6 +508,7 @@ def main():
     per_op_standalone["equal_to_fused"] = same
     per_op_standalone["heads"] = heads
     per_op_standalone["heads_fused_equal_to_separate"] = same_heads
+    per_op_standalone["pair_equal_to_fused"] = same_pair
     # what the fetch-time normalisation replaces: a normalisation pass, then the call
     per_op_standalone["fwd_norm_two_calls_ms"] = round(
         standalone["edge_normalize_sym"] + statistics.median(times["fwd"]), 4)

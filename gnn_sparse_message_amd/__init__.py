@@ -33,6 +33,7 @@ __all__ = [
     "mp_spmm_dx_heads", "mp_edge_grad_dw_heads", "mp_spmm_dx_edge_grad_heads", "mp_edge_softmax",
     "mp_edge_softmax_backward", "mp_edge_softmax_heads", "mp_edge_softmax_backward_heads",
     "mp_attention_backward", "mp_spmm_fwd_norm", "mp_spmm_dx_norm", "mp_spmm_dx_edge_grad_norm",
+    "mp_spmm_dx_edge_grad_pair",
     "mp_edge_normalize", "MP_NORM_MEAN", "MP_NORM_SYM",
     "mp_status_string", "mp_version", "library_path",
     "NUM_CLASSES",
@@ -124,6 +125,7 @@ def _load():
         "mp_spmm_fwd_norm": (i32, [gp, i32, vp, vp, i32, i64, vp, vp]),
         "mp_spmm_dx_norm": (i32, [gp, i32, vp, vp, i32, i64, vp, vp]),
         "mp_spmm_dx_edge_grad_norm": (i32, [gp, i32, vp, vp, vp, i32, i64, vp, vp, vp]),
+        "mp_spmm_dx_edge_grad_pair": (i32, [gp, vp, vp, vp, i32, i64, vp, vp]),
         "mp_edge_normalize": (i32, [gp, i32, vp, vp, vp]),
         "mp_status_string": (ctypes.c_char_p, [i32]),
         "mp_last_error_detail": (ctypes.c_char_p, []),
@@ -385,6 +387,27 @@ def mp_spmm_dx_edge_grad_norm(g: Graph, mode: int, w, x, dy, out_dx=None, out_dw
                                           code, h, _ptr(dx), _ptr(dw) if g.num_edges else None,
                                           _stream(dy)), "mp_spmm_dx_edge_grad_norm")
     return dx, dw
+
+
+def mp_spmm_dx_edge_grad_pair(g: Graph, wg, x, dy, out_dx=None):
+    """Fused backward with weights and gradients interleaved: wg is float32
+    [E, 2], wg[:, 0] the weights (read) and wg[:, 1] receiving dw (written in
+    place).  Returns dX; dw is the view wg[:, 1]."""
+    _need_tensor("wg", wg)
+    if wg.dtype != torch.float32:
+        raise TypeError(f"wg must be float32, got {wg.dtype}")
+    if wg.dim() != 2 or tuple(wg.shape) != (g.num_edges, 2):
+        raise ValueError(f"wg must have shape [{g.num_edges}, 2], got {tuple(wg.shape)}")
+    h = _features("x", x, g)
+    if _features("dy", dy, g) != h:
+        raise ValueError("x and dy must have the same feature width")
+    code = _code(dy) if x.dtype == dy.dtype else 0
+    dx = _out(out_dx, (g.num_nodes, h), dy)
+    _check(_lib.mp_spmm_dx_edge_grad_pair(ctypes.byref(g._desc),
+                                          _ptr(wg) if g.num_edges else None, _ptr(x), _ptr(dy),
+                                          code, h, _ptr(dx), _stream(dy)),
+           "mp_spmm_dx_edge_grad_pair")
+    return dx
 
 
 def mp_edge_grad_dw(g: Graph, x, dy, out=None):

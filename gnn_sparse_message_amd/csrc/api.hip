@@ -541,6 +541,34 @@ mp_status mp_spmm_dx_norm(const mp_graph *g, int32_t mode, const float *w, const
                     static_cast<hipStream_t>(stream), &nm);
 }
 
+mp_status mp_spmm_dx_edge_grad_pair(const mp_graph *g, float *wg, const void *x,
+                                    const void *dy, mp_dtype dtype, int64_t h, float *dx,
+                                    void *stream) {
+    mp_status st = check_spmm(g, wg, 1, dy, dtype, h, dx, "dy", "dx");
+    if (st != MP_OK) return st;
+    const int64_t n = g->num_nodes, e = g->num_edges;
+    if (!x) return fail(MP_ERR_NULL, "x is NULL");
+    const size_t xs = dtype_size(dtype);
+    if (!aligned(x, xs)) return fail(MP_ERR_ALIGN, "x not aligned to %zu bytes", xs);
+    if ((st = check_device(x, "x")) != MP_OK) return st;
+    const Range rwg = range(wg, 2 * e, 4, "wg");
+    RangeList others = graph_ranges(g);
+    others.add(range(x, n * h, xs, "x"));
+    others.add(range(dy, n * h, xs, "dy"));
+    others.add(range(dx, n * h, 4, "dx"));
+    if (const char *hit = others.overlapping(rwg))
+        return fail(MP_ERR_ALIAS, "wg overlaps %s", hit);
+    if (overlap(range(dx, n * h, 4, "dx"), range(x, n * h, xs, "x")))
+        return fail(MP_ERR_ALIAS, "dx overlaps x");
+    if (!spmm_fused_supported(dtype, h, 1, dy, x, dx))
+        return fail(MP_ERR_SHAPE,
+                    "the interleaved layout needs the fused backward (H up to 64 lanes of "
+                    "16-byte slices, aligned rows); H = %lld", (long long)h);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return spmm_fused_run(transpose_view(g), wg, 1, dy, dtype, h, dx, x,
+                          e > 0 ? wg + 1 : nullptr, nullptr, s, nullptr, e > 0);
+}
+
 mp_status mp_spmm_dx_edge_grad_norm(const mp_graph *g, int32_t mode, const float *w,
                                     const void *x, const void *dy, mp_dtype dtype, int64_t h,
                                     float *dx, float *dw, void *stream) {

@@ -114,10 +114,12 @@ mp_status spmm_run(const CsrView &csr, const float *w, int64_t heads, const void
 // (spmm_fused_supported).
 bool spmm_fused_supported(mp_dtype dt, int64_t h, int64_t heads, const void *x,
                           const void *x_own, const void *out);
+// pair: w and dw are one interleaved [E][2] array (w at [e][0], dw stored to
+// [e][1]; dw points at [0][1]); one head, no row dots, no normalisation.
 mp_status spmm_fused_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
                          mp_dtype dt, int64_t h, float *out, const void *x_own, float *dw,
                          const float *row_dot, hipStream_t stream,
-                         const NormSpec *norm = nullptr);
+                         const NormSpec *norm = nullptr, bool pair = false);
 
 // ---------------------------------------------------------------- SDDMM
 // dw[e * K + q] = <x[src_e], dy[dst_e]> over head q's columns, COO order.

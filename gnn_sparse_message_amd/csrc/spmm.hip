@@ -163,6 +163,7 @@ __device__ __forceinline__ float head_sum(float part, int lane, int sub, int seg
 constexpr int kPlain = 0;        // nothing: forward or input gradient
 constexpr int kDw = 1;           // edge-weight gradients (fused backward)
 constexpr int kScoreGrad = 2;    // gradients of the scores behind softmax weights
+constexpr int kDwPair = 3;       // as kDw, with w and dw interleaved ([E][2]: w, dw)
 
 // Feature rows in flight per group per step.  The single-head aggregation
 // keeps six, the fused backward (which also holds the owner row and the dot
@@ -256,7 +257,12 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
             c = __builtin_nontemporal_load(&a.col[p]);
             o = (uint32_t)__builtin_nontemporal_load(&a.order[p]);
             if ((int64_t)o >= a.e) o = 0u;   // never taken: order is a permutation of [0, e)
-            if constexpr (!kHeads) wt = __builtin_nontemporal_load(&a.w[o]);
+            if constexpr (kMode == kDwPair) {
+                // an ordinary load: the line stays in L2 for this edge's dw store
+                wt = a.w[(int64_t)o * 2];
+            } else if constexpr (!kHeads) {
+                wt = __builtin_nontemporal_load(&a.w[o]);
+            }
             if constexpr (kNorm) {
                 // mean needs only the destination's degree, the owner's in the
                 // forward; otherwise the gathered endpoint's row length is read
@@ -336,6 +342,8 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
                     } else if constexpr (kNorm) {
                         const float su = __shfl(sc, slu[u]);
                         if (ok[u] && (lane % L) == 0) a.dw[ou] = part * su;
+                    } else if constexpr (kMode == kDwPair) {
+                        if (ok[u] && (lane % L) == 0) a.dw[(int64_t)ou * 2] = part;
                     } else {
                         if (ok[u] && (lane % L) == 0) a.dw[ou] = part;
                     }
@@ -493,10 +501,12 @@ Thresholds thresholds_for(int L) {
 template <typename T, int VEC, int L>
 mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *x, int64_t h,
                  float *out, const void *x_own, float *dw, const float *row_dot,
-                 const NormSpec *norm, hipStream_t s) {
+                 const NormSpec *norm, bool pair, hipStream_t s) {
     const bool normed = norm && norm->mode != 0;
     if (normed && (heads != 1 || row_dot))
         return fail(MP_ERR_SHAPE, "fetch-time normalisation takes one head and no row dots");
+    if (pair && (heads != 1 || row_dot || normed || !dw))
+        return fail(MP_ERR_SHAPE, "the interleaved weight layout is for the one-head fused backward");
     const Thresholds th = thresholds_for(L);
     SpmmArgs a;
     a.rowptr = csr.rowptr;
@@ -560,6 +570,8 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
                 spmm_kernel<T, VEC, L, kScoreGrad, false, false><<<grid, kBlock, 0, s>>>(a);
         } else if (normed) {
             spmm_kernel<T, VEC, L, kDw, false, true><<<grid, kBlock, 0, s>>>(a);
+        } else if (pair) {
+            spmm_kernel<T, VEC, L, kDwPair, false, false><<<grid, kBlock, 0, s>>>(a);
         } else {
             if (heads > 1) spmm_kernel<T, VEC, L, kDw, true, false><<<grid, kBlock, 0, s>>>(a);
             else spmm_kernel<T, VEC, L, kDw, false, false><<<grid, kBlock, 0, s>>>(a);
@@ -584,15 +596,16 @@ int lanes_for(int64_t h, int vec) {
 template <typename T, int VEC>
 mp_status launch_lanes(const CsrView &csr, const float *w, int64_t heads, const void *x,
                        int64_t h, float *out, const void *x_own, float *dw,
-                       const float *row_dot, const NormSpec *nm, hipStream_t s) {
+                       const float *row_dot, const NormSpec *nm, bool pair,
+                       hipStream_t s) {
     switch (lanes_for(h, VEC)) {
-        case 1: return launch<T, VEC, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
-        case 2: return launch<T, VEC, 2>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
-        case 4: return launch<T, VEC, 4>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
-        case 8: return launch<T, VEC, 8>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
-        case 16: return launch<T, VEC, 16>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
-        case 32: return launch<T, VEC, 32>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
-        default: return launch<T, VEC, 64>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
+        case 1: return launch<T, VEC, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
+        case 2: return launch<T, VEC, 2>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
+        case 4: return launch<T, VEC, 4>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
+        case 8: return launch<T, VEC, 8>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
+        case 16: return launch<T, VEC, 16>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
+        case 32: return launch<T, VEC, 32>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
+        default: return launch<T, VEC, 64>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
     }
 }
 
@@ -602,7 +615,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 mp_status spmm_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
                    mp_dtype dt, int64_t h, float *out, hipStream_t s, const NormSpec *norm) {
-    return spmm_fused_run(csr, w, heads, x, dt, h, out, nullptr, nullptr, nullptr, s, norm);
+    return spmm_fused_run(csr, w, heads, x, dt, h, out, nullptr, nullptr, nullptr, s, norm, false);
 }
 
 // 16-byte lanes need aligned rows and heads that are whole lanes wide.
@@ -620,15 +633,16 @@ bool spmm_fused_supported(mp_dtype dt, int64_t h, int64_t heads, const void *x,
 
 mp_status spmm_fused_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
                          mp_dtype dt, int64_t h, float *out, const void *x_own, float *dw,
-                         const float *row_dot, hipStream_t s, const NormSpec *nm) {
+                         const float *row_dot, hipStream_t s, const NormSpec *nm,
+                         bool pair) {
     if (dt == MP_F32) {
         if (vector_lanes_ok(4, h, heads, x, x_own, out))
-            return launch_lanes<float, 4>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
-        return launch_lanes<float, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
+            return launch_lanes<float, 4>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
+        return launch_lanes<float, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
     }
     if (vector_lanes_ok(8, h, heads, x, x_own, out))
-        return launch_lanes<uint16_t, 8>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
-    return launch_lanes<uint16_t, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, s);
+        return launch_lanes<uint16_t, 8>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
+    return launch_lanes<uint16_t, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
 }
 
 }  // namespace mp

@@ -422,7 +422,13 @@ def main():
     standalone["attention_backward"] = time_op(
         lambda: mp.mp_attention_backward(g, w, x, dy, y, out_dx=dx_att, out_dscores=dscores,
                                          out_row_dot=rdot))
-    del dx_att
+    # ... with the score gradients written over the weights (a copy of them;
+    # the work does not depend on the values, so repeated calls time the same)
+    a_buf = w.clone()
+    standalone["attention_backward_in_place"] = time_op(
+        lambda: mp.mp_attention_backward(g, a_buf, x, dy, y, out_dx=dx_att, out_dscores=a_buf,
+                                         out_row_dot=rdot))
+    del dx_att, a_buf
     log(f"standalone dx {standalone['dx']:.3f} ms, dw {standalone['dw']:.3f} ms, "
         f"equal to the fused results: {same}")
     del alpha, rstats, dscores, rdot, wn
@@ -487,6 +493,7 @@ def main():
     bytes_["fwd_norm_sym"] = bytes_["fwd"] + 4 * (n + 1)
     bytes_["fwd_norm_mean"] = bytes_["fwd"]
     bytes_["bwd_norm_sym"] = bytes_["bwd"] + 4 * (n + 1)
+    bytes_["attention_backward_in_place"] = bytes_["attention_backward"]
     bytes_["attention_backward_heads"] = (bytes_["attention_backward"] + 8 * (heads - 1) * e
                                           + 4 * (heads - 1) * n)
     ms_step = t_total / args.steps * 1e3

@@ -599,12 +599,20 @@ mp_status attention_backward_impl(const mp_graph *g, const float *alpha, int64_t
     if (e > 0 && (st = check_device(dscores, "dscores")) != MP_OK) return st;
     const Range rdx = range(dx, n * h, 4, "dx"), rds = range(dscores, e * heads, 4, "dscores");
     const Range rt = range(row_dot, n * heads, 4, "row_dot");
+    // dscores may be alpha itself (written over it in the fused walk); any
+    // other overlap is rejected.
+    const bool in_place = e > 0 && dscores == alpha;
+    const bool fused = spmm_fused_supported(dtype, h, heads, dy, x, dx);
+    if (in_place && !fused)
+        return fail(MP_ERR_ALIAS, "dscores may be alpha only when the feature rows fit the "
+                                  "fused walk (H up to 64 lanes of 16-byte slices)");
     RangeList others = graph_ranges(g);
     others.add(range(x, n * h, xs, "x"));
     others.add(range(dy, n * h, xs, "dy"));
     others.add(range(y, n * h, 4, "y"));
-    others.add(range(alpha, e * heads, 4, "alpha"));
+    if (!in_place) others.add(range(alpha, e * heads, 4, "alpha"));
     if (const char *hit = others.overlapping(rdx)) return fail(MP_ERR_ALIAS, "dx overlaps %s", hit);
+    if (in_place && overlap(rdx, rds)) return fail(MP_ERR_ALIAS, "dx overlaps alpha");
     others.add(rdx);
     if (const char *hit = others.overlapping(rds))
         return fail(MP_ERR_ALIAS, "dscores overlaps %s", hit);
@@ -614,7 +622,7 @@ mp_status attention_backward_impl(const mp_graph *g, const float *alpha, int64_t
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = attention_row_dot_run(y, dy, dtype, n, h, heads, row_dot, s)) != MP_OK) return st;
     const CsrView v = transpose_view(g);
-    if (spmm_fused_supported(dtype, h, heads, dy, x, dx))
+    if (fused)
         return spmm_fused_run(v, alpha, heads, dy, dtype, h, dx, x, e > 0 ? dscores : nullptr,
                               row_dot, s);
     // Feature rows wider than one column block: dX, then dalpha into dscores,

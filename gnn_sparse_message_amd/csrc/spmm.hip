@@ -164,6 +164,9 @@ constexpr int kPlain = 0;        // nothing: forward or input gradient
 constexpr int kDw = 1;           // edge-weight gradients (fused backward)
 constexpr int kScoreGrad = 2;    // gradients of the scores behind softmax weights
 constexpr int kDwPair = 3;       // as kDw, with w and dw interleaved ([E][2]: w, dw)
+constexpr int kScoreGradInPlace = 4;   // as kScoreGrad, the score gradients written over
+                                       // alpha (dw == w)
+constexpr bool score_mode(int m) { return m == kScoreGrad || m == kScoreGradInPlace; }
 
 // Feature rows in flight per group per step.  The single-head aggregation
 // keeps six, the fused backward (which also holds the owner row and the dot
@@ -231,7 +234,9 @@ __host__ __device__ inline Partition partition(int64_t at_hub, int64_t at_wave, 
 // reduces their dot product over its L lanes (same lane order and butterfly as
 // the COO-order edge-gradient kernel) and one lane writes dw[order[p]].  With
 // kMode == kScoreGrad the weights are softmax outputs alpha and that lane
-// writes the score gradient alpha * (dot - t[dst]) instead (t from row_dot).
+// writes the score gradient alpha * (dot - t[dst]) instead (t from row_dot);
+// kScoreGradInPlace writes it over alpha itself (each edge is read once, by the
+// group that then writes it).
 // With kHeads every lane reads the weight of its own head, `head`, per edge.
 // With kNorm every weight is scaled as it is fetched by its edge's degree
 // factor (own_deg: the owner row's length), and the fused backward's dot by the
@@ -260,6 +265,8 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
             if constexpr (kMode == kDwPair) {
                 // an ordinary load: the line stays in L2 for this edge's dw store
                 wt = a.w[(int64_t)o * 2];
+            } else if constexpr (kMode == kScoreGradInPlace && !kHeads) {
+                wt = a.w[o];   // likewise: the score gradient is stored over it
             } else if constexpr (!kHeads) {
                 wt = __builtin_nontemporal_load(&a.w[o]);
             }
@@ -310,7 +317,7 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
             // Score-gradient mode: the row terms of the gathered rows, loaded with
             // the feature rows so their latency overlaps (a random 4-byte read each).
             float tv[kUnroll];
-            if constexpr (kMode == kScoreGrad) {
+            if constexpr (score_mode(kMode)) {
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
                     const int64_t slot = kHeads ? (int64_t)cu[u] * a.heads + head : cu[u];
@@ -336,7 +343,7 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
 #pragma unroll
                     for (int off = L / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
                     const uint32_t ou = (uint32_t)__shfl((int)o, slu[u]);
-                    if constexpr (kMode == kScoreGrad) {
+                    if constexpr (score_mode(kMode)) {
                         const float wu = __shfl(wt, slu[u]);
                         if (ok[u] && (lane % L) == 0) a.dw[ou] = wu * (part - tv[u]);
                     } else if constexpr (kNorm) {
@@ -357,7 +364,7 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
                     const float part = head_sum(edge_dot<T, VEC>(xr, xv[u]), lane, sub, seg);
                     if (ok[u] && active && sub % seg == 0) {
                         const int64_t slot = (int64_t)oh[u] * a.heads + head;
-                        if constexpr (kMode == kScoreGrad)
+                        if constexpr (score_mode(kMode))
                             a.dw[slot] = wh[u] * (part - tv[u]);
                         else
                             a.dw[slot] = part;
@@ -563,7 +570,12 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
     const dim3 grid((unsigned)gx, (unsigned)gy);
     if (dw) {   // fused backward: one column block holds the whole feature row
         if (gy != 1) return fail(MP_ERR_SHAPE, "fused backward needs H <= %d", L * VEC);
-        if (row_dot) {
+        if (row_dot && dw == w) {   // score gradients written over alpha
+            if (heads > 1)
+                spmm_kernel<T, VEC, L, kScoreGradInPlace, true, false><<<grid, kBlock, 0, s>>>(a);
+            else
+                spmm_kernel<T, VEC, L, kScoreGradInPlace, false, false><<<grid, kBlock, 0, s>>>(a);
+        } else if (row_dot) {
             if (heads > 1)
                 spmm_kernel<T, VEC, L, kScoreGrad, true, false><<<grid, kBlock, 0, s>>>(a);
             else

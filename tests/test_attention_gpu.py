@@ -432,8 +432,9 @@ def test_attention_backward_rejections(mp):
         mp.mp_attention_backward(g, torch.rand((wl.e, 3), device=DEV), t["x"], t["dy"], y)
     with pytest.raises(ValueError):                  # dx aliases y
         mp.mp_attention_backward(g, alpha, t["x"], t["dy"], y, out_dx=y)
-    with pytest.raises(ValueError):                  # dscores aliases alpha
-        mp.mp_attention_backward(g, alpha, t["x"], t["dy"], y, out_dscores=alpha)
+    with pytest.raises(ValueError):                  # dscores overlaps alpha, shifted
+        buf = torch.rand((wl.e + 1, 2), device=DEV)
+        mp.mp_attention_backward(g, buf[:-1], t["x"], t["dy"], y, out_dscores=buf[1:])
     ds = torch.empty((wl.e, 2), device=DEV)
     with pytest.raises(ValueError):                  # row_dot inside dscores
         mp.mp_attention_backward(g, alpha, t["x"], t["dy"], y, out_dscores=ds,
@@ -480,3 +481,28 @@ def test_dot_product_attention_layer_chain(mp):
     check_close("dK", dk, rdk, sdk, TAU["f32"])
     rdq, sdq = oracle.forward(wl.n, wl.src, wl.dst, ds32, kk)
     check_close("dQ", dq, rdq, sdq, TAU["f32"])
+
+
+@pytest.mark.parametrize("k", [1, 4])
+def test_attention_backward_in_place(mp, k):
+    """Score gradients written over alpha equal the separate call bit for bit;
+    on rows too wide for the fused walk the in-place form is refused."""
+    wl = synth.chung_lu(seed=66, n=20000, e=400000, cap=20000.0, h=128, feat_dtype="bf16")
+    a32, ry, sy = _attention_case(wl, k, 11)
+    t = upload(wl, DEV)
+    g = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    alpha = torch.from_numpy(a32 if k > 1 else a32[:, 0].copy()).to(DEV)
+    y = torch.from_numpy(ry.astype(np.float32)).to(DEV)
+    dx, ds, rdot = mp.mp_attention_backward(g, alpha, t["x"], t["dy"], y)
+    buf = alpha.clone()
+    dx2, ds2, rdot2 = mp.mp_attention_backward(g, buf, t["x"], t["dy"], y, out_dscores=buf)
+    torch.cuda.synchronize()
+    assert ds2.data_ptr() == buf.data_ptr()
+    assert torch.equal(dx2, dx) and torch.equal(buf, ds) and torch.equal(rdot2, rdot)
+    wide = synth.random_graph(300, 3000, 600, 67)
+    tw = upload(wide, DEV)
+    gw = mp.mp_graph_build(tw["src"], tw["dst"], wide.n)
+    aw = torch.rand((wide.e, 3), device=DEV)
+    yw = torch.zeros((wide.n, 600), device=DEV)
+    with pytest.raises(ValueError):
+        mp.mp_attention_backward(gw, aw, tw["x"], tw["dy"], yw, out_dscores=aw)

@@ -71,6 +71,40 @@ __device__ inline int64_t rows_at_least_device(const uint32_t *totals, int64_t l
     return r < n ? r : n;
 }
 
+// Shortest length of the longest nonempty class (0 when every row is empty).
+inline int64_t top_class_len_host(const int64_t *cc) {
+    for (int c = MP_NUM_CLASSES - 1; c >= 1; --c)
+        if (cc[c] > 0) return (int64_t)1 << (c - 1);
+    return 0;
+}
+
+// The device record's rows per class spread over one wave: lane c holds class c
+// (lanes 0 and 33..63 hold zero), so one load per lane and a few cross-lane steps
+// answer both queries above.  Every lane of the wave must call these together.
+struct ClassLane {
+    uint32_t rows;   // rows of class `lane`
+    int lane;
+};
+__device__ inline ClassLane load_class_lane(const uint32_t *totals) {
+    ClassLane r;
+    r.lane = (int)(threadIdx.x & 63u);
+    r.rows = r.lane >= 1 && r.lane < MP_NUM_CLASSES ? totals[32 - r.lane] : 0u;
+    return r;
+}
+__device__ inline int64_t rows_at_least(const ClassLane &cl, int64_t len, int64_t n) {
+    uint32_t v = cl.lane >= 1 && ((int64_t)1 << (cl.lane - 1)) >= len ? cl.rows : 0u;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += (uint32_t)__shfl_xor((int)v, off);
+    v = (uint32_t)__builtin_amdgcn_readfirstlane((int)v);   // wave-uniform: scalar registers
+    return (int64_t)v < n ? (int64_t)v : n;
+}
+__device__ inline int64_t top_class_len(const ClassLane &cl) {
+    const uint64_t m = __ballot(cl.rows > 0u);
+    if (m == 0) return 0;
+    const int c = __builtin_amdgcn_readfirstlane(63 - __clzll((long long)m));
+    return (int64_t)1 << (c - 1);
+}
+
 // ---------------------------------------------------------------- SpMM
 // One aggregation over a CSR form (rows = owners).  `x` holds [n, h] features
 // of dtype `dt`; `out` receives [n, h] float32.

@@ -195,13 +195,62 @@ struct SpmmArgs {
     int32_t n_hub, n_wave, n_group;   // rows of each owner kind, consecutive in the plan
     int32_t blk_hub, blk_wave, blk_group;   // blocks given to each kind (wave and group
                                             // owners stride over their rows)
+    int32_t hub_apart;                // hub rows go to spmm_hub_kernel (no hub blocks here)
     const uint32_t *dev_totals;       // asynchronously built graph: the plan's rows per class
-                                      // on the device; the six fields above are then derived
-    int32_t hub_min, wave_min;        // in the kernel from these owner-size thresholds
+                                      // on the device; the seven fields above are then
+                                      // derived in the kernel, by owner_rule
+    int32_t wave_min;                 // rows this long or longer (below hub) get a wave
+    int32_t force_hub, force_apart;   // owner_rule overrides (> 0 / >= 0), else -1
     NormSpec norm;                    // normalising kernels only: fetch-time weight scaling
 };
 
 constexpr int64_t kMaxKindBlocks = 1 << 22;   // wave and group owners stride beyond this
+
+// Hub rows: workgroups of four waves in the main launch, or of 16 waves in a
+// launch of their own (spmm_hub_kernel).
+constexpr int kHubWaves = 16;
+constexpr int kHubBlock = kHubWaves * kWave;
+constexpr int64_t kWaveSlots = 256 * 4 * 4;   // CUs x SIMDs x four waves
+// Hub blocks of an asynchronously built graph's launches (counts unknown to the
+// host: the grid is a bound, so it is kept small and the blocks stride).
+constexpr int64_t kAsyncHubBlocks = 1024, kAsyncHubBlocks16 = 256;
+constexpr int kLargeHubLen = 4096;
+
+struct OwnerRule {
+    int32_t hub_min;   // rows this long or longer get a workgroup
+    int32_t apart;     // ... of 16 waves in their own launch, else of four in the main one
+};
+
+// Owner sizes from the edge count, the lane-group width (G edges per wave step)
+// and the longest nonempty length class only, all of which the host knows for a
+// synchronously built graph and the kernels read for an asynchronously built
+// one; the owners, and with them the summation order, are the same either way.
+// The chip's wave slots share the edges: a row much longer than one slot's share
+// finishes after the rest of the launch.  When the longest class starts beyond
+// eight shares (a few hub rows hold a large part of the edges, as in RMAT) even
+// four waves leave such a row as the tail, so rows of 128 edges and more (at
+// least two steps of 16 waves) get 16 waves each.  Otherwise rows of about one
+// share (a power of two, at most 4096 and at least two steps of four waves) get
+// the main launch's four-wave workgroups, so no single wave holds more than
+// about a share.
+__host__ __device__ inline OwnerRule owner_rule(int64_t top_len, int64_t e, int G,
+                                                int32_t force_hub, int32_t force_apart) {
+    const int64_t share = e / kWaveSlots;
+    OwnerRule r;
+    r.apart = force_apart >= 0 ? force_apart : (top_len > 8 * share ? 1 : 0);
+    int64_t len;
+    if (r.apart) {
+        len = (int64_t)2 * kHubWaves * G;
+        if (len < 128) len = 128;
+    } else {
+        len = 1;
+        while (len * 2 <= share && len < kLargeHubLen) len *= 2;
+        const int64_t lo = (int64_t)8 * G > 128 ? (int64_t)8 * G : 128;
+        if (len < lo) len = lo;
+    }
+    r.hub_min = force_hub > 0 ? force_hub : (int32_t)len;
+    return r;
+}
 
 // Owner partition of a plan: rows of each kind and blocks given to each.
 struct Partition {
@@ -209,7 +258,8 @@ struct Partition {
 };
 
 template <int L>
-__host__ __device__ inline Partition partition(int64_t at_hub, int64_t at_wave, int64_t n) {
+__host__ __device__ inline Partition partition(int64_t at_hub, int64_t at_wave, int64_t n,
+                                               int64_t hub_cap = kMaxKindBlocks) {
     if (at_wave < at_hub) at_wave = at_hub;
     Partition p;
     p.n_hub = (int32_t)at_hub;
@@ -218,7 +268,7 @@ __host__ __device__ inline Partition partition(int64_t at_hub, int64_t at_wave, 
     const int64_t rows_per_blk = kBlock / L;
     const int64_t bw = (p.n_wave + kWavesPerBlock - 1) / kWavesPerBlock;
     const int64_t bg = (p.n_group + rows_per_blk - 1) / rows_per_blk;
-    p.blk_hub = p.n_hub;
+    p.blk_hub = (int32_t)(p.n_hub < hub_cap ? p.n_hub : hub_cap);   // hub owners stride too
     p.blk_wave = (int32_t)(bw < kMaxKindBlocks ? bw : kMaxKindBlocks);
     p.blk_group = (int32_t)(bg < kMaxKindBlocks ? bg : kMaxKindBlocks);
     return p;
@@ -386,6 +436,53 @@ __device__ __forceinline__ void own_row(const SpmmArgs &a, int row, int64_t hoff
     }
 }
 
+// Hub rows first .. n_hub - 1, every stride-th: each row by the whole workgroup
+// of kWaves waves, the waves' partial sums added in wave order.
+template <typename T, int VEC, int L, int kMode, bool kHeads, bool kNorm, int kWaves>
+__device__ __forceinline__ void hub_rows(const SpmmArgs &a, int32_t first, int32_t n_hub,
+                                         int32_t stride, float (*s_red)[L * VEC]) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int sub = lane % L;
+    const int64_t hoff = (int64_t)blockIdx.y * (L * VEC) + (int64_t)sub * VEC;
+    const bool active = hoff < a.h;
+    const int head = kHeads && active ? (int)(hoff / a.head_w) : 0;
+    for (int32_t idx = first; idx < n_hub; idx += stride) {
+        const int row = a.plan[idx];
+        if ((uint32_t)row >= (uint64_t)a.n) continue;   // the plan is a permutation of [0, n)
+        const int64_t beg = a.rowptr[row], end = a.rowptr[row + 1];
+        float acc[VEC], xr[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+        own_row<T, VEC, kMode>(a, row, hoff, active, xr);
+        accumulate<T, VEC, L, kWave, kMode, kHeads, kNorm>(a, beg + (int64_t)wv * kWave, end,
+                                                               (int64_t)kWaves * kWave, lane,
+                                                               hoff, head, active, xr, acc,
+                                                               (double)(end - beg));
+#pragma unroll
+        for (int off = L; off < kWave; off <<= 1)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) acc[v] += __shfl_xor(acc[v], off);
+        if (lane < L) {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) s_red[wv][sub * VEC + v] = acc[v];
+        }
+        __syncthreads();
+        if (wv == 0 && lane < L && active) {
+            float r[VEC];
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                float t = s_red[0][sub * VEC + v];
+#pragma unroll
+                for (int w2 = 1; w2 < kWaves; ++w2) t += s_red[w2][sub * VEC + v];
+                r[v] = t;
+            }
+            store_row<VEC>(a.y + (int64_t)row * a.h + hoff, r);
+        }
+        __syncthreads();   // s_red is written again for the next row
+    }
+}
+
 // Occupancy floors: the single-head fused backward is held to five waves per
 // SIMD (8.20 ms against 8.80 ms at four before the rows were held packed; it
 // now fits five without spilling), the single-head aggregation to four.  The
@@ -408,41 +505,22 @@ void spmm_kernel(SpmmArgs a) {
     for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
 
     Partition pt{a.n_hub, a.n_wave, a.n_group, a.blk_hub, a.blk_wave, a.blk_group};
-    if (a.dev_totals)   // counts on the device only: the grid is an upper bound
-        pt = partition<L>(rows_at_least_device(a.dev_totals, a.hub_min, a.n),
-                          rows_at_least_device(a.dev_totals, a.wave_min, a.n), a.n);
+    int32_t apart = a.hub_apart;
+    if (a.dev_totals) {   // counts on the device only: the grid is an upper bound
+        const ClassLane cr = load_class_lane(a.dev_totals);
+        const OwnerRule r = owner_rule(top_class_len(cr), a.e, kWave / L, a.force_hub,
+                                       a.force_apart);
+        pt = partition<L>(rows_at_least(cr, r.hub_min, a.n), rows_at_least(cr, a.wave_min, a.n),
+                          a.n, kAsyncHubBlocks);
+        apart = r.apart;
+    }
+    if (apart) pt.blk_hub = 0;
     int64_t b = blockIdx.x;
     if (b < pt.blk_hub) {
-        // ---- hub row: the whole workgroup
+        // ---- hub rows: the whole workgroup
         __shared__ float s_red[kWavesPerBlock][L * VEC];
-        const int row = a.plan[b];
-        if ((uint32_t)row >= (uint64_t)a.n) return;   // the plan is a permutation of [0, n)
-        const int64_t beg = a.rowptr[row], end = a.rowptr[row + 1];
-        own_row<T, VEC, kMode>(a, row, hoff, active, xr);
-        accumulate<T, VEC, L, kWave, kMode, kHeads, kNorm>(a, beg + (int64_t)wv * kWave, end,
-                                                               (int64_t)kBlock, lane, hoff, head,
-                                                               active, xr, acc,
-                                                               (double)(end - beg));
-#pragma unroll
-        for (int off = L; off < kWave; off <<= 1)
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) acc[v] += __shfl_xor(acc[v], off);
-        if (lane < L) {
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) s_red[wv][sub * VEC + v] = acc[v];
-        }
-        __syncthreads();
-        if (wv == 0 && lane < L && active) {
-            float r[VEC];
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) {
-                float s = s_red[0][sub * VEC + v];
-#pragma unroll
-                for (int w2 = 1; w2 < kWavesPerBlock; ++w2) s += s_red[w2][sub * VEC + v];
-                r[v] = s;
-            }
-            store_row<VEC>(a.y + (int64_t)row * a.h + hoff, r);
-        }
+        hub_rows<T, VEC, L, kMode, kHeads, kNorm, kWavesPerBlock>(a, (int32_t)b, pt.n_hub,
+                                                                  pt.blk_hub, s_red);
         return;
     }
     b -= pt.blk_hub;
@@ -486,23 +564,50 @@ void spmm_kernel(SpmmArgs a) {
     }
 }
 
+// Hub rows in a launch of their own, 16 waves per row: a workgroup-owned row is
+// bound by the feature rows its waves keep in flight, so four times the waves
+// of the main launch take a long row four times as fast when few rows are left
+// to overlap it.  Same walk and fixed-order reduction as the hub owners above,
+// over 16 waves.
+
+template <typename T, int VEC, int L, int kMode, bool kHeads, bool kNorm>
+__global__ __launch_bounds__(kHubBlock) void spmm_hub_kernel(SpmmArgs a) {
+    int32_t n_hub = a.n_hub;
+    if (a.dev_totals) {
+        const ClassLane cr = load_class_lane(a.dev_totals);
+        const OwnerRule r = owner_rule(top_class_len(cr), a.e, kWave / L, a.force_hub,
+                                       a.force_apart);
+        n_hub = r.apart ? (int32_t)rows_at_least(cr, r.hub_min, a.n) : 0;
+    }
+    __shared__ float s_red[kHubWaves][L * VEC];
+    hub_rows<T, VEC, L, kMode, kHeads, kNorm, kHubWaves>(a, (int32_t)blockIdx.x, n_hub,
+                                                         (int32_t)gridDim.x, s_red);
+}
+
 // ------------------------------------------------------------------ dispatch
-struct Thresholds {
-    int hub_min_len;     // rows this long or longer get a workgroup
-    int wave_min_len;    // rows this long or longer (below hub) get a wave
+// Overrides of the owner sizes for tuning and tests: MP_HUB_MIN_LEN,
+// MP_HUB_APART (0 or 1) and MP_WAVE_MIN_LEN.
+struct Overrides {
+    int32_t hub_min, apart, wave_min;
 };
 
-// Owner-size thresholds.  MP_HUB_MIN_LEN / MP_WAVE_MIN_LEN override them (tuning).
-Thresholds thresholds_for(int L) {
-    Thresholds t;
+Overrides overrides_for(int L) {
+    Overrides o;
     const int G = kWave / L;
-    t.hub_min_len = 4096;
-    t.wave_min_len = G > 1 ? 4 * G : (1 << 30);
-    if (const char *s = getenv("MP_HUB_MIN_LEN")) t.hub_min_len = atoi(s);
-    if (const char *s = getenv("MP_WAVE_MIN_LEN")) t.wave_min_len = atoi(s);
-    if (t.hub_min_len < 1) t.hub_min_len = 1;
-    if (t.wave_min_len < 1) t.wave_min_len = 1;
-    return t;
+    o.hub_min = -1;
+    o.apart = -1;
+    o.wave_min = G > 1 ? 4 * G : (1 << 30);
+    if (const char *s = getenv("MP_HUB_MIN_LEN")) o.hub_min = atoi(s) < 1 ? 1 : atoi(s);
+    if (const char *s = getenv("MP_HUB_APART")) o.apart = atoi(s) != 0 ? 1 : 0;
+    if (const char *s = getenv("MP_WAVE_MIN_LEN")) o.wave_min = atoi(s) < 1 ? 1 : atoi(s);
+    return o;
+}
+
+// Hub rows first, in their own launch, then every other row.
+template <typename T, int VEC, int L, int kMode, bool kHeads, bool kNorm>
+void go(const SpmmArgs &a, const dim3 &hub, const dim3 &rest, hipStream_t s) {
+    if (hub.x) spmm_hub_kernel<T, VEC, L, kMode, kHeads, kNorm><<<hub, kHubBlock, 0, s>>>(a);
+    if (rest.x) spmm_kernel<T, VEC, L, kMode, kHeads, kNorm><<<rest, kBlock, 0, s>>>(a);
 }
 
 template <typename T, int VEC, int L>
@@ -514,7 +619,8 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
         return fail(MP_ERR_SHAPE, "fetch-time normalisation takes one head and no row dots");
     if (pair && (heads != 1 || row_dot || normed || !dw))
         return fail(MP_ERR_SHAPE, "the interleaved weight layout is for the one-head fused backward");
-    const Thresholds th = thresholds_for(L);
+    const Overrides ov = overrides_for(L);
+    const int G = kWave / L;
     SpmmArgs a;
     a.rowptr = csr.rowptr;
     a.col = csr.col;
@@ -532,11 +638,14 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
     a.n = csr.n;
     a.e = csr.e;
     a.dev_totals = csr.dev_totals;
-    a.hub_min = th.hub_min_len;
-    a.wave_min = th.wave_min_len;
+    a.wave_min = ov.wave_min;
+    a.force_hub = ov.hub_min;
+    a.force_apart = ov.apart;
     a.norm = normed ? *norm : NormSpec{0, false, nullptr};
     // A launch holds at most 2^32 - 1 work-items; wave and group owners stride.
     Partition pt;
+    a.hub_apart = 0;
+    int64_t hub_blocks = 0;   // blocks of the 16-wave launch
     if (csr.dev_totals) {
         // Counts live on the device: launch for the largest partition N and E
         // allow (a row of length >= len needs len edges of its own).
@@ -544,16 +653,30 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
             const int64_t r = csr.e / (len > 0 ? len : 1);
             return r < csr.n ? r : csr.n;
         };
+        // The rule is taken in the kernels; bound each launch by the shortest
+        // hub length either of its forms may choose.
+        const OwnerRule four = owner_rule(0, csr.e, G, ov.hub_min, 0);
+        const OwnerRule sixteen = owner_rule(0, csr.e, G, ov.hub_min, 1);
         pt = partition<L>(0, 0, 0);
-        const Partition ph = partition<L>(most(th.hub_min_len), most(th.hub_min_len), 0);
-        const Partition pw = partition<L>(0, most(th.wave_min_len), 0);
+        const Partition pw = partition<L>(0, most(ov.wave_min), 0);
         const Partition pg = partition<L>(0, 0, csr.n);
-        pt.blk_hub = ph.blk_hub;
+        pt.blk_hub =
+            ov.apart == 1 ? 0 : partition<L>(most(four.hub_min), 0, 0, kAsyncHubBlocks).blk_hub;
         pt.blk_wave = pw.blk_wave;
         pt.blk_group = pg.blk_group;
+        hub_blocks = ov.apart == 0
+                         ? 0
+                         : partition<L>(most(sixteen.hub_min), 0, 0, kAsyncHubBlocks16).blk_hub;
     } else {
-        pt = partition<L>(rows_at_least_host(csr.class_count, th.hub_min_len),
-                          rows_at_least_host(csr.class_count, th.wave_min_len), csr.n);
+        const OwnerRule r = owner_rule(top_class_len_host(csr.class_count), csr.e, G,
+                                       ov.hub_min, ov.apart);
+        pt = partition<L>(rows_at_least_host(csr.class_count, r.hub_min),
+                          rows_at_least_host(csr.class_count, ov.wave_min), csr.n);
+        a.hub_apart = r.apart;
+        if (r.apart) {
+            hub_blocks = pt.blk_hub;
+            pt.blk_hub = 0;   // the main launch skips the hub rows
+        }
     }
     a.n_hub = pt.n_hub;
     a.n_wave = pt.n_wave;
@@ -561,38 +684,35 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
     a.blk_hub = pt.blk_hub;
     a.blk_wave = pt.blk_wave;
     a.blk_group = pt.blk_group;
+    const int64_t hx = hub_blocks;
     const int64_t gx = (int64_t)a.blk_hub + a.blk_wave + a.blk_group;
     const int64_t gy = (h + (int64_t)L * VEC - 1) / ((int64_t)L * VEC);
-    if (gx <= 0) return MP_OK;
-    if (gx > (int64_t)3 << 22 || gy > 65535)
+    if (gx + hx <= 0) return MP_OK;
+    if (gx > (int64_t)3 << 22 || hx > (int64_t)3 << 22 || gy > 65535)
         return fail(MP_ERR_SHAPE, "launch grid too large (%lld x %lld)", (long long)gx,
                     (long long)gy);
-    const dim3 grid((unsigned)gx, (unsigned)gy);
+    const dim3 hub((unsigned)hx, (unsigned)gy), rest((unsigned)gx, (unsigned)gy);
     if (dw) {   // fused backward: one column block holds the whole feature row
         if (gy != 1) return fail(MP_ERR_SHAPE, "fused backward needs H <= %d", L * VEC);
         if (row_dot && dw == w) {   // score gradients written over alpha
-            if (heads > 1)
-                spmm_kernel<T, VEC, L, kScoreGradInPlace, true, false><<<grid, kBlock, 0, s>>>(a);
-            else
-                spmm_kernel<T, VEC, L, kScoreGradInPlace, false, false><<<grid, kBlock, 0, s>>>(a);
+            if (heads > 1) go<T, VEC, L, kScoreGradInPlace, true, false>(a, hub, rest, s);
+            else go<T, VEC, L, kScoreGradInPlace, false, false>(a, hub, rest, s);
         } else if (row_dot) {
-            if (heads > 1)
-                spmm_kernel<T, VEC, L, kScoreGrad, true, false><<<grid, kBlock, 0, s>>>(a);
-            else
-                spmm_kernel<T, VEC, L, kScoreGrad, false, false><<<grid, kBlock, 0, s>>>(a);
+            if (heads > 1) go<T, VEC, L, kScoreGrad, true, false>(a, hub, rest, s);
+            else go<T, VEC, L, kScoreGrad, false, false>(a, hub, rest, s);
         } else if (normed) {
-            spmm_kernel<T, VEC, L, kDw, false, true><<<grid, kBlock, 0, s>>>(a);
+            go<T, VEC, L, kDw, false, true>(a, hub, rest, s);
         } else if (pair) {
-            spmm_kernel<T, VEC, L, kDwPair, false, false><<<grid, kBlock, 0, s>>>(a);
+            go<T, VEC, L, kDwPair, false, false>(a, hub, rest, s);
         } else {
-            if (heads > 1) spmm_kernel<T, VEC, L, kDw, true, false><<<grid, kBlock, 0, s>>>(a);
-            else spmm_kernel<T, VEC, L, kDw, false, false><<<grid, kBlock, 0, s>>>(a);
+            if (heads > 1) go<T, VEC, L, kDw, true, false>(a, hub, rest, s);
+            else go<T, VEC, L, kDw, false, false>(a, hub, rest, s);
         }
     } else if (normed) {
-        spmm_kernel<T, VEC, L, kPlain, false, true><<<grid, kBlock, 0, s>>>(a);
+        go<T, VEC, L, kPlain, false, true>(a, hub, rest, s);
     } else {
-        if (heads > 1) spmm_kernel<T, VEC, L, kPlain, true, false><<<grid, kBlock, 0, s>>>(a);
-        else spmm_kernel<T, VEC, L, kPlain, false, false><<<grid, kBlock, 0, s>>>(a);
+        if (heads > 1) go<T, VEC, L, kPlain, true, false>(a, hub, rest, s);
+        else go<T, VEC, L, kPlain, false, false>(a, hub, rest, s);
     }
     MP_HIP_CHECK(hipGetLastError(), "spmm launch");
     return MP_OK;

@@ -57,24 +57,33 @@ def _power_law_small(seed, n=20000, e=400000, h=32, feat="f32"):
     return wl
 
 
+@pytest.mark.parametrize("apart", ["0", "1"])
 @pytest.mark.parametrize("feat,h", [("f32", 16), ("f32", 64), ("bf16", 128), ("f32", 256)])
-def test_power_law_all_owner_kinds(mp, feat, h):
+def test_power_law_all_owner_kinds(mp, feat, h, apart, monkeypatch):
+    """Rows of 4096 edges and more as four-wave workgroups of the main launch
+    (the large-graph form) or as 16-wave workgroups of their own launch."""
     wl = _power_law_small(40 + h, h=h, feat=feat)
     deg = np.bincount(wl.dst, minlength=wl.n)
     assert deg.max() >= 4096 and (deg == 0).any()
+    monkeypatch.setenv("MP_HUB_MIN_LEN", "4096")
+    monkeypatch.setenv("MP_HUB_APART", apart)
     g, t, y, dx, dw = run_path(mp, wl, DEV)
     check_structure(g, wl)
     check_floats(wl, y, dx, dw)
 
 
-@pytest.mark.parametrize("hub,wave", [("1", "1"), ("1000000000", "1000000000"), ("64", "2"),
-                                      ("2", "1000000000")])
-def test_owner_thresholds_do_not_change_results(mp, hub, wave, monkeypatch):
-    """Every row handled by workgroups, by single lane groups, or mixed: same
-    values to tolerance (the split only changes the summation order)."""
+@pytest.mark.parametrize("hub,wave,apart", [("1", "1", "0"), ("1", "1", "1"),
+                                            ("1000000000", "1000000000", "0"),
+                                            ("64", "2", "0"), ("64", "2", "1"),
+                                            ("2", "1000000000", "1")])
+def test_owner_thresholds_do_not_change_results(mp, hub, wave, apart, monkeypatch):
+    """Every row handled by workgroups (four waves in the main launch or 16 in
+    their own), by single lane groups, or mixed: same values to tolerance (the
+    split only changes the summation order)."""
     wl = _power_law_small(7, n=3000, e=60000, h=40)
     monkeypatch.setenv("MP_HUB_MIN_LEN", hub)
     monkeypatch.setenv("MP_WAVE_MIN_LEN", wave)
+    monkeypatch.setenv("MP_HUB_APART", apart)
     g, t, y, dx, dw = run_path(mp, wl, DEV)
     check_floats(wl, y, dx, dw)
 

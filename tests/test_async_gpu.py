@@ -51,9 +51,14 @@ def _workloads():
     yield synth.chung_lu(seed=33, n=20000, e=400000, cap=20000.0, h=32, feat_dtype="f32")
     yield synth.chung_lu(seed=34, n=8000, e=160000, cap=8000.0, h=128, feat_dtype="bf16")
     yield synth.minibatches(1, h=64)[0]
+    # about 3,000 rows of ~200 edges: four-wave hub owners in the main launch,
+    # more of them than its hub blocks, which then stride
+    yield synth.random_graph(3000, 600000, 16, 5)
+    # RMAT-16: 16-wave hub owners in their own launch, more rows than its blocks
+    yield synth.rmat16()
 
 
-@pytest.mark.parametrize("idx", range(6))
+@pytest.mark.parametrize("idx", range(8))
 def test_async_build_equals_sync(mp, idx):
     wl = list(_workloads())[idx]
     t = upload(wl, DEV)

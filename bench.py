@@ -26,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -54,12 +55,23 @@ def algorithmic_bytes(n, e, h, s_feat, s_idx):
             "dw": e * (2 * h * s_feat + 12)}
 
 
+def _code_only(text):
+    """Source text without comments and with runs of white space made one
+    blank, so that edits of comments alone leave a kernel's hash unchanged
+    (none of the hashed sources has a string literal holding a comment
+    marker)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return re.sub(r"\s+", " ", text).strip()
+
+
 def kernel_source_hash(kernel):
-    """Hash of the source files that define `kernel` (a key of KERNEL_SOURCES)."""
+    """Hash of the code (comments left out) of the source files that define
+    `kernel` (a key of KERNEL_SOURCES)."""
     hsh = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            hsh.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            hsh.update(_code_only(f.read()).encode())
     return hsh.hexdigest()[:16]
 
 

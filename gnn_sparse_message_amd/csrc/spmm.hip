@@ -10,13 +10,16 @@
 // Mapping on gfx950.  A feature row is split over a "group" of L lanes, each
 // lane holding VEC contiguous features (16-byte loads: 4 fp32 or 8 bf16).  Rows
 // are visited through the degree plan (rows sorted by length class, longest
-// first) and handed to owners of three sizes within ONE launch, so long rows
+// first) and handed to owners of three sizes within one launch, so long rows
 // start first and their tail overlaps the short ones:
 //   hub  rows -> a whole 256-thread workgroup (4 waves split the edges, then a
 //                fixed-order LDS reduction);
 //   long rows -> one 64-lane wave (64/L groups split the edges, butterfly
 //                reduction across groups);
 //   short rows (and empty rows, written as zeros) -> one group of L lanes.
+// When a few rows hold much of a graph (owner_rule below) the hub rows instead
+// get 1024-thread workgroups, 16 waves each, in a launch just before the main
+// one (spmm_hub_kernel).
 // For each run of edges the team loads col[p] and order[p] once, coalesced, one
 // edge per lane, and gathers w[order[p]]; it broadcasts them with lane permutes
 // while every group gathers U feature rows at a time (several 16-byte loads in

@@ -199,8 +199,10 @@ struct SpmmArgs {
     int32_t blk_hub, blk_wave, blk_group;   // blocks given to each kind (wave and group
                                             // owners stride over their rows)
     int32_t hub_apart;                // hub rows go to spmm_hub_kernel (no hub blocks here)
+    int32_t n_full;                   // rows with an edge: plan positions from here on are
+                                      // empty rows (class 0 comes last)
     const uint32_t *dev_totals;       // asynchronously built graph: the plan's rows per class
-                                      // on the device; the seven fields above are then
+                                      // on the device; the eight fields above are then
                                       // derived in the kernel, by owner_rule
     int32_t wave_min;                 // rows this long or longer (below hub) get a wave
     int32_t force_hub, force_apart;   // owner_rule overrides (> 0 / >= 0), else -1
@@ -231,8 +233,8 @@ struct OwnerRule {
 // The chip's wave slots share the edges: a row much longer than one slot's share
 // finishes after the rest of the launch.  When the longest class starts beyond
 // eight shares (a few hub rows hold a large part of the edges, as in RMAT) even
-// four waves leave such a row as the tail, so rows of 128 edges and more (at
-// least two steps of 16 waves) get 16 waves each.  Otherwise rows of about one
+// four waves leave such a row as the tail, so rows of 128 edges or two steps of
+// 16 waves, whichever is longer, get 16 waves each.  Otherwise rows of about one
 // share (a power of two, at most 4096 and at least two steps of four waves) get
 // the main launch's four-wave workgroups, so no single wave holds more than
 // about a share.
@@ -509,6 +511,7 @@ void spmm_kernel(SpmmArgs a) {
 
     Partition pt{a.n_hub, a.n_wave, a.n_group, a.blk_hub, a.blk_wave, a.blk_group};
     int32_t apart = a.hub_apart;
+    int32_t n_full = a.n_full;
     if (a.dev_totals) {   // counts on the device only: the grid is an upper bound
         const ClassLane cr = load_class_lane(a.dev_totals);
         const OwnerRule r = owner_rule(top_class_len(cr), a.e, kWave / L, a.force_hub,
@@ -516,6 +519,7 @@ void spmm_kernel(SpmmArgs a) {
         pt = partition<L>(rows_at_least(cr, r.hub_min, a.n), rows_at_least(cr, a.wave_min, a.n),
                           a.n, kAsyncHubBlocks);
         apart = r.apart;
+        n_full = (int32_t)rows_at_least(cr, 1, a.n);
     }
     if (apart) pt.blk_hub = 0;
     int64_t b = blockIdx.x;
@@ -554,9 +558,14 @@ void spmm_kernel(SpmmArgs a) {
     constexpr int64_t kRowsPerBlock = kBlock / L;
     for (int64_t idx = b * kRowsPerBlock + threadIdx.x / L; idx < pt.n_group;
          idx += (int64_t)pt.blk_group * kRowsPerBlock) {
-        const int row = a.plan[pt.n_hub + pt.n_wave + idx];
+        const int32_t at = pt.n_hub + pt.n_wave + (int32_t)idx;
+        const int row = a.plan[at];
         if ((uint32_t)row >= (uint64_t)a.n) continue;
-        const int64_t beg = a.rowptr[row], end = a.rowptr[row + 1];
+        int64_t beg = 0, end = 0;   // an empty row (at >= n_full) needs no extent read
+        if (at < n_full) {
+            beg = a.rowptr[row];
+            end = a.rowptr[row + 1];
+        }
 #pragma unroll
         for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
         own_row<T, VEC, kMode>(a, row, hoff, active && end > beg, xr);
@@ -681,6 +690,7 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
             pt.blk_hub = 0;   // the main launch skips the hub rows
         }
     }
+    a.n_full = csr.dev_totals ? 0 : (int32_t)rows_at_least_host(csr.class_count, 1);
     a.n_hub = pt.n_hub;
     a.n_wave = pt.n_wave;
     a.n_group = pt.n_group;

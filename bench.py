@@ -408,6 +408,15 @@ def main():
         lambda: mp.mp_edge_softmax_backward(g, alpha, dw, dscores, rdot))
     standalone["edge_normalize_sym"] = time_op(
         lambda: mp.mp_edge_normalize(g, mp.MP_NORM_SYM, w, out=wn))
+    # The attention forward with alpha formed at the fetch, against the softmax
+    # then the aggregation on its alpha (bitwise the same Y).
+    y_s = torch.empty_like(y)
+    standalone["attention_forward"] = time_op(
+        lambda: mp.mp_spmm_fwd_softmax(g, w, x, out=y_s, out_row_stats=rstats))
+    attn_fwd_two_calls = time_op(lambda: (mp.mp_edge_softmax(g, w, alpha, rstats),
+                                          mp.mp_spmm_fwd(g, alpha, x, out=y)))
+    torch.cuda.synchronize()
+    attn_fwd_equal = bool(torch.equal(y_s, y))
     # Degree normalisation applied at the weight fetch (GCN's symmetric and
     # SAGE's mean), against normalising the weights first (edge_normalize_sym).
     standalone["fwd_norm_sym"] = time_op(
@@ -489,6 +498,10 @@ def main():
     bytes_["edge_softmax_backward"] = 28 * e + 16 * n
     # symmetric normalisation: in, out, src, dst per edge; both row pointers once.
     bytes_["edge_normalize_sym"] = 16 * e + 8 * (n + 1)
+    # attention forward: the aggregation's bytes (the score in the weight's
+    # place) plus the softmax's row pass (order + score per edge, two stats per
+    # row written, then read once per row)
+    bytes_["attention_forward"] = bytes_["fwd"] + 8 * e + 16 * n
     # multi-head: the edge's weight (or dw) term grows from 4 to 4K bytes.
     bytes_["fwd_heads"] = bytes_["fwd"] + 4 * (heads - 1) * e
     bytes_["bwd_heads"] = bytes_["dx"] + bytes_["dw"] + 8 * (heads - 1) * e
@@ -528,6 +541,10 @@ def main():
     per_op_standalone["heads"] = heads
     per_op_standalone["heads_fused_equal_to_separate"] = same_heads
     per_op_standalone["pair_equal_to_fused"] = same_pair
+    # what the fetch-time softmax replaces: the softmax (writing alpha), then the
+    # aggregation on alpha; the two give the same Y bit for bit
+    per_op_standalone["attention_forward_two_calls_ms"] = round(attn_fwd_two_calls, 4)
+    per_op_standalone["attention_forward_equal_to_two_calls"] = attn_fwd_equal
     # what the fetch-time normalisation replaces: a normalisation pass, then the call
     per_op_standalone["fwd_norm_two_calls_ms"] = round(
         standalone["edge_normalize_sym"] + statistics.median(times["fwd"]), 4)

@@ -32,7 +32,7 @@ __all__ = [
     "mp_spmm_dx", "mp_edge_grad_dw", "mp_spmm_dx_edge_grad", "mp_spmm_fwd_heads",
     "mp_spmm_dx_heads", "mp_edge_grad_dw_heads", "mp_spmm_dx_edge_grad_heads", "mp_edge_softmax",
     "mp_edge_softmax_backward", "mp_edge_softmax_heads", "mp_edge_softmax_backward_heads",
-    "mp_attention_backward", "mp_spmm_fwd_norm", "mp_spmm_dx_norm", "mp_spmm_dx_edge_grad_norm",
+    "mp_attention_backward", "mp_spmm_fwd_softmax", "mp_spmm_fwd_norm", "mp_spmm_dx_norm", "mp_spmm_dx_edge_grad_norm",
     "mp_spmm_dx_edge_grad_pair",
     "mp_edge_normalize", "MP_NORM_MEAN", "MP_NORM_SYM",
     "mp_status_string", "mp_version", "library_path",
@@ -123,6 +123,7 @@ def _load():
         "mp_edge_softmax_backward_heads": (i32, [gp, vp, vp, i64, vp, vp, vp]),
         "mp_attention_backward": (i32, [gp, vp, i64, vp, vp, vp, i32, i64, vp, vp, vp, vp]),
         "mp_spmm_fwd_norm": (i32, [gp, i32, vp, vp, i32, i64, vp, vp]),
+        "mp_spmm_fwd_softmax": (i32, [gp, vp, vp, i32, i64, vp, vp, vp]),
         "mp_spmm_dx_norm": (i32, [gp, i32, vp, vp, i32, i64, vp, vp]),
         "mp_spmm_dx_edge_grad_norm": (i32, [gp, i32, vp, vp, vp, i32, i64, vp, vp, vp]),
         "mp_spmm_dx_edge_grad_pair": (i32, [gp, vp, vp, vp, i32, i64, vp, vp]),
@@ -526,6 +527,20 @@ def mp_edge_softmax(g: Graph, scores, out_alpha=None, out_row_stats=None):
                                 _ptr(alpha) if g.num_edges else None, _ptr(stats),
                                 _stream(scores)), "mp_edge_softmax")
     return alpha, stats
+
+
+def mp_spmm_fwd_softmax(g: Graph, scores, x, out=None, out_row_stats=None):
+    """Y = A_alpha X with alpha = softmax(scores) over each destination, alpha
+    formed at the fetch and never written: returns (Y [N, H], row_stats [N, 2]),
+    bitwise mp_edge_softmax followed by mp_spmm_fwd on its alpha."""
+    _edge_f32("scores", scores, g)
+    h = _features("x", x, g)
+    y = _out(out, (g.num_nodes, h), x)
+    stats = _out(out_row_stats, (g.num_nodes, 2), x)
+    _check(_lib.mp_spmm_fwd_softmax(ctypes.byref(g._desc),
+                                    _ptr(scores) if g.num_edges else None, _ptr(x), _code(x), h,
+                                    _ptr(y), _ptr(stats), _stream(x)), "mp_spmm_fwd_softmax")
+    return y, stats
 
 
 def mp_edge_softmax_backward(g: Graph, alpha, dalpha, out_dscores=None, out_row_dot=None):

@@ -531,6 +531,29 @@ mp_status mp_spmm_fwd_norm(const mp_graph *g, int32_t mode, const float *w, cons
                     &nm);
 }
 
+mp_status mp_spmm_fwd_softmax(const mp_graph *g, const float *scores, const void *x,
+                              mp_dtype x_dtype, int64_t h, float *y, float *row_stats,
+                              void *stream) {
+    const char *what = "mp_spmm_fwd_softmax";
+    mp_status st = check_spmm(g, scores, 1, x, x_dtype, h, y, "x", "y");
+    if (st != MP_OK) return st;
+    const int64_t n = g->num_nodes, e = g->num_edges;
+    if (!row_stats) return fail(MP_ERR_NULL, "%s: row_stats is NULL", what);
+    if (!aligned(row_stats, 8)) return fail(MP_ERR_ALIGN, "%s: row_stats misaligned", what);
+    if ((st = check_device(row_stats, "row_stats")) != MP_OK) return st;
+    const Range rs = range(row_stats, 2 * n, 4, "row_stats");
+    RangeList others = graph_ranges(g);
+    others.add(range(x, n * h, dtype_size(x_dtype), "x"));
+    others.add(range(scores, e, 4, "scores"));
+    others.add(range(y, n * h, 4, "y"));
+    if (const char *hit = others.overlapping(rs))
+        return fail(MP_ERR_ALIAS, "%s: row_stats overlaps %s", what, hit);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = edge_softmax_stats_run(g, scores, row_stats, s)) != MP_OK) return st;
+    NormSpec nm{kFetchSoftmax, true, nullptr, reinterpret_cast<const float2 *>(row_stats)};
+    return spmm_run(forward_view(g), scores, 1, x, x_dtype, h, y, s, &nm);
+}
+
 mp_status mp_spmm_dx_norm(const mp_graph *g, int32_t mode, const float *w, const void *dy,
                           mp_dtype dy_dtype, int64_t h, float *dx, void *stream) {
     mp_status st = check_norm_mode(mode, "mp_spmm_dx_norm");

@@ -126,10 +126,16 @@ struct CsrView {
 // lengths of the two CSR forms.  own_is_dst: the walked CSR's rows are
 // destinations (forward); rowptr_other: row pointers of the other form, which
 // give the gathered endpoint's degree.
+// Weight transform at the fetch: MP_NORM_MEAN / MP_NORM_SYM degree factors, or
+// kFetchSoftmax (forward only): the weight read is an edge score s and the
+// kernel uses exp(s - m) / z of the owner row's softmax statistics (m, z), as
+// the softmax's own apply step forms alpha.
+constexpr int32_t kFetchSoftmax = 3;
 struct NormSpec {
     int32_t mode;
     bool own_is_dst;
     const int32_t *rowptr_other;
+    const float2 *stats;   // kFetchSoftmax: row statistics [N] (max, sum)
 };
 
 // `heads` = K: w holds K weights per edge ([E, K], edge-major) and head q owns
@@ -165,6 +171,9 @@ mp_status sddmm_run(const int32_t *src, const int32_t *dst, int64_t e, const voi
 // `heads` = K score columns per edge ([E, K]); statistics are [N, K].
 mp_status edge_softmax_run(const mp_graph *g, const float *s, int64_t heads, float *alpha,
                            float *row_stats, hipStream_t stream);
+// The row statistics (max, sum) of the one-head softmax only (no alpha).
+mp_status edge_softmax_stats_run(const mp_graph *g, const float *s, float *row_stats,
+                                 hipStream_t st);
 mp_status edge_softmax_backward_run(const mp_graph *g, const float *alpha, const float *dalpha,
                                     int64_t heads, float *ds, float *row_dot, hipStream_t stream);
 

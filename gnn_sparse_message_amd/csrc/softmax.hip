@@ -418,6 +418,19 @@ mp_status edge_softmax_run(const mp_graph *g, const float *s, int64_t heads, flo
     return MP_OK;
 }
 
+mp_status edge_softmax_stats_run(const mp_graph *g, const float *s, float *row_stats,
+                                 hipStream_t st) {
+    RowArgs r = row_args(g);
+    r.a = s;
+    r.stats = reinterpret_cast<float2 *>(row_stats);
+    r.dot = nullptr;
+    r.heads = 1;
+    const int64_t gx = (int64_t)r.blk_hub + r.blk_wave + r.blk_lane;
+    launch_row_stats<false>(r, 1, (unsigned)gx, st);
+    MP_HIP_CHECK(hipGetLastError(), "edge softmax statistics launch");
+    return MP_OK;
+}
+
 mp_status edge_softmax_backward_run(const mp_graph *g, const float *alpha, const float *dalpha,
                                     int64_t heads, float *ds, float *rdot, hipStream_t st) {
     RowArgs r = row_args(g);

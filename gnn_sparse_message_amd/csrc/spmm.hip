@@ -300,7 +300,7 @@ template <typename T, int VEC, int L, int TL, int kMode, bool kHeads, bool kNorm
 __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int64_t end,
                                            int64_t stride, int lane, int64_t hoff, int head,
                                            bool active, const float (&xr)[VEC],
-                                           float (&acc)[VEC], double own_deg) {
+                                           float (&acc)[VEC], double own_deg, float2 own_st) {
     constexpr int G = TL / L;                 // groups per team
     constexpr int kUnroll = unroll_for<kMode, kHeads, kNorm>();
     const int tl = lane % TL;
@@ -326,18 +326,26 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
                 wt = __builtin_nontemporal_load(&a.w[o]);
             }
             if constexpr (kNorm) {
-                // mean needs only the destination's degree, the owner's in the
-                // forward; otherwise the gathered endpoint's row length is read
-                const bool mean_own = a.norm.mode == MP_NORM_MEAN && a.norm.own_is_dst;
-                const uint32_t cc = (uint64_t)(uint32_t)c < (uint64_t)a.n ? (uint32_t)c : 0u;
-                const double other = mean_own ? 0.0
-                                              : (double)(a.norm.rowptr_other[cc + 1] -
-                                                         a.norm.rowptr_other[cc]);
-                double f;
-                if (a.norm.mode == MP_NORM_MEAN) f = 1.0 / (a.norm.own_is_dst ? own_deg : other);
-                else f = 1.0 / sqrt(own_deg * other);
-                sc = (float)f;
-                wt = wt * sc;
+                if (kMode == kPlain && a.norm.mode == kFetchSoftmax) {
+                    // the score's softmax weight, formed as the softmax apply step does
+                    wt = expf(wt - own_st.x) / own_st.y;
+                } else {
+                    // mean needs only the destination's degree, the owner's in the
+                    // forward; otherwise the gathered endpoint's row length is read
+                    const bool mean_own = a.norm.mode == MP_NORM_MEAN && a.norm.own_is_dst;
+                    const uint32_t cc =
+                        (uint64_t)(uint32_t)c < (uint64_t)a.n ? (uint32_t)c : 0u;
+                    const double other = mean_own ? 0.0
+                                                  : (double)(a.norm.rowptr_other[cc + 1] -
+                                                             a.norm.rowptr_other[cc]);
+                    double f;
+                    if (a.norm.mode == MP_NORM_MEAN)
+                        f = 1.0 / (a.norm.own_is_dst ? own_deg : other);
+                    else
+                        f = 1.0 / sqrt(own_deg * other);
+                    sc = (float)f;
+                    wt = wt * sc;
+                }
             }
         }
         const int n = end - base < TL ? (int)(end - base) : TL;
@@ -463,7 +471,8 @@ __device__ __forceinline__ void hub_rows(const SpmmArgs &a, int32_t first, int32
         accumulate<T, VEC, L, kWave, kMode, kHeads, kNorm>(a, beg + (int64_t)wv * kWave, end,
                                                                (int64_t)kWaves * kWave, lane,
                                                                hoff, head, active, xr, acc,
-                                                               (double)(end - beg));
+                                                               (double)(end - beg),
+                                                               own_stats<kMode, kNorm>(a, row));
 #pragma unroll
         for (int off = L; off < kWave; off <<= 1)
 #pragma unroll
@@ -486,6 +495,16 @@ __device__ __forceinline__ void hub_rows(const SpmmArgs &a, int32_t first, int32
         }
         __syncthreads();   // s_red is written again for the next row
     }
+}
+
+// The owner row's softmax statistics (max, sum) when the forward forms softmax
+// weights at the fetch; unused otherwise.
+template <int kMode, bool kNorm>
+__device__ __forceinline__ float2 own_stats(const SpmmArgs &a, int row) {
+    if constexpr (kNorm && kMode == kPlain) {
+        if (a.norm.mode == kFetchSoftmax) return a.norm.stats[row];
+    }
+    return make_float2(0.f, 1.f);
 }
 
 // Occupancy floors: the single-head fused backward is held to five waves per
@@ -543,7 +562,8 @@ void spmm_kernel(SpmmArgs a) {
             own_row<T, VEC, kMode>(a, row, hoff, active, xr);
             accumulate<T, VEC, L, kWave, kMode, kHeads, kNorm>(a, beg, end, (int64_t)kWave,
                                                                    lane, hoff, head, active, xr,
-                                                                   acc, (double)(end - beg));
+                                                                   acc, (double)(end - beg),
+                                                                   own_stats<kMode, kNorm>(a, row));
 #pragma unroll
             for (int off = L; off < kWave; off <<= 1)
 #pragma unroll
@@ -571,7 +591,8 @@ void spmm_kernel(SpmmArgs a) {
         own_row<T, VEC, kMode>(a, row, hoff, active && end > beg, xr);
         accumulate<T, VEC, L, L, kMode, kHeads, kNorm>(a, beg, end, (int64_t)L, lane, hoff,
                                                            head, active, xr, acc,
-                                                           (double)(end - beg));
+                                                           (double)(end - beg),
+                                                           own_stats<kMode, kNorm>(a, row));
         if (active) store_row<VEC>(a.y + (int64_t)row * a.h + hoff, acc);
     }
 }
@@ -629,6 +650,8 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
     const bool normed = norm && norm->mode != 0;
     if (normed && (heads != 1 || row_dot))
         return fail(MP_ERR_SHAPE, "fetch-time normalisation takes one head and no row dots");
+    if (normed && norm->mode == kFetchSoftmax && (dw || !norm->stats))
+        return fail(MP_ERR_SHAPE, "softmax weights at the fetch are for the forward, with statistics");
     if (pair && (heads != 1 || row_dot || normed || !dw))
         return fail(MP_ERR_SHAPE, "the interleaved weight layout is for the one-head fused backward");
     const Overrides ov = overrides_for(L);

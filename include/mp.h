@@ -307,6 +307,27 @@ mp_status mp_edge_softmax(const mp_graph *g, const float *scores, float *alpha, 
                           void *stream);
 
 /*
+ * The attention layer's forward, Y = A_alpha X with alpha = softmax(scores)
+ * over each target ("Limits"), without writing alpha: the row statistics
+ * pass of mp_edge_softmax, then the aggregation forms each edge's weight as
+ * it fetches the score, exp(s_e - m_i) / z_i with the owner row's statistics,
+ * in the same fp32 operations as mp_edge_softmax forms alpha.  Y and
+ * row_stats are bit for bit those of mp_edge_softmax followed by mp_spmm_fwd
+ * on its alpha.  For inference, or with a backward that recomputes alpha; the
+ * one-call attention backward takes alpha itself.
+ *   scores     [E] float32, COO order (one head).
+ *   x          [N, H] of x_dtype (MP_F32 or MP_BF16).   h = H.
+ *   y          [N, H] float32 output.
+ *   row_stats  [N][2] float32 output, 8-byte aligned: (m_i, z_i) as in
+ *              mp_edge_softmax.
+ * Errors as mp_spmm_fwd, plus MP_ERR_NULL / MP_ERR_ALIGN / MP_ERR_DEVICE for
+ * row_stats and MP_ERR_ALIAS when it overlaps an input, y or the graph arrays.
+ */
+mp_status mp_spmm_fwd_softmax(const mp_graph *g, const float *scores, const void *x,
+                              mp_dtype x_dtype, int64_t h, float *y, float *row_stats,
+                              void *stream);
+
+/*
  * Backward of mp_edge_softmax: given alpha and the upstream gradient dalpha
  * (for the attention layer, dalpha = mp_edge_grad_dw(g, X, dY) or the dw of
  * mp_spmm_dx_edge_grad), writes

@@ -179,6 +179,9 @@ def test_compute_calls_reject_unbuilt_graphs(mp):
     assert fn(None, 1, 0x100, 0x200, 0x300, mp.MP_F32, 4, 0x400, 0x500, None) == mp.MP_ERR_NULL
     assert fn(ctypes.byref(g), 1, 0x100, 0x200, 0x300, mp.MP_F32, 4, 0x400, 0x500, None) \
         == mp.MP_ERR_GRAPH
+    fs = lib.mp_spmm_fwd_softmax
+    assert fs(None, 0x100, 0x200, mp.MP_F32, 4, 0x300, 0x400, None) == mp.MP_ERR_NULL
+    assert fs(ctypes.byref(g), 0x100, 0x200, mp.MP_F32, 4, 0x300, 0x400, None) == mp.MP_ERR_GRAPH
     ab = lib.mp_attention_backward
     args = (0x100, 2, 0x200, 0x300, 0x380, mp.MP_F32, 4, 0x400, 0x500, 0x600, None)
     assert ab(None, *args) == mp.MP_ERR_NULL

@@ -506,3 +506,66 @@ def test_attention_backward_in_place(mp, k):
     yw = torch.zeros((wide.n, 600), device=DEV)
     with pytest.raises(ValueError):
         mp.mp_attention_backward(gw, aw, tw["x"], tw["dy"], yw, out_dscores=aw)
+
+
+def _fwd_softmax_cases():
+    yield "witness", synth.witness(), {}
+    yield "empty", synth.random_graph(5, 0, 8, 61), {}
+    yield "random_f32_h24", synth.random_graph(700, 9000, 24, 62), {}
+    yield "random_bf16_h128", synth.random_graph(900, 20000, 128, 63, feat_dtype="bf16"), {}
+    yield "random_f32_h7", synth.random_graph(300, 4000, 7, 64), {}              # scalar lanes
+    yield "random_f32_h300", synth.random_graph(300, 4000, 300, 65), {}          # column blocks
+    yield "power_law", _power_law(66), {}
+    yield "power_law_four_wave_hubs", _power_law(67), {"MP_HUB_APART": "0",
+                                                        "MP_HUB_MIN_LEN": "4096"}
+    yield "rmat16", synth.rmat16(), {}                                          # 16-wave hubs
+
+
+def _power_law(seed):
+    return synth.chung_lu(seed=seed, n=20000, e=400000, cap=20000.0, h=64, feat_dtype="f32")
+
+
+@pytest.mark.parametrize("idx", range(9))
+def test_fwd_softmax_equals_softmax_then_forward(mp, idx, monkeypatch):
+    """mp_spmm_fwd_softmax (alpha formed at the fetch, never written) against
+    mp_edge_softmax followed by mp_spmm_fwd on its alpha: Y and the row
+    statistics bit for bit, on synchronously and asynchronously built graphs;
+    that alpha against the oracle's softmax and Y against the oracle's
+    aggregation with it."""
+    name, wl, env = list(_fwd_softmax_cases())[idx]
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    print(f"case {name}: N={wl.n} E={wl.e} H={wl.h} {wl.feat_dtype}", flush=True)
+    t = upload(wl, DEV)
+    scores = torch.from_numpy(wl.w).to(DEV)
+    for g in (mp.mp_graph_build(t["src"], t["dst"], wl.n),
+              mp.mp_graph_build_async(t["src"], t["dst"], wl.n)):
+        y, stats = mp.mp_spmm_fwd_softmax(g, scores, t["x"])
+        alpha, ref_stats = mp.mp_edge_softmax(g, scores)
+        ref_y = mp.mp_spmm_fwd(g, alpha, t["x"])
+        torch.cuda.synchronize()
+        assert torch.equal(stats, ref_stats), "row statistics"
+        assert torch.equal(y, ref_y), "aggregation"
+    if wl.e:
+        # the weights used: alpha against the oracle's softmax, then Y against the
+        # oracle's aggregation with those float32 weights
+        _check_softmax(wl, wl.w, alpha, stats[:, 0], stats[:, 1])
+        a32 = alpha.cpu().numpy()
+        check_close("Y", y, *oracle.forward(wl.n, wl.src, wl.dst, a32, wl.x), TAU["f32"])
+
+
+def test_fwd_softmax_rejections(mp):
+    wl = synth.random_graph(50, 400, 8, 68)
+    t = upload(wl, DEV)
+    g = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    s = torch.from_numpy(wl.w).to(DEV)
+    with pytest.raises(TypeError):
+        mp.mp_spmm_fwd_softmax(g, s.double(), t["x"])
+    with pytest.raises(ValueError):
+        mp.mp_spmm_fwd_softmax(g, s[:-1], t["x"])
+    y = torch.empty((wl.n, wl.h), device=DEV)
+    buf = torch.empty(2 * wl.n + 1, device=DEV)
+    with pytest.raises(ValueError, match="align"):      # row statistics off their 8-byte line
+        mp.mp_spmm_fwd_softmax(g, s, t["x"], out=y, out_row_stats=buf[1:].view(wl.n, 2))
+    with pytest.raises(ValueError, match="overlap"):
+        mp.mp_spmm_fwd_softmax(g, s, t["x"], out=y, out_row_stats=y.view(-1)[: 2 * wl.n].view(wl.n, 2))

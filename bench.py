@@ -449,6 +449,15 @@ def main():
     standalone["attention_backward_in_place"] = time_op(
         lambda: mp.mp_attention_backward(g, a_buf, x, dy, y, out_dx=dx_att, out_dscores=a_buf,
                                          out_row_dot=rdot))
+    # ... with alpha formed in the walk from the scores (the edge weights) and
+    # their softmax statistics (rstats, from the attention forward above)
+    standalone["attention_backward_scores"] = time_op(
+        lambda: mp.mp_attention_backward_scores(g, w, rstats, x, dy, y, out_dx=dx_att,
+                                                out_dscores=dscores, out_row_dot=rdot))
+    a_buf.copy_(w)
+    standalone["attention_backward_scores_in_place"] = time_op(
+        lambda: mp.mp_attention_backward_scores(g, a_buf, rstats, x, dy, y, out_dx=dx_att,
+                                                out_dscores=a_buf, out_row_dot=rdot))
     del dx_att, a_buf
     log(f"standalone dx {standalone['dx']:.3f} ms, dw {standalone['dw']:.3f} ms, "
         f"equal to the fused results: {same}")
@@ -519,6 +528,9 @@ def main():
     bytes_["fwd_norm_mean"] = bytes_["fwd"]
     bytes_["bwd_norm_sym"] = bytes_["bwd"] + 4 * (n + 1)
     bytes_["attention_backward_in_place"] = bytes_["attention_backward"]
+    # scores in alpha's place, plus each row's two statistics read once
+    bytes_["attention_backward_scores"] = bytes_["attention_backward"] + 8 * n
+    bytes_["attention_backward_scores_in_place"] = bytes_["attention_backward_scores"]
     bytes_["attention_backward_heads"] = (bytes_["attention_backward"] + 8 * (heads - 1) * e
                                           + 4 * (heads - 1) * n)
     ms_step = t_total / args.steps * 1e3

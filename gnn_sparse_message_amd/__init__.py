@@ -32,7 +32,7 @@ __all__ = [
     "mp_spmm_dx", "mp_edge_grad_dw", "mp_spmm_dx_edge_grad", "mp_spmm_fwd_heads",
     "mp_spmm_dx_heads", "mp_edge_grad_dw_heads", "mp_spmm_dx_edge_grad_heads", "mp_edge_softmax",
     "mp_edge_softmax_backward", "mp_edge_softmax_heads", "mp_edge_softmax_backward_heads",
-    "mp_attention_backward", "mp_spmm_fwd_softmax", "mp_spmm_fwd_norm", "mp_spmm_dx_norm", "mp_spmm_dx_edge_grad_norm",
+    "mp_attention_backward", "mp_attention_backward_scores", "mp_spmm_fwd_softmax", "mp_spmm_fwd_norm", "mp_spmm_dx_norm", "mp_spmm_dx_edge_grad_norm",
     "mp_spmm_dx_edge_grad_pair",
     "mp_edge_normalize", "MP_NORM_MEAN", "MP_NORM_SYM",
     "mp_status_string", "mp_version", "library_path",
@@ -122,6 +122,7 @@ def _load():
         "mp_edge_softmax_heads": (i32, [gp, vp, i64, vp, vp, vp]),
         "mp_edge_softmax_backward_heads": (i32, [gp, vp, vp, i64, vp, vp, vp]),
         "mp_attention_backward": (i32, [gp, vp, i64, vp, vp, vp, i32, i64, vp, vp, vp, vp]),
+        "mp_attention_backward_scores": (i32, [gp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp]),
         "mp_spmm_fwd_norm": (i32, [gp, i32, vp, vp, i32, i64, vp, vp]),
         "mp_spmm_fwd_softmax": (i32, [gp, vp, vp, i32, i64, vp, vp, vp]),
         "mp_spmm_dx_norm": (i32, [gp, i32, vp, vp, i32, i64, vp, vp]),
@@ -621,6 +622,34 @@ def mp_attention_backward(g: Graph, alpha, x, dy, y, out_dx=None, out_dscores=No
                                       _ptr(dy), _ptr(y), code, h, _ptr(dx),
                                       _ptr(ds) if g.num_edges else None, _ptr(rdot),
                                       _stream(dy)), "mp_attention_backward")
+    return dx, ds, rdot
+
+
+def mp_attention_backward_scores(g: Graph, scores, row_stats, x, dy, y, out_dx=None,
+                                 out_dscores=None, out_row_dot=None):
+    """mp_attention_backward for one head with alpha formed in the walk from the
+    scores [E] and the softmax row statistics [N, 2] (of mp_spmm_fwd_softmax or
+    mp_edge_softmax): returns (dX, dscores [E], row_dot [N]), bitwise those of
+    mp_attention_backward given alpha; out_dscores may be scores itself."""
+    h = _features("x", x, g)
+    if _features("dy", dy, g) != h or _features("y", y, g) != h:
+        raise ValueError("x, dy and y must have the same feature width")
+    if y.dtype != torch.float32:
+        raise TypeError(f"y must be float32, got {y.dtype}")
+    _edge_f32("scores", scores, g)
+    _need_tensor("row_stats", row_stats)
+    if row_stats.dtype != torch.float32 or tuple(row_stats.shape) != (g.num_nodes, 2):
+        raise ValueError(f"row_stats must be float32 [{g.num_nodes}, 2]")
+    code = _code(dy) if x.dtype == dy.dtype else 0
+    dx = _out(out_dx, (g.num_nodes, h), dy)
+    ds = _out(out_dscores, (g.num_edges,), dy)
+    rdot = _out(out_row_dot, (g.num_nodes,), dy)
+    _check(_lib.mp_attention_backward_scores(ctypes.byref(g._desc),
+                                             _ptr(scores) if g.num_edges else None,
+                                             _ptr(row_stats), _ptr(x), _ptr(dy), _ptr(y), code, h,
+                                             _ptr(dx), _ptr(ds) if g.num_edges else None,
+                                             _ptr(rdot), _stream(dy)),
+           "mp_attention_backward_scores")
     return dx, ds, rdot
 
 

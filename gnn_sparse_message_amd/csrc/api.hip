@@ -601,10 +601,12 @@ mp_status mp_spmm_dx_edge_grad_norm(const mp_graph *g, int32_t mode, const float
 }
 
 namespace {
+// With stats, `alpha` holds the scores and each alpha is formed from its score
+// and its destination's softmax statistics [N][2] in the walk (one head).
 mp_status attention_backward_impl(const mp_graph *g, const float *alpha, int64_t heads,
                                   const void *x, const void *dy, const float *y, mp_dtype dtype,
                                   int64_t h, float *dx, float *dscores, float *row_dot,
-                                  void *stream) {
+                                  void *stream, const float *stats = nullptr) {
     mp_status st = check_spmm(g, alpha, heads, dy, dtype, h, dx, "dy", "dx");
     if (st != MP_OK) return st;
     const int64_t n = g->num_nodes, e = g->num_edges;
@@ -629,7 +631,15 @@ mp_status attention_backward_impl(const mp_graph *g, const float *alpha, int64_t
     if (in_place && !fused)
         return fail(MP_ERR_ALIAS, "dscores may be alpha only when the feature rows fit the "
                                   "fused walk (H up to 64 lanes of 16-byte slices)");
+    if (stats && !fused)
+        return fail(MP_ERR_SHAPE, "alpha formed from scores needs feature rows that fit the "
+                                  "fused walk (H up to 64 lanes of 16-byte slices)");
     RangeList others = graph_ranges(g);
+    if (stats) {
+        if (!aligned(stats, 8)) return fail(MP_ERR_ALIGN, "row_stats not aligned to 8 bytes");
+        if ((st = check_device(stats, "row_stats")) != MP_OK) return st;
+        others.add(range(stats, 2 * n, 4, "row_stats"));
+    }
     others.add(range(x, n * h, xs, "x"));
     others.add(range(dy, n * h, xs, "dy"));
     others.add(range(y, n * h, 4, "y"));
@@ -645,6 +655,11 @@ mp_status attention_backward_impl(const mp_graph *g, const float *alpha, int64_t
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = attention_row_dot_run(y, dy, dtype, n, h, heads, row_dot, s)) != MP_OK) return st;
     const CsrView v = transpose_view(g);
+    if (stats) {
+        const NormSpec nm{kFetchSoftmax, false, nullptr, reinterpret_cast<const float2 *>(stats)};
+        return spmm_fused_run(v, alpha, 1, dy, dtype, h, dx, x, e > 0 ? dscores : nullptr,
+                              row_dot, s, &nm);
+    }
     if (fused)
         return spmm_fused_run(v, alpha, heads, dy, dtype, h, dx, x, e > 0 ? dscores : nullptr,
                               row_dot, s);
@@ -657,6 +672,15 @@ mp_status attention_backward_impl(const mp_graph *g, const float *alpha, int64_t
     return score_grad_apply_run(g->dst, alpha, row_dot, e, heads, dscores, s);
 }
 }  // namespace
+
+mp_status mp_attention_backward_scores(const mp_graph *g, const float *scores,
+                                       const float *row_stats, const void *x, const void *dy,
+                                       const float *y, mp_dtype dtype, int64_t h, float *dx,
+                                       float *dscores, float *row_dot, void *stream) {
+    if (!row_stats) return fail(MP_ERR_NULL, "row_stats is NULL");
+    return attention_backward_impl(g, scores, 1, x, dy, y, dtype, h, dx, dscores, row_dot,
+                                   stream, row_stats);
+}
 
 mp_status mp_attention_backward(const mp_graph *g, const float *alpha, int64_t heads,
                                 const void *x, const void *dy, const float *y, mp_dtype dtype,

@@ -325,7 +325,13 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
             } else if constexpr (!kHeads) {
                 wt = __builtin_nontemporal_load(&a.w[o]);
             }
-            if constexpr (kNorm) {
+            if constexpr (kNorm && score_mode(kMode)) {
+                // the score's softmax weight from its destination's statistics (the
+                // gathered row here), formed as the softmax apply step does
+                const uint32_t cc = (uint64_t)(uint32_t)c < (uint64_t)a.n ? (uint32_t)c : 0u;
+                const float2 st = a.norm.stats[cc];
+                wt = expf(wt - st.x) / st.y;
+            } else if constexpr (kNorm) {
                 if (kMode == kPlain && a.norm.mode == kFetchSoftmax) {
                     // the score's softmax weight, formed as the softmax apply step does
                     wt = expf(wt - own_st.x) / own_st.y;
@@ -648,10 +654,12 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
                  float *out, const void *x_own, float *dw, const float *row_dot,
                  const NormSpec *norm, bool pair, hipStream_t s) {
     const bool normed = norm && norm->mode != 0;
-    if (normed && (heads != 1 || row_dot))
+    const bool soft = normed && norm->mode == kFetchSoftmax;
+    if (normed && (heads != 1 || (row_dot && !soft)))
         return fail(MP_ERR_SHAPE, "fetch-time normalisation takes one head and no row dots");
-    if (normed && norm->mode == kFetchSoftmax && (dw || !norm->stats))
-        return fail(MP_ERR_SHAPE, "softmax weights at the fetch are for the forward, with statistics");
+    if (soft && (!norm->stats || (dw && !row_dot)))
+        return fail(MP_ERR_SHAPE, "softmax weights at the fetch need statistics, and with edge "
+                                  "outputs the score-gradient form");
     if (pair && (heads != 1 || row_dot || normed || !dw))
         return fail(MP_ERR_SHAPE, "the interleaved weight layout is for the one-head fused backward");
     const Overrides ov = overrides_for(L);
@@ -730,11 +738,13 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
     const dim3 hub((unsigned)hx, (unsigned)gy), rest((unsigned)gx, (unsigned)gy);
     if (dw) {   // fused backward: one column block holds the whole feature row
         if (gy != 1) return fail(MP_ERR_SHAPE, "fused backward needs H <= %d", L * VEC);
-        if (row_dot && dw == w) {   // score gradients written over alpha
+        if (row_dot && dw == w) {   // score gradients written over alpha (or the scores)
             if (heads > 1) go<T, VEC, L, kScoreGradInPlace, true, false>(a, hub, rest, s);
+            else if (soft) go<T, VEC, L, kScoreGradInPlace, false, true>(a, hub, rest, s);
             else go<T, VEC, L, kScoreGradInPlace, false, false>(a, hub, rest, s);
         } else if (row_dot) {
             if (heads > 1) go<T, VEC, L, kScoreGrad, true, false>(a, hub, rest, s);
+            else if (soft) go<T, VEC, L, kScoreGrad, false, true>(a, hub, rest, s);
             else go<T, VEC, L, kScoreGrad, false, false>(a, hub, rest, s);
         } else if (normed) {
             go<T, VEC, L, kDw, false, true>(a, hub, rest, s);

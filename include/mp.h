@@ -390,6 +390,25 @@ mp_status mp_attention_backward(const mp_graph *g, const float *alpha, int64_t h
                                 int64_t h, float *dx, float *dscores, float *row_dot,
                                 void *stream);
 
+/*
+ * mp_attention_backward for one head with alpha never stored: given the scores
+ * and the row statistics of mp_spmm_fwd_softmax (or mp_edge_softmax), the
+ * transpose walk forms each edge's alpha_e = exp(s_e - m_dst) / z_dst from its
+ * score and its destination's statistics, in the fp32 operations the softmax
+ * forms alpha, then proceeds as mp_attention_backward.  Its outputs are bit
+ * for bit those of mp_attention_backward given that alpha.
+ *   scores     [E] float32, COO order.   row_stats  [N][2] float32, 8-byte aligned.
+ *   x, dy, y, h, dtype, dx, dscores, row_dot as mp_attention_backward (K = 1).
+ * dscores may be scores itself (written over them).  Feature rows must fit the
+ * fused walk (H up to 64 lanes of 16-byte slices), else MP_ERR_SHAPE; other
+ * errors as mp_attention_backward, and MP_ERR_NULL / MP_ERR_ALIGN /
+ * MP_ERR_DEVICE / MP_ERR_ALIAS for row_stats.
+ */
+mp_status mp_attention_backward_scores(const mp_graph *g, const float *scores,
+                                       const float *row_stats, const void *x, const void *dy,
+                                       const float *y, mp_dtype dtype, int64_t h, float *dx,
+                                       float *dscores, float *row_dot, void *stream);
+
 /* Normalisation modes for mp_edge_normalize. */
 #define MP_NORM_MEAN 1
 #define MP_NORM_SYM  2

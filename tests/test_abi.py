@@ -186,6 +186,11 @@ def test_compute_calls_reject_unbuilt_graphs(mp):
     args = (0x100, 2, 0x200, 0x300, 0x380, mp.MP_F32, 4, 0x400, 0x500, 0x600, None)
     assert ab(None, *args) == mp.MP_ERR_NULL
     assert ab(ctypes.byref(g), *args) == mp.MP_ERR_GRAPH
+    abs_ = lib.mp_attention_backward_scores
+    args = (0x100, 0x180, 0x200, 0x300, 0x380, mp.MP_F32, 4, 0x400, 0x500, 0x600, None)
+    assert abs_(None, *args) == mp.MP_ERR_NULL
+    assert abs_(ctypes.byref(g), *args) == mp.MP_ERR_GRAPH
+    assert abs_(ctypes.byref(g), 0x100, None, *args[2:]) == mp.MP_ERR_NULL
 
 
 def test_forward_and_input_grad_kernels_have_no_atomics(tmp_path):

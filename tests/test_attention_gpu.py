@@ -569,3 +569,52 @@ def test_fwd_softmax_rejections(mp):
         mp.mp_spmm_fwd_softmax(g, s, t["x"], out=y, out_row_stats=buf[1:].view(wl.n, 2))
     with pytest.raises(ValueError, match="overlap"):
         mp.mp_spmm_fwd_softmax(g, s, t["x"], out=y, out_row_stats=y.view(-1)[: 2 * wl.n].view(wl.n, 2))
+
+
+@pytest.mark.parametrize("idx", [0, 2, 3, 4, 6, 7, 8])
+def test_attention_backward_scores_equals_alpha_form(mp, idx, monkeypatch):
+    """mp_attention_backward_scores (alpha formed in the transpose walk from the
+    scores and the destinations' statistics) against mp_attention_backward
+    given alpha from mp_edge_softmax: dX, the score gradients and the row dots
+    bit for bit, on both build forms, and with the score gradients written
+    over the scores."""
+    name, wl, env = list(_fwd_softmax_cases())[idx]
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    print(f"case {name}: N={wl.n} E={wl.e} H={wl.h} {wl.feat_dtype}", flush=True)
+    t = upload(wl, DEV)
+    scores = torch.from_numpy(wl.w).to(DEV)
+    for g in (mp.mp_graph_build(t["src"], t["dst"], wl.n),
+              mp.mp_graph_build_async(t["src"], t["dst"], wl.n)):
+        y, stats = mp.mp_spmm_fwd_softmax(g, scores, t["x"])
+        alpha, _ = mp.mp_edge_softmax(g, scores)
+        ref = mp.mp_attention_backward(g, alpha, t["x"], t["dy"], y)
+        got = mp.mp_attention_backward_scores(g, scores, stats, t["x"], t["dy"], y)
+        s_ip = scores.clone()
+        ip = mp.mp_attention_backward_scores(g, s_ip, stats, t["x"], t["dy"], y, out_dscores=s_ip)
+        torch.cuda.synchronize()
+        for k, (a, b) in enumerate(zip(got, ref)):
+            assert torch.equal(a, b), f"output {k}"
+        assert torch.equal(ip[0], ref[0]) and torch.equal(s_ip, ref[1]), "in place"
+
+
+def test_attention_backward_scores_rejections(mp):
+    wl = synth.random_graph(300, 4000, 300, 69)            # wider than one column block
+    t = upload(wl, DEV)
+    g = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    s = torch.from_numpy(wl.w).to(DEV)
+    y, stats = mp.mp_spmm_fwd_softmax(g, s, t["x"])
+    with pytest.raises(ValueError, match="fused walk"):
+        mp.mp_attention_backward_scores(g, s, stats, t["x"], t["dy"], y)
+    wl = synth.random_graph(50, 400, 8, 70)
+    t = upload(wl, DEV)
+    g = mp.mp_graph_build(t["src"], t["dst"], wl.n)
+    s = torch.from_numpy(wl.w).to(DEV)
+    y, stats = mp.mp_spmm_fwd_softmax(g, s, t["x"])
+    buf = torch.empty(2 * wl.n + 1, device=DEV)
+    buf[1:].copy_(stats.view(-1))
+    with pytest.raises(ValueError, match="align"):
+        mp.mp_attention_backward_scores(g, s, buf[1:].view(wl.n, 2), t["x"], t["dy"], y)
+    with pytest.raises(ValueError, match="overlap"):
+        mp.mp_attention_backward_scores(g, s, stats, t["x"], t["dy"], y,
+                                        out_row_dot=stats.view(-1)[: wl.n])

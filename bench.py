@@ -1,13 +1,16 @@
 """Benchmark: weighted sparse message passing on one MI355X.
 
 One step = one pass of the whole path over one synthetic input: the device
-lowering (mp_graph_build), the forward aggregation (mp_spmm_fwd), and both
-gradients (mp_spmm_dx_edge_grad: the input gradient and the edge-weight
-gradient in one pass over the transpose CSR, bitwise equal to mp_spmm_dx and
-mp_edge_grad_dw, which are timed on their own after the steps).  Workload: the
-power-law Chung-Lu graph, N = 2,000,000, E = 100,000,000, degree exponent 2.1,
-per-direction expected degree capped at 100,000, H = 128 bf16 features with
-fp32 accumulation and fp32 outputs; inputs are resident in HBM before timing.
+lowering (mp_graph_build), the forward aggregation, and both gradients in one
+pass over the transpose CSR (the input gradient and the edge-weight gradient,
+bitwise equal to mp_spmm_dx and mp_edge_grad_dw, which are timed on their own
+after the steps).  The timed step keeps the edge weights and their gradients
+interleaved in one [E][2] array, both in COO order (mp_spmm_fwd_pair, then
+mp_spmm_dx_edge_grad_pair); the same step on two separate arrays (mp_spmm_fwd,
+mp_spmm_dx_edge_grad) is timed after it.  Workload: the power-law Chung-Lu
+graph, N = 2,000,000, E = 100,000,000, degree exponent 2.1, per-direction
+expected degree capped at 100,000, H = 128 bf16 features with fp32
+accumulation and fp32 outputs; inputs are resident in HBM before timing.
 
 Throughput is effective HBM bandwidth over algorithmic bytes (each edge
 touches its operand rows once):
@@ -15,8 +18,12 @@ touches its operand rows once):
     B_dX    = B_fwd
     B_dw    = E (2 H s + 12)
     B_build = E (2 s_idx + 16) + 8 (N + 1)            s_idx = 8 (int64 input)
-value = (B_build + B_fwd + B_dX + B_dw) / step time.  Per-op times come from
-HIP events recorded on the stream the kernels run on.
+    B_bwd   = E (H s + 16) + 4 (N + 1) + N H s + 4 N H
+B_bwd prices the fused backward launch at what it processes: per edge one
+gathered dY row, col_t, transpose_order, w and dw; per row the owner's X row,
+the dX row and a row pointer.  value = (B_build + B_fwd + B_bwd) / step time.
+B_dX and B_dw price the separate calls.  Per-op times come from HIP events
+recorded on the stream the kernels run on.
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
@@ -42,6 +49,7 @@ KERNEL_SOURCES = {
     "spmm_kernel": ["gnn_sparse_message_amd/csrc/spmm.hip", "gnn_sparse_message_amd/csrc/common.h"],
     "sddmm_kernel": ["gnn_sparse_message_amd/csrc/sddmm.hip",
                      "gnn_sparse_message_amd/csrc/common.h"],
+    "lowering": ["gnn_sparse_message_amd/csrc/lower.hip", "gnn_sparse_message_amd/csrc/common.h"],
 }
 
 
@@ -50,9 +58,14 @@ def log(*a):
 
 
 def algorithmic_bytes(n, e, h, s_feat, s_idx):
+    """Gather-model bytes of each call: the build, the forward, the separate
+    input-gradient and edge-gradient calls, and the fused backward launch (one
+    dY row, col_t, transpose_order, w and dw per edge; the owner's X row, its
+    dX row and a row pointer per row)."""
     fwd = e * (h * s_feat + 12) + 4 * (n + 1) + 4 * n * h
     return {"build": e * (2 * s_idx + 16) + 8 * (n + 1), "fwd": fwd, "dx": fwd,
-            "dw": e * (2 * h * s_feat + 12)}
+            "dw": e * (2 * h * s_feat + 12),
+            "bwd": e * (h * s_feat + 16) + 4 * (n + 1) + n * h * s_feat + 4 * n * h}
 
 
 def _code_only(text):
@@ -90,24 +103,63 @@ def measured_traffic(kernel_key):
     return k.get("hbm_bytes_per_launch")
 
 
+def cpu_baseline_all_cores(wl):
+    """The oracle's definitions on every host core (oracle/baseline_omp.c: an
+    OpenMP loop over the rows of the oracle's own CSR for the aggregations,
+    over the edges for the edge gradient; the counting sort stays serial), over
+    the whole workload: lowering of both directions, forward, input gradient,
+    edge gradient, fp64."""
+    import platform
+    from oracle import baseline
+    n, e, h = wl.n, wl.e, wl.h
+    nthreads = baseline.threads()
+    secs = baseline.run_path(n, wl.src, wl.dst, wl.w, wl.x, wl.dy)
+    dt = sum(secs.values())
+    b = algorithmic_bytes(n, e, h, 2, 8)
+    total = b["build"] + b["fwd"] + b["dx"] + b["dw"]
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": nthreads,
+            "kind": "oracle_openmp", "seconds": round(dt, 2),
+            "seconds_per_stage": {k: round(v, 2) for k, v in secs.items()},
+            "edges_per_s": round(e / dt, 1), "nproc": os.cpu_count(), "cpu_model": model,
+            "sample": f"all {e} COO edges, all {n} nodes, H={h}; lowering (both directions, "
+                      "serial counting sort) + forward + input gradient (OpenMP over CSR rows) + "
+                      "edge gradient (OpenMP over edges), fp64 C"}
+
+
 def cpu_baseline(wl, sample_edges):
     """The oracle as it stands (single-threaded C, fp64) on the first
-    `sample_edges` COO edges of the same workload, all N nodes, same H."""
+    `sample_edges` COO edges of the same workload, all N nodes, same H; one
+    progress line per stage."""
     import oracle
     n, h = wl.n, wl.h
     src, dst, w = wl.src[:sample_edges], wl.dst[:sample_edges], wl.w[:sample_edges]
     oracle._load()
-    t0 = time.perf_counter()
-    oracle.lower(n, dst, src)
-    oracle.lower(n, src, dst)
-    oracle.forward(n, src, dst, w, wl.x)
-    oracle.input_grad(n, src, dst, w, wl.dy)
-    oracle.edge_grad(src, dst, wl.x, wl.dy)
-    dt = time.perf_counter() - t0
+    stages = (("lowering", lambda: (oracle.lower(n, dst, src), oracle.lower(n, src, dst))),
+              ("forward", lambda: oracle.forward(n, src, dst, w, wl.x)),
+              ("input_grad", lambda: oracle.input_grad(n, src, dst, w, wl.dy)),
+              ("edge_grad", lambda: oracle.edge_grad(src, dst, wl.x, wl.dy)))
+    secs = {}
+    for name, fn in stages:
+        t0 = time.perf_counter()
+        fn()
+        secs[name] = time.perf_counter() - t0
+        log(f"  oracle {name} over {sample_edges} edges: {secs[name]:.1f}s")
+    dt = sum(secs.values())
     b = algorithmic_bytes(n, sample_edges, h, 2, 8)
-    return {"value": round(sum(b.values()) / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+    total = b["build"] + b["fwd"] + b["dx"] + b["dw"]
+    return {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle", "seconds": round(dt, 2),
-            "edges_per_s": round(sample_edges / dt, 1),
+            "seconds_per_stage": {k: round(v, 2) for k, v in secs.items()},
+            "edges_per_s": round(sample_edges / dt, 1), "nproc": os.cpu_count(),
             "sample": f"first {sample_edges} of the {wl.e} COO edges, all {n} nodes, H={h}; "
                       "lowering (both directions) + forward + input gradient + edge gradient, "
                       "single-threaded fp64 C oracle"}
@@ -177,7 +229,6 @@ def other_configs_bench(mp, torch, dev, reps=20):
                  "dw": lambda: mp.mp_edge_grad_dw(g, x, dy, out=dw),
                  "bwd": lambda: mp.mp_spmm_dx_edge_grad(g, w, x, dy, out_dx=dx, out_dw=dw)}
         b = algorithmic_bytes(n, e, h, 4, 8)
-        b["bwd"] = b["dx"] + b["dw"]
         res = {"num_nodes": n, "num_edges": e, "feature_width": h, "feature_storage": "f32"}
         for name, fn in calls.items():
             for _ in range(3):
@@ -285,7 +336,7 @@ def minibatch_bench(mp, torch, dev, n_batches=64, h=256):
     b_total = 0
     for t in staged:
         bb = algorithmic_bytes(t["n"], t["e"], h, 4, 8)
-        b_total += bb["build"] + bb["fwd"] + bb["dx"] + bb["dw"]
+        b_total += bb["build"] + bb["fwd"] + bb["bwd"]
     e_total = sum(t["e"] for t in staged)
     res = {"batches": len(staged), "feature_width": h, "feature_dtype": "f32",
            "edges_total": e_total, "nodes_max": n_max, "edges_max": e_max,
@@ -307,6 +358,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-sample-edges", type=int, default=10_000_000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="run the single-core oracle baseline over all E edges (minutes) "
+                         "instead of the first --cpu-sample-edges")
     ap.add_argument("--no-minibatch", action="store_true",
                     help="skip the back-to-back minibatch schedules")
     ap.add_argument("--no-other-configs", action="store_true",
@@ -340,41 +394,60 @@ def main():
     y = torch.empty((n, h), dtype=torch.float32, device=dev)
     dx = torch.empty_like(y)
     dw = torch.empty(e, dtype=torch.float32, device=dev)
+    # the parameter and its gradient side by side: wg[:, 0] = w, wg[:, 1] <- dw
+    wg = torch.empty((e, 2), dtype=torch.float32, device=dev)
+    wg[:, 0] = w
+    dx_p = torch.empty_like(dx)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
 
     ops = ("build", "fwd", "bwd")
-    times = {k: [] for k in ops}
 
-    def step(record):
+    def step(record, pair):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
         if record:
             ev[0].record(stream)
         g = mp.mp_graph_build(src, dst, n)
         if record:
             ev[1].record(stream)
-        mp.mp_spmm_fwd(g, w, x, out=y)
+        if pair:
+            mp.mp_spmm_fwd_pair(g, wg, x, out=y)
+        else:
+            mp.mp_spmm_fwd(g, w, x, out=y)
         if record:
             ev[2].record(stream)
-        mp.mp_spmm_dx_edge_grad(g, w, x, dy, out_dx=dx, out_dw=dw)
+        if pair:
+            mp.mp_spmm_dx_edge_grad_pair(g, wg, x, dy, out_dx=dx_p)
+        else:
+            mp.mp_spmm_dx_edge_grad(g, w, x, dy, out_dx=dx, out_dw=dw)
         if record:
             ev[3].record(stream)
         return ev, g
 
-    for i in range(args.warmup):
-        step(False)
-        log(f"warmup step {i + 1}/{args.warmup}")
+    def run_steps(pair, label):
+        for i in range(args.warmup):
+            step(False, pair)
+            log(f"{label}: warmup step {i + 1}/{args.warmup}")
+        torch.cuda.synchronize()
+        events = []
+        t_start = time.perf_counter()
+        for i in range(args.steps):
+            events.append(step(True, pair)[0])
+        torch.cuda.synchronize()
+        t_total = time.perf_counter() - t_start
+        times = {k: [] for k in ops}
+        for ev in events:
+            for k, name in enumerate(ops):
+                times[name].append(ev[k].elapsed_time(ev[k + 1]))
+        log(f"{label}: timed {args.steps} steps in {t_total:.3f}s")
+        return t_total, times
+
+    # The headline steps (interleaved weights and gradients), then the same
+    # step on separate weight and gradient arrays.
+    t_total, times = run_steps(True, "step")
+    t_total_2, times_2 = run_steps(False, "step on two arrays")
     torch.cuda.synchronize()
-    events = []
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        events.append(step(True)[0])
-    torch.cuda.synchronize()
-    t_total = time.perf_counter() - t_start
-    for ev in events:
-        for k, name in enumerate(ops):
-            times[name].append(ev[k].elapsed_time(ev[k + 1]))
-    log(f"timed {args.steps} steps in {t_total:.3f}s")
+    same_layouts = bool(torch.equal(dx_p, dx) and torch.equal(wg[:, 1], dw))
 
     def time_op(fn, reps=5):
         fn()
@@ -429,13 +502,6 @@ def main():
         lambda: mp.mp_spmm_dx_edge_grad_norm(g, mp.MP_NORM_SYM, w, x, dy, out_dx=dx_n,
                                              out_dw=dw_n))
     del dx_n, dw_n
-    # The fused backward with weights and gradients interleaved ([E, 2]).
-    wg = torch.empty((e, 2), dtype=torch.float32, device=dev)
-    wg[:, 0] = w
-    dx_p = torch.empty_like(dx)
-    standalone["bwd_pair"] = time_op(
-        lambda: mp.mp_spmm_dx_edge_grad_pair(g, wg, x, dy, out_dx=dx_p))
-    same_pair = bool(torch.equal(dx_p, dx) and torch.equal(wg[:, 1], dw))
     del wg, dx_p
     # The whole attention backward in one call (alpha = the edge weights, Y = the
     # forward output of the steps): replaces the fused backward + softmax backward.
@@ -498,42 +564,47 @@ def main():
         log("copy calibration: 1 GiB read, 1 GiB written")
 
     bytes_ = algorithmic_bytes(n, e, h, 2, 8)
-    bytes_["bwd"] = bytes_["dx"] + bytes_["dw"]
+    # Gather-model bytes of the adjacent calls: every edge touches its operands
+    # once, and a per-edge read of a node-sized array (row statistics, row dots,
+    # degrees) counts once per edge, as the feature rows do.
     # target softmax: row pass reads order + score per edge and writes 2 stats per
-    # row; the edge pass reads dst + score, writes alpha.  Backward: row pass reads
-    # order + alpha + dalpha, the edge pass dst + alpha + dalpha and writes ds.
+    # row; the edge pass reads dst + score + the row's two statistics, writes alpha.
+    # Backward: row pass reads order + alpha + dalpha, writes a row dot; the edge
+    # pass reads dst + alpha + dalpha + the row dot and writes ds.
     # (Definition bytes of the operation, not of this implementation's passes.)
-    bytes_["edge_softmax"] = 20 * e + 24 * n
-    bytes_["edge_softmax_backward"] = 28 * e + 16 * n
-    # symmetric normalisation: in, out, src, dst per edge; both row pointers once.
-    bytes_["edge_normalize_sym"] = 16 * e + 8 * (n + 1)
+    bytes_["edge_softmax"] = 28 * e + 8 * n
+    bytes_["edge_softmax_backward"] = 32 * e + 4 * n
+    # symmetric normalisation: in, out, src, dst and two row lengths (two row
+    # pointers each) per edge.
+    bytes_["edge_normalize_sym"] = 32 * e
     # attention forward: the aggregation's bytes (the score in the weight's
     # place) plus the softmax's row pass (order + score per edge, two stats per
     # row written, then read once per row)
     bytes_["attention_forward"] = bytes_["fwd"] + 8 * e + 16 * n
     # multi-head: the edge's weight (or dw) term grows from 4 to 4K bytes.
     bytes_["fwd_heads"] = bytes_["fwd"] + 4 * (heads - 1) * e
-    bytes_["bwd_heads"] = bytes_["dx"] + bytes_["dw"] + 8 * (heads - 1) * e
+    bytes_["bwd_heads"] = bytes_["bwd"] + 8 * (heads - 1) * e
     # per-head softmax: the single-head bytes with K values per edge and per row
-    bytes_["edge_softmax_heads"] = 4 * e + 16 * e * heads + 24 * n * heads
-    bytes_["edge_softmax_backward_heads"] = 8 * e + 20 * e * heads + 16 * n * heads
-    # attention backward: the fused backward's bytes (alpha for w, ds for dw) plus
-    # the kept forward output Y and dY read once more for the row dots, and the
-    # row dots written; with K heads, K values per edge and per row.
-    bytes_["attention_backward"] = bytes_["bwd"] + (4 + 2) * n * h + 4 * n
-    # normalised at the fetch: the plain call's bytes plus the other CSR's row
-    # pointers, where the degrees come from
-    bytes_["bwd_pair"] = bytes_["bwd"]
-    bytes_["fwd_norm_sym"] = bytes_["fwd"] + 4 * (n + 1)
+    bytes_["edge_softmax_heads"] = 4 * e + 24 * e * heads + 8 * n * heads
+    bytes_["edge_softmax_backward_heads"] = 8 * e + 24 * e * heads + 4 * n * heads
+    # attention backward: the fused backward's bytes (alpha for w, ds for dw),
+    # the row dot gathered per edge, plus the kept forward output Y and dY read
+    # once more for the row dots, and the row dots written; with K heads, K
+    # values per edge and per row.
+    bytes_["attention_backward"] = bytes_["bwd"] + 4 * e + (4 + 2) * n * h + 4 * n
+    # normalised at the fetch: the plain call's bytes plus the gathered
+    # endpoint's row length (two row pointers) per edge
+    bytes_["fwd_norm_sym"] = bytes_["fwd"] + 8 * e
     bytes_["fwd_norm_mean"] = bytes_["fwd"]
-    bytes_["bwd_norm_sym"] = bytes_["bwd"] + 4 * (n + 1)
+    bytes_["bwd_norm_sym"] = bytes_["bwd"] + 8 * e
     bytes_["attention_backward_in_place"] = bytes_["attention_backward"]
-    # scores in alpha's place, plus each row's two statistics read once
-    bytes_["attention_backward_scores"] = bytes_["attention_backward"] + 8 * n
+    # scores in alpha's place, plus the destination's two statistics per edge
+    bytes_["attention_backward_scores"] = bytes_["attention_backward"] + 8 * e
     bytes_["attention_backward_scores_in_place"] = bytes_["attention_backward_scores"]
-    bytes_["attention_backward_heads"] = (bytes_["attention_backward"] + 8 * (heads - 1) * e
+    bytes_["attention_backward_heads"] = (bytes_["attention_backward"] + 12 * (heads - 1) * e
                                           + 4 * (heads - 1) * n)
     ms_step = t_total / args.steps * 1e3
+    ms_step_2 = t_total_2 / args.steps * 1e3
 
     def rate(nbytes, ms):
         gbps = nbytes / (ms * 1e-3) / 1e9
@@ -544,39 +615,49 @@ def main():
         v = sorted(v)
         return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
 
-    per_op = {k: rate(bytes_[k], statistics.median(times[k])) for k in ops}
-    for k in ops:
-        per_op[k]["p10_ms"] = round(pct(times[k], 0.1), 4)
-        per_op[k]["p90_ms"] = round(pct(times[k], 0.9), 4)
+    def ops_of(tms):
+        res = {k: rate(bytes_[k], statistics.median(tms[k])) for k in ops}
+        for k in ops:
+            res[k]["p10_ms"] = round(pct(tms[k], 0.1), 4)
+            res[k]["p90_ms"] = round(pct(tms[k], 0.9), 4)
+        return res
+
+    per_op = ops_of(times)
+    per_op_2 = ops_of(times_2)
+    build_traffic = measured_traffic("lowering:build")
+    if build_traffic is not None:
+        per_op["build"]["traffic"] = build_traffic
+        per_op["build"]["traffic_GBps"] = round(build_traffic / (per_op["build"]["ms"] * 1e-3)
+                                                / 1e9, 1)
     per_op_standalone = {k: rate(bytes_[k], v) for k, v in standalone.items()}
     per_op_standalone["equal_to_fused"] = same
     per_op_standalone["heads"] = heads
     per_op_standalone["heads_fused_equal_to_separate"] = same_heads
-    per_op_standalone["pair_equal_to_fused"] = same_pair
     # what the fetch-time softmax replaces: the softmax (writing alpha), then the
     # aggregation on alpha; the two give the same Y bit for bit
     per_op_standalone["attention_forward_two_calls_ms"] = round(attn_fwd_two_calls, 4)
     per_op_standalone["attention_forward_equal_to_two_calls"] = attn_fwd_equal
     # what the fetch-time normalisation replaces: a normalisation pass, then the call
     per_op_standalone["fwd_norm_two_calls_ms"] = round(
-        standalone["edge_normalize_sym"] + statistics.median(times["fwd"]), 4)
+        standalone["edge_normalize_sym"] + per_op_2["fwd"]["ms"], 4)
     per_op_standalone["bwd_norm_two_calls_ms"] = round(
-        standalone["edge_normalize_sym"] * 2 + statistics.median(times["bwd"]), 4)
+        standalone["edge_normalize_sym"] * 2 + per_op_2["bwd"]["ms"], 4)
     # what the one-call attention backward replaces: fused backward + softmax backward
     per_op_standalone["attention_backward_unfused_ms"] = round(
-        statistics.median(times["bwd"]) + standalone["edge_softmax_backward"], 4)
+        per_op_2["bwd"]["ms"] + standalone["edge_softmax_backward"], 4)
     per_op_standalone["attention_backward_heads_unfused_ms"] = round(
         standalone["bwd_heads"] + standalone["edge_softmax_backward_heads"], 4)
-    # Kernels of the compute ops.  The dominant kernel is the one with the most
-    # GPU time per step; its achieved bandwidth is the algorithmic bytes of the
-    # units one launch processes over its average launch duration (the fused
-    # backward processes both the dX and the dw units).  `traffic` is the
+    # Kernels of the step.  The dominant kernel is the one with the most GPU time
+    # per step; its achieved bandwidth is the algorithmic bytes of what one launch
+    # processes (B_bwd for the fused backward: one gathered dY row per edge feeds
+    # both gradients) over its average launch duration.  `traffic` is the
     # calibrated HBM counter bytes of one launch.
-    kernels = {"spmm_kernel_fused_backward": ("bwd", "spmm_kernel:bwd"),
-               "spmm_kernel": ("fwd", "spmm_kernel:fwd")}
+    kernels = {"spmm_kernel_fused_backward": ("bwd", "spmm_kernel:bwd_pair", per_op),
+               "spmm_kernel": ("fwd", "spmm_kernel:fwd_pair", per_op),
+               "spmm_kernel_fused_backward_two_arrays": ("bwd", "spmm_kernel:bwd", per_op_2)}
     roof = {}
-    for kname, (op, tkey) in kernels.items():
-        launch_ms = per_op[op]["ms"]
+    for kname, (op, tkey, src_ops) in kernels.items():
+        launch_ms = src_ops[op]["ms"]
         achieved = bytes_[op] / (launch_ms * 1e-3) / 1e9
         traffic = measured_traffic(tkey)
         roof[kname] = {"bound": "hbm", "kernel": f"{kname} ({op})",
@@ -585,9 +666,11 @@ def main():
                        "traffic_GBps": None if traffic is None
                        else round(traffic / (launch_ms * 1e-3) / 1e9, 1),
                        "algorithmic_bytes_per_launch": bytes_[op], "avg_launch_ms": launch_ms}
-    dominant = max(roof, key=lambda k: roof[k]["avg_launch_ms"])
-    total_bytes = bytes_["build"] + bytes_["fwd"] + bytes_["dx"] + bytes_["dw"]
+    dominant = max(("spmm_kernel_fused_backward", "spmm_kernel"),
+                   key=lambda k: roof[k]["avg_launch_ms"])
+    total_bytes = bytes_["build"] + bytes_["fwd"] + bytes_["bwd"]
     value = total_bytes / (ms_step * 1e-3) / 1e9
+    value_2 = total_bytes / (ms_step_2 * 1e-3) / 1e9
     out = {
         "metric": "SpMM fwd/dX + SDDMM dw effective HBM GB/s and edges/s; % of HBM roofline",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -596,10 +679,17 @@ def main():
         "config": {"workload": "chung_lu_powerlaw", "num_nodes": n, "num_edges": e,
                    "feature_width": h, "degree_exponent": 2.1, "degree_cap": 100000,
                    "feature_storage": "bf16", "index_input": "int64",
-                   "step": "mp_graph_build + mp_spmm_fwd + mp_spmm_dx_edge_grad"},
+                   "weights": "w and dw interleaved in one [E][2] array, COO order",
+                   "step": "mp_graph_build + mp_spmm_fwd_pair + mp_spmm_dx_edge_grad_pair"},
+        "algorithmic_bytes_per_step": total_bytes,
         "edges_per_s": round(e / (ms_step * 1e-3), 1),
         "frac_of_hbm_peak": round(value / PEAK_HBM_GBPS, 4),
         "per_op": per_op,
+        "step_two_arrays": {
+            "step": "mp_graph_build + mp_spmm_fwd + mp_spmm_dx_edge_grad (w and dw separate)",
+            "ms_per_step": round(ms_step_2, 4), "value": round(value_2, 1), "unit": "GB/s",
+            "frac_of_hbm_peak": round(value_2 / PEAK_HBM_GBPS, 4), "per_op": per_op_2,
+            "outputs_equal_to_interleaved_step": same_layouts},
         "per_op_standalone": per_op_standalone,
         "roofline": roof[dominant],
         "roofline_other_kernels": {k: v for k, v in roof.items() if k != dominant},
@@ -617,8 +707,11 @@ def main():
         log("minibatch ms per batch: " + ", ".join(
             f"{k} {out['minibatch'][k]['ms_per_batch']}" for k in ("sync", "async", "pipelined")))
     if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle on {args.cpu_sample_edges} edges ...")
-        out["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_sample_edges, e))
+        sample = e if args.cpu_full else min(args.cpu_sample_edges, e)
+        log(f"cpu baseline: oracle on {sample} edges, one core ...")
+        out["cpu_baseline"] = cpu_baseline(wl, sample)
+        log("cpu baseline: the same definitions on every core, all edges ...")
+        out["cpu_baseline_all_cores"] = cpu_baseline_all_cores(wl)
         log("cpu baseline of the adjacent operations ...")
         out["cpu_baseline_adjacent"] = cpu_baseline_adjacent(wl, min(args.cpu_sample_edges, e))
     else:

@@ -33,9 +33,10 @@ __all__ = [
     "mp_spmm_dx_heads", "mp_edge_grad_dw_heads", "mp_spmm_dx_edge_grad_heads", "mp_edge_softmax",
     "mp_edge_softmax_backward", "mp_edge_softmax_heads", "mp_edge_softmax_backward_heads",
     "mp_attention_backward", "mp_attention_backward_scores", "mp_spmm_fwd_softmax", "mp_spmm_fwd_norm", "mp_spmm_dx_norm", "mp_spmm_dx_edge_grad_norm",
-    "mp_spmm_dx_edge_grad_pair",
+    "mp_spmm_dx_edge_grad_pair", "mp_spmm_fwd_pair",
     "mp_edge_normalize", "MP_NORM_MEAN", "MP_NORM_SYM",
-    "mp_status_string", "mp_version", "library_path",
+    "mp_status_string", "mp_version", "library_path", "mp_set_owner_overrides",
+    "owner_overrides",
     "NUM_CLASSES",
 ]
 
@@ -45,6 +46,7 @@ _LIB_PATH = os.path.join(_HERE, "libmp.so")
 MP_OK = 0
 MP_ERR_NULL, MP_ERR_SHAPE, MP_ERR_DTYPE, MP_ERR_DEVICE, MP_ERR_INDEX = -1, -2, -3, -4, -5
 MP_ERR_ALIAS, MP_ERR_ALIGN, MP_ERR_WORKSPACE, MP_ERR_GRAPH, MP_ERR_HIP = -6, -7, -8, -9, -10
+MP_ERR_INTERNAL = -11
 MP_I32, MP_I64, MP_F32, MP_BF16 = 1, 2, 3, 4
 MP_NORM_MEAN, MP_NORM_SYM = 1, 2
 GRAPH_INFO_WORDS = 576
@@ -128,10 +130,12 @@ def _load():
         "mp_spmm_dx_norm": (i32, [gp, i32, vp, vp, i32, i64, vp, vp]),
         "mp_spmm_dx_edge_grad_norm": (i32, [gp, i32, vp, vp, vp, i32, i64, vp, vp, vp]),
         "mp_spmm_dx_edge_grad_pair": (i32, [gp, vp, vp, vp, i32, i64, vp, vp]),
+        "mp_spmm_fwd_pair": (i32, [gp, vp, vp, i32, i64, vp, vp]),
         "mp_edge_normalize": (i32, [gp, i32, vp, vp, vp]),
         "mp_status_string": (ctypes.c_char_p, [i32]),
         "mp_last_error_detail": (ctypes.c_char_p, []),
         "mp_version": (i32, []),
+        "mp_set_owner_overrides": (i32, [i32, i32, i32]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -153,6 +157,34 @@ def mp_version() -> int:
 
 def mp_status_string(status: int) -> str:
     return _lib.mp_status_string(status).decode()
+
+
+def mp_set_owner_overrides(hub_min_len: int = -1, hub_apart: int = -1,
+                           wave_min_len: int = -1) -> None:
+    """Replace the aggregation kernels' owner sizes for every later call in this
+    process (tests and tuning only; -1 restores the rule): rows of at least
+    hub_min_len edges get a workgroup, of 16 waves in a launch of their own when
+    hub_apart is 1 or of four waves in the main launch when 0, and rows of at
+    least wave_min_len edges get one wave.  Other owners change the summation
+    order, so the bits (not the tolerance) of the results."""
+    _check(_lib.mp_set_owner_overrides(int(hub_min_len), int(hub_apart), int(wave_min_len)),
+           "mp_set_owner_overrides")
+
+
+class owner_overrides:
+    """Context manager: mp_set_owner_overrides(...) inside the block, the rule
+    again after it."""
+
+    def __init__(self, hub_min_len: int = -1, hub_apart: int = -1, wave_min_len: int = -1):
+        self.args = (hub_min_len, hub_apart, wave_min_len)
+
+    def __enter__(self):
+        mp_set_owner_overrides(*self.args)
+        return self
+
+    def __exit__(self, *exc):
+        mp_set_owner_overrides(-1, -1, -1)
+        return False
 
 
 def _check(status: int, call: str):
@@ -391,15 +423,30 @@ def mp_spmm_dx_edge_grad_norm(g: Graph, mode: int, w, x, dy, out_dx=None, out_dw
     return dx, dw
 
 
-def mp_spmm_dx_edge_grad_pair(g: Graph, wg, x, dy, out_dx=None):
-    """Fused backward with weights and gradients interleaved: wg is float32
-    [E, 2], wg[:, 0] the weights (read) and wg[:, 1] receiving dw (written in
-    place).  Returns dX; dw is the view wg[:, 1]."""
+def _pair(wg, g: Graph):
     _need_tensor("wg", wg)
     if wg.dtype != torch.float32:
         raise TypeError(f"wg must be float32, got {wg.dtype}")
     if wg.dim() != 2 or tuple(wg.shape) != (g.num_edges, 2):
         raise ValueError(f"wg must have shape [{g.num_edges}, 2], got {tuple(wg.shape)}")
+
+
+def mp_spmm_fwd_pair(g: Graph, wg, x, out=None):
+    """Y = A_w X with the weights in column 0 of the interleaved float32 [E, 2]
+    array wg (column 1 is not read); bitwise mp_spmm_fwd(g, wg[:, 0], x)."""
+    _pair(wg, g)
+    h = _features("x", x, g)
+    y = _out(out, (g.num_nodes, h), x)
+    _check(_lib.mp_spmm_fwd_pair(ctypes.byref(g._desc), _ptr(wg) if g.num_edges else None,
+                                 _ptr(x), _code(x), h, _ptr(y), _stream(x)), "mp_spmm_fwd_pair")
+    return y
+
+
+def mp_spmm_dx_edge_grad_pair(g: Graph, wg, x, dy, out_dx=None):
+    """Fused backward with weights and gradients interleaved: wg is float32
+    [E, 2], wg[:, 0] the weights (read) and wg[:, 1] receiving dw (written in
+    place).  Returns dX; dw is the view wg[:, 1]."""
+    _pair(wg, g)
     h = _features("x", x, g)
     if _features("dy", dy, g) != h:
         raise ValueError("x and dy must have the same feature width")

@@ -76,15 +76,21 @@ bool overlap(const Range &a, const Range &b) {
     return a.lo < b.hi && b.lo < a.hi;
 }
 
-// A short list of address ranges with a fixed capacity; adding beyond it
-// aborts rather than writing past the end.
+// A short list of address ranges with a fixed capacity.  A range added beyond
+// the capacity is refused and remembered: every check against the list then
+// returns MP_ERR_INTERNAL instead of passing on an incomplete list (the largest
+// list any entry point builds holds 18 ranges).
+#ifndef MP_RANGE_LIST_CAP
+#define MP_RANGE_LIST_CAP 24
+#endif
 struct RangeList {
-    static constexpr int kCap = 24;
+    static constexpr int kCap = MP_RANGE_LIST_CAP;
     Range r[kCap];
     int k = 0;
+    bool refused = false;
     void add(const Range &x) {
-        if (k >= kCap) abort();
-        r[k++] = x;
+        if (k < kCap) r[k++] = x;
+        else refused = true;
     }
     // Name of the first range that overlaps `x`, or nullptr.
     const char *overlapping(const Range &x) const {
@@ -93,6 +99,20 @@ struct RangeList {
         return nullptr;
     }
 };
+
+mp_status list_overflow() {
+    return fail(MP_ERR_INTERNAL, "internal: more address ranges than the overlap check holds (%d)",
+                RangeList::kCap);
+}
+
+// MP_OK when `x` overlaps no range of `list`, else MP_ERR_ALIAS naming the
+// first one it overlaps (`prefix` opens the detail text).
+mp_status apart(const RangeList &list, const Range &x, const char *prefix = "") {
+    if (list.refused) return list_overflow();
+    if (const char *hit = list.overlapping(x))
+        return fail(MP_ERR_ALIAS, "%s%s overlaps %s", prefix, x.name, hit);
+    return MP_OK;
+}
 
 // Ranges of every array a graph descriptor points to.
 RangeList graph_ranges(const mp_graph *g) {
@@ -154,9 +174,10 @@ mp_status check_heads(int64_t h, int64_t heads) {
 }
 
 // Shared validation of one aggregation call (forward or input gradient); w
-// holds `heads` weights per edge.
+// holds `heads` weights per edge, in w_span floats per edge (0: heads).
 mp_status check_spmm(const mp_graph *g, const float *w, int64_t heads, const void *x,
-                     mp_dtype dt, int64_t h, float *y, const char *xname, const char *yname) {
+                     mp_dtype dt, int64_t h, float *y, const char *xname, const char *yname,
+                     int64_t w_span = 0) {
     mp_status st = check_graph(g);
     if (st != MP_OK) return st;
     const int64_t n = g->num_nodes, e = g->num_edges;
@@ -177,18 +198,18 @@ mp_status check_spmm(const mp_graph *g, const float *w, int64_t heads, const voi
     const Range ry = range(y, n * h, 4, yname);
     RangeList others = graph_ranges(g);
     others.add(range(x, n * h, xs, xname));
-    others.add(range(w, e * heads, 4, "w"));
-    if (const char *hit = others.overlapping(ry))
-        return fail(MP_ERR_ALIAS, "%s overlaps %s", yname, hit);
-    return MP_OK;
+    others.add(range(w, e * (w_span > 0 ? w_span : heads), 4, "w"));
+    return apart(others, ry);
 }
 
 mp_status spmm_fwd_impl(const mp_graph *g, const float *w, int64_t heads, const void *x,
-                        mp_dtype x_dtype, int64_t h, float *y, void *stream) {
-    mp_status st = check_spmm(g, w, heads, x, x_dtype, h, y, "x", "y");
+                        mp_dtype x_dtype, int64_t h, float *y, void *stream,
+                        bool pair = false) {
+    // with interleaved weights and gradients the weight array spans 2E floats
+    mp_status st = check_spmm(g, w, heads, x, x_dtype, h, y, "x", "y", pair ? 2 : 0);
     if (st != MP_OK) return st;
     return spmm_run(forward_view(g), w, heads, x, x_dtype, h, y,
-                    static_cast<hipStream_t>(stream));
+                    static_cast<hipStream_t>(stream), nullptr, pair);
 }
 
 mp_status spmm_dx_impl(const mp_graph *g, const float *w, int64_t heads, const void *dy,
@@ -222,8 +243,7 @@ mp_status edge_grad_impl(const mp_graph *g, const void *x, const void *dy, mp_dt
     RangeList others = graph_ranges(g);
     others.add(range(x, n * h, xs, "x"));
     others.add(range(dy, n * h, xs, "dy"));
-    if (const char *hit = others.overlapping(rdw))
-        return fail(MP_ERR_ALIAS, "dw overlaps %s", hit);
+    if ((st = apart(others, rdw)) != MP_OK) return st;
     return sddmm_run(g->src, g->dst, e, x, dy, dtype, h, heads, dw,
                      static_cast<hipStream_t>(stream));
 }
@@ -261,8 +281,7 @@ mp_status dx_edge_grad_impl(const mp_graph *g, const float *w, int64_t heads, co
     others.add(range(dy, n * h, xs, "dy"));
     others.add(range(w, e * heads, 4, "w"));
     others.add(rdx);
-    if (const char *hit = others.overlapping(rdw))
-        return fail(MP_ERR_ALIAS, "dw overlaps %s", hit);
+    if ((st = apart(others, rdw)) != MP_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const CsrView v = transpose_view(g);
     const NormSpec nm = norm_spec(g, norm_mode, false);
@@ -347,6 +366,7 @@ mp_status build_impl(const void *src, const void *dst, mp_dtype idx_dtype, int64
     r.add(Range{reinterpret_cast<uintptr_t>(workspace),
                 reinterpret_cast<uintptr_t>(workspace) + need, "workspace"});
     const Range in_s = range(src, e, is, "src"), in_d = range(dst, e, is, "dst");
+    if (r.refused) return list_overflow();
     for (int i = 0; i < r.k; ++i) {
         if (overlap(r.r[i], in_s) || overlap(r.r[i], in_d))
             return fail(MP_ERR_ALIAS, "%s overlaps the input edge list", r.r[i].name);
@@ -403,6 +423,11 @@ mp_status mp_graph_finish(mp_graph *g, void *stream) {
 mp_status mp_spmm_fwd(const mp_graph *g, const float *w, const void *x, mp_dtype x_dtype,
                       int64_t h, float *y, void *stream) {
     return spmm_fwd_impl(g, w, 1, x, x_dtype, h, y, stream);
+}
+
+mp_status mp_spmm_fwd_pair(const mp_graph *g, const float *wg, const void *x, mp_dtype x_dtype,
+                           int64_t h, float *y, void *stream) {
+    return spmm_fwd_impl(g, wg, 1, x, x_dtype, h, y, stream, true);
 }
 
 mp_status mp_spmm_dx(const mp_graph *g, const float *w, const void *dy, mp_dtype dy_dtype,
@@ -472,9 +497,10 @@ mp_status check_softmax(const mp_graph *g, int64_t heads, const float *edge_in,
     RangeList others = graph_ranges(g);
     others.add(range(edge_in, ek, 4, "edge input"));
     others.add(range(edge_in2, edge_in2 ? ek : 0, 4, "second edge input"));
+    char prefix[96];
+    snprintf(prefix, sizeof(prefix), "%s: ", what);
     for (int i = 0; i < 2; ++i)
-        if (const char *hit = others.overlapping(outs[i]))
-            return fail(MP_ERR_ALIAS, "%s: %s overlaps %s", what, outs[i].name, hit);
+        if ((st = apart(others, outs[i], prefix)) != MP_OK) return st;
     if (overlap(outs[0], outs[1]))
         return fail(MP_ERR_ALIAS, "%s: edge output overlaps row output", what);
     return MP_OK;
@@ -546,8 +572,7 @@ mp_status mp_spmm_fwd_softmax(const mp_graph *g, const float *scores, const void
     others.add(range(x, n * h, dtype_size(x_dtype), "x"));
     others.add(range(scores, e, 4, "scores"));
     others.add(range(y, n * h, 4, "y"));
-    if (const char *hit = others.overlapping(rs))
-        return fail(MP_ERR_ALIAS, "%s: row_stats overlaps %s", what, hit);
+    if ((st = apart(others, rs, "mp_spmm_fwd_softmax: ")) != MP_OK) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = edge_softmax_stats_run(g, scores, row_stats, s)) != MP_OK) return st;
     NormSpec nm{kFetchSoftmax, true, nullptr, reinterpret_cast<const float2 *>(row_stats)};
@@ -567,7 +592,7 @@ mp_status mp_spmm_dx_norm(const mp_graph *g, int32_t mode, const float *w, const
 mp_status mp_spmm_dx_edge_grad_pair(const mp_graph *g, float *wg, const void *x,
                                     const void *dy, mp_dtype dtype, int64_t h, float *dx,
                                     void *stream) {
-    mp_status st = check_spmm(g, wg, 1, dy, dtype, h, dx, "dy", "dx");
+    mp_status st = check_spmm(g, wg, 1, dy, dtype, h, dx, "dy", "dx", 2);
     if (st != MP_OK) return st;
     const int64_t n = g->num_nodes, e = g->num_edges;
     if (!x) return fail(MP_ERR_NULL, "x is NULL");
@@ -579,8 +604,7 @@ mp_status mp_spmm_dx_edge_grad_pair(const mp_graph *g, float *wg, const void *x,
     others.add(range(x, n * h, xs, "x"));
     others.add(range(dy, n * h, xs, "dy"));
     others.add(range(dx, n * h, 4, "dx"));
-    if (const char *hit = others.overlapping(rwg))
-        return fail(MP_ERR_ALIAS, "wg overlaps %s", hit);
+    if ((st = apart(others, rwg)) != MP_OK) return st;
     if (overlap(range(dx, n * h, 4, "dx"), range(x, n * h, xs, "x")))
         return fail(MP_ERR_ALIAS, "dx overlaps x");
     if (!spmm_fused_supported(dtype, h, 1, dy, x, dx))
@@ -644,14 +668,12 @@ mp_status attention_backward_impl(const mp_graph *g, const float *alpha, int64_t
     others.add(range(dy, n * h, xs, "dy"));
     others.add(range(y, n * h, 4, "y"));
     if (!in_place) others.add(range(alpha, e * heads, 4, "alpha"));
-    if (const char *hit = others.overlapping(rdx)) return fail(MP_ERR_ALIAS, "dx overlaps %s", hit);
+    if ((st = apart(others, rdx)) != MP_OK) return st;
     if (in_place && overlap(rdx, rds)) return fail(MP_ERR_ALIAS, "dx overlaps alpha");
     others.add(rdx);
-    if (const char *hit = others.overlapping(rds))
-        return fail(MP_ERR_ALIAS, "dscores overlaps %s", hit);
+    if ((st = apart(others, rds)) != MP_OK) return st;
     others.add(rds);
-    if (const char *hit = others.overlapping(rt))
-        return fail(MP_ERR_ALIAS, "row_dot overlaps %s", hit);
+    if ((st = apart(others, rt)) != MP_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = attention_row_dot_run(y, dy, dtype, n, h, heads, row_dot, s)) != MP_OK) return st;
     const CsrView v = transpose_view(g);
@@ -706,8 +728,7 @@ mp_status mp_edge_normalize(const mp_graph *g, int32_t mode, const float *in, fl
     const Range ro = range(out, e, 4, "out"), ri = range(in, e, 4, "in");
     if (ro.lo != ri.lo && overlap(ro, ri))
         return fail(MP_ERR_ALIAS, "mp_edge_normalize: out partially overlaps in");
-    if (const char *hit = graph_ranges(g).overlapping(ro))
-        return fail(MP_ERR_ALIAS, "mp_edge_normalize: out overlaps %s", hit);
+    if ((st = apart(graph_ranges(g), ro, "mp_edge_normalize: ")) != MP_OK) return st;
     return edge_normalize_run(g, mode, in, out, static_cast<hipStream_t>(stream));
 }
 
@@ -724,11 +745,16 @@ const char *mp_status_string(mp_status s) {
         case MP_ERR_WORKSPACE: return "MP_ERR_WORKSPACE: workspace missing or too small";
         case MP_ERR_GRAPH: return "MP_ERR_GRAPH: graph not built";
         case MP_ERR_HIP: return "MP_ERR_HIP: HIP runtime error";
+        case MP_ERR_INTERNAL: return "MP_ERR_INTERNAL: internal limit of the library reached";
         default: return "unknown mp_status";
     }
 }
 
 const char *mp_last_error_detail(void) { return g_detail; }
+
+mp_status mp_set_owner_overrides(int32_t hub_min_len, int32_t hub_apart, int32_t wave_min_len) {
+    return set_owner_overrides(hub_min_len, hub_apart, wave_min_len);
+}
 
 int32_t mp_version(void) { return 100; }   // 0.1.0
 

@@ -140,10 +140,11 @@ struct NormSpec {
 
 // `heads` = K: w holds K weights per edge ([E, K], edge-major) and head q owns
 // columns [q*h/K, (q+1)*h/K) of every row (h is a multiple of K; K = 1 is the
-// scalar case).
+// scalar case).  pair: one head, the weight of edge e at w[2 e] (weights and
+// their gradients interleaved).
 mp_status spmm_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
                    mp_dtype dt, int64_t h, float *out, hipStream_t stream,
-                   const NormSpec *norm = nullptr);
+                   const NormSpec *norm = nullptr, bool pair = false);
 // The same aggregation over the transpose CSR that also writes, for every edge
 // q of owner row j, dw[order[q]] = <x_own[j, :], x[col[q], :]> (fused backward;
 // per head, dw[order[q] * K + head], when K > 1).  With row_dot (attention
@@ -154,6 +155,9 @@ mp_status spmm_run(const CsrView &csr, const float *w, int64_t heads, const void
 // (spmm_fused_supported).
 bool spmm_fused_supported(mp_dtype dt, int64_t h, int64_t heads, const void *x,
                           const void *x_own, const void *out);
+// Owner-size overrides (mp_set_owner_overrides): values <= 0 (hub_apart < 0)
+// restore the rule's choice.
+mp_status set_owner_overrides(int32_t hub_min_len, int32_t hub_apart, int32_t wave_min_len);
 // pair: w and dw are one interleaved [E][2] array (w at [e][0], dw stored to
 // [e][1]; dw points at [0][1]); one head, no row dots, no normalisation.
 mp_status spmm_fused_run(const CsrView &csr, const float *w, int64_t heads, const void *x,

@@ -41,7 +41,8 @@
 #include "common.h"
 
 #include <math.h>
-#include <stdlib.h>
+
+#include <atomic>
 
 namespace mp {
 namespace {
@@ -184,6 +185,8 @@ struct SpmmArgs {
     const int32_t *order;
     const int32_t *plan;
     const float *w;
+    int64_t w_stride;                 // floats from one edge's weight to the next: 1, or 2
+                                      // when weights and gradients are interleaved
     const void *x;                    // gathered rows (X forward, dY input gradient)
     float *y;
     const void *x_own;                // fused backward only: X, read at the owner row
@@ -323,7 +326,7 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
             } else if constexpr (kMode == kScoreGradInPlace && !kHeads) {
                 wt = a.w[o];   // likewise: the score gradient is stored over it
             } else if constexpr (!kHeads) {
-                wt = __builtin_nontemporal_load(&a.w[o]);
+                wt = __builtin_nontemporal_load(&a.w[(int64_t)o * a.w_stride]);
             }
             if constexpr (kNorm && score_mode(kMode)) {
                 // the score's softmax weight from its destination's statistics (the
@@ -624,8 +627,11 @@ __global__ __launch_bounds__(kHubBlock) void spmm_hub_kernel(SpmmArgs a) {
 }
 
 // ------------------------------------------------------------------ dispatch
-// Overrides of the owner sizes for tuning and tests: MP_HUB_MIN_LEN,
-// MP_HUB_APART (0 or 1) and MP_WAVE_MIN_LEN.
+// Owner-size overrides set through mp_set_owner_overrides (tests and tuning
+// only; none is set unless a caller asks): hub rows from this length, hub rows
+// apart (0 or 1), wave rows from this length; -1 leaves the rule's choice.
+std::atomic<int32_t> g_force_hub{-1}, g_force_apart{-1}, g_force_wave{-1};
+
 struct Overrides {
     int32_t hub_min, apart, wave_min;
 };
@@ -633,12 +639,10 @@ struct Overrides {
 Overrides overrides_for(int L) {
     Overrides o;
     const int G = kWave / L;
-    o.hub_min = -1;
-    o.apart = -1;
-    o.wave_min = G > 1 ? 4 * G : (1 << 30);
-    if (const char *s = getenv("MP_HUB_MIN_LEN")) o.hub_min = atoi(s) < 1 ? 1 : atoi(s);
-    if (const char *s = getenv("MP_HUB_APART")) o.apart = atoi(s) != 0 ? 1 : 0;
-    if (const char *s = getenv("MP_WAVE_MIN_LEN")) o.wave_min = atoi(s) < 1 ? 1 : atoi(s);
+    o.hub_min = g_force_hub.load(std::memory_order_relaxed);
+    o.apart = g_force_apart.load(std::memory_order_relaxed);
+    const int32_t wave = g_force_wave.load(std::memory_order_relaxed);
+    o.wave_min = wave > 0 ? wave : (G > 1 ? 4 * G : (1 << 30));
     return o;
 }
 
@@ -660,8 +664,9 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
     if (soft && (!norm->stats || (dw && !row_dot)))
         return fail(MP_ERR_SHAPE, "softmax weights at the fetch need statistics, and with edge "
                                   "outputs the score-gradient form");
-    if (pair && (heads != 1 || row_dot || normed || !dw))
-        return fail(MP_ERR_SHAPE, "the interleaved weight layout is for the one-head fused backward");
+    if (pair && (heads != 1 || row_dot || normed))
+        return fail(MP_ERR_SHAPE, "the interleaved weight layout takes one head, no row dots and "
+                                  "no normalisation");
     const Overrides ov = overrides_for(L);
     const int G = kWave / L;
     SpmmArgs a;
@@ -670,6 +675,7 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
     a.order = csr.order;
     a.plan = csr.plan;
     a.w = w;
+    a.w_stride = pair ? 2 : 1;
     a.x = x;
     a.y = out;
     a.x_own = x_own;
@@ -792,8 +798,9 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 }  // namespace
 
 mp_status spmm_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
-                   mp_dtype dt, int64_t h, float *out, hipStream_t s, const NormSpec *norm) {
-    return spmm_fused_run(csr, w, heads, x, dt, h, out, nullptr, nullptr, nullptr, s, norm, false);
+                   mp_dtype dt, int64_t h, float *out, hipStream_t s, const NormSpec *norm,
+                   bool pair) {
+    return spmm_fused_run(csr, w, heads, x, dt, h, out, nullptr, nullptr, nullptr, s, norm, pair);
 }
 
 // 16-byte lanes need aligned rows and heads that are whole lanes wide.
@@ -821,6 +828,15 @@ mp_status spmm_fused_run(const CsrView &csr, const float *w, int64_t heads, cons
     if (vector_lanes_ok(8, h, heads, x, x_own, out))
         return launch_lanes<uint16_t, 8>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
     return launch_lanes<uint16_t, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
+}
+
+mp_status set_owner_overrides(int32_t hub_min_len, int32_t hub_apart, int32_t wave_min_len) {
+    if (hub_apart > 1)
+        return fail(MP_ERR_SHAPE, "hub_apart %d: expected 0, 1 or a negative value", (int)hub_apart);
+    g_force_hub.store(hub_min_len > 0 ? hub_min_len : -1, std::memory_order_relaxed);
+    g_force_apart.store(hub_apart >= 0 ? hub_apart : -1, std::memory_order_relaxed);
+    g_force_wave.store(wave_min_len > 0 ? wave_min_len : -1, std::memory_order_relaxed);
+    return MP_OK;
 }
 
 }  // namespace mp

@@ -32,7 +32,10 @@
  *     exception crosses this interface.  mp_last_error_detail() returns a
  *     thread-local text describing the last non-OK status on this thread.
  *   - Determinism: for a fixed graph, H, feature dtype and device, results
- *     are bitwise reproducible (fixed reduction order, no atomics).
+ *     are bitwise reproducible (fixed reduction order, no atomics).  The one
+ *     thing outside the arguments that changes the bits is
+ *     mp_set_owner_overrides (tests and tuning only; unset by default), which
+ *     moves rows between owners and so changes their summation order.
  */
 #ifndef MP_H
 #define MP_H
@@ -57,6 +60,7 @@ typedef int32_t mp_status;
 #define MP_ERR_WORKSPACE (-8)   /* workspace missing or smaller than required         */
 #define MP_ERR_GRAPH     (-9)   /* mp_graph not produced by a successful build        */
 #define MP_ERR_HIP      (-10)   /* the HIP runtime reported an error (see detail)     */
+#define MP_ERR_INTERNAL (-11)   /* an internal limit of the library was reached (a bug) */
 
 /* Element type codes. */
 typedef int32_t mp_dtype;
@@ -258,6 +262,20 @@ mp_status mp_spmm_dx_edge_grad_pair(const mp_graph *g, float *wg, const void *x,
                                     void *stream);
 
 /*
+ * The forward aggregation Y = A_w X of mp_spmm_fwd with the weights read from
+ * the interleaved array of mp_spmm_dx_edge_grad_pair: wg[e * 2] holds w_e
+ * (COO order, "Edge order is explicit"); nothing else of wg is read.  Y is
+ * bitwise that of mp_spmm_fwd on the weights w_e.  With it, a training step
+ * keeps one [E][2] array for a parameter and its gradient: this forward, then
+ * mp_spmm_dx_edge_grad_pair, which writes dw_e into wg[e * 2 + 1].
+ *   wg     [E][2] float32 (may be NULL when E = 0).
+ *   x      [N, H] of `x_dtype` (MP_F32 or MP_BF16).   y  [N, H] float32 output.
+ * Errors as mp_spmm_fwd; y must not overlap wg, x or the graph arrays.
+ */
+mp_status mp_spmm_fwd_pair(const mp_graph *g, const float *wg, const void *x, mp_dtype x_dtype,
+                           int64_t h, float *y, void *stream);
+
+/*
  * Multi-head edge weights.  tinymesh "Weighted aggregation experiment",
  * "Limits" lists vector edge weights among what the scalar experiment leaves
  * open; these calls take the per-head reading of it.  Each edge carries
@@ -456,6 +474,26 @@ mp_status mp_spmm_dx_norm(const mp_graph *g, int32_t mode, const float *w, const
 mp_status mp_spmm_dx_edge_grad_norm(const mp_graph *g, int32_t mode, const float *w,
                                     const void *x, const void *dy, mp_dtype dtype, int64_t h,
                                     float *dx, float *dw, void *stream);
+
+/*
+ * Owner sizes of the aggregation kernels, for tests and tuning only.  Every
+ * aggregation (forward, input gradient, fused backward, and their multi-head,
+ * normalised and attention forms) hands each row to an owner -- a lane group,
+ * one wave, or a workgroup -- by a rule taken from E, the feature width and
+ * the degree classes of the graph.  These values replace the rule's results
+ * for every later call in the process:
+ *   hub_min_len   rows at least this long get a workgroup (<= 0: the rule's)
+ *   hub_apart     1: those workgroups have 16 waves and run in a launch of
+ *                 their own; 0: four waves, inside the main launch
+ *                 (< 0: the rule's; > 1 is MP_ERR_SHAPE)
+ *   wave_min_len  rows at least this long (and below hub_min_len) get one
+ *                 wave (<= 0: four lane-group steps, the default)
+ * Results stay within the same tolerance of the exact sums, but rows summed
+ * by other owners round differently, so bits are reproducible only for the
+ * same overrides.  mp_set_owner_overrides(-1, -1, -1) restores the rule.  The
+ * setting is process-wide; set it while no compute call is being enqueued.
+ */
+mp_status mp_set_owner_overrides(int32_t hub_min_len, int32_t hub_apart, int32_t wave_min_len);
 
 /* Static text for a status code. */
 const char *mp_status_string(mp_status status);

@@ -11,6 +11,9 @@ Comparison rules:
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -88,3 +91,72 @@ def check_floats(wl, y, dx, dw, tau=None):
     rdw, sdw = oracle.edge_grad(wl.src, wl.dst, wl.x, wl.dy)
     return (check_close("Y", y, ry, sy, tau), check_close("dX", dx, rdx, sdx, tau),
             check_close("dw", dw, rdw, sdw, tau))
+
+
+def oracle_threads() -> int:
+    """Threads for oracle work: the host cores this process may use, at most 16."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return max(1, min(16, cores))
+
+
+def ratios(got, ref, s):
+    """|got - ref| / S elementwise (0 where S = 0), after checking that every
+    element with no terms is exactly 0."""
+    err = np.abs(got.astype(np.float64) - ref)
+    zero = s == 0
+    if np.any(got[zero] != 0):
+        raise AssertionError(f"{int(np.sum(got[zero] != 0))} elements with no terms are not 0")
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.where(zero, 0.0, err / np.where(zero, 1.0, s))
+
+
+def check_all_rows(name, got, n, rows_fn, taus, chunks=None):
+    """Compare every row of `got` ([n, H], numpy) with the oracle, whose rows are
+    evaluated by rows_fn(rows) -> (ref, S) in strided row sets on several threads
+    (the oracle's C calls release the GIL; strided sets spread the long rows of
+    skewed graphs).  Raises at the first bound exceeded; returns the worst
+    |err|/S."""
+    t = oracle_threads()
+    c = chunks or 4 * t
+
+    def one(i):
+        rows = np.arange(i, n, c, dtype=np.int64)
+        ref, s = rows_fn(rows)
+        r = ratios(got[rows], ref, s)
+        return float(r.max()) if r.size else 0.0, i
+
+    with ThreadPoolExecutor(t) as ex:
+        res = list(ex.map(one, range(c)))
+    worst, at = max(res)
+    for tau in taus:
+        if worst > tau:
+            raise AssertionError(f"{name}: max |err|/S = {worst:.3e} > {tau:g} (row set {at} of {c})")
+    return worst
+
+
+def check_all_edges(name, got, e, edges_fn, taus, chunks=None):
+    """The same for an edge output ([E], numpy): edges_fn(lo, hi) -> (ref, S) for
+    the COO range [lo, hi)."""
+    t = oracle_threads()
+    c = chunks or 4 * t
+    bounds = np.linspace(0, e, c + 1).astype(np.int64)
+
+    def one(i):
+        lo, hi = int(bounds[i]), int(bounds[i + 1])
+        if hi == lo:
+            return 0.0, i
+        ref, s = edges_fn(lo, hi)
+        r = ratios(got[lo:hi], ref, s)
+        return float(r.max()), i
+
+    with ThreadPoolExecutor(t) as ex:
+        res = list(ex.map(one, range(c)))
+    worst, at = max(res)
+    for tau in taus:
+        if worst > tau:
+            raise AssertionError(f"{name}: max |err|/S = {worst:.3e} > {tau:g} "
+                                 f"(edges {bounds[at]}..{bounds[at + 1]})")
+    return worst

@@ -30,6 +30,14 @@ def mp():
     return gnn_sparse_message_amd
 
 
+@pytest.fixture(autouse=True)
+def _owner_rule_after_each_test():
+    """Tests that set owner overrides leave the rule in place for the next."""
+    yield
+    import gnn_sparse_message_amd
+    gnn_sparse_message_amd.mp_set_owner_overrides(-1, -1, -1)
+
+
 def _lanes(deg):
     return np.where(deg < 64, 1, np.where(deg < 4096, 64, 256))
 
@@ -516,8 +524,7 @@ def _fwd_softmax_cases():
     yield "random_f32_h7", synth.random_graph(300, 4000, 7, 64), {}              # scalar lanes
     yield "random_f32_h300", synth.random_graph(300, 4000, 300, 65), {}          # column blocks
     yield "power_law", _power_law(66), {}
-    yield "power_law_four_wave_hubs", _power_law(67), {"MP_HUB_APART": "0",
-                                                        "MP_HUB_MIN_LEN": "4096"}
+    yield "power_law_four_wave_hubs", _power_law(67), {"hub_apart": 0, "hub_min_len": 4096}
     yield "rmat16", synth.rmat16(), {}                                          # 16-wave hubs
 
 
@@ -526,15 +533,14 @@ def _power_law(seed):
 
 
 @pytest.mark.parametrize("idx", range(9))
-def test_fwd_softmax_equals_softmax_then_forward(mp, idx, monkeypatch):
+def test_fwd_softmax_equals_softmax_then_forward(mp, idx):
     """mp_spmm_fwd_softmax (alpha formed at the fetch, never written) against
     mp_edge_softmax followed by mp_spmm_fwd on its alpha: Y and the row
     statistics bit for bit, on synchronously and asynchronously built graphs;
     that alpha against the oracle's softmax and Y against the oracle's
     aggregation with it."""
     name, wl, env = list(_fwd_softmax_cases())[idx]
-    for k, v in env.items():
-        monkeypatch.setenv(k, v)
+    mp.mp_set_owner_overrides(**env)   # the module's fixture restores the rule
     print(f"case {name}: N={wl.n} E={wl.e} H={wl.h} {wl.feat_dtype}", flush=True)
     t = upload(wl, DEV)
     scores = torch.from_numpy(wl.w).to(DEV)
@@ -572,15 +578,14 @@ def test_fwd_softmax_rejections(mp):
 
 
 @pytest.mark.parametrize("idx", [0, 1, 2, 3, 4, 6, 7, 8])
-def test_attention_backward_scores_equals_alpha_form(mp, idx, monkeypatch):
+def test_attention_backward_scores_equals_alpha_form(mp, idx):
     """mp_attention_backward_scores (alpha formed in the transpose walk from the
     scores and the destinations' statistics) against mp_attention_backward
     given alpha from mp_edge_softmax: dX, the score gradients and the row dots
     bit for bit, on both build forms, and with the score gradients written
     over the scores."""
     name, wl, env = list(_fwd_softmax_cases())[idx]
-    for k, v in env.items():
-        monkeypatch.setenv(k, v)
+    mp.mp_set_owner_overrides(**env)   # the module's fixture restores the rule
     print(f"case {name}: N={wl.n} E={wl.e} H={wl.h} {wl.feat_dtype}", flush=True)
     t = upload(wl, DEV)
     scores = torch.from_numpy(wl.w).to(DEV)

@@ -1,7 +1,9 @@
-"""The fused backward with weights and gradients interleaved
-(mp_spmm_dx_edge_grad_pair): dX and dw bit for bit equal to the two-array call
-(itself held to the oracle by the parity tests), the weight half of the array
-left as it was, on an asynchronously built graph as well, and its rejections."""
+"""The calls on weights and gradients interleaved in one [E][2] array: the
+fused backward (mp_spmm_dx_edge_grad_pair) with dX and dw bit for bit equal to
+the two-array call, and the forward (mp_spmm_fwd_pair) bit for bit equal to
+mp_spmm_fwd (both held to the oracle by the parity tests), the weight half of
+the array left as it was, on an asynchronously built graph as well, and their
+rejections; wide rows (column blocks) for the forward."""
 import numpy as np
 import pytest
 import torch
@@ -53,6 +55,26 @@ def test_pair_equals_two_arrays(mp, idx):
     assert torch.equal(dx, rdx)
     assert torch.equal(wg[:, 1], rdw)
     assert torch.equal(wg[:, 0], t["w"])                  # the weights are not written
+    y = mp.mp_spmm_fwd_pair(g, wg, t["x"])
+    ry = mp.mp_spmm_fwd(g, t["w"], t["x"])
+    torch.cuda.synchronize()
+    assert torch.equal(y, ry)
+
+
+@pytest.mark.parametrize("h", [7, 300, 600])
+def test_pair_forward_wide_and_scalar_rows(mp, h):
+    """Scalar lanes (H = 7) and column blocks (H = 300, 600) read the weights
+    at the same stride."""
+    wl = synth.random_graph(400, 5000, h, 90 + h)
+    t = upload(wl, DEV)
+    for g in (mp.mp_graph_build(t["src"], t["dst"], wl.n),
+              mp.mp_graph_build_async(t["src"], t["dst"], wl.n)):
+        wg = _pair(t, wl)
+        y = mp.mp_spmm_fwd_pair(g, wg, t["x"])
+        ry = mp.mp_spmm_fwd(g, t["w"], t["x"])
+        torch.cuda.synchronize()
+        assert torch.equal(y, ry)
+    check_close("Y", y, *oracle.forward(wl.n, wl.src, wl.dst, wl.w, wl.x), TAU["f32"])
 
 
 def test_pair_against_oracle(mp):
@@ -94,6 +116,12 @@ def test_pair_rejections(mp):
         wv = big[:wl.e * 2].view(wl.e, 2)
         mp.mp_spmm_dx_edge_grad_pair(g, wv, t["x"], t["dy"],
                                      out_dx=big[wl.e:wl.e + wl.n * 8].view(wl.n, 8))
+    with pytest.raises(ValueError):                   # the forward's output inside wg
+        big = torch.empty((wl.n * 8 + wl.e * 2,), device=DEV)
+        wv = big[:wl.e * 2].view(wl.e, 2)
+        mp.mp_spmm_fwd_pair(g, wv, t["x"], out=big[wl.e:wl.e + wl.n * 8].view(wl.n, 8))
+    with pytest.raises(ValueError):
+        mp.mp_spmm_fwd_pair(g, t["w"], t["x"])
     wide = synth.random_graph(100, 500, 600, 81)      # beyond one column block
     tw = upload(wide, DEV)
     gw = mp.mp_graph_build(tw["src"], tw["dst"], wide.n)

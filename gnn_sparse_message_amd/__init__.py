@@ -28,6 +28,7 @@ import torch  # noqa: F401  -- loaded first so libmp.so binds to torch's HIP run
 
 __all__ = [
     "Graph", "MpError", "mp_graph_build", "mp_graph_build_async", "mp_graph_finish",
+    "mp_graph_build_noalloc", "STATIC_WORKSPACE_BYTES",
     "mp_graph_build_workspace_size", "mp_spmm_fwd",
     "mp_spmm_dx", "mp_edge_grad_dw", "mp_spmm_dx_edge_grad", "mp_spmm_fwd_heads",
     "mp_spmm_dx_heads", "mp_edge_grad_dw_heads", "mp_spmm_dx_edge_grad_heads", "mp_edge_softmax",
@@ -52,6 +53,7 @@ MP_NORM_MEAN, MP_NORM_SYM = 1, 2
 GRAPH_INFO_WORDS = 576
 GRAPH_BUILT, GRAPH_ON_DEVICE = 0x6d705f6772617068, 0x6d705f6465766963
 NUM_CLASSES = 33
+STATIC_WORKSPACE_BYTES = 64 << 20   # MP_STATIC_WORKSPACE_BYTES
 
 _DTYPE = {torch.int32: MP_I32, torch.int64: MP_I64, torch.float32: MP_F32,
           torch.bfloat16: MP_BF16}
@@ -111,6 +113,7 @@ def _load():
         "mp_graph_build": (i32, [vp, vp, i32, i64, i64, gp, vp, sz, vp]),
         "mp_graph_build_async": (i32, [vp, vp, i32, i64, i64, gp, vp, sz, vp]),
         "mp_graph_finish": (i32, [gp, vp]),
+        "mp_graph_build_noalloc": (i32, [vp, vp, i32, i64, i64, gp, vp]),
         "mp_spmm_fwd": (i32, [gp, vp, vp, i32, i64, vp, vp]),
         "mp_spmm_dx": (i32, [gp, vp, vp, i32, i64, vp, vp]),
         "mp_edge_grad_dw": (i32, [gp, vp, vp, i32, i64, vp, vp]),
@@ -324,6 +327,24 @@ def mp_graph_build_async(src, dst, num_nodes: int, workspace=None) -> Graph:
     several streams need their own workspaces (mp_graph_build_workspace_size)."""
     return _build_graph(_lib.mp_graph_build_async, "mp_graph_build_async", src, dst, num_nodes,
                   workspace)
+
+
+def mp_graph_build_noalloc(src, dst, num_nodes: int) -> Graph:
+    """mp_graph_build_async with the library's static per-GPU workspace
+    (MP_STATIC_WORKSPACE_BYTES) instead of a workspace argument: the C call
+    allocates nothing.  This wrapper allocates only the graph's own arrays (the
+    call's outputs), before the call.  Builds whose work overlaps on one GPU
+    (other streams, other threads) race on that workspace."""
+    _need_tensor("src", src)
+    _need_tensor("dst", dst)
+    if src.dim() != 1 or dst.dim() != 1 or src.shape[0] != dst.shape[0]:
+        raise ValueError("src and dst must be 1-D with the same length")
+    e = int(src.shape[0])
+    g = Graph(num_nodes, e, src.device)
+    _check(_lib.mp_graph_build_noalloc(_ptr(src) if e else None, _ptr(dst) if e else None,
+                                       _code(src), int(num_nodes), e, ctypes.byref(g._desc),
+                                       _stream(src)), "mp_graph_build_noalloc")
+    return g
 
 
 def mp_graph_finish(g: Graph, stream=None) -> Graph:

@@ -316,9 +316,10 @@ mp_status mp_graph_build_workspace_size(int64_t num_nodes, int64_t num_edges, si
 
 namespace mp {
 namespace {
+// static_ws: the workspace is this device's static array (mp_graph_build_noalloc).
 mp_status build_impl(const void *src, const void *dst, mp_dtype idx_dtype, int64_t num_nodes,
                      int64_t num_edges, mp_graph *g, void *workspace, size_t workspace_bytes,
-                     void *stream, bool async) {
+                     void *stream, bool async, bool static_ws = false) {
     if (!g) return fail(MP_ERR_NULL, "graph descriptor is NULL");
     g->built = 0;
     mp_status st = check_sizes(num_nodes, num_edges);
@@ -344,6 +345,11 @@ mp_status build_impl(const void *src, const void *dst, mp_dtype idx_dtype, int64
         if (a.p && !aligned(a.p, 4)) return fail(MP_ERR_ALIGN, "%s not aligned to 4 bytes", a.name);
     }
     const size_t need = lower_layout(n, e).total;
+    if (static_ws && need > workspace_bytes)
+        return fail(MP_ERR_WORKSPACE,
+                    "N = %lld, E = %lld need %zu bytes of workspace; the static workspace of "
+                    "mp_graph_build_noalloc holds %zu", (long long)n, (long long)e, need,
+                    workspace_bytes);
     if (!workspace) return fail(MP_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
     if (workspace_bytes < need)
         return fail(MP_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
@@ -357,7 +363,7 @@ mp_status build_impl(const void *src, const void *dst, mp_dtype idx_dtype, int64
     }
     for (const auto &a : arrays)
         if (a.count > 0 && (st = check_device(a.p, a.name)) != MP_OK) return st;
-    if ((st = check_device(workspace, "workspace")) != MP_OK) return st;
+    if (!static_ws && (st = check_device(workspace, "workspace")) != MP_OK) return st;
 
     // Outputs (graph arrays, workspace) must not overlap each other or the inputs.
     g->num_nodes = n;
@@ -400,6 +406,19 @@ mp_status mp_graph_build_async(const void *src, const void *dst, mp_dtype idx_dt
                                void *workspace, size_t workspace_bytes, void *stream) {
     return build_impl(src, dst, idx_dtype, num_nodes, num_edges, g, workspace, workspace_bytes,
                       stream, true);
+}
+
+mp_status mp_graph_build_noalloc(const void *src, const void *dst, mp_dtype idx_dtype,
+                                 int64_t num_nodes, int64_t num_edges, mp_graph *g,
+                                 void *stream) {
+    if (!g) return fail(MP_ERR_NULL, "graph descriptor is NULL");
+    g->built = 0;
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    mp_status st = static_workspace(&ws, &ws_bytes);
+    if (st != MP_OK) return st;
+    return build_impl(src, dst, idx_dtype, num_nodes, num_edges, g, ws, ws_bytes, stream, true,
+                      true);
 }
 
 mp_status mp_graph_finish(mp_graph *g, void *stream) {

@@ -53,6 +53,10 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
                     mp_graph *g, void *ws, hipStream_t stream, bool async, int *bad_index);
 // Copy the class counts and the index flag of g->info to the host (synchronous).
 mp_status lower_read_info(mp_graph *g, hipStream_t stream, int *bad_index);
+// This device's static lowering workspace (MP_STATIC_WORKSPACE_BYTES, shared
+// by every mp_graph_build_noalloc on the device): its device address, looked up
+// on the first call on each device.
+mp_status static_workspace(void **ptr, size_t *bytes);
 
 // Rows whose length is >= len, from class counts: classes are sorted high to
 // low in the plan, and a class counts only if all its rows qualify (2^(c-1) >= len).

@@ -27,6 +27,14 @@
 // then delimited by a binary search per row over the sorted keys.
 #include "common.h"
 
+#include <mutex>
+
+// The lowering's workspace for mp_graph_build_noalloc, whose callers cannot
+// allocate device memory: one array per GPU, held until the process ends.
+// Host code never passes its name to a kernel (on the host the name is only a
+// stand-in); it takes the device address from static_workspace() below.
+static __device__ __align__(256) unsigned char scratch[MP_STATIC_WORKSPACE_BYTES];
+
 namespace mp {
 namespace {
 
@@ -733,6 +741,30 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
         return MP_OK;
     }
     return lower_read_info(g, s, bad_index);
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch[kMaxDevices] = {};   // device address of `scratch` on each GPU
+}  // namespace
+
+mp_status static_workspace(void **ptr, size_t *bytes) {
+    int dev = -1;
+    MP_HIP_CHECK(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MP_ERR_DEVICE, "device %d beyond the %d the static workspace serves", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch[dev]) {   // first use on this device, with it current
+        void *p = nullptr;
+        MP_HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)),
+                     "address of the static workspace");
+        g_scratch[dev] = p;
+    }
+    *ptr = g_scratch[dev];
+    *bytes = sizeof(scratch);
+    return MP_OK;
 }
 
 }  // namespace mp

@@ -184,6 +184,32 @@ mp_status mp_graph_build_async(const void *src, const void *dst, mp_dtype idx_dt
                                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * mp_graph_build_async without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The lowering's scratch is a static array
+ * of MP_STATIC_WORKSPACE_BYTES in the library's device code, one per GPU the
+ * library runs on, held until the process ends; this call allocates nothing
+ * and calls no allocating routine.  The caller still allocates the graph
+ * arrays (see mp_graph) and the inputs.
+ *   Sizes: N and E whose mp_graph_build_workspace_size is at most
+ *   MP_STATIC_WORKSPACE_BYTES (about 1.9 million edges when N <= E); larger
+ *   ones return MP_ERR_WORKSPACE and launch nothing.
+ *   Sharing: every call on one GPU uses that GPU's one array, and the work it
+ *   enqueues is in flight until the stream reaches it.  Calls whose work
+ *   overlaps on one GPU (enqueued on different streams without ordering, or
+ *   from several threads) race on the array and corrupt each other's graphs;
+ *   calls on one stream, or ordered by events, are safe.  The array's contents
+ *   on entry are ignored (everything the lowering reads is written first).
+ * Arguments, validation, results (bit for bit those of mp_graph_build) and
+ * completion (mp_graph_finish, or compute calls reading the device record)
+ * are those of mp_graph_build_async.
+ */
+#define MP_STATIC_WORKSPACE_BYTES 67108864u   /* 64 MiB */
+mp_status mp_graph_build_noalloc(const void *src, const void *dst, mp_dtype idx_dtype,
+                                 int64_t num_nodes, int64_t num_edges, mp_graph *g,
+                                 void *stream);
+
+/*
  * Complete an asynchronous build: synchronise `stream`, copy the class counts
  * from g->info into the descriptor and check the endpoints.  Returns MP_OK and
  * sets g->built = MP_GRAPH_BUILT, or MP_ERR_INDEX (and g->built = 0) when an

@@ -71,6 +71,15 @@ int main(int argc, char **argv) {
 
     VALID(mp_graph_build(src, dst, MP_I64, n, e, &g, ws, ws_bytes, nullptr));
     VALID(mp_graph_build_async(src, dst, MP_I64, n, e, &g, ws, ws_bytes, nullptr));
+    VALID(mp_graph_build_noalloc(src, dst, MP_I64, n, e, &g, nullptr));
+    {   // too large for the static workspace: refused before any range list
+        const int b = g_launches;
+        mp_graph big = g;
+        big.num_edges = 5000000;
+        expect("mp_graph_build_noalloc (too large)",
+               mp_graph_build_noalloc(src, dst, MP_I64, n, 5000000, &big, nullptr),
+               MP_ERR_WORKSPACE, b);
+    }
     // the workspace over a graph array
     ALIAS(mp_graph_build(src, dst, MP_I64, n, e, &g, g.col, ws_bytes, nullptr));
     g.built = MP_GRAPH_BUILT;

@@ -43,14 +43,28 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E peak, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-# Sources that define each counted kernel: its recorded counter bytes stand only
-# while these files are unchanged.
-KERNEL_SOURCES = {
-    "spmm_kernel": ["gnn_sparse_message_amd/csrc/spmm.hip", "gnn_sparse_message_amd/csrc/common.h"],
-    "sddmm_kernel": ["gnn_sparse_message_amd/csrc/sddmm.hip",
-                     "gnn_sparse_message_amd/csrc/common.h"],
-    "lowering": ["gnn_sparse_message_amd/csrc/lower.hip", "gnn_sparse_message_amd/csrc/common.h"],
+# Sources that define the kernels of each profiled op: its recorded counter
+# bytes stand only while these files' code is unchanged.
+_SPMM = ["gnn_sparse_message_amd/csrc/spmm.hip", "gnn_sparse_message_amd/csrc/common.h"]
+_SOFTMAX = ["gnn_sparse_message_amd/csrc/softmax.hip"] + _SPMM
+OP_SOURCES = {
+    "build": ["gnn_sparse_message_amd/csrc/lower.hip", "gnn_sparse_message_amd/csrc/common.h"],
+    "fwd_pair": _SPMM, "bwd_pair": _SPMM, "fwd": _SPMM, "bwd": _SPMM, "dx": _SPMM,
+    "dw": ["gnn_sparse_message_amd/csrc/sddmm.hip", "gnn_sparse_message_amd/csrc/common.h"],
+    "edge_softmax": _SOFTMAX, "edge_softmax_backward": _SOFTMAX,
+    "edge_normalize_sym": ["gnn_sparse_message_amd/csrc/normalize.hip",
+                           "gnn_sparse_message_amd/csrc/common.h"],
+    "attention_forward": _SOFTMAX, "fwd_norm_sym": _SPMM, "bwd_norm_sym": _SPMM,
+    "fwd_heads": _SPMM, "bwd_heads": _SPMM,
+    "attention_backward": ["gnn_sparse_message_amd/csrc/attention.hip"] + _SPMM,
+    "attention_backward_in_place": ["gnn_sparse_message_amd/csrc/attention.hip"] + _SPMM,
+    "copy_calibration": [],
 }
+# The ops of the counter runs (bench.py --profile-ops), in launch order; each is
+# preceded by one marker kernel (a fill of a small int8 tensor, a kernel nothing
+# else here launches), so every dispatch between two markers belongs to one op.
+PROFILE_OPS = tuple(OP_SOURCES)
+MARKER_KERNEL = "FillFunctor<signed char>"
 
 
 def log(*a):
@@ -78,29 +92,29 @@ def _code_only(text):
     return re.sub(r"\s+", " ", text).strip()
 
 
-def kernel_source_hash(kernel):
-    """Hash of the code (comments left out) of the source files that define
-    `kernel` (a key of KERNEL_SOURCES)."""
+def op_source_hash(op):
+    """Hash of the code (comments left out) of the source files that define the
+    kernels of `op` (a key of OP_SOURCES)."""
     hsh = hashlib.sha256()
-    for rel in KERNEL_SOURCES[kernel]:
+    for rel in OP_SOURCES[op]:
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
             hsh.update(_code_only(f.read()).encode())
     return hsh.hexdigest()[:16]
 
 
-def measured_traffic(kernel_key):
-    """HBM bytes per launch ("kernel:use" key) from the committed counter
-    summary, or None when that kernel's sources changed since the counters were
-    taken."""
+def measured_traffic(op):
+    """Calibrated HBM bytes of one call of `op` from the committed counter
+    summary, or None when the sources of its kernels changed since the counters
+    were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    k = rec.get("kernels", {}).get(kernel_key)
-    if k is None or k.get("source_hash") != kernel_source_hash(kernel_key.split(":")[0]):
+    k = rec.get("ops", {}).get(op)
+    if k is None or k.get("source_hash") != op_source_hash(op):
         return None
-    return k.get("hbm_bytes_per_launch")
+    return k.get("hbm_bytes_per_call")
 
 
 def cpu_baseline_all_cores(wl):
@@ -351,6 +365,221 @@ def minibatch_bench(mp, torch, dev, n_batches=64, h=256):
     return res
 
 
+# rocprofv3 commands whose output --summarize-profiles reads (run from the
+# repository root on the GPU machine; <repo> is its absolute path).
+PROFILE_COMMANDS = {
+    "trace": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
+             "-d <repo>/gpurun_out/p_trace -o run -- python3 <repo>/bench.py --steps 5 "
+             "--warmup 2 --no-cpu-baseline --no-minibatch --no-other-configs",
+    "fetch": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc FETCH_SIZE --output-format csv "
+             "-d <repo>/gpurun_out/p_fetch -o run -- python3 <repo>/bench.py --profile-ops",
+    "write": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc WRITE_SIZE --output-format csv "
+             "-d <repo>/gpurun_out/p_write -o run -- python3 <repo>/bench.py --profile-ops",
+    "l2": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv "
+          "-d <repo>/gpurun_out/p_l2 -o run -- python3 <repo>/bench.py --profile-ops",
+    "summary": "python3 bench.py --summarize-profiles gpurun_out",
+}
+
+
+def run_profile_ops(mp, torch, dev, src, dst, w, x, dy, n, e, h):
+    """Each op of PROFILE_OPS once after a warm-up of all of them, each preceded
+    by a marker kernel, for the counter runs.  Returns the op names in order."""
+    y = torch.empty((n, h), dtype=torch.float32, device=dev)
+    dx = torch.empty_like(y)
+    dw = torch.empty(e, dtype=torch.float32, device=dev)
+    wg = torch.empty((e, 2), dtype=torch.float32, device=dev)
+    wg[:, 0] = w
+    g = mp.mp_graph_build(src, dst, n)
+    alpha = torch.empty_like(w)
+    rstats = torch.empty((n, 2), dtype=torch.float32, device=dev)
+    dscores = torch.empty_like(w)
+    rdot = torch.empty(n, dtype=torch.float32, device=dev)
+    wn = torch.empty_like(w)
+    a_buf = w.clone()
+    heads = 4
+    wk = torch.empty((e, heads), device=dev).uniform_(
+        -1.0, 1.0, generator=torch.Generator(device=dev).manual_seed(7))
+    dwk = torch.empty((e, heads), dtype=torch.float32, device=dev)
+    ca = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cb = torch.empty_like(ca)
+    marker = torch.empty(64, dtype=torch.int8, device=dev)
+    ops = {
+        "build": lambda: mp.mp_graph_build(src, dst, n),
+        "fwd_pair": lambda: mp.mp_spmm_fwd_pair(g, wg, x, out=y),
+        "bwd_pair": lambda: mp.mp_spmm_dx_edge_grad_pair(g, wg, x, dy, out_dx=dx),
+        "fwd": lambda: mp.mp_spmm_fwd(g, w, x, out=y),
+        "bwd": lambda: mp.mp_spmm_dx_edge_grad(g, w, x, dy, out_dx=dx, out_dw=dw),
+        "dx": lambda: mp.mp_spmm_dx(g, w, dy, out=dx),
+        "dw": lambda: mp.mp_edge_grad_dw(g, x, dy, out=dw),
+        "edge_softmax": lambda: mp.mp_edge_softmax(g, w, alpha, rstats),
+        "edge_softmax_backward": lambda: mp.mp_edge_softmax_backward(g, alpha, dw, dscores, rdot),
+        "edge_normalize_sym": lambda: mp.mp_edge_normalize(g, mp.MP_NORM_SYM, w, out=wn),
+        "attention_forward": lambda: mp.mp_spmm_fwd_softmax(g, w, x, out=y, out_row_stats=rstats),
+        "fwd_norm_sym": lambda: mp.mp_spmm_fwd_norm(g, mp.MP_NORM_SYM, w, x, out=y),
+        "bwd_norm_sym": lambda: mp.mp_spmm_dx_edge_grad_norm(g, mp.MP_NORM_SYM, w, x, dy,
+                                                             out_dx=dx, out_dw=dw),
+        "fwd_heads": lambda: mp.mp_spmm_fwd_heads(g, wk, x, out=y),
+        "bwd_heads": lambda: mp.mp_spmm_dx_edge_grad_heads(g, wk, x, dy, out_dx=dx, out_dw=dwk),
+        "attention_backward": lambda: mp.mp_attention_backward(
+            g, w, x, dy, y, out_dx=dx, out_dscores=dscores, out_row_dot=rdot),
+        "attention_backward_in_place": lambda: mp.mp_attention_backward(
+            g, a_buf, x, dy, y, out_dx=dx, out_dscores=a_buf, out_row_dot=rdot),
+        "copy_calibration": lambda: torch.mul(ca, 1.0, out=cb),
+    }
+    assert tuple(ops) == PROFILE_OPS
+    for fn in ops.values():
+        fn()
+    torch.cuda.synchronize()
+    for name, fn in ops.items():
+        marker.fill_(1)
+        fn()
+        torch.cuda.synchronize()
+        log(f"profiled {name}")
+    return list(ops)
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _short_name(name):
+    name = name.replace("mp::(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    depth, out = 0, []
+    for ch in name:     # drop the argument list, keep template arguments
+        if ch == "(" and depth == 0:
+            break
+        depth += ch == "<"
+        depth -= ch == ">"
+        out.append(ch)
+    return "".join(out)
+
+
+def _per_op_counters(path, counters):
+    """{op: {counter: summed value, "kernels": {short name: dispatches}}} from a
+    counter-collection CSV of a --profile-ops run: the dispatches between one
+    marker and the next belong to one op."""
+    rows = _read_csv(path)
+    by_id = {}
+    for r in rows:
+        d = by_id.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    ids = sorted(by_id)
+    marks = [i for i in ids if MARKER_KERNEL in by_id[i]["name"]]
+    if len(marks) != len(PROFILE_OPS):
+        raise SystemExit(f"{path}: {len(marks)} markers, expected {len(PROFILE_OPS)}")
+    out = {}
+    for k, op in enumerate(PROFILE_OPS):
+        lo = marks[k]
+        hi = marks[k + 1] if k + 1 < len(marks) else ids[-1] + 1
+        rec = {c: 0.0 for c in counters}
+        rec["kernels"] = {}
+        for i in ids:
+            if lo < i < hi:
+                for c in counters:
+                    rec[c] += by_id[i].get(c, 0.0)
+                nm = _short_name(by_id[i]["name"])
+                rec["kernels"][nm] = rec["kernels"].get(nm, 0) + 1
+        out[op] = rec
+    return out
+
+
+def summarize_profiles(base):
+    """Write profiles/kernel_trace_chung_lu_step.md, profiles/hbm_counters_chung_lu_step.md,
+    profiles/l2_hit_rates_chung_lu_step.md and profiles/traffic.json from the
+    rocprofv3 output directories p_trace, p_fetch, p_write and p_l2 under `base`
+    (the commands of PROFILE_COMMANDS)."""
+    prof = os.path.join(ROOT, "profiles")
+    cmds = "\n".join(PROFILE_COMMANDS[k] for k in ("fetch", "write"))
+    # kernel durations
+    stats = _read_csv(os.path.join(base, "p_trace", "run_kernel_stats.csv"))
+    lines = ["# Kernel trace: power-law workload (N=2,000,000, E=100,000,000, H=128 bf16), "
+             "one step = build + forward + fused backward", "",
+             "Command (run from the repository root on the GPU box):", "", "```",
+             PROFILE_COMMANDS["trace"], "```", "",
+             "Summary from rocprofv3's own `run_kernel_stats.csv` (7 steps on the interleaved "
+             "weights, then 7 on two arrays, then each standalone call of the benchmark; "
+             "kernels of one template share a line):", "",
+             "| kernel | calls | avg us | min us | max us | % of GPU time |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for r in stats:
+        lines.append(f"| `{_short_name(r['Name'])}` | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
+    lines += ["", "Generated by `" + PROFILE_COMMANDS["summary"] + "`.", ""]
+    with open(os.path.join(prof, "kernel_trace_chung_lu_step.md"), "w") as f:
+        f.write("\n".join(lines))
+    # HBM bytes per op
+    fetch = _per_op_counters(os.path.join(base, "p_fetch", "run_counter_collection.csv"),
+                             ["FETCH_SIZE"])
+    write = _per_op_counters(os.path.join(base, "p_write", "run_counter_collection.csv"),
+                             ["WRITE_SIZE"])
+    gib_kib = float(1 << 20)
+    cal_f = gib_kib / fetch["copy_calibration"]["FETCH_SIZE"]
+    cal_w = gib_kib / write["copy_calibration"]["WRITE_SIZE"]
+    rec = {"calibration": {"kernel": "torch elementwise x*1.0, 1 GiB read + 1 GiB written",
+                           "FETCH_SIZE_KiB": fetch["copy_calibration"]["FETCH_SIZE"],
+                           "WRITE_SIZE_KiB": write["copy_calibration"]["WRITE_SIZE"],
+                           "fetch_factor": round(cal_f, 4), "write_factor": round(cal_w, 4)},
+           "commands": [PROFILE_COMMANDS[k] for k in ("fetch", "write")], "ops": {}}
+    lines = ["# HBM byte counters per call: power-law workload (N=2,000,000, E=100,000,000, "
+             "H=128 bf16)", "",
+             "Two runs, one counter each (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), of "
+             "`bench.py --profile-ops` (every op once, each after a marker kernel):", "", "```",
+             cmds, "```", "",
+             f"Calibration: a plain elementwise copy of 1 GiB (1 GiB read, 1 GiB written) reads "
+             f"FETCH_SIZE = {fetch['copy_calibration']['FETCH_SIZE']:.0f} KiB and WRITE_SIZE = "
+             f"{write['copy_calibration']['WRITE_SIZE']:.0f} KiB, so bytes = FETCH_SIZE x 1024 x "
+             f"{cal_f:.3f} and WRITE_SIZE x 1024 x {cal_w:.3f}.  FETCH_SIZE counts L2 misses, "
+             "whichever of the Infinity Cache and HBM serves them.", "",
+             "| op | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | GB read | GB written | "
+             "GB total |", "|---|---:|---:|---:|---:|---:|---:|"]
+    for op in PROFILE_OPS:
+        if op == "copy_calibration":
+            continue
+        fk, wk = fetch[op]["FETCH_SIZE"], write[op]["WRITE_SIZE"]
+        rb, wb = fk * 1024 * cal_f, wk * 1024 * cal_w
+        nd = sum(fetch[op]["kernels"].values())
+        rec["ops"][op] = {"hbm_bytes_per_call": int(round(rb + wb)), "read_bytes": int(round(rb)),
+                          "write_bytes": int(round(wb)), "fetch_KiB": fk, "write_KiB": wk,
+                          "dispatches": nd, "kernels": fetch[op]["kernels"],
+                          "source_hash": op_source_hash(op)}
+        lines.append(f"| {op} | {nd} | {fk:.0f} | {wk:.0f} | {rb / 1e9:.3f} | {wb / 1e9:.3f} | "
+                     f"{(rb + wb) / 1e9:.3f} |")
+    lines += ["", "Kernels of each op:", ""]
+    for op in PROFILE_OPS:
+        if op != "copy_calibration":
+            ks = ", ".join(f"`{k}` x{v}" for k, v in fetch[op]["kernels"].items())
+            lines.append(f"- {op}: {ks}")
+    lines += ["", "`profiles/traffic.json` holds the same figures with a hash of the code of "
+              "each op's source files; bench.py reports an op's traffic only while that hash "
+              "matches.", "", "Generated by `" + PROFILE_COMMANDS["summary"] + "`.", ""]
+    with open(os.path.join(prof, "hbm_counters_chung_lu_step.md"), "w") as f:
+        f.write("\n".join(lines))
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    # L2 hit rates per op
+    l2_csv = os.path.join(base, "p_l2", "run_counter_collection.csv")
+    if os.path.exists(l2_csv):
+        l2 = _per_op_counters(l2_csv, ["TCC_HIT_sum", "TCC_MISS_sum"])
+        lines = ["# L2 hits and misses per call: power-law workload (N=2,000,000, "
+                 "E=100,000,000, H=128 bf16)", "", "```", PROFILE_COMMANDS["l2"], "```", "",
+                 "| op | L2 hits | L2 misses | hit rate |", "|---|---:|---:|---:|"]
+        for op in PROFILE_OPS:
+            hit, miss = l2[op]["TCC_HIT_sum"], l2[op]["TCC_MISS_sum"]
+            rate = hit / (hit + miss) if hit + miss else 0.0
+            lines.append(f"| {op} | {hit:.4g} | {miss:.4g} | {rate:.3f} |")
+        lines += ["", "Source hashes of the code these figures were taken with: " +
+                  ", ".join(f"{op} {op_source_hash(op)}" for op in ("build", "fwd", "dw")),
+                  "", "Generated by `" + PROFILE_COMMANDS["summary"] + "`.", ""]
+        with open(os.path.join(prof, "l2_hit_rates_chung_lu_step.md"), "w") as f:
+            f.write("\n".join(lines))
+    print(json.dumps({op: v["hbm_bytes_per_call"] for op, v in rec["ops"].items()}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -368,7 +597,16 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the steps, run one plain 1 GiB -> 1 GiB elementwise copy "
                          "(reference for the HBM byte counters)")
+    ap.add_argument("--profile-ops", action="store_true",
+                    help="run every profiled op once, each after a marker kernel (for the "
+                         "rocprofv3 counter runs), then exit")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write the profiles/ summaries from the rocprofv3 output under DIR "
+                         "(p_trace, p_fetch, p_write, p_l2), then exit")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py: this build runs on exactly one GPU (got --gpus {args.gpus}); "
               "multi-GPU sharding is described in the design notes, not implemented.",
@@ -391,6 +629,11 @@ def main():
     x = torch.from_numpy(wl.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     dy = torch.from_numpy(wl.dy_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     n, e, h = wl.n, wl.e, wl.h
+    if args.profile_ops:
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_ops": run_profile_ops(mp, torch, dev, src, dst, w, x, dy,
+                                                         n, e, h)}), flush=True)
+        return
     y = torch.empty((n, h), dtype=torch.float32, device=dev)
     dx = torch.empty_like(y)
     dw = torch.empty(e, dtype=torch.float32, device=dev)
@@ -624,7 +867,7 @@ def main():
 
     per_op = ops_of(times)
     per_op_2 = ops_of(times_2)
-    build_traffic = measured_traffic("lowering:build")
+    build_traffic = measured_traffic("build")
     if build_traffic is not None:
         per_op["build"]["traffic"] = build_traffic
         per_op["build"]["traffic_GBps"] = round(build_traffic / (per_op["build"]["ms"] * 1e-3)
@@ -652,9 +895,9 @@ def main():
     # processes (B_bwd for the fused backward: one gathered dY row per edge feeds
     # both gradients) over its average launch duration.  `traffic` is the
     # calibrated HBM counter bytes of one launch.
-    kernels = {"spmm_kernel_fused_backward": ("bwd", "spmm_kernel:bwd_pair", per_op),
-               "spmm_kernel": ("fwd", "spmm_kernel:fwd_pair", per_op),
-               "spmm_kernel_fused_backward_two_arrays": ("bwd", "spmm_kernel:bwd", per_op_2)}
+    kernels = {"spmm_kernel_fused_backward": ("bwd", "bwd_pair", per_op),
+               "spmm_kernel": ("fwd", "fwd_pair", per_op),
+               "spmm_kernel_fused_backward_two_arrays": ("bwd", "bwd", per_op_2)}
     roof = {}
     for kname, (op, tkey, src_ops) in kernels.items():
         launch_ms = src_ops[op]["ms"]

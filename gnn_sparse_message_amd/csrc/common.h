@@ -109,6 +109,36 @@ __device__ inline int64_t top_class_len(const ClassLane &cl) {
     return (int64_t)1 << (c - 1);
 }
 
+// ---------------------------------------------------------------- lane reductions
+// A DPP move: every lane reads `v` from the lane the control word names inside
+// its 16-lane row (no LDS traffic, unlike a lane permute).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <- 15 - i within each 16 lanes
+
+// Sum of `v` over each aligned run of `width` lanes (a power of two up to 64,
+// uniform across the wave), the total in every lane of the run.  Butterfly
+// from the smallest distance up: pairs, quads, eights and sixteens are joined
+// with DPP moves, 32s and 64s with lane permutes.  After each step every lane
+// of a run of that step's size holds the same bits (fp addition commutes), so
+// the mirrors join exactly the runs an xor with 4 and 8 would.  Every kernel
+// that must return the same edge dot products (the fused backward and the
+// edge-gradient kernel) reduces with this one function.
+__device__ __forceinline__ float run_sum(float v, int width) {
+    if (width >= 2) v += dpp_move<kDppQuadXor1>(v);
+    if (width >= 4) v += dpp_move<kDppQuadXor2>(v);
+    if (width >= 8) v += dpp_move<kDppHalfMirror>(v);
+    if (width >= 16) v += dpp_move<kDppMirror>(v);
+    if (width >= 32) v += __shfl_xor(v, 16);
+    if (width >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
 // ---------------------------------------------------------------- SpMM
 // One aggregation over a CSR form (rows = owners).  `x` holds [n, h] features
 // of dtype `dt`; `out` receives [n, h] float32.

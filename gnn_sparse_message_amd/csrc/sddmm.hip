@@ -7,16 +7,17 @@
 // Mapping on gfx950.  Each wave takes 64 consecutive edges: one coalesced load
 // of src/dst per lane, then groups of L lanes (VEC features per lane, 16-byte
 // loads) take the edges G = 64/L at a time, U edges per group in flight.  Each
-// group reduces its dot product across its L lanes with xor-permutes, the
+// group reduces its dot product across its L lanes (run_sum: DPP moves inside a
+// 16-lane row, lane permutes beyond), the
 // results are collected so that lane k holds edge k, and the wave writes its
 // 64 values with one coalesced store.  fp32 accumulation; bf16 widened exactly.
 //
 // Multi-head weights (K per edge, head q owning columns [q*H/K, (q+1)*H/K)):
 // the work items are the E*K (edge, head) pairs in dw's own [E, K] order, each
 // a dot product over one head's columns, so the store stays coalesced.  A
-// head's lanes are reduced with an xor butterfly when their count is a power of
-// two (or the whole wave), else in lane order -- the same order as the fused
-// backward, so both give equal dw.
+// head's lanes are reduced with run_sum when their count is a power of two (or
+// the whole wave), else in lane order -- the same order as the fused backward,
+// so both give equal dw.
 #include "common.h"
 
 namespace mp {
@@ -130,8 +131,7 @@ __global__ __launch_bounds__(kBlock) void sddmm_kernel(const int32_t *__restrict
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 if (!kHeads || tree) {
-#pragma unroll
-                    for (int off = L / 2; off >= 1; off >>= 1) part[u] += __shfl_xor(part[u], off);
+                    part[u] = run_sum(part[u], L);
                 } else {   // a head of seg < 64 lanes, seg not a power of two: lane order
                     float t = __shfl(part[u], g * L);
                     for (int i = 1; i < seg; ++i) t += __shfl(part[u], g * L + i);

@@ -149,14 +149,11 @@ __device__ __forceinline__ float edge_dot(const float (&xr)[VEC], const Raw<T, V
 
 // Sum of `part` over the `seg` lanes of one head (aligned runs of seg lanes
 // inside a group; every lane of the run gets the total).  A power-of-two run is
-// reduced with an xor butterfly, any other in lane order; the COO-order
-// multi-head edge-gradient kernel reduces its lanes the same way, so both give
-// equal dw.  `seg` is uniform across the wave.
+// reduced by run_sum, any other in lane order; the COO-order multi-head
+// edge-gradient kernel reduces its lanes the same way, so both give equal dw.
+// `seg` is uniform across the wave.
 __device__ __forceinline__ float head_sum(float part, int lane, int sub, int seg) {
-    if ((seg & (seg - 1)) == 0) {
-        for (int off = seg >> 1; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-        return part;
-    }
+    if ((seg & (seg - 1)) == 0) return run_sum(part, seg);
     const int first = lane - sub % seg;
     float t = __shfl(part, first);
     for (int i = 1; i < seg; ++i) t += __shfl(part, first + i);
@@ -411,9 +408,7 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
             if constexpr (kMode != kPlain && !kHeads) {
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
-                    float part = edge_dot<T, VEC>(xr, xv[u]);
-#pragma unroll
-                    for (int off = L / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+                    const float part = run_sum(edge_dot<T, VEC>(xr, xv[u]), L);
                     const uint32_t ou = (uint32_t)__shfl((int)o, slu[u]);
                     if constexpr (score_mode(kMode)) {
                         const float wu = __shfl(wt, slu[u]);

@@ -61,6 +61,31 @@ def test_random_sizes(mp, n, e, seed):
     check_structure(_build(mp, wl), wl)
 
 
+# Lists above 4M edges (one direction per launch, 4096-key tiles, the counted
+# first pass): keys of 9 to 26 bits (one to four passes), lists one key either
+# side of a multiple of 16,384 keys, and skew onto a few rows.
+@pytest.mark.parametrize("n,e,seed,hubs", [
+    (300, (1 << 22) + 1, 40, 0),              # 9-bit keys: two passes
+    (1 << 20, 16384 * 257 - 1, 41, 0),        # 20-bit keys: three passes, a tile one short
+    (1 << 20, 16384 * 257, 42, 0),            # ... the last tile full
+    (1 << 20, 16384 * 257 + 1, 43, 0),        # ... one key in the last tile
+    (1 << 22, 4_500_000, 44, 0),              # 22-bit keys
+    ((1 << 22) + 5, 4_500_000, 45, 0),        # 23-bit keys
+    (50_000_000, 4_300_000, 46, 0),           # 26-bit keys: four passes, rows mostly empty
+    (5000, 4_500_000, 47, 3),                 # three hub rows hold 3/4 of the edges
+    (1 << 21, 4_200_000, 48, 1),              # one row holds 3/4 of the edges, 21-bit keys
+])
+def test_large_list_key_widths(mp, n, e, seed, hubs):
+    wl = synth.random_graph(n, e, 1, seed)
+    if hubs:
+        rng = np.random.default_rng(seed)
+        pick = rng.random(e) < 0.75
+        wl.dst[pick] = rng.integers(0, hubs, int(pick.sum())) * 7
+        wl.src[rng.random(e) < 0.5] = n - 1
+    print(f"case N={n} E={e} hubs={hubs}", flush=True)
+    check_structure(_build(mp, wl), wl)
+
+
 @pytest.mark.parametrize("idx_dtype", [torch.int32, torch.int64])
 def test_large_list_index_dtypes(mp, idx_dtype):
     wl = synth.random_graph(40000, 4_500_000, 1, 32)

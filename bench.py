@@ -237,13 +237,23 @@ def other_configs_bench(mp, torch, dev, reps=20):
         dw = torch.empty(e, device=dev)
         g = mp.mp_graph_build(src, dst, n)
         stream = torch.cuda.current_stream(dev)
+        # the split calls (longest rows cut across workgroups) where a row is long enough
+        need = mp.mp_spmm_split_workspace_size(g, h)
+        sws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         calls = {"build": lambda: mp.mp_graph_build(src, dst, n),
                  "fwd": lambda: mp.mp_spmm_fwd(g, w, x, out=y),
                  "dx": lambda: mp.mp_spmm_dx(g, w, dy, out=dx),
                  "dw": lambda: mp.mp_edge_grad_dw(g, x, dy, out=dw),
                  "bwd": lambda: mp.mp_spmm_dx_edge_grad(g, w, x, dy, out_dx=dx, out_dw=dw)}
+        if need:
+            calls["fwd_split"] = lambda: mp.mp_spmm_fwd_split(g, w, x, out=y, workspace=sws)
+            calls["dx_split"] = lambda: mp.mp_spmm_dx_split(g, w, dy, out=dx, workspace=sws)
+            calls["bwd_split"] = lambda: mp.mp_spmm_dx_edge_grad_split(g, w, x, dy, out_dx=dx,
+                                                                       out_dw=dw, workspace=sws)
         b = algorithmic_bytes(n, e, h, 4, 8)
-        res = {"num_nodes": n, "num_edges": e, "feature_width": h, "feature_storage": "f32"}
+        b["fwd_split"], b["dx_split"], b["bwd_split"] = b["fwd"], b["dx"], b["bwd"]
+        res = {"num_nodes": n, "num_edges": e, "feature_width": h, "feature_storage": "f32",
+               "split_workspace_bytes": need}
         for name, fn in calls.items():
             for _ in range(3):
                 fn()
@@ -264,7 +274,7 @@ def other_configs_bench(mp, torch, dev, reps=20):
                          "edges_per_s": round(e / (med * 1e-3), 1),
                          "algorithmic_bytes": b[name]}
         out[wl.name] = res
-        del g, src, dst, w, x, dy, y, dx, dw
+        del g, src, dst, w, x, dy, y, dx, dw, sws
     return out
 
 

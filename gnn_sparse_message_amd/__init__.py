@@ -34,7 +34,8 @@ __all__ = [
     "mp_spmm_dx_heads", "mp_edge_grad_dw_heads", "mp_spmm_dx_edge_grad_heads", "mp_edge_softmax",
     "mp_edge_softmax_backward", "mp_edge_softmax_heads", "mp_edge_softmax_backward_heads",
     "mp_attention_backward", "mp_attention_backward_scores", "mp_spmm_fwd_softmax", "mp_spmm_fwd_norm", "mp_spmm_dx_norm", "mp_spmm_dx_edge_grad_norm",
-    "mp_spmm_dx_edge_grad_pair", "mp_spmm_fwd_pair",
+    "mp_spmm_dx_edge_grad_pair", "mp_spmm_fwd_pair", "mp_spmm_split_workspace_size",
+    "mp_spmm_fwd_split", "mp_spmm_dx_split", "mp_spmm_dx_edge_grad_split",
     "mp_edge_normalize", "MP_NORM_MEAN", "MP_NORM_SYM",
     "mp_status_string", "mp_version", "library_path", "mp_set_owner_overrides",
     "owner_overrides",
@@ -134,6 +135,10 @@ def _load():
         "mp_spmm_dx_edge_grad_norm": (i32, [gp, i32, vp, vp, vp, i32, i64, vp, vp, vp]),
         "mp_spmm_dx_edge_grad_pair": (i32, [gp, vp, vp, vp, i32, i64, vp, vp]),
         "mp_spmm_fwd_pair": (i32, [gp, vp, vp, i32, i64, vp, vp]),
+        "mp_spmm_split_workspace_size": (i32, [gp, i64, ctypes.POINTER(sz)]),
+        "mp_spmm_fwd_split": (i32, [gp, vp, vp, i32, i64, vp, vp, sz, vp]),
+        "mp_spmm_dx_split": (i32, [gp, vp, vp, i32, i64, vp, vp, sz, vp]),
+        "mp_spmm_dx_edge_grad_split": (i32, [gp, vp, vp, vp, i32, i64, vp, vp, vp, sz, vp]),
         "mp_edge_normalize": (i32, [gp, i32, vp, vp, vp]),
         "mp_status_string": (ctypes.c_char_p, [i32]),
         "mp_last_error_detail": (ctypes.c_char_p, []),
@@ -507,6 +512,73 @@ def mp_spmm_dx_edge_grad(g: Graph, w, x, dy, out_dx=None, out_dw=None):
                                      _ptr(x), _ptr(dy), code, h, _ptr(dx),
                                      _ptr(dw) if g.num_edges else None, _stream(dy)),
            "mp_spmm_dx_edge_grad")
+    return dx, dw
+
+
+def mp_spmm_split_workspace_size(g: Graph, h: int) -> int:
+    """Bytes of workspace the split calls need for this finished graph and
+    feature width (0: no row is long enough to split)."""
+    out = ctypes.c_size_t(0)
+    _check(_lib.mp_spmm_split_workspace_size(ctypes.byref(g._desc), int(h), ctypes.byref(out)),
+           "mp_spmm_split_workspace_size")
+    return int(out.value)
+
+
+def _split_workspace(g: Graph, h: int, workspace, like):
+    need = mp_spmm_split_workspace_size(g, h)
+    if workspace is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=like.device) if need else None
+    _need_tensor("workspace", workspace)
+    if workspace.dtype != torch.uint8 or workspace.numel() < need:
+        raise ValueError(f"workspace must be a uint8 tensor of at least {need} bytes")
+    return workspace
+
+
+def mp_spmm_fwd_split(g: Graph, w, x, out=None, workspace=None):
+    """Y = A_w X with the longest rows split across workgroups (partial sums in
+    `workspace`, a uint8 device tensor of mp_spmm_split_workspace_size bytes,
+    allocated here when None)."""
+    _weights(w, g)
+    h = _features("x", x, g)
+    y = _out(out, (g.num_nodes, h), x)
+    ws = _split_workspace(g, h, workspace, x)
+    _check(_lib.mp_spmm_fwd_split(ctypes.byref(g._desc), _ptr(w) if g.num_edges else None,
+                                  _ptr(x), _code(x), h, _ptr(y), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream(x)),
+           "mp_spmm_fwd_split")
+    return y
+
+
+def mp_spmm_dx_split(g: Graph, w, dy, out=None, workspace=None):
+    """dX = A_w^T dY with the longest rows split (as mp_spmm_fwd_split)."""
+    _weights(w, g)
+    h = _features("dy", dy, g)
+    dx = _out(out, (g.num_nodes, h), dy)
+    ws = _split_workspace(g, h, workspace, dy)
+    _check(_lib.mp_spmm_dx_split(ctypes.byref(g._desc), _ptr(w) if g.num_edges else None,
+                                 _ptr(dy), _code(dy), h, _ptr(dx), _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream(dy)),
+           "mp_spmm_dx_split")
+    return dx
+
+
+def mp_spmm_dx_edge_grad_split(g: Graph, w, x, dy, out_dx=None, out_dw=None, workspace=None):
+    """(dX, dw) in one pass with the longest rows split; dX bitwise
+    mp_spmm_dx_split, dw bitwise mp_edge_grad_dw."""
+    _weights(w, g)
+    h = _features("x", x, g)
+    if _features("dy", dy, g) != h:
+        raise ValueError("x and dy must have the same feature width")
+    code = _code(dy) if x.dtype == dy.dtype else 0
+    dx = _out(out_dx, (g.num_nodes, h), dy)
+    dw = _out(out_dw, (g.num_edges,), dy)
+    ws = _split_workspace(g, h, workspace, dy)
+    _check(_lib.mp_spmm_dx_edge_grad_split(ctypes.byref(g._desc),
+                                           _ptr(w) if g.num_edges else None, _ptr(x), _ptr(dy),
+                                           code, h, _ptr(dx), _ptr(dw) if g.num_edges else None,
+                                           _ptr(ws), 0 if ws is None else ws.numel(),
+                                           _stream(dy)),
+           "mp_spmm_dx_edge_grad_split")
     return dx, dw
 
 

@@ -260,9 +260,30 @@ mp_status check_norm_mode(int32_t mode, const char *what) {
     return MP_OK;
 }
 
+// The split calls' workspace for one CSR form: `need` bytes (0 when no row of
+// it is long enough to split), device memory aligned to 256 bytes, overlapping
+// none of `others` (the graph arrays and the call's inputs and outputs).
+mp_status check_split(const mp_graph *g, const CsrView &v, int64_t h, void *ws, size_t ws_bytes,
+                      RangeList others, size_t *need) {
+    if (g->built != MP_GRAPH_BUILT)
+        return fail(MP_ERR_GRAPH, "the split calls need a finished graph (mp_graph_build, or "
+                                  "mp_graph_finish after an asynchronous build)");
+    *need = split_workspace_bytes(v.class_count, v.e, h);
+    if (*need == 0) return MP_OK;
+    if (!ws) return fail(MP_ERR_WORKSPACE, "split workspace is NULL (%zu bytes needed)", *need);
+    if (ws_bytes < *need)
+        return fail(MP_ERR_WORKSPACE, "split workspace has %zu bytes, %zu needed", ws_bytes, *need);
+    if (!aligned(ws, 256)) return fail(MP_ERR_ALIGN, "split workspace not aligned to 256 bytes");
+    mp_status st = check_device(ws, "split workspace");
+    if (st != MP_OK) return st;
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(ws);
+    return apart(others, Range{lo, lo + *need, "split workspace"});
+}
+
 mp_status dx_edge_grad_impl(const mp_graph *g, const float *w, int64_t heads, const void *x,
                             const void *dy, mp_dtype dtype, int64_t h, float *dx, float *dw,
-                            void *stream, int32_t norm_mode = 0) {
+                            void *stream, int32_t norm_mode = 0, bool split = false,
+                            void *split_ws = nullptr, size_t split_bytes = 0) {
     mp_status st = check_spmm(g, w, heads, dy, dtype, h, dx, "dy", "dx");
     if (st != MP_OK) return st;
     const int64_t n = g->num_nodes, e = g->num_edges;
@@ -286,12 +307,19 @@ mp_status dx_edge_grad_impl(const mp_graph *g, const float *w, int64_t heads, co
     const CsrView v = transpose_view(g);
     const NormSpec nm = norm_spec(g, norm_mode, false);
     const NormSpec *pn = norm_mode ? &nm : nullptr;
+    float *sw = nullptr;
+    if (split) {
+        others.add(rdw);
+        size_t need = 0;
+        if ((st = check_split(g, v, h, split_ws, split_bytes, others, &need)) != MP_OK) return st;
+        if (need) sw = static_cast<float *>(split_ws);
+    }
     if (spmm_fused_supported(dtype, h, heads, dy, x, dx))
         return spmm_fused_run(v, w, heads, dy, dtype, h, dx, x, e > 0 ? dw : nullptr,
-                              nullptr, s, pn);
+                              nullptr, s, pn, false, sw);
     // Feature rows wider than one column block: the two kernels back to back
     // (and the edge gradients scaled by their factors in place).
-    if ((st = spmm_run(v, w, heads, dy, dtype, h, dx, s, pn)) != MP_OK) return st;
+    if ((st = spmm_run(v, w, heads, dy, dtype, h, dx, s, pn, false, sw)) != MP_OK) return st;
     if (e == 0) return MP_OK;
     if ((st = sddmm_run(g->src, g->dst, e, x, dy, dtype, h, heads, dw, s)) != MP_OK) return st;
     return norm_mode ? edge_normalize_run(g, norm_mode, dw, dw, s) : MP_OK;
@@ -463,6 +491,64 @@ mp_status mp_spmm_dx_edge_grad(const mp_graph *g, const float *w, const void *x,
                                const void *dy, mp_dtype dtype, int64_t h, float *dx, float *dw,
                                void *stream) {
     return dx_edge_grad_impl(g, w, 1, x, dy, dtype, h, dx, dw, stream);
+}
+
+mp_status mp_spmm_split_workspace_size(const mp_graph *g, int64_t h, size_t *bytes) {
+    if (!bytes) return fail(MP_ERR_NULL, "bytes is NULL");
+    mp_status st = check_graph(g);
+    if (st != MP_OK) return st;
+    if (g->built != MP_GRAPH_BUILT)
+        return fail(MP_ERR_GRAPH, "the split calls need a finished graph (mp_graph_build, or "
+                                  "mp_graph_finish after an asynchronous build)");
+    if ((st = check_h(g->num_nodes, h)) != MP_OK) return st;
+    const size_t f = split_workspace_bytes(g->class_count, g->num_edges, h);
+    const size_t t = split_workspace_bytes(g->class_count_t, g->num_edges, h);
+    *bytes = f > t ? f : t;
+    return MP_OK;
+}
+
+namespace {
+// mp_spmm_fwd_split / mp_spmm_dx_split: the aggregation of one CSR form with
+// its long rows split.
+mp_status spmm_split_impl(const mp_graph *g, const CsrView &v, const float *w, const void *x,
+                          mp_dtype dt, int64_t h, float *y, void *ws, size_t ws_bytes,
+                          void *stream, const char *xname, const char *yname) {
+    mp_status st = check_spmm(g, w, 1, x, dt, h, y, xname, yname);
+    if (st != MP_OK) return st;
+    const int64_t n = g->num_nodes, e = g->num_edges;
+    RangeList others = graph_ranges(g);
+    others.add(range(x, n * h, dtype_size(dt), xname));
+    others.add(range(w, e, 4, "w"));
+    others.add(range(y, n * h, 4, yname));
+    size_t need = 0;
+    if ((st = check_split(g, v, h, ws, ws_bytes, others, &need)) != MP_OK) return st;
+    return spmm_run(v, w, 1, x, dt, h, y, static_cast<hipStream_t>(stream), nullptr, false,
+                    need ? static_cast<float *>(ws) : nullptr);
+}
+}  // namespace
+
+mp_status mp_spmm_fwd_split(const mp_graph *g, const float *w, const void *x, mp_dtype x_dtype,
+                            int64_t h, float *y, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+    if (mp_status st = check_graph(g)) return st;
+    return spmm_split_impl(g, forward_view(g), w, x, x_dtype, h, y, workspace, workspace_bytes,
+                           stream, "x", "y");
+}
+
+mp_status mp_spmm_dx_split(const mp_graph *g, const float *w, const void *dy, mp_dtype dy_dtype,
+                           int64_t h, float *dx, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    if (mp_status st = check_graph(g)) return st;
+    return spmm_split_impl(g, transpose_view(g), w, dy, dy_dtype, h, dx, workspace,
+                           workspace_bytes, stream, "dy", "dx");
+}
+
+mp_status mp_spmm_dx_edge_grad_split(const mp_graph *g, const float *w, const void *x,
+                                     const void *dy, mp_dtype dtype, int64_t h, float *dx,
+                                     float *dw, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
+    return dx_edge_grad_impl(g, w, 1, x, dy, dtype, h, dx, dw, stream, 0, true, workspace,
+                             workspace_bytes);
 }
 
 mp_status mp_spmm_fwd_heads(const mp_graph *g, const float *w, int64_t heads, const void *x,

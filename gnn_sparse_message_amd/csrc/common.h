@@ -176,9 +176,13 @@ struct NormSpec {
 // columns [q*h/K, (q+1)*h/K) of every row (h is a multiple of K; K = 1 is the
 // scalar case).  pair: one head, the weight of edge e at w[2 e] (weights and
 // their gradients interleaved).
+// split_ws (the split calls): rows long enough are cut into chunks whose
+// partial sums go to this workspace (split_workspace_bytes) and are added in
+// chunk order by a second launch.
 mp_status spmm_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
                    mp_dtype dt, int64_t h, float *out, hipStream_t stream,
-                   const NormSpec *norm = nullptr, bool pair = false);
+                   const NormSpec *norm = nullptr, bool pair = false, float *split_ws = nullptr);
+size_t split_workspace_bytes(const int64_t *class_count, int64_t e, int64_t h);
 // The same aggregation over the transpose CSR that also writes, for every edge
 // q of owner row j, dw[order[q]] = <x_own[j, :], x[col[q], :]> (fused backward;
 // per head, dw[order[q] * K + head], when K > 1).  With row_dot (attention
@@ -197,7 +201,8 @@ mp_status set_owner_overrides(int32_t hub_min_len, int32_t hub_apart, int32_t wa
 mp_status spmm_fused_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
                          mp_dtype dt, int64_t h, float *out, const void *x_own, float *dw,
                          const float *row_dot, hipStream_t stream,
-                         const NormSpec *norm = nullptr, bool pair = false);
+                         const NormSpec *norm = nullptr, bool pair = false,
+                         float *split_ws = nullptr);
 
 // ---------------------------------------------------------------- SDDMM
 // dw[e * K + q] = <x[src_e], dy[dst_e]> over head q's columns, COO order.

@@ -207,6 +207,15 @@ struct SpmmArgs {
     int32_t wave_min;                 // rows this long or longer (below hub) get a wave
     int32_t force_hub, force_apart;   // owner_rule overrides (> 0 / >= 0), else -1
     NormSpec norm;                    // normalising kernels only: fetch-time weight scaling
+    // Split rows (the split calls): plan positions [0, n_split) are cut into
+    // chunks of chunk_len edges.  Chunk items come first in the main launch;
+    // item i writes its partial row sum to partials[i * h ...]; the combine
+    // launch then adds each row's partials in chunk order.  Rows of one degree
+    // class get the same number of item slots (enough for its longest row);
+    // cls_items / cls_rows are cumulative over the split classes, highest first.
+    float *partials;
+    int32_t n_split, blk_chunk, chunk_len, n_split_cls;
+    int32_t cls_items[MP_NUM_CLASSES], cls_rows[MP_NUM_CLASSES], cls_slots[MP_NUM_CLASSES];
 };
 
 constexpr int64_t kMaxKindBlocks = 1 << 22;   // wave and group owners stride beyond this
@@ -453,52 +462,95 @@ __device__ __forceinline__ void own_row(const SpmmArgs &a, int row, int64_t hoff
     }
 }
 
-// Hub rows first .. n_hub - 1, every stride-th: each row by the whole workgroup
-// of kWaves waves, the waves' partial sums added in wave order.
+// Edges [beg, end) of row `row` by the whole workgroup of kWaves waves, the
+// waves' partial sums added in wave order and stored to out (the row's slice of
+// the output, or a partial row of a split row).  len: the row's full length.
 template <typename T, int VEC, int L, int kMode, bool kHeads, bool kNorm, int kWaves>
-__device__ __forceinline__ void hub_rows(const SpmmArgs &a, int32_t first, int32_t n_hub,
-                                         int32_t stride, float (*s_red)[L * VEC]) {
+__device__ __forceinline__ void hub_segment(const SpmmArgs &a, int row, int64_t beg, int64_t end,
+                                            int64_t len, float *out,
+                                            float (*s_red)[L * VEC]) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
     const int sub = lane % L;
     const int64_t hoff = (int64_t)blockIdx.y * (L * VEC) + (int64_t)sub * VEC;
     const bool active = hoff < a.h;
     const int head = kHeads && active ? (int)(hoff / a.head_w) : 0;
+    float acc[VEC], xr[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+    own_row<T, VEC, kMode>(a, row, hoff, active, xr);
+    accumulate<T, VEC, L, kWave, kMode, kHeads, kNorm>(a, beg + (int64_t)wv * kWave, end,
+                                                           (int64_t)kWaves * kWave, lane, hoff,
+                                                           head, active, xr, acc, (double)len,
+                                                           own_stats<kMode, kNorm>(a, row));
+#pragma unroll
+    for (int off = L; off < kWave; off <<= 1)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] += __shfl_xor(acc[v], off);
+    if (lane < L) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) s_red[wv][sub * VEC + v] = acc[v];
+    }
+    __syncthreads();
+    if (wv == 0 && lane < L && active) {
+        float r[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            float t = s_red[0][sub * VEC + v];
+#pragma unroll
+            for (int w2 = 1; w2 < kWaves; ++w2) t += s_red[w2][sub * VEC + v];
+            r[v] = t;
+        }
+        store_row<VEC>(out + hoff, r);
+    }
+    __syncthreads();   // s_red is written again by the next segment
+}
+
+// Hub rows first .. n_hub - 1, every stride-th: each row by the whole workgroup
+// of kWaves waves (hub_segment).
+template <typename T, int VEC, int L, int kMode, bool kHeads, bool kNorm, int kWaves>
+__device__ __forceinline__ void hub_rows(const SpmmArgs &a, int32_t first, int32_t n_hub,
+                                         int32_t stride, float (*s_red)[L * VEC]) {
     for (int32_t idx = first; idx < n_hub; idx += stride) {
         const int row = a.plan[idx];
         if ((uint32_t)row >= (uint64_t)a.n) continue;   // the plan is a permutation of [0, n)
         const int64_t beg = a.rowptr[row], end = a.rowptr[row + 1];
-        float acc[VEC], xr[VEC];
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
-        own_row<T, VEC, kMode>(a, row, hoff, active, xr);
-        accumulate<T, VEC, L, kWave, kMode, kHeads, kNorm>(a, beg + (int64_t)wv * kWave, end,
-                                                               (int64_t)kWaves * kWave, lane,
-                                                               hoff, head, active, xr, acc,
-                                                               (double)(end - beg),
-                                                               own_stats<kMode, kNorm>(a, row));
-#pragma unroll
-        for (int off = L; off < kWave; off <<= 1)
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) acc[v] += __shfl_xor(acc[v], off);
-        if (lane < L) {
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) s_red[wv][sub * VEC + v] = acc[v];
-        }
-        __syncthreads();
-        if (wv == 0 && lane < L && active) {
-            float r[VEC];
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) {
-                float t = s_red[0][sub * VEC + v];
-#pragma unroll
-                for (int w2 = 1; w2 < kWaves; ++w2) t += s_red[w2][sub * VEC + v];
-                r[v] = t;
-            }
-            store_row<VEC>(a.y + (int64_t)row * a.h + hoff, r);
-        }
-        __syncthreads();   // s_red is written again for the next row
+        hub_segment<T, VEC, L, kMode, kHeads, kNorm, kWaves>(a, row, beg, end, end - beg,
+                                                             a.y + (int64_t)row * a.h, s_red);
     }
+}
+
+// Chunk item `item` of the split rows: its class (a short uniform search over
+// the split classes), its row and chunk, then the chunk's edges by the whole
+// workgroup into its partial row.  Empty slots (rows shorter than their
+// class's longest) store nothing.
+__device__ __forceinline__ bool chunk_of(const SpmmArgs &a, int32_t item, int &row, int64_t &beg,
+                                         int64_t &end, int64_t &len) {
+    int c = 0;
+    while (c + 1 < a.n_split_cls && item >= a.cls_items[c]) ++c;
+    const int32_t item0 = c ? a.cls_items[c - 1] : 0;
+    const int32_t pos0 = c ? a.cls_rows[c - 1] : 0;
+    const int32_t rel = item - item0;
+    const int32_t pos = pos0 + rel / a.cls_slots[c];
+    const int64_t k = rel % a.cls_slots[c];
+    if (pos >= a.n_split) return false;
+    row = a.plan[pos];
+    if ((uint32_t)row >= (uint64_t)a.n) return false;
+    const int64_t rb = a.rowptr[row], re = a.rowptr[row + 1];
+    len = re - rb;
+    beg = rb + k * a.chunk_len;
+    end = beg + a.chunk_len < re ? beg + a.chunk_len : re;
+    return beg < re;
+}
+
+template <typename T, int VEC, int L, int kMode, bool kHeads, bool kNorm>
+__device__ __forceinline__ void chunk_item(const SpmmArgs &a, int32_t item,
+                                           float (*s_red)[L * VEC]) {
+    int row;
+    int64_t beg, end, len;
+    if (!chunk_of(a, item, row, beg, end, len)) return;   // the same for the whole block
+    hub_segment<T, VEC, L, kMode, kHeads, kNorm, kWavesPerBlock>(
+        a, row, beg, end, len, a.partials + (int64_t)item * a.h, s_red);
 }
 
 // The owner row's softmax statistics (max, sum) when the forward forms softmax
@@ -546,11 +598,17 @@ void spmm_kernel(SpmmArgs a) {
     }
     if (apart) pt.blk_hub = 0;
     int64_t b = blockIdx.x;
+    __shared__ float s_red[kWavesPerBlock][L * VEC];
+    if (b < a.blk_chunk) {
+        // ---- chunks of the split rows: partial sums, combined by the next launch
+        chunk_item<T, VEC, L, kMode, kHeads, kNorm>(a, (int32_t)b, s_red);
+        return;
+    }
+    b -= a.blk_chunk;
     if (b < pt.blk_hub) {
-        // ---- hub rows: the whole workgroup
-        __shared__ float s_red[kWavesPerBlock][L * VEC];
-        hub_rows<T, VEC, L, kMode, kHeads, kNorm, kWavesPerBlock>(a, (int32_t)b, pt.n_hub,
-                                                                  pt.blk_hub, s_red);
+        // ---- hub rows (after the split ones): the whole workgroup
+        hub_rows<T, VEC, L, kMode, kHeads, kNorm, kWavesPerBlock>(a, a.n_split + (int32_t)b,
+                                                                  pt.n_hub, pt.blk_hub, s_red);
         return;
     }
     b -= pt.blk_hub;
@@ -621,6 +679,27 @@ __global__ __launch_bounds__(kHubBlock) void spmm_hub_kernel(SpmmArgs a) {
                                                          (int32_t)gridDim.x, s_red);
 }
 
+// Each split row's output: its partial rows added in chunk order (one block per
+// split row; plan position = block index).
+__global__ __launch_bounds__(kBlock) void split_combine_kernel(SpmmArgs a) {
+    const int32_t pos = blockIdx.x;
+    int c = 0;
+    while (c + 1 < a.n_split_cls && pos >= a.cls_rows[c]) ++c;
+    const int32_t item0 = (c ? a.cls_items[c - 1] : 0) +
+                          (pos - (c ? a.cls_rows[c - 1] : 0)) * a.cls_slots[c];
+    const int row = a.plan[pos];
+    if ((uint32_t)row >= (uint64_t)a.n) return;
+    const int64_t len = a.rowptr[row + 1] - a.rowptr[row];
+    int64_t nk = (len + a.chunk_len - 1) / a.chunk_len;
+    if (nk > a.cls_slots[c]) nk = a.cls_slots[c];   // never taken: slots cover the class
+    const float *p = a.partials + (int64_t)item0 * a.h;
+    for (int64_t col = threadIdx.x; col < a.h; col += blockDim.x) {
+        float t = p[col];
+        for (int64_t k = 1; k < nk; ++k) t += p[k * a.h + col];
+        a.y[(int64_t)row * a.h + col] = t;
+    }
+}
+
 // ------------------------------------------------------------------ dispatch
 // Owner-size overrides set through mp_set_owner_overrides (tests and tuning
 // only; none is set unless a caller asks): hub rows from this length, hub rows
@@ -641,6 +720,39 @@ Overrides overrides_for(int L) {
     return o;
 }
 
+// Rows split across workgroups (the split calls), from the host class counts:
+// chunks of at least four shares of the chip's wave slots (512 edges or more),
+// rows of two chunks or longer split.  Rows of one class get the slots their
+// longest member needs.  items = 0: nothing to split.
+struct SplitPlan {
+    int32_t n_split = 0, items = 0, chunk_len = 0, n_cls = 0;
+    int32_t cls_items[MP_NUM_CLASSES] = {}, cls_rows[MP_NUM_CLASSES] = {},
+            cls_slots[MP_NUM_CLASSES] = {};
+};
+
+SplitPlan split_plan(const int64_t *cc, int64_t e) {
+    SplitPlan p;
+    const int64_t share = e / kWaveSlots;
+    int64_t chunk = 512;
+    while (chunk < 4 * share) chunk *= 2;
+    p.chunk_len = (int32_t)chunk;
+    int64_t items = 0, rows = 0;
+    for (int c = MP_NUM_CLASSES - 1; c >= 1; --c) {
+        if (((int64_t)1 << (c - 1)) < 2 * chunk) break;   // lower classes hold shorter rows
+        if (cc[c] == 0) continue;
+        const int64_t slots = ((((int64_t)1 << c) - 1) + chunk - 1) / chunk;
+        items += cc[c] * slots;
+        rows += cc[c];
+        p.cls_items[p.n_cls] = (int32_t)items;
+        p.cls_rows[p.n_cls] = (int32_t)rows;
+        p.cls_slots[p.n_cls] = (int32_t)slots;
+        ++p.n_cls;
+    }
+    p.n_split = (int32_t)rows;
+    p.items = (int32_t)items;
+    return p;
+}
+
 // Hub rows first, in their own launch, then every other row.
 template <typename T, int VEC, int L, int kMode, bool kHeads, bool kNorm>
 void go(const SpmmArgs &a, const dim3 &hub, const dim3 &rest, hipStream_t s) {
@@ -651,7 +763,7 @@ void go(const SpmmArgs &a, const dim3 &hub, const dim3 &rest, hipStream_t s) {
 template <typename T, int VEC, int L>
 mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *x, int64_t h,
                  float *out, const void *x_own, float *dw, const float *row_dot,
-                 const NormSpec *norm, bool pair, hipStream_t s) {
+                 const NormSpec *norm, bool pair, hipStream_t s, float *split_ws) {
     const bool normed = norm && norm->mode != 0;
     const bool soft = normed && norm->mode == kFetchSoftmax;
     if (normed && (heads != 1 || (row_dot && !soft)))
@@ -686,6 +798,27 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
     a.force_hub = ov.hub_min;
     a.force_apart = ov.apart;
     a.norm = normed ? *norm : NormSpec{0, false, nullptr};
+    a.partials = nullptr;
+    a.n_split = a.blk_chunk = a.chunk_len = a.n_split_cls = 0;
+    SplitPlan sp;
+    if (split_ws) {
+        if (csr.dev_totals || normed || heads != 1 || row_dot || pair)
+            return fail(MP_ERR_SHAPE, "split rows need a finished graph, one head and the plain "
+                                      "aggregation or fused backward");
+        sp = split_plan(csr.class_count, csr.e);
+        if (sp.items > 0) {
+            a.partials = split_ws;
+            a.n_split = sp.n_split;
+            a.blk_chunk = sp.items;
+            a.chunk_len = sp.chunk_len;
+            a.n_split_cls = sp.n_cls;
+            for (int c = 0; c < MP_NUM_CLASSES; ++c) {
+                a.cls_items[c] = sp.cls_items[c];
+                a.cls_rows[c] = sp.cls_rows[c];
+                a.cls_slots[c] = sp.cls_slots[c];
+            }
+        }
+    }
     // A launch holds at most 2^32 - 1 work-items; wave and group owners stride.
     Partition pt;
     a.hub_apart = 0;
@@ -711,6 +844,17 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
         hub_blocks = ov.apart == 0
                          ? 0
                          : partition<L>(most(sixteen.hub_min), 0, 0, kAsyncHubBlocks16).blk_hub;
+    } else if (a.n_split > 0) {
+        // Split rows: the longest rows are cut into chunks, so every other hub row
+        // takes a four-wave workgroup of the main launch (no 16-wave launch); the
+        // split rows lead the hub rows.
+        const OwnerRule r = owner_rule(top_class_len_host(csr.class_count), csr.e, G,
+                                       ov.hub_min, 0);
+        int64_t at_hub = rows_at_least_host(csr.class_count, r.hub_min);
+        if (at_hub < a.n_split) at_hub = a.n_split;
+        pt = partition<L>(at_hub, rows_at_least_host(csr.class_count, ov.wave_min), csr.n);
+        const int64_t rest = pt.n_hub - a.n_split;
+        pt.blk_hub = (int32_t)(rest < kMaxKindBlocks ? rest : kMaxKindBlocks);
     } else {
         const OwnerRule r = owner_rule(top_class_len_host(csr.class_count), csr.e, G,
                                        ov.hub_min, ov.apart);
@@ -730,7 +874,7 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
     a.blk_wave = pt.blk_wave;
     a.blk_group = pt.blk_group;
     const int64_t hx = hub_blocks;
-    const int64_t gx = (int64_t)a.blk_hub + a.blk_wave + a.blk_group;
+    const int64_t gx = (int64_t)a.blk_chunk + a.blk_hub + a.blk_wave + a.blk_group;
     const int64_t gy = (h + (int64_t)L * VEC - 1) / ((int64_t)L * VEC);
     if (gx + hx <= 0) return MP_OK;
     if (gx > (int64_t)3 << 22 || hx > (int64_t)3 << 22 || gy > 65535)
@@ -762,8 +906,21 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
         else go<T, VEC, L, kPlain, false, false>(a, hub, rest, s);
     }
     MP_HIP_CHECK(hipGetLastError(), "spmm launch");
+    if (a.n_split > 0) {
+        split_combine_kernel<<<(unsigned)a.n_split, kBlock, 0, s>>>(a);
+        MP_HIP_CHECK(hipGetLastError(), "split row combine launch");
+    }
     return MP_OK;
 }
+
+}  // namespace
+
+// Workspace of the split calls: one partial row of h floats per chunk item.
+size_t split_workspace_bytes(const int64_t *class_count, int64_t e, int64_t h) {
+    return (size_t)split_plan(class_count, e).items * (size_t)h * sizeof(float);
+}
+
+namespace {
 
 int lanes_for(int64_t h, int vec) {
     const int64_t need = (h + vec - 1) / vec;
@@ -776,15 +933,15 @@ template <typename T, int VEC>
 mp_status launch_lanes(const CsrView &csr, const float *w, int64_t heads, const void *x,
                        int64_t h, float *out, const void *x_own, float *dw,
                        const float *row_dot, const NormSpec *nm, bool pair,
-                       hipStream_t s) {
+                       hipStream_t s, float *sw) {
     switch (lanes_for(h, VEC)) {
-        case 1: return launch<T, VEC, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
-        case 2: return launch<T, VEC, 2>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
-        case 4: return launch<T, VEC, 4>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
-        case 8: return launch<T, VEC, 8>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
-        case 16: return launch<T, VEC, 16>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
-        case 32: return launch<T, VEC, 32>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
-        default: return launch<T, VEC, 64>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
+        case 1: return launch<T, VEC, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s, sw);
+        case 2: return launch<T, VEC, 2>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s, sw);
+        case 4: return launch<T, VEC, 4>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s, sw);
+        case 8: return launch<T, VEC, 8>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s, sw);
+        case 16: return launch<T, VEC, 16>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s, sw);
+        case 32: return launch<T, VEC, 32>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s, sw);
+        default: return launch<T, VEC, 64>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s, sw);
     }
 }
 
@@ -794,8 +951,9 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 mp_status spmm_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
                    mp_dtype dt, int64_t h, float *out, hipStream_t s, const NormSpec *norm,
-                   bool pair) {
-    return spmm_fused_run(csr, w, heads, x, dt, h, out, nullptr, nullptr, nullptr, s, norm, pair);
+                   bool pair, float *split_ws) {
+    return spmm_fused_run(csr, w, heads, x, dt, h, out, nullptr, nullptr, nullptr, s, norm, pair,
+                          split_ws);
 }
 
 // 16-byte lanes need aligned rows and heads that are whole lanes wide.
@@ -814,15 +972,19 @@ bool spmm_fused_supported(mp_dtype dt, int64_t h, int64_t heads, const void *x,
 mp_status spmm_fused_run(const CsrView &csr, const float *w, int64_t heads, const void *x,
                          mp_dtype dt, int64_t h, float *out, const void *x_own, float *dw,
                          const float *row_dot, hipStream_t s, const NormSpec *nm,
-                         bool pair) {
+                         bool pair, float *sw) {
     if (dt == MP_F32) {
         if (vector_lanes_ok(4, h, heads, x, x_own, out))
-            return launch_lanes<float, 4>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
-        return launch_lanes<float, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
+            return launch_lanes<float, 4>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair,
+                                          s, sw);
+        return launch_lanes<float, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s,
+                                      sw);
     }
     if (vector_lanes_ok(8, h, heads, x, x_own, out))
-        return launch_lanes<uint16_t, 8>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
-    return launch_lanes<uint16_t, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s);
+        return launch_lanes<uint16_t, 8>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair,
+                                         s, sw);
+    return launch_lanes<uint16_t, 1>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair, s,
+                                     sw);
 }
 
 mp_status set_owner_overrides(int32_t hub_min_len, int32_t hub_apart, int32_t wave_min_len) {

@@ -302,6 +302,47 @@ mp_status mp_spmm_fwd_pair(const mp_graph *g, const float *wg, const void *x, mp
                            int64_t h, float *y, void *stream);
 
 /*
+ * The aggregations with their longest rows split across workgroups, for graphs
+ * where a few rows hold much of the edges (tinymesh "Weighted aggregation
+ * experiment", "Limits": degree skew still weighs on both CSR directions).
+ * A row of at least two chunks (a chunk is at least four of the chip's
+ * E / 4096 edge shares, and at least 512 edges) is cut into chunks; each chunk's
+ * partial row sum is written to the caller's workspace, and a second launch adds
+ * each row's partials in chunk order into the output.  Every other row is
+ * summed as in the plain calls, but with no row left to a 16-wave workgroup.
+ * Results are deterministic (fixed chunks, fixed order, no atomics) and within
+ * the plain calls' tolerance of the exact sums, but not bitwise equal to them
+ * when a row is split; the split fused backward gives dX bitwise equal to
+ * mp_spmm_dx_split and dw bitwise equal to mp_edge_grad_dw.  When no row is
+ * long enough, each call is exactly its plain counterpart and needs no
+ * workspace.
+ *
+ * mp_spmm_split_workspace_size: bytes of workspace (one float partial row of
+ *   H per chunk item, for whichever CSR form needs more) that the split calls
+ *   take for this graph and feature width; 0 when no row is split.  The graph
+ *   must be finished (MP_GRAPH_BUILT: mp_graph_build, or mp_graph_finish after
+ *   an asynchronous build), else MP_ERR_GRAPH.
+ * The calls take the arguments of mp_spmm_fwd, mp_spmm_dx and
+ *   mp_spmm_dx_edge_grad plus the workspace: device memory, 256-byte aligned,
+ *   at least mp_spmm_split_workspace_size bytes (else MP_ERR_WORKSPACE /
+ *   MP_ERR_ALIGN), overlapping no input, output or graph array (MP_ERR_ALIAS);
+ *   it may be NULL when the size is 0.  Its contents on entry are ignored; calls
+ *   that share one workspace must not overlap in time.  One weight per edge;
+ *   finished graphs only.
+ */
+mp_status mp_spmm_split_workspace_size(const mp_graph *g, int64_t h, size_t *bytes);
+mp_status mp_spmm_fwd_split(const mp_graph *g, const float *w, const void *x, mp_dtype x_dtype,
+                            int64_t h, float *y, void *workspace, size_t workspace_bytes,
+                            void *stream);
+mp_status mp_spmm_dx_split(const mp_graph *g, const float *w, const void *dy, mp_dtype dy_dtype,
+                           int64_t h, float *dx, void *workspace, size_t workspace_bytes,
+                           void *stream);
+mp_status mp_spmm_dx_edge_grad_split(const mp_graph *g, const float *w, const void *x,
+                                     const void *dy, mp_dtype dtype, int64_t h, float *dx,
+                                     float *dw, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
+/*
  * Multi-head edge weights.  tinymesh "Weighted aggregation experiment",
  * "Limits" lists vector edge weights among what the scalar experiment leaves
  * open; these calls take the per-head reading of it.  Each edge carries

@@ -96,6 +96,19 @@ int main(int argc, char **argv) {
     ALIAS(mp_spmm_dx_edge_grad_pair(&g, (float *)g.col_t, x, dy, MP_BF16, h, dx, nullptr));
     VALID(mp_spmm_fwd_pair(&g, w, x, MP_BF16, h, y, nullptr));
     ALIAS(mp_spmm_fwd_pair(&g, w, x, MP_BF16, h, (float *)g.rowptr, nullptr));
+    {   // split calls: a workspace of the size the (stub) plan asks for
+        size_t need = 0;
+        if (mp_spmm_split_workspace_size(&g, h, &need) != MP_OK) {
+            printf("FAIL split workspace size\n");
+            ++failures;
+        }
+        void *sw = slot(s++);
+        VALID(mp_spmm_fwd_split(&g, w, x, MP_BF16, h, y, sw, need, nullptr));
+        VALID(mp_spmm_dx_split(&g, w, dy, MP_BF16, h, dx, sw, need, nullptr));
+        VALID(mp_spmm_dx_edge_grad_split(&g, w, x, dy, MP_BF16, h, dx, dw, sw, need, nullptr));
+        ALIAS(mp_spmm_fwd_split(&g, w, x, MP_BF16, h, y, y, need, nullptr));
+        ALIAS(mp_spmm_dx_edge_grad_split(&g, w, x, dy, MP_BF16, h, dx, dw, dw, need, nullptr));
+    }
     VALID(mp_spmm_fwd_heads(&g, w, k, x, MP_BF16, h, y, nullptr));
     VALID(mp_spmm_dx_heads(&g, w, k, dy, MP_BF16, h, dx, nullptr));
     VALID(mp_edge_grad_dw_heads(&g, x, dy, MP_BF16, h, k, dw, nullptr));

@@ -45,7 +45,7 @@ mp_status lower_read_info(mp_graph *, hipStream_t, int *bad) {
     return MP_OK;
 }
 mp_status spmm_run(const CsrView &, const float *, int64_t, const void *, mp_dtype, int64_t,
-                   float *, hipStream_t, const NormSpec *, bool) {
+                   float *, hipStream_t, const NormSpec *, bool, float *) {
     ++g_launches;
     return MP_OK;
 }
@@ -55,11 +55,12 @@ bool spmm_fused_supported(mp_dtype, int64_t h, int64_t, const void *, const void
 }
 mp_status spmm_fused_run(const CsrView &, const float *, int64_t, const void *, mp_dtype, int64_t,
                          float *, const void *, float *, const float *, hipStream_t,
-                         const NormSpec *, bool) {
+                         const NormSpec *, bool, float *) {
     ++g_launches;
     return MP_OK;
 }
 mp_status set_owner_overrides(int32_t, int32_t, int32_t) { return MP_OK; }
+size_t split_workspace_bytes(const int64_t *, int64_t, int64_t h) { return 4096 * (size_t)h; }
 mp_status sddmm_run(const int32_t *, const int32_t *, int64_t, const void *, const void *,
                     mp_dtype, int64_t, int64_t, float *, hipStream_t) {
     ++g_launches;

@@ -139,6 +139,16 @@ __device__ __forceinline__ float run_sum(float v, int width) {
     return v;
 }
 
+// fp32 feature rows of at least kWideF32Cols columns (and heads whose width is
+// a multiple of 8) use 32-byte lane slices, 8 floats in two 16-byte loads, so a
+// wave carries two rows of 256 features at once instead of one.  The
+// aggregation and the edge-gradient kernels take their lane width from this one
+// rule, which keeps their edge dot products equal.
+constexpr int64_t kWideF32Cols = 256;
+inline int f32_vec(int64_t h, int64_t heads) {
+    return h >= kWideF32Cols && (h / heads) % 8 == 0 ? 8 : 4;
+}
+
 // ---------------------------------------------------------------- SpMM
 // One aggregation over a CSR form (rows = owners).  `x` holds [n, h] features
 // of dtype `dt`; `out` receives [n, h] float32.

@@ -5,8 +5,9 @@
 // the whole GNN literature", Step 4, evaluated at the edges only).
 //
 // Mapping on gfx950.  Each wave takes 64 consecutive edges: one coalesced load
-// of src/dst per lane, then groups of L lanes (VEC features per lane, 16-byte
-// loads) take the edges G = 64/L at a time, U edges per group in flight.  Each
+// of src/dst per lane, then groups of L lanes (VEC features per lane: 16-byte
+// loads, or two for rows of 256 fp32 features or more, by the same rule as the
+// aggregation, f32_vec) take the edges G = 64/L at a time, U edges per group in flight.  Each
 // group reduces its dot product across its L lanes (run_sum: DPP moves inside a
 // 16-lane row, lane permutes beyond), the
 // results are collected so that lane k holds edge k, and the wave writes its
@@ -37,6 +38,23 @@ struct Feat2<float, 4> {
         s = fmaf(p.y, q.y, s);
         s = fmaf(p.z, q.z, s);
         return fmaf(p.w, q.w, s);
+    }
+};
+template <>
+struct Feat2<float, 8> {
+    static __device__ __forceinline__ float dot(const float *a, const float *b) {
+        const float4 p0 = *reinterpret_cast<const float4 *>(a);
+        const float4 q0 = *reinterpret_cast<const float4 *>(b);
+        const float4 p1 = *reinterpret_cast<const float4 *>(a + 4);
+        const float4 q1 = *reinterpret_cast<const float4 *>(b + 4);
+        float s = fmaf(p0.x, q0.x, 0.f);
+        s = fmaf(p0.y, q0.y, s);
+        s = fmaf(p0.z, q0.z, s);
+        s = fmaf(p0.w, q0.w, s);
+        s = fmaf(p1.x, q1.x, s);
+        s = fmaf(p1.y, q1.y, s);
+        s = fmaf(p1.z, q1.z, s);
+        return fmaf(p1.w, q1.w, s);
     }
 };
 template <>
@@ -199,6 +217,8 @@ mp_status sddmm_run(const int32_t *src, const int32_t *dst, int64_t e, const voi
     const bool vec_ok = aligned16(x) && aligned16(dy);
     const int64_t hw = h / heads;
     if (dt == MP_F32) {
+        if (vec_ok && hw % 4 == 0 && f32_vec(h, heads) == 8)
+            return launch_lanes<float, 8>(src, dst, e, x, dy, h, heads, dw, s);
         if (vec_ok && hw % 4 == 0)
             return launch_lanes<float, 4>(src, dst, e, x, dy, h, heads, dw, s);
         return launch_lanes<float, 1>(src, dst, e, x, dy, h, heads, dw, s);

@@ -8,7 +8,8 @@
 // row has exactly one owner, there are no atomics and no [E, H] message rows.
 //
 // Mapping on gfx950.  A feature row is split over a "group" of L lanes, each
-// lane holding VEC contiguous features (16-byte loads: 4 fp32 or 8 bf16).  Rows
+// lane holding VEC contiguous features (16-byte loads: 4 fp32 or 8 bf16; 8 fp32
+// in two loads for rows of 256 fp32 features or more, f32_vec).  Rows
 // are visited through the degree plan (rows sorted by length class, longest
 // first) and handed to owners of three sizes within one launch, so long rows
 // start first and their tail overlaps the short ones:
@@ -56,6 +57,15 @@ struct Feat<float, 4> {
     static __device__ __forceinline__ void load(const float *p, float (&v)[4]) {
         const float4 q = *reinterpret_cast<const float4 *>(p);
         v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    }
+};
+template <>
+struct Feat<float, 8> {
+    static __device__ __forceinline__ void load(const float *p, float (&v)[8]) {
+        const float4 q0 = *reinterpret_cast<const float4 *>(p);
+        const float4 q1 = *reinterpret_cast<const float4 *>(p + 4);
+        v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w;
+        v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
     }
 };
 template <>
@@ -965,7 +975,7 @@ bool vector_lanes_ok(int vec, int64_t h, int64_t heads, const void *x, const voi
 
 bool spmm_fused_supported(mp_dtype dt, int64_t h, int64_t heads, const void *x,
                           const void *x_own, const void *out) {
-    const int vec = dt == MP_F32 ? 4 : 8;
+    const int vec = dt == MP_F32 ? f32_vec(h, heads) : 8;
     return h <= (int64_t)kWave * (vector_lanes_ok(vec, h, heads, x, x_own, out) ? vec : 1);
 }
 
@@ -974,6 +984,9 @@ mp_status spmm_fused_run(const CsrView &csr, const float *w, int64_t heads, cons
                          const float *row_dot, hipStream_t s, const NormSpec *nm,
                          bool pair, float *sw) {
     if (dt == MP_F32) {
+        if (f32_vec(h, heads) == 8 && vector_lanes_ok(8, h, heads, x, x_own, out))
+            return launch_lanes<float, 8>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair,
+                                          s, sw);
         if (vector_lanes_ok(4, h, heads, x, x_own, out))
             return launch_lanes<float, 4>(csr, w, heads, x, h, out, x_own, dw, row_dot, nm, pair,
                                           s, sw);

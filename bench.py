@@ -289,6 +289,7 @@ def minibatch_bench(mp, torch, dev, n_batches=64, h=256):
       async     -- mp_graph_build_async, no host synchronisation, one stream;
       pipelined -- mp_graph_build_async of batch b + 1 on a second stream while
                    batch b computes (two workspaces, events between the streams).
+      graph     -- the async schedule captured once in a HIP graph and replayed.
     Returns the timings and the aggregate algorithmic rates."""
     import synth
     batches = synth.minibatches(n_batches, h=h, features=False)
@@ -346,8 +347,27 @@ def minibatch_bench(mp, torch, dev, n_batches=64, h=256):
                 graphs[b] = None
         torch.cuda.current_stream(dev).wait_stream(sa)
 
+    # The asynchronous schedule captured once into a HIP graph and replayed: no
+    # host launch work per batch (each replay repeats the same 64 builds and
+    # compute calls on the staged batches).
+    cur = torch.cuda.current_stream(dev)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):                     # allocator warm-up outside the capture
+        run_async()
+    cur.wait_stream(side)
+    torch.cuda.synchronize()
+    ref = (y.clone(), dx.clone(), dw.clone())         # the last batch, eager
+    cg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cg, capture_error_mode="relaxed"):
+        run_async()
+
+    def run_graph():
+        cg.replay()
+
     out = {}
-    for name, fn in (("sync", run_sync), ("async", run_async), ("pipelined", run_pipelined)):
+    for name, fn in (("sync", run_sync), ("async", run_async), ("pipelined", run_pipelined),
+                     ("graph", run_graph)):
         fn()                                  # warm-up: allocator, code objects
         torch.cuda.synchronize()
         reps = []
@@ -362,7 +382,11 @@ def minibatch_bench(mp, torch, dev, n_batches=64, h=256):
         bb = algorithmic_bytes(t["n"], t["e"], h, 4, 8)
         b_total += bb["build"] + bb["fwd"] + bb["bwd"]
     e_total = sum(t["e"] for t in staged)
+    run_graph()
+    torch.cuda.synchronize()
+    graph_equal = bool(torch.equal(y, ref[0]) and torch.equal(dx, ref[1]) and torch.equal(dw, ref[2]))
     res = {"batches": len(staged), "feature_width": h, "feature_dtype": "f32",
+           "graph_replay_equal_to_eager": graph_equal,
            "edges_total": e_total, "nodes_max": n_max, "edges_max": e_max,
            "algorithmic_bytes_total": b_total,
            "step": "per batch: build + mp_spmm_fwd + mp_spmm_dx_edge_grad"}
@@ -370,7 +394,7 @@ def minibatch_bench(mp, torch, dev, n_batches=64, h=256):
         res[name] = {"ms_total": round(ms, 3), "ms_per_batch": round(ms / len(staged), 4),
                      "GBps": round(b_total / (ms * 1e-3) / 1e9, 1),
                      "edges_per_s": round(e_total / (ms * 1e-3), 1)}
-    del staged, y, dx, dw, wss
+    del staged, y, dx, dw, wss, cg
     torch.cuda.empty_cache()
     return res
 
@@ -958,7 +982,8 @@ def main():
         log("minibatch schedules (64 sampled batches) ...")
         out["minibatch"] = minibatch_bench(mp, torch, dev)
         log("minibatch ms per batch: " + ", ".join(
-            f"{k} {out['minibatch'][k]['ms_per_batch']}" for k in ("sync", "async", "pipelined")))
+            f"{k} {out['minibatch'][k]['ms_per_batch']}"
+            for k in ("sync", "async", "pipelined", "graph")))
     if not args.no_cpu_baseline:
         sample = e if args.cpu_full else min(args.cpu_sample_edges, e)
         log(f"cpu baseline: oracle on {sample} edges, one core ...")

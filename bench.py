@@ -493,7 +493,8 @@ def _short_name(name):
 
 
 def _per_op_counters(path, counters):
-    """{op: {counter: summed value, "kernels": {short name: dispatches}}} from a
+    """{op: {counter: summed value, "kernels": {short name: dispatches},
+    "per_kernel": {short name: {counter: summed value}}}} from a
     counter-collection CSV of a --profile-ops run: the dispatches between one
     marker and the next belong to one op."""
     rows = _read_csv(path)
@@ -511,12 +512,15 @@ def _per_op_counters(path, counters):
         hi = marks[k + 1] if k + 1 < len(marks) else ids[-1] + 1
         rec = {c: 0.0 for c in counters}
         rec["kernels"] = {}
+        rec["per_kernel"] = {}
         for i in ids:
             if lo < i < hi:
-                for c in counters:
-                    rec[c] += by_id[i].get(c, 0.0)
                 nm = _short_name(by_id[i]["name"])
                 rec["kernels"][nm] = rec["kernels"].get(nm, 0) + 1
+                pk = rec["per_kernel"].setdefault(nm, {c: 0.0 for c in counters})
+                for c in counters:
+                    rec[c] += by_id[i].get(c, 0.0)
+                    pk[c] += by_id[i].get(c, 0.0)
         out[op] = rec
     return out
 
@@ -588,6 +592,13 @@ def summarize_profiles(base):
         if op != "copy_calibration":
             ks = ", ".join(f"`{k}` x{v}" for k, v in fetch[op]["kernels"].items())
             lines.append(f"- {op}: {ks}")
+    lines += ["", "The build's kernels (one lowering of both directions; a line sums the "
+              "dispatches of one template):", "",
+              "| kernel | dispatches | GB read | GB written |", "|---|---:|---:|---:|"]
+    for nm, nd in fetch["build"]["kernels"].items():
+        rb = fetch["build"]["per_kernel"][nm]["FETCH_SIZE"] * 1024 * cal_f
+        wb = write["build"]["per_kernel"][nm]["WRITE_SIZE"] * 1024 * cal_w
+        lines.append(f"| `{nm}` | {nd} | {rb / 1e9:.3f} | {wb / 1e9:.3f} |")
     lines += ["", "`profiles/traffic.json` holds the same figures with a hash of the code of "
               "each op's source files; bench.py reports an op's traffic only while that hash "
               "matches.", "", "Generated by `" + PROFILE_COMMANDS["summary"] + "`.", ""]

@@ -42,7 +42,7 @@ struct LowerLayout {
     size_t k0[2], k1[2];      // [E] u32: ping-pong keys
     size_t v0[2], o0[2];      // [E] u32: one ordinal and one endpoint buffer
     size_t hist[2];           // [256 * tiles] u32 per-tile digit counts (digit-major)
-    size_t dtot[2];           // [256] u32 digit totals of the current pass
+    size_t seg[2];            // [256 * 8] u32 segment totals of the count scan
     size_t total;
 };
 LowerLayout lower_layout(int64_t n, int64_t e);

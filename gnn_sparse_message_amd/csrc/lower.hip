@@ -44,6 +44,22 @@ constexpr int kItemsSmall = 4;                    // the same for small lists: 1
 constexpr int kBins = 256;                        // 8-bit digits
 constexpr int kDigitBits = 8;                     // at most 8 bits per pass
 constexpr int kPlanBits = 6;                      // plan keys 32 - class lie in [0, 32]
+constexpr int kScanSegs = 8;                      // most blocks per digit in the count scan
+constexpr int64_t kScanSegTiles = 2048;           // tiles per extra segment
+
+// Segments of a digit's count row: one per 2048 tiles, at most kScanSegs (a
+// short row is scanned by one block, as more blocks would only add launch
+// work).
+__host__ __device__ inline int scan_segs(int64_t ntiles) {
+    const int64_t k = ntiles / kScanSegTiles;
+    return k < 1 ? 1 : (k > kScanSegs ? kScanSegs : (int)k);
+}
+
+// Tiles per segment (the last segment may be shorter).
+__host__ __device__ inline int64_t scan_seg_len(int64_t ntiles) {
+    const int k = scan_segs(ntiles);
+    return (ntiles + k - 1) / k;
+}
 
 static_assert(kBlock == kBins, "scan and downsweep map one thread to one digit");
 static_assert(kInfoPlanT - kInfoPlanF == kBins, "one plan record holds every digit total");
@@ -166,8 +182,9 @@ struct PassDir {
     KeySrc keys;
     Payload pl;
     uint32_t *hist;   // [kBins * ntiles] per-tile digit counts, digit-major
-    uint32_t *dtot;   // [kBins] digit totals (from the scan, or from tile 0 of an
-                      // inline-scan downsweep when not nullptr)
+    uint32_t *seg;    // [kBins * kScanSegs] per-segment digit totals from the scan
+    uint32_t *dtot;   // [kBins] digit totals, written by tile 0 of the downsweep when
+                      // not nullptr
 };
 
 // Digit counts of one tile: k[r] is the key at tile-local index li0 + r * 64,
@@ -199,7 +216,75 @@ __device__ __forceinline__ void tile_digit_counts(const uint32_t (&k)[IT], int l
     hist[(int64_t)d * ntiles + t] = c;
 }
 
-template <class KeySrc, bool kDual, int IT>
+// Digits of at most this many bits may be counted with tile_lane_counts.
+constexpr int kLaneDigitBits = 7;
+constexpr int kLaneBins = 1 << kLaneDigitBits;
+
+// The same counts for digits below kLaneBins, with lane-private byte counters
+// instead of matching: word (j, lane) of a wave's table holds, one byte per
+// digit, how many of that lane's keys have digit 4j, 4j+1, 4j+2 or 4j+3, so
+// each key is one LDS add to a word no other lane touches (no ballots, no
+// bank or address conflicts).  The reduction sums 8 lanes' words bytewise
+// (at most 8 * IT per byte, below 256), splits the bytes into 16-bit fields
+// and adds those over the waves and the 8 lanes of a group.  Digits from
+// kLaneBins to kBins - 1 are written as 0.  Contains barriers: every thread
+// of the block calls it.
+template <int IT>
+__device__ __forceinline__ void tile_lane_counts(const uint32_t (&k)[IT], int li0, int lim,
+                                                 int shift, uint32_t mask,
+                                                 uint32_t *__restrict__ hist, int64_t ntiles,
+                                                 int64_t t) {
+    static_assert(8 * IT < 256, "a byte holds the keys of 8 lanes for one digit");
+    constexpr int kRows = kLaneBins / 4;                      // words per lane per wave
+    constexpr int kWords = kWavesPerBlock * kRows * kWave;
+    __shared__ uint4 s_lc4[kWords / 4];
+    uint32_t *s_lc = reinterpret_cast<uint32_t *>(s_lc4);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    for (int i = threadIdx.x; i < kWords / 4; i += kBlock) s_lc4[i] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    uint32_t *mine = s_lc + wv * kRows * kWave + lane;
+#pragma unroll
+    for (int r = 0; r < IT; ++r) {
+        const uint32_t d = (k[r] >> shift) & mask;          // keys past the tile add 0
+        const uint32_t one = li0 + r * kWave < lim ? 1u : 0u;
+        __hip_atomic_fetch_add(mine + (d >> 2) * kWave, one << ((d & 3u) * 8u), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();
+    // Thread (j, part) adds the words of lanes [8 part, 8 part + 8) of row j.
+    const int j = threadIdx.x >> 3, part = threadIdx.x & 7;
+    uint32_t lo = 0u, hi = 0u;                                // digits (4j, 4j+2), (4j+1, 4j+3)
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+        const uint4 *q = reinterpret_cast<const uint4 *>(s_lc + (w * kRows + j) * kWave + part * 8);
+        const uint4 x = q[0], y = q[1];
+        const uint32_t b = x.x + x.y + x.z + x.w + y.x + y.y + y.z + y.w;
+        lo += b & 0x00ff00ffu;
+        hi += (b >> 8) & 0x00ff00ffu;
+    }
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+        lo += __shfl_xor(lo, off);
+        hi += __shfl_xor(hi, off);
+    }
+    const uint32_t f = (part & 1) ? hi : lo;
+    const uint32_t c = (part & 2) ? f >> 16 : f & 0xffffu;
+    const int d = part < 4 ? 4 * j + part : kLaneBins + 4 * j + (part - 4);
+    hist[(int64_t)d * ntiles + t] = part < 4 ? c : 0u;
+}
+
+// Digit counts of a tile by whichever method the template selects.
+template <bool kLane, int IT>
+__device__ __forceinline__ void count_tile(const uint32_t (&k)[IT], int li0, int lim, int shift,
+                                           uint32_t mask, uint32_t *__restrict__ hist,
+                                           int64_t ntiles, int64_t t) {
+    if constexpr (kLane) tile_lane_counts(k, li0, lim, shift, mask, hist, ntiles, t);
+    else tile_digit_counts(k, li0, lim, shift, mask, hist, ntiles, t);
+}
+
+// kLane: the pass's digits have at most kLaneDigitBits bits.
+template <class KeySrc, bool kDual, bool kLane, int IT>
 __global__ __launch_bounds__(kBlock) void rs_upsweep(PassDir<KeySrc> a0, PassDir<KeySrc> a1,
                                                      int64_t count, int shift, int bits,
                                                      int64_t ntiles) {
@@ -219,7 +304,7 @@ __global__ __launch_bounds__(kBlock) void rs_upsweep(PassDir<KeySrc> a0, PassDir
         const int li = li0 + r * kWave;
         k[r] = li < lim ? tk(li) : 0u;
     }
-    tile_digit_counts(k, li0, lim, shift, mask, a.hist, ntiles, t);
+    count_tile<kLane>(k, li0, lim, shift, mask, a.hist, ntiles, t);
 }
 
 // Intake: block t copies tile t of the caller's endpoints to int32, checking
@@ -228,7 +313,7 @@ __global__ __launch_bounds__(kBlock) void rs_upsweep(PassDir<KeySrc> a0, PassDir
 // both keys, dst for the forward sort and src for the transpose sort, so the
 // first pass of each direction needs no upsweep of its own.  Tiles as in the
 // radix passes (IT keys per thread, digit-major counts).
-template <typename IdxT, int IT>
+template <typename IdxT, bool kLane, int IT>
 __global__ __launch_bounds__(kBlock) void intake_count_kernel(
     const IdxT *__restrict__ src, const IdxT *__restrict__ dst, int64_t e, int64_t n,
     int32_t *__restrict__ src32, int32_t *__restrict__ dst32, uint32_t *__restrict__ flag,
@@ -242,13 +327,22 @@ __global__ __launch_bounds__(kBlock) void intake_count_kernel(
     const int li0 = wv * (kWave * IT) + lane;
     uint32_t kd[IT], ks[IT];
     bool bad = false;
+    // Every load is issued before the first store, so that a wave has all of
+    // its tile's loads in flight at once.
+    int64_t svs[IT], dvs[IT];
+#pragma unroll
+    for (int r = 0; r < IT; ++r) {
+        const int li = li0 + r * kWave;
+        svs[r] = li < lim ? (int64_t)src[tbase + li] : 0;
+        dvs[r] = li < lim ? (int64_t)dst[tbase + li] : 0;
+    }
 #pragma unroll
     for (int r = 0; r < IT; ++r) {
         const int li = li0 + r * kWave;
         kd[r] = ks[r] = 0u;
         if (li < lim) {
-            const int64_t sv = (int64_t)src[tbase + li];
-            const int64_t dv = (int64_t)dst[tbase + li];
+            const int64_t sv = svs[r];
+            const int64_t dv = dvs[r];
             const bool ok_s = sv >= 0 && sv < n;
             const bool ok_d = dv >= 0 && dv < n;
             ks[r] = ok_s ? (uint32_t)sv : 0u;
@@ -260,42 +354,52 @@ __global__ __launch_bounds__(kBlock) void intake_count_kernel(
     }
     if (bad) *flag = 1u;   // plain store: every writer stores the same value
     const uint32_t mask = (1u << bits) - 1u;
-    tile_digit_counts(kd, li0, lim, 0, mask, hist_f, ntiles, t);
+    count_tile<kLane>(kd, li0, lim, 0, mask, hist_f, ntiles, t);
     __syncthreads();       // the counts' LDS is reused by the second key
-    tile_digit_counts(ks, li0, lim, 0, mask, hist_t, ntiles, t);
+    count_tile<kLane>(ks, li0, lim, 0, mask, hist_t, ntiles, t);
 }
 
-// One block per digit (and direction): exclusive scan, in tile order, of that
-// digit's per-tile counts (in place), and the digit's total.
+// One block per (direction, digit, segment): exclusive scan, in tile order, of
+// that digit's per-tile counts over the segment's tiles (in place), and the
+// segment's total.  The downsweep adds the totals of the earlier segments.
+// Only the pass's own digits are scanned: the rows of the others hold zeros,
+// which are their own exclusive scan.
 template <bool kDual>
 __global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist0,
-                                                  uint32_t *__restrict__ dtot0,
+                                                  uint32_t *__restrict__ seg0,
                                                   uint32_t *__restrict__ hist1,
-                                                  uint32_t *__restrict__ dtot1, int64_t ntiles) {
+                                                  uint32_t *__restrict__ seg1, int64_t ntiles,
+                                                  int digits) {
     constexpr int kPer = 16;
-    const int dir = kDual && blockIdx.x >= kBins ? 1 : 0;
-    const int digit = blockIdx.x - dir * kBins;
+    const int segs = scan_segs(ntiles);
+    const int per_dir = digits * segs;
+    const int dir = kDual && (int)blockIdx.x >= per_dir ? 1 : 0;
+    const int rem = (int)blockIdx.x - dir * per_dir;
+    const int digit = rem / segs, sg = rem % segs;
+    const int64_t len = scan_seg_len(ntiles);
+    const int64_t lo = sg * len;
+    const int64_t hi = lo + len < ntiles ? lo + len : ntiles;
     uint32_t *row = (dir ? hist1 : hist0) + (int64_t)digit * ntiles;
     uint32_t carry = 0;
-    for (int64_t chunk = 0; chunk < ntiles; chunk += (int64_t)kBlock * kPer) {
+    for (int64_t chunk = lo; chunk < hi; chunk += (int64_t)kBlock * kPer) {
         const int64_t beg = chunk + (int64_t)threadIdx.x * kPer;
         uint32_t v[kPer];
         uint32_t sum = 0;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            v[j] = beg + j < ntiles ? row[beg + j] : 0u;
+            v[j] = beg + j < hi ? row[beg + j] : 0u;
             sum += v[j];
         }
         uint32_t total;
         uint32_t run = carry + block_exclusive_scan(sum, &total);
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            if (beg + j < ntiles) row[beg + j] = run;
+            if (beg + j < hi) row[beg + j] = run;
             run += v[j];
         }
         carry += total;
     }
-    if (threadIdx.x == 0) (dir ? dtot1 : dtot0)[digit] = carry;
+    if (threadIdx.x == 0) (dir ? seg1 : seg0)[digit * kScanSegs + sg] = carry;
 }
 
 // kInlineScan: hist holds raw per-tile counts (no scan kernel ran); each thread
@@ -368,8 +472,23 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
         }
         if (t == 0 && a.dtot) a.dtot[tid] = dsum;
     } else {
-        dsum = a.dtot[tid];
+        // The scan left the exclusive count within this tile's segment; add the
+        // totals of the segments before it (digits beyond the pass have none).
+        const int segs = scan_segs(ntiles);
+        const int64_t sg = t / scan_seg_len(ntiles);
         before_tile = a.hist[(int64_t)tid * ntiles + t];
+        dsum = 0u;
+        if (tid < (1 << bits)) {
+            uint32_t c[kScanSegs];
+#pragma unroll
+            for (int j = 0; j < kScanSegs; ++j) c[j] = j < segs ? a.seg[tid * kScanSegs + j] : 0u;
+#pragma unroll
+            for (int j = 0; j < kScanSegs; ++j) {
+                dsum += c[j];
+                before_tile += j < sg ? c[j] : 0u;
+            }
+        }
+        if (t == 0 && a.dtot) a.dtot[tid] = dsum;
     }
     const uint32_t dbase = block_exclusive_scan(dsum, &all);
     s_cnt[0][tid] = tstart;
@@ -487,20 +606,37 @@ int first_pass_bits(int64_t n) {
     return per < bits ? per : bits;
 }
 
+// Large tiles count digits of at most kLaneDigitBits bits with lane-private
+// counters; small tiles (4 keys per lane) and wider digits match with ballots.
+template <int IT>
+constexpr bool lane_counts(int bits) {
+    return IT == kItems && bits <= kLaneDigitBits;
+}
+
+template <bool kLane, int IT>
+void intake_launch(const void *src, const void *dst, mp_dtype idx_dtype, int64_t e, int64_t n,
+                   mp_graph *g, int first_bits, uint32_t *hist_f, uint32_t *hist_t, int64_t nt,
+                   hipStream_t s) {
+    if (idx_dtype == MP_I64)
+        intake_count_kernel<int64_t, kLane, IT><<<(unsigned)nt, kBlock, 0, s>>>(
+            static_cast<const int64_t *>(src), static_cast<const int64_t *>(dst), e, n, g->src,
+            g->dst, g->info + kInfoFlag, first_bits, hist_f, hist_t, nt);
+    else
+        intake_count_kernel<int32_t, kLane, IT><<<(unsigned)nt, kBlock, 0, s>>>(
+            static_cast<const int32_t *>(src), static_cast<const int32_t *>(dst), e, n, g->src,
+            g->dst, g->info + kInfoFlag, first_bits, hist_f, hist_t, nt);
+}
+
 // Counting intake over tiles of 256 * IT edges.
 template <int IT>
 void intake_count(const void *src, const void *dst, mp_dtype idx_dtype, int64_t e, int64_t n,
                   mp_graph *g, int first_bits, uint32_t *hist_f, uint32_t *hist_t,
                   hipStream_t s) {
     const int64_t nt = tiles_for(e, IT);
-    if (idx_dtype == MP_I64)
-        intake_count_kernel<int64_t, IT><<<(unsigned)nt, kBlock, 0, s>>>(
-            static_cast<const int64_t *>(src), static_cast<const int64_t *>(dst), e, n, g->src,
-            g->dst, g->info + kInfoFlag, first_bits, hist_f, hist_t, nt);
+    if (lane_counts<IT>(first_bits))
+        intake_launch<true, IT>(src, dst, idx_dtype, e, n, g, first_bits, hist_f, hist_t, nt, s);
     else
-        intake_count_kernel<int32_t, IT><<<(unsigned)nt, kBlock, 0, s>>>(
-            static_cast<const int32_t *>(src), static_cast<const int32_t *>(dst), e, n, g->src,
-            g->dst, g->info + kInfoFlag, first_bits, hist_f, hist_t, nt);
+        intake_launch<false, IT>(src, dst, idx_dtype, e, n, g, first_bits, hist_f, hist_t, nt, s);
 }
 
 
@@ -521,15 +657,21 @@ mp_status radix_pass(const PassDir<KeySrc> &d0, const PassDir<KeySrc> &d1, int64
                      int shift, int bits, hipStream_t s, bool counted = false) {
     const int64_t ntiles = tiles_for(count, IT);
     const unsigned grid = (unsigned)((kDual ? 2 : 1) * ntiles);
-    if (!counted)
-        rs_upsweep<KeySrc, kDual, IT><<<grid, kBlock, 0, s>>>(d0, d1, count, shift, bits,
-                                                              ntiles);
+    if (!counted) {
+        if (lane_counts<IT>(bits))
+            rs_upsweep<KeySrc, kDual, true, IT><<<grid, kBlock, 0, s>>>(d0, d1, count, shift, bits,
+                                                                        ntiles);
+        else
+            rs_upsweep<KeySrc, kDual, false, IT><<<grid, kBlock, 0, s>>>(d0, d1, count, shift,
+                                                                         bits, ntiles);
+    }
     if (ntiles <= kInlineScanMaxTiles) {
         rs_downsweep<KeySrc, kIota, kOther, kWriteKeys, kDual, true, IT>
             <<<grid, kBlock, 0, s>>>(d0, d1, count, shift, bits, ntiles);
     } else {
-        rs_scan<kDual><<<(kDual ? 2 : 1) * kBins, kBlock, 0, s>>>(d0.hist, d0.dtot, d1.hist,
-                                                                   d1.dtot, ntiles);
+        const int digits = 1 << bits;
+        rs_scan<kDual><<<(kDual ? 2 : 1) * digits * scan_segs(ntiles), kBlock, 0, s>>>(
+            d0.hist, d0.seg, d1.hist, d1.seg, ntiles, digits);
         rs_downsweep<KeySrc, kIota, kOther, kWriteKeys, kDual, false, IT>
             <<<grid, kBlock, 0, s>>>(d0, d1, count, shift, bits, ntiles);
     }
@@ -539,7 +681,7 @@ mp_status radix_pass(const PassDir<KeySrc> &d0, const PassDir<KeySrc> &d1, int64
 
 // Sort buffers of one direction.
 struct SortBufs {
-    uint32_t *k0, *k1, *v0, *o0, *hist, *dtot;
+    uint32_t *k0, *k1, *v0, *o0, *hist, *seg;
 };
 
 // One direction of the edge sort: keys, the opposite endpoint, and where the
@@ -571,7 +713,8 @@ mp_status sort_edges(const EdgeDir *dirs, int64_t e, int64_t n, const uint32_t *
         pd[i].pl.vals_in = nullptr;
         pd[i].pl.other_in = reinterpret_cast<const uint32_t *>(dirs[i].other);
         pd[i].hist = dirs[i].b.hist;
-        pd[i].dtot = dirs[i].b.dtot;
+        pd[i].seg = dirs[i].b.seg;
+        pd[i].dtot = nullptr;
     }
     if (!kDual) pd[1] = pd[0];
     for (int pass = 0; pass < passes; ++pass) {
@@ -625,16 +768,18 @@ mp_status row_pointers(const RowsDir &r0, const RowsDir &r1, int64_t e, int64_t 
 // many row tiles).  The digit totals, i.e. the rows per class, land in
 // totals0 / totals1.
 template <int IT>
-mp_status plans(int64_t n, mp_graph *g, uint32_t *hist0, uint32_t *hist1, uint32_t *totals0,
-                uint32_t *totals1, hipStream_t s) {
+mp_status plans(int64_t n, mp_graph *g, const SortBufs &b0, const SortBufs &b1,
+                uint32_t *totals0, uint32_t *totals1, hipStream_t s) {
     PassDir<KeysFromDegree> p0, p1;
     p0.keys = KeysFromDegree{g->rowptr};
     p1.keys = KeysFromDegree{g->rowptr_t};
     p0.pl = Payload{nullptr, nullptr, nullptr, reinterpret_cast<uint32_t *>(g->row_plan), nullptr};
     p1.pl = Payload{nullptr, nullptr, nullptr, reinterpret_cast<uint32_t *>(g->row_plan_t),
                     nullptr};
-    p0.hist = hist0;
-    p1.hist = hist1;
+    p0.hist = b0.hist;
+    p1.hist = b1.hist;
+    p0.seg = b0.seg;
+    p1.seg = b1.seg;
     p0.dtot = totals0;
     p1.dtot = totals1;
     return radix_pass<KeysFromDegree, true, false, false, true, IT>(p0, p1, n, 0, kPlanBits, s);
@@ -664,7 +809,7 @@ LowerLayout lower_layout(int64_t n, int64_t e) {
             L.o0[i] = off; off += ebytes;
         }
         L.hist[i] = off; off += hbytes;
-        L.dtot[i] = off; off += align_up(kBins * sizeof(uint32_t));
+        L.seg[i] = off; off += align_up((size_t)kBins * kScanSegs * sizeof(uint32_t));
     }
     L.total = off;
     return L;
@@ -691,7 +836,7 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
     SortBufs b[2];
     for (int i = 0; i < 2; ++i)
         b[i] = SortBufs{at(L.k0[i]), at(L.k1[i]), at(L.v0[i]), at(L.o0[i]), at(L.hist[i]),
-                        at(L.dtot[i])};
+                        at(L.seg[i])};
     uint32_t *info = g->info;
 
     // A fill kernel, not a memset: the sequence stays valid under graph capture.
@@ -730,9 +875,8 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
     }
     if (st == MP_OK)
         st = dual_mode(e)
-            ? plans<kItemsSmall>(n, g, b[0].hist, b[1].hist, info + kInfoPlanF,
-                                 info + kInfoPlanT, s)
-            : plans<kItems>(n, g, b[0].hist, b[1].hist, info + kInfoPlanF, info + kInfoPlanT, s);
+            ? plans<kItemsSmall>(n, g, b[0], b[1], info + kInfoPlanF, info + kInfoPlanT, s)
+            : plans<kItems>(n, g, b[0], b[1], info + kInfoPlanF, info + kInfoPlanT, s);
     if (st != MP_OK) return st;
 
     *bad_index = 0;

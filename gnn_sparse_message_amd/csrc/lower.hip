@@ -436,6 +436,23 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
         const int li = li0 + r * kWave;
         k[r] = li < lim ? tk(li) : 0u;
     }
+    // The ordinal and endpoint payloads.  Small tiles (few keys per thread, few
+    // registers) load them with the keys, so a block waits for memory once;
+    // large tiles load each just before writing it out (see below).
+    constexpr bool kEarly = IT <= kItemsSmall;
+    uint32_t v[IT], o[IT];
+    auto load_payloads = [&]() {
+        const uint32_t *vin = kIotaVals ? nullptr : pl.vals_in + tbase;
+        const uint32_t *oin = kOther ? pl.other_in + tbase : nullptr;
+#pragma unroll
+        for (int r = 0; r < IT; ++r) {
+            const int li = li0 + r * kWave;
+            if constexpr (kIotaVals) v[r] = (uint32_t)tbase + (uint32_t)li;
+            else v[r] = li < lim ? vin[li] : 0u;
+            if constexpr (kOther) o[r] = li < lim ? oin[li] : 0u;
+        }
+    };
+    if constexpr (kEarly) load_payloads();
     __syncthreads();
     // Rank inside the wave: earlier rounds (running count) + lower lanes now.
     uint32_t pos[IT];
@@ -515,9 +532,7 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
             gp[j] = s_gbase[d] + ((uint32_t)i - s_tstart[d]);
         }
     }
-    // Regroup each payload through LDS, then write it out in digit runs.  The
-    // ordinal and endpoint payloads are read only now, which keeps few
-    // registers live across the ranking (more resident blocks per CU).
+    // Regroup each payload through LDS, then write it out in digit runs.
     auto emit = [&](const uint32_t(&src)[IT], uint32_t *__restrict__ out) {
 #pragma unroll
         for (int r = 0; r < IT; ++r)
@@ -529,26 +544,31 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
         __syncthreads();
     };
     if (kWriteKeys) emit(k, pl.keys_out);
-    {
-        uint32_t v[IT];
-        const uint32_t *vin = kIotaVals ? nullptr : pl.vals_in + tbase;
-#pragma unroll
-        for (int r = 0; r < IT; ++r) {
-            const int li = li0 + r * kWave;
-            if (kIotaVals) v[r] = (uint32_t)tbase + (uint32_t)li;
-            else v[r] = li < lim ? vin[li] : 0u;
-        }
+    if constexpr (kEarly) {
         emit(v, pl.vals_out);
-    }
-    if (kOther) {
-        uint32_t o[IT];
-        const uint32_t *oin = pl.other_in + tbase;
+        if constexpr (kOther) emit(o, pl.other_out);
+    } else {
+        // One payload at a time keeps few registers live across the ranking
+        // (more resident blocks per CU for the large tiles).
+        {
+            const uint32_t *vin = kIotaVals ? nullptr : pl.vals_in + tbase;
 #pragma unroll
-        for (int r = 0; r < IT; ++r) {
-            const int li = li0 + r * kWave;
-            o[r] = li < lim ? oin[li] : 0u;
+            for (int r = 0; r < IT; ++r) {
+                const int li = li0 + r * kWave;
+                if constexpr (kIotaVals) v[r] = (uint32_t)tbase + (uint32_t)li;
+                else v[r] = li < lim ? vin[li] : 0u;
+            }
+            emit(v, pl.vals_out);
         }
-        emit(o, pl.other_out);
+        if constexpr (kOther) {
+            const uint32_t *oin = pl.other_in + tbase;
+#pragma unroll
+            for (int r = 0; r < IT; ++r) {
+                const int li = li0 + r * kWave;
+                o[r] = li < lim ? oin[li] : 0u;
+            }
+            emit(o, pl.other_out);
+        }
     }
 }
 

@@ -404,12 +404,27 @@ __global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist0,
 
 // kInlineScan: hist holds raw per-tile counts (no scan kernel ran); each thread
 // sums its digit's counts over all tiles and over the tiles before this one.
+// kDma (large tiles carrying the endpoint, payload inputs 16-byte aligned):
+// the ordinal and endpoint tiles are copied to LDS by direct global->LDS loads
+// issued with the keys, so they arrive during the ranking without holding
+// registers; each is then regrouped in place.
 template <class KeySrc, bool kIotaVals, bool kOther, bool kWriteKeys, bool kDual,
-          bool kInlineScan, int IT>
+          bool kInlineScan, int IT, bool kDma = false>
 __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassDir<KeySrc> a1,
                                                        int64_t count, int shift, int bits,
                                                        int64_t ntiles) {
-    __shared__ uint32_t s_buf[(kBlock * IT)];          // one payload at a time, in tile-sorted order
+    static_assert(!kDma || (kOther && IT % 4 == 0), "the copied tiles are whole 16-byte rows");
+    constexpr int kTile = kBlock * IT;
+    // kDma: [0, kTile) the ordinal tile, then the regroup buffer of the keys;
+    // [kTile, 2 kTile) the endpoint tile.  Otherwise one regroup buffer.
+    uint32_t *pay;
+    if constexpr (kDma) {
+        __shared__ __attribute__((aligned(16))) uint32_t s_pay[2 * kTile];
+        pay = s_pay;
+    } else {
+        __shared__ uint32_t s_buf[kTile];              // one payload at a time, in tile-sorted order
+        pay = s_buf;
+    }
     __shared__ uint8_t s_dig[(kBlock * IT)];           // digit of each tile-sorted position
     __shared__ uint32_t s_cnt[kWavesPerBlock][kBins];
     __shared__ uint32_t s_tstart[kBins];
@@ -429,7 +444,11 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
     const KeySrc tk = a.keys.at(tbase);
     const int li0 = wv * (kWave * IT) + lane;                   // tile-local index, round 0
 
-    for (int i = tid; i < kWavesPerBlock * kBins; i += kBlock) (&s_cnt[0][0])[i] = 0u;
+    // Each wave clears and then ranks with its own row of counters, so no block
+    // barrier is needed before the ranking (a wave's LDS accesses stay in
+    // order), and the copies below stay in flight through it.
+#pragma unroll
+    for (int m = 0; m < kBins / kWave; ++m) s_cnt[wv][lane + m * kWave] = 0u;
     uint32_t k[IT];
 #pragma unroll
     for (int r = 0; r < IT; ++r) {
@@ -453,7 +472,36 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
         }
     };
     if constexpr (kEarly) load_payloads();
-    __syncthreads();
+    // kDma: each wave copies its own quarter of a payload tile, which is exactly
+    // the slots its threads read back (tile-local indices wv * 1024 + [0, 1024)):
+    // rows of 64 lanes x 16 bytes for a whole tile, 64 x 4 bytes (indices past
+    // the list read the tile's first word, never used) for the last one.
+    auto dma = [&](const uint32_t *src, uint32_t *dst) {
+        if constexpr (kDma) {
+            typedef __attribute__((address_space(3))) void *lds_ptr;
+            const int w0 = wv * (kWave * IT);
+            if (lim == kTile) {
+#pragma unroll
+                for (int i = 0; i < IT / 4; ++i) {
+                    const int w = w0 + i * (kWave * 4);
+                    __builtin_amdgcn_global_load_lds(src + tbase + w + lane * 4, (lds_ptr)(dst + w),
+                                                     16, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < IT; ++i) {
+                    const int w = w0 + i * kWave;
+                    const int li = w + lane;
+                    __builtin_amdgcn_global_load_lds(src + tbase + (li < lim ? li : 0),
+                                                     (lds_ptr)(dst + w), 4, 0, 0);
+                }
+            }
+        }
+    };
+    if constexpr (kDma) {
+        if constexpr (!kIotaVals) dma(pl.vals_in, pay);
+        dma(pl.other_in, pay + kTile);
+    }
     // Rank inside the wave: earlier rounds (running count) + lower lanes now.
     uint32_t pos[IT];
 #pragma unroll
@@ -533,16 +581,42 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
         }
     }
     // Regroup each payload through LDS, then write it out in digit runs.
-    auto emit = [&](const uint32_t(&src)[IT], uint32_t *__restrict__ out) {
+    auto emit_to = [&](const uint32_t(&src)[IT], uint32_t *buf, uint32_t *__restrict__ out) {
 #pragma unroll
         for (int r = 0; r < IT; ++r)
-            if (li0 + r * kWave < lim) s_buf[pos[r]] = src[r];
+            if (li0 + r * kWave < lim) buf[pos[r]] = src[r];
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < IT; ++j)
-            if ((int64_t)gp[j] < count) out[gp[j]] = s_buf[tid + j * kBlock];
+            if ((int64_t)gp[j] < count) out[gp[j]] = buf[tid + j * kBlock];
         __syncthreads();
     };
+    auto emit = [&](const uint32_t(&src)[IT], uint32_t *__restrict__ out) {
+        emit_to(src, pay, out);
+    };
+    if constexpr (kDma) {
+        // The copies were issued before the ranking; wait for this wave's (no
+        // store is outstanding yet), then regroup each tile in place: every
+        // thread reads its own slots, and writes them by rank after a barrier.
+        __builtin_amdgcn_s_waitcnt(0);
+        auto emit_lds = [&](uint32_t *buf, uint32_t *__restrict__ out) {
+            uint32_t x[IT];
+#pragma unroll
+            for (int r = 0; r < IT; ++r) x[r] = buf[li0 + r * kWave];
+            __syncthreads();
+            emit_to(x, buf, out);
+        };
+        if constexpr (kIotaVals) {
+#pragma unroll
+            for (int r = 0; r < IT; ++r) v[r] = (uint32_t)tbase + (uint32_t)(li0 + r * kWave);
+            emit_to(v, pay, pl.vals_out);
+        } else {
+            emit_lds(pay, pl.vals_out);
+        }
+        emit_lds(pay + kTile, pl.other_out);
+        if (kWriteKeys) emit_to(k, pay, pl.keys_out);
+        return;
+    }
     if (kWriteKeys) emit(k, pl.keys_out);
     if constexpr (kEarly) {
         emit(v, pl.vals_out);
@@ -669,6 +743,8 @@ constexpr int64_t kInlineScanMaxTiles = 64;
 
 bool dual_mode(int64_t e) { return e <= kDualMaxEdges; }
 
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
 // One radix pass for one direction (d1 unused) or both (kDual), with tiles of
 // 256 * IT keys.
 // counted: the per-tile digit counts are already in hist (the counting intake).
@@ -692,8 +768,16 @@ mp_status radix_pass(const PassDir<KeySrc> &d0, const PassDir<KeySrc> &d1, int64
         const int digits = 1 << bits;
         rs_scan<kDual><<<(kDual ? 2 : 1) * digits * scan_segs(ntiles), kBlock, 0, s>>>(
             d0.hist, d0.seg, d1.hist, d1.seg, ntiles, digits);
-        rs_downsweep<KeySrc, kIota, kOther, kWriteKeys, kDual, false, IT>
-            <<<grid, kBlock, 0, s>>>(d0, d1, count, shift, bits, ntiles);
+        // Large single-direction edge passes copy their payload tiles to LDS
+        // directly when the inputs allow 16-byte rows.
+        const bool dma = kOther && !kDual && IT == kItems &&
+                         (kIota || aligned16(d0.pl.vals_in)) && aligned16(d0.pl.other_in);
+        if (dma)
+            rs_downsweep<KeySrc, kIota, kOther, kWriteKeys, kDual, false, IT, kOther && !kDual>
+                <<<grid, kBlock, 0, s>>>(d0, d1, count, shift, bits, ntiles);
+        else
+            rs_downsweep<KeySrc, kIota, kOther, kWriteKeys, kDual, false, IT>
+                <<<grid, kBlock, 0, s>>>(d0, d1, count, shift, bits, ntiles);
     }
     MP_HIP_CHECK(hipGetLastError(), "radix pass launch");
     return MP_OK;

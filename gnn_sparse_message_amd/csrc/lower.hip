@@ -45,6 +45,9 @@ constexpr int kBins = 256;                        // 8-bit digits
 constexpr int kDigitBits = 8;                     // at most 8 bits per pass
 constexpr int kPlanBits = 6;                      // plan keys 32 - class lie in [0, 32]
 constexpr int kScanSegs = 8;                      // most blocks per digit in the count scan
+// Rows of 64 lanes x 16 bytes per wave that copy the segment totals of all
+// kBins digits (kBins * kScanSegs words) with the four waves of a block.
+constexpr int kSegRowsPerWave = kBins * kScanSegs / (64 * 4 * 4);
 constexpr int64_t kScanSegTiles = 2048;           // tiles per extra segment
 
 // Segments of a digit's count row: one per 2048 tiles, at most kScanSegs (a
@@ -413,7 +416,9 @@ template <class KeySrc, bool kIotaVals, bool kOther, bool kWriteKeys, bool kDual
 __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassDir<KeySrc> a1,
                                                        int64_t count, int shift, int bits,
                                                        int64_t ntiles) {
-    static_assert(!kDma || (kOther && IT % 4 == 0), "the copied tiles are whole 16-byte rows");
+    static_assert(!kDma || (kOther && IT % 4 == 0 && !kInlineScan),
+                  "the copied tiles are whole 16-byte rows; the offsets come from the scan");
+    static_assert(kBins == kWavesPerBlock * kWave, "one digit offset per thread");
     constexpr int kTile = kBlock * IT;
     // kDma: [0, kTile) the ordinal tile, then the regroup buffer of the keys;
     // [kTile, 2 kTile) the endpoint tile.  Otherwise one regroup buffer.
@@ -502,6 +507,30 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
         if constexpr (!kIotaVals) dma(pl.vals_in, pay);
         dma(pl.other_in, pay + kTile);
     }
+    // kDma (the scan kernel ran): this tile's exclusive count of every digit
+    // within its segment (one word per lane, wave w taking digits 64w ...) and
+    // the segment totals (16-byte rows), copied to LDS with the payloads.
+    __shared__ uint32_t s_hv[kDma ? kBins : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t s_sv[kDma ? kBins * kScanSegs : 1];
+    // (Every pointer is an argument, as in dma: built with the pass record's
+    // pointers taken inside the lambda, the host pass dropped this kernel's
+    // launch stub and the library failed to load.)
+    auto dma_offsets = [&](const uint32_t *hist, const uint32_t *seg, uint32_t *hv, uint32_t *sv) {
+        if constexpr (kDma) {
+            typedef __attribute__((address_space(3))) void *lds_ptr;
+            const int d = wv * kWave + lane;
+            __builtin_amdgcn_global_load_lds(hist + (int64_t)d * ntiles + t,
+                                             (lds_ptr)(hv + wv * kWave), 4, 0, 0);
+            // 16-byte rows of 64 lanes: kSegRowsPerWave per wave
+#pragma unroll
+            for (int i = 0; i < kSegRowsPerWave; ++i) {
+                const int w = (wv * kSegRowsPerWave + i) * (kWave * 4);
+                __builtin_amdgcn_global_load_lds(seg + w + lane * 4, (lds_ptr)(sv + w), 16, 0,
+                                                 0);
+            }
+        }
+    };
+    if constexpr (kDma) dma_offsets(a.hist, a.seg, s_hv, s_sv);
     // Rank inside the wave: earlier rounds (running count) + lower lanes now.
     uint32_t pos[IT];
 #pragma unroll
@@ -539,14 +568,20 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
     } else {
         // The scan left the exclusive count within this tile's segment; add the
         // totals of the segments before it (digits beyond the pass have none).
+        // kDma: both are in LDS already (the barriers after the ranking waited
+        // for every wave's copies).
         const int segs = scan_segs(ntiles);
         const int64_t sg = t / scan_seg_len(ntiles);
-        before_tile = a.hist[(int64_t)tid * ntiles + t];
+        if constexpr (kDma) before_tile = s_hv[tid];
+        else before_tile = a.hist[(int64_t)tid * ntiles + t];
         dsum = 0u;
         if (tid < (1 << bits)) {
             uint32_t c[kScanSegs];
 #pragma unroll
-            for (int j = 0; j < kScanSegs; ++j) c[j] = j < segs ? a.seg[tid * kScanSegs + j] : 0u;
+            for (int j = 0; j < kScanSegs; ++j) {
+                if constexpr (kDma) c[j] = j < segs ? s_sv[tid * kScanSegs + j] : 0u;
+                else c[j] = j < segs ? a.seg[tid * kScanSegs + j] : 0u;
+            }
 #pragma unroll
             for (int j = 0; j < kScanSegs; ++j) {
                 dsum += c[j];

@@ -166,3 +166,36 @@ def test_rejects_host_and_bad_dtype(mp):
                           torch.tensor([1, 0], device=DEV, dtype=torch.int16), 2)
     with pytest.raises(ValueError):
         mp.mp_graph_build(torch.tensor([0], device=DEV), torch.tensor([0], device=DEV), 0)
+
+
+@pytest.mark.parametrize("n,e,seed", [
+    (3_000_000, 5_000_000, 40),     # three passes: the second reads the first's output arrays
+    (1 << 21, (1 << 22) + 4096 * 5 + 3, 41),   # a ragged last tile
+])
+def test_large_list_unaligned_graph_arrays(mp, n, e, seed):
+    """Graph arrays need only 4-byte alignment.  With the CSR position maps and
+    columns 4 bytes past a 16-byte boundary the large passes that read them
+    take the register path instead of copying 16-byte rows to LDS; the result
+    is the aligned build's, bit for bit, and the oracle's."""
+    wl = synth.random_graph(n, e, 1, seed)
+    src = torch.from_numpy(wl.src).to(DEV)
+    dst = torch.from_numpy(wl.dst).to(DEV)
+    ref = mp.mp_graph_build(src, dst, n)
+    g = mp.Graph(n, e, DEV)
+    keep = []
+    for name in ("col", "edge_order", "col_t", "transpose_order"):
+        buf = torch.empty(e + 4, dtype=torch.int32, device=DEV)
+        view = buf[1:e + 1]                      # 4 bytes past the allocation's start
+        assert view.data_ptr() % 16 == 4
+        keep.append(buf)
+        g.arrays[name] = view
+        setattr(g._desc, name, mp._ptr(view))
+    ws = torch.empty(mp.mp_graph_build_workspace_size(n, e), dtype=torch.uint8, device=DEV)
+    st = mp._lib.mp_graph_build(mp._ptr(src), mp._ptr(dst), mp.MP_I64, n, e,
+                                mp.ctypes.byref(g._desc), mp._ptr(ws), ws.numel(), mp._stream(src))
+    assert st == 0
+    torch.cuda.synchronize()
+    for name in mp.Graph._ARRAYS:
+        assert torch.equal(g.arrays[name], ref.arrays[name]), name
+    assert g.class_count == ref.class_count and g.class_count_t == ref.class_count_t
+    check_structure(g, wl)

@@ -47,7 +47,7 @@ constexpr int kPlanBits = 6;                      // plan keys 32 - class lie in
 constexpr int kScanSegs = 8;                      // most blocks per digit in the count scan
 // Rows of 64 lanes x 16 bytes per wave that copy the segment totals of all
 // kBins digits (kBins * kScanSegs words) with the four waves of a block.
-constexpr int kSegRowsPerWave = kBins * kScanSegs / (64 * 4 * 4);
+constexpr int kSegRowsPerWave = kBins * kScanSegs / (kWave * 4 * kWavesPerBlock);
 constexpr int64_t kScanSegTiles = 2048;           // tiles per extra segment
 
 // Segments of a digit's count row: one per 2048 tiles, at most kScanSegs (a
@@ -408,9 +408,10 @@ __global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist0,
 // kInlineScan: hist holds raw per-tile counts (no scan kernel ran); each thread
 // sums its digit's counts over all tiles and over the tiles before this one.
 // kDma (large tiles carrying the endpoint, payload inputs 16-byte aligned):
-// the ordinal and endpoint tiles are copied to LDS by direct global->LDS loads
-// issued with the keys, so they arrive during the ranking without holding
-// registers; each is then regrouped in place.
+// the ordinal and endpoint tiles, and the tile's digit offsets, are copied to
+// LDS by direct global->LDS loads issued with the key loads, so a block waits
+// for memory once (before its ranking) and holds no registers for them; each
+// payload tile is then regrouped in place.
 template <class KeySrc, bool kIotaVals, bool kOther, bool kWriteKeys, bool kDual,
           bool kInlineScan, int IT, bool kDma = false>
 __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassDir<KeySrc> a1,
@@ -451,7 +452,7 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
 
     // Each wave clears and then ranks with its own row of counters, so no block
     // barrier is needed before the ranking (a wave's LDS accesses stay in
-    // order), and the copies below stay in flight through it.
+    // order).
 #pragma unroll
     for (int m = 0; m < kBins / kWave; ++m) s_cnt[wv][lane + m * kWave] = 0u;
     uint32_t k[IT];
@@ -462,7 +463,8 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
     }
     // The ordinal and endpoint payloads.  Small tiles (few keys per thread, few
     // registers) load them with the keys, so a block waits for memory once;
-    // large tiles load each just before writing it out (see below).
+    // large tiles copy them to LDS with the keys (kDma), or else load each
+    // just before writing it out (see below).
     constexpr bool kEarly = IT <= kItemsSmall;
     uint32_t v[IT], o[IT];
     auto load_payloads = [&]() {
@@ -509,7 +511,9 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
     }
     // kDma (the scan kernel ran): this tile's exclusive count of every digit
     // within its segment (one word per lane, wave w taking digits 64w ...) and
-    // the segment totals (16-byte rows), copied to LDS with the payloads.
+    // the segment totals (16-byte rows, wave w taking those of the same 64
+    // digits), copied to LDS with the payloads; each thread later reads only
+    // its own digit's, copied by its own wave.
     __shared__ uint32_t s_hv[kDma ? kBins : 1];
     __shared__ __attribute__((aligned(16))) uint32_t s_sv[kDma ? kBins * kScanSegs : 1];
     // (Every pointer is an argument, as in dma: built with the pass record's
@@ -568,10 +572,12 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
     } else {
         // The scan left the exclusive count within this tile's segment; add the
         // totals of the segments before it (digits beyond the pass have none).
-        // kDma: both are in LDS already (the barriers after the ranking waited
-        // for every wave's copies).
+        // kDma: both are in LDS already.
         const int segs = scan_segs(ntiles);
         const int64_t sg = t / scan_seg_len(ntiles);
+        // kDma: this thread's digit offsets were copied by its own wave; wait for
+        // that wave's copies (the compiler has in practice waited already).
+        if constexpr (kDma) __builtin_amdgcn_s_waitcnt(0);
         if constexpr (kDma) before_tile = s_hv[tid];
         else before_tile = a.hist[(int64_t)tid * ntiles + t];
         dsum = 0u;

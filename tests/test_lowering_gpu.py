@@ -74,6 +74,9 @@ def test_random_sizes(mp, n, e, seed):
     (50_000_000, 4_300_000, 46, 0),           # 26-bit keys: four passes, rows mostly empty
     (5000, 4_500_000, 47, 3),                 # three hub rows hold 3/4 of the edges
     (1 << 21, 4_200_000, 48, 1),              # one row holds 3/4 of the edges, 21-bit keys
+    # count scans cut into segments (one per 2048 tiles): two and four segments
+    (1 << 21, 20_000_003, 49, 0),             # 4,883 tiles, a ragged last tile
+    (1 << 20, 4096 * 8192 + 5, 50, 1),        # 8,193 tiles, one row holding 3/4 of the edges
 ])
 def test_large_list_key_widths(mp, n, e, seed, hubs):
     wl = synth.random_graph(n, e, 1, seed)

@@ -238,6 +238,10 @@ constexpr int64_t kWaveSlots = 256 * 4 * 4;   // CUs x SIMDs x four waves
 // Hub blocks of an asynchronously built graph's launches (counts unknown to the
 // host: the grid is a bound, so it is kept small and the blocks stride).
 constexpr int64_t kAsyncHubBlocks = 1024, kAsyncHubBlocks16 = 256;
+// The same for its wave and lane-group owners: a bound sized for every row of
+// the graph would launch hundreds of thousands of blocks that find no work
+// (about 0.4 ms on the power-law graph).
+constexpr int64_t kAsyncKindBlocks = 16384;
 constexpr int kLargeHubLen = 4096;
 
 struct OwnerRule {
@@ -283,7 +287,8 @@ struct Partition {
 
 template <int L>
 __host__ __device__ inline Partition partition(int64_t at_hub, int64_t at_wave, int64_t n,
-                                               int64_t hub_cap = kMaxKindBlocks) {
+                                               int64_t hub_cap = kMaxKindBlocks,
+                                               int64_t kind_cap = kMaxKindBlocks) {
     if (at_wave < at_hub) at_wave = at_hub;
     Partition p;
     p.n_hub = (int32_t)at_hub;
@@ -293,8 +298,8 @@ __host__ __device__ inline Partition partition(int64_t at_hub, int64_t at_wave, 
     const int64_t bw = (p.n_wave + kWavesPerBlock - 1) / kWavesPerBlock;
     const int64_t bg = (p.n_group + rows_per_blk - 1) / rows_per_blk;
     p.blk_hub = (int32_t)(p.n_hub < hub_cap ? p.n_hub : hub_cap);   // hub owners stride too
-    p.blk_wave = (int32_t)(bw < kMaxKindBlocks ? bw : kMaxKindBlocks);
-    p.blk_group = (int32_t)(bg < kMaxKindBlocks ? bg : kMaxKindBlocks);
+    p.blk_wave = (int32_t)(bw < kind_cap ? bw : kind_cap);
+    p.blk_group = (int32_t)(bg < kind_cap ? bg : kind_cap);
     return p;
 }
 
@@ -602,7 +607,7 @@ void spmm_kernel(SpmmArgs a) {
         const OwnerRule r = owner_rule(top_class_len(cr), a.e, kWave / L, a.force_hub,
                                        a.force_apart);
         pt = partition<L>(rows_at_least(cr, r.hub_min, a.n), rows_at_least(cr, a.wave_min, a.n),
-                          a.n, kAsyncHubBlocks);
+                          a.n, kAsyncHubBlocks, kAsyncKindBlocks);
         apart = r.apart;
         n_full = (int32_t)rows_at_least(cr, 1, a.n);
     }
@@ -845,8 +850,9 @@ mp_status launch(const CsrView &csr, const float *w, int64_t heads, const void *
         const OwnerRule four = owner_rule(0, csr.e, G, ov.hub_min, 0);
         const OwnerRule sixteen = owner_rule(0, csr.e, G, ov.hub_min, 1);
         pt = partition<L>(0, 0, 0);
-        const Partition pw = partition<L>(0, most(ov.wave_min), 0);
-        const Partition pg = partition<L>(0, 0, csr.n);
+        const Partition pw = partition<L>(0, most(ov.wave_min), 0, kAsyncHubBlocks,
+                                          kAsyncKindBlocks);
+        const Partition pg = partition<L>(0, 0, csr.n, kAsyncHubBlocks, kAsyncKindBlocks);
         pt.blk_hub =
             ov.apart == 1 ? 0 : partition<L>(most(four.hub_min), 0, 0, kAsyncHubBlocks).blk_hub;
         pt.blk_wave = pw.blk_wave;

@@ -28,7 +28,8 @@ import torch  # noqa: F401  -- loaded first so libmp.so binds to torch's HIP run
 
 __all__ = [
     "Graph", "MpError", "mp_graph_build", "mp_graph_build_async", "mp_graph_finish",
-    "mp_graph_build_noalloc", "STATIC_WORKSPACE_BYTES",
+    "mp_graph_build_noalloc", "STATIC_WORKSPACE_BYTES", "mp_graph_build_overlap",
+    "mp_graph_build_overlap_workspace_size",
     "mp_graph_build_workspace_size", "mp_spmm_fwd",
     "mp_spmm_dx", "mp_edge_grad_dw", "mp_spmm_dx_edge_grad", "mp_spmm_fwd_heads",
     "mp_spmm_dx_heads", "mp_edge_grad_dw_heads", "mp_spmm_dx_edge_grad_heads", "mp_edge_softmax",
@@ -113,6 +114,8 @@ def _load():
         "mp_graph_build_workspace_size": (i32, [i64, i64, ctypes.POINTER(sz)]),
         "mp_graph_build": (i32, [vp, vp, i32, i64, i64, gp, vp, sz, vp]),
         "mp_graph_build_async": (i32, [vp, vp, i32, i64, i64, gp, vp, sz, vp]),
+        "mp_graph_build_overlap_workspace_size": (i32, [i64, i64, ctypes.POINTER(sz)]),
+        "mp_graph_build_overlap": (i32, [vp, vp, i32, i64, i64, gp, vp, sz, vp, vp, vp]),
         "mp_graph_finish": (i32, [gp, vp]),
         "mp_graph_build_noalloc": (i32, [vp, vp, i32, i64, i64, gp, vp]),
         "mp_spmm_fwd": (i32, [gp, vp, vp, i32, i64, vp, vp]),
@@ -332,6 +335,52 @@ def mp_graph_build_async(src, dst, num_nodes: int, workspace=None) -> Graph:
     several streams need their own workspaces (mp_graph_build_workspace_size)."""
     return _build_graph(_lib.mp_graph_build_async, "mp_graph_build_async", src, dst, num_nodes,
                   workspace)
+
+
+def mp_graph_build_overlap_workspace_size(num_nodes: int, num_edges: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.mp_graph_build_overlap_workspace_size(int(num_nodes), int(num_edges),
+                                                      ctypes.byref(out)),
+           "mp_graph_build_overlap_workspace_size")
+    return int(out.value)
+
+
+def mp_graph_build_overlap(src, dst, num_nodes: int, side_stream, workspace=None):
+    """The asynchronous lowering with the transpose direction on `side_stream`:
+    the intake, the forward CSR and its plan are enqueued on the current stream,
+    the transpose CSR and its plan on `side_stream` (after the intake).  Returns
+    (graph, transpose_done): the forward calls may run on the current stream at
+    once; calls that read the transpose CSR (mp_spmm_dx and its forms, the fused
+    backward and attention backward calls) and mp_graph_finish must run after
+    ``torch.cuda.current_stream().wait_event(transpose_done)``."""
+    _need_tensor("src", src)
+    _need_tensor("dst", dst)
+    if src.dim() != 1 or dst.dim() != 1 or src.shape[0] != dst.shape[0]:
+        raise ValueError("src and dst must be 1-D with the same length")
+    if not isinstance(side_stream, torch.cuda.Stream):
+        raise TypeError("side_stream must be a torch.cuda.Stream")
+    e = int(src.shape[0])
+    g = Graph(num_nodes, e, src.device)
+    ws_bytes = mp_graph_build_overlap_workspace_size(num_nodes, e)
+    if workspace is None:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=src.device)
+    else:
+        _need_tensor("workspace", workspace)
+        if workspace.dtype != torch.uint8 or workspace.numel() < ws_bytes:
+            raise ValueError(f"workspace must be a uint8 tensor of at least {ws_bytes} bytes")
+        ws = workspace
+    done = torch.cuda.Event()
+    done.record(side_stream)          # creates the event; the call records it again
+    status = _lib.mp_graph_build_overlap(_ptr(src) if e else None, _ptr(dst) if e else None,
+                                         _code(src), int(num_nodes), e, ctypes.byref(g._desc),
+                                         _ptr(ws), ws.numel(), _stream(src),
+                                         side_stream.cuda_stream, done.cuda_event)
+    _check(status, "mp_graph_build_overlap")
+    # The side stream uses the inputs, the graph's arrays and the workspace.
+    for t in [src, dst, ws, g.info] + [a for a in g.arrays.values() if a.numel()]:
+        t.record_stream(side_stream)
+    g._overlap_ws = ws
+    return g, done
 
 
 def mp_graph_build_noalloc(src, dst, num_nodes: int) -> Graph:

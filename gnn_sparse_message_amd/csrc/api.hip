@@ -340,14 +340,25 @@ mp_status mp_graph_build_workspace_size(int64_t num_nodes, int64_t num_edges, si
     return MP_OK;
 }
 
+mp_status mp_graph_build_overlap_workspace_size(int64_t num_nodes, int64_t num_edges,
+                                                size_t *bytes) {
+    if (!bytes) return fail(MP_ERR_NULL, "bytes is NULL");
+    mp_status st = check_sizes(num_nodes, num_edges);
+    if (st != MP_OK) return st;
+    *bytes = lower_layout(num_nodes, num_edges, true).total;
+    return MP_OK;
+}
+
 }  // extern "C"
 
 namespace mp {
 namespace {
 // static_ws: the workspace is this device's static array (mp_graph_build_noalloc).
+// side / side_done: mp_graph_build_overlap (the transpose direction on `side`).
 mp_status build_impl(const void *src, const void *dst, mp_dtype idx_dtype, int64_t num_nodes,
                      int64_t num_edges, mp_graph *g, void *workspace, size_t workspace_bytes,
-                     void *stream, bool async, bool static_ws = false) {
+                     void *stream, bool async, bool static_ws = false, void *side = nullptr,
+                     void *side_done = nullptr) {
     if (!g) return fail(MP_ERR_NULL, "graph descriptor is NULL");
     g->built = 0;
     mp_status st = check_sizes(num_nodes, num_edges);
@@ -372,7 +383,7 @@ mp_status build_impl(const void *src, const void *dst, mp_dtype idx_dtype, int64
         if (a.count > 0 && !a.p) return fail(MP_ERR_NULL, "%s is NULL", a.name);
         if (a.p && !aligned(a.p, 4)) return fail(MP_ERR_ALIGN, "%s not aligned to 4 bytes", a.name);
     }
-    const size_t need = lower_layout(n, e).total;
+    const size_t need = lower_layout(n, e, side != nullptr).total;
     if (static_ws && need > workspace_bytes)
         return fail(MP_ERR_WORKSPACE,
                     "N = %lld, E = %lld need %zu bytes of workspace; the static workspace of "
@@ -411,7 +422,8 @@ mp_status build_impl(const void *src, const void *dst, mp_dtype idx_dtype, int64
 
     int bad = 0;
     st = lower_run(src, dst, idx_dtype, n, e, g, workspace, static_cast<hipStream_t>(stream),
-                   async, &bad);
+                   async, &bad, static_cast<hipStream_t>(side),
+                   static_cast<hipEvent_t>(side_done));
     if (st != MP_OK) return st;
     if (bad) return fail(MP_ERR_INDEX, "an edge endpoint lies outside [0, %lld)", (long long)n);
     g->built = async ? MP_GRAPH_ON_DEVICE : MP_GRAPH_BUILT;
@@ -434,6 +446,20 @@ mp_status mp_graph_build_async(const void *src, const void *dst, mp_dtype idx_dt
                                void *workspace, size_t workspace_bytes, void *stream) {
     return build_impl(src, dst, idx_dtype, num_nodes, num_edges, g, workspace, workspace_bytes,
                       stream, true);
+}
+
+mp_status mp_graph_build_overlap(const void *src, const void *dst, mp_dtype idx_dtype,
+                                 int64_t num_nodes, int64_t num_edges, mp_graph *g,
+                                 void *workspace, size_t workspace_bytes, void *stream,
+                                 void *side_stream, void *transpose_done) {
+    if (!g) return fail(MP_ERR_NULL, "graph descriptor is NULL");
+    g->built = 0;
+    if (!side_stream) return fail(MP_ERR_NULL, "side_stream is NULL (the null stream would "
+                                  "serialise with stream)");
+    if (!transpose_done) return fail(MP_ERR_NULL, "transpose_done event is NULL");
+    if (side_stream == stream) return fail(MP_ERR_ALIAS, "side_stream is stream");
+    return build_impl(src, dst, idx_dtype, num_nodes, num_edges, g, workspace, workspace_bytes,
+                      stream, true, false, side_stream, transpose_done);
 }
 
 mp_status mp_graph_build_noalloc(const void *src, const void *dst, mp_dtype idx_dtype,

@@ -45,12 +45,18 @@ struct LowerLayout {
     size_t seg[2];            // [256 * 8] u32 segment totals of the count scan
     size_t total;
 };
-LowerLayout lower_layout(int64_t n, int64_t e);
+// split_dirs: each direction has its own sort buffers (the two directions of
+// mp_graph_build_overlap run at once).
+LowerLayout lower_layout(int64_t n, int64_t e, bool split_dirs = false);
 
 // Enqueue the whole lowering.  Unless `async`, then synchronise `stream` and
-// copy the class counts and the index flag back to the host.
+// copy the class counts and the index flag back to the host.  With a `side`
+// stream (async only; the workspace laid out with split_dirs): the intake and
+// the forward CSR with its plan go on `stream`, the transpose CSR with its plan
+// on `side` after the intake, and `side_done` is recorded on `side` at its end.
 mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_t n, int64_t e,
-                    mp_graph *g, void *ws, hipStream_t stream, bool async, int *bad_index);
+                    mp_graph *g, void *ws, hipStream_t stream, bool async, int *bad_index,
+                    hipStream_t side = nullptr, hipEvent_t side_done = nullptr);
 // Copy the class counts and the index flag of g->info to the host (synchronous).
 mp_status lower_read_info(mp_graph *g, hipStream_t stream, int *bad_index);
 // This device's static lowering workspace (MP_STATIC_WORKSPACE_BYTES, shared

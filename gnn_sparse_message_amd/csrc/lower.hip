@@ -930,11 +930,23 @@ mp_status plans(int64_t n, mp_graph *g, const SortBufs &b0, const SortBufs &b1,
     return radix_pass<KeysFromDegree, true, false, false, true, IT>(p0, p1, n, 0, kPlanBits, s);
 }
 
+// The degree plan of one direction (the plan pass on its own launches).
+mp_status plan_one(int64_t n, const int32_t *rowptr, int32_t *row_plan, const SortBufs &b,
+                   uint32_t *totals, hipStream_t s) {
+    PassDir<KeysFromDegree> p;
+    p.keys = KeysFromDegree{rowptr};
+    p.pl = Payload{nullptr, nullptr, nullptr, reinterpret_cast<uint32_t *>(row_plan), nullptr};
+    p.hist = b.hist;
+    p.seg = b.seg;
+    p.dtot = totals;
+    return radix_pass<KeysFromDegree, true, false, false, false, kItems>(p, p, n, 0, kPlanBits, s);
+}
+
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-LowerLayout lower_layout(int64_t n, int64_t e) {
+LowerLayout lower_layout(int64_t n, int64_t e, bool split_dirs) {
     LowerLayout L;
     size_t off = 0;
     const size_t ebytes = align_up((size_t)(e > 0 ? e : 1) * sizeof(uint32_t));
@@ -942,7 +954,7 @@ LowerLayout lower_layout(int64_t n, int64_t e) {
     const int it = dual_mode(e) ? kItemsSmall : kItems;
     const size_t hbytes = align_up((size_t)kBins * tiles_for(most, it) * sizeof(uint32_t));
     for (int i = 0; i < 2; ++i) {
-        if (i == 1 && !dual_mode(e)) {   // one direction at a time: one set of sort buffers
+        if (i == 1 && !dual_mode(e) && !split_dirs) {   // one direction at a time: one set
             L.k0[1] = L.k0[0];
             L.k1[1] = L.k1[0];
             L.v0[1] = L.v0[0];
@@ -974,8 +986,12 @@ mp_status lower_read_info(mp_graph *g, hipStream_t s, int *bad_index) {
 }
 
 mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_t n, int64_t e,
-                    mp_graph *g, void *ws, hipStream_t s, bool async, int *bad_index) {
-    const LowerLayout L = lower_layout(n, e);
+                    mp_graph *g, void *ws, hipStream_t s, bool async, int *bad_index,
+                    hipStream_t side, hipEvent_t side_done) {
+    const bool split = side != nullptr;
+    if (split && (!async || !side_done))
+        return fail(MP_ERR_INTERNAL, "a side-stream lowering is asynchronous and records an event");
+    const LowerLayout L = lower_layout(n, e, split);
     char *base = static_cast<char *>(ws);
     auto at = [&](size_t off) { return reinterpret_cast<uint32_t *>(base + off); };
     SortBufs b[2];
@@ -991,7 +1007,7 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
     const bool counted = e > 0;
     if (counted) {
         const int fb = first_pass_bits(n);
-        if (dual_mode(e))
+        if (dual_mode(e) && !split)
             intake_count<kItemsSmall>(src, dst, idx_dtype, e, n, g, fb, b[0].hist, b[1].hist, s);
         else
             intake_count<kItems>(src, dst, idx_dtype, e, n, g, fb, b[0].hist, b[1].hist, s);
@@ -1006,6 +1022,32 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
     // other direction's sort overwrites them.
     const uint32_t *sorted[2] = {b[0].k0, b[1].k0};
     mp_status st = MP_OK;
+    if (split) {
+        // Each direction on its own stream, with its own sort buffers and large
+        // tiles (the intake counted the first passes in them); the transpose
+        // waits only for the intake.
+        hipEvent_t fork = nullptr;
+        MP_HIP_CHECK(hipEventCreateWithFlags(&fork, hipEventDisableTiming), "fork event");
+        hipError_t he = hipEventRecord(fork, s);
+        if (he == hipSuccess) he = hipStreamWaitEvent(side, fork, 0);
+        (void)hipEventDestroy(fork);   // released once the wait no longer needs it
+        MP_HIP_CHECK(he, "fork of the transpose lowering");
+        for (int i = 0; i < 2 && st == MP_OK; ++i) {
+            hipStream_t q = i == 0 ? s : side;
+            if (e > 0) st = sort_edges<false>(&dirs[i], e, n, &sorted[i], q, counted);
+            const RowsDir r{sorted[i], i == 0 ? g->rowptr : g->rowptr_t};
+            if (st == MP_OK) st = row_pointers<false>(r, r, e, n, q);
+            if (st == MP_OK)
+                st = plan_one(n, i == 0 ? g->rowptr : g->rowptr_t,
+                              i == 0 ? g->row_plan : g->row_plan_t, b[i],
+                              info + (i == 0 ? kInfoPlanF : kInfoPlanT), q);
+        }
+        if (st != MP_OK) return st;
+        MP_HIP_CHECK(hipEventRecord(side_done, side), "transpose lowering event");
+        *bad_index = 0;
+        for (int c = 0; c < MP_NUM_CLASSES; ++c) g->class_count[c] = g->class_count_t[c] = 0;
+        return MP_OK;
+    }
     if (dual_mode(e)) {
         if (e > 0) st = sort_edges<true>(dirs, e, n, sorted, s, counted);
         if (st == MP_OK)

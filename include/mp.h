@@ -184,6 +184,40 @@ mp_status mp_graph_build_async(const void *src, const void *dst, mp_dtype idx_dt
                                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The asynchronous lowering with its two directions on two streams, so that
+ * the forward CSR can be used while the transpose CSR is still being built:
+ * a training step's forward aggregation then overlaps the transpose half of
+ * the build (the forward needs only rowptr, col, edge_order and row_plan;
+ * "Edge order is explicit" keeps the two lowerings independent).
+ *
+ *   stream          the intake, then the forward CSR (rowptr, col, edge_order)
+ *                   and its degree plan (row_plan).
+ *   side_stream     the transpose CSR (rowptr_t, col_t, transpose_order) and its
+ *                   plan (row_plan_t), after the intake; not NULL, not `stream`.
+ *   transpose_done  a hipEvent_t created by the caller; recorded on side_stream
+ *                   once the transpose CSR and its plan are written.
+ *   workspace       at least mp_graph_build_overlap_workspace_size(N, E) bytes
+ *                   (each direction has its own sort buffers), 256-byte aligned.
+ *
+ * The other arguments, the validation and the results (bit for bit those of
+ * mp_graph_build) are those of mp_graph_build_async; g is left as it leaves it
+ * (g->built = MP_GRAPH_ON_DEVICE).  Work on `stream` may use the forward CSR at
+ * once (mp_spmm_fwd and its forms, and mp_edge_grad_dw, which reads only the
+ * COO copies the intake writes); work that reads the transpose CSR
+ * (mp_spmm_dx and its forms, the fused backward calls, the attention backward
+ * calls) and mp_graph_finish must first wait for transpose_done
+ * (hipStreamWaitEvent).  The workspace is in use until both streams have run
+ * the build.  Returns MP_ERR_NULL for a NULL side_stream or transpose_done,
+ * MP_ERR_ALIAS when side_stream is stream.
+ */
+mp_status mp_graph_build_overlap_workspace_size(int64_t num_nodes, int64_t num_edges,
+                                                size_t *bytes);
+mp_status mp_graph_build_overlap(const void *src, const void *dst, mp_dtype idx_dtype,
+                                 int64_t num_nodes, int64_t num_edges, mp_graph *g,
+                                 void *workspace, size_t workspace_bytes, void *stream,
+                                 void *side_stream, void *transpose_done);
+
+/*
  * mp_graph_build_async without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  The lowering's scratch is a static array

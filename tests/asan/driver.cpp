@@ -80,6 +80,30 @@ int main(int argc, char **argv) {
                mp_graph_build_noalloc(src, dst, MP_I64, n, 5000000, &big, nullptr),
                MP_ERR_WORKSPACE, b);
     }
+    {   // the two-stream build: its own workspace size, two streams, an event
+        size_t ows = 0;
+        if (mp_graph_build_overlap_workspace_size(n, e, &ows) != MP_OK || ows < ws_bytes) {
+            printf("FAIL overlap workspace size\n");
+            ++failures;
+        }
+        void *s0 = reinterpret_cast<void *>(0x100), *s1 = reinterpret_cast<void *>(0x200);
+        void *ev = reinterpret_cast<void *>(0x300);
+        VALID(mp_graph_build_overlap(src, dst, MP_I64, n, e, &g, ws, ows, s0, s1, ev));
+        ALIAS(mp_graph_build_overlap(src, dst, MP_I64, n, e, &g, g.col_t, ows, s0, s1, ev));
+        int b = g_launches;
+        expect("mp_graph_build_overlap (no side stream)",
+               mp_graph_build_overlap(src, dst, MP_I64, n, e, &g, ws, ows, s0, nullptr, ev),
+               MP_ERR_NULL, b);
+        expect("mp_graph_build_overlap (no event)",
+               mp_graph_build_overlap(src, dst, MP_I64, n, e, &g, ws, ows, s0, s1, nullptr),
+               MP_ERR_NULL, b);
+        expect("mp_graph_build_overlap (one stream)",
+               mp_graph_build_overlap(src, dst, MP_I64, n, e, &g, ws, ows, s0, s0, ev),
+               MP_ERR_ALIAS, b);
+        expect("mp_graph_build_overlap (workspace of the one-stream build)",
+               mp_graph_build_overlap(src, dst, MP_I64, n, e, &g, ws, ws_bytes, s0, s1, ev),
+               ows > ws_bytes ? MP_ERR_WORKSPACE : (small_lists ? MP_ERR_INTERNAL : MP_OK), b);
+    }
     // the workspace over a graph array
     ALIAS(mp_graph_build(src, dst, MP_I64, n, e, &g, g.col, ws_bytes, nullptr));
     g.built = MP_GRAPH_BUILT;

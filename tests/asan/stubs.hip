@@ -24,13 +24,13 @@ const char *hipGetErrorString(hipError_t) { return "stub"; }
 }
 
 namespace mp {
-LowerLayout lower_layout(int64_t, int64_t e) {
+LowerLayout lower_layout(int64_t, int64_t e, bool split_dirs) {
     LowerLayout L = {};
-    L.total = 4096 + (size_t)(e > 0 ? e : 1) * 64;
+    L.total = 4096 + (size_t)(e > 0 ? e : 1) * (split_dirs ? 96 : 64);
     return L;
 }
 mp_status lower_run(const void *, const void *, mp_dtype, int64_t, int64_t, mp_graph *, void *,
-                    hipStream_t, bool, int *bad) {
+                    hipStream_t, bool, int *bad, hipStream_t, hipEvent_t) {
     ++g_launches;
     *bad = 0;
     return MP_OK;

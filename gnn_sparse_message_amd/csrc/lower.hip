@@ -136,6 +136,71 @@ __device__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *total) {
     return wbase + inc - x;
 }
 
+// Exclusive scan over R * kBlock entries held round-wise (entry tid + j * kBlock
+// is v[j], so that loads and stores of the entries are coalesced): ex[j] =
+// op over the entries before it (kFromLeft) or after it, `none` if there are
+// none.  Returns op over all entries.  op is associative and commutative with
+// identity `none`.  Contains barriers: every thread of the block calls it.
+template <bool kFromLeft, int R, class Op>
+__device__ __forceinline__ uint32_t rounds_exclusive(const uint32_t (&v)[R], uint32_t (&ex)[R],
+                                                     uint32_t none, Op op) {
+    __shared__ uint32_t s_t[R][kWavesPerBlock];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        uint32_t inc = v[j];
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            if constexpr (kFromLeft) {
+                const uint32_t y = __shfl_up(inc, off);
+                if (lane >= off) inc = op(inc, y);
+            } else {
+                const uint32_t y = __shfl_down(inc, off);
+                if (lane + off < kWave) inc = op(inc, y);
+            }
+        }
+        if (lane == (kFromLeft ? kWave - 1 : 0)) s_t[j][wv] = inc;
+        // this wave's lanes before (after) this one in the round
+        uint32_t w;
+        if constexpr (kFromLeft) {
+            w = __shfl_up(inc, 1);
+            if (lane == 0) w = none;
+        } else {
+            w = __shfl_down(inc, 1);
+            if (lane == kWave - 1) w = none;
+        }
+        ex[j] = w;
+    }
+    __syncthreads();
+    uint32_t run = none;   // the whole rounds already passed
+#pragma unroll
+    for (int jj = 0; jj < R; ++jj) {
+        const int j = kFromLeft ? jj : R - 1 - jj;
+        uint32_t waves = none, all = none;
+#pragma unroll
+        for (int w = 0; w < kWavesPerBlock; ++w) {
+            const uint32_t t = s_t[j][w];
+            if (kFromLeft ? w < wv : w > wv) waves = op(waves, t);
+            all = op(all, t);
+        }
+        ex[j] = op(run, op(waves, ex[j]));
+        run = op(run, all);
+    }
+    __syncthreads();
+    return run;
+}
+
+struct OpSum {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+struct OpMax {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
+};
+struct OpMin {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; }
+};
+
 // ------------------------------------------------------------------ intake
 __global__ void zero_words_kernel(uint32_t *p, int n) {
     for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
@@ -179,6 +244,16 @@ struct Payload {
     uint32_t *other_out;
 };
 
+// What the last pass of an edge sort writes instead of the sorted keys when it
+// also delimits the rows (see row_heads): the first position of every key
+// that is not the first of its tile's run, and one record per (digit, tile)
+// run, digit-major like hist.
+struct RowsOut {
+    int32_t *rowptr;   // [n + 1]
+    uint2 *runs;       // (first key, last key + 1) of the run; (0, 0) if empty
+                       // (hist receives the run's output position)
+};
+
 // One direction's share of a pass.
 template <class KeySrc>
 struct PassDir {
@@ -188,6 +263,7 @@ struct PassDir {
     uint32_t *seg;    // [kBins * kScanSegs] per-segment digit totals from the scan
     uint32_t *dtot;   // [kBins] digit totals, written by tile 0 of the downsweep when
                       // not nullptr
+    RowsOut rows;     // only for the row-delimiting last pass
 };
 
 // Digit counts of one tile: k[r] is the key at tile-local index li0 + r * 64,
@@ -367,13 +443,14 @@ __global__ __launch_bounds__(kBlock) void intake_count_kernel(
 // segment's total.  The downsweep adds the totals of the earlier segments.
 // Only the pass's own digits are scanned: the rows of the others hold zeros,
 // which are their own exclusive scan.
-template <bool kDual>
+// kPer counts per thread per step: segments of up to a few hundred tiles take
+// one or four, so a short row does not pay for sixteen rounds of scan.
+template <bool kDual, int kPer>
 __global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist0,
                                                   uint32_t *__restrict__ seg0,
                                                   uint32_t *__restrict__ hist1,
                                                   uint32_t *__restrict__ seg1, int64_t ntiles,
                                                   int digits) {
-    constexpr int kPer = 16;
     const int segs = scan_segs(ntiles);
     const int per_dir = digits * segs;
     const int dir = kDual && (int)blockIdx.x >= per_dir ? 1 : 0;
@@ -385,24 +462,62 @@ __global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist0,
     uint32_t *row = (dir ? hist1 : hist0) + (int64_t)digit * ntiles;
     uint32_t carry = 0;
     for (int64_t chunk = lo; chunk < hi; chunk += (int64_t)kBlock * kPer) {
-        const int64_t beg = chunk + (int64_t)threadIdx.x * kPer;
-        uint32_t v[kPer];
-        uint32_t sum = 0;
+        uint32_t v[kPer], ex[kPer];
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            v[j] = beg + j < hi ? row[beg + j] : 0u;
-            sum += v[j];
+            const int64_t i = chunk + threadIdx.x + (int64_t)j * kBlock;
+            v[j] = i < hi ? row[i] : 0u;
         }
-        uint32_t total;
-        uint32_t run = carry + block_exclusive_scan(sum, &total);
+        const uint32_t total = rounds_exclusive<true>(v, ex, 0u, OpSum{});
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            if (beg + j < hi) row[beg + j] = run;
-            run += v[j];
+            const int64_t i = chunk + threadIdx.x + (int64_t)j * kBlock;
+            if (i < hi) row[i] = carry + ex[j];
         }
         carry += total;
     }
     if (threadIdx.x == 0) (dir ? seg1 : seg0)[digit * kScanSegs + sg] = carry;
+}
+
+// Rows from the last pass of an edge sort, in place of writing the sorted keys
+// for a search.  The tile's keys are regrouped into buf in tile-sorted order; a
+// tile's run of one digit is written to consecutive output positions, so
+// inside a run (buf[i - 1] of the same digit) the key before slot i is
+// buf[i - 1].  Where it differs, slot i holds the first edge of its key:
+// rowptr[key] = its position.  The first slot of a run has its predecessor in
+// another tile; the run's record (first key, last key + 1; its output
+// position in hist) lets rows_fixup_kernel settle it.  Keys that occur
+// nowhere keep the marker rows_init_kernel wrote (rows_apply_kernel fills
+// them).  Contains barriers: every thread of the block calls it.
+template <int IT>
+__device__ __forceinline__ void row_heads(const uint32_t (&k)[IT], const uint32_t (&pos)[IT],
+                                          const uint32_t (&gp)[IT], int li0, int lim,
+                                          uint32_t *buf, int shift, uint32_t mask,
+                                          const uint32_t *tstart, const uint32_t *gbase,
+                                          int digits, const RowsOut &ro,
+                                          uint32_t *__restrict__ hist, int64_t ntiles,
+                                          int64_t t) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int r = 0; r < IT; ++r)
+        if (li0 + r * kWave < lim) buf[pos[r]] = k[r];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < IT; ++j) {
+        const int i = tid + j * kBlock;
+        if (i > 0 && i < lim) {
+            const uint32_t key = buf[i], prev = buf[i - 1];
+            if (key != prev && (((key ^ prev) >> shift) & mask) == 0u)
+                ro.rowptr[key] = (int32_t)gp[j];
+        }
+    }
+    if (tid < digits) {
+        const uint32_t b = tstart[tid];
+        const uint32_t end = tid + 1 < kBins ? tstart[tid + 1] : (uint32_t)lim;
+        const int64_t q = (int64_t)tid * ntiles + t;
+        ro.runs[q] = end > b ? make_uint2(buf[b], buf[end - 1] + 1u) : make_uint2(0u, 0u);
+        hist[q] = gbase[tid];   // only this block reads its column of hist
+    }
 }
 
 // kInlineScan: hist holds raw per-tile counts (no scan kernel ran); each thread
@@ -412,13 +527,17 @@ __global__ __launch_bounds__(kBlock) void rs_scan(uint32_t *__restrict__ hist0,
 // LDS by direct global->LDS loads issued with the key loads, so a block waits
 // for memory once (before its ranking) and holds no registers for them; each
 // payload tile is then regrouped in place.
+// kRows (the last pass of an edge sort, one direction, after the scan): the
+// rows are delimited by row_heads instead of writing the keys.
 template <class KeySrc, bool kIotaVals, bool kOther, bool kWriteKeys, bool kDual,
-          bool kInlineScan, int IT, bool kDma = false>
+          bool kInlineScan, int IT, bool kDma = false, bool kRows = false>
 __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassDir<KeySrc> a1,
                                                        int64_t count, int shift, int bits,
                                                        int64_t ntiles) {
     static_assert(!kDma || (kOther && IT % 4 == 0 && !kInlineScan),
                   "the copied tiles are whole 16-byte rows; the offsets come from the scan");
+    static_assert(!kRows || (!kWriteKeys && !kDual && !kInlineScan),
+                  "row heads replace the key output of a one-direction pass after the scan");
     static_assert(kBins == kWavesPerBlock * kWave, "one digit offset per thread");
     constexpr int kTile = kBlock * IT;
     // kDma: [0, kTile) the ordinal tile, then the regroup buffer of the keys;
@@ -656,6 +775,9 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
         }
         emit_lds(pay + kTile, pl.other_out);
         if (kWriteKeys) emit_to(k, pay, pl.keys_out);
+        if constexpr (kRows)
+            row_heads(k, pos, gp, li0, lim, pay, shift, mask, s_tstart, s_gbase, 1 << bits,
+                      a.rows, a.hist, ntiles, t);
         return;
     }
     if (kWriteKeys) emit(k, pl.keys_out);
@@ -685,6 +807,9 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
             emit(o, pl.other_out);
         }
     }
+    if constexpr (kRows)
+        row_heads(k, pos, gp, li0, lim, pay, shift, mask, s_tstart, s_gbase, 1 << bits, a.rows,
+                  a.hist, ntiles, t);
 }
 
 // ------------------------------------------------------------------ rows
@@ -712,6 +837,164 @@ __global__ __launch_bounds__(kBlock) void rowptr_kernel(RowsDir r0, RowsDir r1, 
             else hi = mid;
         }
         r.rowptr[i] = (int32_t)lo;
+    }
+}
+
+// Rows delimited by the last sort pass (row_heads), then completed here:
+//   rows_init   -- before that pass: every row pointer holds the marker
+//                  0xffffffff, rowptr[n] = e;
+//   rows_chunk_max, rows_fixup -- the first slot of each nonempty run starts
+//                  its key when the edge before it (the last of the nearest
+//                  earlier nonempty run, in digit-major order) has a smaller
+//                  key;
+//   rows_chunk_min, rows_apply -- a key that occurs nowhere starts where the
+//                  next key that occurs does: every marker takes the smallest
+//                  row pointer after it (the row pointers of occurring keys
+//                  increase with the key, and rowptr[n] = e ends the list).
+// Each row pointer is written by exactly one of them; none uses atomics.
+constexpr int kRowsPer = 16;                        // entries per thread
+constexpr int kRowsChunk = kBlock * kRowsPer;       // entries per block
+constexpr uint32_t kNoRow = 0xffffffffu;
+
+// Max (kMax) or min over the block.  Contains barriers.
+template <bool kMax>
+__device__ uint32_t block_reduce(uint32_t x) {
+    __shared__ uint32_t s_red[kWavesPerBlock];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t y = __shfl_xor(x, off);
+        x = kMax ? (y > x ? y : x) : (y < x ? y : x);
+    }
+    if (lane == 0) s_red[wv] = x;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+        const uint32_t y = s_red[w];
+        x = kMax ? (y > x ? y : x) : (y < x ? y : x);
+    }
+    __syncthreads();
+    return x;
+}
+
+__global__ __launch_bounds__(kBlock) void rows_init_kernel(int32_t *__restrict__ rowptr,
+                                                           int64_t n, int64_t e) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i <= n; i += stride)
+        rowptr[i] = i == n ? (int32_t)e : (int32_t)kNoRow;
+}
+
+// cmax[c]: the largest run end (last key + 1) of record chunk c, 0 if all its
+// runs are empty.
+__global__ __launch_bounds__(kBlock) void rows_chunk_max_kernel(const uint2 *__restrict__ runs,
+                                                                int64_t count,
+                                                                uint32_t *__restrict__ cmax) {
+    const int64_t c0 = (int64_t)blockIdx.x * kRowsChunk;
+    uint32_t m = 0u;
+#pragma unroll
+    for (int j = 0; j < kRowsPer; ++j) {
+        const int64_t q = c0 + threadIdx.x + (int64_t)j * kBlock;
+        const uint32_t v = q < count ? runs[q].y : 0u;
+        m = v > m ? v : m;
+    }
+    m = block_reduce<true>(m);
+    if (threadIdx.x == 0) cmax[blockIdx.x] = m;
+}
+
+// One block per kRowsChunk run records (count = digits * ntiles).
+__global__ __launch_bounds__(kBlock) void rows_fixup_kernel(const uint2 *__restrict__ runs,
+                                                            const uint32_t *__restrict__ pstart,
+                                                            const uint32_t *__restrict__ cmax,
+                                                            int64_t count,
+                                                            int32_t *__restrict__ rowptr) {
+    const int64_t c0 = (int64_t)blockIdx.x * kRowsChunk;
+    const int tid = threadIdx.x;
+    uint32_t l[kRowsPer], f[kRowsPer], ps[kRowsPer];
+#pragma unroll
+    for (int j = 0; j < kRowsPer; ++j) {
+        const int64_t q = c0 + tid + (int64_t)j * kBlock;
+        const bool in = q < count;
+        const uint2 r = in ? runs[q] : make_uint2(0u, 0u);
+        f[j] = r.x;
+        l[j] = r.y;
+        ps[j] = in ? pstart[q] : 0u;
+    }
+    // The last key (+ 1) before this chunk: the nearest earlier chunk maximum
+    // that is not 0 (they grow along the records), found kRowsChunk chunks at
+    // a time.  The trip count is the same for the whole block.
+    uint32_t carry = 0u;
+    for (int64_t wend = blockIdx.x; carry == 0u && wend > 0;) {
+        const int64_t wbeg = wend > kRowsChunk ? wend - kRowsChunk : 0;
+        uint32_t m = 0u;
+#pragma unroll
+        for (int j = 0; j < kRowsPer; ++j) {
+            const int64_t c = wbeg + tid + (int64_t)j * kBlock;
+            const uint32_t v = c < wend ? cmax[c] : 0u;
+            m = v > m ? v : m;
+        }
+        carry = block_reduce<true>(m);
+        wend = wbeg;
+    }
+    uint32_t ex[kRowsPer];
+    rounds_exclusive<true>(l, ex, 0u, OpMax{});
+#pragma unroll
+    for (int j = 0; j < kRowsPer; ++j) {
+        // a nonempty run starts its key when the edge before it has a smaller one
+        const uint32_t before = ex[j] > carry ? ex[j] : carry;   // last key + 1; 0: none
+        if (l[j] > 0u && before <= f[j]) rowptr[f[j]] = (int32_t)ps[j];
+    }
+}
+
+// cmin[c]: the smallest row pointer of chunk c (kNoRow if it holds only markers).
+__global__ __launch_bounds__(kBlock) void rows_chunk_min_kernel(const int32_t *__restrict__ rowptr,
+                                                                int64_t n1,
+                                                                uint32_t *__restrict__ cmin) {
+    const int64_t c0 = (int64_t)blockIdx.x * kRowsChunk;
+    uint32_t m = kNoRow;
+#pragma unroll
+    for (int j = 0; j < kRowsPer; ++j) {
+        const int64_t i = c0 + threadIdx.x + (int64_t)j * kBlock;
+        const uint32_t v = i < n1 ? (uint32_t)rowptr[i] : kNoRow;
+        m = v < m ? v : m;
+    }
+    m = block_reduce<false>(m);
+    if (threadIdx.x == 0) cmin[blockIdx.x] = m;
+}
+
+// Every marker of chunk blockIdx.x takes the smallest row pointer after it.
+__global__ __launch_bounds__(kBlock) void rows_apply_kernel(int32_t *__restrict__ rowptr,
+                                                            int64_t n1,
+                                                            const uint32_t *__restrict__ cmin,
+                                                            int64_t nchunks) {
+    const int64_t c0 = (int64_t)blockIdx.x * kRowsChunk;
+    const int tid = threadIdx.x;
+    uint32_t v[kRowsPer];
+#pragma unroll
+    for (int j = 0; j < kRowsPer; ++j) {
+        const int64_t i = c0 + tid + (int64_t)j * kBlock;
+        v[j] = i < n1 ? (uint32_t)rowptr[i] : kNoRow;
+    }
+    // The smallest row pointer after this chunk: the first chunk minimum that
+    // is not a marker (they grow with the chunk).  Uniform trip count.
+    uint32_t carry = kNoRow;
+    for (int64_t w = (int64_t)blockIdx.x + 1; carry == kNoRow && w < nchunks; w += kRowsChunk) {
+        uint32_t m = kNoRow;
+#pragma unroll
+        for (int j = 0; j < kRowsPer; ++j) {
+            const int64_t q = w + tid + (int64_t)j * kBlock;
+            const uint32_t x = q < nchunks ? cmin[q] : kNoRow;
+            m = x < m ? x : m;
+        }
+        carry = block_reduce<false>(m);
+    }
+    uint32_t ex[kRowsPer];
+    rounds_exclusive<false>(v, ex, kNoRow, OpMin{});
+#pragma unroll
+    for (int j = 0; j < kRowsPer; ++j) {
+        const int64_t i = c0 + tid + (int64_t)j * kBlock;
+        const uint32_t after = ex[j] < carry ? ex[j] : carry;
+        if (i < n1 && v[j] == kNoRow) rowptr[i] = (int32_t)after;
     }
 }
 
@@ -786,13 +1069,36 @@ bool dual_mode(int64_t e) { return e <= kDualMaxEdges; }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The count scan of a pass over ntiles tiles (the digits' rows of both
+// directions with kDual), with as many counts per thread per step as the
+// segment length calls for.
+template <bool kDual, class KeySrc>
+void scan_launch(const PassDir<KeySrc> &d0, const PassDir<KeySrc> &d1, int64_t ntiles,
+                 int digits, hipStream_t s) {
+    const unsigned grid = (unsigned)((kDual ? 2 : 1) * digits * scan_segs(ntiles));
+    const int64_t len = scan_seg_len(ntiles);
+    if (len <= kBlock)
+        rs_scan<kDual, 1><<<grid, kBlock, 0, s>>>(d0.hist, d0.seg, d1.hist, d1.seg, ntiles, digits);
+    else if (len <= 4 * kBlock)
+        rs_scan<kDual, 4><<<grid, kBlock, 0, s>>>(d0.hist, d0.seg, d1.hist, d1.seg, ntiles, digits);
+    else
+        rs_scan<kDual, 16><<<grid, kBlock, 0, s>>>(d0.hist, d0.seg, d1.hist, d1.seg, ntiles,
+                                                   digits);
+}
+
 // One radix pass for one direction (d1 unused) or both (kDual), with tiles of
 // 256 * IT keys.
 // counted: the per-tile digit counts are already in hist (the counting intake).
-template <class KeySrc, bool kIota, bool kOther, bool kWriteKeys, bool kDual, int IT>
+// kRows: the last pass of a one-direction edge sort over more than
+// kInlineScanMaxTiles tiles, delimiting the rows (d0.rows) instead of writing
+// the keys.
+template <class KeySrc, bool kIota, bool kOther, bool kWriteKeys, bool kDual, int IT,
+          bool kRows = false>
 mp_status radix_pass(const PassDir<KeySrc> &d0, const PassDir<KeySrc> &d1, int64_t count,
                      int shift, int bits, hipStream_t s, bool counted = false) {
     const int64_t ntiles = tiles_for(count, IT);
+    if (kRows && ntiles <= kInlineScanMaxTiles)
+        return fail(MP_ERR_INTERNAL, "row heads need the scan kernel");
     const unsigned grid = (unsigned)((kDual ? 2 : 1) * ntiles);
     if (!counted) {
         if (lane_counts<IT>(bits))
@@ -802,13 +1108,23 @@ mp_status radix_pass(const PassDir<KeySrc> &d0, const PassDir<KeySrc> &d1, int64
             rs_upsweep<KeySrc, kDual, false, IT><<<grid, kBlock, 0, s>>>(d0, d1, count, shift,
                                                                          bits, ntiles);
     }
-    if (ntiles <= kInlineScanMaxTiles) {
+    if constexpr (kRows) {
+        const int digits = 1 << bits;
+        scan_launch<false>(d0, d0, ntiles, digits, s);
+        const bool dma = IT == kItems && (kIota || aligned16(d0.pl.vals_in)) &&
+                         aligned16(d0.pl.other_in);
+        if (dma)
+            rs_downsweep<KeySrc, kIota, true, false, false, false, IT, true, true>
+                <<<grid, kBlock, 0, s>>>(d0, d1, count, shift, bits, ntiles);
+        else
+            rs_downsweep<KeySrc, kIota, true, false, false, false, IT, false, true>
+                <<<grid, kBlock, 0, s>>>(d0, d1, count, shift, bits, ntiles);
+    } else if (ntiles <= kInlineScanMaxTiles) {
         rs_downsweep<KeySrc, kIota, kOther, kWriteKeys, kDual, true, IT>
             <<<grid, kBlock, 0, s>>>(d0, d1, count, shift, bits, ntiles);
     } else {
         const int digits = 1 << bits;
-        rs_scan<kDual><<<(kDual ? 2 : 1) * digits * scan_segs(ntiles), kBlock, 0, s>>>(
-            d0.hist, d0.seg, d1.hist, d1.seg, ntiles, digits);
+        scan_launch<kDual>(d0, d1, ntiles, digits, s);
         // Large single-direction edge passes copy their payload tiles to LDS
         // directly when the inputs allow 16-byte rows.
         const bool dma = kOther && !kDual && IT == kItems &&
@@ -822,6 +1138,21 @@ mp_status radix_pass(const PassDir<KeySrc> &d0, const PassDir<KeySrc> &d1, int64
     }
     MP_HIP_CHECK(hipGetLastError(), "radix pass launch");
     return MP_OK;
+}
+
+// Whether the last pass of a one-direction sort delimits the rows itself
+// (row_heads and the rows_* kernels) rather than writing the sorted keys for
+// a binary search per row.  It saves a key write and a search read per edge
+// and costs about 16 bytes per row pointer (markers, chunk minima, fill), so it
+// is taken for at least two edges per row; it needs the scan kernel (more than
+// kInlineScanMaxTiles tiles) and room for the run records and the chunk
+// maxima and minima in the pass's free key buffer ([e] words).
+bool rows_by_sort(int64_t e, int64_t n, int last_bits) {
+    const int64_t ntiles = tiles_for(e, kItems);
+    const int64_t runs = ((int64_t)1 << last_bits) * ntiles;
+    const int64_t rchunks = (runs + kRowsChunk - 1) / kRowsChunk;
+    const int64_t nchunks = (n + 1 + kRowsChunk - 1) / kRowsChunk;
+    return ntiles > kInlineScanMaxTiles && 2 * (n + 1) <= e && 2 * runs + rchunks + nchunks <= e;
 }
 
 // Sort buffers of one direction.
@@ -845,12 +1176,24 @@ struct EdgeDir {
 // directions in every launch; else dirs[0] only.
 // first_counted: the first pass's per-tile counts are already in the hist
 // buffers (the counting intake).
+// rowptr (one direction only): where the rows may be delimited by the last
+// pass (rows_by_sort); *rows_done tells whether they were, else the caller
+// takes them from the sorted keys.
 template <bool kDual>
 mp_status sort_edges(const EdgeDir *dirs, int64_t e, int64_t n, const uint32_t **sorted,
-                     hipStream_t s, bool first_counted = false) {
+                     hipStream_t s, bool first_counted = false, int32_t *rowptr = nullptr,
+                     bool *rows_done = nullptr) {
     constexpr int kDirs = kDual ? 2 : 1;
     const int bits = key_bits(n);
     const int passes = (bits + kDigitBits - 1) / kDigitBits;
+    const int per_bits = (bits + passes - 1) / passes;
+    const int last_bits = bits - (passes - 1) * per_bits;
+    const bool by_sort = !kDual && rowptr && rows_by_sort(e, n, last_bits);
+    if (rows_done) *rows_done = by_sort;
+    if (by_sort) {
+        rows_init_kernel<<<grid_for(n + 1), kBlock, 0, s>>>(rowptr, n, e);
+        MP_HIP_CHECK(hipGetLastError(), "row pointer marker launch");
+    }
     PassDir<KeysFromArray> pd[2];
     const uint32_t *kin[2];
     for (int i = 0; i < kDirs; ++i) {
@@ -881,7 +1224,35 @@ mp_status sort_edges(const EdgeDir *dirs, int64_t e, int64_t n, const uint32_t *
         if (!kDual) pd[1] = pd[0];
         // Small lists (both directions per launch) use small tiles.
         constexpr int IT = kDual ? kItemsSmall : kItems;
-        mp_status st = pass == 0
+        mp_status st;
+        if (by_sort && pass == passes - 1) {
+            // The free key buffer holds the run records, then the chunk maxima
+            // of their ends and the chunk minima of the row pointers.
+            const int64_t runs = ((int64_t)1 << pb) * tiles_for(e, IT);
+            uint32_t *rec = pd[0].pl.keys_out;
+            uint2 *run_recs = reinterpret_cast<uint2 *>(rec);
+            pd[0].rows = RowsOut{rowptr, run_recs};
+            pd[1] = pd[0];
+            st = pass == 0
+                ? radix_pass<KeysFromArray, true, true, false, false, IT, true>(
+                      pd[0], pd[1], e, shift, pb, s, first_counted)
+                : radix_pass<KeysFromArray, false, true, false, false, IT, true>(
+                      pd[0], pd[1], e, shift, pb, s);
+            if (st != MP_OK) return st;
+            const int64_t rchunks = (runs + kRowsChunk - 1) / kRowsChunk;
+            const int64_t nchunks = (n + 1 + kRowsChunk - 1) / kRowsChunk;
+            uint32_t *cmax = rec + 2 * runs;
+            uint32_t *cmin = cmax + rchunks;
+            rows_chunk_max_kernel<<<(unsigned)rchunks, kBlock, 0, s>>>(run_recs, runs, cmax);
+            rows_fixup_kernel<<<(unsigned)rchunks, kBlock, 0, s>>>(run_recs, pd[0].hist, cmax,
+                                                                    runs, rowptr);
+            rows_chunk_min_kernel<<<(unsigned)nchunks, kBlock, 0, s>>>(rowptr, n + 1, cmin);
+            rows_apply_kernel<<<(unsigned)nchunks, kBlock, 0, s>>>(rowptr, n + 1, cmin, nchunks);
+            MP_HIP_CHECK(hipGetLastError(), "row pointer launches");
+            sorted[0] = nullptr;
+            return MP_OK;
+        }
+        st = pass == 0
             ? radix_pass<KeysFromArray, true, true, true, kDual, IT>(pd[0], pd[1], e, shift, pb, s,
                                                                     first_counted)
             : radix_pass<KeysFromArray, false, true, true, kDual, IT>(pd[0], pd[1], e, shift, pb,
@@ -1034,9 +1405,12 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
         MP_HIP_CHECK(he, "fork of the transpose lowering");
         for (int i = 0; i < 2 && st == MP_OK; ++i) {
             hipStream_t q = i == 0 ? s : side;
-            if (e > 0) st = sort_edges<false>(&dirs[i], e, n, &sorted[i], q, counted);
-            const RowsDir r{sorted[i], i == 0 ? g->rowptr : g->rowptr_t};
-            if (st == MP_OK) st = row_pointers<false>(r, r, e, n, q);
+            int32_t *rowptr = i == 0 ? g->rowptr : g->rowptr_t;
+            bool rows_done = false;
+            if (e > 0)
+                st = sort_edges<false>(&dirs[i], e, n, &sorted[i], q, counted, rowptr, &rows_done);
+            const RowsDir r{sorted[i], rowptr};
+            if (st == MP_OK && !rows_done) st = row_pointers<false>(r, r, e, n, q);
             if (st == MP_OK)
                 st = plan_one(n, i == 0 ? g->rowptr : g->rowptr_t,
                               i == 0 ? g->row_plan : g->row_plan_t, b[i],
@@ -1055,9 +1429,11 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
                                     RowsDir{sorted[1], g->rowptr_t}, e, n, s);
     } else {
         for (int i = 0; i < 2 && st == MP_OK; ++i) {
-            st = sort_edges<false>(&dirs[i], e, n, &sorted[i], s, counted);
-            const RowsDir r{sorted[i], i == 0 ? g->rowptr : g->rowptr_t};
-            if (st == MP_OK) st = row_pointers<false>(r, r, e, n, s);
+            int32_t *rowptr = i == 0 ? g->rowptr : g->rowptr_t;
+            bool rows_done = false;
+            st = sort_edges<false>(&dirs[i], e, n, &sorted[i], s, counted, rowptr, &rows_done);
+            const RowsDir r{sorted[i], rowptr};
+            if (st == MP_OK && !rows_done) st = row_pointers<false>(r, r, e, n, s);
         }
     }
     if (st == MP_OK)

@@ -89,6 +89,49 @@ def test_large_list_key_widths(mp, n, e, seed, hubs):
     check_structure(_build(mp, wl), wl)
 
 
+# Lists of at least two edges per row, whose last sort pass delimits the rows
+# itself: keys already in order (a digit's runs sit in a few tiles, so the
+# first run of a digit follows thousands of empty run records), four keys with
+# long stretches of empty rows before, between and after them, every edge on
+# the first or the last row, keys in part of the range only, and both sides of
+# the two-edges-per-row rule.
+@pytest.mark.parametrize("n,e,seed,shape", [
+    (1 << 21, 20_000_003, 60, "sorted"),
+    (1 << 20, 4_500_000, 61, "sorted"),
+    (1 << 20, 4_500_000, 62, "few"),
+    (1 << 20, 4_500_000, 63, "first"),
+    (1 << 20, 4_500_000, 64, "last"),
+    (2_500_000, 5_000_002, 65, "random"),    # exactly two edges per row pointer
+    (2_500_000, 5_000_001, 66, "random"),    # one short: rows by binary search
+    (200, 4_200_000, 67, "sorted"),          # 8-bit keys: the counted pass is the last
+    # bipartite: destinations only in the upper half, sources in the lower, so
+    # each direction's first or last half of run records is empty
+    (1 << 21, 20_000_003, 68, "halves"),
+    (1 << 20, 4_500_000, 69, "ends"),        # keys in the first and last eighth only
+])
+def test_large_list_rows_from_last_pass(mp, n, e, seed, shape):
+    wl = synth.random_graph(n, e, 1, seed)
+    rng = np.random.default_rng(seed)
+    if shape == "sorted":
+        wl.dst = np.sort(wl.dst)
+        wl.src = np.sort(wl.src)
+    elif shape == "few":
+        wl.dst = np.array([3, 4097, 500_000, n - 7], dtype=wl.dst.dtype)[rng.integers(0, 4, e)]
+    elif shape == "first":
+        wl.dst[:] = 0
+        wl.src[:] = n - 1
+    elif shape == "last":
+        wl.dst[:] = n - 1
+        wl.src[:] = 0
+    elif shape == "halves":
+        wl.dst = n // 2 + wl.dst // 2
+        wl.src = wl.src // 2
+    elif shape == "ends":
+        wl.dst = np.where(wl.dst % 2 == 0, wl.dst // 16, n - 1 - wl.dst // 16)
+    print(f"case N={n} E={e} shape={shape}", flush=True)
+    check_structure(_build(mp, wl), wl)
+
+
 @pytest.mark.parametrize("idx_dtype", [torch.int32, torch.int64])
 def test_large_list_index_dtypes(mp, idx_dtype):
     wl = synth.random_graph(40000, 4_500_000, 1, 32)
@@ -171,22 +214,27 @@ def test_rejects_host_and_bad_dtype(mp):
         mp.mp_graph_build(torch.tensor([0], device=DEV), torch.tensor([0], device=DEV), 0)
 
 
-@pytest.mark.parametrize("n,e,seed", [
-    (3_000_000, 5_000_000, 40),     # three passes: the second reads the first's output arrays
-    (1 << 21, (1 << 22) + 4096 * 5 + 3, 41),   # a ragged last tile
+@pytest.mark.parametrize("n,e,seed,coo", [
+    (3_000_000, 5_000_000, 40, False),   # three passes: the second reads the first's outputs
+    (1 << 21, (1 << 22) + 4096 * 5 + 3, 41, False),   # a ragged last tile
+    # 8-bit keys: the one pass reads the endpoint copies, which are unaligned
+    # too, and delimits the rows itself
+    (200, 4_200_000, 42, True),
 ])
-def test_large_list_unaligned_graph_arrays(mp, n, e, seed):
+def test_large_list_unaligned_graph_arrays(mp, n, e, seed, coo):
     """Graph arrays need only 4-byte alignment.  With the CSR position maps and
-    columns 4 bytes past a 16-byte boundary the large passes that read them
-    take the register path instead of copying 16-byte rows to LDS; the result
-    is the aligned build's, bit for bit, and the oracle's."""
+    columns (and, with `coo`, the int32 endpoint copies) 4 bytes past a 16-byte
+    boundary the large passes that read them take the register path instead of
+    copying 16-byte rows to LDS; the result is the aligned build's, bit for
+    bit, and the oracle's."""
     wl = synth.random_graph(n, e, 1, seed)
     src = torch.from_numpy(wl.src).to(DEV)
     dst = torch.from_numpy(wl.dst).to(DEV)
     ref = mp.mp_graph_build(src, dst, n)
     g = mp.Graph(n, e, DEV)
     keep = []
-    for name in ("col", "edge_order", "col_t", "transpose_order"):
+    names = ("col", "edge_order", "col_t", "transpose_order") + (("src", "dst") if coo else ())
+    for name in names:
         buf = torch.empty(e + 4, dtype=torch.int32, device=DEV)
         view = buf[1:e + 1]                      # 4 bytes past the allocation's start
         assert view.data_ptr() % 16 == 4

@@ -25,13 +25,16 @@ def _workloads():
     yield synth.random_graph(1, 0, 8, 1)                       # no edges
     yield synth.random_graph(700, 9000, 16, 2)                 # a small list
     yield synth.minibatches(1, h=64)[0]
+    # large tiles here, both directions per launch in the one-stream build;
+    # rows delimited by the last sort pass
+    yield synth.random_graph(20_000, 400_000, 16, 4)
     # large lists (one direction per launch, payloads copied to LDS), a ragged
     # last tile, a skewed power law
     yield synth.random_graph(1 << 20, 4_300_001, 16, 3)
     yield synth.chung_lu(seed=35, n=300_000, e=6_000_000, cap=60_000.0, h=32, feat_dtype="bf16")
 
 
-@pytest.mark.parametrize("idx", range(6))
+@pytest.mark.parametrize("idx", range(7))
 def test_overlap_build_equals_one_stream(mp, idx):
     wl = list(_workloads())[idx]
     print(f"case N={wl.n} E={wl.e} H={wl.h}", flush=True)

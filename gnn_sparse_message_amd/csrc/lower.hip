@@ -24,10 +24,13 @@
 // Block-local ranks, never atomics, decide where equal keys land, so the
 // result is the unique stable order.  The opposite endpoint travels with each
 // key, so the last pass writes col[p] = other[order[p]] directly.  Rows are
-// then delimited by a binary search per row over the sorted keys.
+// delimited by the last pass itself when a list has at least two edges per
+// row (each key's first position, see row_heads), else by a binary search per
+// row over the sorted keys.
 #include "common.h"
 
 #include <mutex>
+#include <type_traits>
 
 // The lowering's workspace for mp_graph_build_noalloc, whose callers cannot
 // allocate device memory: one array per GPU, held until the process ends.
@@ -299,48 +302,54 @@ __device__ __forceinline__ void tile_digit_counts(const uint32_t (&k)[IT], int l
 constexpr int kLaneDigitBits = 7;
 constexpr int kLaneBins = 1 << kLaneDigitBits;
 
-// The same counts for digits below kLaneBins, with lane-private byte counters
-// instead of matching: word (j, lane) of a wave's table holds, one byte per
-// digit, how many of that lane's keys have digit 4j, 4j+1, 4j+2 or 4j+3, so
-// each key is one LDS add to a word no other lane touches (no ballots, no
-// bank or address conflicts).  The reduction sums 8 lanes' words bytewise
-// (at most 8 * IT per byte, below 256), splits the bytes into 16-bit fields
-// and adds those over the waves and the 8 lanes of a group.  Digits from
-// kLaneBins to kBins - 1 are written as 0.  Contains barriers: every thread
-// of the block calls it.
-template <int IT>
+// The same counts for digits below kLaneBins, with byte counters per lane
+// slot instead of matching: word (j, lane) of the block's table holds, one
+// byte per digit, how many keys of lane `lane` of any wave have digit 4j,
+// 4j+1, 4j+2 or 4j+3, so each key is one LDS add (atomic: the four waves share
+// the words) and a wave's adds never meet in a bank.  A byte counts at most
+// 4 * IT keys (below 256).  The reduction splits each word into two 16-bit
+// fields (digits 4j and 4j+2, 4j+1 and 4j+3) and adds them over the 64 lanes,
+// 8 words per thread and then across the 8 threads of a row.  One table of
+// 8 KB, not one per wave, so that more blocks fit on a CU.  Digits from
+// kLaneBins to kBins - 1 are written as 0.  kVec4: k holds the keys of
+// 16-byte loads, tile-local index li0 + (r / 4) * 256 + r % 4 for k[r] (else
+// li0 + r * 64).  Contains barriers: every thread of the block calls it.
+template <int IT, bool kVec4 = false>
 __device__ __forceinline__ void tile_lane_counts(const uint32_t (&k)[IT], int li0, int lim,
                                                  int shift, uint32_t mask,
                                                  uint32_t *__restrict__ hist, int64_t ntiles,
                                                  int64_t t) {
-    static_assert(8 * IT < 256, "a byte holds the keys of 8 lanes for one digit");
-    constexpr int kRows = kLaneBins / 4;                      // words per lane per wave
-    constexpr int kWords = kWavesPerBlock * kRows * kWave;
+    static_assert(kWavesPerBlock * IT < 256, "a byte holds one lane slot's keys of a digit");
+    constexpr int kRows = kLaneBins / 4;                      // words per lane slot
+    constexpr int kWords = kRows * kWave;
+    static_assert(kWords / 4 <= 2 * kBlock, "two 16-byte stores per thread clear the table");
     __shared__ uint4 s_lc4[kWords / 4];
     uint32_t *s_lc = reinterpret_cast<uint32_t *>(s_lc4);
     const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x / kWave;
     for (int i = threadIdx.x; i < kWords / 4; i += kBlock) s_lc4[i] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
-    uint32_t *mine = s_lc + wv * kRows * kWave + lane;
+    uint32_t *mine = s_lc + lane;
 #pragma unroll
     for (int r = 0; r < IT; ++r) {
         const uint32_t d = (k[r] >> shift) & mask;          // keys past the tile add 0
-        const uint32_t one = li0 + r * kWave < lim ? 1u : 0u;
+        const int li = kVec4 ? li0 + (r >> 2) * (kWave * 4) + (r & 3) : li0 + r * kWave;
+        const uint32_t one = li < lim ? 1u : 0u;
         __hip_atomic_fetch_add(mine + (d >> 2) * kWave, one << ((d & 3u) * 8u), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     __syncthreads();
-    // Thread (j, part) adds the words of lanes [8 part, 8 part + 8) of row j.
+    // Thread (j, part) adds the words of lane slots [8 part, 8 part + 8) of row j.
     const int j = threadIdx.x >> 3, part = threadIdx.x & 7;
     uint32_t lo = 0u, hi = 0u;                                // digits (4j, 4j+2), (4j+1, 4j+3)
-#pragma unroll
-    for (int w = 0; w < kWavesPerBlock; ++w) {
-        const uint4 *q = reinterpret_cast<const uint4 *>(s_lc + (w * kRows + j) * kWave + part * 8);
+    {
+        const uint4 *q = reinterpret_cast<const uint4 *>(s_lc + j * kWave + part * 8);
         const uint4 x = q[0], y = q[1];
-        const uint32_t b = x.x + x.y + x.z + x.w + y.x + y.y + y.z + y.w;
-        lo += b & 0x00ff00ffu;
-        hi += (b >> 8) & 0x00ff00ffu;
+        const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            lo += w[i] & 0x00ff00ffu;
+            hi += (w[i] >> 8) & 0x00ff00ffu;
+        }
     }
 #pragma unroll
     for (int off = 1; off < 8; off <<= 1) {
@@ -363,10 +372,13 @@ __device__ __forceinline__ void count_tile(const uint32_t (&k)[IT], int li0, int
 }
 
 // kLane: the pass's digits have at most kLaneDigitBits bits.
-template <class KeySrc, bool kDual, bool kLane, int IT>
+// kVec4 (keys from a 16-byte aligned array, lane counts): each lane loads four
+// consecutive keys at a time.
+template <class KeySrc, bool kDual, bool kLane, int IT, bool kVec4 = false>
 __global__ __launch_bounds__(kBlock) void rs_upsweep(PassDir<KeySrc> a0, PassDir<KeySrc> a1,
                                                      int64_t count, int shift, int bits,
                                                      int64_t ntiles) {
+    static_assert(!kVec4 || (kLane && IT % 4 == 0), "16-byte loads feed the lane counters");
     int dir;
     const int64_t t = block_tile<kDual>(ntiles, dir);
     const PassDir<KeySrc> &a = dir ? a1 : a0;
@@ -376,8 +388,27 @@ __global__ __launch_bounds__(kBlock) void rs_upsweep(PassDir<KeySrc> a0, PassDir
     const int64_t left = count - t * (kBlock * IT);
     const int lim = left < (kBlock * IT) ? (int)left : (kBlock * IT);        // keys in this tile
     const KeySrc tk = a.keys.at(t * (kBlock * IT));
-    const int li0 = wv * (kWave * IT) + lane;                   // tile-local index, round 0
     uint32_t k[IT];
+    if constexpr (kVec4) {
+        const int l4 = wv * (kWave * IT) + lane * 4;            // tile-local index of k[0]
+#pragma unroll
+        for (int q = 0; q < IT / 4; ++q) {
+            const int li = l4 + q * (kWave * 4);
+            if (li + 3 < lim) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(tk.k + li);
+                k[4 * q] = v.x;
+                k[4 * q + 1] = v.y;
+                k[4 * q + 2] = v.z;
+                k[4 * q + 3] = v.w;
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) k[4 * q + c] = li + c < lim ? tk.k[li + c] : 0u;
+            }
+        }
+        tile_lane_counts<IT, true>(k, l4, lim, shift, mask, a.hist, ntiles, t);
+        return;
+    }
+    const int li0 = wv * (kWave * IT) + lane;                   // tile-local index, round 0
 #pragma unroll
     for (int r = 0; r < IT; ++r) {
         const int li = li0 + r * kWave;
@@ -1101,7 +1132,14 @@ mp_status radix_pass(const PassDir<KeySrc> &d0, const PassDir<KeySrc> &d1, int64
         return fail(MP_ERR_INTERNAL, "row heads need the scan kernel");
     const unsigned grid = (unsigned)((kDual ? 2 : 1) * ntiles);
     if (!counted) {
-        if (lane_counts<IT>(bits))
+        bool vec = false;   // keys read 16 bytes at a time (lane counts, aligned keys)
+        if constexpr (std::is_same<KeySrc, KeysFromArray>::value && IT % 4 == 0)
+            vec = lane_counts<IT>(bits) && aligned16(d0.keys.k) && aligned16(d1.keys.k);
+        if (vec) {
+            if constexpr (std::is_same<KeySrc, KeysFromArray>::value && IT % 4 == 0)
+                rs_upsweep<KeySrc, kDual, true, IT, true><<<grid, kBlock, 0, s>>>(
+                    d0, d1, count, shift, bits, ntiles);
+        } else if (lane_counts<IT>(bits))
             rs_upsweep<KeySrc, kDual, true, IT><<<grid, kBlock, 0, s>>>(d0, d1, count, shift, bits,
                                                                         ntiles);
         else

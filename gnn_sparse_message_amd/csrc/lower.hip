@@ -887,24 +887,18 @@ constexpr int kRowsPer = 16;                        // entries per thread
 constexpr int kRowsChunk = kBlock * kRowsPer;       // entries per block
 constexpr uint32_t kNoRow = 0xffffffffu;
 
-// Max (kMax) or min over the block.  Contains barriers.
-template <bool kMax>
-__device__ uint32_t block_reduce(uint32_t x) {
+// op (OpMax or OpMin) over the block.  Contains barriers.
+template <class Op>
+__device__ uint32_t block_reduce(uint32_t x, Op op) {
     __shared__ uint32_t s_red[kWavesPerBlock];
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t y = __shfl_xor(x, off);
-        x = kMax ? (y > x ? y : x) : (y < x ? y : x);
-    }
+    for (int off = 1; off < kWave; off <<= 1) x = op(x, __shfl_xor(x, off));
     if (lane == 0) s_red[wv] = x;
     __syncthreads();
 #pragma unroll
-    for (int w = 0; w < kWavesPerBlock; ++w) {
-        const uint32_t y = s_red[w];
-        x = kMax ? (y > x ? y : x) : (y < x ? y : x);
-    }
+    for (int w = 0; w < kWavesPerBlock; ++w) x = op(x, s_red[w]);
     __syncthreads();
     return x;
 }
@@ -929,7 +923,7 @@ __global__ __launch_bounds__(kBlock) void rows_chunk_max_kernel(const uint2 *__r
         const uint32_t v = q < count ? runs[q].y : 0u;
         m = v > m ? v : m;
     }
-    m = block_reduce<true>(m);
+    m = block_reduce(m, OpMax{});
     if (threadIdx.x == 0) cmax[blockIdx.x] = m;
 }
 
@@ -964,7 +958,7 @@ __global__ __launch_bounds__(kBlock) void rows_fixup_kernel(const uint2 *__restr
             const uint32_t v = c < wend ? cmax[c] : 0u;
             m = v > m ? v : m;
         }
-        carry = block_reduce<true>(m);
+        carry = block_reduce(m, OpMax{});
         wend = wbeg;
     }
     uint32_t ex[kRowsPer];
@@ -989,7 +983,7 @@ __global__ __launch_bounds__(kBlock) void rows_chunk_min_kernel(const int32_t *_
         const uint32_t v = i < n1 ? (uint32_t)rowptr[i] : kNoRow;
         m = v < m ? v : m;
     }
-    m = block_reduce<false>(m);
+    m = block_reduce(m, OpMin{});
     if (threadIdx.x == 0) cmin[blockIdx.x] = m;
 }
 
@@ -1017,7 +1011,7 @@ __global__ __launch_bounds__(kBlock) void rows_apply_kernel(int32_t *__restrict_
             const uint32_t x = q < nchunks ? cmin[q] : kNoRow;
             m = x < m ? x : m;
         }
-        carry = block_reduce<false>(m);
+        carry = block_reduce(m, OpMin{});
     }
     uint32_t ex[kRowsPer];
     rounds_exclusive<false>(v, ex, kNoRow, OpMin{});

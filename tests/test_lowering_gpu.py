@@ -132,10 +132,21 @@ def test_large_list_rows_from_last_pass(mp, n, e, seed, shape):
     check_structure(_build(mp, wl), wl)
 
 
+# 16-bit keys (two 8-bit passes, ballot counts in the intake) and 20-bit keys
+# (7-bit passes: the intake reads its endpoints 16 bytes per lane); endpoint
+# arrays one element past a 16-byte boundary take the intake's 4- or 8-byte
+# loads.
 @pytest.mark.parametrize("idx_dtype", [torch.int32, torch.int64])
-def test_large_list_index_dtypes(mp, idx_dtype):
-    wl = synth.random_graph(40000, 4_500_000, 1, 32)
-    check_structure(_build(mp, wl, idx_dtype), wl)
+@pytest.mark.parametrize("n,offset", [(40000, 0), (1 << 20, 0), (1 << 20, 1)])
+def test_large_list_index_dtypes(mp, idx_dtype, n, offset):
+    wl = synth.random_graph(n, 4_500_000 + 4 * 4096 + 3, 1, 32)
+    src = torch.from_numpy(wl.src).to(DEV).to(idx_dtype)[offset:]
+    dst = torch.from_numpy(wl.dst).to(DEV).to(idx_dtype)[offset:]
+    assert (src.data_ptr() % 16 == 0) == (offset == 0)
+    wl.src, wl.dst = wl.src[offset:], wl.dst[offset:]
+    g = mp.mp_graph_build(src, dst, n)
+    torch.cuda.synchronize()
+    check_structure(g, wl)
 
 
 def test_large_list_bad_index(mp):

@@ -43,6 +43,7 @@ struct LowerLayout {
     size_t v0[2], o0[2];      // [E] u32: one ordinal and one endpoint buffer
     size_t hist[2];           // [256 * tiles] u32 per-tile digit counts (digit-major)
     size_t seg[2];            // [256 * 8] u32 segment totals of the count scan
+    size_t bad;               // [tiles] u32 per-tile range words of a small list's intake
     size_t total;
 };
 // split_dirs: each direction has its own sort buffers (the two directions of

@@ -267,6 +267,13 @@ struct PassDir {
     uint32_t *dtot;   // [kBins] digit totals, written by tile 0 of the downsweep when
                       // not nullptr
     RowsOut rows;     // only for the row-delimiting last pass
+    // When flag is not nullptr (the plan pass of a small list), tile 0 of the
+    // downsweep also writes *flag = 1 if any of the intake's per-tile range
+    // words bad[0 .. nbad) is set, else 0, so the flag needs no clearing
+    // launch before the intake.
+    const uint32_t *bad = nullptr;
+    int64_t nbad = 0;
+    uint32_t *flag = nullptr;
 };
 
 // Digit counts of one tile: k[r] is the key at tile-local index li0 + r * 64,
@@ -422,12 +429,15 @@ __global__ __launch_bounds__(kBlock) void rs_upsweep(PassDir<KeySrc> a0, PassDir
 // bounds, and raises the flag), and writes the first pass's digit counts of
 // both keys, dst for the forward sort and src for the transpose sort, so the
 // first pass of each direction needs no upsweep of its own.  Tiles as in the
-// radix passes (IT keys per thread, digit-major counts).
+// radix passes (IT keys per thread, digit-major counts).  With bad_tiles (small
+// lists) the block writes bad_tiles[t] = 1 or 0 instead of raising *flag, so
+// no launch has to clear the flag first (the plan pass reduces the words).
 template <typename IdxT, bool kLane, int IT>
 __global__ __launch_bounds__(kBlock) void intake_count_kernel(
     const IdxT *__restrict__ src, const IdxT *__restrict__ dst, int64_t e, int64_t n,
     int32_t *__restrict__ src32, int32_t *__restrict__ dst32, uint32_t *__restrict__ flag,
-    int bits, uint32_t *__restrict__ hist_f, uint32_t *__restrict__ hist_t, int64_t ntiles) {
+    uint32_t *__restrict__ bad_tiles, int bits, uint32_t *__restrict__ hist_f,
+    uint32_t *__restrict__ hist_t, int64_t ntiles) {
     const int64_t t = xcd_local_tile();
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
@@ -462,7 +472,12 @@ __global__ __launch_bounds__(kBlock) void intake_count_kernel(
             bad |= !(ok_s && ok_d);
         }
     }
-    if (bad) *flag = 1u;   // plain store: every writer stores the same value
+    if (bad_tiles) {       // the same for the whole block
+        const int any = __syncthreads_or((int)bad);
+        if (threadIdx.x == 0) bad_tiles[t] = any ? 1u : 0u;
+    } else if (bad) {
+        *flag = 1u;        // plain store: every writer stores the same value
+    }
     const uint32_t mask = (1u << bits) - 1u;
     count_tile<kLane>(kd, li0, lim, 0, mask, hist_f, ntiles, t);
     __syncthreads();       // the counts' LDS is reused by the second key
@@ -745,6 +760,12 @@ __global__ __launch_bounds__(kBlock) void rs_downsweep(PassDir<KeySrc> a0, PassD
             }
         }
         if (t == 0 && a.dtot) a.dtot[tid] = dsum;
+    }
+    if (t == 0 && a.flag) {   // the same for the whole block
+        uint32_t bad = 0u;
+        for (int64_t i = tid; i < a.nbad; i += kBlock) bad |= a.bad[i];
+        bad = (uint32_t)__syncthreads_or((int)bad);
+        if (tid == 0) *a.flag = bad ? 1u : 0u;
     }
     const uint32_t dbase = block_exclusive_scan(dsum, &all);
     s_cnt[0][tid] = tstart;
@@ -1059,27 +1080,30 @@ constexpr bool lane_counts(int bits) {
 template <bool kLane, int IT>
 void intake_launch(const void *src, const void *dst, mp_dtype idx_dtype, int64_t e, int64_t n,
                    mp_graph *g, int first_bits, uint32_t *hist_f, uint32_t *hist_t, int64_t nt,
-                   hipStream_t s) {
+                   uint32_t *bad_tiles, hipStream_t s) {
     if (idx_dtype == MP_I64)
         intake_count_kernel<int64_t, kLane, IT><<<(unsigned)nt, kBlock, 0, s>>>(
             static_cast<const int64_t *>(src), static_cast<const int64_t *>(dst), e, n, g->src,
-            g->dst, g->info + kInfoFlag, first_bits, hist_f, hist_t, nt);
+            g->dst, g->info + kInfoFlag, bad_tiles, first_bits, hist_f, hist_t, nt);
     else
         intake_count_kernel<int32_t, kLane, IT><<<(unsigned)nt, kBlock, 0, s>>>(
             static_cast<const int32_t *>(src), static_cast<const int32_t *>(dst), e, n, g->src,
-            g->dst, g->info + kInfoFlag, first_bits, hist_f, hist_t, nt);
+            g->dst, g->info + kInfoFlag, bad_tiles, first_bits, hist_f, hist_t, nt);
 }
 
 // Counting intake over tiles of 256 * IT edges.
+// bad_tiles: per-tile range words instead of the flag (see intake_count_kernel).
 template <int IT>
 void intake_count(const void *src, const void *dst, mp_dtype idx_dtype, int64_t e, int64_t n,
                   mp_graph *g, int first_bits, uint32_t *hist_f, uint32_t *hist_t,
-                  hipStream_t s) {
+                  uint32_t *bad_tiles, hipStream_t s) {
     const int64_t nt = tiles_for(e, IT);
     if (lane_counts<IT>(first_bits))
-        intake_launch<true, IT>(src, dst, idx_dtype, e, n, g, first_bits, hist_f, hist_t, nt, s);
+        intake_launch<true, IT>(src, dst, idx_dtype, e, n, g, first_bits, hist_f, hist_t, nt,
+                                bad_tiles, s);
     else
-        intake_launch<false, IT>(src, dst, idx_dtype, e, n, g, first_bits, hist_f, hist_t, nt, s);
+        intake_launch<false, IT>(src, dst, idx_dtype, e, n, g, first_bits, hist_f, hist_t, nt,
+                                 bad_tiles, s);
 }
 
 
@@ -1315,9 +1339,12 @@ mp_status row_pointers(const RowsDir &r0, const RowsDir &r1, int64_t e, int64_t 
 // the plan key, both directions in each launch (its scan only when there are
 // many row tiles).  The digit totals, i.e. the rows per class, land in
 // totals0 / totals1.
+// bad / nbad (small lists): the intake's per-tile range words, reduced into the
+// graph's index flag by the plan's downsweep.
 template <int IT>
 mp_status plans(int64_t n, mp_graph *g, const SortBufs &b0, const SortBufs &b1,
-                uint32_t *totals0, uint32_t *totals1, hipStream_t s) {
+                uint32_t *totals0, uint32_t *totals1, hipStream_t s,
+                const uint32_t *bad = nullptr, int64_t nbad = 0) {
     PassDir<KeysFromDegree> p0, p1;
     p0.keys = KeysFromDegree{g->rowptr};
     p1.keys = KeysFromDegree{g->rowptr_t};
@@ -1330,6 +1357,11 @@ mp_status plans(int64_t n, mp_graph *g, const SortBufs &b0, const SortBufs &b1,
     p1.seg = b1.seg;
     p0.dtot = totals0;
     p1.dtot = totals1;
+    if (bad) {
+        p0.bad = bad;
+        p0.nbad = nbad;
+        p0.flag = g->info + kInfoFlag;
+    }
     return radix_pass<KeysFromDegree, true, false, false, true, IT>(p0, p1, n, 0, kPlanBits, s);
 }
 
@@ -1371,6 +1403,8 @@ LowerLayout lower_layout(int64_t n, int64_t e, bool split_dirs) {
         L.hist[i] = off; off += hbytes;
         L.seg[i] = off; off += align_up((size_t)kBins * kScanSegs * sizeof(uint32_t));
     }
+    // Per-tile range words of a small list's intake (one word per 1024-edge tile).
+    L.bad = off; off += dual_mode(e) ? align_up((size_t)tiles_for(e, kItemsSmall) * 4) : 0;
     L.total = off;
     return L;
 }
@@ -1403,17 +1437,25 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
                         at(L.seg[i])};
     uint32_t *info = g->info;
 
-    // A fill kernel, not a memset: the sequence stays valid under graph capture.
-    zero_words_kernel<<<1, kBlock, 0, s>>>(info, MP_GRAPH_INFO_WORDS);
+    // Small lists (both directions per launch): the intake writes a range word
+    // per tile and the plan pass, the build's last launch, reduces them into
+    // the index flag, so the record needs no clearing launch.  Otherwise a fill
+    // kernel clears it (not a memset: the sequence stays valid under graph
+    // capture).
+    const bool small = dual_mode(e) && !split;
+    uint32_t *bad_tiles = small ? at(L.bad) : nullptr;
+    if (!small) zero_words_kernel<<<1, kBlock, 0, s>>>(info, MP_GRAPH_INFO_WORDS);
     // The intake also counts the first pass's digits of both keys, in the tiles
     // of that pass (1024 keys when both directions share the launches).
     const bool counted = e > 0;
     if (counted) {
         const int fb = first_pass_bits(n);
-        if (dual_mode(e) && !split)
-            intake_count<kItemsSmall>(src, dst, idx_dtype, e, n, g, fb, b[0].hist, b[1].hist, s);
+        if (small)
+            intake_count<kItemsSmall>(src, dst, idx_dtype, e, n, g, fb, b[0].hist, b[1].hist,
+                                      bad_tiles, s);
         else
-            intake_count<kItems>(src, dst, idx_dtype, e, n, g, fb, b[0].hist, b[1].hist, s);
+            intake_count<kItems>(src, dst, idx_dtype, e, n, g, fb, b[0].hist, b[1].hist,
+                                 nullptr, s);
     }
     MP_HIP_CHECK(hipGetLastError(), "intake launch");
 
@@ -1468,9 +1510,12 @@ mp_status lower_run(const void *src, const void *dst, mp_dtype idx_dtype, int64_
             if (st == MP_OK && !rows_done) st = row_pointers<false>(r, r, e, n, s);
         }
     }
+    // The plans; a small list's plan downsweep also settles the index flag.
+    const int64_t nbad = counted ? tiles_for(e, kItemsSmall) : 0;
     if (st == MP_OK)
         st = dual_mode(e)
-            ? plans<kItemsSmall>(n, g, b[0], b[1], info + kInfoPlanF, info + kInfoPlanT, s)
+            ? plans<kItemsSmall>(n, g, b[0], b[1], info + kInfoPlanF, info + kInfoPlanT, s,
+                                 bad_tiles, nbad)
             : plans<kItems>(n, g, b[0], b[1], info + kInfoPlanF, info + kInfoPlanT, s);
     if (st != MP_OK) return st;
 

@@ -215,6 +215,37 @@ def test_index_out_of_range(mp):
                           torch.tensor([0, 0], device=DEV), 3)
 
 
+@pytest.mark.parametrize("n,e,bad_at", [(70_000, 168_000, 0), (70_000, 168_000, 167_999),
+                                         (156_000, 1_500_000, 700_000)])
+def test_index_flag_from_tile_words_with_a_reused_workspace(mp, n, e, bad_at):
+    """Small lists report an out-of-range endpoint through one range word per
+    intake tile, reduced by the plan pass (no launch clears the flag first).
+    On one workspace: a clean build, a build with one bad endpoint (first,
+    last or a middle tile; synchronous and asynchronous), then a clean build
+    again, which must report nothing and equal the first bit for bit."""
+    wl = synth.random_graph(n, e, 1, 70 + bad_at % 7)
+    src = torch.from_numpy(wl.src).to(DEV)
+    dst = torch.from_numpy(wl.dst).to(DEV)
+    ws = torch.empty(mp.mp_graph_build_workspace_size(n, e), dtype=torch.uint8, device=DEV)
+    ref = mp.mp_graph_build(src, dst, n, workspace=ws)
+    check_structure(ref, wl)
+    bad = dst.clone()
+    bad[bad_at] = n
+    with pytest.raises(IndexError):
+        mp.mp_graph_build(src, bad, n, workspace=ws)
+    ga = mp.mp_graph_build_async(bad, src, n, workspace=ws)
+    with pytest.raises(IndexError):
+        mp.mp_graph_finish(ga)
+    again = mp.mp_graph_build(src, dst, n, workspace=ws)
+    ga = mp.mp_graph_build_async(src, dst, n, workspace=ws)
+    mp.mp_graph_finish(ga)
+    torch.cuda.synchronize()
+    for k in ref.arrays:
+        assert torch.equal(again.arrays[k], ref.arrays[k]), k
+        assert torch.equal(ga.arrays[k], ref.arrays[k]), k
+    assert again.class_count == ref.class_count and again.class_count_t == ref.class_count_t
+
+
 def test_rejects_host_and_bad_dtype(mp):
     with pytest.raises(ValueError):
         mp.mp_graph_build(torch.tensor([0, 1]), torch.tensor([1, 0]), 2)       # host memory

@@ -477,6 +477,16 @@ __device__ __forceinline__ void own_row(const SpmmArgs &a, int row, int64_t hoff
     }
 }
 
+// The owner row's softmax statistics (max, sum) when the forward forms softmax
+// weights at the fetch; unused otherwise.
+template <int kMode, bool kNorm>
+__device__ __forceinline__ float2 own_stats(const SpmmArgs &a, int row) {
+    if constexpr (kNorm && kMode == kPlain) {
+        if (a.norm.mode == kFetchSoftmax) return a.norm.stats[row];
+    }
+    return make_float2(0.f, 1.f);
+}
+
 // Edges [beg, end) of row `row` by the whole workgroup of kWaves waves, the
 // waves' partial sums added in wave order and stored to out (the row's slice of
 // the output, or a partial row of a split row).  len: the row's full length.
@@ -566,16 +576,6 @@ __device__ __forceinline__ void chunk_item(const SpmmArgs &a, int32_t item,
     if (!chunk_of(a, item, row, beg, end, len)) return;   // the same for the whole block
     hub_segment<T, VEC, L, kMode, kHeads, kNorm, kWavesPerBlock>(
         a, row, beg, end, len, a.partials + (int64_t)item * a.h, s_red);
-}
-
-// The owner row's softmax statistics (max, sum) when the forward forms softmax
-// weights at the fetch; unused otherwise.
-template <int kMode, bool kNorm>
-__device__ __forceinline__ float2 own_stats(const SpmmArgs &a, int row) {
-    if constexpr (kNorm && kMode == kPlain) {
-        if (a.norm.mode == kFetchSoftmax) return a.norm.stats[row];
-    }
-    return make_float2(0.f, 1.f);
 }
 
 // Occupancy floors: the single-head fused backward is held to five waves per

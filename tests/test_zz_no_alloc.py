@@ -83,3 +83,21 @@ def test_noalloc_rejects_graphs_beyond_the_static_workspace(mp):
     t = upload(wl, DEV)
     g = mp.mp_graph_finish(mp.mp_graph_build_noalloc(t["src"], t["dst"], wl.n))
     check_structure(g, wl)
+
+
+def test_noalloc_index_check_over_the_shared_workspace(mp):
+    """The index check of a small list is one range word per intake tile in the
+    workspace, reduced by the plan pass. On the static workspace, which keeps
+    the last call's contents, a build with an endpoint out of range reports it,
+    and the clean build after it reports nothing and equals a build on a
+    workspace of its own."""
+    wl = synth.random_graph(20_000, 300_000, 1, 8)
+    t = upload(wl, DEV)
+    bad = t["dst"].clone()
+    bad[150_000] = wl.n
+    with pytest.raises(IndexError):
+        mp.mp_graph_finish(mp.mp_graph_build_noalloc(t["src"], bad, wl.n))
+    g = mp.mp_graph_finish(mp.mp_graph_build_noalloc(t["src"], t["dst"], wl.n))
+    ref = mp.mp_graph_finish(mp.mp_graph_build_async(t["src"], t["dst"], wl.n))
+    _same_graph(g, ref)
+    check_structure(g, wl)

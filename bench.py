@@ -411,6 +411,9 @@ PROFILE_COMMANDS = {
              "-d <repo>/gpurun_out/p_write -o run -- python3 <repo>/bench.py --profile-ops",
     "l2": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv "
           "-d <repo>/gpurun_out/p_l2 -o run -- python3 <repo>/bench.py --profile-ops",
+    "minibatch_trace": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format "
+                       "csv -d <repo>/gpurun_out/p_trace_mb -o run -- python3 <repo>/bench.py "
+                       "--minibatch-only",
     "summary": "python3 bench.py --summarize-profiles gpurun_out",
 }
 
@@ -622,7 +625,60 @@ def summarize_profiles(base):
                   "", "Generated by `" + PROFILE_COMMANDS["summary"] + "`.", ""]
         with open(os.path.join(prof, "l2_hit_rates_chung_lu_step.md"), "w") as f:
             f.write("\n".join(lines))
+    mb_csv = os.path.join(base, "p_trace_mb", "run_kernel_stats.csv")
+    if os.path.exists(mb_csv):
+        summarize_minibatch_trace(mb_csv, os.path.join(prof, "kernel_trace_minibatch.md"))
     print(json.dumps({op: v["hbm_bytes_per_call"] for op, v in rec["ops"].items()}))
+
+
+# Kernel templates of the lowering (the build) and of the aggregations, by name prefix.
+_BUILD_KERNELS = ("zero_words_kernel", "intake_count_kernel", "rs_scan", "rs_upsweep",
+                  "rs_downsweep", "rowptr_kernel", "rows_")
+
+
+def summarize_minibatch_trace(csv_path, out_path):
+    """profiles/kernel_trace_minibatch.md from rocprofv3's kernel statistics of
+    `bench.py --minibatch-only`: every kernel template, then the GPU time per
+    build (each template's calls per build times its average duration; one
+    counting intake per build) and per forward and fused backward."""
+    stats = _read_csv(csv_path)
+    lines = ["# Kernel trace: 64 sampled minibatches (about 156K nodes, 168K edges, H = 256 "
+             "fp32 each), build + forward + fused backward per batch", "",
+             "Command (run from the repository root on the GPU box):", "", "```",
+             PROFILE_COMMANDS["minibatch_trace"], "```", "",
+             "Summary from rocprofv3's own `run_kernel_stats.csv` (the four schedules of the "
+             "minibatch object, each a warm-up and three timed passes over the 64 batches, and "
+             "the captured graph's replays; kernels of one template share a line):", "",
+             "| kernel | calls | avg us | min us | max us | % of GPU time |",
+             "|---|---:|---:|---:|---:|---:|"]
+    builds = 0
+    for r in stats:
+        nm = _short_name(r["Name"])
+        if nm.startswith("intake_count_kernel"):
+            builds += int(r["Calls"])
+        lines.append(f"| `{nm}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    if builds:
+        per_build, launches = 0.0, 0.0
+        fwd = bwd = 0.0
+        for r in stats:
+            nm = _short_name(r["Name"])
+            calls, avg = int(r["Calls"]), float(r["AverageNs"]) / 1e3
+            if nm.startswith(_BUILD_KERNELS):
+                per_build += calls / builds * avg
+                launches += calls / builds
+            elif nm.startswith("spmm_kernel<float") and ", 0, " in nm:
+                fwd += calls / builds * avg
+            elif nm.startswith("spmm_kernel<float") and ", 1, " in nm:
+                bwd += calls / builds * avg
+        lines += ["", f"Per build ({builds} builds traced): {launches:.1f} launches of the "
+                  f"lowering, {per_build:.1f} us of kernel time; forward {fwd:.1f} us and fused "
+                  f"backward {bwd:.1f} us per batch (kernel time only, without the gaps between "
+                  "launches)."]
+    lines += ["", "Generated by `" + PROFILE_COMMANDS["summary"] + "`.", ""]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines))
 
 
 def main():
@@ -645,6 +701,9 @@ def main():
     ap.add_argument("--profile-ops", action="store_true",
                     help="run every profiled op once, each after a marker kernel (for the "
                          "rocprofv3 counter runs), then exit")
+    ap.add_argument("--minibatch-only", action="store_true",
+                    help="run only the minibatch schedules and print their object (for the "
+                         "minibatch kernel trace)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write the profiles/ summaries from the rocprofv3 output under DIR "
                          "(p_trace, p_fetch, p_write, p_l2), then exit")
@@ -664,6 +723,10 @@ def main():
     import gnn_sparse_message_amd as mp
     import synth
 
+    if args.minibatch_only:
+        print(json.dumps({"minibatch": minibatch_bench(mp, torch, torch.device("cuda:0"))}),
+              flush=True)
+        return
     t0 = time.perf_counter()
     wl = synth.chung_lu()
     log(f"generated N={wl.n} E={wl.e} H={wl.h} ({wl.feat_dtype}) in {time.perf_counter() - t0:.1f}s")

@@ -400,21 +400,22 @@ def minibatch_bench(mp, torch, dev, n_batches=64, h=256):
 
 
 # rocprofv3 commands whose output --summarize-profiles reads (run from the
-# repository root on the GPU machine; <repo> is its absolute path).
+# repository root on the GPU machine; <repo> is its absolute path, <out> the
+# directory that receives the profiler's output).
 PROFILE_COMMANDS = {
     "trace": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
-             "-d <repo>/gpurun_out/p_trace -o run -- python3 <repo>/bench.py --steps 5 "
+             "-d <out>/p_trace -o run -- python3 <repo>/bench.py --steps 5 "
              "--warmup 2 --no-cpu-baseline --no-minibatch --no-other-configs",
     "fetch": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc FETCH_SIZE --output-format csv "
-             "-d <repo>/gpurun_out/p_fetch -o run -- python3 <repo>/bench.py --profile-ops",
+             "-d <out>/p_fetch -o run -- python3 <repo>/bench.py --profile-ops",
     "write": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc WRITE_SIZE --output-format csv "
-             "-d <repo>/gpurun_out/p_write -o run -- python3 <repo>/bench.py --profile-ops",
+             "-d <out>/p_write -o run -- python3 <repo>/bench.py --profile-ops",
     "l2": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv "
-          "-d <repo>/gpurun_out/p_l2 -o run -- python3 <repo>/bench.py --profile-ops",
+          "-d <out>/p_l2 -o run -- python3 <repo>/bench.py --profile-ops",
     "minibatch_trace": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format "
-                       "csv -d <repo>/gpurun_out/p_trace_mb -o run -- python3 <repo>/bench.py "
+                       "csv -d <out>/p_trace_mb -o run -- python3 <repo>/bench.py "
                        "--minibatch-only",
-    "summary": "python3 bench.py --summarize-profiles gpurun_out",
+    "summary": "python3 bench.py --summarize-profiles <out>",
 }
 
 

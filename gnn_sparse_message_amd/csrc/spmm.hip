@@ -467,13 +467,37 @@ __device__ __forceinline__ void accumulate(const SpmmArgs &a, int64_t first, int
 }
 
 // The owner row's slice of X (fused backward only).
+// Each owner reads its row once, so the load is non-temporal: the row does not
+// displace hot gathered rows in L2 (fused backward on the power-law graph 6.580
+// against 6.597 ms).  The values are those of Feat.
 template <typename T, int VEC, int kMode>
 __device__ __forceinline__ void own_row(const SpmmArgs &a, int row, int64_t hoff, bool active,
                                         float (&xr)[VEC]) {
 #pragma unroll
     for (int v = 0; v < VEC; ++v) xr[v] = 0.f;
     if constexpr (kMode != kPlain) {
-        if (active) Feat<T, VEC>::load(static_cast<const T *>(a.x_own) + (int64_t)row * a.h + hoff, xr);
+        if (!active) return;
+        const T *p = static_cast<const T *>(a.x_own) + (int64_t)row * a.h + hoff;
+        if constexpr (sizeof(T) == 2 && VEC == 8) {
+            typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {   // bf16 widened exactly, as Feat does
+                xr[2 * i] = __uint_as_float(q[i] << 16);
+                xr[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+            }
+        } else if constexpr (sizeof(T) == 4 && VEC % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < VEC; i += 4) {
+                const f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p + i));
+                xr[i] = q[0];
+                xr[i + 1] = q[1];
+                xr[i + 2] = q[2];
+                xr[i + 3] = q[3];
+            }
+        } else {
+            Feat<T, VEC>::load(p, xr);
+        }
     }
 }
 
